@@ -1,0 +1,238 @@
+"""Python binding of the MI355X BPE training library (``libbpe.so``).
+
+Argument marshalling only: every step of training runs in the library's HIP
+kernels; torch supplies device memory (inputs, outputs, workspace) and the
+stream. The C functions keep their names (``bpe_train`` -> ``train`` etc.);
+``include/bpe.h`` documents arguments, layouts, ownership and errors.
+
+Importing fails loudly if the library has not been built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbpe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("bpe_merge_amd: %s is not built (run __graft_entry__.build())" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, DONE = 0, 1
+EINVAL, ETABLE, EIDSPACE, ENOMEM, EHIP, ESTATE = -1, -2, -3, -4, -5, -6
+WORD_START = 0x10000
+ID_MASK = 0xFFFF
+BASE_VOCAB = 256
+MAX_MERGES = 65280
+MAX_BYTES = 0x7FFFFFFF
+
+
+class BpeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.bpe_strerror(status).decode()
+        detail = _lib.bpe_last_error().decode()
+        super().__init__("%s: %s%s" % (where, msg, (" (%s)" % detail) if detail else ""))
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("table_log2", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class Merge(ctypes.Structure):
+    _fields_ = [("left", ctypes.c_uint32), ("right", ctypes.c_uint32), ("count", ctypes.c_uint32)]
+
+
+class ProfileResult(ctypes.Structure):
+    _fields_ = [("find_max_ms", ctypes.c_double), ("merge_ms", ctypes.c_double),
+                ("launches", ctypes.c_uint32), ("merges_done", ctypes.c_uint32)]
+
+
+_vp, _sz, _u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
+_cfgp = ctypes.POINTER(Config)
+_SIGS = {
+    "bpe_workspace_bytes": (_sz, [_sz, _cfgp]),
+    "bpe_train": (ctypes.c_int, [_vp, _sz, _u32, _cfgp, _vp, ctypes.POINTER(_u32), _vp, _sz,
+                                 ctypes.POINTER(_sz)]),
+    "bpe_init": (ctypes.c_int, [_vp, _sz, _cfgp, ctypes.POINTER(_vp)]),
+    "bpe_run": (ctypes.c_int, [_vp, _u32]),
+    "bpe_sync": (ctypes.c_int, [_vp, ctypes.POINTER(_u32)]),
+    "bpe_step": (ctypes.c_int, [_vp, ctypes.POINTER(Merge)]),
+    "bpe_merges": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
+    "bpe_tokens": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_lengths": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
+    "bpe_pair_counts": (ctypes.c_int, [_vp, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult)]),
+    "bpe_free": (None, [_vp]),
+    "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "bpe_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(st: int, where: str) -> int:
+    if st < 0:
+        raise BpeError(st, where)
+    return st
+
+
+def _config(table_log2=None, stream=None, workspace=None) -> Config:
+    c = Config()
+    c.table_log2 = int(table_log2 or 0)
+    c.flags = 0
+    c.stream = stream
+    if workspace is not None:
+        c.workspace = workspace.data_ptr()
+        c.workspace_bytes = workspace.numel() * workspace.element_size()
+    return c
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(n: int, table_log2: int | None = None) -> int:
+    """bpe_workspace_bytes: device workspace for n corpus bytes (0 if invalid)."""
+    cfg = _config(table_log2)
+    return int(_lib.bpe_workspace_bytes(n, ctypes.byref(cfg)))
+
+
+def _workspace(n, table_log2, device):
+    torch = _torch()
+    nbytes = workspace_bytes(n, table_log2)
+    if nbytes == 0:
+        raise BpeError(EINVAL, "bpe_workspace_bytes")
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    shift = (-ws.data_ptr()) % 256
+    return ws[shift: shift + nbytes]
+
+
+def train(data, n_merges: int, table_log2: int | None = None):
+    """bpe_train on a uint8 CUDA tensor.
+
+    Returns (merges, tokens): int32 CUDA tensors of shape [k, 3] (left,
+    right, count; merge i creates id 256 + i) and [n_final] (id | 0x10000
+    on word starts)."""
+    torch = _torch()
+    if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+        raise TypeError("data must be a uint8 CUDA tensor")
+    data = data.contiguous().reshape(-1)
+    n = data.numel()
+    dev = data.device
+    merges = torch.empty((max(n_merges, 1), 3), dtype=torch.int32, device=dev)
+    tokens = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if n == 0:
+        return merges[:0], tokens[:0]
+    ws = _workspace(n, table_log2, dev)
+    cfg = _config(table_log2, _stream_handle(dev), ws)
+    n_done = _u32(0)
+    n_tok = _sz(0)
+    st = _lib.bpe_train(data.data_ptr(), n, n_merges, ctypes.byref(cfg), merges.data_ptr(), ctypes.byref(n_done),
+                        tokens.data_ptr(), tokens.numel(), ctypes.byref(n_tok))
+    _check(st, "bpe_train")
+    return merges[: n_done.value], tokens[: n_tok.value]
+
+
+class State:
+    """bpe_init ... bpe_free on a uint8 CUDA tensor, with a torch workspace."""
+
+    def __init__(self, data, table_log2: int | None = None):
+        torch = _torch()
+        if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+            raise TypeError("data must be a uint8 CUDA tensor")
+        self.data = data.contiguous().reshape(-1)
+        self.n = self.data.numel()
+        self.device = self.data.device
+        self.ws = _workspace(self.n, table_log2, self.device)
+        self.cfg = _config(table_log2, _stream_handle(self.device), self.ws)
+        self._h = _vp(None)
+        _check(_lib.bpe_init(self.data.data_ptr(), self.n, ctypes.byref(self.cfg), ctypes.byref(self._h)),
+               "bpe_init")
+
+    def run(self, n_merges: int) -> None:
+        _check(_lib.bpe_run(self._h, n_merges), "bpe_run")
+
+    def sync(self) -> int:
+        d = _u32(0)
+        _check(_lib.bpe_sync(self._h, ctypes.byref(d)), "bpe_sync")
+        return d.value
+
+    def step(self):
+        m = Merge()
+        st = _check(_lib.bpe_step(self._h, ctypes.byref(m)), "bpe_step")
+        return None if st == DONE else (m.left, m.right, m.count)
+
+    def merges(self):
+        torch = _torch()
+        k = _u32(0)
+        _check(_lib.bpe_merges(self._h, None, 0, ctypes.byref(k)), "bpe_merges")
+        out = torch.empty((max(k.value, 1), 3), dtype=torch.int32, device=self.device)
+        _check(_lib.bpe_merges(self._h, out.data_ptr(), k.value, ctypes.byref(k)), "bpe_merges")
+        return out[: k.value]
+
+    def tokens(self):
+        torch = _torch()
+        n = _sz(0)
+        _check(_lib.bpe_tokens(self._h, None, 0, ctypes.byref(n)), "bpe_tokens")
+        out = torch.empty(max(n.value, 1), dtype=torch.int32, device=self.device)
+        _check(_lib.bpe_tokens(self._h, out.data_ptr(), out.numel(), ctypes.byref(n)), "bpe_tokens")
+        return out[: n.value]
+
+    def lengths(self):
+        torch = _torch()
+        c = _u32(0)
+        _check(_lib.bpe_lengths(self._h, None, 0, ctypes.byref(c)), "bpe_lengths")
+        out = torch.empty(max(c.value, 1), dtype=torch.int32, device=self.device)
+        _check(_lib.bpe_lengths(self._h, out.data_ptr(), c.value, ctypes.byref(c)), "bpe_lengths")
+        return out[: c.value]
+
+    def pair_counts(self):
+        """(keys, counts) int64 host arrays of the current pair table, sorted by key."""
+        import numpy as np
+        n = _sz(0)
+        _check(_lib.bpe_pair_counts(self._h, None, None, 0, ctypes.byref(n)), "bpe_pair_counts")
+        keys = np.zeros(max(n.value, 1), dtype=np.uint32)
+        cnts = np.zeros(max(n.value, 1), dtype=np.uint32)
+        _check(_lib.bpe_pair_counts(self._h, keys.ctypes.data, cnts.ctypes.data, keys.size, ctypes.byref(n)),
+               "bpe_pair_counts")
+        keys, cnts = keys[: n.value].astype(np.int64), cnts[: n.value].astype(np.int64)
+        o = np.argsort(keys)
+        return keys[o], cnts[o]
+
+    def profile(self, n_merges: int) -> ProfileResult:
+        r = ProfileResult()
+        _check(_lib.bpe_profile(self._h, n_merges, ctypes.byref(r)), "bpe_profile")
+        return r
+
+    def free(self) -> None:
+        if self._h:
+            _lib.bpe_free(self._h)
+            self._h = _vp(None)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

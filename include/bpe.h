@@ -1,0 +1,168 @@
+/*
+ * bpe.h - C ABI of an MI355X (gfx950) library for byte-level BPE training.
+ *
+ * The operation is the training loop of the page "bpe - GPU BPE Tokenizer
+ * Pipeline (Egitim + Cikarim)" (llm.istanbul/learn/tr/13_bpe):
+ *   - "Nedir bu ya?": repeatedly find the most frequent adjacent pair of
+ *     symbols and give it one new symbol;
+ *   - "Ne Yapar? 1": each byte gets a character class (Letter, Digit,
+ *     Space, Punct, Newline; "Satir Satir Analiz 1)" prints the function);
+ *     at a class change the symbol is tagged with WORD_START_BIT 0x10000
+ *     and pairs are never counted across the tag;
+ *   - page head, training pipeline: every iteration clears the pair table,
+ *     counts all pairs again, takes a deterministic maximum, merges, and
+ *     compacts the symbol array with a prefix scan ("Ne Yapar? 3");
+ *   - "Ne Yapar? 3": the merged symbol carries WORD_START_BIT.
+ * Readings of points the page leaves open:
+ *   - the first symbol carries the tag, and the tag sits on the right-hand
+ *     symbol of a class change;
+ *   - every adjacent position counts, overlapping ones included
+ *     ("aaa" counts (a,a) twice);
+ *   - the maximum breaks ties to the smallest (left, right);
+ *   - merge k creates id 256 + k;
+ *   - merging is left to right and non-overlapping, so a run of identical
+ *     pairs merges its 1st, 3rd, 5th ... occurrence;
+ *   - the merged symbol keeps the left symbol's tag;
+ *   - tagging happens once, before the first iteration;
+ *   - training stops early when no countable pair is left.
+ *
+ * Symbols are uint32: bits 0-15 hold the id, bit 16 the word-start tag,
+ * bits 17-31 are zero. Ids fit in 16 bits, hence BPE_MAX_MERGES.
+ *
+ * Pointers: arguments named "bytes", "merges", "tokens" and "lengths" may be
+ * host or device pointers (device memory of the state's GPU); the library
+ * tells them apart with hipPointerGetAttributes. Output arrays are owned by
+ * the caller. A state and its workspace are owned by the library unless the
+ * caller passes a workspace in bpe_config, which must then outlive the state.
+ * No call throws, aborts or exits; each returns a bpe_status, and
+ * bpe_last_error() gives a thread-local message for the last failure.
+ * One state must not be used from two threads at once; separate states may.
+ */
+#ifndef BPE_H
+#define BPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BPE_OK = 0,         /* success                                                  */
+    BPE_DONE = 1,       /* bpe_step: no countable pair is left, nothing merged      */
+    BPE_EINVAL = -1,    /* bad argument (null pointer, size out of range, ...)      */
+    BPE_ETABLE = -2,    /* the global pair table overflowed; use a larger table     */
+    BPE_EIDSPACE = -3,  /* more than BPE_MAX_MERGES merges requested                */
+    BPE_ENOMEM = -4,    /* device or host allocation failed                         */
+    BPE_EHIP = -5,      /* a HIP runtime call failed (detail in bpe_last_error)     */
+    BPE_ESTATE = -6     /* the state holds a device-side error from an earlier call */
+} bpe_status;
+
+#define BPE_WORD_START 0x10000u
+#define BPE_ID_MASK 0xFFFFu
+#define BPE_BASE_VOCAB 256u
+#define BPE_MAX_MERGES 65280u            /* 0x10000 - 256: ids stay within 16 bits */
+#define BPE_MAX_BYTES 0x7FFFFFFFull      /* corpus size limit (2^31 - 1 bytes)     */
+
+/* One learned merge: (left, right) became id 256 + its index; count is the
+   number of adjacent (left, right) positions counted when it was chosen. */
+typedef struct {
+    uint32_t left, right, count;
+} bpe_merge;
+
+typedef struct {
+    uint32_t table_log2;     /* global pair table of 2^table_log2 slots (8 B each);
+                                0 = automatic; otherwise 10..30                       */
+    uint32_t flags;          /* reserved, must be 0                                    */
+    void *stream;            /* hipStream_t all work is ordered on; NULL = the state
+                                creates and owns a non-default stream                  */
+    void *workspace;         /* device memory of at least bpe_workspace_bytes();
+                                NULL = the state allocates its own                     */
+    size_t workspace_bytes;  /* size of workspace (ignored when workspace is NULL)     */
+} bpe_config;
+
+typedef struct bpe_state bpe_state;
+
+/* Device workspace needed for a corpus of n bytes with this config (cfg may be
+   NULL for defaults). Host arithmetic only; 0 if n or the config is invalid. */
+size_t bpe_workspace_bytes(size_t n, const bpe_config *cfg);
+
+/*
+ * Train up to n_merges merges on bytes[0..n) and return the result.
+ *   merges    out, n_merges entries (host or device); merge i creates id 256 + i
+ *   n_done    out (host): merges produced; < n_merges if no pair was left
+ *   tokens    out (host or device) or NULL: final symbols, id | tag
+ *   tokens_cap  capacity of tokens in elements (n always suffices)
+ *   n_tokens  out (host) or NULL: number of final symbols
+ * Blocks until the result is available. Equivalent to bpe_init + bpe_run +
+ * bpe_sync + bpe_merges + bpe_tokens + bpe_free. n == 0 is valid (no merges,
+ * no tokens). Errors: BPE_EINVAL, BPE_EIDSPACE (n_merges > BPE_MAX_MERGES),
+ * BPE_ETABLE (table overflow; nothing partial is returned), BPE_ENOMEM, BPE_EHIP.
+ */
+bpe_status bpe_train(const uint8_t *bytes, size_t n, uint32_t n_merges, const bpe_config *cfg,
+                     bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
+                     size_t *n_tokens);
+
+/* Create a training state: tag bytes[0..n) (n >= 1) into symbols and count
+   the pairs of iteration 0. Asynchronous on the state's stream; bytes must
+   stay valid until the next synchronising call (bpe_sync, bpe_step, ...). */
+bpe_status bpe_init(const uint8_t *bytes, size_t n, const bpe_config *cfg, bpe_state **out);
+
+/* Enqueue up to n_merges more iterations without waiting and without any
+   host round trip between iterations. Iterations after the last countable
+   pair do nothing. BPE_EIDSPACE if the total would exceed BPE_MAX_MERGES. */
+bpe_status bpe_run(bpe_state *s, uint32_t n_merges);
+
+/* Wait for the enqueued work; *n_done (may be NULL) = merges produced so far.
+   Returns BPE_ETABLE / BPE_ESTATE if the device reported an error. */
+bpe_status bpe_sync(bpe_state *s, uint32_t *n_done);
+
+/* One iteration, synchronously: *out = the merge made. BPE_DONE (and *out
+   untouched) when no countable pair is left. */
+bpe_status bpe_step(bpe_state *s, bpe_merge *out);
+
+/* Copy the merges produced so far (up to cap) to out; *n_out = how many exist. */
+bpe_status bpe_merges(bpe_state *s, bpe_merge *out, uint32_t cap, uint32_t *n_out);
+
+/* Copy the current symbol sequence to out; *n_out = its length. With out NULL
+   or cap 0 only the length is returned; cap below the length is BPE_EINVAL. */
+bpe_status bpe_tokens(bpe_state *s, uint32_t *out, size_t cap, size_t *n_out);
+
+/* Sequence length before each merge so far, then the current length:
+   out[0] = n, out[i] = length after merge i - 1; *n_out = merges + 1. */
+bpe_status bpe_lengths(bpe_state *s, uint32_t *out, uint32_t cap, uint32_t *n_out);
+
+/* The pair counts the next iteration will choose from (the counts of the
+   current sequence, "Ne Yapar? 2"): keys[i] = left << 16 | right, counts[i]
+   its number of adjacent positions, in table order; *n_out = number of
+   distinct pairs. Both arrays are host or device, cap entries each; with cap
+   0 only the number is returned, with cap below it BPE_EINVAL. */
+bpe_status bpe_pair_counts(bpe_state *s, uint32_t *keys, uint32_t *counts, size_t cap, size_t *n_out);
+
+/* Per-kernel device time of the iterations run by bpe_profile. */
+typedef struct {
+    double find_max_ms;      /* total time of the table sweep + argmax launches      */
+    double merge_ms;         /* total time of the fused merge/compact/count launches */
+    uint32_t launches;       /* number of iterations timed (each has one of each)    */
+    uint32_t merges_done;    /* merges produced by the state after the run           */
+} bpe_profile_result;
+
+/* Like bpe_run followed by bpe_sync, but with a HIP event around every kernel
+   launch on the state's stream, to time each kernel separately. */
+bpe_status bpe_profile(bpe_state *s, uint32_t n_merges, bpe_profile_result *out);
+
+/* Release the state and everything it owns (not a caller workspace). NULL is a no-op. */
+void bpe_free(bpe_state *s);
+
+/* Static description of a status code. */
+const char *bpe_strerror(bpe_status st);
+
+/* Thread-local detail of the most recent failure in this thread ("" if none). */
+const char *bpe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPE_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library loads and exports what include/bpe.h declares; host-side
+argument validation (no GPU needed: every check here runs before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(bpe_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def bpe():
+    import bpe_merge_amd
+    return bpe_merge_amd
+
+
+def test_every_declared_function_is_exported(bpe):
+    declared = _declared()
+    assert "bpe_train" in declared and "bpe_step" in declared
+    lib = ctypes.CDLL(bpe.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(bpe.EXPORTED)
+
+
+def test_library_is_gfx950_only():
+    import subprocess
+    lib = os.path.join(ROOT, "bpe_merge_amd", "libbpe.so")
+    out = subprocess.run(["strings", lib], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+    for other in ("gfx942", "gfx90a", "gfx1100", "sm_"):
+        assert "amdgcn-amd-amdhsa--" + other not in out
+
+
+def test_strerror(bpe):
+    lib = bpe._lib
+    for st, word in [(0, "ok"), (1, "pair"), (-1, "invalid"), (-2, "table"), (-3, "id space"),
+                     (-4, "memory"), (-5, "HIP"), (-6, "device error"), (-99, "unknown")]:
+        assert word in lib.bpe_strerror(st).decode()
+
+
+def test_workspace_bytes(bpe):
+    ws = bpe.workspace_bytes(1 << 28, 22)
+    # two uint32 symbol buffers + an 8-byte-slot table, plus small fixed parts
+    assert 2 * 4 * (1 << 28) + 8 * (1 << 22) <= ws <= 2 * 4 * (1 << 28) + 8 * (1 << 22) + (8 << 20)
+    assert bpe.workspace_bytes(10, 0) > 0
+    assert bpe.workspace_bytes(1 << 31, 22) == 0       # above the size limit
+    assert bpe.workspace_bytes(100, 9) == 0            # table_log2 out of range
+    assert bpe.workspace_bytes(100, 31) == 0
+
+
+def test_train_argument_validation_before_any_device_call(bpe):
+    lib = bpe._lib
+    n_done = ctypes.c_uint32(7)
+    n_tok = ctypes.c_size_t(7)
+    buf = (ctypes.c_uint8 * 16)()
+    merges = (ctypes.c_uint32 * 3 * 8)()
+    toks = (ctypes.c_uint32 * 16)()
+    # too many merges for 16-bit ids
+    st = lib.bpe_train(ctypes.addressof(buf), 16, 65281, None, ctypes.addressof(merges),
+                       ctypes.byref(n_done), None, 0, None)
+    assert st == bpe.EIDSPACE
+    assert "65281" in lib.bpe_last_error().decode()
+    # null pointers
+    assert lib.bpe_train(None, 16, 4, None, ctypes.addressof(merges), ctypes.byref(n_done), None, 0,
+                         None) == bpe.EINVAL
+    assert lib.bpe_train(ctypes.addressof(buf), 16, 4, None, None, ctypes.byref(n_done), None, 0,
+                         None) == bpe.EINVAL
+    assert lib.bpe_train(ctypes.addressof(buf), 16, 4, None, ctypes.addressof(merges), None, None, 0,
+                         None) == bpe.EINVAL
+    # token capacity below n
+    assert lib.bpe_train(ctypes.addressof(buf), 16, 4, None, ctypes.addressof(merges), ctypes.byref(n_done),
+                         ctypes.addressof(toks), 15, ctypes.byref(n_tok)) == bpe.EINVAL
+    # bad config
+    cfg = bpe.Config(); cfg.table_log2 = 5
+    assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
+                         ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
+    cfg = bpe.Config(); cfg.flags = 1
+    assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
+                         ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
+    # an empty corpus is valid and needs no device
+    n_done.value = 9
+    assert lib.bpe_train(None, 0, 4, None, ctypes.addressof(merges), ctypes.byref(n_done), None, 0,
+                         ctypes.byref(n_tok)) == bpe.OK
+    assert n_done.value == 0 and n_tok.value == 0
+
+
+def test_state_calls_reject_null(bpe):
+    lib = bpe._lib
+    h = ctypes.c_void_p()
+    buf = (ctypes.c_uint8 * 4)()
+    assert lib.bpe_init(None, 4, None, ctypes.byref(h)) == bpe.EINVAL
+    assert lib.bpe_init(ctypes.addressof(buf), 0, None, ctypes.byref(h)) == bpe.EINVAL
+    assert lib.bpe_init(ctypes.addressof(buf), 4, None, None) == bpe.EINVAL
+    assert lib.bpe_run(None, 1) == bpe.EINVAL
+    assert lib.bpe_sync(None, None) == bpe.EINVAL
+    assert lib.bpe_step(None, None) == bpe.EINVAL
+    assert lib.bpe_tokens(None, None, 0, None) == bpe.EINVAL
+    assert lib.bpe_merges(None, None, 0, None) == bpe.EINVAL
+    assert lib.bpe_lengths(None, None, 0, None) == bpe.EINVAL
+    assert lib.bpe_pair_counts(None, None, None, 0, None) == bpe.EINVAL
+    assert lib.bpe_profile(None, 1, None) == bpe.EINVAL
+    lib.bpe_free(None)  # no-op
+
+
+def test_binding_has_no_fallback(bpe):
+    # the product path must not import the oracle or any CPU implementation
+    src = open(os.path.join(ROOT, "bpe_merge_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("oracle/", "")
+    assert "import corpus" not in src
