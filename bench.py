@@ -1,0 +1,196 @@
+"""Benchmark: BPE training on one MI355X, one JSON line on stdout.
+
+A step is one whole training job on device-resident bytes: tag + count
+(bpe_init), every merge iteration (pair-table sweep + argmax, merge +
+compaction + recount of the new sequence), and the copy-out of merges and
+tokens. The default workload is the 256 MiB ASCII corpus with 32,000 merges
+and a 2^22-slot pair table. Warm-up steps run without per-kernel events;
+timed steps run with a HIP event between consecutive kernels on the
+library's stream (one host wait per step), which gives both the wall-clock
+value and the per-kernel times behind the roofline figures.
+
+Algorithmic bytes of iteration k (n_k symbols before it, n_{k+1} after):
+  merge kernel     4 n_k + 4 n_{k+1}   (read the symbols once, write the result once)
+  find-max kernel  16 T                (read every 8-byte table slot, reset it)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def pct(a, q):
+    import numpy as np
+    return float(np.percentile(a, q)) if len(a) else 0.0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 256 MiB, 32k merges)")
+    ap.add_argument("--merges", type=int, default=None, help="override the merge count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", default=None, help="write per-iteration details to this JSON file")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the training path here is single-GPU and --gpus %d is not "
+              "supported (multi-GPU sharding is a design note, not built)" % max(args.gpus, world),
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bpe_merge_amd as bpe
+    import corpus
+
+    spec = corpus.CONFIGS[args.config]
+    if args.merges is not None:
+        spec = spec.scaled(spec.n_bytes, n_merges=args.merges)
+    n_merges, tlog2 = spec.n_merges, spec.table_log2
+    T = 1 << tlog2
+    log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
+    data = corpus.generate(spec)
+    sha = corpus.sha256(data)
+    d = torch.from_numpy(data).to("cuda:0")
+    torch.cuda.synchronize()
+
+    def step(profiled: bool):
+        t0 = time.perf_counter()
+        st = bpe.State(d, table_log2=tlog2)
+        prof = None
+        if profiled:
+            prof = st.profile(n_merges, per_iteration=True)
+        else:
+            st.run(n_merges)
+            st.sync()
+        merges = st.merges()
+        tokens = st.tokens()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        lengths = st.lengths().cpu().numpy().astype(np.int64)
+        st.free()
+        return t1 - t0, merges, tokens, lengths, prof
+
+    warm_s = []
+    for i in range(args.warmup):
+        dt, m, t, _, _ = step(False)
+        warm_s.append(dt)
+        log("warmup step %d: %.3f s, %d merges, %d tokens" % (i + 1, dt, m.shape[0], t.shape[0]))
+    wall = []
+    last = None
+    ref = None
+    for i in range(args.steps):
+        torch.cuda.synchronize()
+        dt, m, t, lengths, prof = step(True)
+        wall.append(dt)
+        last = (m, t, lengths, prof)
+        sig = (m.cpu().numpy().tobytes(), t.shape[0])
+        if ref is None:
+            ref = sig
+        elif sig != ref:
+            log("ERROR: timed steps disagree")
+            return 1
+        log("timed step %d: %.3f s, %d merges" % (i + 1, dt, m.shape[0]))
+
+    m, t, lengths, prof = last
+    r, f_ms, m_ms = prof
+    k = m.shape[0]
+    n_k = lengths[:k].astype(np.float64)
+    n_k1 = lengths[1: k + 1].astype(np.float64)
+    f_ms = f_ms[:k].astype(np.float64)
+    m_ms = m_ms[:k].astype(np.float64)
+    it_s = (f_ms + m_ms) / 1e3
+    merge_bytes = 4.0 * n_k + 4.0 * n_k1
+    find_bytes = np.full(k, 16.0 * T)
+    iter_bytes = merge_bytes + find_bytes
+    total_wall = float(sum(wall))
+    value = k * len(wall) / total_wall
+    sym_per_s_agg = float(n_k.sum() / it_s.sum())
+    hbm_agg = float(iter_bytes.sum() / it_s.sum() / 1e9)
+    merge_gbps = float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9)
+    find_gbps = float(find_bytes.sum() / (f_ms.sum() / 1e3) / 1e9)
+    per_it_sym = n_k / it_s
+    per_it_gbps = iter_bytes / it_s / 1e9
+    dominant = "k_merge" if m_ms.sum() >= f_ms.sum() else "k_find_max"
+    if dominant == "k_merge":
+        achieved, avg_bytes, avg_ms = merge_gbps, float(merge_bytes.mean()), float(m_ms.mean())
+    else:
+        achieved, avg_bytes, avg_ms = find_gbps, 16.0 * T, float(f_ms.mean())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle (chunk-multiset, single thread) on the same corpus")
+        t0 = time.perf_counter()
+        om, ot, _ = oracle.train_chunks(data, n_merges)
+        cpu_s = time.perf_counter() - t0
+        same = np.array_equal(om, m.cpu().numpy().astype(np.int64)) and \
+            np.array_equal(ot, t.cpu().numpy().astype(np.uint32))
+        cpu = {"value": round(len(om) / cpu_s, 3), "unit": "merges/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole workload (%d bytes, %d merges) through the chunk-multiset C oracle "
+                         "(oracle/bpe_oracle.c, train_chunks), one thread, %.2f s including chunking; "
+                         "GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, same)}
+        log("oracle: %.2f s, bit-identical to the GPU result: %s" % (cpu_s, same))
+
+    out = {
+        "metric": "BPE train merges/sec + symbols/sec per merge, 256 MiB/32k merges; HBM GB/s",
+        "value": round(value, 3),
+        "unit": "merges/s",
+        "n_gpus": 1,
+        "steps": len(wall),
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * total_wall / len(wall), 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %d-byte seeded corpus (%s), %d merges, pair table 2^%d, sha256 %s"
+                        % (spec.name, spec.n_bytes, spec.kind, n_merges, tlog2, sha[:16]),
+            "corpus_bytes": spec.n_bytes,
+            "n_merges": n_merges,
+            "merges_done": int(k),
+            "table_slots": T,
+            "final_tokens": int(t.shape[0]),
+        },
+        "symbols_per_s_per_merge": {"aggregate": sym_per_s_agg, "p10": pct(per_it_sym, 10),
+                                    "p50": pct(per_it_sym, 50), "p90": pct(per_it_sym, 90)},
+        "hbm_gbps_per_iteration": {"aggregate": round(hbm_agg, 1), "frac_of_peak": round(hbm_agg / HBM_PEAK_GBPS, 4),
+                                   "p10": round(pct(per_it_gbps, 10), 1), "p50": round(pct(per_it_gbps, 50), 1),
+                                   "p90": round(pct(per_it_gbps, 90), 1)},
+        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_find_max": round(float(f_ms.sum()), 3),
+                                "k_merge_gbps": round(merge_gbps, 1), "k_find_max_gbps": round(find_gbps, 1)},
+        "warmup_unprofiled_s": [round(x, 3) for x in warm_s],
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    if args.report:
+        with open(args.report, "w") as fh:
+            json.dump({"summary": out, "lengths": lengths.tolist(), "find_ms": f_ms.tolist(),
+                       "merge_ms": m_ms.tolist()}, fh)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

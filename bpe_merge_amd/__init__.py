@@ -67,7 +67,7 @@ _SIGS = {
     "bpe_tokens": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_lengths": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
     "bpe_pair_counts": (ctypes.c_int, [_vp, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
-    "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult)]),
+    "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp, _vp]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "bpe_last_error": (ctypes.c_char_p, []),
@@ -215,10 +215,15 @@ class State:
         o = np.argsort(keys)
         return keys[o], cnts[o]
 
-    def profile(self, n_merges: int) -> ProfileResult:
+    def profile(self, n_merges: int, per_iteration: bool = False):
+        """bpe_profile; with per_iteration also (find_ms, merge_ms) float32 arrays."""
+        import numpy as np
         r = ProfileResult()
-        _check(_lib.bpe_profile(self._h, n_merges, ctypes.byref(r)), "bpe_profile")
-        return r
+        f = np.zeros(max(n_merges, 1), dtype=np.float32) if per_iteration else None
+        m = np.zeros(max(n_merges, 1), dtype=np.float32) if per_iteration else None
+        _check(_lib.bpe_profile(self._h, n_merges, ctypes.byref(r), f.ctypes.data if per_iteration else None,
+                                m.ctypes.data if per_iteration else None), "bpe_profile")
+        return (r, f[:n_merges], m[:n_merges]) if per_iteration else r
 
     def free(self) -> None:
         if self._h:

@@ -14,22 +14,23 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "../../include/bpe.h"
 #include "kernels.hpp"
+#include "merge.hpp"
 
 using bpek::Ctl;
 
 namespace {
 
 // launch shapes
-constexpr int MERGE_TPB = 256;
-constexpr int MERGE_V = 16;
+constexpr int MERGE_TPB = 512;
 constexpr int MERGE_LT = 4096;             // LDS pair-table slots per workgroup
-constexpr int TILE = MERGE_TPB * MERGE_V;  // symbols per scan tile
+constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 constexpr int FIND_TPB = 256;
@@ -153,7 +154,7 @@ bpe_status launch_iteration(bpe_state* s) {
     const uint32_t T = 1u << s->tlog2;
     hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
                        s->ctl, s->table, T, s->merges);
-    hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_V, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB),
+    hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB),
                        0, s->stream, s->ctl, s->sym0, s->sym1, s->table, T - 1, s->status, s->lengths);
     return BPE_OK;
 }
@@ -170,6 +171,27 @@ bpe_status read_ctl(bpe_state* s, Ctl* h) {
         set_err("device error bits 0x%x", h->err);
         return BPE_ESTATE;
     }
+    return BPE_OK;
+}
+
+// Timing events, kept per device for the life of the process so that a
+// profiled run does not pay for creating them.
+std::mutex g_ev_mu;
+std::vector<hipEvent_t> g_ev[64];
+
+bpe_status event_pool(int device, size_t count, std::vector<hipEvent_t>** out) {
+    if (device < 0 || device >= 64) {
+        set_err("device index %d out of range", device);
+        return BPE_EINVAL;
+    }
+    std::lock_guard<std::mutex> lk(g_ev_mu);
+    std::vector<hipEvent_t>& v = g_ev[device];
+    while (v.size() < count) {
+        hipEvent_t e;
+        HIP_TRY(hipEventCreate(&e));
+        v.push_back(e);
+    }
+    *out = &v;
     return BPE_OK;
 }
 
@@ -287,13 +309,14 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         return fail(BPE_EHIP);
     }
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB, MERGE_V, MERGE_LT>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB, MERGE_LT>,
                                                      MERGE_TPB, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     s->merge_grid = cus * per_cu;
     s->tag_grid = cus * 2;
     const uint32_t T = 1u << tlog2;
-    s->find_grid = int(std::min<size_t>(size_t(cus) * 8, std::max<size_t>(1, (T / 2 + FIND_TPB - 1) / FIND_TPB)));
+    // the sweep covers 4 x 16 bytes (8 slots) per thread per round
+    s->find_grid = int(std::min<size_t>(size_t(cus) * 4, std::max<size_t>(1, (T / 8 + FIND_TPB - 1) / FIND_TPB)));
     s->fill_grid = cus * 4;
 
     // input bytes: device memory is read in place, host memory is uploaded
@@ -477,7 +500,8 @@ bpe_status bpe_pair_counts(bpe_state* s, uint32_t* keys, uint32_t* counts, size_
     return BPE_OK;
 }
 
-bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res) {
+bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res, float* find_ms,
+                       float* merge_ms) {
     g_err.clear();
     if (!s || !res) {
         set_err("state and out must be non-NULL");
@@ -489,43 +513,34 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res)
     }
     HIP_TRY(hipSetDevice(s->device));
     std::memset(res, 0, sizeof *res);
-    bpe_status st = enqueue_run(s, n_merges);
+    std::vector<hipEvent_t>* ev = nullptr;
+    bpe_status st = event_pool(s->device, 2 * size_t(n_merges) + 1, &ev);
     if (st != BPE_OK) return st;
-    constexpr uint32_t BATCH = 256;
-    std::vector<hipEvent_t> ev(2 * BATCH + 1);
-    for (auto& e : ev) HIP_TRY(hipEventCreate(&e));
+    st = enqueue_run(s, n_merges);
+    if (st != BPE_OK) return st;
     const uint32_t T = 1u << s->tlog2;
-    bpe_status rc = BPE_OK;
-    for (uint32_t done = 0; done < n_merges && rc == BPE_OK;) {
-        const uint32_t b = std::min(BATCH, n_merges - done);
-        (void)hipEventRecord(ev[0], s->stream);
-        for (uint32_t i = 0; i < b; ++i) {
-            hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
-                               s->ctl, s->table, T, s->merges);
-            (void)hipEventRecord(ev[2 * i + 1], s->stream);
-            hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_V, MERGE_LT>), dim3(s->merge_grid),
-                               dim3(MERGE_TPB), 0, s->stream, s->ctl, s->sym0, s->sym1, s->table, T - 1,
-                               s->status, s->lengths);
-            (void)hipEventRecord(ev[2 * i + 2], s->stream);
-        }
-        hipError_t e = hipEventSynchronize(ev[2 * b]);
-        if (e != hipSuccess) {
-            set_err("hipEventSynchronize failed: %s", hipGetErrorString(e));
-            rc = BPE_EHIP;
-            break;
-        }
-        for (uint32_t i = 0; i < b; ++i) {
-            float a = 0.f, c = 0.f;
-            (void)hipEventElapsedTime(&a, ev[2 * i], ev[2 * i + 1]);
-            (void)hipEventElapsedTime(&c, ev[2 * i + 1], ev[2 * i + 2]);
-            res->find_max_ms += a;
-            res->merge_ms += c;
-        }
-        res->launches += b;
-        done += b;
+    std::vector<hipEvent_t>& e = *ev;
+    HIP_TRY(hipEventRecord(e[0], s->stream));
+    for (uint32_t i = 0; i < n_merges; ++i) {
+        hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream, s->ctl,
+                           s->table, T, s->merges);
+        HIP_TRY(hipEventRecord(e[2 * size_t(i) + 1], s->stream));
+        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0,
+                           s->stream, s->ctl, s->sym0, s->sym1, s->table, T - 1, s->status, s->lengths);
+        HIP_TRY(hipEventRecord(e[2 * size_t(i) + 2], s->stream));
     }
-    for (auto& e : ev) (void)hipEventDestroy(e);
-    if (rc != BPE_OK) return rc;
+    HIP_TRY(hipGetLastError());
+    HIP_TRY(hipEventSynchronize(e[2 * size_t(n_merges)]));
+    for (uint32_t i = 0; i < n_merges; ++i) {
+        float a = 0.f, c = 0.f;
+        HIP_TRY(hipEventElapsedTime(&a, e[2 * size_t(i)], e[2 * size_t(i) + 1]));
+        HIP_TRY(hipEventElapsedTime(&c, e[2 * size_t(i) + 1], e[2 * size_t(i) + 2]));
+        res->find_max_ms += a;
+        res->merge_ms += c;
+        if (find_ms) find_ms[i] = a;
+        if (merge_ms) merge_ms[i] = c;
+    }
+    res->launches = n_merges;
     Ctl h;
     st = read_ctl(s, &h);
     res->merges_done = h.k;

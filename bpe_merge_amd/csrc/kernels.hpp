@@ -107,65 +107,142 @@ __device__ __forceinline__ void global_add(uint32_t* table, uint32_t mask, uint3
     atomicExch(&ctl->done, 1u);
 }
 
-// Workgroup table in LDS: LT slots; a key that finds no slot within
-// LDS_PROBES goes straight to the global table.
+// Workgroup pair table in LDS: LT slots in buckets of 4, read with one
+// 16-byte LDS load, so a key sits at its first probe unless its whole home
+// bucket was taken first. Counting a batch of keys is two phases per group
+// of 8 keys per thread:
+//   1. every lane reads the home buckets of its keys and adds the counts of
+//      keys it finds (no divergent probe loops);
+//   2. keys not found are queued in LDS and, after a barrier, the whole
+//      block inserts them, one queued key per lane (claiming slots with CAS,
+//      probing further buckets, or going to the global table).
+// The table is flushed into the global table and cleared once it is half
+// full, and at the end of a kernel. Plain data (no constructor) so that it
+// can live in __shared__.
 template <int LT>
-__device__ __forceinline__ void lds_add(uint32_t* keys, uint32_t* cnts, uint32_t key, uint32_t c,
-                                        uint32_t* table, uint32_t mask, Ctl* ctl) {
-    uint32_t h = mix32(key) & (LT - 1);
-    for (uint32_t p = 1; p <= LDS_PROBES; ++p) {
-        uint32_t cur = __hip_atomic_load(keys + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (cur == EMPTY) {
-            cur = atomicCAS(keys + h, EMPTY, key);
-            if (cur == EMPTY) cur = key;
+struct LdsTable {
+    static_assert(LT % 4 == 0 && (LT & (LT - 1)) == 0, "LT: power of two, buckets of 4");
+    static constexpr uint32_t NB = LT / 4;
+    alignas(16) uint32_t keys[LT];
+    uint32_t cnts[LT];
+    uint32_t used;  // claimed slots
+    uint32_t qn;    // queued keys
+
+    // every thread of the block; a barrier must follow before use
+    __device__ __forceinline__ void clear(int tpb) {
+        for (int i = threadIdx.x; i < LT; i += tpb) {
+            keys[i] = EMPTY;
+            cnts[i] = 0u;
         }
-        if (cur == key) {
-            atomicAdd(cnts + h, c);
-            return;
-        }
-        h = (h + p) & (LT - 1);
-    }
-    global_add(table, mask, key, c, ctl);
-}
-
-template <int TPB, int LT>
-__device__ __forceinline__ void lds_table_clear(uint32_t* keys, uint32_t* cnts) {
-    for (int i = threadIdx.x; i < LT; i += TPB) {
-        keys[i] = EMPTY;
-        cnts[i] = 0u;
-    }
-}
-
-template <int TPB, int LT>
-__device__ __forceinline__ void lds_table_flush(const uint32_t* keys, const uint32_t* cnts,
-                                                uint32_t* table, uint32_t mask, Ctl* ctl) {
-    for (int i = threadIdx.x; i < LT; i += TPB) {
-        uint32_t k = keys[i];
-        if (k != EMPTY) global_add(table, mask, k, cnts[i], ctl);
-    }
-}
-
-// Run-length pre-aggregation of one thread's counted pairs before the LDS
-// table: consecutive equal keys (long runs of one byte) become one add.
-template <int LT>
-struct PairCounter {
-    uint32_t key = EMPTY;
-    uint32_t cnt = 0;
-    __device__ __forceinline__ void add(uint32_t k, uint32_t* keys, uint32_t* cnts, uint32_t* table,
-                                        uint32_t mask, Ctl* ctl) {
-        if (k == key) {
-            ++cnt;
-        } else {
-            if (cnt) lds_add<LT>(keys, cnts, key, cnt, table, mask, ctl);
-            key = k;
-            cnt = 1;
+        if (threadIdx.x == 0) {
+            used = 0u;
+            qn = 0u;
         }
     }
-    __device__ __forceinline__ void finish(uint32_t* keys, uint32_t* cnts, uint32_t* table,
-                                           uint32_t mask, Ctl* ctl) {
-        if (cnt) lds_add<LT>(keys, cnts, key, cnt, table, mask, ctl);
-        cnt = 0;
-        key = EMPTY;
+
+    // full insert: home bucket, then further buckets, then the global table
+    __device__ __forceinline__ void insert(uint32_t key, uint32_t c, uint32_t* table, uint32_t mask, Ctl* ctl) {
+        uint32_t b = mix32(key) & (NB - 1);
+        for (uint32_t p = 1; p <= LDS_PROBES; ++p) {
+            for (uint32_t s = 0; s < 4; ++s) {
+                uint32_t* slot = keys + 4 * b + s;
+                uint32_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (cur == EMPTY) {
+                    cur = atomicCAS(slot, EMPTY, key);
+                    if (cur == EMPTY) {
+                        atomicAdd(&used, 1u);
+                        cur = key;
+                    }
+                }
+                if (cur == key) {
+                    atomicAdd(cnts + 4 * b + s, c);
+                    return;
+                }
+            }
+            b = (b + p) & (NB - 1);
+        }
+        global_add(table, mask, key, c, ctl);
+    }
+
+    // Count one per non-EMPTY key k[j]. A set bit j of fold means key j
+    // equals the next non-EMPTY key, whose add carries it (a run of one key
+    // costs one add). qk/qc: LDS scratch of qcap >= 8 * tpb entries each.
+    // Every thread of the block calls this (it contains barriers).
+    template <int V>
+    __device__ __forceinline__ void count(const uint32_t (&k)[V], uint32_t fold, uint32_t* qk, uint32_t* qc,
+                                          uint32_t qcap, int tpb, uint32_t* table, uint32_t mask, Ctl* ctl) {
+        constexpr int G = 4;  // keys probed together (one 16-byte LDS load each)
+        static_assert(V % (2 * G) == 0, "keys come in groups of 8");
+        uint32_t carry = 0;
+#pragma unroll
+        for (int g = 0; g < V; g += G) {
+            uint32_t bk[G];
+            uint4 kv[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) bk[j] = mix32(k[g + j]) & (NB - 1);
+#pragma unroll
+            for (int j = 0; j < G; ++j) kv[j] = reinterpret_cast<const uint4*>(keys)[bk[j]];
+            uint32_t miss = 0, cnt[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                cnt[j] = 0;
+                const uint32_t key = k[g + j];
+                if (key != EMPTY) {
+                    if ((fold >> (g + j)) & 1u) {
+                        ++carry;
+                    } else {
+                        cnt[j] = carry + 1;
+                        carry = 0;
+                        const uint32_t s = kv[j].x == key ? 0u : kv[j].y == key ? 1u : kv[j].z == key ? 2u
+                                         : kv[j].w == key ? 3u : 4u;
+                        if (s < 4u) atomicAdd(cnts + 4 * bk[j] + s, cnt[j]);
+                        else miss |= 1u << j;
+                    }
+                }
+            }
+            if (miss) {
+                uint32_t q = atomicAdd(&qn, (uint32_t)__popc(miss));
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if ((miss >> j) & 1u) {
+                        if (q < qcap) {
+                            qk[q] = k[g + j];
+                            qc[q] = cnt[j];
+                        } else {
+                            global_add(table, mask, k[g + j], cnt[j], ctl);
+                        }
+                        ++q;
+                    }
+                }
+            }
+            if ((g / G) % 2 == 0) continue;  // drain after every 8 keys per thread
+            __syncthreads();
+            const uint32_t nq = min(qn, qcap);
+            if (nq) {  // uniform: read after the barrier
+                for (uint32_t i = threadIdx.x; i < nq; i += tpb) insert(qk[i], qc[i], table, mask, ctl);
+                __syncthreads();
+                if (threadIdx.x == 0) qn = 0u;
+                __syncthreads();
+            }
+        }
+    }
+
+    // every thread of the block
+    __device__ __forceinline__ void flush(int tpb, uint32_t* table, uint32_t mask, Ctl* ctl) {
+        for (int i = threadIdx.x; i < LT; i += tpb) {
+            const uint32_t key = keys[i];
+            if (key != EMPTY) global_add(table, mask, key, cnts[i], ctl);
+        }
+    }
+
+    // every thread of the block, after a barrier that follows the last count
+    __device__ __forceinline__ void flush_if_half_full(int tpb, uint32_t* table, uint32_t mask, Ctl* ctl) {
+        if (2u * used > (uint32_t)LT) {
+            flush(tpb, table, mask, ctl);
+            __syncthreads();
+            clear(tpb);
+            __syncthreads();
+        }
     }
 };
 
@@ -194,21 +271,25 @@ __global__ void k_fill64(unsigned long long* p, size_t count, unsigned long long
 }
 
 // ---------------------------------------------------------------- tag + count (iteration 0)
-// Each thread step covers 16 consecutive bytes: one 16-byte load when the
-// input is aligned, four 16-byte stores of symbols.
+// Blocks take chunks of TPB * 16 bytes in turn; a thread covers 16
+// consecutive bytes (one 16-byte load when the input is aligned, four
+// 16-byte stores of symbols). The chunk loop is uniform over the block so
+// that the LDS table can be flushed between chunks.
 
 template <int TPB, int LT>
 __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ bytes, uint32_t n,
                                                    uint32_t* __restrict__ sym, uint32_t* table,
                                                    uint32_t mask, Ctl* ctl) {
-    __shared__ uint32_t s_keys[LT];
-    __shared__ uint32_t s_cnts[LT];
-    lds_table_clear<TPB, LT>(s_keys, s_cnts);
+    constexpr uint32_t CHUNK = TPB * 16;
+    constexpr uint32_t QCAP = TPB * 8;
+    __shared__ LdsTable<LT> tab;
+    __shared__ uint32_t s_qk[QCAP], s_qc[QCAP];
+    tab.clear(TPB);
     __syncthreads();
-    PairCounter<LT> pc;
     const bool aligned = ((uintptr_t)bytes & 15u) == 0;
-    const size_t stride = (size_t)gridDim.x * TPB * 16;
-    for (size_t base = ((size_t)blockIdx.x * TPB + threadIdx.x) * 16; base < n; base += stride) {
+    const uint32_t nchunks = (n + CHUNK - 1) / CHUNK;
+    for (uint32_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+        const size_t base = (size_t)ch * CHUNK + threadIdx.x * 16;
         uint32_t b[16];
         if (aligned && base + 16 <= n) {
             uint4 v = *reinterpret_cast<const uint4*>(bytes + base);
@@ -219,7 +300,7 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
 #pragma unroll
             for (int j = 0; j < 16; ++j) b[j] = (base + j < n) ? bytes[base + j] : 0u;
         }
-        uint32_t prev = base ? bytes[base - 1] : 0u;
+        const uint32_t prev = (base && base - 1 < n) ? bytes[base - 1] : 0u;
         uint32_t pcls = byte_class(prev);
         uint32_t s[16];
 #pragma unroll
@@ -237,16 +318,26 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
             for (int j = 0; j < 16; ++j)
                 if (base + j < n) sym[base + j] = s[j];
         }
-        uint32_t left = prev;
+        // pairs whose right symbol starts no word; equal keys folded into one add
+        uint32_t keys[16];
+        uint32_t fold = 0, lastkey = EMPTY, prevj = 0, left = prev;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (base + j < n && !(s[j] & WS)) pc.add(pair_key(left, b[j]), s_keys, s_cnts, table, mask, ctl);
+            keys[j] = EMPTY;
+            if (base + j < n && !(s[j] & WS)) {
+                const uint32_t key = pair_key(left, b[j]);
+                if (key == lastkey) fold |= 1u << prevj;
+                lastkey = key;
+                keys[j] = key;
+                prevj = j;
+            }
             left = b[j];
         }
+        tab.template count<16>(keys, fold, s_qk, s_qc, QCAP, TPB, table, mask, ctl);
+        tab.flush_if_half_full(TPB, table, mask, ctl);
     }
-    pc.finish(s_keys, s_cnts, table, mask, ctl);
     __syncthreads();
-    lds_table_flush<TPB, LT>(s_keys, s_cnts, table, mask, ctl);
+    tab.flush(TPB, table, mask, ctl);
 }
 
 // ---------------------------------------------------------------- find max
@@ -275,20 +366,30 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, uint32_t* table, uin
     const uint32_t limit = ld_relaxed(&ctl->limit);
     if (done || k != m || k >= limit) return;  // uniform over the grid
 
+    // four 16-byte loads (eight slots) in flight per thread per round
     unsigned long long best = 0ull;
     uint4* t4 = reinterpret_cast<uint4*>(table);
     const uint32_t n4 = n_slots / 2;
-    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < n4; i += gridDim.x * TPB) {
-        uint4 v = t4[i];
-        if (v.x != EMPTY) {
-            unsigned long long p = ((unsigned long long)v.y << 32) | (uint32_t)~v.x;
-            best = p > best ? p : best;
+    constexpr uint32_t U = 4;
+    for (uint32_t i0 = blockIdx.x * TPB * U + threadIdx.x; i0 < n4; i0 += gridDim.x * TPB * U) {
+        uint4 v[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t i = i0 + u * TPB;
+            v[u] = (i < n4) ? t4[i] : make_uint4(EMPTY, 0u, EMPTY, 0u);
         }
-        if (v.z != EMPTY) {
-            unsigned long long p = ((unsigned long long)v.w << 32) | (uint32_t)~v.z;
-            best = p > best ? p : best;
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            if (v[u].x != EMPTY) {
+                const unsigned long long p = ((unsigned long long)v[u].y << 32) | (uint32_t)~v[u].x;
+                best = p > best ? p : best;
+            }
+            if (v[u].z != EMPTY) {
+                const unsigned long long p = ((unsigned long long)v[u].w << 32) | (uint32_t)~v[u].z;
+                best = p > best ? p : best;
+            }
+            if (v[u].x != EMPTY || v[u].z != EMPTY) t4[i0 + u * TPB] = make_uint4(EMPTY, 0u, EMPTY, 0u);
         }
-        if (v.x != EMPTY || v.z != EMPTY) t4[i] = make_uint4(EMPTY, 0u, EMPTY, 0u);
     }
     best = wave_max_u64(best);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -323,285 +424,6 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, uint32_t* table, uin
         ctl->best = 0ull;
         ctl->sweep_done = 0u;
     }
-}
-
-// ---------------------------------------------------------------- merge + compact + count
-//
-// Selection: an occurrence at position i (right symbol of the pair) is
-//   occ_i = no tag on s_i, id(s_{i-1}) == L, id(s_i) == R
-// and the left-to-right scan merges it iff sel_i = occ_i and not sel_{i-1}.
-// A segment's effect on this recurrence and on the number of symbols it
-// keeps is the 4-tuple below, composed associatively across lanes, waves
-// and tiles:
-//   c0  symbols kept when the segment is entered with sel = 0
-//   d   extra symbol kept when entered with sel = 1 (0 or 1: only the
-//       leading chain of occurrences depends on the entry state)
-//   o0, o1  sel of the segment's last position for entry sel = 0 / 1
-// Packed into 32 bits: c0 in bits 0-23, d bit 24, o0 bit 25, o1 bit 26.
-
-__device__ __forceinline__ uint32_t tup_make(uint32_t c0, uint32_t d, uint32_t o0, uint32_t o1) {
-    return c0 | (d << 24) | (o0 << 25) | (o1 << 26);
-}
-constexpr uint32_t TUP_ID = 1u << 26;  // empty segment: keeps nothing, passes sel through
-
-// segment a followed by segment b
-__device__ __forceinline__ uint32_t tup_then(uint32_t a, uint32_t b) {
-    const uint32_t ac0 = a & 0xFFFFFFu, ad = (a >> 24) & 1u, ao0 = (a >> 25) & 1u, ao1 = (a >> 26) & 1u;
-    const uint32_t bc0 = b & 0xFFFFFFu, bd = (b >> 24) & 1u, bo0 = (b >> 25) & 1u, bo1 = (b >> 26) & 1u;
-    const uint32_t c0 = ac0 + bc0 + (ao0 & bd);
-    const uint32_t c1 = ac0 + ad + bc0 + (ao1 & bd);
-    const uint32_t o0 = ao0 ? bo1 : bo0;
-    const uint32_t o1 = ao1 ? bo1 : bo0;
-    return tup_make(c0, c1 - c0, o0, o1);
-}
-
-// Tile status words for the look-back: flag (bits 62-63: 1 aggregate,
-// 2 inclusive prefix), epoch = iteration + 1 (bits 32-61), payload (bits 0-31:
-// a tuple for an aggregate; kept-count | sel << 31 for a prefix). Stale words
-// of earlier iterations carry another epoch, so nothing is reset in between.
-constexpr unsigned long long ST_AGG = 1ull << 62;
-constexpr unsigned long long ST_PRE = 2ull << 62;
-
-__device__ __forceinline__ unsigned long long st_pack(unsigned long long flag, uint32_t epoch, uint32_t payload) {
-    return flag | ((unsigned long long)epoch << 32) | payload;
-}
-
-__device__ __forceinline__ void st_store(unsigned long long* p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned long long st_load(const unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave 0 of a tile's workgroup: find the exclusive prefix (kept symbols
-// before the tile, sel of the position before it) from the predecessors'
-// status words, 64 tiles per round.
-__device__ __forceinline__ void lookback(const unsigned long long* status, uint32_t t, uint32_t epoch,
-                                         uint32_t lane, Ctl* ctl, uint32_t& off, uint32_t& sel) {
-    // tiles already passed (those closest to t), unpacked: the kept count can
-    // exceed the 24 bits of a packed tuple when the prefix lies far back
-    uint32_t acc_c0 = 0, acc_d = 0, acc_o0 = 0, acc_o1 = 1;
-    long long j = (long long)t - 1;
-    uint32_t spins = 0;
-    for (;;) {
-        const long long idx = j - (long long)lane;
-        unsigned long long st = (idx >= 0) ? st_load(status + idx) : st_pack(ST_PRE, epoch, 0u);
-        int p;
-        for (;;) {
-            const bool valid = (st >> 62) != 0ull && (uint32_t)((st >> 32) & 0x3FFFFFFFull) == epoch;
-            const unsigned long long pm = __ballot(valid && (st >> 62) == 2ull);
-            const unsigned long long vm = __ballot(valid);
-            p = pm ? (__ffsll((long long)pm) - 1) : 64;
-            const unsigned long long need = (p >= 63) ? ~0ull : ((2ull << p) - 1ull);
-            if ((vm & need) == need) break;
-            if (++spins > SPIN_LIMIT) {  // bounded wait: report and carry on
-                if (lane == 0) {
-                    atomicOr(&ctl->err, ERR_SPIN);
-                    atomicExch(&ctl->done, 1u);
-                }
-                off = 0;
-                sel = 0;
-                return;
-            }
-            if (!valid && idx >= 0) st = st_load(status + idx);
-        }
-        // compose the aggregates of lanes [0, p): lane 63 holds the lowest tile
-        uint32_t a = (lane < (uint32_t)p) ? (uint32_t)(st & 0xFFFFFFFFull) : TUP_ID;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            uint32_t other = __shfl_down(a, o);
-            if (lane + o < 64) a = tup_then(other, a);
-        }
-        a = __shfl(a, 0);
-        {   // acc = (window a, then acc)
-            const uint32_t ac0 = a & 0xFFFFFFu, ad = (a >> 24) & 1u, ao0 = (a >> 25) & 1u, ao1 = (a >> 26) & 1u;
-            const uint32_t c0 = ac0 + acc_c0 + (ao0 & acc_d);
-            const uint32_t c1 = ac0 + ad + acc_c0 + (ao1 & acc_d);
-            const uint32_t o0 = ao0 ? acc_o1 : acc_o0;
-            const uint32_t o1 = ao1 ? acc_o1 : acc_o0;
-            acc_c0 = c0; acc_d = c1 - c0; acc_o0 = o0; acc_o1 = o1;
-        }
-        if (p < 64) {
-            const uint32_t pay = __shfl((uint32_t)(st & 0xFFFFFFFFull), p);
-            const uint32_t base = pay & 0x7FFFFFFFu, bsel = pay >> 31;
-            off = base + acc_c0 + (bsel ? acc_d : 0u);
-            sel = bsel ? acc_o1 : acc_o0;
-            return;
-        }
-        j -= 64;
-    }
-}
-
-// LDS index skew for the staged output (spreads thread-contiguous runs over banks)
-__device__ __forceinline__ uint32_t skew(uint32_t i) { return i + (i >> 5); }
-
-template <int TPB, int V, int LT>
-__global__ __launch_bounds__(TPB) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
-                                               uint32_t* __restrict__ buf1, uint32_t* table,
-                                               uint32_t mask, unsigned long long* status,
-                                               uint32_t* lengths) {
-    constexpr int TILE = TPB * V;
-    constexpr int NW = TPB / 64;
-    static_assert(V == 16, "a thread owns 16 symbols (four 16-byte loads)");
-    __shared__ uint32_t s_keys[LT];
-    __shared__ uint32_t s_cnts[LT];
-    __shared__ uint32_t s_stage[TILE + TILE / 32];
-    __shared__ uint32_t s_wagg[NW];
-    __shared__ uint32_t s_tile, s_off, s_sel;
-
-    const uint32_t k = ld_relaxed(&ctl->k);
-    const uint32_t it = ld_relaxed(&ctl->m);
-    if (it >= k) return;  // no merge pending (uniform)
-    const uint32_t L = ctl->L, R = ctl->R, X = ctl->X;
-    const uint32_t n = ctl->n[it & 1u];
-    const uint32_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
-    uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
-    const uint32_t ntiles = (n + TILE - 1) / TILE;
-    const uint32_t epoch = it + 1;
-    const bool do_count = X != IDM;  // the last possible id: nothing can follow
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
-
-    lds_table_clear<TPB, LT>(s_keys, s_cnts);
-    PairCounter<LT> pc;
-
-    for (;;) {
-        if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr, 1u);
-        __syncthreads();
-        const uint32_t t = s_tile;
-        if (t >= ntiles) break;
-        const uint32_t g0 = t * TILE + tid * V;
-
-        // ---- load 16 symbols plus two on the left and one on the right
-        uint32_t x[V];
-        if (g0 + V <= n) {
-            const uint4* p4 = reinterpret_cast<const uint4*>(in + g0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint4 v = p4[q];
-                x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < V; ++j) x[j] = (g0 + j < n) ? in[g0 + j] : WS;
-        }
-        const uint32_t a1 = (g0 >= 1 && g0 - 1 < n) ? in[g0 - 1] : WS;
-        const uint32_t a2 = (g0 >= 2 && g0 - 2 < n) ? in[g0 - 2] : WS;
-        const uint32_t b1 = (g0 + V < n) ? in[g0 + V] : WS;
-
-        // ---- occurrences (bit j: position g0 + j; bit V: position g0 + V)
-        uint32_t occ = 0, valid = 0;
-        {
-            uint32_t prev = a1;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const bool v = g0 + j < n;
-                const bool o = v && (g0 + j >= 1) && !(x[j] & WS) && (prev & IDM) == L && (x[j] & IDM) == R;
-                occ |= (uint32_t)o << j;
-                valid |= (uint32_t)v << j;
-                prev = x[j];
-            }
-            const bool oV = (g0 + V < n) && !(b1 & WS) && (x[V - 1] & IDM) == L && (b1 & IDM) == R;
-            occ |= (uint32_t)oV << V;
-        }
-
-        // ---- this thread's tuple
-        uint32_t tup;
-        {
-            uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const uint32_t o = (occ >> j) & 1u, v = (valid >> j) & 1u;
-                s0 = o & ~s0 & 1u;
-                s1 = o & ~s1 & 1u;
-                c0 += v & ~s0 & 1u;
-                c1 += v & ~s1 & 1u;
-            }
-            tup = tup_make(c0, c1 - c0, s0, s1);
-        }
-
-        // ---- inclusive scan over the wave, then over waves
-        uint32_t incl = tup;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            uint32_t u = __shfl_up(incl, o);
-            if (lane >= (uint32_t)o) incl = tup_then(u, incl);
-        }
-        uint32_t lane_excl = __shfl_up(incl, 1);
-        if (lane == 0) lane_excl = TUP_ID;
-        if (lane == 63) s_wagg[w] = incl;
-        __syncthreads();
-        uint32_t wave_excl = TUP_ID, tile_agg = TUP_ID;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            if (i == (int)w) wave_excl = tile_agg;
-            tile_agg = tup_then(tile_agg, s_wagg[i]);
-        }
-
-        // ---- decoupled look-back (wave 0)
-        if (w == 0) {
-            uint32_t off = 0, sel = 0;
-            if (t == 0) {
-                // nothing before tile 0
-            } else {
-                if (lane == 0) st_store(status + t, st_pack(ST_AGG, epoch, tile_agg));
-                lookback(status, t, epoch, lane, ctl, off, sel);
-            }
-            if (lane == 0) {
-                const uint32_t kept = (tile_agg & 0xFFFFFFu) + (sel ? ((tile_agg >> 24) & 1u) : 0u);
-                const uint32_t osel = sel ? ((tile_agg >> 26) & 1u) : ((tile_agg >> 25) & 1u);
-                st_store(status + t, st_pack(ST_PRE, epoch, (off + kept) | (osel << 31)));
-                s_off = off;
-                s_sel = sel;
-            }
-        }
-        __syncthreads();
-        const uint32_t tile_off = s_off, tile_sel = s_sel;
-        const uint32_t texcl = tup_then(wave_excl, lane_excl);
-        const uint32_t my_local = (texcl & 0xFFFFFFu) + (tile_sel ? ((texcl >> 24) & 1u) : 0u);
-        const uint32_t sel_in = tile_sel ? ((texcl >> 26) & 1u) : ((texcl >> 25) & 1u);
-        const uint32_t tile_kept = (tile_agg & 0xFFFFFFu) + (tile_sel ? ((tile_agg >> 24) & 1u) : 0u);
-
-        // ---- resolve sel for real, emit kept symbols to LDS, count new pairs
-        uint32_t selbits = 0;
-        {
-            uint32_t s = sel_in;
-#pragma unroll
-            for (int j = 0; j <= V; ++j) {
-                s = (occ >> j) & ~s & 1u;
-                selbits |= s << j;
-            }
-        }
-        uint32_t prevval;
-        if (sel_in) prevval = X | (a2 & WS);              // g0-1 merged into g0-2
-        else prevval = (selbits & 1u) ? (X | (a1 & WS)) : a1;
-        uint32_t o = my_local;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            if (((valid >> j) & 1u) && !((selbits >> j) & 1u)) {
-                const uint32_t v = ((selbits >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
-                s_stage[skew(o)] = v;
-                ++o;
-                if (do_count && !(v & WS)) pc.add(pair_key(prevval, v), s_keys, s_cnts, table, mask, ctl);
-                prevval = v;
-            }
-        }
-        pc.finish(s_keys, s_cnts, table, mask, ctl);
-        __syncthreads();
-
-        // ---- coalesced write of the tile's kept symbols
-        for (uint32_t i = tid; i < tile_kept; i += TPB) out[tile_off + i] = s_stage[skew(i)];
-        if (t == ntiles - 1 && tid == 0) {
-            const uint32_t total = tile_off + tile_kept;
-            ctl->n[(it + 1) & 1u] = total;
-            lengths[it + 1] = total;
-            __threadfence();
-            atomicExch(&ctl->m, it + 1);
-        }
-        __syncthreads();
-    }
-    __syncthreads();
-    lds_table_flush<TPB, LT>(s_keys, s_cnts, table, mask, ctl);
 }
 
 }  // namespace bpek

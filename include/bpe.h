@@ -148,9 +148,14 @@ typedef struct {
     uint32_t merges_done;    /* merges produced by the state after the run           */
 } bpe_profile_result;
 
-/* Like bpe_run followed by bpe_sync, but with a HIP event around every kernel
-   launch on the state's stream, to time each kernel separately. */
-bpe_status bpe_profile(bpe_state *s, uint32_t n_merges, bpe_profile_result *out);
+/* Like bpe_run followed by bpe_sync, but with a HIP event recorded on the
+   state's stream between consecutive kernel launches, to time each kernel.
+   find_ms / merge_ms (host, n_merges entries each, or NULL) receive the
+   per-iteration times; iterations after training stopped take ~0 ms. One
+   host wait at the end, as in bpe_run + bpe_sync. The events are created
+   once per device and kept until the process ends. */
+bpe_status bpe_profile(bpe_state *s, uint32_t n_merges, bpe_profile_result *out, float *find_ms,
+                       float *merge_ms);
 
 /* Release the state and everything it owns (not a caller workspace). NULL is a no-op. */
 void bpe_free(bpe_state *s);
