@@ -46,6 +46,8 @@ def main() -> int:
     ap.add_argument("--merges", type=int, default=None, help="override the merge count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="write per-iteration details to this JSON file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -59,6 +61,16 @@ def main() -> int:
 
     import bpe_merge_amd as bpe
     import corpus
+
+    if args.copy_calibration:
+        nb = args.copy_calibration // 16 * 16
+        src = torch.ones(nb // 4, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read + %d bytes written per copy, 2 copies" % (nb, nb))
+        del src, dst
 
     spec = corpus.CONFIGS[args.config]
     if args.merges is not None:

@@ -17,6 +17,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/bpe.h"
@@ -33,7 +34,9 @@ constexpr int MERGE_LT = 4096;             // LDS pair-table slots per workgroup
 constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
-constexpr int FIND_TPB = 256;
+constexpr int SEL_TPB = 1024;
+constexpr int SEL_LT = 16384;              // LDS slots of the select stage, per partition
+constexpr size_t MAX_GRID = 2048;          // bound on workgroups of the counting kernels
 
 thread_local std::string g_err;
 
@@ -69,12 +72,25 @@ uint32_t table_log2_for(size_t n, const bpe_config* cfg) {
     return std::min<uint32_t>(22, std::max<uint32_t>(12, l));
 }
 
+// Workgroups of the counting kernels (merge and tag passes): enough to fill
+// the chip, never more than there are tiles to hand out.
+size_t grid_bound(size_t n) { return std::min(MAX_GRID, (n + TILE - 1) / TILE + 1); }
+
+// Select-stage LDS slots per partition for a table of 2^tlog2 slots in all.
+uint32_t sel_slots(uint32_t tlog2) {
+    const uint32_t per = tlog2 >= 8 ? (1u << (tlog2 - 8)) : 1u;  // NPART = 256
+    return std::min<uint32_t>(SEL_LT, std::max<uint32_t>(64, per));
+}
+
 struct Layout {
-    size_t ctl, sym0, sym1, table, status, merges, lengths, total;
-    uint32_t max_tiles;
+    size_t ctl, sym0, sym1, pool, part_n, status, merges, lengths, total;
+    uint32_t max_tiles, pcap;
 };
 
-Layout layout_for(size_t n, uint32_t tlog2) {
+// Record pool: a pass writes at most one record per counted pair (n - 1),
+// spread by hash over the partitions; each partition gets twice its even
+// share, plus one partly used chunk per workgroup.
+Layout layout_for(size_t n) {
     Layout L{};
     size_t a = 0;
     L.ctl = a;
@@ -84,8 +100,11 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     a = align_up(a + 4 * sym_elems, 256);
     L.sym1 = a;
     a = align_up(a + 4 * sym_elems, 256);
-    L.table = a;
-    a = align_up(a + (size_t(8) << tlog2), 256);
+    L.pcap = uint32_t(align_up(2 * ((n + bpek::NPART - 1) / bpek::NPART) + (grid_bound(n) + 1) * bpek::CHUNK, 2));
+    L.pool = a;
+    a = align_up(a + 8 * size_t(L.pcap) * bpek::NPART, 256);
+    L.part_n = a;
+    a = align_up(a + 4 * size_t(bpek::NPART), 256);
     L.max_tiles = uint32_t((n + TILE - 1) / TILE) + 1;
     L.status = a;
     a = align_up(a + 8 * size_t(L.max_tiles), 256);
@@ -139,23 +158,33 @@ struct bpe_state {
     Ctl* ctl = nullptr;
     uint32_t* sym0 = nullptr;
     uint32_t* sym1 = nullptr;
-    uint32_t* table = nullptr;
+    uint2* pool_rec = nullptr;
+    uint32_t* part_n = nullptr;
     unsigned long long* status = nullptr;
     uint32_t* merges = nullptr;
     uint32_t* lengths = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
-    int merge_grid = 0, find_grid = 0, tag_grid = 0, fill_grid = 0;
+    int merge_grid = 0, tag_grid = 0, fill_grid = 0;
     bool poisoned = false;   // a device error was seen
+
+    bpek::Pool pool() const { return bpek::Pool{pool_rec, part_n, lay.pcap}; }
 };
 
 namespace {
 
+void launch_select(bpe_state* s) {
+    hipLaunchKernelGGL((bpek::k_select<SEL_TPB, SEL_LT>), dim3(bpek::NPART), dim3(SEL_TPB), 0, s->stream, s->ctl,
+                       s->pool(), sel_slots(s->tlog2), s->merges);
+}
+
+void launch_merge(bpe_state* s) {
+    hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0, s->stream,
+                       s->ctl, s->sym0, s->sym1, s->pool(), s->status, s->lengths);
+}
+
 bpe_status launch_iteration(bpe_state* s) {
-    const uint32_t T = 1u << s->tlog2;
-    hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
-                       s->ctl, s->table, T, s->merges);
-    hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB),
-                       0, s->stream, s->ctl, s->sym0, s->sym1, s->table, T - 1, s->status, s->lengths);
+    launch_select(s);
+    launch_merge(s);
     return BPE_OK;
 }
 
@@ -165,7 +194,7 @@ bpe_status read_ctl(bpe_state* s, Ctl* h) {
     if (h->err) {
         s->poisoned = true;
         if (h->err & bpek::ERR_TABLE) {
-            set_err("the global pair table (2^%u slots) overflowed; use a larger table_log2", s->tlog2);
+            set_err("pair counting ran out of record space (%u records per partition)", s->lay.pcap);
             return BPE_ETABLE;
         }
         set_err("device error bits 0x%x", h->err);
@@ -211,7 +240,7 @@ extern "C" {
 
 size_t bpe_workspace_bytes(size_t n, const bpe_config* cfg) {
     if (!config_ok(n, cfg)) return 0;
-    return layout_for(n, table_log2_for(n, cfg)).total;
+    return layout_for(n).total;
 }
 
 const char* bpe_strerror(bpe_status st) {
@@ -219,7 +248,7 @@ const char* bpe_strerror(bpe_status st) {
         case BPE_OK: return "ok";
         case BPE_DONE: return "no countable pair is left";
         case BPE_EINVAL: return "invalid argument";
-        case BPE_ETABLE: return "global pair table overflow";
+        case BPE_ETABLE: return "pair counting capacity (table) exceeded";
         case BPE_EIDSPACE: return "merge count exceeds the 16-bit id space";
         case BPE_ENOMEM: return "out of memory";
         case BPE_EHIP: return "HIP runtime error";
@@ -243,7 +272,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     }
     if (!config_ok(n, cfg)) return BPE_EINVAL;
     const uint32_t tlog2 = table_log2_for(n, cfg);
-    const Layout lay = layout_for(n, tlog2);
+    const Layout lay = layout_for(n);
     if (cfg && cfg->workspace && cfg->workspace_bytes < lay.total) {
         set_err("workspace of %zu bytes is smaller than the %zu bytes needed", cfg->workspace_bytes, lay.total);
         return BPE_EINVAL;
@@ -297,7 +326,8 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->ctl = reinterpret_cast<Ctl*>(base + lay.ctl);
     s->sym0 = reinterpret_cast<uint32_t*>(base + lay.sym0);
     s->sym1 = reinterpret_cast<uint32_t*>(base + lay.sym1);
-    s->table = reinterpret_cast<uint32_t*>(base + lay.table);
+    s->pool_rec = reinterpret_cast<uint2*>(base + lay.pool);
+    s->part_n = reinterpret_cast<uint32_t*>(base + lay.part_n);
     s->status = reinterpret_cast<unsigned long long*>(base + lay.status);
     s->merges = reinterpret_cast<uint32_t*>(base + lay.merges);
     s->lengths = reinterpret_cast<uint32_t*>(base + lay.lengths);
@@ -312,11 +342,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB, MERGE_LT>,
                                                      MERGE_TPB, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    s->merge_grid = cus * per_cu;
-    s->tag_grid = cus * 2;
-    const uint32_t T = 1u << tlog2;
-    // the sweep covers 4 x 16 bytes (8 slots) per thread per round
-    s->find_grid = int(std::min<size_t>(size_t(cus) * 4, std::max<size_t>(1, (T / 8 + FIND_TPB - 1) / FIND_TPB)));
+    // the record pool was sized for at most grid_bound(n) workgroups
+    s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, grid_bound(n)));
+    s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, grid_bound(n)));
     s->fill_grid = cus * 4;
 
     // input bytes: device memory is read in place, host memory is uploaded
@@ -331,12 +359,11 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         src = reinterpret_cast<const uint8_t*>(s->sym1);
     }
     hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
-    hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream,
-                       reinterpret_cast<unsigned long long*>(s->table), size_t(T), ~0ull >> 32);
+    hipLaunchKernelGGL(bpek::k_fill32, dim3(1), dim3(256), 0, s->stream, s->part_n, size_t(bpek::NPART), 0u);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->status,
                        size_t(lay.max_tiles), 0ull);
     hipLaunchKernelGGL((bpek::k_tag_count<TAG_TPB, TAG_LT>), dim3(s->tag_grid), dim3(TAG_TPB), 0, s->stream,
-                       src, uint32_t(n), s->sym0, s->table, T - 1, s->ctl);
+                       src, uint32_t(n), s->sym0, s->pool(), s->ctl);
     e = hipGetLastError();
     if (e != hipSuccess) {
         set_err("kernel launch failed: %s", hipGetErrorString(e));
@@ -478,14 +505,24 @@ bpe_status bpe_pair_counts(bpe_state* s, uint32_t* keys, uint32_t* counts, size_
     Ctl h;
     bpe_status st = read_ctl(s, &h);
     if (st != BPE_OK) return st;
-    const size_t T = size_t(1) << s->tlog2;
-    std::vector<uint32_t> tab(2 * T);
-    HIP_TRY(hipMemcpy(tab.data(), s->table, 8 * T, hipMemcpyDeviceToHost));
+    // the pending partial counts: every reserved record of every partition
+    std::vector<uint32_t> pn(bpek::NPART);
+    HIP_TRY(hipMemcpy(pn.data(), s->part_n, 4 * pn.size(), hipMemcpyDeviceToHost));
+    std::unordered_map<uint32_t, uint64_t> sum;
+    std::vector<uint2> rec;
+    for (uint32_t p = 0; p < bpek::NPART; ++p) {
+        const uint32_t cnt = std::min(pn[p], s->lay.pcap);
+        rec.resize(cnt);
+        if (cnt)
+            HIP_TRY(hipMemcpy(rec.data(), s->pool_rec + size_t(p) * s->lay.pcap, 8 * size_t(cnt),
+                              hipMemcpyDeviceToHost));
+        for (const uint2& r : rec)
+            if (r.x != bpek::EMPTY) sum[r.x] += r.y;
+    }
     std::vector<uint32_t> k, c;
-    for (size_t i = 0; i < T; ++i) {
-        if (tab[2 * i] == bpek::EMPTY) continue;
-        k.push_back(tab[2 * i]);
-        c.push_back(tab[2 * i + 1]);
+    for (const auto& kv : sum) {
+        k.push_back(kv.first);
+        c.push_back(uint32_t(kv.second));
     }
     if (n_out) *n_out = k.size();
     if (cap == 0) return BPE_OK;
@@ -518,15 +555,12 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res,
     if (st != BPE_OK) return st;
     st = enqueue_run(s, n_merges);
     if (st != BPE_OK) return st;
-    const uint32_t T = 1u << s->tlog2;
     std::vector<hipEvent_t>& e = *ev;
     HIP_TRY(hipEventRecord(e[0], s->stream));
     for (uint32_t i = 0; i < n_merges; ++i) {
-        hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream, s->ctl,
-                           s->table, T, s->merges);
+        launch_select(s);
         HIP_TRY(hipEventRecord(e[2 * size_t(i) + 1], s->stream));
-        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0,
-                           s->stream, s->ctl, s->sym0, s->sym1, s->table, T - 1, s->status, s->lengths);
+        launch_merge(s);
         HIP_TRY(hipEventRecord(e[2 * size_t(i) + 2], s->stream));
     }
     HIP_TRY(hipGetLastError());

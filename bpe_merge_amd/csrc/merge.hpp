@@ -8,7 +8,7 @@
 //   2. compacts the symbol array with an exclusive prefix scan of the kept
 //      flags ("Ne Yapar? 3"), carrying WORD_START_BIT on merged symbols,
 //   3. counts the adjacent pairs of the new sequence into an LDS hash table
-//      flushed into the global table ("Ne Yapar? 2"), which are the counts
+//      flushed as partial-count records ("Ne Yapar? 2"), the counts
 //      the next iteration's maximum is taken over.
 // The page runs these as separate dispatches with a three-pass scan; here
 // the scan is a single-pass decoupled look-back over 8192-symbol tiles, so
@@ -169,8 +169,8 @@ __device__ __forceinline__ uint32_t skew(uint32_t i) { return i + (i >> 5); }
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
-                                               uint32_t* __restrict__ buf1, uint32_t* table,
-                                               uint32_t mask, unsigned long long* status,
+                                               uint32_t* __restrict__ buf1, Pool pool,
+                                               unsigned long long* status,
                                                uint32_t* lengths) {
     constexpr int V = 16;  // symbols per thread: four 16-byte loads
     constexpr int TILE = TPB * V;
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     constexpr uint32_t QCAP = 8 * TPB;  // queued keys per group of 8 keys per thread
     static_assert(2 * QCAP <= TILE + TILE / 32, "the miss queue fits in the staging buffer");
     __shared__ LdsTable<LT> tab;
+    __shared__ Emitter em;
     __shared__ uint32_t s_stage[TILE + TILE / 32];
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile, s_off, s_sel;
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
 
     tab.clear(TPB);
+    em.init(TPB);
 
     for (;;) {
         if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr, 1u);
@@ -349,11 +351,13 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         }
         __syncthreads();
         // ---- count the new pairs; the staging buffer now holds the miss queue
-        tab.template count<V>(keys, fold, s_stage, s_stage + QCAP, QCAP, TPB, table, mask, ctl);
-        tab.flush_if_half_full(TPB, table, mask, ctl);
+        tab.template count<V>(keys, fold, s_stage, s_stage + QCAP, QCAP, TPB, pool, ctl);
+        flush_if_half_full(tab, em, TPB, pool, ctl);
     }
     __syncthreads();
-    tab.flush(TPB, table, mask, ctl);
+    em.flush(tab, TPB, pool, ctl);
+    __syncthreads();
+    em.pad(TPB, pool);
 }
 
 }  // namespace bpek

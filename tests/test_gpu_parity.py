@@ -171,12 +171,16 @@ def test_determinism_and_table_size_independence(bpe):
     assert np.array_equal(ref[0], om) and np.array_equal(ref[1], ot)
 
 
-def test_table_overflow_is_reported(bpe):
-    # random bytes have far more distinct countable pairs than 1024 slots
+def test_small_select_table_takes_several_passes(bpe):
+    # random bytes have far more distinct countable pairs than a 2^10-slot
+    # table (64 LDS slots per partition): the select stage sums each
+    # partition in several passes and the result must not change
     d = corpus.generate(corpus.CONFIGS[5].scaled(200_000, seed=12))
-    with pytest.raises(bpe.BpeError) as e:
-        gpu_train(bpe, d, 4, table_log2=10)
-    assert e.value.status == bpe.ETABLE
+    small = gpu_train(bpe, d, 30, table_log2=10)
+    big = gpu_train(bpe, d, 30, table_log2=22)
+    om, ot, _ = oracle.train_chunks(d, 30)
+    assert np.array_equal(small[0], om) and np.array_equal(small[1], ot)
+    assert np.array_equal(big[0], om) and np.array_equal(big[1], ot)
 
 
 def test_config1_full_with_invariants(bpe):
