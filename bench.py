@@ -10,8 +10,10 @@ library's stream (one host wait per step), which gives both the wall-clock
 value and the per-kernel times behind the roofline figures.
 
 Algorithmic bytes of iteration k (n_k symbols before it, n_{k+1} after):
-  merge kernel     4 n_k + 4 n_{k+1}   (read the symbols once, write the result once)
-  find-max kernel  16 T                (read every 8-byte table slot, reset it)
+  4 n_k + 4 n_{k+1}: the merge pass reads the symbols once and writes the
+  compacted result once. The select pass moves only partial-count records
+  (implementation overhead, timed but not credited); this design has no
+  table sweep, so no table term is added.
 """
 from __future__ import annotations
 
@@ -30,6 +32,30 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 
 def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bpe_merge_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hpp"))) + [os.path.join(csrc, "bpe.hip")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, only if it was taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    return t
 
 
 def pct(a, q):
@@ -130,21 +156,18 @@ def main() -> int:
     m_ms = m_ms[:k].astype(np.float64)
     it_s = (f_ms + m_ms) / 1e3
     merge_bytes = 4.0 * n_k + 4.0 * n_k1
-    find_bytes = np.full(k, 16.0 * T)
-    iter_bytes = merge_bytes + find_bytes
+    iter_bytes = merge_bytes
     total_wall = float(sum(wall))
     value = k * len(wall) / total_wall
     sym_per_s_agg = float(n_k.sum() / it_s.sum())
     hbm_agg = float(iter_bytes.sum() / it_s.sum() / 1e9)
     merge_gbps = float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9)
-    find_gbps = float(find_bytes.sum() / (f_ms.sum() / 1e3) / 1e9)
     per_it_sym = n_k / it_s
     per_it_gbps = iter_bytes / it_s / 1e9
-    dominant = "k_merge" if m_ms.sum() >= f_ms.sum() else "k_find_max"
-    if dominant == "k_merge":
-        achieved, avg_bytes, avg_ms = merge_gbps, float(merge_bytes.mean()), float(m_ms.mean())
-    else:
-        achieved, avg_bytes, avg_ms = find_gbps, 16.0 * T, float(f_ms.mean())
+    dominant = "k_merge"  # the merge pass takes >90% of the time (see kernels_ms_per_step)
+    achieved, avg_bytes, avg_ms = merge_gbps, float(merge_bytes.mean()), float(m_ms.mean())
+
+    traffic = measured_traffic(spec.name, dominant)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -188,17 +211,25 @@ def main() -> int:
         "hbm_gbps_per_iteration": {"aggregate": round(hbm_agg, 1), "frac_of_peak": round(hbm_agg / HBM_PEAK_GBPS, 4),
                                    "p10": round(pct(per_it_gbps, 10), 1), "p50": round(pct(per_it_gbps, 50), 1),
                                    "p90": round(pct(per_it_gbps, 90), 1)},
-        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_find_max": round(float(f_ms.sum()), 3),
-                                "k_merge_gbps": round(merge_gbps, 1), "k_find_max_gbps": round(find_gbps, 1)},
+        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_select": round(float(f_ms.sum()), 3),
+                                "k_merge_gbps": round(merge_gbps, 1)},
         "warmup_unprofiled_s": [round(x, 3) for x in warm_s],
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": (round(traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"])
+                                 if traffic else None),
+                     "traffic_detail": ({"read": round(traffic["fetch_bytes_per_launch"]),
+                                         "write": round(traffic["write_bytes_per_launch"]),
+                                         "launches": traffic["launches"],
+                                         "algorithmic_same_launches": round(traffic["algorithmic_bytes_per_launch"]),
+                                         "source": "profiles/traffic_%s_%s.json" % (dominant, spec.name)}
+                                        if traffic else None),
                      "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
     }
     if args.report:
         with open(args.report, "w") as fh:
-            json.dump({"summary": out, "lengths": lengths.tolist(), "find_ms": f_ms.tolist(),
+            json.dump({"summary": out, "lengths": lengths.tolist(), "select_ms": f_ms.tolist(),
                        "merge_ms": m_ms.tolist()}, fh)
     print(json.dumps(out), flush=True)
     return 0
