@@ -1,8 +1,9 @@
 // Host driver and C ABI of the BPE training library (include/bpe.h).
 //
 // The whole merge loop is enqueued on one stream with no host round trip
-// between iterations: each iteration is a table sweep (k_find_max) followed
-// by the fused merge/compact/count pass (k_merge); both read the iteration
+// between iterations: each iteration is a sweep of the global pair table
+// for the maximum (k_find_max) followed by the fused merge / compaction /
+// count-update pass (k_merge); both read the iteration
 // number, the merge and the sequence length from the device control block,
 // and do nothing once training has stopped. The host reads back a few bytes
 // of status at the end, then copies only the merges and tokens that exist,
@@ -17,7 +18,7 @@
 #include <mutex>
 #include <new>
 #include <string>
-#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "../../include/bpe.h"
@@ -30,13 +31,11 @@ namespace {
 
 // launch shapes
 constexpr int MERGE_TPB = 512;
-constexpr int MERGE_LT = 4096;             // LDS pair-table slots per workgroup
+constexpr int MERGE_LT = 2048;             // LDS slots for count changes, per workgroup
 constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
-constexpr int SEL_TPB = 1024;
-constexpr int SEL_LT = 16384;              // LDS slots of the select stage, per partition
-constexpr size_t MAX_GRID = 2048;          // bound on workgroups of the counting kernels
+constexpr int FIND_TPB = 256;
 
 thread_local std::string g_err;
 
@@ -72,25 +71,19 @@ uint32_t table_log2_for(size_t n, const bpe_config* cfg) {
     return std::min<uint32_t>(22, std::max<uint32_t>(12, l));
 }
 
-// Workgroups of the counting kernels (merge and tag passes): enough to fill
-// the chip, never more than there are tiles to hand out.
-size_t grid_bound(size_t n) { return std::min(MAX_GRID, (n + TILE - 1) / TILE + 1); }
+// Workgroups of the merge and tag passes: enough to fill the chip, never
+// more than there are tiles to hand out.
+size_t grid_bound(size_t n) { return (n + TILE - 1) / TILE + 1; }
 
-// Select-stage LDS slots per partition for a table of 2^tlog2 slots in all.
-uint32_t sel_slots(uint32_t tlog2) {
-    const uint32_t per = tlog2 >= 8 ? (1u << (tlog2 - 8)) : 1u;  // NPART = 256
-    return std::min<uint32_t>(SEL_LT, std::max<uint32_t>(64, per));
-}
+// The global table counts as full at 7/8 load (linear probing stays short).
+uint32_t table_limit(uint32_t tlog2) { return uint32_t((1ull << tlog2) - (1ull << tlog2) / 8); }
 
 struct Layout {
-    size_t ctl, sym0, sym1, pool, part_n, status, merges, lengths, total;
-    uint32_t max_tiles, pcap;
+    size_t ctl, sym0, sym1, table, status, merges, lengths, total;
+    uint32_t max_tiles;
 };
 
-// Record pool: a pass writes at most one record per counted pair (n - 1),
-// spread by hash over the partitions; each partition gets twice its even
-// share, plus one partly used chunk per workgroup.
-Layout layout_for(size_t n) {
+Layout layout_for(size_t n, uint32_t tlog2) {
     Layout L{};
     size_t a = 0;
     L.ctl = a;
@@ -100,11 +93,8 @@ Layout layout_for(size_t n) {
     a = align_up(a + 4 * sym_elems, 256);
     L.sym1 = a;
     a = align_up(a + 4 * sym_elems, 256);
-    L.pcap = uint32_t(align_up(2 * ((n + bpek::NPART - 1) / bpek::NPART) + (grid_bound(n) + 1) * bpek::CHUNK, 2));
-    L.pool = a;
-    a = align_up(a + 8 * size_t(L.pcap) * bpek::NPART, 256);
-    L.part_n = a;
-    a = align_up(a + 4 * size_t(bpek::NPART), 256);
+    L.table = a;
+    a = align_up(a + 8 * (size_t(1) << tlog2), 256);
     L.max_tiles = uint32_t((n + TILE - 1) / TILE) + 1;
     L.status = a;
     a = align_up(a + 8 * size_t(L.max_tiles), 256);
@@ -158,32 +148,32 @@ struct bpe_state {
     Ctl* ctl = nullptr;
     uint32_t* sym0 = nullptr;
     uint32_t* sym1 = nullptr;
-    uint2* pool_rec = nullptr;
-    uint32_t* part_n = nullptr;
+    unsigned long long* table = nullptr;
     unsigned long long* status = nullptr;
     uint32_t* merges = nullptr;
     uint32_t* lengths = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
-    int merge_grid = 0, tag_grid = 0, fill_grid = 0;
+    int merge_grid = 0, tag_grid = 0, fill_grid = 0, find_grid = 0;
     bool poisoned = false;   // a device error was seen
 
-    bpek::Pool pool() const { return bpek::Pool{pool_rec, part_n, lay.pcap}; }
+    uint32_t slots() const { return 1u << tlog2; }
+    bpek::GTable gtable() const { return bpek::GTable{table, slots() - 1u, table_limit(tlog2)}; }
 };
 
 namespace {
 
-void launch_select(bpe_state* s) {
-    hipLaunchKernelGGL((bpek::k_select<SEL_TPB, SEL_LT>), dim3(bpek::NPART), dim3(SEL_TPB), 0, s->stream, s->ctl,
-                       s->pool(), sel_slots(s->tlog2), s->merges);
+void launch_find_max(bpe_state* s) {
+    hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream, s->ctl,
+                       s->table, s->slots(), s->merges);
 }
 
 void launch_merge(bpe_state* s) {
     hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0, s->stream,
-                       s->ctl, s->sym0, s->sym1, s->pool(), s->status, s->lengths);
+                       s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths);
 }
 
 bpe_status launch_iteration(bpe_state* s) {
-    launch_select(s);
+    launch_find_max(s);
     launch_merge(s);
     return BPE_OK;
 }
@@ -194,7 +184,8 @@ bpe_status read_ctl(bpe_state* s, Ctl* h) {
     if (h->err) {
         s->poisoned = true;
         if (h->err & bpek::ERR_TABLE) {
-            set_err("pair counting ran out of record space (%u records per partition)", s->lay.pcap);
+            set_err("the global pair table is full (%u of %u slots claimed; give a larger table_log2)",
+                    table_limit(s->tlog2), s->slots());
             return BPE_ETABLE;
         }
         set_err("device error bits 0x%x", h->err);
@@ -240,7 +231,7 @@ extern "C" {
 
 size_t bpe_workspace_bytes(size_t n, const bpe_config* cfg) {
     if (!config_ok(n, cfg)) return 0;
-    return layout_for(n).total;
+    return layout_for(n, table_log2_for(n, cfg)).total;
 }
 
 const char* bpe_strerror(bpe_status st) {
@@ -248,7 +239,7 @@ const char* bpe_strerror(bpe_status st) {
         case BPE_OK: return "ok";
         case BPE_DONE: return "no countable pair is left";
         case BPE_EINVAL: return "invalid argument";
-        case BPE_ETABLE: return "pair counting capacity (table) exceeded";
+        case BPE_ETABLE: return "the global pair table is full";
         case BPE_EIDSPACE: return "merge count exceeds the 16-bit id space";
         case BPE_ENOMEM: return "out of memory";
         case BPE_EHIP: return "HIP runtime error";
@@ -272,7 +263,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     }
     if (!config_ok(n, cfg)) return BPE_EINVAL;
     const uint32_t tlog2 = table_log2_for(n, cfg);
-    const Layout lay = layout_for(n);
+    const Layout lay = layout_for(n, tlog2);
     if (cfg && cfg->workspace && cfg->workspace_bytes < lay.total) {
         set_err("workspace of %zu bytes is smaller than the %zu bytes needed", cfg->workspace_bytes, lay.total);
         return BPE_EINVAL;
@@ -326,8 +317,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->ctl = reinterpret_cast<Ctl*>(base + lay.ctl);
     s->sym0 = reinterpret_cast<uint32_t*>(base + lay.sym0);
     s->sym1 = reinterpret_cast<uint32_t*>(base + lay.sym1);
-    s->pool_rec = reinterpret_cast<uint2*>(base + lay.pool);
-    s->part_n = reinterpret_cast<uint32_t*>(base + lay.part_n);
+    s->table = reinterpret_cast<unsigned long long*>(base + lay.table);
     s->status = reinterpret_cast<unsigned long long*>(base + lay.status);
     s->merges = reinterpret_cast<uint32_t*>(base + lay.merges);
     s->lengths = reinterpret_cast<uint32_t*>(base + lay.lengths);
@@ -342,10 +332,10 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB, MERGE_LT>,
                                                      MERGE_TPB, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    // the record pool was sized for at most grid_bound(n) workgroups
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, grid_bound(n)));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, grid_bound(n)));
     s->fill_grid = cus * 4;
+    s->find_grid = int(std::min<size_t>(size_t(cus) * 4, std::max<size_t>(1, s->slots() / 2 / FIND_TPB)));
 
     // input bytes: device memory is read in place, host memory is uploaded
     // into the second symbol buffer first (4n bytes hold n bytes)
@@ -359,11 +349,12 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         src = reinterpret_cast<const uint8_t*>(s->sym1);
     }
     hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
-    hipLaunchKernelGGL(bpek::k_fill32, dim3(1), dim3(256), 0, s->stream, s->part_n, size_t(bpek::NPART), 0u);
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->table, size_t(s->slots()),
+                       bpek::GT_EMPTY);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->status,
                        size_t(lay.max_tiles), 0ull);
     hipLaunchKernelGGL((bpek::k_tag_count<TAG_TPB, TAG_LT>), dim3(s->tag_grid), dim3(TAG_TPB), 0, s->stream,
-                       src, uint32_t(n), s->sym0, s->pool(), s->ctl);
+                       src, uint32_t(n), s->sym0, s->gtable(), s->ctl);
     e = hipGetLastError();
     if (e != hipSuccess) {
         set_err("kernel launch failed: %s", hipGetErrorString(e));
@@ -505,20 +496,12 @@ bpe_status bpe_pair_counts(bpe_state* s, uint32_t* keys, uint32_t* counts, size_
     Ctl h;
     bpe_status st = read_ctl(s, &h);
     if (st != BPE_OK) return st;
-    // the pending partial counts: every reserved record of every partition
-    std::vector<uint32_t> pn(bpek::NPART);
-    HIP_TRY(hipMemcpy(pn.data(), s->part_n, 4 * pn.size(), hipMemcpyDeviceToHost));
-    std::unordered_map<uint32_t, uint64_t> sum;
-    std::vector<uint2> rec;
-    for (uint32_t p = 0; p < bpek::NPART; ++p) {
-        const uint32_t cnt = std::min(pn[p], s->lay.pcap);
-        rec.resize(cnt);
-        if (cnt)
-            HIP_TRY(hipMemcpy(rec.data(), s->pool_rec + size_t(p) * s->lay.pcap, 8 * size_t(cnt),
-                              hipMemcpyDeviceToHost));
-        for (const uint2& r : rec)
-            if (r.x != bpek::EMPTY) sum[r.x] += r.y;
-    }
+    // the global table holds the counts of the current sequence
+    std::vector<unsigned long long> tab(s->slots());
+    HIP_TRY(hipMemcpy(tab.data(), s->table, 8 * tab.size(), hipMemcpyDeviceToHost));
+    std::vector<std::pair<uint32_t, uint32_t>> sum;
+    for (unsigned long long v : tab)
+        if (v >> 32) sum.emplace_back(uint32_t(v), uint32_t(v >> 32));
     std::vector<uint32_t> k, c;
     for (const auto& kv : sum) {
         k.push_back(kv.first);
@@ -558,7 +541,7 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res,
     std::vector<hipEvent_t>& e = *ev;
     HIP_TRY(hipEventRecord(e[0], s->stream));
     for (uint32_t i = 0; i < n_merges; ++i) {
-        launch_select(s);
+        launch_find_max(s);
         HIP_TRY(hipEventRecord(e[2 * size_t(i) + 1], s->stream));
         launch_merge(s);
         HIP_TRY(hipEventRecord(e[2 * size_t(i) + 2], s->stream));

@@ -3,29 +3,29 @@
 // Steps of one training iteration, after the page "bpe - GPU BPE Tokenizer
 // Pipeline (Egitim + Cikarim)" (llm.istanbul/learn/tr/13_bpe): word-boundary
 // tagging ("Ne Yapar? 1", once), pair counting in two levels, first in a
-// workgroup-local table and then across workgroups ("Ne Yapar? 2"), a
+// workgroup-local table and then in one global table ("Ne Yapar? 2"), a
 // deterministic maximum (pipeline list at the head of the page), then merge
 // + prefix-scan compaction of the symbol array ("Ne Yapar? 3").
 //
 // How the work is laid out here (not the page's WGSL dispatch plan):
 //   k_tag_count  bytes -> tagged uint32 symbols, and the pair counts of
-//                iteration 0.
+//                iteration 0 in the global table (LDS aggregation first).
+//   k_find_max   one sweep of the global table for the maximum; the last
+//                workgroup to finish records the merge (device-resident, no
+//                host round trip).
 //   k_merge      (merge.hpp) one persistent pass over the symbols that
 //                applies the merge, compacts with a single-pass decoupled
-//                look-back scan, and counts the pairs of the new sequence for
-//                the next iteration: the symbols are read once and written
-//                once per iteration.
-//   k_select     the second counting level plus the maximum: one workgroup
-//                per key partition sums that partition's partial counts in
-//                LDS, takes its maximum, and the last workgroup to finish
-//                records the merge (device-resident, no host round trip).
-// Counting: a workgroup aggregates its pairs in an LDS hash table; when the
-// table is half full (and at the end) it is flushed as (key, count) records
-// into NPART hash partitions of a record pool, grouped by partition in LDS
-// and written with one atomic reservation per partition and 64-record chunk.
-// Global memory sees no per-pair atomics: MI355X performs device-scope
-// atomics at a few tens of G/s, far below the symbol rate, and most pairs of
-// a tile are distinct once training is past its first iterations.
+//                look-back scan, and updates the global table by the pairs
+//                the merge destroyed and created: the symbols are read once
+//                and written once per iteration.
+// The global table always holds the exact pair counts of the current
+// sequence, as a full recount would give them. A merge changes only the
+// pairs at its own sites: every other adjacency of the new sequence is an
+// adjacency of the old one, and the other way round. So the recount the
+// page does every iteration is replaced by subtracting the old pairs that
+// touch a changed position and adding the new pairs that touch a new
+// symbol, which costs work in proportion to the merge's occurrences rather
+// than to the sequence length.
 // All arithmetic is integer; results do not depend on scheduling.
 #pragma once
 
@@ -39,14 +39,12 @@ constexpr uint32_t IDM = 0xFFFFu;        // id field of a symbol
 constexpr uint32_t EMPTY = 0xFFFFFFFFu;  // empty key (the pair 65535,65535 is never counted)
 constexpr uint32_t BASE = 256u;
 
-constexpr uint32_t ERR_TABLE = 1u;  // counting capacity exceeded (record pool or select table)
+constexpr uint32_t ERR_TABLE = 1u;  // the global pair table is full
 constexpr uint32_t ERR_SPIN = 2u;   // a look-back wait exceeded its bound
 
-constexpr uint32_t LDS_PROBES = 16;       // buckets probed before giving up on an LDS table
+constexpr uint32_t LDS_PROBES = 16;        // buckets probed before giving up on an LDS table
+constexpr uint32_t GT_PROBES = 4096;       // slots probed before giving up on the global table
 constexpr uint32_t SPIN_LIMIT = 1u << 22;  // polls of one look-back before giving up
-
-constexpr uint32_t NPART = 256;  // key partitions of the record pool
-constexpr uint32_t CHUNK = 64;   // records reserved at a time per partition and workgroup
 
 // Device-resident control block; one per training state.
 struct alignas(64) Ctl {
@@ -58,18 +56,23 @@ struct alignas(64) Ctl {
     uint32_t n[2];        // symbol counts; n[m & 1] is the current one
     uint32_t L, R, X;     // merge being applied: (L, R) -> X
     uint32_t tile_ctr;    // dynamic tile counter of k_merge
-    uint32_t sweep_done;  // k_select workgroups finished
-    uint32_t pad[3];
-    unsigned long long best;  // packed argmax of the current selection
+    uint32_t sweep_done;  // k_find_max workgroups finished
+    uint32_t used;        // claimed slots of the global table
+    uint32_t pad_;
+    unsigned long long best;  // packed maximum of the current sweep
 };
 
-// Record pool: partition p owns records [p * pcap, (p + 1) * pcap); part_n[p]
-// of them are reserved (filled, or padded with EMPTY keys).
-struct Pool {
-    uint2* rec;        // {key, count}
-    uint32_t* part_n;  // NPART reservation counters
-    uint32_t pcap;     // records per partition
+// Global pair table: open addressing with linear probing over 64-bit slots
+// holding count << 32 | key. An empty slot holds key EMPTY with count 0; a
+// claimed slot keeps its key for good (a pair whose count falls to zero
+// never occurs again: every new adjacency involves the newest id), so probe
+// chains are never broken.
+struct GTable {
+    unsigned long long* slot;
+    uint32_t mask;   // slots - 1 (a power of two)
+    uint32_t limit;  // claims allowed before the table counts as full
 };
+constexpr unsigned long long GT_EMPTY = 0xFFFFFFFFull;
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -85,8 +88,6 @@ __device__ __forceinline__ uint32_t mix32(uint32_t h) {
     h ^= h >> 16;
     return h;
 }
-
-__device__ __forceinline__ uint32_t part_of(uint32_t key) { return mix32(key) >> 24; }
 
 // Character class: 4 newline, 2 space, 1 ASCII digit, 0 letter (ASCII
 // letters and every byte >= 0x80, so UTF-8 letters stay letters), 3 other.
@@ -104,16 +105,35 @@ __device__ __forceinline__ uint32_t pair_key(uint32_t left_sym, uint32_t right_s
     return ((left_sym & IDM) << 16) | (right_sym & IDM);
 }
 
-// One record written on its own (rare: an LDS table with no free bucket).
-__device__ __forceinline__ void emit_one(const Pool& pool, uint32_t key, uint32_t c, Ctl* ctl) {
-    const uint32_t p = part_of(key);
-    const uint32_t pos = atomicAdd(pool.part_n + p, 1u);
-    if (pos < pool.pcap) {
-        pool.rec[(size_t)p * pool.pcap + pos] = make_uint2(key, c);
-    } else {
-        atomicOr(&ctl->err, ERR_TABLE);
-        atomicExch(&ctl->done, 1u);
+__device__ __forceinline__ void fail_table(Ctl* ctl) {
+    atomicOr(&ctl->err, ERR_TABLE);
+    atomicExch(&ctl->done, 1u);
+}
+
+// Add delta (two's complement, so negative deltas work) to the count of key
+// in the global table, claiming a slot for a new key. Within one launch a
+// key only ever receives deltas of one sign, so no count goes below zero.
+__device__ __forceinline__ void gt_add(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl) {
+    uint32_t h = mix32(key) & gt.mask;
+    for (uint32_t p = 0; p < GT_PROBES; ++p) {
+        unsigned long long* slot = gt.slot + h;
+        uint32_t cur = (uint32_t)__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cur == EMPTY) {
+            const unsigned long long old = atomicCAS(slot, GT_EMPTY, (unsigned long long)key);
+            if (old == GT_EMPTY) {
+                if (atomicAdd(&ctl->used, 1u) >= gt.limit) fail_table(ctl);
+                cur = key;
+            } else {
+                cur = (uint32_t)old;
+            }
+        }
+        if (cur == key) {
+            atomicAdd(slot, (unsigned long long)(long long)(int)delta << 32);
+            return;
+        }
+        h = (h + 1) & gt.mask;
     }
+    fail_table(ctl);
 }
 
 // ---------------------------------------------------------------- LDS table
@@ -188,7 +208,7 @@ struct LdsTable {
     // qcap >= 8 * tpb entries each. Every thread of the block calls this.
     template <int V>
     __device__ __forceinline__ void count(const uint32_t (&k)[V], uint32_t fold, uint32_t* qk, uint32_t* qc,
-                                          uint32_t qcap, int tpb, const Pool& pool, Ctl* ctl) {
+                                          uint32_t qcap, int tpb, const GTable& gt, Ctl* ctl) {
         constexpr int G = 4;
         static_assert(V % (2 * G) == 0, "keys come in groups of 8");
         uint32_t carry = 0;
@@ -227,7 +247,7 @@ struct LdsTable {
                             qk[q] = k[g + j];
                             qc[q] = cnt[j];
                         } else {
-                            emit_one(pool, k[g + j], cnt[j], ctl);
+                            gt_add(gt, k[g + j], cnt[j], ctl);
                         }
                         ++q;
                     }
@@ -238,7 +258,7 @@ struct LdsTable {
             const uint32_t nq = min(qn, qcap);
             if (nq) {  // uniform: read after the barrier
                 for (uint32_t i = threadIdx.x; i < nq; i += tpb)
-                    if (!insert(qk[i], qc[i])) emit_one(pool, qk[i], qc[i], ctl);
+                    if (!insert(qk[i], qc[i])) gt_add(gt, qk[i], qc[i], ctl);
                 __syncthreads();
                 if (threadIdx.x == 0) qn = 0u;
                 __syncthreads();
@@ -247,94 +267,20 @@ struct LdsTable {
     }
 };
 
-// ---------------------------------------------------------------- record emission
-// Per-workgroup state for writing LDS table contents to the record pool.
-// For each partition the workgroup holds a reserved chunk (cur_base, with
-// cur_left records unused). A flush counts its entries per partition,
-// reserves fresh contiguous chunks where the current one is too small (one
-// global atomic per partition that needs space), ranks entries within their
-// partition with LDS atomics and writes them.
-struct Emitter {
-    uint32_t cur_base[NPART];
-    uint32_t cur_left[NPART];
-    uint32_t hist[NPART];
-    uint32_t rank[NPART];
-    uint32_t avail[NPART];
-    uint32_t obase[NPART];
-    uint32_t nbase[NPART];
-
-    // every thread; a barrier must follow before use
-    __device__ __forceinline__ void init(int tpb) {
-        for (int p = threadIdx.x; p < (int)NPART; p += tpb) {
-            cur_left[p] = 0u;
-            cur_base[p] = 0u;
-            hist[p] = 0u;
-        }
-    }
-
-    // Write every occupied slot of tab as a record. Every thread of the
-    // block, after a barrier that follows the last change to tab.
-    template <int LT>
-    __device__ __forceinline__ void flush(const LdsTable<LT>& tab, int tpb, const Pool& pool, Ctl* ctl) {
-        for (int i = threadIdx.x; i < LT; i += tpb) {
-            const uint32_t key = tab.keys[i];
-            if (key != EMPTY) atomicAdd(hist + part_of(key), 1u);
-        }
-        __syncthreads();
-        for (int p = threadIdx.x; p < (int)NPART; p += tpb) {
-            const uint32_t need = hist[p], left = cur_left[p];
-            avail[p] = min(need, left);
-            obase[p] = cur_base[p];
-            rank[p] = 0u;
-            if (need > left) {
-                const uint32_t rest = need - left;
-                const uint32_t nch = (rest + CHUNK - 1) / CHUNK;
-                const uint32_t b = atomicAdd(pool.part_n + p, nch * CHUNK);
-                nbase[p] = b;
-                cur_base[p] = b + rest;
-                cur_left[p] = nch * CHUNK - rest;
-            } else {
-                cur_base[p] += need;
-                cur_left[p] = left - need;
-            }
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < LT; i += tpb) {
-            const uint32_t key = tab.keys[i];
-            if (key == EMPTY) continue;
-            const uint32_t p = part_of(key);
-            const uint32_t r = atomicAdd(rank + p, 1u);
-            const uint32_t pos = (r < avail[p]) ? obase[p] + r : nbase[p] + (r - avail[p]);
-            if (pos < pool.pcap) {
-                pool.rec[(size_t)p * pool.pcap + pos] = make_uint2(key, tab.cnts[i]);
-            } else {
-                atomicOr(&ctl->err, ERR_TABLE);
-                atomicExch(&ctl->done, 1u);
-            }
-        }
-        __syncthreads();
-        for (int p = threadIdx.x; p < (int)NPART; p += tpb) hist[p] = 0u;
-    }
-
-    // Fill the unused rest of every reserved chunk with EMPTY records (end
-    // of the kernel; every thread of the block).
-    __device__ __forceinline__ void pad(int tpb, const Pool& pool) {
-        for (int p = threadIdx.x; p < (int)NPART; p += tpb) {
-            const uint32_t b = cur_base[p], e = min(cur_base[p] + cur_left[p], pool.pcap);
-            for (uint32_t i = b; i < e; ++i) pool.rec[(size_t)p * pool.pcap + i] = make_uint2(EMPTY, 0u);
-        }
-    }
-};
-
-// every thread of the block, after a barrier that follows the last count
+// Add every nonzero LDS count to the global table and clear the LDS table.
+// Every thread of the block, after a barrier that follows the last change
+// to tab; a barrier must follow before tab is used again.
 template <int LT>
-__device__ __forceinline__ void flush_if_half_full(LdsTable<LT>& tab, Emitter& em, int tpb, const Pool& pool,
-                                                   Ctl* ctl) {
-    if (2u * tab.used > (uint32_t)LT) {
-        em.flush(tab, tpb, pool, ctl);
-        __syncthreads();
-        tab.clear(tpb);
-        __syncthreads();
+__device__ __forceinline__ void flush_table(LdsTable<LT>& tab, int tpb, const GTable& gt, Ctl* ctl) {
+    for (int i = threadIdx.x; i < LT; i += tpb) {
+        const uint32_t key = tab.keys[i], c = tab.cnts[i];
+        if (key != EMPTY && c != 0u) gt_add(gt, key, c, ctl);
+        tab.keys[i] = EMPTY;
+        tab.cnts[i] = 0u;
+    }
+    if (threadIdx.x == 0) {
+        tab.used = 0u;
+        tab.qn = 0u;
     }
 }
 
@@ -345,7 +291,7 @@ __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
         ctl->k = 0; ctl->m = 0; ctl->limit = 0; ctl->done = 0; ctl->err = 0;
         ctl->n[0] = n; ctl->n[1] = 0;
         ctl->L = 0; ctl->R = 0; ctl->X = 0;
-        ctl->tile_ctr = 0; ctl->sweep_done = 0;
+        ctl->tile_ctr = 0; ctl->sweep_done = 0; ctl->used = 0; ctl->pad_ = 0;
         ctl->best = 0ull;
         lengths[0] = n;
     }
@@ -355,15 +301,8 @@ __global__ void k_set_limit(Ctl* ctl, uint32_t limit) {
     if (threadIdx.x == 0 && blockIdx.x == 0) ctl->limit = limit;
 }
 
-// fill a buffer of 64-bit words with one value (status reset)
+// fill a buffer of 64-bit words with one value (status words, table slots)
 __global__ void k_fill64(unsigned long long* p, size_t count, unsigned long long v) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = v;
-}
-
-// fill a buffer of 32-bit words with one value (reservation counters)
-__global__ void k_fill32(uint32_t* p, size_t count, uint32_t v) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count;
          i += (size_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -377,14 +316,12 @@ __global__ void k_fill32(uint32_t* p, size_t count, uint32_t v) {
 
 template <int TPB, int LT>
 __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ bytes, uint32_t n,
-                                                   uint32_t* __restrict__ sym, Pool pool, Ctl* ctl) {
+                                                   uint32_t* __restrict__ sym, GTable gt, Ctl* ctl) {
     constexpr uint32_t CH = TPB * 16;
     constexpr uint32_t QCAP = TPB * 8;
     __shared__ LdsTable<LT> tab;
-    __shared__ Emitter em;
     __shared__ uint32_t s_qk[QCAP], s_qc[QCAP];
     tab.clear(TPB);
-    em.init(TPB);
     __syncthreads();
     const bool aligned = ((uintptr_t)bytes & 15u) == 0;
     const uint32_t nchunks = (n + CH - 1) / CH;
@@ -433,24 +370,23 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
             }
             left = b[j];
         }
-        tab.template count<16>(keys, fold, s_qk, s_qc, QCAP, TPB, pool, ctl);
-        flush_if_half_full(tab, em, TPB, pool, ctl);
+        tab.template count<16>(keys, fold, s_qk, s_qc, QCAP, TPB, gt, ctl);
+        if (2u * tab.used > (uint32_t)LT) {  // uniform: read after the barrier that ends count
+            flush_table(tab, TPB, gt, ctl);
+            __syncthreads();
+        }
     }
     __syncthreads();
-    em.flush(tab, TPB, pool, ctl);
-    __syncthreads();
-    em.pad(TPB, pool);
+    flush_table(tab, TPB, gt, ctl);
 }
 
-// ---------------------------------------------------------------- select
-// One workgroup per partition: sum the partition's records in an LDS table
-// of `slots` slots, take the maximum of the packed value (count << 32 |
-// ~key) (highest count, ties to the smallest (left, right), independent of
-// order), fold it into ctl->best with atomicMax, and reset the partition.
-// A partition with more distinct pairs than the table holds is summed in S
-// passes over its records, pass s taking the keys whose hash bits 12.. are
-// s modulo S (S doubles until every pass fits). The last workgroup to
-// finish records the merge and sets up the merge pass.
+// ---------------------------------------------------------------- maximum
+// Sweep of the global table for the maximum of the packed value
+// (count << 32 | ~key) over slots with a nonzero count: highest count, ties
+// to the smallest (left, right), whatever the order of the sweep. Each
+// workgroup folds its maximum into ctl->best with atomicMax; the last
+// workgroup to finish records the merge and sets up the merge pass, or
+// marks training done when no pair has a nonzero count.
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -463,63 +399,30 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-template <int TPB, int LT>
-__global__ __launch_bounds__(TPB) void k_select(Ctl* ctl, Pool pool, uint32_t slots, uint32_t* merges) {
-    __shared__ LdsTable<LT> tab;
+// slot value -> packed candidate (0 for an empty or zero-count slot)
+__device__ __forceinline__ unsigned long long candidate(unsigned long long v) {
+    return (v >> 32) ? (v ^ 0xFFFFFFFFull) : 0ull;
+}
+
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long long* __restrict__ table,
+                                                  uint32_t slots, uint32_t* merges) {
     __shared__ unsigned long long s_best[TPB / 64];
-    __shared__ uint32_t s_last, s_nrec, s_fail;
+    __shared__ uint32_t s_last;
     const uint32_t done = ld_relaxed(&ctl->done);
     const uint32_t k = ld_relaxed(&ctl->k);
     const uint32_t m = ld_relaxed(&ctl->m);
     const uint32_t limit = ld_relaxed(&ctl->limit);
     if (done || k != m || k >= limit) return;  // uniform over the grid
 
-    const uint32_t p = blockIdx.x;
-    slots = min(max(slots, 64u), (uint32_t)LT);
-    const uint32_t nbmask = slots / 4 - 1;
-    if (threadIdx.x == 0) s_nrec = min(pool.part_n[p], pool.pcap);
-    __syncthreads();
-    const uint32_t nrec = s_nrec;
-    const uint4* r4 = reinterpret_cast<const uint4*>(pool.rec + (size_t)p * pool.pcap);
+    // two slots per 16-byte load (slots is a power of two >= 1024)
+    const ulonglong2* t2 = reinterpret_cast<const ulonglong2*>(table);
     unsigned long long best = 0ull;
-    for (uint32_t S = 1;; S *= 2) {
-        bool failed = false;
-        best = 0ull;
-        for (uint32_t pass = 0; pass < S; ++pass) {
-            tab.clear_first(slots, TPB);
-            if (threadIdx.x == 0) s_fail = 0u;
-            __syncthreads();
-            for (uint32_t i = threadIdx.x; 2 * i < nrec; i += TPB) {
-                const uint4 v = r4[i];
-                if (v.x != EMPTY && ((mix32(v.x) >> 12) & (S - 1)) == pass && !tab.insert(v.x, v.y, nbmask))
-                    s_fail = 1u;
-                if (2 * i + 1 < nrec && v.z != EMPTY && ((mix32(v.z) >> 12) & (S - 1)) == pass &&
-                    !tab.insert(v.z, v.w, nbmask))
-                    s_fail = 1u;
-            }
-            __syncthreads();
-            if (s_fail) {  // uniform: read after the barrier
-                failed = true;
-                break;
-            }
-            for (uint32_t i = threadIdx.x; i < slots; i += TPB) {
-                const uint32_t key = tab.keys[i];
-                if (key != EMPTY) {
-                    const unsigned long long v = ((unsigned long long)tab.cnts[i] << 32) | (uint32_t)~key;
-                    best = v > best ? v : best;
-                }
-            }
-            __syncthreads();
-        }
-        if (!failed) break;
-        if (S >= 4096) {  // cannot happen below 2^12 * slots distinct pairs
-            if (threadIdx.x == 0) {
-                atomicOr(&ctl->err, ERR_TABLE);
-                atomicExch(&ctl->done, 1u);
-            }
-            break;
-        }
-        __syncthreads();
+    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < slots / 2; i += gridDim.x * TPB) {
+        const ulonglong2 v = t2[i];
+        const unsigned long long a = candidate(v.x), b = candidate(v.y);
+        best = a > best ? a : best;
+        best = b > best ? b : best;
     }
     best = wave_max_u64(best);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -529,7 +432,6 @@ __global__ __launch_bounds__(TPB) void k_select(Ctl* ctl, Pool pool, uint32_t sl
         unsigned long long b = 0ull;
         for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
         if (b) atomicMax(&ctl->best, b);
-        pool.part_n[p] = 0u;  // consumed
         __threadfence();
         const uint32_t prev = atomicAdd(&ctl->sweep_done, 1u);
         s_last = (prev == gridDim.x - 1) ? 1u : 0u;

@@ -1,5 +1,5 @@
-// Merge + compaction + recount: one pass over the symbols per training
-// iteration (gfx950, wave64).
+// Merge + compaction + count update: one pass over the symbols per
+// training iteration (gfx950, wave64).
 //
 // For the merge (L, R) -> X chosen by k_find_max, the pass
 //   1. applies the merge left to right without overlap (page "bpe - GPU BPE
@@ -7,9 +7,11 @@
 //      resolved by run-length parity),
 //   2. compacts the symbol array with an exclusive prefix scan of the kept
 //      flags ("Ne Yapar? 3"), carrying WORD_START_BIT on merged symbols,
-//   3. counts the adjacent pairs of the new sequence into an LDS hash table
-//      flushed as partial-count records ("Ne Yapar? 2"), the counts
-//      the next iteration's maximum is taken over.
+//   3. brings the global pair table ("Ne Yapar? 2") to the counts of the new
+//      sequence: every old pair that touches a changed position loses one,
+//      every new pair that touches a new symbol X gains one. A workgroup
+//      sums these changes in an LDS table and adds the sums to the global
+//      table at the end.
 // The page runs these as separate dispatches with a three-pass scan; here
 // the scan is a single-pass decoupled look-back over 8192-symbol tiles, so
 // the symbols are read once and written once per iteration.
@@ -166,19 +168,39 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
 // LDS index skew for staged output (thread-contiguous runs spread over banks)
 __device__ __forceinline__ uint32_t skew(uint32_t i) { return i + (i >> 5); }
 
+// Count changes of one thread's positions (bit j: position g0 + j).
+// sel holds sel for positions g0 .. g0 + V (bit V: the next thread's first),
+// sel_in the sel of position g0 - 1; x the old symbols, left the old symbol
+// at g0 - 1. Position i changes if it is dropped (sel_i) or becomes X
+// (sel_{i+1}). An old pair (i - 1, i), counted when i carries no word-start
+// tag, is gone if i - 1 or i changes. A kept position i with no tag forms
+// the new pair (left neighbour, value) and it is new if either side is an X:
+// the left neighbour is X when i - 1 was dropped (sel_{i-1}), otherwise the
+// unchanged old symbol i - 1; the value is X when sel_{i+1}.
+template <int V>
+struct Changes {
+    uint32_t gone, born;  // position masks
+    __device__ __forceinline__ Changes(const uint32_t (&x)[V], uint32_t sel, uint32_t sel_in) {
+        constexpr uint32_t VM = (1u << V) - 1u;
+        uint32_t untagged = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) untagged |= (uint32_t)!(x[j] & WS) << j;  // positions past n carry WS
+        const uint32_t sm1 = ((sel << 1) | sel_in) & VM, s0 = sel & VM, sp1 = (sel >> 1) & VM;
+        gone = (sm1 | s0 | sp1) & untagged;
+        born = ~s0 & (sm1 | sp1) & untagged & VM;
+    }
+};
+
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
-                                               uint32_t* __restrict__ buf1, Pool pool,
+                                               uint32_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
                                                uint32_t* lengths) {
     constexpr int V = 16;  // symbols per thread: four 16-byte loads
     constexpr int TILE = TPB * V;
     constexpr int NW = TPB / 64;
-    constexpr uint32_t QCAP = 8 * TPB;  // queued keys per group of 8 keys per thread
-    static_assert(2 * QCAP <= TILE + TILE / 32, "the miss queue fits in the staging buffer");
-    __shared__ LdsTable<LT> tab;
-    __shared__ Emitter em;
+    __shared__ LdsTable<LT> tab;  // count changes of this workgroup
     __shared__ uint32_t s_stage[TILE + TILE / 32];
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile, s_off, s_sel;
@@ -192,12 +214,12 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
     const uint32_t ntiles = (n + TILE - 1) / TILE;
     const uint32_t epoch = it + 1;
-    const bool do_count = X != IDM;  // the last possible id: no later iteration reads counts
+    // X == 65535 is the last possible id: no later iteration reads counts,
+    // and the pair (X, X) would collide with the empty key
+    const bool do_count = X != IDM;
     const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
 
     tab.clear(TPB);
-    em.init(TPB);
-
     for (;;) {
         if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr, 1u);
         __syncthreads();
@@ -205,7 +227,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         if (t >= ntiles) break;
         const uint32_t g0 = t * TILE + tid * V;
 
-        // ---- 16 symbols, then one neighbour on the right and two on the left
+        // ---- 16 symbols, then one neighbour on each side
         uint32_t x[V];
         if (t * TILE + TILE <= n) {
             const uint4* p4 = reinterpret_cast<const uint4*>(in + g0);
@@ -218,11 +240,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
 #pragma unroll
             for (int j = 0; j < V; ++j) x[j] = (g0 + j < n) ? in[g0 + j] : WS;
         }
-        uint32_t a1 = __shfl_up(x[V - 1], 1), a2 = __shfl_up(x[V - 2], 1), b1 = __shfl_down(x[0], 1);
-        if (lane == 0) {
-            a1 = (g0 >= 1 && g0 - 1 < n) ? in[g0 - 1] : WS;
-            a2 = (g0 >= 2 && g0 - 2 < n) ? in[g0 - 2] : WS;
-        }
+        uint32_t a1 = __shfl_up(x[V - 1], 1), b1 = __shfl_down(x[0], 1);
+        if (lane == 0) a1 = (g0 >= 1 && g0 - 1 < n) ? in[g0 - 1] : WS;
         if (lane == 63) b1 = (g0 + V < n) ? in[g0 + V] : WS;
 
         // ---- occurrences (bit j: position g0 + j; bit V: position g0 + V)
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         const uint32_t sel_in = tup_o(texcl, tile_sel);
         const uint32_t tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
 
-        // ---- resolve sel, stage kept symbols in LDS, form the new pairs
+        // ---- resolve sel and stage the kept symbols in LDS
         uint32_t selbits = 0;
         {
             uint32_t s = sel_in;
@@ -303,27 +322,14 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                 selbits |= s << j;
             }
         }
-        uint32_t prevval;
-        if (sel_in) prevval = X | (a2 & WS);  // position g0-1 merged into g0-2
-        else prevval = (selbits & 1u) ? (X | (a1 & WS)) : a1;
-        uint32_t keys[V];
-        uint32_t fold = 0, lastkey = EMPTY, prevj = 0;
-        uint32_t o = my_local;
+        {
+            uint32_t o = my_local;
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            keys[j] = EMPTY;
-            if (((valid >> j) & 1u) && !((selbits >> j) & 1u)) {
-                const uint32_t v = ((selbits >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
-                s_stage[skew(o)] = v;
-                ++o;
-                if (do_count && !(v & WS)) {
-                    const uint32_t key = pair_key(prevval, v);
-                    if (key == lastkey) fold |= 1u << prevj;  // runs of one key: one add
-                    lastkey = key;
-                    keys[j] = key;
-                    prevj = j;
+            for (int j = 0; j < V; ++j) {
+                if (((valid >> j) & 1u) && !((selbits >> j) & 1u)) {
+                    s_stage[skew(o)] = ((selbits >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
+                    ++o;
                 }
-                prevval = v;
             }
         }
         __syncthreads();
@@ -349,15 +355,31 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             __threadfence();
             atomicExch(&ctl->m, it + 1);
         }
-        __syncthreads();
-        // ---- count the new pairs; the staging buffer now holds the miss queue
-        tab.template count<V>(keys, fold, s_stage, s_stage + QCAP, QCAP, TPB, pool, ctl);
-        flush_if_half_full(tab, em, TPB, pool, ctl);
+
+        // ---- count changes at this thread's merge sites (none for most threads)
+        if (do_count && (occ | sel_in)) {
+            const Changes<V> ch(x, selbits, sel_in);
+            if (ch.gone | ch.born) {
+                uint32_t prev = a1;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    if ((ch.gone >> j) & 1u) {
+                        const uint32_t key = pair_key(prev, x[j]);
+                        if (!tab.insert(key, 0xFFFFFFFFu)) gt_add(gt, key, 0xFFFFFFFFu, ctl);
+                    }
+                    if ((ch.born >> j) & 1u) {
+                        const uint32_t l = (j == 0 ? sel_in : (selbits >> (j - 1)) & 1u) ? X : prev;
+                        const uint32_t r = ((selbits >> (j + 1)) & 1u) ? X : x[j];
+                        const uint32_t key = pair_key(l, r);
+                        if (!tab.insert(key, 1u)) gt_add(gt, key, 1u, ctl);
+                    }
+                    prev = x[j];
+                }
+            }
+        }
     }
     __syncthreads();
-    em.flush(tab, TPB, pool, ctl);
-    __syncthreads();
-    em.pad(TPB, pool);
+    if (tab.used) flush_table(tab, TPB, gt, ctl);  // uniform: read after the barrier
 }
 
 }  // namespace bpek

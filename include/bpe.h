@@ -25,6 +25,11 @@
  *   - the merged symbol keeps the left symbol's tag;
  *   - tagging happens once, before the first iteration;
  *   - training stops early when no countable pair is left.
+ * The counts are those of a full recount, but they are not recounted: the
+ * library counts once (after tagging) into a global table and then, at
+ * every merge, subtracts the old pairs that touch a changed position and
+ * adds the new pairs that touch the new symbol. Every other adjacency is
+ * the same before and after the merge, so the table stays exact.
  *
  * Symbols are uint32: bits 0-15 hold the id, bit 16 the word-start tag,
  * bits 17-31 are zero. Ids fit in 16 bits, hence BPE_MAX_MERGES.
@@ -135,8 +140,8 @@ bpe_status bpe_lengths(bpe_state *s, uint32_t *out, uint32_t cap, uint32_t *n_ou
 
 /* The pair counts the next iteration will choose from (the counts of the
    current sequence, "Ne Yapar? 2"): keys[i] = left << 16 | right, counts[i]
-   its number of adjacent positions, in table order; *n_out = number of
-   distinct pairs. Both arrays are host or device, cap entries each; with cap
+   its number of adjacent positions (pairs whose count fell to zero are left
+   out), in table order; *n_out = number of distinct pairs. Both arrays are host or device, cap entries each; with cap
    0 only the number is returned, with cap below it BPE_EINVAL. */
 bpe_status bpe_pair_counts(bpe_state *s, uint32_t *keys, uint32_t *counts, size_t cap, size_t *n_out);
 

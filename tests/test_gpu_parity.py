@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Bit-exact everywhere: all work is integer. Inputs are the seeded synthetic
-corpora at sizes that span several 4096-symbol scan tiles and end in a
+corpora at sizes that span several 8192-symbol scan tiles and end in a
 ragged tail, plus adversarial runs and the degenerate cases."""
 import os
 import sys
@@ -171,15 +171,15 @@ def test_determinism_and_table_size_independence(bpe):
     assert np.array_equal(ref[0], om) and np.array_equal(ref[1], ot)
 
 
-def test_small_select_table_takes_several_passes(bpe):
-    # random bytes have far more distinct countable pairs than a 2^10-slot
-    # table (64 LDS slots per partition): the select stage sums each
-    # partition in several passes and the result must not change
+def test_full_pair_table_is_reported_not_dropped(bpe):
+    # random bytes have far more distinct countable pairs than 7/8 of a
+    # 2^10-slot table: training must stop with BPE_ETABLE, never go on with
+    # a count missing; the same input trains bit-exactly with a large table
     d = corpus.generate(corpus.CONFIGS[5].scaled(200_000, seed=12))
-    small = gpu_train(bpe, d, 30, table_log2=10)
+    with pytest.raises(RuntimeError, match="table"):
+        gpu_train(bpe, d, 30, table_log2=10)
     big = gpu_train(bpe, d, 30, table_log2=22)
     om, ot, _ = oracle.train_chunks(d, 30)
-    assert np.array_equal(small[0], om) and np.array_equal(small[1], ot)
     assert np.array_equal(big[0], om) and np.array_equal(big[1], ot)
 
 
