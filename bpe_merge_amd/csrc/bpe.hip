@@ -31,11 +31,12 @@ namespace {
 
 // launch shapes
 constexpr int MERGE_TPB = 512;
-constexpr int MERGE_LT = 2048;             // LDS slots for count changes, per workgroup
+constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
 constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 constexpr int FIND_TPB = 256;
+constexpr int FIND_U = 8;                  // 16-byte loads in flight per sweep thread
 
 thread_local std::string g_err;
 
@@ -79,7 +80,7 @@ size_t grid_bound(size_t n) { return (n + TILE - 1) / TILE + 1; }
 uint32_t table_limit(uint32_t tlog2) { return uint32_t((1ull << tlog2) - (1ull << tlog2) / 8); }
 
 struct Layout {
-    size_t ctl, sym0, sym1, table, status, merges, lengths, total;
+    size_t ctl, sweep, sym0, sym1, table, status, merges, lengths, total;
     uint32_t max_tiles;
 };
 
@@ -88,6 +89,8 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     size_t a = 0;
     L.ctl = a;
     a += 256;
+    L.sweep = a;
+    a = align_up(a + sizeof(bpek::Sweep), 256);
     const size_t sym_elems = align_up(n ? n : 1, TILE) + 64;
     L.sym0 = a;
     a = align_up(a + 4 * sym_elems, 256);
@@ -146,6 +149,7 @@ struct bpe_state {
     uint32_t tlog2 = 0;
     Layout lay{};
     Ctl* ctl = nullptr;
+    bpek::Sweep* sweep = nullptr;
     uint32_t* sym0 = nullptr;
     uint32_t* sym1 = nullptr;
     unsigned long long* table = nullptr;
@@ -163,8 +167,8 @@ struct bpe_state {
 namespace {
 
 void launch_find_max(bpe_state* s) {
-    hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream, s->ctl,
-                       s->table, s->slots(), s->merges);
+    hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB, FIND_U>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
+                       s->ctl, s->table, s->slots(), s->sweep, s->merges);
 }
 
 void launch_merge(bpe_state* s) {
@@ -315,6 +319,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     }
     char* base = static_cast<char*>(s->ws);
     s->ctl = reinterpret_cast<Ctl*>(base + lay.ctl);
+    s->sweep = reinterpret_cast<bpek::Sweep*>(base + lay.sweep);
     s->sym0 = reinterpret_cast<uint32_t*>(base + lay.sym0);
     s->sym1 = reinterpret_cast<uint32_t*>(base + lay.sym1);
     s->table = reinterpret_cast<unsigned long long*>(base + lay.table);
@@ -335,7 +340,10 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, grid_bound(n)));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, grid_bound(n)));
     s->fill_grid = cus * 4;
-    s->find_grid = int(std::min<size_t>(size_t(cus) * 4, std::max<size_t>(1, s->slots() / 2 / FIND_TPB)));
+    // one sweep workgroup per CU at most (each finishing workgroup costs a
+    // returning atomic), fewer for small tables
+    s->find_grid = int(std::min<size_t>(std::min<size_t>(cus, bpek::SWEEP_MAX_BLOCKS),
+                                        std::max<size_t>(1, s->slots() / 2 / (FIND_TPB * FIND_U))));
 
     // input bytes: device memory is read in place, host memory is uploaded
     // into the second symbol buffer first (4n bytes hold n bytes)
@@ -349,6 +357,8 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         src = reinterpret_cast<const uint8_t*>(s->sym1);
     }
     hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s->stream,
+                       reinterpret_cast<unsigned long long*>(s->sweep), sizeof(bpek::Sweep) / 8, 0ull);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->table, size_t(s->slots()),
                        bpek::GT_EMPTY);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->status,

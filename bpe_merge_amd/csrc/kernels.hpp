@@ -58,8 +58,19 @@ struct alignas(64) Ctl {
     uint32_t tile_ctr;    // dynamic tile counter of k_merge
     uint32_t sweep_done;  // k_find_max workgroups finished
     uint32_t used;        // claimed slots of the global table
-    uint32_t pad_;
-    unsigned long long best;  // packed maximum of the current sweep
+};
+
+// Scratch of one k_find_max launch: a maximum per workgroup, then one per
+// group of workgroups. The group counters sit 256 bytes apart (separate
+// memory channels): returning atomics on one address are serialized, so
+// finishing workgroups count in SWEEP_GROUPS places and only the last of
+// each group goes on to the counter in Ctl.
+constexpr uint32_t SWEEP_GROUPS = 8;
+constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;
+struct Sweep {
+    unsigned long long bmax[SWEEP_MAX_BLOCKS];
+    unsigned long long gmax[SWEEP_GROUPS * 32];  // group g at 32 * g
+    uint32_t gcnt[SWEEP_GROUPS * 64];            // group g at 64 * g
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -73,6 +84,17 @@ struct GTable {
     uint32_t limit;  // claims allowed before the table counts as full
 };
 constexpr unsigned long long GT_EMPTY = 0xFFFFFFFFull;
+
+// Workgroup barrier that orders LDS only. __syncthreads() also orders the
+// workgroup's global memory accesses, which on gfx9 means waiting for every
+// outstanding global load and store of the wave (one vmcnt counter for
+// both) at every barrier. Waves of these kernels share data only through
+// LDS, so their global loads and stores stay in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -254,14 +276,14 @@ struct LdsTable {
                 }
             }
             if ((g / G) % 2 == 0) continue;  // drain after every 8 keys per thread
-            __syncthreads();
+            lds_barrier();
             const uint32_t nq = min(qn, qcap);
             if (nq) {  // uniform: read after the barrier
                 for (uint32_t i = threadIdx.x; i < nq; i += tpb)
                     if (!insert(qk[i], qc[i])) gt_add(gt, qk[i], qc[i], ctl);
-                __syncthreads();
+                lds_barrier();
                 if (threadIdx.x == 0) qn = 0u;
-                __syncthreads();
+                lds_barrier();
             }
         }
     }
@@ -291,8 +313,7 @@ __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
         ctl->k = 0; ctl->m = 0; ctl->limit = 0; ctl->done = 0; ctl->err = 0;
         ctl->n[0] = n; ctl->n[1] = 0;
         ctl->L = 0; ctl->R = 0; ctl->X = 0;
-        ctl->tile_ctr = 0; ctl->sweep_done = 0; ctl->used = 0; ctl->pad_ = 0;
-        ctl->best = 0ull;
+        ctl->tile_ctr = 0; ctl->sweep_done = 0; ctl->used = 0;
         lengths[0] = n;
     }
 }
@@ -322,7 +343,7 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
     __shared__ LdsTable<LT> tab;
     __shared__ uint32_t s_qk[QCAP], s_qc[QCAP];
     tab.clear(TPB);
-    __syncthreads();
+    lds_barrier();
     const bool aligned = ((uintptr_t)bytes & 15u) == 0;
     const uint32_t nchunks = (n + CH - 1) / CH;
     for (uint32_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
@@ -373,10 +394,10 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
         tab.template count<16>(keys, fold, s_qk, s_qc, QCAP, TPB, gt, ctl);
         if (2u * tab.used > (uint32_t)LT) {  // uniform: read after the barrier that ends count
             flush_table(tab, TPB, gt, ctl);
-            __syncthreads();
+            lds_barrier();
         }
     }
-    __syncthreads();
+    lds_barrier();
     flush_table(tab, TPB, gt, ctl);
 }
 
@@ -384,9 +405,9 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
 // Sweep of the global table for the maximum of the packed value
 // (count << 32 | ~key) over slots with a nonzero count: highest count, ties
 // to the smallest (left, right), whatever the order of the sweep. Each
-// workgroup folds its maximum into ctl->best with atomicMax; the last
-// workgroup to finish records the merge and sets up the merge pass, or
-// marks training done when no pair has a nonzero count.
+// workgroup publishes its maximum; the last workgroup of each group folds
+// its group's, and the last group to finish records the merge and sets up
+// the merge pass, or marks training done when no pair has a nonzero count.
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -404,11 +425,36 @@ __device__ __forceinline__ unsigned long long candidate(unsigned long long v) {
     return (v >> 32) ? (v ^ 0xFFFFFFFFull) : 0ull;
 }
 
-template <int TPB>
+__device__ __forceinline__ unsigned long long ld64(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Record the merge of the maximum b (0: no pair left). One thread.
+__device__ __forceinline__ void choose(Ctl* ctl, unsigned long long b, uint32_t k, uint32_t* merges) {
+    if (b == 0ull) {
+        ctl->done = 1u;  // no countable pair is left
+        return;
+    }
+    const uint32_t key = ~(uint32_t)(b & 0xFFFFFFFFull);
+    const uint32_t cnt = (uint32_t)(b >> 32);
+    merges[3 * k + 0] = key >> 16;
+    merges[3 * k + 1] = key & IDM;
+    merges[3 * k + 2] = cnt;
+    ctl->L = key >> 16;
+    ctl->R = key & IDM;
+    ctl->X = BASE + k;
+    ctl->tile_ctr = 0u;
+    ctl->k = k + 1;
+}
+
+// U 16-byte loads in flight per thread; gridDim.x <= SWEEP_MAX_BLOCKS
+template <int TPB, int U>
 __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long long* __restrict__ table,
-                                                  uint32_t slots, uint32_t* merges) {
+                                                  uint32_t slots, Sweep* sw, uint32_t* merges) {
     __shared__ unsigned long long s_best[TPB / 64];
-    __shared__ uint32_t s_last;
     const uint32_t done = ld_relaxed(&ctl->done);
     const uint32_t k = ld_relaxed(&ctl->k);
     const uint32_t m = ld_relaxed(&ctl->m);
@@ -417,46 +463,48 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
 
     // two slots per 16-byte load (slots is a power of two >= 1024)
     const ulonglong2* t2 = reinterpret_cast<const ulonglong2*>(table);
+    const uint32_t n2 = slots / 2;
     unsigned long long best = 0ull;
-    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < slots / 2; i += gridDim.x * TPB) {
-        const ulonglong2 v = t2[i];
-        const unsigned long long a = candidate(v.x), b = candidate(v.y);
-        best = a > best ? a : best;
-        best = b > best ? b : best;
+    for (uint32_t i0 = blockIdx.x * (TPB * U) + threadIdx.x; i0 < n2; i0 += gridDim.x * (TPB * U)) {
+        ulonglong2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = (i0 + u * TPB < n2) ? t2[i0 + u * TPB] : make_ulonglong2(0ull, 0ull);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const unsigned long long a = candidate(v[u].x), c = candidate(v[u].y);
+            best = a > best ? a : best;
+            best = c > best ? c : best;
+        }
     }
     best = wave_max_u64(best);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) s_best[w] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long b = 0ull;
-        for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
-        if (b) atomicMax(&ctl->best, b);
-        __threadfence();
-        const uint32_t prev = atomicAdd(&ctl->sweep_done, 1u);
-        s_last = (prev == gridDim.x - 1) ? 1u : 0u;
+    lds_barrier();
+    if (threadIdx.x != 0) return;
+    unsigned long long b = 0ull;
+    for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
+
+    const uint32_t G = gridDim.x, NG = min(G, SWEEP_GROUPS), g = blockIdx.x % NG;
+    const uint32_t members = (G - g + NG - 1) / NG;  // workgroups g, g + NG, ...
+    st64(sw->bmax + blockIdx.x, b);
+    __threadfence();
+    if (atomicAdd(sw->gcnt + 64 * g, 1u) != members - 1) return;
+    __hip_atomic_store(sw->gcnt + 64 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    for (uint32_t i = g; i < G; i += NG) {
+        const unsigned long long o = ld64(sw->bmax + i);
+        b = o > b ? o : b;
     }
-    __syncthreads();
-    if (s_last && threadIdx.x == 0) {
-        __threadfence();
-        const unsigned long long b = __hip_atomic_load(&ctl->best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (b == 0ull) {
-            ctl->done = 1u;  // no countable pair is left
-        } else {
-            const uint32_t key = ~(uint32_t)(b & 0xFFFFFFFFull);
-            const uint32_t cnt = (uint32_t)(b >> 32);
-            merges[3 * k + 0] = key >> 16;
-            merges[3 * k + 1] = key & IDM;
-            merges[3 * k + 2] = cnt;
-            ctl->L = key >> 16;
-            ctl->R = key & IDM;
-            ctl->X = BASE + k;
-            ctl->tile_ctr = 0u;
-            ctl->k = k + 1;
-        }
-        ctl->best = 0ull;
-        ctl->sweep_done = 0u;
+    st64(sw->gmax + 32 * g, b);
+    __threadfence();
+    if (atomicAdd(&ctl->sweep_done, 1u) != NG - 1) return;
+    ctl->sweep_done = 0u;
+    __threadfence();
+    for (uint32_t i = 0; i < NG; ++i) {
+        const unsigned long long o = ld64(sw->gmax + 32 * i);
+        b = o > b ? o : b;
     }
+    choose(ctl, b, k, merges);
 }
 
 }  // namespace bpek

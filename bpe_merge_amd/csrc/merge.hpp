@@ -191,6 +191,193 @@ struct Changes {
     }
 };
 
+// Apply one thread's count changes (masks from Changes) to the workgroup's
+// LDS table (the global table when LDS has no room), one changed pair per
+// loop turn, so that the insert code exists once. The old symbol at a
+// position j of the thread is needed without indexing registers: a dropped
+// position held R, one that becomes X held L, and any other position is
+// kept unchanged and already staged in LDS (st, at the thread's offset o
+// plus the number of kept positions before j). left: old symbol at g0 - 1.
+template <int LT>
+__device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, uint32_t gone,
+                                              uint32_t born, uint32_t sel, uint32_t sel_in, uint32_t left,
+                                              const uint32_t* st, uint32_t o, uint32_t kept, uint32_t L,
+                                              uint32_t R, uint32_t X) {
+    auto old_id = [&](uint32_t j) -> uint32_t {
+        if ((sel >> j) & 1u) return R;
+        if ((sel >> (j + 1)) & 1u) return L;
+        return st[skew(o + __popc(kept & ((1u << j) - 1u)))] & IDM;
+    };
+    const uint32_t sm1 = (sel << 1) | sel_in;  // bit j: sel of position j - 1
+    while (gone | born) {
+        const bool is_gone = gone != 0u;
+        const uint32_t j = __ffs(is_gone ? gone : born) - 1;
+        const uint32_t xl = j ? old_id(j - 1) : left;
+        uint32_t key, delta;
+        if (is_gone) {
+            key = pair_key(xl, old_id(j));
+            delta = 0xFFFFFFFFu;
+            gone &= gone - 1u;
+        } else {
+            key = pair_key(((sm1 >> j) & 1u) ? X : xl, ((sel >> (j + 1)) & 1u) ? X : old_id(j));
+            delta = 1u;
+            born &= born - 1u;
+        }
+        if (!tab.insert(key, delta)) gt_add(gt, key, delta, ctl);
+    }
+}
+
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw buffer, gfx9 (dword 3 of the resource)
+constexpr uint32_t BUF_OOB = 0x80000000u;   // an offset past any buffer: the store is dropped
+
+// Issue the loads of a thread's V = 16 symbols at g0 = tile * TILE + tid * 16
+// and, on the wave's edge lanes, of the neighbours the shuffles cannot
+// supply: h1 = sym[g0 - 1], h2 = sym[g0 - 2] on lane 0, hr = sym[g0 + 16] on
+// lane 63. Buffer loads through a resource covering the tile, the two
+// symbols before it and the one after it (within n): every lane issues the
+// same seven loads, a lane with nothing to load uses an offset past the
+// resource (the hardware returns 0 without a memory access), and a tile
+// past the end gets an empty resource. With no branch and a fixed count,
+// the compiler can wait for these loads alone, later. Values outside
+// [0, n) are undefined here; fix_tile replaces them by WS.
+template <int TILE>
+__device__ __forceinline__ void load_tile(const uint32_t* __restrict__ in, uint32_t n, uint32_t tile,
+                                          uint32_t ntiles, uint32_t tid, uint32_t lane, uint32_t (&x)[16],
+                                          uint32_t& h1, uint32_t& h2, uint32_t& hr) {
+    tile = __builtin_amdgcn_readfirstlane(tile);  // uniform: the resource lives in SGPRs
+    const uint32_t ts = tile * TILE, hb = ts >= 2u ? ts - 2u : 0u;
+    const uint32_t end = tile < ntiles ? min(n, ts + TILE + 1u) : hb;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(in) + hb, 0, (int)(4u * (end - hb)), BUF_RSRC_FLAGS);
+    const uint32_t g0 = ts + tid * 16u, o = 4u * (g0 - hb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    h1 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 1u) ? o - 4u : BUF_OOB, 0, 0);
+    h2 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 8u : BUF_OOB, 0, 0);
+    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 64u : BUF_OOB, 0, 0);
+}
+
+// After load_tile: WS in place of every value outside [0, n), then the
+// neighbours a1 = sym[g0 - 1], a2 = sym[g0 - 2], b1 = sym[g0 + 16].
+__device__ __forceinline__ void fix_tile(uint32_t (&x)[16], uint32_t h1, uint32_t h2, uint32_t hr, uint32_t g0,
+                                         uint32_t n, uint32_t lane, bool full, uint32_t& a1, uint32_t& a2,
+                                         uint32_t& b1) {
+    if (!full) {  // uniform: the last tile
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? x[j] : WS;
+    }
+    a1 = __shfl_up(x[15], 1);
+    a2 = __shfl_up(x[14], 1);
+    b1 = __shfl_down(x[0], 1);
+    if (lane == 0) {
+        a1 = g0 >= 1u ? h1 : WS;
+        a2 = g0 >= 2u ? h2 : WS;
+    }
+    if (lane == 63) b1 = (g0 + 16u < n) ? hr : WS;
+}
+
+// Occurrence bits of a thread (bit j: position g0 + j, bit V: position
+// g0 + V) and its valid positions; a1 = sym[g0 - 1], b1 = sym[g0 + V].
+template <int V>
+__device__ __forceinline__ void occurrences(const uint32_t (&x)[V], uint32_t a1, uint32_t b1, uint32_t g0,
+                                            uint32_t n, uint32_t L, uint32_t R, uint32_t& occ,
+                                            uint32_t& valid) {
+    // bitwise, not short-circuit: no branch per position. A position
+    // past n holds WS, and position 0 always carries WS, so the tag test
+    // also rules those out.
+    occ = 0;
+    uint32_t prev = a1;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const uint32_t o = (uint32_t)((prev & IDM) == L) & (uint32_t)((x[j] & (WS | IDM)) == R);
+        occ |= o << j;
+        prev = x[j];
+    }
+    occ |= ((uint32_t)((x[V - 1] & IDM) == L) & (uint32_t)((b1 & (WS | IDM)) == R)) << V;
+    valid = (g0 >= n) ? 0u : (n - g0 >= (uint32_t)V ? (1u << V) - 1u : (1u << (n - g0)) - 1u);
+}
+
+// Write the kept symbols of a tile from LDS (st) to out[tile_off ..
+// tile_off + tile_kept): up to 3 single symbols to reach 16-byte alignment,
+// whole 16-byte groups, up to 3 single symbols at the end. Each thread
+// issues the same fixed sequence of buffer stores (one 4-byte, TILE/4/TPB
+// 16-byte, one 4-byte); a store with nothing to write gets an offset past
+// the buffer, which the hardware drops. With no branch and a fixed count,
+// the compiler can wait for loads issued before these stores without
+// waiting for the stores themselves.
+template <int TPB, int TILE>
+__device__ __forceinline__ void store_tile(uint32_t* __restrict__ out, const uint32_t* st, uint32_t tile_off,
+                                           uint32_t tile_kept) {
+    const uint32_t tid = threadIdx.x;
+    tile_off = __builtin_amdgcn_readfirstlane(tile_off);  // uniform: the resource lives in SGPRs
+    tile_kept = __builtin_amdgcn_readfirstlane(tile_kept);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(out + tile_off, 0, (int)(4u * tile_kept), BUF_RSRC_FLAGS);
+    const uint32_t head = min(tile_kept, (4u - (tile_off & 3u)) & 3u);
+    const uint32_t body = (tile_kept - head) >> 2;
+    const uint32_t rest = head + 4 * body;
+    {
+        const bool on = tid < head;
+        const uint32_t i = on ? tid : 0u;
+        __builtin_amdgcn_raw_buffer_store_b32(st[skew(i)], rs, on ? 4u * i : BUF_OOB, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < TILE / 4 / TPB; ++q) {
+        const uint32_t g = tid + q * TPB;
+        const bool on = g < body;
+        const uint32_t b = on ? head + 4 * g : 0u;
+        const v4u32 v = {st[skew(b)], st[skew(b + 1)], st[skew(b + 2)], st[skew(b + 3)]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * b : BUF_OOB, 0, 0);
+    }
+    {
+        const bool on = tid < tile_kept - rest;
+        const uint32_t i = on ? rest + tid : 0u;
+        __builtin_amdgcn_raw_buffer_store_b32(st[skew(i)], rs, on ? 4u * i : BUF_OOB, 0, 0);
+    }
+}
+
+// Stage the kept symbols of a thread at tile-local offset o; a symbol whose
+// right neighbour merges into it becomes X (keeping its tag).
+template <int V>
+__device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
+                                      uint32_t sel, uint32_t X) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
+            st[skew(o)] = ((sel >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
+            ++o;
+        }
+    }
+}
+
+// The last tile publishes the new length and advances the iteration.
+__device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, uint32_t it, uint32_t total) {
+    ctl->n[(it + 1) & 1u] = total;
+    lengths[it + 1] = total;
+    __threadfence();
+    atomicExch(&ctl->m, it + 1);
+}
+
+// One persistent pass per iteration. Workgroups take 8192-symbol tiles from
+// a counter, in order, so every tile a look-back waits for is held by a
+// running workgroup that has already published or is about to publish its
+// aggregate.
+//
+// L != R (nearly every merge): occurrences cannot overlap, so every
+// occurrence is merged and sel_i = occ_i. A tile's kept symbols, its staged
+// output and its count changes are then known from the tile and two
+// symbols before it; the look-back only supplies the tile's output offset.
+// The workgroup publishes the tile's aggregate, stages and counts, takes
+// the next tile and issues its loads, and only then waits for the look-back
+// and writes: the next tile's loads are in flight while it waits.
+//
+// L == R: the selection carries along runs (sel_i = occ_i and not
+// sel_{i-1}) and a tile's selection can depend on every tile before it, so
+// staging waits for the look-back's sel as well.
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
@@ -200,10 +387,12 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     constexpr int V = 16;  // symbols per thread: four 16-byte loads
     constexpr int TILE = TPB * V;
     constexpr int NW = TPB / 64;
+    constexpr uint32_t VM = (1u << V) - 1u;
+    constexpr uint32_t SST = TILE + TILE / 32;  // one staging buffer (skewed)
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
-    __shared__ uint32_t s_stage[TILE + TILE / 32];
+    __shared__ uint32_t s_stage[2 * SST];
     __shared__ uint32_t s_wagg[NW];
-    __shared__ uint32_t s_tile, s_off, s_sel;
+    __shared__ uint32_t s_tile[2], s_off[2], s_sel;
 
     const uint32_t k = ld_relaxed(&ctl->k);
     const uint32_t it = ld_relaxed(&ctl->m);
@@ -220,165 +409,183 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
 
     tab.clear(TPB);
-    for (;;) {
-        if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr, 1u);
-        __syncthreads();
-        const uint32_t t = s_tile;
-        if (t >= ntiles) break;
-        const uint32_t g0 = t * TILE + tid * V;
+    if (tid == 0) s_tile[0] = atomicAdd(&ctl->tile_ctr, 1u);
+    lds_barrier();
+    uint32_t t = s_tile[0];
+    uint32_t x[V], h1, h2, hr;
+    static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
+    load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
 
-        // ---- 16 symbols, then one neighbour on each side
-        uint32_t x[V];
-        if (t * TILE + TILE <= n) {
-            const uint4* p4 = reinterpret_cast<const uint4*>(in + g0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 v = p4[q];
-                x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < V; ++j) x[j] = (g0 + j < n) ? in[g0 + j] : WS;
-        }
-        uint32_t a1 = __shfl_up(x[V - 1], 1), b1 = __shfl_down(x[0], 1);
-        if (lane == 0) a1 = (g0 >= 1 && g0 - 1 < n) ? in[g0 - 1] : WS;
-        if (lane == 63) b1 = (g0 + V < n) ? in[g0 + V] : WS;
+    if (L != R) {
+        // tp: the tile staged in the previous round, waiting for its offset
+        // (ntiles: none); kp its kept count; cur the staging buffer of the
+        // current tile (the pending one is in the other)
+        uint32_t tp = ntiles, kp = 0, cur = 0;
+        // The tile after t, taken one round ahead: waiting for a returning
+        // atomic waits for every older access of the wave (one counter), so
+        // it is issued after the stores of a round and consumed in the next.
+        uint32_t grab = 0;
+        if (tid == 0) grab = atomicAdd(&ctl->tile_ctr, 1u);
+        // the loop-top waits count on the stores each round issues after its
+        // loads; the first loads get the same six stores (nothing written)
+        store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
+        for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
+            uint32_t tn = ntiles, tile_kept = 0;
+            if (t < ntiles) {  // uniform
+                const uint32_t g0 = t * TILE + tid * V;
+                uint32_t a1, a2, b1;
+                fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
+                uint32_t occ, valid;
+                occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
+                // sel = occ; the position before g0 is merged iff it is an occurrence
+                const uint32_t sel_in = (g0 >= 1 && !(a1 & WS) && (a2 & IDM) == L && (a1 & IDM) == R) ? 1u : 0u;
 
-        // ---- occurrences (bit j: position g0 + j; bit V: position g0 + V)
-        uint32_t occ = 0, valid = 0;
-        {
-            uint32_t prev = a1;
+                // ---- kept counts: wave scan, then across the waves
+                const uint32_t kept = __popc(valid & ~occ & VM);
+                uint32_t incl = kept;
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const bool v = g0 + j < n;
-                const bool o = v && (g0 + j >= 1) && !(x[j] & WS) && (prev & IDM) == L && (x[j] & IDM) == R;
-                occ |= (uint32_t)o << j;
-                valid |= (uint32_t)v << j;
-                prev = x[j];
-            }
-            const bool oV = (g0 + V < n) && !(b1 & WS) && (x[V - 1] & IDM) == L && (b1 & IDM) == R;
-            occ |= (uint32_t)oV << V;
-        }
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t u = __shfl_up(incl, o);
+                    if (lane >= (uint32_t)o) incl += u;
+                }
+                if (lane == 63) s_wagg[w] = incl;
+                if (tid == 0) s_tile[round & 1u] = grab;
+                lds_barrier();
+                uint32_t my_local = incl - kept;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    if (i < (int)w) my_local += s_wagg[i];
+                    tile_kept += s_wagg[i];
+                }
+                // the tile's aggregate goes out before anything else is done
+                if (tid == 0 && t != 0)
+                    st_store(status + t, st_pack(ST_AGG, epoch, tup_make(tile_kept, 0u, 0u, 0u)));
 
-        // ---- this thread's tuple, then inclusive scans over the wave and the waves
-        uint32_t tup;
-        {
-            uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const uint32_t o = (occ >> j) & 1u, v = (valid >> j) & 1u;
-                s0 = o & ~s0 & 1u;
-                s1 = o & ~s1 & 1u;
-                c0 += v & ~s0 & 1u;
-                c1 += v & ~s1 & 1u;
+                uint32_t* st = s_stage + cur * SST;
+                stage<V>(st, my_local, x, valid, occ, X);
+                if (do_count && (occ | sel_in)) {
+                    const Changes<V> ch(x, occ, sel_in);
+                    count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, occ, sel_in, a1, st, my_local,
+                                      valid & ~occ, L, R, X);
+                }
+                // ---- the next tile's loads are in flight during the look-back and stores below
+                tn = s_tile[round & 1u];
+                load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             }
-            tup = tup_make(c0, c1 - c0, s0, s1);
-        }
-        uint32_t incl = tup;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t u = __shfl_up(incl, o);
-            if (lane >= (uint32_t)o) incl = tup_then(u, incl);
-        }
-        uint32_t lane_excl = __shfl_up(incl, 1);
-        if (lane == 0) lane_excl = TUP_ID;
-        if (lane == 63) s_wagg[w] = incl;
-        __syncthreads();
-        uint32_t wave_excl = TUP_ID, tile_agg = TUP_ID;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            if (i == (int)w) wave_excl = tile_agg;
-            tile_agg = tup_then(tile_agg, s_wagg[i]);
-        }
-
-        // ---- decoupled look-back (wave 0)
-        if (w == 0) {
-            uint32_t off = 0, sel = 0;
-            if (t != 0) {
-                if (lane == 0) st_store(status + t, st_pack(ST_AGG, epoch, tile_agg));
-                lookback<4>(status, t, epoch, lane, ctl, off, sel);
-            }
-            if (lane == 0) {
-                const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
-                st_store(status + t, st_pack(ST_PRE, epoch, (off + kept) | (tup_o(tile_agg, sel) << 31)));
-                s_off = off;
-                s_sel = sel;
-            }
-        }
-        __syncthreads();
-        const uint32_t tile_off = s_off, tile_sel = s_sel;
-        const uint32_t texcl = tup_then(wave_excl, lane_excl);
-        const uint32_t my_local = tup_c0(texcl) + (tile_sel ? tup_d(texcl) : 0u);
-        const uint32_t sel_in = tup_o(texcl, tile_sel);
-        const uint32_t tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
-
-        // ---- resolve sel and stage the kept symbols in LDS
-        uint32_t selbits = 0;
-        {
-            uint32_t s = sel_in;
-#pragma unroll
-            for (int j = 0; j <= V; ++j) {
-                s = (occ >> j) & ~s & 1u;
-                selbits |= s << j;
-            }
-        }
-        {
-            uint32_t o = my_local;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                if (((valid >> j) & 1u) && !((selbits >> j) & 1u)) {
-                    s_stage[skew(o)] = ((selbits >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
-                    ++o;
+            // ---- the previous tile: its predecessors have had a round to publish
+            if (tp < ntiles && w == 0) {
+                uint32_t off = 0, sel = 0;
+                if (tp != 0) lookback<4>(status, tp, epoch, lane, ctl, off, sel);
+                if (lane == 0) {
+                    st_store(status + tp, st_pack(ST_PRE, epoch, off + kp));
+                    s_off[round & 1u] = off;
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- the tile's kept symbols, 16-byte stores where aligned
-        {
-            const uint32_t head = min(tile_kept, (4u - (tile_off & 3u)) & 3u);
-            if (tid < head) out[tile_off + tid] = s_stage[skew(tid)];
-            const uint32_t body = (tile_kept - head) >> 2;
-            uint4* o4 = reinterpret_cast<uint4*>(out + tile_off + head);
-            for (uint32_t i = tid; i < body; i += TPB) {
-                const uint32_t b = head + 4 * i;
-                o4[i] = make_uint4(s_stage[skew(b)], s_stage[skew(b + 1)], s_stage[skew(b + 2)],
-                                   s_stage[skew(b + 3)]);
+            lds_barrier();
+            // the grab goes before the stores so that waiting for it later
+            // does not wait for them; the stores are issued in every round
+            // (all dropped when no tile is pending) to keep their count fixed
+            if (tid == 0 && tn < ntiles) grab = atomicAdd(&ctl->tile_ctr, 1u);
+            const uint32_t tile_off = tp < ntiles ? s_off[round & 1u] : 0u;
+            store_tile<TPB, TILE>(out, s_stage + (cur ^ 1u) * SST, tile_off, tp < ntiles ? kp : 0u);
+            if (tp == ntiles - 1 && tid == 0) finish_iteration(ctl, lengths, it, tile_off + kp);
+            if (t < ntiles) {
+                tp = t;
+                kp = tile_kept;
+                cur ^= 1u;
+            } else {
+                tp = ntiles;
             }
-            const uint32_t rest = head + 4 * body;
-            if (tid < tile_kept - rest) out[tile_off + rest + tid] = s_stage[skew(rest + tid)];
+            t = tn;
         }
-        if (t == ntiles - 1 && tid == 0) {
-            const uint32_t total = tile_off + tile_kept;
-            ctl->n[(it + 1) & 1u] = total;
-            lengths[it + 1] = total;
-            __threadfence();
-            atomicExch(&ctl->m, it + 1);
-        }
+    } else {
+        for (uint32_t round = 1; t < ntiles; ++round) {
+            const uint32_t g0 = t * TILE + tid * V;
+            uint32_t a1, a2, b1;
+            fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
+            uint32_t occ, valid;
+            occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
 
-        // ---- count changes at this thread's merge sites (none for most threads)
-        if (do_count && (occ | sel_in)) {
-            const Changes<V> ch(x, selbits, sel_in);
-            if (ch.gone | ch.born) {
-                uint32_t prev = a1;
+            // ---- this thread's tuple, then inclusive scans over the wave and the waves
+            uint32_t tup;
+            {
+                uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    if ((ch.gone >> j) & 1u) {
-                        const uint32_t key = pair_key(prev, x[j]);
-                        if (!tab.insert(key, 0xFFFFFFFFu)) gt_add(gt, key, 0xFFFFFFFFu, ctl);
-                    }
-                    if ((ch.born >> j) & 1u) {
-                        const uint32_t l = (j == 0 ? sel_in : (selbits >> (j - 1)) & 1u) ? X : prev;
-                        const uint32_t r = ((selbits >> (j + 1)) & 1u) ? X : x[j];
-                        const uint32_t key = pair_key(l, r);
-                        if (!tab.insert(key, 1u)) gt_add(gt, key, 1u, ctl);
-                    }
-                    prev = x[j];
+                    const uint32_t o = (occ >> j) & 1u, v = (valid >> j) & 1u;
+                    s0 = o & ~s0 & 1u;
+                    s1 = o & ~s1 & 1u;
+                    c0 += v & ~s0 & 1u;
+                    c1 += v & ~s1 & 1u;
+                }
+                tup = tup_make(c0, c1 - c0, s0, s1);
+            }
+            uint32_t incl = tup;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t u = __shfl_up(incl, o);
+                if (lane >= (uint32_t)o) incl = tup_then(u, incl);
+            }
+            uint32_t lane_excl = __shfl_up(incl, 1);
+            if (lane == 0) lane_excl = TUP_ID;
+            if (lane == 63) s_wagg[w] = incl;
+            lds_barrier();
+            uint32_t wave_excl = TUP_ID, tile_agg = TUP_ID;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                if (i == (int)w) wave_excl = tile_agg;
+                tile_agg = tup_then(tile_agg, s_wagg[i]);
+            }
+
+            // ---- decoupled look-back (wave 0)
+            if (w == 0) {
+                uint32_t off = 0, sel = 0;
+                if (t != 0) {
+                    if (lane == 0) st_store(status + t, st_pack(ST_AGG, epoch, tile_agg));
+                    lookback<4>(status, t, epoch, lane, ctl, off, sel);
+                }
+                if (lane == 0) {
+                    const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
+                    st_store(status + t, st_pack(ST_PRE, epoch, (off + kept) | (tup_o(tile_agg, sel) << 31)));
+                    s_off[0] = off;
+                    s_sel = sel;
                 }
             }
+            lds_barrier();
+            const uint32_t tile_off = s_off[0], tile_sel = s_sel;
+            const uint32_t texcl = tup_then(wave_excl, lane_excl);
+            const uint32_t my_local = tup_c0(texcl) + (tile_sel ? tup_d(texcl) : 0u);
+            const uint32_t sel_in = tup_o(texcl, tile_sel);
+            const uint32_t tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
+
+            // ---- resolve sel, stage, count changes
+            uint32_t selbits = 0;
+            {
+                uint32_t s = sel_in;
+#pragma unroll
+                for (int j = 0; j <= V; ++j) {
+                    s = (occ >> j) & ~s & 1u;
+                    selbits |= s << j;
+                }
+            }
+            stage<V>(s_stage, my_local, x, valid, selbits, X);
+            if (do_count && (occ | sel_in)) {
+                const Changes<V> ch(x, selbits, sel_in);
+                count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, selbits, sel_in, a1, s_stage, my_local,
+                                  valid & ~selbits, L, R, X);
+            }
+
+            // ---- next tile, then write this one
+            if (tid == 0) s_tile[round & 1u] = atomicAdd(&ctl->tile_ctr, 1u);
+            lds_barrier();
+            const uint32_t tn = s_tile[round & 1u];
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
+            store_tile<TPB, TILE>(out, s_stage, tile_off, tile_kept);
+            if (t == ntiles - 1 && tid == 0) finish_iteration(ctl, lengths, it, tile_off + tile_kept);
+            t = tn;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tab.used) flush_table(tab, TPB, gt, ctl);  // uniform: read after the barrier
 }
 
