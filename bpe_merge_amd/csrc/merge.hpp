@@ -230,6 +230,9 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw buffer, gfx9 (dword 3 of the resource)
 constexpr uint32_t BUF_OOB = 0x80000000u;   // an offset past any buffer: the store is dropped
+// cache policy of the output stores: non-temporal (the next iteration reads
+// them back long after this pass has streamed the rest of the array)
+constexpr int BUF_NT = 2;
 
 // Issue the loads of a thread's V = 16 symbols at g0 = tile * TILE + tid * 16
 // and, on the wave's edge lanes, of the neighbours the shuffles cannot
@@ -331,7 +334,7 @@ __device__ __forceinline__ void store_tile(uint32_t* __restrict__ out, const uin
         const bool on = g < body;
         const uint32_t b = on ? head + 4 * g : 0u;
         const v4u32 v = {st[skew(b)], st[skew(b + 1)], st[skew(b + 2)], st[skew(b + 3)]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * b : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * b : BUF_OOB, 0, BUF_NT);
     }
     {
         const bool on = tid < tile_kept - rest;
