@@ -168,12 +168,13 @@ namespace {
 
 void launch_find_max(bpe_state* s) {
     hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB, FIND_U>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
-                       s->ctl, s->table, s->slots(), s->sweep, s->merges);
+                       s->ctl, s->table, s->slots(), s->sweep);
 }
 
 void launch_merge(bpe_state* s) {
     hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0, s->stream,
-                       s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths);
+                       s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                       uint32_t(s->find_grid), s->merges);
 }
 
 bpe_status launch_iteration(bpe_state* s) {
@@ -340,9 +341,10 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, grid_bound(n)));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, grid_bound(n)));
     s->fill_grid = cus * 4;
-    // one sweep workgroup per CU at most (each finishing workgroup costs a
-    // returning atomic), fewer for small tables
-    s->find_grid = int(std::min<size_t>(std::min<size_t>(cus, bpek::SWEEP_MAX_BLOCKS),
+    // four sweep workgroups per CU (one round of loads each on the largest
+    // default table), fewer for small tables; each merge workgroup reads
+    // every sweep workgroup's maximum
+    s->find_grid = int(std::min<size_t>(std::min<size_t>(size_t(cus) * 4, bpek::SWEEP_MAX_BLOCKS),
                                         std::max<size_t>(1, s->slots() / 2 / (FIND_TPB * FIND_U))));
 
     // input bytes: device memory is read in place, host memory is uploaded

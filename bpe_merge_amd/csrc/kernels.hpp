@@ -55,22 +55,24 @@ struct alignas(64) Ctl {
     uint32_t err;         // ERR_* bits
     uint32_t n[2];        // symbol counts; n[m & 1] is the current one
     uint32_t L, R, X;     // merge being applied: (L, R) -> X
-    uint32_t tile_ctr;    // dynamic tile counter of k_merge
-    uint32_t sweep_done;  // k_find_max workgroups finished
+    uint32_t tile_ctr;    // tiles handed out by k_merge, counted across iterations (mod 2^32)
     uint32_t used;        // claimed slots of the global table
 };
 
-// Scratch of one k_find_max launch: a maximum per workgroup, then one per
-// group of workgroups. The group counters sit 256 bytes apart (separate
-// memory channels): returning atomics on one address are serialized, so
-// finishing workgroups count in SWEEP_GROUPS places and only the last of
-// each group goes on to the counter in Ctl.
-constexpr uint32_t SWEEP_GROUPS = 8;
+// What a k_find_max launch leaves for the k_merge launch after it: one
+// maximum per sweep workgroup (the kernel boundary publishes them, so the
+// sweep needs no atomics or fences), and the iteration it swept for
+// (NO_ITER if training had stopped), and the tile counter's value before
+// the iteration (tile numbers are counter values minus this base, modulo
+// 2^32, so the counter never needs a reset). k_merge reads the iteration from here,
+// never from the live counters in Ctl, so that all its workgroups agree on
+// it even if one starts after the last tile was written.
 constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;
+constexpr uint32_t NO_ITER = 0xFFFFFFFFu;
 struct Sweep {
     unsigned long long bmax[SWEEP_MAX_BLOCKS];
-    unsigned long long gmax[SWEEP_GROUPS * 32];  // group g at 32 * g
-    uint32_t gcnt[SWEEP_GROUPS * 64];            // group g at 64 * g
+    uint32_t iter;
+    uint32_t tile_base;
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -313,7 +315,7 @@ __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
         ctl->k = 0; ctl->m = 0; ctl->limit = 0; ctl->done = 0; ctl->err = 0;
         ctl->n[0] = n; ctl->n[1] = 0;
         ctl->L = 0; ctl->R = 0; ctl->X = 0;
-        ctl->tile_ctr = 0; ctl->sweep_done = 0; ctl->used = 0;
+        ctl->tile_ctr = 0; ctl->used = 0;
         lengths[0] = n;
     }
 }
@@ -405,9 +407,10 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
 // Sweep of the global table for the maximum of the packed value
 // (count << 32 | ~key) over slots with a nonzero count: highest count, ties
 // to the smallest (left, right), whatever the order of the sweep. Each
-// workgroup publishes its maximum; the last workgroup of each group folds
-// its group's, and the last group to finish records the merge and sets up
-// the merge pass, or marks training done when no pair has a nonzero count.
+// workgroup stores its maximum in Sweep; the merge pass that follows takes
+// the maximum of those, records the merge, or marks training done when no
+// pair has a nonzero count. Workgroup 0 also records the iteration and the
+// tile counter's base for it.
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -425,41 +428,20 @@ __device__ __forceinline__ unsigned long long candidate(unsigned long long v) {
     return (v >> 32) ? (v ^ 0xFFFFFFFFull) : 0ull;
 }
 
-__device__ __forceinline__ unsigned long long ld64(const unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st64(unsigned long long* p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Record the merge of the maximum b (0: no pair left). One thread.
-__device__ __forceinline__ void choose(Ctl* ctl, unsigned long long b, uint32_t k, uint32_t* merges) {
-    if (b == 0ull) {
-        ctl->done = 1u;  // no countable pair is left
-        return;
-    }
-    const uint32_t key = ~(uint32_t)(b & 0xFFFFFFFFull);
-    const uint32_t cnt = (uint32_t)(b >> 32);
-    merges[3 * k + 0] = key >> 16;
-    merges[3 * k + 1] = key & IDM;
-    merges[3 * k + 2] = cnt;
-    ctl->L = key >> 16;
-    ctl->R = key & IDM;
-    ctl->X = BASE + k;
-    ctl->tile_ctr = 0u;
-    ctl->k = k + 1;
-}
-
 // U 16-byte loads in flight per thread; gridDim.x <= SWEEP_MAX_BLOCKS
 template <int TPB, int U>
 __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long long* __restrict__ table,
-                                                  uint32_t slots, Sweep* sw, uint32_t* merges) {
+                                                  uint32_t slots, Sweep* sw) {
     __shared__ unsigned long long s_best[TPB / 64];
     const uint32_t done = ld_relaxed(&ctl->done);
-    const uint32_t k = ld_relaxed(&ctl->k);
     const uint32_t m = ld_relaxed(&ctl->m);
     const uint32_t limit = ld_relaxed(&ctl->limit);
-    if (done || k != m || k >= limit) return;  // uniform over the grid
+    const bool active = !done && m < limit;  // uniform over the grid
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sw->iter = active ? m : NO_ITER;
+        sw->tile_base = ld_relaxed(&ctl->tile_ctr);  // no k_merge runs during the sweep
+    }
+    if (!active) return;
 
     // two slots per 16-byte load (slots is a power of two >= 1024)
     const ulonglong2* t2 = reinterpret_cast<const ulonglong2*>(table);
@@ -479,32 +461,12 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
     best = wave_max_u64(best);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) s_best[w] = best;
-    lds_barrier();
-    if (threadIdx.x != 0) return;
-    unsigned long long b = 0ull;
-    for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
-
-    const uint32_t G = gridDim.x, NG = min(G, SWEEP_GROUPS), g = blockIdx.x % NG;
-    const uint32_t members = (G - g + NG - 1) / NG;  // workgroups g, g + NG, ...
-    st64(sw->bmax + blockIdx.x, b);
-    __threadfence();
-    if (atomicAdd(sw->gcnt + 64 * g, 1u) != members - 1) return;
-    __hip_atomic_store(sw->gcnt + 64 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    for (uint32_t i = g; i < G; i += NG) {
-        const unsigned long long o = ld64(sw->bmax + i);
-        b = o > b ? o : b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long b = 0ull;
+        for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
+        sw->bmax[blockIdx.x] = b;
     }
-    st64(sw->gmax + 32 * g, b);
-    __threadfence();
-    if (atomicAdd(&ctl->sweep_done, 1u) != NG - 1) return;
-    ctl->sweep_done = 0u;
-    __threadfence();
-    for (uint32_t i = 0; i < NG; ++i) {
-        const unsigned long long o = ld64(sw->gmax + 32 * i);
-        b = o > b ? o : b;
-    }
-    choose(ctl, b, k, merges);
 }
 
 }  // namespace bpek

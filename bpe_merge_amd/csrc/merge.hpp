@@ -90,18 +90,37 @@ __device__ __forceinline__ bool st_valid(unsigned long long s, uint32_t epoch) {
 // up to the nearest prefix is published, and folds the aggregates in
 // between. The wait is bounded: past SPIN_LIMIT polls it records ERR_SPIN
 // and returns a zero prefix, so the kernel always finishes.
+// The status words of one window (tiles top - PL*lane - q); below tile 0 a
+// zero prefix. Every lane issues its PL loads (tile 0's word stands in for
+// indexes below 0), so that the number of loads is fixed.
+template <int PL>
+__device__ __forceinline__ void lookback_window(const unsigned long long* status, long long top, uint32_t epoch,
+                                                uint32_t lane, unsigned long long (&st)[PL]) {
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+        const long long idx = top - (long long)(PL * lane + q);
+        const unsigned long long v = st_load(status + (idx >= 0 ? idx : 0));
+        st[q] = (idx >= 0) ? v : st_pack(ST_PRE, epoch, 0u);
+    }
+}
+
+// first: the first window (tiles below t), already loaded by the caller
+// with lookback_window(status, t - 1, ...), so that its loads can be issued
+// ahead of other memory traffic.
 template <int PL>
 __device__ __forceinline__ void lookback(const unsigned long long* status, uint32_t t, uint32_t epoch,
-                                         uint32_t lane, Ctl* ctl, uint32_t& off, uint32_t& sel) {
+                                         uint32_t lane, Ctl* ctl, const unsigned long long (&first)[PL],
+                                         uint32_t& off, uint32_t& sel) {
     Span acc{0u, 0u, 0u, 1u};
     long long top = (long long)t - 1;
     uint32_t spins = 0;
-    for (;;) {
+    for (bool at_first = true;; at_first = false) {
         unsigned long long st[PL];
+        if (at_first) {
 #pragma unroll
-        for (int q = 0; q < PL; ++q) {
-            const long long idx = top - (long long)(PL * lane + q);
-            st[q] = (idx >= 0) ? st_load(status + idx) : st_pack(ST_PRE, epoch, 0u);
+            for (int q = 0; q < PL; ++q) st[q] = first[q];
+        } else {
+            lookback_window<PL>(status, top, epoch, lane, st);
         }
         int fq;          // this lane's first q holding a prefix (PL if none)
         uint32_t plane;  // first lane holding a prefix (64 if none)
@@ -254,14 +273,16 @@ __device__ __forceinline__ void load_tile(const uint32_t* __restrict__ in, uint3
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(in) + hb, 0, (int)(4u * (end - hb)), BUF_RSRC_FLAGS);
     const uint32_t g0 = ts + tid * 16u, o = 4u * (g0 - hb);
+    // the edge values first: the compiler can then wait for them without
+    // waiting for the 16-byte loads (one in-order counter)
+    h1 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 1u) ? o - 4u : BUF_OOB, 0, 0);
+    h2 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 8u : BUF_OOB, 0, 0);
+    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 64u : BUF_OOB, 0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
         x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
     }
-    h1 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 1u) ? o - 4u : BUF_OOB, 0, 0);
-    h2 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 8u : BUF_OOB, 0, 0);
-    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 64u : BUF_OOB, 0, 0);
 }
 
 // After load_tile: WS in place of every value outside [0, n), then the
@@ -361,6 +382,7 @@ __device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (
 __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, uint32_t it, uint32_t total) {
     ctl->n[(it + 1) & 1u] = total;
     lengths[it + 1] = total;
+    ctl->k = it + 1;
     __threadfence();
     atomicExch(&ctl->m, it + 1);
 }
@@ -386,7 +408,8 @@ template <int TPB, int LT>
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
                                                uint32_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
-                                               uint32_t* lengths) {
+                                               uint32_t* lengths, const Sweep* sw, uint32_t nsweep,
+                                               uint32_t* merges) {
     constexpr int V = 16;  // symbols per thread: four 16-byte loads
     constexpr int TILE = TPB * V;
     constexpr int NW = TPB / 64;
@@ -396,28 +419,62 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     __shared__ uint32_t s_stage[2 * SST];
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile[2], s_off[2], s_sel;
+    __shared__ unsigned long long s_best[NW];
 
-    const uint32_t k = ld_relaxed(&ctl->k);
-    const uint32_t it = ld_relaxed(&ctl->m);
-    if (it >= k) return;  // no merge pending (uniform)
-    const uint32_t L = ctl->L, R = ctl->R, X = ctl->X;
+    const uint32_t it = sw->iter;  // written by the sweep before this launch
+    if (it == NO_ITER) return;     // training has stopped (uniform)
     const uint32_t n = ctl->n[it & 1u];
     const uint32_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
     uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
     const uint32_t ntiles = (n + TILE - 1) / TILE;
     const uint32_t epoch = it + 1;
+    const uint32_t X = BASE + it;
     // X == 65535 is the last possible id: no later iteration reads counts,
     // and the pair (X, X) would collide with the empty key
     const bool do_count = X != IDM;
     const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+    uint32_t* tile_ctr = &ctl->tile_ctr;
+    const uint32_t tile_base = sw->tile_base;
+
+    // ---- the merge: the maximum of the sweep's per-workgroup maxima. These
+    // loads go first: waiting for them then does not wait for the tile's.
+    unsigned long long best = 0ull;
+    {
+        // nsweep <= SWEEP_MAX_BLOCKS = 2 * TPB
+        const unsigned long long b0 = tid < nsweep ? sw->bmax[tid] : 0ull;
+        const unsigned long long b1 = tid + TPB < nsweep ? sw->bmax[tid + TPB] : 0ull;
+        best = b0 > b1 ? b0 : b1;
+    }
+    static_assert(SWEEP_MAX_BLOCKS <= 2 * TPB, "two sweep maxima per thread");
 
     tab.clear(TPB);
-    if (tid == 0) s_tile[0] = atomicAdd(&ctl->tile_ctr, 1u);
+    if (tid == 0) s_tile[0] = atomicAdd(tile_ctr, 1u) - tile_base;
     lds_barrier();
     uint32_t t = s_tile[0];
     uint32_t x[V], h1, h2, hr;
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
     load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
+
+    best = wave_max_u64(best);
+    if (lane == 0) s_best[w] = best;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) best = s_best[i] > best ? s_best[i] : best;
+    if (best == 0ull) {  // uniform: no countable pair is left
+        if (blockIdx.x == 0 && tid == 0) ctl->done = 1u;
+        return;
+    }
+    // uniform: keep the merge in scalar registers
+    const uint32_t key = __builtin_amdgcn_readfirstlane(~(uint32_t)best);
+    const uint32_t L = key >> 16, R = key & IDM;
+    if (blockIdx.x == 0 && tid == 0) {
+        merges[3 * it + 0] = L;
+        merges[3 * it + 1] = R;
+        merges[3 * it + 2] = __builtin_amdgcn_readfirstlane((uint32_t)(best >> 32));
+        ctl->L = L;
+        ctl->R = R;
+        ctl->X = X;
+    }
 
     if (L != R) {
         // tp: the tile staged in the previous round, waiting for its offset
@@ -428,12 +485,13 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         // atomic waits for every older access of the wave (one counter), so
         // it is issued after the stores of a round and consumed in the next.
         uint32_t grab = 0;
-        if (tid == 0) grab = atomicAdd(&ctl->tile_ctr, 1u);
+        if (tid == 0) grab = atomicAdd(tile_ctr, 1u);
         // the loop-top waits count on the stores each round issues after its
         // loads; the first loads get the same six stores (nothing written)
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0;
+            unsigned long long lbw[4];
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
                 uint32_t a1, a2, b1;
@@ -452,7 +510,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     if (lane >= (uint32_t)o) incl += u;
                 }
                 if (lane == 63) s_wagg[w] = incl;
-                if (tid == 0) s_tile[round & 1u] = grab;
+                if (tid == 0) s_tile[round & 1u] = grab - tile_base;
                 lds_barrier();
                 uint32_t my_local = incl - kept;
 #pragma unroll
@@ -471,14 +529,17 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, occ, sel_in, a1, st, my_local,
                                       valid & ~occ, L, R, X);
                 }
-                // ---- the next tile's loads are in flight during the look-back and stores below
                 tn = s_tile[round & 1u];
-                load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             }
+            // ---- the previous tile's first look-back window, then the next
+            // tile's loads (an empty resource when there is none): both in
+            // flight together, the window first
+            if (w == 0) lookback_window<4>(status, (long long)min(tp, ntiles - 1u) - 1, epoch, lane, lbw);
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
-                if (tp != 0) lookback<4>(status, tp, epoch, lane, ctl, off, sel);
+                if (tp != 0) lookback<4>(status, tp, epoch, lane, ctl, lbw, off, sel);
                 if (lane == 0) {
                     st_store(status + tp, st_pack(ST_PRE, epoch, off + kp));
                     s_off[round & 1u] = off;
@@ -488,7 +549,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // the grab goes before the stores so that waiting for it later
             // does not wait for them; the stores are issued in every round
             // (all dropped when no tile is pending) to keep their count fixed
-            if (tid == 0 && tn < ntiles) grab = atomicAdd(&ctl->tile_ctr, 1u);
+            if (tid == 0 && tn < ntiles) grab = atomicAdd(tile_ctr, 1u);
             const uint32_t tile_off = tp < ntiles ? s_off[round & 1u] : 0u;
             store_tile<TPB, TILE>(out, s_stage + (cur ^ 1u) * SST, tile_off, tp < ntiles ? kp : 0u);
             if (tp == ntiles - 1 && tid == 0) finish_iteration(ctl, lengths, it, tile_off + kp);
@@ -545,7 +606,9 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                 uint32_t off = 0, sel = 0;
                 if (t != 0) {
                     if (lane == 0) st_store(status + t, st_pack(ST_AGG, epoch, tile_agg));
-                    lookback<4>(status, t, epoch, lane, ctl, off, sel);
+                    unsigned long long lbw[4];
+                    lookback_window<4>(status, (long long)t - 1, epoch, lane, lbw);
+                    lookback<4>(status, t, epoch, lane, ctl, lbw, off, sel);
                 }
                 if (lane == 0) {
                     const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
@@ -579,7 +642,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             }
 
             // ---- next tile, then write this one
-            if (tid == 0) s_tile[round & 1u] = atomicAdd(&ctl->tile_ctr, 1u);
+            if (tid == 0) s_tile[round & 1u] = atomicAdd(tile_ctr, 1u) - tile_base;
             lds_barrier();
             const uint32_t tn = s_tile[round & 1u];
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
