@@ -491,7 +491,11 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0;
+            // the previous tile's first look-back window, issued before
+            // anything else of the round so that it has arrived by the time
+            // wave 0 examines it
             unsigned long long lbw[4];
+            if (w == 0) lookback_window<4>(status, (long long)min(tp, ntiles - 1u) - 1, epoch, lane, lbw);
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
                 uint32_t a1, a2, b1;
@@ -531,10 +535,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                 }
                 tn = s_tile[round & 1u];
             }
-            // ---- the previous tile's first look-back window, then the next
-            // tile's loads (an empty resource when there is none): both in
-            // flight together, the window first
-            if (w == 0) lookback_window<4>(status, (long long)min(tp, ntiles - 1u) - 1, epoch, lane, lbw);
+            // ---- the next tile's loads (an empty resource when there is none)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
