@@ -98,7 +98,8 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     a = align_up(a + 4 * sym_elems, 256);
     L.table = a;
     a = align_up(a + 8 * (size_t(1) << tlog2), 256);
-    L.max_tiles = uint32_t((n + TILE - 1) / TILE) + 1;
+    // at least 512 words: the look-back copies a 512-word window from index 0
+    L.max_tiles = std::max<uint32_t>(uint32_t((n + TILE - 1) / TILE) + 1, 512);
     L.status = a;
     a = align_up(a + 8 * size_t(L.max_tiles), 256);
     L.merges = a;

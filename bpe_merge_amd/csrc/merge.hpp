@@ -105,12 +105,17 @@ __device__ __forceinline__ void lookback_window(const unsigned long long* status
 }
 
 // first: the first window (tiles below t), already loaded by the caller
-// with lookback_window(status, t - 1, ...), so that its loads can be issued
-// ahead of other memory traffic.
+// (from global memory with lookback_window(status, t - 1, ...), or from
+// lwin), so that its loads can be issued ahead of other memory traffic.
+// lwin, if given, is an earlier copy of status words [lbase, lbase + nwin)
+// in LDS; later windows that lie inside it are read from there. A stale
+// copy is fine: a word only ever moves from invalid to aggregate to prefix
+// within an epoch, and invalid words are read again from global memory.
 template <int PL>
 __device__ __forceinline__ void lookback(const unsigned long long* status, uint32_t t, uint32_t epoch,
                                          uint32_t lane, Ctl* ctl, const unsigned long long (&first)[PL],
-                                         uint32_t& off, uint32_t& sel) {
+                                         uint32_t& off, uint32_t& sel, const unsigned long long* lwin = nullptr,
+                                         long long lbase = 0, long long nwin = 0) {
     Span acc{0u, 0u, 0u, 1u};
     long long top = (long long)t - 1;
     uint32_t spins = 0;
@@ -119,6 +124,9 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
         if (at_first) {
 #pragma unroll
             for (int q = 0; q < PL; ++q) st[q] = first[q];
+        } else if (lwin && top - (64 * PL - 1) >= lbase && top < lbase + nwin) {
+#pragma unroll
+            for (int q = 0; q < PL; ++q) st[q] = lwin[top - (long long)(PL * lane + q) - lbase];
         } else {
             lookback_window<PL>(status, top, epoch, lane, st);
         }
@@ -387,6 +395,16 @@ __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, ui
     atomicExch(&ctl->m, it + 1);
 }
 
+// Look-back of the pipelined path: windows of 64 * LB_PL status words; the
+// LB_WIN words below the tile (two windows) are copied to LDS by
+// global_load_lds.
+constexpr int LB_PL = 4;
+constexpr int LB_WIN = 2 * 64 * LB_PL;
+constexpr int LDS_DMA_SC1 = 16;  // cache policy sc1: agent-coherent, like st_load
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 7, expcnt and lgkmcnt untouched
+constexpr int WAIT_VM7 = 0x0F77;
+static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
+
 // One persistent pass per iteration. Workgroups take 8192-symbol tiles from
 // a counter, in order, so every tile a look-back waits for is held by a
 // running workgroup that has already published or is about to publish its
@@ -420,6 +438,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile[2], s_off[2], s_sel;
     __shared__ unsigned long long s_best[NW];
+    __shared__ __align__(16) unsigned long long s_win[LB_WIN];
 
     const uint32_t it = sw->iter;  // written by the sweep before this launch
     if (it == NO_ITER) return;     // training has stopped (uniform)
@@ -491,11 +510,19 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0;
-            // the previous tile's first look-back window, issued before
-            // anything else of the round so that it has arrived by the time
-            // wave 0 examines it
-            unsigned long long lbw[4];
-            if (w == 0) lookback_window<4>(status, (long long)min(tp, ntiles - 1u) - 1, epoch, lane, lbw);
+            // the previous tile's first look-back window (the 512 status
+            // words below it), copied straight into LDS before anything else
+            // of the round, so that it has arrived by the time wave 0
+            // examines it and occupies no registers meanwhile
+            const long long lb_top = (long long)tp - 1;
+            const long long lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
+            if (w == 0 && tp < ntiles && tp != 0) {
+#pragma unroll
+                for (int q = 0; q < LB_WIN / 128; ++q)
+                    __builtin_amdgcn_global_load_lds(status + lb_base + 2 * (lane + 64 * q),
+                                                     (__attribute__((address_space(3))) void*)(s_win + 128 * q),
+                                                     16, 0, LDS_DMA_SC1);
+            }
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
                 uint32_t a1, a2, b1;
@@ -540,7 +567,19 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
-                if (tp != 0) lookback<4>(status, tp, epoch, lane, ctl, lbw, off, sel);
+                if (tp != 0) {
+                    // the window's copies are older than the seven loads of
+                    // load_tile above: all but the last seven accesses done
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM7);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    unsigned long long lbw[LB_PL];
+#pragma unroll
+                    for (int q = 0; q < LB_PL; ++q) {
+                        const long long idx = lb_top - (long long)(LB_PL * lane + q);
+                        lbw[q] = idx >= 0 ? s_win[idx - lb_base] : st_pack(ST_PRE, epoch, 0u);
+                    }
+                    lookback<LB_PL>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
+                }
                 if (lane == 0) {
                     st_store(status + tp, st_pack(ST_PRE, epoch, off + kp));
                     s_off[round & 1u] = off;
