@@ -7,6 +7,8 @@ benchmark's CPU-baseline leg, never by the GPU library or its binding.
 * ``train_literal``  - oracle A in plain C: full recount every iteration.
 * ``train_chunks``   - oracle B in plain C: the same result computed on the
                         multiset of distinct chunks with incremental counts.
+* ``encode``         - the encoder in plain C: a merge list applied in order
+                        (``reference.encode`` is the same in Python).
 
 All three return ``(merges, tokens, lengths)``: merges is an int64 array of
 shape [k, 3] (left, right, count; merge i creates id 256 + i), tokens a
@@ -57,6 +59,8 @@ def _load():
         lib.oracle_char_class.restype = ctypes.c_uint32
         lib.oracle_tag.argtypes = [vp, ctypes.c_uint64, vp]
         lib.oracle_tag.restype = None
+        lib.oracle_encode.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint32, vp, vp, vp]
+        lib.oracle_encode.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -116,3 +120,26 @@ def train_python(data, n_merges: int):
     merges, toks = reference.train(bytes(_as_u8(data)), n_merges, lengths)
     return (np.array(merges, dtype=np.int64).reshape(-1, 3), np.array(toks, dtype=np.uint32),
             np.array(lengths, dtype=np.int64))
+
+
+def encode(data, pairs):
+    """The encoder in C: ``pairs`` is [k, 2] (left, right) or [k, 3] (a
+    merge list with counts; the counts are ignored). Returns (counts,
+    tokens): counts[k] = occurrences of pair k just before merge k."""
+    b = _as_u8(data)
+    p = np.asarray(pairs, dtype=np.int64)
+    p = p.reshape(0, 2) if p.size == 0 else p.reshape(p.shape[0], -1)
+    p = np.ascontiguousarray(p[:, :2], dtype=np.uint32)
+    k = p.shape[0]
+    if k > MAX_MERGES:
+        raise ValueError("at most %d merges" % MAX_MERGES)
+    counts = np.zeros(max(k, 1), dtype=np.uint32)
+    tokens = np.empty(max(b.size, 1), dtype=np.uint32)
+    n_tok = ctypes.c_uint64(0)
+    rc = _load().oracle_encode(b.ctypes.data if b.size else None, b.size, p.ctypes.data if k else None, k,
+                               counts.ctypes.data, tokens.ctypes.data, ctypes.addressof(n_tok))
+    if rc == -1:
+        raise ValueError("bad merge list (an id that does not exist yet)")
+    if rc != 0:
+        raise RuntimeError("oracle failed with code %d" % rc)
+    return counts[:k].astype(np.int64), tokens[: n_tok.value]

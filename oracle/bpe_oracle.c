@@ -31,7 +31,15 @@
  *                          merged pair, and a lazy max-heap for the argmax.
  *                          Pinned to the literal oracle by tests.
  *
- * Outputs of both:
+ * And the encoder of the same method (text encoded with a learned merge
+ * list, "Nedir bu ya?"):
+ *   oracle_encode        - tag, then apply merge k = pairs[2k], pairs[2k+1]
+ *                          (new id 256 + k) over the whole sequence, k in
+ *                          order, each exactly as a training iteration
+ *                          applies its pair; counts[k] = occurrences of the
+ *                          pair just before merge k. O(n * merges).
+ *
+ * Outputs of both trainers:
  *   merges[3k+0..2] = left, right, count of merge k (new id 256 + k)
  *   tokens[0..*n_tokens) = final symbols, id | 0x10000 on chunk starts
  *   lengths[k] = sequence length before merge k, lengths[*n_done] = final
@@ -511,4 +519,42 @@ out:
     if (ch) for (uint32_t c = 0; c < nch; c++) free(ch[c].sym);
     free(ch); free(first); free(blen); free(seq);
     return rc;
+}
+
+/* ======================================================================== */
+/* encoder                                                                   */
+
+int oracle_encode(const uint8_t *b, uint64_t n, const uint32_t *pairs, uint32_t n_merges, uint32_t *counts,
+                  uint32_t *tokens, uint64_t *n_tokens) {
+    if ((!b && n) || (!pairs && n_merges) || !n_tokens || n_merges > O_MAX_MERGES) return -1;
+    for (uint32_t k = 0; k < n_merges; k++)
+        if (pairs[2 * k] >= O_BASE + k || pairs[2 * k + 1] >= O_BASE + k) return -1;
+    uint32_t *s = (uint32_t *)malloc(sizeof(uint32_t) * (n ? n : 1));
+    uint32_t *t = (uint32_t *)malloc(sizeof(uint32_t) * (n ? n : 1));
+    if (!s || !t) { free(s); free(t); return -2; }
+    oracle_tag(b, n, s);
+    uint64_t len = n;
+    for (uint32_t k = 0; k < n_merges; k++) {
+        const uint32_t L = pairs[2 * k], R = pairs[2 * k + 1], X = O_BASE + k;
+        uint32_t c = 0;
+        for (uint64_t i = 1; i < len; i++)
+            if (!(s[i] & O_WS) && (s[i - 1] & O_ID) == L && (s[i] & O_ID) == R) c++;
+        if (counts) counts[k] = c;
+        uint64_t o = 0;
+        for (uint64_t i = 0; i < len;) {
+            if (i + 1 < len && !(s[i + 1] & O_WS) && (s[i] & O_ID) == L && (s[i + 1] & O_ID) == R) {
+                t[o++] = X | (s[i] & O_WS);
+                i += 2;
+            } else {
+                t[o++] = s[i];
+                i += 1;
+            }
+        }
+        uint32_t *tmp = s; s = t; t = tmp;
+        len = o;
+    }
+    *n_tokens = len;
+    if (tokens) memcpy(tokens, s, sizeof(uint32_t) * len);
+    free(s); free(t);
+    return 0;
 }

@@ -18,6 +18,8 @@ llm.istanbul/learn/tr/13_bpe):
   pairs are counted again on every iteration, then a deterministic maximum
   is taken.
 * "Ne Yapar? section 3": the merged symbol carries WORD_START_BIT.
+* "Nedir bu ya?" again, for encoding: text is encoded with a learned merge
+  list by applying its merges in the order they were learned.
 
 Readings where the page is silent (each one also listed in the design notes):
   - position 0 carries WORD_START_BIT (the first symbol starts a word);
@@ -134,3 +136,21 @@ def train(data: bytes, n_merges: int, lengths: list[int] | None = None):
     if lengths is not None:
         lengths.append(len(s))
     return merges, s
+
+
+def encode(data: bytes, pairs):
+    """Encode data with a merge list: tag it, then apply merge k (the pair
+    pairs[k] = (left, right), new id 256 + k) over the whole sequence for
+    k = 0, 1, ... in order, each exactly as a training iteration applies
+    its chosen pair. Returns (counts, tokens): counts[k] is the number of
+    adjacent positions holding pairs[k] just before merge k (0 if none),
+    tokens the final symbols. A pair naming an id that does not exist yet
+    (>= 256 + k) is an error."""
+    s = tag(bytes(data))
+    counts = []
+    for k, (left, right) in enumerate(pairs):
+        if not (0 <= left < BASE + k and 0 <= right < BASE + k):
+            raise ValueError("merge %d names an id that does not exist yet" % k)
+        counts.append(count_pairs(s).get((left, right), 0))
+        s = merge_pair(s, left, right, BASE + k)
+    return counts, s
