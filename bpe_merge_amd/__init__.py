@@ -68,6 +68,8 @@ _SIGS = {
     "bpe_lengths": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
     "bpe_pair_counts": (ctypes.c_int, [_vp, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp, _vp]),
+    "bpe_replay": (ctypes.c_int, [_vp, _vp, _u32]),
+    "bpe_encode": (ctypes.c_int, [_vp, _sz, _vp, _u32, _cfgp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "bpe_last_error": (ctypes.c_char_p, []),
@@ -149,6 +151,42 @@ def train(data, n_merges: int, table_log2: int | None = None):
     return merges[: n_done.value], tokens[: n_tok.value]
 
 
+def _merge_list(merges, device):
+    """A [k, 2] or [k, 3] merge list as a contiguous int32 [k, 3] CUDA tensor
+    (bpe_merge layout: left, right, count; the count is not read)."""
+    torch = _torch()
+    m = torch.as_tensor(merges)
+    if m.numel() == 0:
+        m = m.reshape(0, 3)
+    if m.dim() != 2 or m.shape[1] not in (2, 3):
+        raise ValueError("merges must have shape [k, 2] or [k, 3]")
+    if m.shape[1] == 2:
+        m = torch.cat([m, torch.zeros((m.shape[0], 1), dtype=m.dtype, device=m.device)], dim=1)
+    return m.to(device=device, dtype=torch.int32).contiguous()
+
+
+def encode(data, merges, table_log2: int | None = None):
+    """bpe_encode on a uint8 CUDA tensor with a merge list ([k, 2] or [k, 3];
+    merge i creates id 256 + i). Returns the int32 CUDA tensor of final
+    symbols (id | 0x10000 on word starts)."""
+    torch = _torch()
+    if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+        raise TypeError("data must be a uint8 CUDA tensor")
+    data = data.contiguous().reshape(-1)
+    n = data.numel()
+    dev = data.device
+    m = _merge_list(merges, dev)
+    tokens = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if n == 0:
+        return tokens[:0]
+    ws = _workspace(n, table_log2, dev)
+    cfg = _config(table_log2, _stream_handle(dev), ws)
+    n_tok = _sz(0)
+    _check(_lib.bpe_encode(data.data_ptr(), n, m.data_ptr(), m.shape[0], ctypes.byref(cfg), tokens.data_ptr(),
+                           tokens.numel(), ctypes.byref(n_tok)), "bpe_encode")
+    return tokens[: n_tok.value]
+
+
 class State:
     """bpe_init ... bpe_free on a uint8 CUDA tensor, with a torch workspace."""
 
@@ -177,6 +215,12 @@ class State:
         m = Merge()
         st = _check(_lib.bpe_step(self._h, ctypes.byref(m)), "bpe_step")
         return None if st == DONE else (m.left, m.right, m.count)
+
+    def replay(self, merges) -> None:
+        """bpe_replay: apply a merge list ([k, 2] or [k, 3]) as the next k
+        iterations; training can continue afterwards."""
+        m = _merge_list(merges, self.device)
+        _check(_lib.bpe_replay(self._h, m.data_ptr(), m.shape[0]), "bpe_replay")
 
     def merges(self):
         torch = _torch()

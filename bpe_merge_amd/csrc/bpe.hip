@@ -80,7 +80,7 @@ size_t grid_bound(size_t n) { return (n + TILE - 1) / TILE + 1; }
 uint32_t table_limit(uint32_t tlog2) { return uint32_t((1ull << tlog2) - (1ull << tlog2) / 8); }
 
 struct Layout {
-    size_t ctl, sweep, sym0, sym1, table, status, merges, lengths, total;
+    size_t ctl, sweep, sym0, sym1, table, status, merges, lengths, fpairs, total;
     uint32_t max_tiles;
 };
 
@@ -106,6 +106,8 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     a = align_up(a + 12 * size_t(BPE_MAX_MERGES), 256);
     L.lengths = a;
     a = align_up(a + 4 * (size_t(BPE_MAX_MERGES) + 1), 256);
+    L.fpairs = a;  // pairs of replayed iterations, indexed by iteration
+    a = align_up(a + 8 * size_t(BPE_MAX_MERGES), 256);
     L.total = a;
     return L;
 }
@@ -157,6 +159,7 @@ struct bpe_state {
     unsigned long long* status = nullptr;
     uint32_t* merges = nullptr;
     uint32_t* lengths = nullptr;
+    uint32_t* fpairs = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
     int merge_grid = 0, tag_grid = 0, fill_grid = 0, find_grid = 0;
     bool poisoned = false;   // a device error was seen
@@ -176,6 +179,10 @@ void launch_merge(bpe_state* s) {
     hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0, s->stream,
                        s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
                        uint32_t(s->find_grid), s->merges);
+}
+
+void launch_force(bpe_state* s) {
+    hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(64), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs);
 }
 
 bpe_status launch_iteration(bpe_state* s) {
@@ -328,6 +335,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->status = reinterpret_cast<unsigned long long*>(base + lay.status);
     s->merges = reinterpret_cast<uint32_t*>(base + lay.merges);
     s->lengths = reinterpret_cast<uint32_t*>(base + lay.lengths);
+    s->fpairs = reinterpret_cast<uint32_t*>(base + lay.fpairs);
 
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, s->device);
@@ -577,6 +585,61 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res,
     return st;
 }
 
+bpe_status bpe_replay(bpe_state* s, const bpe_merge* merges, uint32_t k) {
+    g_err.clear();
+    if (!s || (!merges && k)) {
+        set_err("state must be non-NULL, and merges non-NULL when k > 0");
+        return BPE_EINVAL;
+    }
+    if (s->poisoned) {
+        set_err("the state holds a device error from an earlier call");
+        return BPE_ESTATE;
+    }
+    HIP_TRY(hipSetDevice(s->device));
+    Ctl h;
+    bpe_status st = read_ctl(s, &h);
+    if (st != BPE_OK) return st;
+    if (k == 0) return BPE_OK;
+    if (h.done) {
+        set_err("training on this state has stopped; nothing can be replayed");
+        return BPE_ESTATE;
+    }
+    const uint32_t m0 = h.k;
+    if (size_t(m0) + k > BPE_MAX_MERGES) {
+        set_err("%u + %u merges exceed the id space (%u merges)", m0, k, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    std::vector<bpe_merge> hm(k);
+    HIP_TRY(hipMemcpy(hm.data(), merges, sizeof(bpe_merge) * size_t(k), hipMemcpyDefault));
+    std::vector<uint32_t> pairs(2 * size_t(k));
+    for (uint32_t i = 0; i < k; ++i) {
+        const uint32_t lim = bpek::BASE + m0 + i;  // ids that exist before merge m0 + i
+        if (hm[i].left >= lim || hm[i].right >= lim) {
+            set_err("merge %u (%u, %u) names an id that does not exist before it (ids < %u)", m0 + i,
+                    hm[i].left, hm[i].right, lim);
+            return BPE_EINVAL;
+        }
+        pairs[2 * i] = hm[i].left;
+        pairs[2 * i + 1] = hm[i].right;
+    }
+    HIP_TRY(hipMemcpyAsync(s->fpairs + 2 * size_t(m0), pairs.data(), 4 * pairs.size(), hipMemcpyHostToDevice,
+                           s->stream));
+    s->requested = m0 + k;
+    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->requested);
+    for (uint32_t i = 0; i < k; ++i) {
+        launch_force(s);
+        launch_merge(s);
+    }
+    HIP_TRY(hipGetLastError());
+    st = read_ctl(s, &h);  // also keeps pairs alive until the copy has run
+    if (st != BPE_OK) return st;
+    if (h.k != m0 + k) {
+        set_err("replay stopped after %u of %u merges", h.k - m0, k);
+        return BPE_ESTATE;
+    }
+    return BPE_OK;
+}
+
 void bpe_free(bpe_state* s) {
     if (!s) return;
     (void)hipSetDevice(s->device);
@@ -615,6 +678,33 @@ bpe_status bpe_train(const uint8_t* bytes, size_t n, uint32_t n_merges, const bp
     if (st == BPE_OK && done) st = bpe_merges(s, merges, done, nullptr);
     if (st == BPE_OK && (tokens || n_tokens)) st = bpe_tokens(s, tokens, tokens ? tokens_cap : 0, n_tokens);
     if (st == BPE_OK) *n_done = done;
+    bpe_free(s);
+    return st;
+}
+
+bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, uint32_t n_merges,
+                      const bpe_config* cfg, uint32_t* tokens, size_t tokens_cap, size_t* n_tokens) {
+    g_err.clear();
+    if (!n_tokens || (!merges && n_merges) || (n && !bytes)) {
+        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_tokens must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    if (!config_ok(n, cfg)) return BPE_EINVAL;
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    bpe_state* s = nullptr;
+    bpe_status st = bpe_init(bytes, n, cfg, &s);
+    if (st != BPE_OK) return st;
+    st = bpe_replay(s, merges, n_merges);
+    if (st == BPE_OK) st = bpe_tokens(s, tokens, tokens ? tokens_cap : 0, n_tokens);
     bpe_free(s);
     return st;
 }

@@ -69,10 +69,15 @@ struct alignas(64) Ctl {
 // it even if one starts after the last tile was written.
 constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;
 constexpr uint32_t NO_ITER = 0xFFFFFFFFu;
+// A replayed iteration (k_force) instead names its merge: forced = 1,
+// fkey = left << 16 | right, fcount = the pair's current count.
 struct Sweep {
     unsigned long long bmax[SWEEP_MAX_BLOCKS];
     uint32_t iter;
     uint32_t tile_base;
+    uint32_t forced;
+    uint32_t fkey;
+    uint32_t fcount;
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -440,6 +445,7 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sw->iter = active ? m : NO_ITER;
         sw->tile_base = ld_relaxed(&ctl->tile_ctr);  // no k_merge runs during the sweep
+        sw->forced = 0u;
     }
     if (!active) return;
 
@@ -467,6 +473,41 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
         for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
         sw->bmax[blockIdx.x] = b;
     }
+}
+
+// ---------------------------------------------------------------- replay
+// A replayed iteration: the merge is the given pair pairs[2m], pairs[2m+1]
+// for iteration m (a learned merge list applied in order, "Nedir bu ya?"),
+// not the table's maximum. Its count is looked up in the table (0 if the
+// pair does not occur; the merge pass then changes nothing but still uses
+// up id 256 + m). One thread.
+
+__device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
+    uint32_t h = mix32(key) & gt.mask;
+    for (uint32_t p = 0; p < GT_PROBES; ++p) {
+        const unsigned long long v =
+            __hip_atomic_load(gt.slot + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t cur = (uint32_t)v;
+        if (cur == key) return (uint32_t)(v >> 32);
+        if (cur == EMPTY) return 0u;
+        h = (h + 1) & gt.mask;
+    }
+    return 0u;
+}
+
+__global__ void k_force(Ctl* ctl, GTable gt, Sweep* sw, const uint32_t* __restrict__ pairs) {
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    const uint32_t done = ld_relaxed(&ctl->done);
+    const uint32_t m = ld_relaxed(&ctl->m);
+    const uint32_t limit = ld_relaxed(&ctl->limit);
+    const bool active = !done && m < limit;
+    sw->iter = active ? m : NO_ITER;
+    sw->tile_base = ld_relaxed(&ctl->tile_ctr);
+    sw->forced = 1u;
+    if (!active) return;
+    const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
+    sw->fkey = key;
+    sw->fcount = gt_count(gt, key);
 }
 
 }  // namespace bpek

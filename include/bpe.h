@@ -145,6 +145,33 @@ bpe_status bpe_lengths(bpe_state *s, uint32_t *out, uint32_t cap, uint32_t *n_ou
    0 only the number is returned, with cap below it BPE_EINVAL. */
 bpe_status bpe_pair_counts(bpe_state *s, uint32_t *keys, uint32_t *counts, size_t cap, size_t *n_out);
 
+/* Apply a given merge list as the state's next k iterations, in order
+   (page "bpe - GPU BPE Tokenizer Pipeline", "Nedir bu ya?": a learned merge
+   list is the tokenizer; its merges are applied in the order they were
+   learned). Iteration m = (merges made so far) + i merges the pair
+   (merges[i].left, merges[i].right) into the new id 256 + m exactly as a
+   training iteration merges its chosen pair (left to right, non-
+   overlapping, never across the word-start bit), and keeps the pair counts
+   up to date, so training can go on afterwards (bpe_run / bpe_step): this
+   is resume by replaying a saved merge list. The count recorded for each
+   replayed merge is the pair's count just before it (0 if it does not
+   occur; the merge then changes nothing but still uses up its id).
+   merges: k entries, host or device, caller-owned; only left and right are
+   read. Blocks until the k iterations are done.
+   Errors: BPE_EINVAL (NULL pointers, or a pair naming an id >= 256 + m,
+   which does not exist yet; nothing is applied), BPE_EIDSPACE (the ids run
+   out), BPE_ESTATE (training on this state has stopped, or a device
+   error), BPE_ETABLE, BPE_EHIP. */
+bpe_status bpe_replay(bpe_state *s, const bpe_merge *merges, uint32_t k);
+
+/* Encode bytes[0..n) with a learned merge list: bpe_init, bpe_replay of all
+   n_merges merges, then the final symbols (id | 0x10000 on word starts) to
+   tokens (host or device, capacity tokens_cap >= n, or NULL to get only
+   the length in *n_tokens). Equal to training's tokens when the list was
+   learned on the same bytes. Errors as bpe_init and bpe_replay. */
+bpe_status bpe_encode(const uint8_t *bytes, size_t n, const bpe_merge *merges, uint32_t n_merges,
+                      const bpe_config *cfg, uint32_t *tokens, size_t tokens_cap, size_t *n_tokens);
+
 /* Per-kernel device time of the iterations run by bpe_profile. */
 typedef struct {
     double find_max_ms;      /* total time of the table sweep + argmax launches      */

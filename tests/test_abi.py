@@ -120,3 +120,23 @@ def test_binding_has_no_fallback(bpe):
     src = open(os.path.join(ROOT, "bpe_merge_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("oracle/", "")
     assert "import corpus" not in src
+
+
+def test_encode_and_replay_argument_validation_before_any_device_call(bpe):
+    lib = bpe._lib
+    buf = (ctypes.c_uint8 * 16)()
+    merges = (ctypes.c_uint32 * 3 * 4)()
+    n_tok = ctypes.c_size_t(5)
+    assert lib.bpe_replay(None, ctypes.addressof(merges), 1) == bpe.EINVAL
+    # null bytes with n > 0, null merges with n_merges > 0, null n_tokens
+    assert lib.bpe_encode(None, 16, ctypes.addressof(merges), 1, None, None, 0, ctypes.byref(n_tok)) == bpe.EINVAL
+    assert lib.bpe_encode(ctypes.addressof(buf), 16, None, 1, None, None, 0, ctypes.byref(n_tok)) == bpe.EINVAL
+    assert lib.bpe_encode(ctypes.addressof(buf), 16, ctypes.addressof(merges), 1, None, None, 0, None) == bpe.EINVAL
+    assert lib.bpe_encode(ctypes.addressof(buf), 16, ctypes.addressof(merges), 65281, None, None, 0,
+                          ctypes.byref(n_tok)) == bpe.EIDSPACE
+    toks = (ctypes.c_uint32 * 8)()
+    assert lib.bpe_encode(ctypes.addressof(buf), 16, ctypes.addressof(merges), 1, None, ctypes.addressof(toks), 8,
+                          ctypes.byref(n_tok)) == bpe.EINVAL          # capacity below n
+    # an empty text is valid and needs no device
+    assert lib.bpe_encode(None, 0, ctypes.addressof(merges), 1, None, None, 0, ctypes.byref(n_tok)) == bpe.OK
+    assert n_tok.value == 0

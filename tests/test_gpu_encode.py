@@ -1,0 +1,101 @@
+"""GPU parity of the encoder and of resume by merge-list replay (the HIP
+path through the C ABI against the oracle). Bit-exact: all work is integer."""
+import numpy as np
+import pytest
+
+import corpus
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bpe():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bpe_merge_amd
+    return bpe_merge_amd
+
+
+def _dev(data):
+    import torch
+    return torch.from_numpy(np.array(data, dtype=np.uint8)).to("cuda:0")
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_encoding_the_training_corpus_gives_training_tokens(bpe):
+    d = corpus.generate(corpus.CONFIGS[3].scaled(600_000, seed=41))
+    _say("encode training corpus")
+    gm, gt = bpe.train(_dev(d), 150, 19)
+    tokens = bpe.encode(_dev(d), gm, 19)
+    assert np.array_equal(_np(tokens).astype(np.uint32), _np(gt).astype(np.uint32))
+    _, ot = oracle.encode(d, _np(gm))
+    assert np.array_equal(_np(tokens).astype(np.uint32), ot)
+
+
+@pytest.mark.parametrize("c", [1, 2, 4, 5])
+@pytest.mark.parametrize("n", [1, 3, 8191, 8193, 70_001])
+def test_encode_new_text_matches_oracle(bpe, c, n):
+    learn = corpus.generate(corpus.CONFIGS[c].scaled(50_000, seed=300 + c))
+    om, _, _ = oracle.train_chunks(learn, 90)
+    text = corpus.generate(corpus.CONFIGS[c].scaled(n, seed=400 + c + n))
+    _, ot = oracle.encode(text, om)
+    _say("encode new text c=%d n=%d" % (c, n))
+    gt = _np(bpe.encode(_dev(text), om, 18)).astype(np.uint32)
+    assert np.array_equal(gt, ot), (c, n)
+
+
+@pytest.mark.parametrize("k", [0, 1, 60, 120])
+def test_replay_then_train_equals_training_straight_through(bpe, k):
+    d = corpus.generate(corpus.CONFIGS[5].scaled(400_000, seed=52))
+    _say("replay k=%d" % k)
+    gm, gt = bpe.train(_dev(d), 120, 20)
+    with bpe.State(_dev(d), table_log2=20) as st:
+        st.replay(gm[:k])
+        mk = _np(st.merges())
+        assert np.array_equal(mk, _np(gm)[:k])      # counts recorded as in training
+        st.run(120 - k)
+        st.sync()
+        assert np.array_equal(_np(st.merges()), _np(gm))
+        assert np.array_equal(_np(st.tokens()), _np(gt))
+        k2, c2 = st.pair_counts()
+    # the count table after replay and training equals a recount of the result
+    s = _np(gt).astype(np.int64)
+    ok = (s[1:] & 0x10000) == 0
+    keys = ((s[:-1] & 0xFFFF) << 16 | (s[1:] & 0xFFFF))[ok]
+    u, c = np.unique(keys, return_counts=True)
+    assert np.array_equal(np.asarray(k2, dtype=np.int64), u) and np.array_equal(np.asarray(c2, dtype=np.int64), c)
+
+
+def test_replay_of_absent_pairs_and_runs(bpe):
+    # runs of identical bytes (L == R merges) and pairs that never occur:
+    # an absent pair records count 0, changes nothing, and uses up its id
+    d = np.array(list(b"aaaaaaa bbbb aaab ab ") * 3000, dtype=np.uint8)
+    merges = np.array([[97, 97, 0], [120, 121, 0], [256, 256, 0], [256, 97, 0], [98, 98, 0], [259, 98, 0]])
+    oc, ot = oracle.encode(d, merges)
+    _say("replay absent pairs and runs")
+    with bpe.State(_dev(d), table_log2=16) as st:
+        st.replay(merges)
+        gm = _np(st.merges())
+        assert np.array_equal(gm[:, :2], merges[:, :2]) and np.array_equal(gm[:, 2], oc)
+        assert np.array_equal(_np(st.tokens()).astype(np.uint32), ot)
+
+
+def test_replay_rejects_an_unknown_id_and_the_state_stays_usable(bpe):
+    d = corpus.generate(corpus.CONFIGS[1].scaled(20_000, seed=61))
+    _say("replay rejection")
+    with bpe.State(_dev(d), table_log2=17) as st:
+        with pytest.raises(RuntimeError):
+            st.replay(np.array([[97, 98], [300, 97]]))   # id 300 cannot exist before merge 1
+        st.run(10)
+        st.sync()
+        om, ot, _ = oracle.train_chunks(d, 10)
+        assert np.array_equal(_np(st.merges()).astype(np.int64), om)
+        assert np.array_equal(_np(st.tokens()).astype(np.uint32), ot)
