@@ -182,7 +182,8 @@ void launch_merge(bpe_state* s) {
 }
 
 void launch_force(bpe_state* s) {
-    hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(64), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs);
+    hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(bpek::FORCE_TPB), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs,
+                       uint32_t(s->find_grid));
 }
 
 bpe_status launch_iteration(bpe_state* s) {

@@ -69,15 +69,10 @@ struct alignas(64) Ctl {
 // it even if one starts after the last tile was written.
 constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;
 constexpr uint32_t NO_ITER = 0xFFFFFFFFu;
-// A replayed iteration (k_force) instead names its merge: forced = 1,
-// fkey = left << 16 | right, fcount = the pair's current count.
 struct Sweep {
     unsigned long long bmax[SWEEP_MAX_BLOCKS];
     uint32_t iter;
     uint32_t tile_base;
-    uint32_t forced;
-    uint32_t fkey;
-    uint32_t fcount;
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -445,7 +440,6 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sw->iter = active ? m : NO_ITER;
         sw->tile_base = ld_relaxed(&ctl->tile_ctr);  // no k_merge runs during the sweep
-        sw->forced = 0u;
     }
     if (!active) return;
 
@@ -478,9 +472,12 @@ __global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long 
 // ---------------------------------------------------------------- replay
 // A replayed iteration: the merge is the given pair pairs[2m], pairs[2m+1]
 // for iteration m (a learned merge list applied in order, "Nedir bu ya?"),
-// not the table's maximum. Its count is looked up in the table (0 if the
-// pair does not occur; the merge pass then changes nothing but still uses
-// up id 256 + m). One thread.
+// not the table's maximum. It takes the sweep's place: the pair, with its
+// count looked up in the table, becomes the only nonzero per-workgroup
+// maximum, so the merge pass picks it through its ordinary reduction (the
+// value is never 0 since ~key != 0 for 16-bit ids, so a pair that does not
+// occur still counts as a merge: count 0, nothing changes, id 256 + m is
+// used up).
 
 __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     uint32_t h = mix32(key) & gt.mask;
@@ -495,19 +492,29 @@ __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     return 0u;
 }
 
-__global__ void k_force(Ctl* ctl, GTable gt, Sweep* sw, const uint32_t* __restrict__ pairs) {
-    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+// One workgroup of FORCE_TPB threads; nsweep (<= SWEEP_MAX_BLOCKS) is the
+// number of maxima the merge pass reduces.
+constexpr int FORCE_TPB = 256;
+__global__ __launch_bounds__(FORCE_TPB) void k_force(Ctl* ctl, GTable gt, Sweep* sw,
+                                                     const uint32_t* __restrict__ pairs, uint32_t nsweep) {
+    if (blockIdx.x != 0) return;
     const uint32_t done = ld_relaxed(&ctl->done);
     const uint32_t m = ld_relaxed(&ctl->m);
     const uint32_t limit = ld_relaxed(&ctl->limit);
     const bool active = !done && m < limit;
-    sw->iter = active ? m : NO_ITER;
-    sw->tile_base = ld_relaxed(&ctl->tile_ctr);
-    sw->forced = 1u;
+    if (threadIdx.x == 0) {
+        sw->iter = active ? m : NO_ITER;
+        sw->tile_base = ld_relaxed(&ctl->tile_ctr);
+    }
     if (!active) return;
-    const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
-    sw->fkey = key;
-    sw->fcount = gt_count(gt, key);
+    for (uint32_t i = threadIdx.x; i < nsweep; i += FORCE_TPB) {
+        unsigned long long v = 0ull;
+        if (i == 0) {
+            const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
+            v = ((unsigned long long)gt_count(gt, key) << 32) | (uint32_t)~key;
+        }
+        sw->bmax[i] = v;
+    }
 }
 
 }  // namespace bpek

@@ -455,14 +455,10 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     uint32_t* tile_ctr = &ctl->tile_ctr;
     const uint32_t tile_base = sw->tile_base;
 
-    // ---- the merge: the maximum of the sweep's per-workgroup maxima, or
-    // the named pair of a replayed iteration. These loads go first: waiting
-    // for them then does not wait for the tile's.
-    const bool forced = sw->forced != 0u;  // uniform
+    // ---- the merge: the maximum of the sweep's per-workgroup maxima. These
+    // loads go first: waiting for them then does not wait for the tile's.
     unsigned long long best = 0ull;
-    if (forced) {
-        best = ((unsigned long long)sw->fcount << 32) | (uint32_t)~sw->fkey;
-    } else {
+    {
         // nsweep <= SWEEP_MAX_BLOCKS = 2 * TPB
         const unsigned long long b0 = tid < nsweep ? sw->bmax[tid] : 0ull;
         const unsigned long long b1 = tid + TPB < nsweep ? sw->bmax[tid + TPB] : 0ull;
@@ -478,14 +474,12 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
     load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
 
-    if (!forced) {  // uniform
-        best = wave_max_u64(best);
-        if (lane == 0) s_best[w] = best;
-        lds_barrier();
+    best = wave_max_u64(best);
+    if (lane == 0) s_best[w] = best;
+    lds_barrier();
 #pragma unroll
-        for (int i = 0; i < NW; ++i) best = s_best[i] > best ? s_best[i] : best;
-    }
-    if (!forced && best == 0ull) {  // uniform: no countable pair is left
+    for (int i = 0; i < NW; ++i) best = s_best[i] > best ? s_best[i] : best;
+    if (best == 0ull) {  // uniform: no countable pair is left
         if (blockIdx.x == 0 && tid == 0) ctl->done = 1u;
         return;
     }
