@@ -9,6 +9,9 @@ benchmark's CPU-baseline leg, never by the GPU library or its binding.
                         multiset of distinct chunks with incremental counts.
 * ``encode``         - the encoder in plain C: a merge list applied in order
                         (``reference.encode`` is the same in Python).
+* ``trie_encode``    - greedy longest-match inference with the vocabulary of a
+                        merge list, in plain C over a pointer trie
+                        (``reference.trie_encode`` is a dictionary form).
 
 All three return ``(merges, tokens, lengths)``: merges is an int64 array of
 shape [k, 3] (left, right, count; merge i creates id 256 + i), tokens a
@@ -61,6 +64,8 @@ def _load():
         lib.oracle_tag.restype = None
         lib.oracle_encode.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint32, vp, vp, vp]
         lib.oracle_encode.restype = ctypes.c_int
+        lib.oracle_trie_encode.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint32, vp, vp]
+        lib.oracle_trie_encode.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -143,3 +148,24 @@ def encode(data, pairs):
     if rc != 0:
         raise RuntimeError("oracle failed with code %d" % rc)
     return counts[:k].astype(np.int64), tokens[: n_tok.value]
+
+
+def trie_encode(data, pairs):
+    """Greedy longest-match inference in C: ``pairs`` is [k, 2] or [k, 3]
+    (counts ignored). Returns the uint32 array of token ids (no flags)."""
+    b = _as_u8(data)
+    p = np.asarray(pairs, dtype=np.int64)
+    p = p.reshape(0, 2) if p.size == 0 else p.reshape(p.shape[0], -1)
+    p = np.ascontiguousarray(p[:, :2], dtype=np.uint32)
+    k = p.shape[0]
+    if k > MAX_MERGES:
+        raise ValueError("at most %d merges" % MAX_MERGES)
+    tokens = np.empty(max(b.size, 1), dtype=np.uint32)
+    n_tok = ctypes.c_uint64(0)
+    rc = _load().oracle_trie_encode(b.ctypes.data if b.size else None, b.size, p.ctypes.data if k else None, k,
+                                    tokens.ctypes.data, ctypes.addressof(n_tok))
+    if rc == -1:
+        raise ValueError("bad merge list (an id that does not exist yet)")
+    if rc != 0:
+        raise RuntimeError("oracle failed with code %d" % rc)
+    return tokens[: n_tok.value]

@@ -39,6 +39,16 @@
  *                          applies its pair; counts[k] = occurrences of the
  *                          pair just before merge k. O(n * merges).
  *
+ * And inference ("Nedir bu ya?", inference paragraph; "Ne Yapar? 4"):
+ *   oracle_trie_encode   - greedy longest match: from the current position,
+ *                          emit the id of the longest vocabulary string the
+ *                          text continues with there, move past it. The
+ *                          vocabulary is the merge list's: id b < 256 is the
+ *                          byte b, id 256 + k the string of pairs[2k]
+ *                          followed by that of pairs[2k+1]; a string several
+ *                          ids spell maps to the smallest. A plain pointer
+ *                          trie (first child / next sibling lists).
+ *
  * Outputs of both trainers:
  *   merges[3k+0..2] = left, right, count of merge k (new id 256 + k)
  *   tokens[0..*n_tokens) = final symbols, id | 0x10000 on chunk starts
@@ -557,4 +567,110 @@ int oracle_encode(const uint8_t *b, uint64_t n, const uint32_t *pairs, uint32_t 
     if (tokens) memcpy(tokens, s, sizeof(uint32_t) * len);
     free(s); free(t);
     return 0;
+}
+
+/* ======================================================================== */
+/* greedy longest-match inference                                            */
+
+typedef struct {
+    int32_t first;    /* first child, -1 if none          */
+    int32_t next;     /* next sibling, -1 if none         */
+    int32_t tok;      /* id spelled by the path, -1 if none */
+    uint8_t byte;     /* edge label from the parent        */
+} tnode_t;
+
+typedef struct {
+    tnode_t *v;
+    uint64_t n, cap;
+} ttrie_t;
+
+static int64_t tt_child(const ttrie_t *t, int64_t node, uint8_t c) {
+    for (int32_t k = t->v[node].first; k >= 0; k = t->v[k].next)
+        if (t->v[k].byte == c) return k;
+    return -1;
+}
+
+static int64_t tt_add(ttrie_t *t, int64_t node, uint8_t c) {
+    int64_t k = tt_child(t, node, c);
+    if (k >= 0) return k;
+    if (t->n == t->cap) {
+        uint64_t cap = t->cap ? 2 * t->cap : 1024;
+        tnode_t *v = (tnode_t *)realloc(t->v, sizeof(tnode_t) * cap);
+        if (!v) return -2;
+        t->v = v;
+        t->cap = cap;
+    }
+    k = (int64_t)t->n++;
+    t->v[k].first = -1;
+    t->v[k].tok = -1;
+    t->v[k].byte = c;
+    t->v[k].next = t->v[node].first;
+    t->v[node].first = (int32_t)k;
+    return k;
+}
+
+/* Returns 0, -1 on bad arguments (an id that does not exist yet), -2 on
+   allocation failure or a vocabulary too large for 32-bit node indexes. */
+int oracle_trie_encode(const uint8_t *b, uint64_t n, const uint32_t *pairs, uint32_t n_merges, uint32_t *tokens,
+                       uint64_t *n_tokens) {
+    if ((!b && n) || (!pairs && n_merges) || !n_tokens || n_merges > O_MAX_MERGES) return -1;
+    const uint32_t nv = O_BASE + n_merges;
+    uint64_t *off = (uint64_t *)malloc(sizeof(uint64_t) * nv);
+    uint64_t *len = (uint64_t *)malloc(sizeof(uint64_t) * nv);
+    if (!off || !len) { free(off); free(len); return -2; }
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < nv; i++) {
+        if (i < O_BASE) {
+            len[i] = 1;
+        } else {
+            const uint32_t k = i - O_BASE, l = pairs[2 * k], r = pairs[2 * k + 1];
+            if (l >= i || r >= i) { free(off); free(len); return -1; }
+            len[i] = len[l] + len[r];
+        }
+        off[i] = total;
+        total += len[i];
+        if (total > ((uint64_t)1 << 31)) { free(off); free(len); return -2; }
+    }
+    uint8_t *pool = (uint8_t *)malloc(total ? total : 1);
+    if (!pool) { free(off); free(len); return -2; }
+    for (uint32_t i = 0; i < nv; i++) {
+        if (i < O_BASE) {
+            pool[off[i]] = (uint8_t)i;
+        } else {
+            const uint32_t k = i - O_BASE, l = pairs[2 * k], r = pairs[2 * k + 1];
+            memcpy(pool + off[i], pool + off[l], len[l]);
+            memcpy(pool + off[i] + len[l], pool + off[r], len[r]);
+        }
+    }
+    ttrie_t t = {(tnode_t *)malloc(sizeof(tnode_t) * 1024), 0, 1024};
+    int rc = t.v ? 0 : -2;
+    if (!rc) {  /* node 0 is the root */
+        t.n = 1;
+        t.v[0].first = -1; t.v[0].next = -1; t.v[0].tok = -1; t.v[0].byte = 0;
+    }
+    for (uint32_t i = 0; i < nv && !rc; i++) {
+        int64_t node = 0;
+        for (uint64_t j = 0; j < len[i]; j++) {
+            node = tt_add(&t, node, pool[off[i] + j]);
+            if (node < 0 || t.n > 0x7FFFFFFFu) { rc = -2; break; }
+        }
+        if (!rc && t.v[node].tok < 0) t.v[node].tok = (int32_t)i;   /* smallest id keeps the string */
+    }
+    uint64_t o = 0;
+    for (uint64_t i = 0; i < n && !rc;) {
+        int64_t node = 0, best = -1;
+        uint64_t best_len = 0;
+        for (uint64_t j = i; j < n; j++) {
+            node = tt_child(&t, node, b[j]);
+            if (node < 0) break;
+            if (t.v[node].tok >= 0) { best = t.v[node].tok; best_len = j - i + 1; }
+        }
+        /* every byte is a token, so best_len >= 1 */
+        if (tokens) tokens[o] = (uint32_t)best;
+        o++;
+        i += best_len;
+    }
+    *n_tokens = o;
+    free(t.v); free(pool); free(off); free(len);
+    return rc;
 }

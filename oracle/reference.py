@@ -20,6 +20,9 @@ llm.istanbul/learn/tr/13_bpe):
 * "Ne Yapar? section 3": the merged symbol carries WORD_START_BIT.
 * "Nedir bu ya?" again, for encoding: text is encoded with a learned merge
   list by applying its merges in the order they were learned.
+* "Nedir bu ya?", inference paragraph, and "Ne Yapar? 4": inference walks a
+  prefix tree of the vocabulary and takes, at each position, the longest
+  vocabulary string the text continues with (greedy longest match).
 
 Readings where the page is silent (each one also listed in the design notes):
   - position 0 carries WORD_START_BIT (the first symbol starts a word);
@@ -154,3 +157,37 @@ def encode(data: bytes, pairs):
         counts.append(count_pairs(s).get((left, right), 0))
         s = merge_pair(s, left, right, BASE + k)
     return counts, s
+
+
+def vocab_strings(pairs) -> list[bytes]:
+    """The byte string of every id of a merge list: id b < 256 is the byte
+    b, id 256 + k the string of pairs[k][0] followed by that of pairs[k][1]."""
+    out = [bytes([b]) for b in range(BASE)]
+    for k, (left, right) in enumerate(pairs):
+        if not (0 <= left < BASE + k and 0 <= right < BASE + k):
+            raise ValueError("merge %d names an id that does not exist yet" % k)
+        out.append(out[left] + out[right])
+    return out
+
+
+def trie_encode(data: bytes, pairs) -> list[int]:
+    """Greedy longest-match inference with the vocabulary of a merge list:
+    from the current position, emit the id of the longest vocabulary string
+    that the text continues with there and move past it. Every single byte
+    is in the vocabulary, so some string always matches. A string that
+    several ids spell maps to the smallest of them. Tokens are plain ids."""
+    data = bytes(data)
+    vocab: dict[bytes, int] = {}
+    for i, v in enumerate(vocab_strings(pairs)):
+        vocab.setdefault(v, i)
+    longest = max(len(v) for v in vocab)
+    out = []
+    i = 0
+    while i < len(data):
+        for ln in range(min(longest, len(data) - i), 0, -1):
+            t = vocab.get(data[i:i + ln])
+            if t is not None:
+                out.append(t)
+                i += ln
+                break
+    return out
