@@ -70,6 +70,10 @@ _SIGS = {
     "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp, _vp]),
     "bpe_replay": (ctypes.c_int, [_vp, _vp, _u32]),
     "bpe_encode": (ctypes.c_int, [_vp, _sz, _vp, _u32, _cfgp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_trie_build": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(_vp)]),
+    "bpe_trie_info": (ctypes.c_int, [_vp, ctypes.POINTER(_u32), ctypes.POINTER(_u32)]),
+    "bpe_trie_encode": (ctypes.c_int, [_vp, _vp, _sz, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_trie_free": (None, [_vp]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "bpe_last_error": (ctypes.c_char_p, []),
@@ -185,6 +189,71 @@ def encode(data, merges, table_log2: int | None = None):
     _check(_lib.bpe_encode(data.data_ptr(), n, m.data_ptr(), m.shape[0], ctypes.byref(cfg), tokens.data_ptr(),
                            tokens.numel(), ctypes.byref(n_tok)), "bpe_encode")
     return tokens[: n_tok.value]
+
+
+class Trie:
+    """bpe_trie_build ... bpe_trie_free: greedy longest-match inference with
+    the vocabulary of a merge list ([k, 2] or [k, 3]; merge i is id 256 + i),
+    built on the current CUDA device."""
+
+    def __init__(self, merges):
+        torch = _torch()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        m = _merge_list(merges, dev)
+        self.device = dev
+        self._h = _vp(None)
+        _check(_lib.bpe_trie_build(m.data_ptr() if m.numel() else None, m.shape[0], ctypes.byref(self._h)),
+               "bpe_trie_build")
+
+    def info(self):
+        """(slots of the double array, longest vocabulary string in bytes)."""
+        a, b = _u32(0), _u32(0)
+        _check(_lib.bpe_trie_info(self._h, ctypes.byref(a), ctypes.byref(b)), "bpe_trie_info")
+        return a.value, b.value
+
+    def encode(self, data, out=None):
+        """Tokenize a uint8 CUDA tensor on the current stream. Returns the
+        int32 CUDA tensor of token ids (a prefix of ``out`` if given; it
+        needs room for data.numel() ids)."""
+        torch = _torch()
+        if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+            raise TypeError("data must be a uint8 CUDA tensor")
+        data = data.contiguous().reshape(-1)
+        n = data.numel()
+        if out is None:
+            out = torch.empty(max(n, 1), dtype=torch.int32, device=data.device)
+        if not (out.is_cuda and out.dtype == torch.int32 and out.is_contiguous() and out.numel() >= n):
+            raise ValueError("out must be a contiguous int32 CUDA tensor with room for n ids")
+        n_tok = _sz(0)
+        _check(_lib.bpe_trie_encode(self._h, data.data_ptr() if n else None, n, _stream_handle(data.device),
+                                    out.data_ptr(), out.numel(), ctypes.byref(n_tok)), "bpe_trie_encode")
+        return out[: n_tok.value]
+
+    def count(self, data) -> int:
+        """Number of tokens only (no token output)."""
+        torch = _torch()
+        data = data.contiguous().reshape(-1)
+        n_tok = _sz(0)
+        _check(_lib.bpe_trie_encode(self._h, data.data_ptr() if data.numel() else None, data.numel(),
+                                    _stream_handle(data.device), None, 0, ctypes.byref(n_tok)), "bpe_trie_encode")
+        return n_tok.value
+
+    def free(self) -> None:
+        if self._h:
+            _lib.bpe_trie_free(self._h)
+            self._h = _vp(None)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
 
 
 class State:

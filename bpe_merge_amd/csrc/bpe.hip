@@ -18,12 +18,14 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <utility>
 #include <vector>
 
 #include "../../include/bpe.h"
 #include "kernels.hpp"
 #include "merge.hpp"
+#include "trie.hpp"
 
 using bpek::Ctl;
 
@@ -708,6 +710,378 @@ bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, u
     if (st == BPE_OK) st = bpe_tokens(s, tokens, tokens ? tokens_cap : 0, n_tokens);
     bpe_free(s);
     return st;
+}
+
+}  // extern "C"
+
+// ======================================================================== inference
+// Greedy longest-match tokenization over a double-array trie of a merge
+// list's vocabulary (page "bpe - GPU BPE Tokenizer Pipeline", "Nedir bu
+// ya?" inference paragraph, "Ne Yapar? 4", "Host Mimarisi 1-4").
+
+struct bpe_trie {
+    int device = 0;
+    hipStream_t stream = nullptr;               // used when the caller passes none
+    unsigned long long* da = nullptr;           // the double array
+    size_t da_slots = 0;
+    uint32_t root_base = 0;
+    uint32_t max_len = 0;
+    bpek::TrieCtl* ctl = nullptr;
+    // pooled buffers, grown by half again when a call needs more ("Host
+    // Mimarisi 2"); kept until bpe_trie_free
+    unsigned long long* status = nullptr;
+    size_t status_cap = 0;
+    uint8_t* text_buf = nullptr;
+    size_t text_cap = 0;
+    uint32_t* tok_buf = nullptr;
+    size_t tok_cap = 0;
+    uint32_t epoch = 0;
+    uint32_t tile_base = 0;                     // tile counter value at the start of the next launch
+    unsigned long long wait_limit = 0;          // look-back wait bound, wall-clock ticks
+    int grid = 0;
+    bool poisoned = false;
+};
+
+namespace {
+
+constexpr int TRIE_TPB = 512;
+constexpr uint32_t TRIE_TILE = TRIE_TPB * 16;
+constexpr uint64_t TRIE_MAX_STRING_BYTES = uint64_t(1) << 27;  // total vocabulary string bytes accepted
+
+// The page's char_class, on the host.
+uint32_t host_byte_class(uint32_t b) {
+    if (b == 0x0Au) return 4u;
+    if (b == 0x20u) return 2u;
+    if (b >= 0x30u && b <= 0x39u) return 1u;
+    if (b >= 0x80u || (b >= 0x61u && b <= 0x7Au) || (b >= 0x41u && b <= 0x5Au)) return 0u;
+    return 3u;
+}
+
+// Vocabulary of a merge list -> prefix tree -> double array. Trie nodes are
+// placed in BFS order (children of a node sorted by byte, "Host Mimarisi 1");
+// a node's base is the lowest value >= 1 that puts all of its children on
+// free slots (first fit, with a next-free-slot union-find).
+bpe_status build_double_array(const std::vector<bpe_merge>& hm, std::vector<unsigned long long>* da,
+                              uint32_t* root_base, uint32_t* max_len) {
+    const uint32_t k = uint32_t(hm.size()), nv = bpek::BASE + k;
+    std::vector<uint64_t> len(nv), off(nv);
+    std::vector<uint32_t> cls(nv);
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < nv; ++i) {
+        if (i < bpek::BASE) {
+            len[i] = 1;
+            cls[i] = host_byte_class(i);
+        } else {
+            const uint32_t l = hm[i - bpek::BASE].left, r = hm[i - bpek::BASE].right;
+            if (l >= i || r >= i) {
+                set_err("merge %u (%u, %u) names an id that does not exist before it (ids < %u)", i - bpek::BASE, l,
+                        r, i);
+                return BPE_EINVAL;
+            }
+            if (cls[l] != cls[r]) {
+                set_err("merge %u (%u, %u) joins strings of different byte classes; no trained merge does, and "
+                        "such a string could match across a word start", i - bpek::BASE, l, r);
+                return BPE_EINVAL;
+            }
+            len[i] = len[l] + len[r];
+            cls[i] = cls[l];
+        }
+        off[i] = total;
+        total += len[i];
+        if (total > TRIE_MAX_STRING_BYTES) {
+            set_err("the vocabulary's strings exceed %llu bytes", (unsigned long long)TRIE_MAX_STRING_BYTES);
+            return BPE_EINVAL;
+        }
+    }
+    std::vector<uint8_t> pool(total);
+    for (uint32_t i = 0; i < nv; ++i) {
+        if (i < bpek::BASE) {
+            pool[off[i]] = uint8_t(i);
+        } else {
+            const uint32_t l = hm[i - bpek::BASE].left, r = hm[i - bpek::BASE].right;
+            std::memcpy(&pool[off[i]], &pool[off[l]], len[l]);
+            std::memcpy(&pool[off[i] + len[l]], &pool[off[r]], len[r]);
+        }
+        *max_len = uint32_t(std::max<uint64_t>(*max_len, len[i]));
+    }
+
+    // prefix tree: node 0 is the root; id i's node is reached from the node
+    // of its left part by the bytes of its right part
+    std::unordered_map<uint64_t, uint32_t> child;
+    child.reserve(size_t(nv) * 2);
+    std::vector<int32_t> tok(1, -1);
+    std::vector<std::vector<uint8_t>> kids(1);
+    std::vector<uint32_t> node_of(nv);
+    for (uint32_t i = 0; i < nv; ++i) {
+        uint32_t node = 0;
+        uint64_t from = off[i], to = off[i] + len[i];
+        if (i >= bpek::BASE) {
+            const uint32_t l = hm[i - bpek::BASE].left;
+            node = node_of[l];
+            from = off[i] + len[l];
+        }
+        for (uint64_t j = from; j < to; ++j) {
+            const uint64_t key = (uint64_t(node) << 8) | pool[j];
+            auto it = child.find(key);
+            if (it == child.end()) {
+                const uint32_t nn = uint32_t(tok.size());
+                if (nn >= bpek::TR_MAX_SLOTS) {
+                    set_err("the vocabulary needs more than %u trie nodes", bpek::TR_MAX_SLOTS);
+                    return BPE_EINVAL;
+                }
+                child.emplace(key, nn);
+                tok.push_back(-1);
+                kids.emplace_back();
+                kids[node].push_back(pool[j]);
+                node = nn;
+            } else {
+                node = it->second;
+            }
+        }
+        node_of[i] = node;
+        if (tok[node] < 0) tok[node] = int32_t(i);  // the smallest id keeps a string
+    }
+
+    // double array
+    const uint32_t lim = bpek::TR_MAX_SLOTS + 256u;
+    std::vector<uint32_t> nf(size_t(lim) + 1);  // next free slot at or after i
+    for (uint32_t i = 0; i <= lim; ++i) nf[i] = i;
+    auto find = [&](uint32_t i) {
+        while (nf[i] != i) {
+            nf[i] = nf[nf[i]];
+            i = nf[i];
+        }
+        return i;
+    };
+    auto take = [&](uint32_t i) { nf[i] = i + 1; };
+    std::vector<uint32_t> slot_of(tok.size()), base_of(tok.size(), 0), parent_slot(tok.size(), 0);
+    std::vector<uint32_t> order;
+    order.reserve(tok.size());
+    order.push_back(0);
+    slot_of[0] = 0;
+    take(0);
+    uint32_t top = 1;
+    for (size_t qi = 0; qi < order.size(); ++qi) {
+        const uint32_t node = order[qi];
+        std::vector<uint8_t>& ks = kids[node];
+        if (ks.empty()) continue;
+        std::sort(ks.begin(), ks.end());
+        uint32_t b = std::max<uint32_t>(1u, find(1u) > ks[0] ? find(1u) - ks[0] : 1u);
+        for (;;) {
+            if (b + 255u >= lim) {
+                set_err("the vocabulary needs more than %u trie slots", bpek::TR_MAX_SLOTS);
+                return BPE_EINVAL;
+            }
+            const uint32_t f = find(b + ks[0]);
+            b = f - ks[0];
+            bool ok = true;
+            for (size_t j = 1; j < ks.size() && ok; ++j) ok = find(b + ks[j]) == b + ks[j];
+            if (ok) break;
+            ++b;
+        }
+        if (b + 255u >= lim) {
+            set_err("the vocabulary needs more than %u trie slots", bpek::TR_MAX_SLOTS);
+            return BPE_EINVAL;
+        }
+        base_of[node] = b;
+        for (uint8_t c : ks) {
+            const uint32_t kn = child.at((uint64_t(node) << 8) | c);
+            slot_of[kn] = b + c;
+            parent_slot[kn] = slot_of[node];
+            take(b + c);
+            order.push_back(kn);
+        }
+        top = std::max(top, b + 256u);
+    }
+    da->assign(top, 0ull);
+    for (uint32_t node : order) {
+        const uint32_t check = node == 0 ? 0u : parent_slot[node] + 1u;
+        const uint32_t t1 = tok[node] < 0 ? 0u : uint32_t(tok[node]) + 1u;
+        (*da)[slot_of[node]] = bpek::tr_pack(check, base_of[node], t1);
+    }
+    *root_base = base_of[0];
+    return BPE_OK;
+}
+
+template <typename T>
+bpe_status pool_grow(T** p, size_t* cap, size_t need, bool zero) {
+    if (*cap >= need) return BPE_OK;
+    const size_t ncap = std::max(need, *cap + *cap / 2);
+    if (*p) HIP_TRY(hipFree(*p));
+    *p = nullptr;
+    *cap = 0;
+    if (hipMalloc(reinterpret_cast<void**>(p), ncap * sizeof(T)) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("hipMalloc of %zu bytes failed", ncap * sizeof(T));
+        return BPE_ENOMEM;
+    }
+    if (zero) HIP_TRY(hipMemset(*p, 0, ncap * sizeof(T)));
+    *cap = ncap;
+    return BPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpe_status bpe_trie_build(const bpe_merge* merges, uint32_t n_merges, bpe_trie** out) {
+    g_err.clear();
+    if (!out || (!merges && n_merges)) {
+        set_err("out must be non-NULL, and merges non-NULL when n_merges > 0");
+        return BPE_EINVAL;
+    }
+    *out = nullptr;
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    std::vector<bpe_merge> hm(n_merges);
+    if (n_merges) HIP_TRY(hipMemcpy(hm.data(), merges, sizeof(bpe_merge) * n_merges, hipMemcpyDefault));
+    std::vector<unsigned long long> da;
+    uint32_t root_base = 0, max_len = 0;
+    bpe_status st = build_double_array(hm, &da, &root_base, &max_len);
+    if (st != BPE_OK) return st;
+
+    bpe_trie* t = new (std::nothrow) bpe_trie();
+    if (!t) {
+        set_err("out of host memory");
+        return BPE_ENOMEM;
+    }
+    auto fail = [&](bpe_status s) {
+        bpe_trie_free(t);
+        return s;
+    };
+    if (hipGetDevice(&t->device) != hipSuccess) return fail(BPE_EHIP);
+    int cus = 0, per_cu = 0, rate_khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, t->device) != hipSuccess ||
+        hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, t->device) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_trie_encode<TRIE_TPB>, TRIE_TPB, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0 || rate_khz <= 0) {
+        (void)hipGetLastError();
+        set_err("cannot query the device");
+        return fail(BPE_EHIP);
+    }
+    t->grid = cus * per_cu;
+    t->wait_limit = 10ull * 1000ull * (unsigned long long)rate_khz;  // 10 s
+    if (hipStreamCreateWithFlags(&t->stream, hipStreamNonBlocking) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("hipStreamCreate failed");
+        return fail(BPE_EHIP);
+    }
+    t->da_slots = da.size();
+    t->root_base = root_base;
+    t->max_len = max_len;
+    if (hipMalloc(reinterpret_cast<void**>(&t->da), da.size() * sizeof(unsigned long long)) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&t->ctl), sizeof(bpek::TrieCtl)) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("hipMalloc failed");
+        return fail(BPE_ENOMEM);
+    }
+    if (hipMemcpy(t->da, da.data(), da.size() * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(t->ctl, 0, sizeof(bpek::TrieCtl)) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("uploading the trie failed");
+        return fail(BPE_EHIP);
+    }
+    *out = t;
+    return BPE_OK;
+}
+
+bpe_status bpe_trie_info(const bpe_trie* t, uint32_t* slots, uint32_t* max_len) {
+    g_err.clear();
+    if (!t) {
+        set_err("trie must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (slots) *slots = uint32_t(t->da_slots);
+    if (max_len) *max_len = t->max_len;
+    return BPE_OK;
+}
+
+bpe_status bpe_trie_encode(bpe_trie* t, const uint8_t* bytes, size_t n, void* stream, uint32_t* tokens,
+                           size_t tokens_cap, size_t* n_tokens) {
+    g_err.clear();
+    if (!t || !n_tokens || (n && !bytes)) {
+        set_err("trie and n_tokens must be non-NULL, and bytes non-NULL when n > 0");
+        return BPE_EINVAL;
+    }
+    if (n > BPE_MAX_BYTES) {
+        set_err("n = %zu exceeds the limit of %llu bytes", n, (unsigned long long)BPE_MAX_BYTES);
+        return BPE_EINVAL;
+    }
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    HIP_TRY(hipSetDevice(t->device));
+    hipStream_t s = stream ? reinterpret_cast<hipStream_t>(stream) : t->stream;
+    if (t->poisoned) {
+        // an earlier call failed after its launch: the counters are unknown
+        HIP_TRY(hipMemset(t->ctl, 0, sizeof(bpek::TrieCtl)));
+        if (t->status) HIP_TRY(hipMemset(t->status, 0, t->status_cap * sizeof(unsigned long long)));
+        t->tile_base = 0;
+        t->epoch = 0;
+        t->poisoned = false;
+    }
+    const uint32_t ntiles = uint32_t((n + TRIE_TILE - 1) / TRIE_TILE);
+    bpe_status st = pool_grow(&t->status, &t->status_cap, ntiles, true);
+    if (st != BPE_OK) return st;
+    const uint8_t* src = bytes;
+    if (!is_device_pointer(bytes)) {
+        st = pool_grow(&t->text_buf, &t->text_cap, n, false);
+        if (st != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(t->text_buf, bytes, n, hipMemcpyHostToDevice, s));
+        src = t->text_buf;
+    }
+    uint32_t* dst = tokens;
+    if (!tokens || !is_device_pointer(tokens)) {
+        st = pool_grow(&t->tok_buf, &t->tok_cap, n, false);
+        if (st != BPE_OK) return st;
+        dst = t->tok_buf;
+    }
+    if (t->epoch + 1u >= (1u << 30)) {  // epochs are 30 bits: start over on clean status words
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(256), dim3(256), 0, s, t->status, t->status_cap, 0ull);
+        t->epoch = 0;
+    }
+    t->epoch += 1u;
+    const uint32_t grid = uint32_t(std::min<size_t>(size_t(t->grid), ntiles));
+    t->poisoned = true;  // until the launch is known to have completed
+    hipLaunchKernelGGL(bpek::k_trie_encode<TRIE_TPB>, dim3(grid), dim3(TRIE_TPB), 0, s, src, uint32_t(n), t->da,
+                       t->root_base, dst, t->ctl, t->status, t->epoch, ntiles, t->tile_base, t->wait_limit);
+    HIP_TRY(hipGetLastError());
+    bpek::TrieCtl h;
+    HIP_TRY(hipMemcpyAsync(&h, t->ctl, sizeof h, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    t->tile_base += ntiles + grid;
+    t->poisoned = false;
+    if (h.err_epoch == t->epoch) {
+        set_err("a look-back wait exceeded its bound (one word took longer than 10 s to match)");
+        return BPE_ESTATE;
+    }
+    if (h.total > n) {
+        t->poisoned = true;
+        set_err("device reported %u tokens for %zu bytes", h.total, n);
+        return BPE_ESTATE;
+    }
+    *n_tokens = h.total;
+    if (tokens && dst != tokens) HIP_TRY(hipMemcpy(tokens, dst, sizeof(uint32_t) * size_t(h.total), hipMemcpyDefault));
+    return BPE_OK;
+}
+
+void bpe_trie_free(bpe_trie* t) {
+    if (!t) return;
+    (void)hipSetDevice(t->device);
+    if (t->stream) (void)hipStreamSynchronize(t->stream);
+    if (t->da) (void)hipFree(t->da);
+    if (t->ctl) (void)hipFree(t->ctl);
+    if (t->status) (void)hipFree(t->status);
+    if (t->text_buf) (void)hipFree(t->text_buf);
+    if (t->tok_buf) (void)hipFree(t->tok_buf);
+    if (t->stream) (void)hipStreamDestroy(t->stream);
+    delete t;
 }
 
 }  // extern "C"

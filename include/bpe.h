@@ -172,6 +172,48 @@ bpe_status bpe_replay(bpe_state *s, const bpe_merge *merges, uint32_t k);
 bpe_status bpe_encode(const uint8_t *bytes, size_t n, const bpe_merge *merges, uint32_t n_merges,
                       const bpe_config *cfg, uint32_t *tokens, size_t tokens_cap, size_t *n_tokens);
 
+/* ---------------------------------------------------------------- inference
+   Greedy longest-match tokenization with a learned vocabulary (page "bpe -
+   GPU BPE Tokenizer Pipeline": the inference paragraph of "Nedir bu ya?",
+   "Ne Yapar? 4", "Host Mimarisi 1-4"): at each position the token is the
+   longest vocabulary string the text continues with there. The vocabulary
+   is a merge list's: id b < 256 is the byte b, id 256 + k the string of
+   merge k's left id followed by its right id's. A string that several ids
+   spell maps to the smallest id. */
+typedef struct bpe_trie bpe_trie;
+
+/* Build the prefix tree of the vocabulary of merges[0..n_merges) (host or
+   device; counts are not read) on the current device, as a double array in
+   device memory, and create the trie's own stream. Errors: BPE_EINVAL for a
+   NULL out, an id that does not exist before its merge, a merge joining
+   strings of different byte classes (no trained merge does; such a string
+   could match across a word start, which the kernel's per-word
+   decomposition excludes), or a vocabulary past 2^21 - 1 trie slots or
+   2^27 string bytes; BPE_EIDSPACE above 65,280 merges; BPE_ENOMEM,
+   BPE_EHIP. */
+bpe_status bpe_trie_build(const bpe_merge *merges, uint32_t n_merges, bpe_trie **out);
+
+/* Size of the trie's double array in 8-byte slots, and the longest
+   vocabulary string in bytes (either pointer may be NULL). */
+bpe_status bpe_trie_info(const bpe_trie *t, uint32_t *slots, uint32_t *max_len);
+
+/* Tokenize bytes[0..n) (host or device). stream: a hipStream_t, or NULL for
+   the trie's own stream; device input is read on it. tokens (host or
+   device, capacity tokens_cap >= n, or NULL to get only the count) receive
+   plain token ids; *n_tokens the count. One kernel launch, then a wait for
+   the 4-byte total and a sized copy when tokens is host memory. The trie
+   keeps pooled device buffers between calls (grown by half when a call
+   needs more), so calls on one trie must not overlap. Errors: BPE_EINVAL
+   (NULL trie or n_tokens, NULL bytes with n > 0, n > BPE_MAX_BYTES,
+   tokens_cap < n), BPE_ESTATE when a tile waited more than 10 s on the
+   tiles before it (a single word that takes that long to match), BPE_ENOMEM,
+   BPE_EHIP. */
+bpe_status bpe_trie_encode(bpe_trie *t, const uint8_t *bytes, size_t n, void *stream, uint32_t *tokens,
+                           size_t tokens_cap, size_t *n_tokens);
+
+/* Release the trie and its buffers. NULL is a no-op. */
+void bpe_trie_free(bpe_trie *t);
+
 /* Per-kernel device time of the iterations run by bpe_profile. */
 typedef struct {
     double find_max_ms;      /* total time of the table sweep + argmax launches      */
