@@ -73,6 +73,7 @@ _SIGS = {
     "bpe_trie_build": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(_vp)]),
     "bpe_trie_info": (ctypes.c_int, [_vp, ctypes.POINTER(_u32), ctypes.POINTER(_u32)]),
     "bpe_trie_encode": (ctypes.c_int, [_vp, _vp, _sz, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_trie_profile": (ctypes.c_int, [_vp, _vp, _sz, _u32, _vp, ctypes.POINTER(_sz)]),
     "bpe_trie_free": (None, [_vp]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -229,9 +230,22 @@ class Trie:
                                     out.data_ptr(), out.numel(), ctypes.byref(n_tok)), "bpe_trie_encode")
         return out[: n_tok.value]
 
+    def profile(self, data, reps: int):
+        """bpe_trie_profile: (n_tokens, device ms as a numpy array of shape
+        [reps, 3]: walk, scan and copy kernels of each run)."""
+        import numpy as np
+        data = data.contiguous().reshape(-1)
+        ms = np.zeros(3 * max(reps, 1), dtype=np.float32)
+        n_tok = _sz(0)
+        _check(_lib.bpe_trie_profile(self._h, data.data_ptr(), data.numel(), reps, ms.ctypes.data,
+                                     ctypes.byref(n_tok)), "bpe_trie_profile")
+        return n_tok.value, ms[: 3 * reps].reshape(reps, 3)
+
     def count(self, data) -> int:
         """Number of tokens only (no token output)."""
         torch = _torch()
+        if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+            raise TypeError("data must be a uint8 CUDA tensor")
         data = data.contiguous().reshape(-1)
         n_tok = _sz(0)
         _check(_lib.bpe_trie_encode(self._h, data.data_ptr() if data.numel() else None, data.numel(),

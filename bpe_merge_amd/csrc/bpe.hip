@@ -726,26 +726,27 @@ struct bpe_trie {
     size_t da_slots = 0;
     uint32_t root_base = 0;
     uint32_t max_len = 0;
-    bpek::TrieCtl* ctl = nullptr;
+    uint32_t* total = nullptr;                  // device: token count of the last call
     // pooled buffers, grown by half again when a call needs more ("Host
     // Mimarisi 2"); kept until bpe_trie_free
-    unsigned long long* status = nullptr;
-    size_t status_cap = 0;
+    uint16_t* slices = nullptr;                 // per-tile token slices (walk -> copy)
+    size_t slices_cap = 0;
+    uint32_t* tiles = nullptr;                  // cnt, ovf_pos, ovf_n, pfx: 4 x ntiles
+    size_t tiles_cap = 0;
     uint8_t* text_buf = nullptr;
     size_t text_cap = 0;
     uint32_t* tok_buf = nullptr;
     size_t tok_cap = 0;
-    uint32_t epoch = 0;
-    uint32_t tile_base = 0;                     // tile counter value at the start of the next launch
-    unsigned long long wait_limit = 0;          // look-back wait bound, wall-clock ticks
-    int grid = 0;
-    bool poisoned = false;
+    int walk_grid = 0, copy_grid = 0;
 };
 
 namespace {
 
 constexpr int TRIE_TPB = 512;
 constexpr uint32_t TRIE_TILE = TRIE_TPB * 16;
+constexpr uint32_t TRIE_CAP = TRIE_TILE + TRIE_TPB * bpek::TRIE_HALO_PER_THREAD;
+constexpr int TRIE_SCAN_TPB = 1024;
+constexpr int TRIE_COPY_TPB = 256;
 constexpr uint64_t TRIE_MAX_STRING_BYTES = uint64_t(1) << 27;  // total vocabulary string bytes accepted
 
 // The page's char_class, on the host.
@@ -952,18 +953,17 @@ bpe_status bpe_trie_build(const bpe_merge* merges, uint32_t n_merges, bpe_trie**
         return s;
     };
     if (hipGetDevice(&t->device) != hipSuccess) return fail(BPE_EHIP);
-    int cus = 0, per_cu = 0, rate_khz = 0;
+    int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, t->device) != hipSuccess ||
-        hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, t->device) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_trie_encode<TRIE_TPB>, TRIE_TPB, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_trie_walk<TRIE_TPB>, TRIE_TPB, 0) !=
             hipSuccess ||
-        cus <= 0 || per_cu <= 0 || rate_khz <= 0) {
+        cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         set_err("cannot query the device");
         return fail(BPE_EHIP);
     }
-    t->grid = cus * per_cu;
-    t->wait_limit = 10ull * 1000ull * (unsigned long long)rate_khz;  // 10 s
+    t->walk_grid = cus * per_cu;
+    t->copy_grid = cus * 8;
     if (hipStreamCreateWithFlags(&t->stream, hipStreamNonBlocking) != hipSuccess) {
         (void)hipGetLastError();
         set_err("hipStreamCreate failed");
@@ -973,13 +973,12 @@ bpe_status bpe_trie_build(const bpe_merge* merges, uint32_t n_merges, bpe_trie**
     t->root_base = root_base;
     t->max_len = max_len;
     if (hipMalloc(reinterpret_cast<void**>(&t->da), da.size() * sizeof(unsigned long long)) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void**>(&t->ctl), sizeof(bpek::TrieCtl)) != hipSuccess) {
+        hipMalloc(reinterpret_cast<void**>(&t->total), sizeof(uint32_t)) != hipSuccess) {
         (void)hipGetLastError();
         set_err("hipMalloc failed");
         return fail(BPE_ENOMEM);
     }
-    if (hipMemcpy(t->da, da.data(), da.size() * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemset(t->ctl, 0, sizeof(bpek::TrieCtl)) != hipSuccess) {
+    if (hipMemcpy(t->da, da.data(), da.size() * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipGetLastError();
         set_err("uploading the trie failed");
         return fail(BPE_EHIP);
@@ -998,6 +997,44 @@ bpe_status bpe_trie_info(const bpe_trie* t, uint32_t* slots, uint32_t* max_len) 
     if (max_len) *max_len = t->max_len;
     return BPE_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// The three passes on stream s: walk, scan, copy. ev, if given, gets an
+// event recorded after each pass (3 events).
+bpe_status trie_enqueue(bpe_trie* t, const uint8_t* src, uint32_t n, uint32_t* dst, hipStream_t s,
+                        hipEvent_t* ev) {
+    const uint32_t ntiles = (n + TRIE_TILE - 1) / TRIE_TILE;
+    uint32_t* cnt = t->tiles;
+    uint32_t* ovf_pos = cnt + ntiles;
+    uint32_t* ovf_n = ovf_pos + ntiles;
+    uint32_t* pfx = ovf_n + ntiles;
+    hipLaunchKernelGGL(bpek::k_trie_walk<TRIE_TPB>, dim3(std::min<uint32_t>(ntiles, t->walk_grid)), dim3(TRIE_TPB),
+                       0, s, src, n, t->da, t->root_base, t->slices, cnt, ovf_pos, ovf_n, ntiles);
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    hipLaunchKernelGGL(bpek::k_trie_scan<TRIE_SCAN_TPB>, dim3(1), dim3(TRIE_SCAN_TPB), 0, s, cnt, ovf_n, pfx,
+                       ntiles, t->total);
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    hipLaunchKernelGGL(bpek::k_trie_copy<TRIE_COPY_TPB>, dim3(std::min<uint32_t>(ntiles, t->copy_grid)),
+                       dim3(TRIE_COPY_TPB), 0, s, src, n, t->da, t->root_base, t->slices, cnt, ovf_pos, ovf_n,
+                       pfx, dst, ntiles, TRIE_TILE, TRIE_CAP);
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    HIP_TRY(hipGetLastError());
+    return BPE_OK;
+}
+
+bpe_status trie_pools(bpe_trie* t, size_t n) {
+    const size_t ntiles = (n + TRIE_TILE - 1) / TRIE_TILE;
+    bpe_status st = pool_grow(&t->slices, &t->slices_cap, ntiles * TRIE_CAP, false);
+    if (st == BPE_OK) st = pool_grow(&t->tiles, &t->tiles_cap, 4 * ntiles, false);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
 
 bpe_status bpe_trie_encode(bpe_trie* t, const uint8_t* bytes, size_t n, void* stream, uint32_t* tokens,
                            size_t tokens_cap, size_t* n_tokens) {
@@ -1018,16 +1055,7 @@ bpe_status bpe_trie_encode(bpe_trie* t, const uint8_t* bytes, size_t n, void* st
     if (n == 0) return BPE_OK;
     HIP_TRY(hipSetDevice(t->device));
     hipStream_t s = stream ? reinterpret_cast<hipStream_t>(stream) : t->stream;
-    if (t->poisoned) {
-        // an earlier call failed after its launch: the counters are unknown
-        HIP_TRY(hipMemset(t->ctl, 0, sizeof(bpek::TrieCtl)));
-        if (t->status) HIP_TRY(hipMemset(t->status, 0, t->status_cap * sizeof(unsigned long long)));
-        t->tile_base = 0;
-        t->epoch = 0;
-        t->poisoned = false;
-    }
-    const uint32_t ntiles = uint32_t((n + TRIE_TILE - 1) / TRIE_TILE);
-    bpe_status st = pool_grow(&t->status, &t->status_cap, ntiles, true);
+    bpe_status st = trie_pools(t, n);
     if (st != BPE_OK) return st;
     const uint8_t* src = bytes;
     if (!is_device_pointer(bytes)) {
@@ -1042,32 +1070,57 @@ bpe_status bpe_trie_encode(bpe_trie* t, const uint8_t* bytes, size_t n, void* st
         if (st != BPE_OK) return st;
         dst = t->tok_buf;
     }
-    if (t->epoch + 1u >= (1u << 30)) {  // epochs are 30 bits: start over on clean status words
-        hipLaunchKernelGGL(bpek::k_fill64, dim3(256), dim3(256), 0, s, t->status, t->status_cap, 0ull);
-        t->epoch = 0;
-    }
-    t->epoch += 1u;
-    const uint32_t grid = uint32_t(std::min<size_t>(size_t(t->grid), ntiles));
-    t->poisoned = true;  // until the launch is known to have completed
-    hipLaunchKernelGGL(bpek::k_trie_encode<TRIE_TPB>, dim3(grid), dim3(TRIE_TPB), 0, s, src, uint32_t(n), t->da,
-                       t->root_base, dst, t->ctl, t->status, t->epoch, ntiles, t->tile_base, t->wait_limit);
-    HIP_TRY(hipGetLastError());
-    bpek::TrieCtl h;
-    HIP_TRY(hipMemcpyAsync(&h, t->ctl, sizeof h, hipMemcpyDeviceToHost, s));
+    st = trie_enqueue(t, src, uint32_t(n), dst, s, nullptr);
+    if (st != BPE_OK) return st;
+    uint32_t total = 0;
+    HIP_TRY(hipMemcpyAsync(&total, t->total, sizeof total, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
-    t->tile_base += ntiles + grid;
-    t->poisoned = false;
-    if (h.err_epoch == t->epoch) {
-        set_err("a look-back wait exceeded its bound (one word took longer than 10 s to match)");
+    if (total > n) {
+        set_err("device reported %u tokens for %zu bytes", total, n);
         return BPE_ESTATE;
     }
-    if (h.total > n) {
-        t->poisoned = true;
-        set_err("device reported %u tokens for %zu bytes", h.total, n);
+    *n_tokens = total;
+    if (tokens && dst != tokens) HIP_TRY(hipMemcpy(tokens, dst, sizeof(uint32_t) * size_t(total), hipMemcpyDefault));
+    return BPE_OK;
+}
+
+bpe_status bpe_trie_profile(bpe_trie* t, const uint8_t* bytes, size_t n, uint32_t reps, float* ms,
+                            size_t* n_tokens) {
+    g_err.clear();
+    if (!t || !n_tokens || !bytes || n == 0 || reps == 0 || n > BPE_MAX_BYTES) {
+        set_err("trie, bytes and n_tokens must be non-NULL, 0 < n <= BPE_MAX_BYTES and reps > 0");
+        return BPE_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(t->device));
+    if (!is_device_pointer(bytes)) {
+        set_err("bpe_trie_profile reads device bytes only");
+        return BPE_EINVAL;
+    }
+    size_t first = 0;
+    bpe_status st = bpe_trie_encode(t, bytes, n, nullptr, nullptr, 0, &first);  // sizes the pools
+    if (st != BPE_OK) return st;
+    std::vector<hipEvent_t>* ev = nullptr;
+    st = event_pool(t->device, 3 * size_t(reps) + 1, &ev);
+    if (st != BPE_OK) return st;
+    std::vector<hipEvent_t>& e = *ev;
+    HIP_TRY(hipEventRecord(e[0], t->stream));
+    for (uint32_t r = 0; r < reps; ++r) {
+        st = trie_enqueue(t, bytes, uint32_t(n), t->tok_buf, t->stream, &e[3 * size_t(r) + 1]);
+        if (st != BPE_OK) return st;
+    }
+    uint32_t total = 0;
+    HIP_TRY(hipMemcpyAsync(&total, t->total, sizeof total, hipMemcpyDeviceToHost, t->stream));
+    HIP_TRY(hipStreamSynchronize(t->stream));
+    if (total != first) {
+        set_err("repeated runs disagree on the token count (%u vs %zu)", total, first);
         return BPE_ESTATE;
     }
-    *n_tokens = h.total;
-    if (tokens && dst != tokens) HIP_TRY(hipMemcpy(tokens, dst, sizeof(uint32_t) * size_t(h.total), hipMemcpyDefault));
+    for (size_t i = 0; i < 3 * size_t(reps); ++i) {
+        float a = 0.f;
+        HIP_TRY(hipEventElapsedTime(&a, e[i], e[i + 1]));
+        if (ms) ms[i] = a;
+    }
+    *n_tokens = first;
     return BPE_OK;
 }
 
@@ -1076,8 +1129,9 @@ void bpe_trie_free(bpe_trie* t) {
     (void)hipSetDevice(t->device);
     if (t->stream) (void)hipStreamSynchronize(t->stream);
     if (t->da) (void)hipFree(t->da);
-    if (t->ctl) (void)hipFree(t->ctl);
-    if (t->status) (void)hipFree(t->status);
+    if (t->total) (void)hipFree(t->total);
+    if (t->slices) (void)hipFree(t->slices);
+    if (t->tiles) (void)hipFree(t->tiles);
     if (t->text_buf) (void)hipFree(t->text_buf);
     if (t->tok_buf) (void)hipFree(t->tok_buf);
     if (t->stream) (void)hipStreamDestroy(t->stream);

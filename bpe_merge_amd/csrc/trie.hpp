@@ -16,8 +16,11 @@
 // same-class run) can be matched on its own. A workgroup takes a tile of
 // TILE bytes and owns the words that start in it; one thread walks one
 // word's chain of longest matches to the word's end, which may lie past the
-// tile. Token starts are marked in LDS, compacted, and written at an offset
-// found by a decoupled look-back over tile token counts.
+// tile. Three passes, as the page's three dispatches (chunked walk, prefix
+// sum, compaction): the walk writes each tile's tokens compacted into a
+// per-tile slice with a count, one workgroup scans the counts, and a copy
+// pass moves every slice to its place. The walk time of a tile varies with
+// its words, so no tile ever waits for another.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,16 +49,6 @@ __host__ __device__ __forceinline__ unsigned long long tr_pack(uint32_t check, u
     return (unsigned long long)check | ((unsigned long long)base << TR_FIELD) |
            ((unsigned long long)tok1 << (2 * TR_FIELD));
 }
-
-// Control words of one trie: a monotonic tile counter (each launch starts
-// at the count the host expects, so nothing is reset between launches), the
-// total token count, and the epoch of the last launch that hit the wait
-// bound (0 if none).
-struct alignas(64) TrieCtl {
-    uint32_t tile_ctr;
-    uint32_t total;
-    uint32_t err_epoch;
-};
 
 // ---------------------------------------------------------------- helpers
 
@@ -90,57 +83,27 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_
     return before + x - v;
 }
 
-// Look-back over tile token counts (one wave): the number of tokens in
-// tiles below t. Status words as in the merge pass (flag, epoch, payload =
-// the tile's count for an aggregate, the inclusive count for a prefix).
-// The wait is bounded by wall-clock time: past `limit` ticks it reports
-// failure and returns 0, so the kernel always finishes.
-__device__ __forceinline__ uint32_t count_lookback(const unsigned long long* status, uint32_t t, uint32_t epoch,
-                                                   uint32_t lane, unsigned long long limit, bool* failed) {
-    constexpr unsigned long long AGG = 1ull << 62, PRE = 2ull << 62;
-    uint32_t acc = 0;
-    long long top = (long long)t - 1;
-    const unsigned long long t_start = wall_clock64();
-    for (;;) {
-        const long long idx = top - (long long)lane;
-        unsigned long long s = (idx >= 0) ? __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : (PRE | ((unsigned long long)epoch << 32));
-        for (;;) {
-            const bool v = (s >> 62) != 0ull && (uint32_t)((s >> 32) & 0x3FFFFFFFull) == epoch;
-            const unsigned long long pm = __ballot(v && (s >> 62) == 2ull);
-            const uint32_t plane = pm ? (uint32_t)(__ffsll((long long)pm) - 1) : 64u;
-            const bool ok = (lane <= plane) ? v : true;
-            if (__ballot(!ok) == 0ull) {
-                acc += wave_sum_u32((lane <= plane) ? (uint32_t)s : 0u);
-                if (plane < 64u) return acc;
-                break;
-            }
-            if (wall_clock64() - t_start > limit) {
-                *failed = true;
-                return 0u;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            if (idx >= 0 && !v) s = __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        top -= 64;
-    }
-    (void)AGG;
-}
-
-// One longest match from relative position p (byte b0 = byte(p), class
-// cls): the token id and its length in bytes. byte(q) fetches text bytes;
-// nrel is the text length relative to the tile start.
+// One longest match at relative position p (byte b0, word class cls),
+// reading text bytes with byte_at(q) for q < lim: the token id and its
+// length in bytes. *cut is set when the walk stopped only because it
+// reached lim with more of the word and of the trie left (the caller then
+// matches again with a reader that goes further).
 template <typename ByteAt>
 __device__ __forceinline__ void longest_match(const unsigned long long* __restrict__ da,
                                               const unsigned long long* s_root, uint32_t root_base, uint32_t p,
-                                              uint32_t nrel, uint32_t b0, uint32_t cls, ByteAt byte_at,
-                                              uint32_t* tok, uint32_t* len) {
+                                              uint32_t lim, uint32_t b0, uint32_t cls, ByteAt byte_at,
+                                              uint32_t* tok, uint32_t* len, bool* cut) {
     unsigned long long e = s_root[b0];
     uint32_t slot = root_base + b0;
     uint32_t best = tr_tok1(e) - 1u, blen = 1u;  // every byte is a token
+    bool c_ut = false;
     for (uint32_t j = 1;; ++j) {
         const uint32_t base = tr_base(e);
-        if (base == 0u || p + j >= nrel) break;
+        if (base == 0u) break;
+        if (p + j >= lim) {
+            c_ut = true;
+            break;
+        }
         const uint32_t c = byte_at(p + j);
         if (byte_class(c) != cls) break;  // the word ends; no string crosses it
         const unsigned long long e2 = da[base + c];
@@ -155,26 +118,59 @@ __device__ __forceinline__ void longest_match(const unsigned long long* __restri
     }
     *tok = best;
     *len = blen;
+    *cut = c_ut;
 }
 
-// ---------------------------------------------------------------- the kernel
-// text: n bytes (any alignment); da: the double array (every base + 255 is
-// inside it); out: room for n tokens. Tiles are handed out in order by the
-// monotonic counter ctl->tile_ctr (minus tile_base), so every tile a
-// workgroup waits on is held by a running workgroup.
+// The rest of a word from relative position p (a token start, p < nrel)
+// with bytes read from global memory: a match that ran past the LDS copy,
+// and every token past it. Tokens at positions below cap are recorded in
+// LDS (s_flag, s_tok); the others are counted into *ovf_n, the first of
+// them noted in *ovf_pos. Returns nothing else; runs for at most one word
+// per tile (the last one), so it is kept out of line.
+__device__ __attribute__((noinline)) void finish_word_global(
+    const uint8_t* __restrict__ text, uint32_t t0, uint32_t nrel, uint32_t p, uint32_t cls,
+    const unsigned long long* __restrict__ da, const unsigned long long* s_root, uint32_t root_base, uint32_t cap,
+    uint32_t* s_flag, uint16_t* s_tok, uint32_t* ovf_pos, uint32_t* ovf_n) {
+    auto gbyte = [&](uint32_t q) -> uint32_t { return text[t0 + q]; };
+    for (;;) {
+        uint32_t tok, len;
+        bool cut;
+        longest_match(da, s_root, root_base, p, nrel, gbyte(p), cls, gbyte, &tok, &len, &cut);
+        if (p < cap) {
+            atomicOr(&s_flag[p >> 5], 1u << (p & 31u));
+            s_tok[p] = (uint16_t)tok;
+        } else {
+            if (*ovf_pos == 0xFFFFFFFFu) *ovf_pos = p;
+            *ovf_n += 1u;
+        }
+        p += len;
+        if (p >= nrel || byte_class(gbyte(p)) != cls) break;
+    }
+}
+
+// ---------------------------------------------------------------- pass 1: walk
+constexpr uint32_t TRIE_HALO_PER_THREAD = 4;  // LDS bytes past the tile, per thread
+constexpr uint32_t NO_OVF = 0xFFFFFFFFu;
+
+// Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x, ...
+// Outputs for tile t: tok16[t * CAP + i], i < cnt[t], the ids of the tokens
+// of the words starting in the tile, in order, as far as CAP bytes from the
+// tile start; for a last word running further, ovf_pos[t] is the relative
+// position of its first token at or past CAP and ovf_n[t] the number of its
+// tokens from there (NO_OVF and 0 otherwise). text: n bytes, any alignment;
+// da: the double array (every base + 255 inside it).
 template <int TPB>
-__global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__ text, uint32_t n,
-                                                     const unsigned long long* __restrict__ da, uint32_t root_base,
-                                                     uint32_t* __restrict__ out, TrieCtl* ctl,
-                                                     unsigned long long* status, uint32_t epoch, uint32_t ntiles,
-                                                     uint32_t tile_base, unsigned long long wait_limit) {
+__global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ text, uint32_t n,
+                                                   const unsigned long long* __restrict__ da, uint32_t root_base,
+                                                   uint16_t* __restrict__ tok16, uint32_t* __restrict__ cnt,
+                                                   uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
+                                                   uint32_t ntiles) {
     constexpr uint32_t TILE = TPB * 16u;          // words starting here are this tile's
-    constexpr uint32_t HALO = 2048u;              // bytes past the tile kept in LDS
+    constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
     constexpr uint32_t CAP = TILE + HALO;         // token starts recorded in LDS
     constexpr uint32_t PER = CAP / TPB;           // positions per thread in the compaction
     constexpr uint32_t NCH = (CAP + 32u) / 16u;   // 16-byte chunks loaded per tile
     static_assert(CAP % TPB == 0 && PER <= 32, "compaction covers CAP positions, at most 32 per thread");
-    constexpr unsigned long long AGG = 1ull << 62, PRE = 2ull << 62;
 
     __shared__ __align__(16) uint8_t s_txt[NCH * 16u];  // s_txt[p + 16 + mis] = text[t0 + p]
     __shared__ uint32_t s_flag[CAP / 32u];             // token starts
@@ -182,9 +178,9 @@ __global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__
     __shared__ uint16_t s_aux[CAP];                    // word list, then staged output
     __shared__ unsigned long long s_root[256];
     __shared__ uint32_t s_w[TPB / 64];
-    __shared__ uint32_t s_tile, s_prefix, s_ovf_pos, s_ovf_n, s_fail;
+    __shared__ uint32_t s_ovf_pos, s_ovf_n;
 
-    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t tid = threadIdx.x;
     // the text through a 16-byte aligned base; the range is rounded up to
     // whole 16-byte blocks (bytes past n in the last block are loaded but
     // never used, and lie in the same block, so on the same page)
@@ -194,17 +190,12 @@ __global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__
 
     for (uint32_t i = tid; i < 256u; i += TPB) s_root[i] = da[root_base + i];
 
-    for (;;) {
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         if (tid == 0) {
-            s_tile = atomicAdd(&ctl->tile_ctr, 1u) - tile_base;
-            s_ovf_pos = 0xFFFFFFFFu;
+            s_ovf_pos = NO_OVF;
             s_ovf_n = 0u;
-            s_fail = 0u;
         }
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
-        __syncthreads();  // also orders the previous tile's LDS reads before the new writes
-        const uint32_t t = s_tile;
-        if (t >= ntiles) break;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
 
@@ -214,11 +205,9 @@ __global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__
             const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
             *reinterpret_cast<v4*>(s_txt + 16u * k) = v;
         }
-        __syncthreads();
+        __syncthreads();  // also orders the previous tile's LDS reads before these writes
         const uint32_t sh = 16u + mis;
-        auto byte_at = [&](uint32_t q) -> uint32_t {
-            return (q < CAP) ? (uint32_t)s_txt[q + sh] : (uint32_t)text[t0 + q];
-        };
+        auto lbyte = [&](uint32_t q) -> uint32_t { return s_txt[q + sh]; };  // q < CAP
 
         // word starts in [t0, t0 + TILE)
         uint32_t starts = 0;
@@ -238,26 +227,33 @@ __global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__
         for (uint32_t m = starts; m; m &= m - 1u) s_aux[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
         __syncthreads();
 
-        // one thread per word: its chain of longest matches to the word's end
+        // one thread per word: its chain of longest matches to the word's
+        // end, from the LDS copy; a word that runs past it (only the tile's
+        // last word can) is finished from global memory
+        const uint32_t lim = nrel < CAP ? nrel : CAP;
         for (uint32_t w = tid; w < nwords; w += TPB) {
             uint32_t p = s_aux[w];
-            uint32_t b = s_txt[p + sh];
+            uint32_t b = lbyte(p);
             const uint32_t cls = byte_class(b);
             for (;;) {
                 uint32_t tok, len;
-                longest_match(da, s_root, root_base, p, nrel, b, cls, byte_at, &tok, &len);
-                if (p < CAP) {
-                    atomicOr(&s_flag[p >> 5], 1u << (p & 31u));
-                    s_tok[p] = (uint16_t)tok;
-                } else {
-                    // only the tile's last word runs this far; its later
-                    // tokens are counted now and written after the look-back
-                    if (s_ovf_pos == 0xFFFFFFFFu) s_ovf_pos = p;
-                    s_ovf_n += 1u;
+                bool cut;
+                longest_match(da, s_root, root_base, p, lim, b, cls, lbyte, &tok, &len, &cut);
+                if (cut) {
+                    finish_word_global(text, t0, nrel, p, cls, da, s_root, root_base, CAP, s_flag, s_tok,
+                                       &s_ovf_pos, &s_ovf_n);
+                    break;
                 }
+                atomicOr(&s_flag[p >> 5], 1u << (p & 31u));
+                s_tok[p] = (uint16_t)tok;
                 p += len;
-                if (p >= nrel) break;
-                b = byte_at(p);
+                if (p >= lim) {
+                    if (p < nrel && byte_class(text[t0 + p]) == cls)
+                        finish_word_global(text, t0, nrel, p, cls, da, s_root, root_base, CAP, s_flag, s_tok,
+                                           &s_ovf_pos, &s_ovf_n);
+                    break;
+                }
+                b = lbyte(p);
                 if (byte_class(b) != cls) break;
             }
         }
@@ -274,57 +270,71 @@ __global__ __launch_bounds__(TPB) void k_trie_encode(const uint8_t* __restrict__
         }
         uint32_t nlds;
         uint32_t off = block_exclusive_sum<TPB>(__popc(bits), s_w, &nlds);
-        const uint32_t novf = s_ovf_n;
-        const uint32_t count = nlds + novf;
-
-        if (tid < 64u) {
-            uint32_t prefix = 0;
-            if (t == 0u) {
-                if (lane == 0u)
-                    __hip_atomic_store(status, PRE | ((unsigned long long)epoch << 32) | count, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                if (lane == 0u)
-                    __hip_atomic_store(status + t, AGG | ((unsigned long long)epoch << 32) | count, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                bool failed = false;
-                prefix = count_lookback(status, t, epoch, lane, wait_limit, &failed);
-                if (lane == 0u) {
-                    __hip_atomic_store(status + t, PRE | ((unsigned long long)epoch << 32) | (prefix + count),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (failed) {
-                        s_fail = 1u;
-                        atomicExch(&ctl->err_epoch, epoch);
-                    }
-                }
-            }
-            if (lane == 0u) s_prefix = prefix;
-        }
-        // stage this thread's tokens in order (s_aux is free again)
         for (uint32_t m = bits; m; m &= m - 1u) s_aux[off++] = s_tok[PER * tid + (__ffs(m) - 1)];
         __syncthreads();
+        uint16_t* dst = tok16 + (size_t)t * CAP;
+        for (uint32_t i = tid; i < nlds; i += TPB) dst[i] = s_aux[i];
+        if (tid == 0) {
+            cnt[t] = nlds;
+            ovf_pos[t] = s_ovf_pos;
+            ovf_n[t] = s_ovf_n;
+        }
+    }
+}
 
-        const uint32_t prefix = s_prefix;
-        if (s_fail == 0u) {
-            for (uint32_t i = tid; i < nlds; i += TPB) out[prefix + i] = s_aux[i];
-            if (tid == 0u && novf) {
-                // the rest of the last word, walked again from its first
-                // token past the recorded range
-                uint32_t p = s_ovf_pos;
-                uint32_t b = text[t0 + p];
-                const uint32_t cls = byte_class(b);
-                uint32_t o = prefix + nlds;
-                for (uint32_t k = 0; k < novf; ++k) {
-                    uint32_t tok, len;
-                    longest_match(da, s_root, root_base, p, nrel, b, cls, byte_at, &tok, &len);
-                    out[o++] = tok;
-                    p += len;
-                    if (p >= nrel) break;
-                    b = byte_at(p);
-                }
+// ---------------------------------------------------------------- pass 2: scan
+// One workgroup: pfx[t] = tokens of all tiles below t (cnt + ovf_n), and
+// *total = all of them.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_trie_scan(const uint32_t* __restrict__ cnt,
+                                                   const uint32_t* __restrict__ ovf_n, uint32_t* __restrict__ pfx,
+                                                   uint32_t ntiles, uint32_t* total) {
+    __shared__ uint32_t s_w[TPB / 64];
+    const uint32_t per = (ntiles + TPB - 1u) / TPB;
+    const uint32_t lo = threadIdx.x * per, hi = lo + per < ntiles ? lo + per : ntiles;
+    uint32_t sum = 0;
+    for (uint32_t t = lo; t < hi; ++t) sum += cnt[t] + ovf_n[t];
+    uint32_t all;
+    uint32_t run = block_exclusive_sum<TPB>(sum, s_w, &all);
+    for (uint32_t t = lo; t < hi; ++t) {
+        pfx[t] = run;
+        run += cnt[t] + ovf_n[t];
+    }
+    if (threadIdx.x == 0) *total = all;
+}
+
+// ---------------------------------------------------------------- pass 3: copy
+// Tile slices to their places in out (16-bit ids widened to 32 bits); the
+// tokens of a tile's last word past its recorded range are walked again,
+// from global memory, by one thread.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_trie_copy(const uint8_t* __restrict__ text, uint32_t n,
+                                                   const unsigned long long* __restrict__ da, uint32_t root_base,
+                                                   const uint16_t* __restrict__ tok16,
+                                                   const uint32_t* __restrict__ cnt,
+                                                   const uint32_t* __restrict__ ovf_pos,
+                                                   const uint32_t* __restrict__ ovf_n,
+                                                   const uint32_t* __restrict__ pfx, uint32_t* __restrict__ out,
+                                                   uint32_t ntiles, uint32_t tile, uint32_t cap) {
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint32_t c = cnt[t], base = pfx[t];
+        const uint16_t* src = tok16 + (size_t)t * cap;
+        for (uint32_t i = threadIdx.x; i < c; i += TPB) out[base + i] = src[i];
+        const uint32_t no = ovf_n[t];
+        if (threadIdx.x == 0 && no) {
+            const uint32_t t0 = t * tile, nrel = n - t0;
+            uint32_t p = ovf_pos[t];
+            const uint32_t cls = byte_class(text[t0 + p]);
+            auto gbyte = [&](uint32_t q) -> uint32_t { return text[t0 + q]; };
+            uint32_t o = base + c;
+            for (uint32_t k = 0; k < no && p < nrel; ++k) {
+                uint32_t tok, len;
+                bool cut;
+                longest_match(da, da + root_base, root_base, p, nrel, gbyte(p), cls, gbyte, &tok, &len, &cut);
+                out[o++] = tok;
+                p += len;
             }
         }
-        if (tid == 0u && t == ntiles - 1u) ctl->total = prefix + count;
     }
 }
 

@@ -200,16 +200,25 @@ bpe_status bpe_trie_info(const bpe_trie *t, uint32_t *slots, uint32_t *max_len);
 /* Tokenize bytes[0..n) (host or device). stream: a hipStream_t, or NULL for
    the trie's own stream; device input is read on it. tokens (host or
    device, capacity tokens_cap >= n, or NULL to get only the count) receive
-   plain token ids; *n_tokens the count. One kernel launch, then a wait for
-   the 4-byte total and a sized copy when tokens is host memory. The trie
-   keeps pooled device buffers between calls (grown by half when a call
-   needs more), so calls on one trie must not overlap. Errors: BPE_EINVAL
+   plain token ids; *n_tokens the count. Three kernels (walk, scan of the
+   per-tile counts, copy), then a wait for the 4-byte total and a sized
+   copy when tokens is host memory. The trie keeps pooled device buffers
+   between calls (grown by half when a call needs more; about 3 bytes per
+   input byte), so calls on one trie must not overlap. Errors: BPE_EINVAL
    (NULL trie or n_tokens, NULL bytes with n > 0, n > BPE_MAX_BYTES,
-   tokens_cap < n), BPE_ESTATE when a tile waited more than 10 s on the
-   tiles before it (a single word that takes that long to match), BPE_ENOMEM,
-   BPE_EHIP. */
+   tokens_cap < n), BPE_ENOMEM, BPE_EHIP. */
 bpe_status bpe_trie_encode(bpe_trie *t, const uint8_t *bytes, size_t n, void *stream, uint32_t *tokens,
                            size_t tokens_cap, size_t *n_tokens);
+
+/* Time the inference kernels: bpe_trie_encode of device bytes[0..n) once
+   (tokens to the trie's pooled buffer), then reps runs back to back on the
+   trie's own stream with a HIP event after each kernel, one host wait at
+   the end. ms (host, 3 * reps entries, or NULL) receives the device time of
+   each run's walk, scan and copy kernels in that order; *n_tokens the token
+   count. Errors: BPE_EINVAL (NULL arguments, n = 0, reps = 0, host bytes),
+   BPE_ESTATE (runs disagree), BPE_ENOMEM, BPE_EHIP. */
+bpe_status bpe_trie_profile(bpe_trie *t, const uint8_t *bytes, size_t n, uint32_t reps, float *ms,
+                            size_t *n_tokens);
 
 /* Release the trie and its buffers. NULL is a no-op. */
 void bpe_trie_free(bpe_trie *t);
