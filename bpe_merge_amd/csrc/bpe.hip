@@ -1002,20 +1002,28 @@ bpe_status bpe_trie_info(const bpe_trie* t, uint32_t* slots, uint32_t* max_len) 
 
 namespace {
 
+// Per-tile arrays are padded to a multiple of 4 scan threads' worth, so the
+// scan reads them with 16-byte loads.
+uint32_t trie_npad(uint32_t ntiles) {
+    const uint32_t q = 4u * TRIE_SCAN_TPB;
+    return (ntiles + q - 1u) / q * q;
+}
+
 // The three passes on stream s: walk, scan, copy. ev, if given, gets an
 // event recorded after each pass (3 events).
 bpe_status trie_enqueue(bpe_trie* t, const uint8_t* src, uint32_t n, uint32_t* dst, hipStream_t s,
                         hipEvent_t* ev) {
     const uint32_t ntiles = (n + TRIE_TILE - 1) / TRIE_TILE;
+    const uint32_t npad = trie_npad(ntiles);
     uint32_t* cnt = t->tiles;
-    uint32_t* ovf_pos = cnt + ntiles;
-    uint32_t* ovf_n = ovf_pos + ntiles;
-    uint32_t* pfx = ovf_n + ntiles;
+    uint32_t* ovf_pos = cnt + npad;
+    uint32_t* ovf_n = ovf_pos + npad;
+    uint32_t* pfx = ovf_n + npad;
     hipLaunchKernelGGL(bpek::k_trie_walk<TRIE_TPB>, dim3(std::min<uint32_t>(ntiles, t->walk_grid)), dim3(TRIE_TPB),
                        0, s, src, n, t->da, t->root_base, t->slices, cnt, ovf_pos, ovf_n, ntiles);
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     hipLaunchKernelGGL(bpek::k_trie_scan<TRIE_SCAN_TPB>, dim3(1), dim3(TRIE_SCAN_TPB), 0, s, cnt, ovf_n, pfx,
-                       ntiles, t->total);
+                       ntiles, npad, t->total);
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     hipLaunchKernelGGL(bpek::k_trie_copy<TRIE_COPY_TPB>, dim3(std::min<uint32_t>(ntiles, t->copy_grid)),
                        dim3(TRIE_COPY_TPB), 0, s, src, n, t->da, t->root_base, t->slices, cnt, ovf_pos, ovf_n,
@@ -1028,7 +1036,7 @@ bpe_status trie_enqueue(bpe_trie* t, const uint8_t* src, uint32_t n, uint32_t* d
 bpe_status trie_pools(bpe_trie* t, size_t n) {
     const size_t ntiles = (n + TRIE_TILE - 1) / TRIE_TILE;
     bpe_status st = pool_grow(&t->slices, &t->slices_cap, ntiles * TRIE_CAP, false);
-    if (st == BPE_OK) st = pool_grow(&t->tiles, &t->tiles_cap, 4 * ntiles, false);
+    if (st == BPE_OK) st = pool_grow(&t->tiles, &t->tiles_cap, 4 * size_t(trie_npad(uint32_t(ntiles))), false);
     return st;
 }
 

@@ -174,11 +174,12 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
 
     __shared__ __align__(16) uint8_t s_txt[NCH * 16u];  // s_txt[p + 16 + mis] = text[t0 + p]
     __shared__ uint32_t s_flag[CAP / 32u];             // token starts
+    __shared__ uint32_t s_sb[TILE / 32u];              // word starts in the tile
     __shared__ uint16_t s_tok[CAP];                    // token id at each start
     __shared__ uint16_t s_aux[CAP];                    // word list, then staged output
     __shared__ unsigned long long s_root[256];
     __shared__ uint32_t s_w[TPB / 64];
-    __shared__ uint32_t s_ovf_pos, s_ovf_n;
+    __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after;
 
     const uint32_t tid = threadIdx.x;
     // the text through a 16-byte aligned base; the range is rounded up to
@@ -194,8 +195,10 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
         if (tid == 0) {
             s_ovf_pos = NO_OVF;
             s_ovf_n = 0u;
+            s_after = CAP;
         }
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
+        for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
 
@@ -209,52 +212,147 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
         const uint32_t sh = 16u + mis;
         auto lbyte = [&](uint32_t q) -> uint32_t { return s_txt[q + sh]; };  // q < CAP
 
-        // word starts in [t0, t0 + TILE)
-        uint32_t starts = 0;
+        // Word starts in [t0, t0 + TILE), 16 positions per thread: into the
+        // LDS bitmap s_sb. A one-byte word is its own token (every byte is
+        // one) and is recorded here; longer words go to the list s_aux.
+        // The first word start in [t0 + TILE, t0 + CAP) ends the tile's last
+        // word (if there is none, that word may run past the copy).
+        uint32_t multi;
         {
             const uint32_t p0 = 16u * tid;
             uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+            uint32_t starts = 0, bnd = 0;  // bnd bit k: a word boundary at p0 + k (k = 1..16)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t c = byte_class(s_txt[p0 + j + sh]);
-                const bool st = (p0 + j < nrel) && (t0 + p0 + j == 0u || c != pc);
-                starts |= (st ? 1u : 0u) << j;
+            for (int k = 0; k <= 16; ++k) {
+                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+                const bool inside = p0 + k < nrel;
+                const bool change = c != pc || t0 + p0 + k == 0u;
+                if (k < 16) starts |= ((inside && change) ? 1u : 0u) << k;
+                if (k >= 1) bnd |= ((!inside || change) ? 1u : 0u) << k;
                 pc = c;
             }
+            const uint32_t single = starts & (bnd >> 1);
+            multi = starts & ~single;
+            const uint32_t sb = p0 & 31u;  // the 16 positions share one 32-bit word
+            if (starts) atomicOr(&s_sb[p0 >> 5], starts << sb);
+            if (single) {
+                atomicOr(&s_flag[p0 >> 5], single << sb);
+                for (uint32_t m = single; m; m &= m - 1u) {
+                    const uint32_t k = __ffs(m) - 1;
+                    s_tok[p0 + k] = (uint16_t)lbyte(p0 + k);
+                }
+            }
+        }
+        uint32_t after = CAP;
+        {
+            const uint32_t p0 = TILE + TRIE_HALO_PER_THREAD * tid;
+            uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+#pragma unroll
+            for (int k = 0; k < (int)TRIE_HALO_PER_THREAD; ++k) {
+                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+                if (p0 + k < nrel && c != pc && after == CAP) after = p0 + k;
+                pc = c;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) after = min(after, (uint32_t)__shfl_xor(after, o));
+            if ((tid & 63u) == 0u) atomicMin(&s_after, after);
         }
         uint32_t nwords;
-        uint32_t woff = block_exclusive_sum<TPB>(__popc(starts), s_w, &nwords);
-        for (uint32_t m = starts; m; m &= m - 1u) s_aux[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
+        uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
+        for (uint32_t m = multi; m; m &= m - 1u) s_aux[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
         __syncthreads();
 
-        // one thread per word: its chain of longest matches to the word's
-        // end, from the LDS copy; a word that runs past it (only the tile's
-        // last word can) is finished from global memory
-        const uint32_t lim = nrel < CAP ? nrel : CAP;
-        for (uint32_t w = tid; w < nwords; w += TPB) {
-            uint32_t p = s_aux[w];
-            uint32_t b = lbyte(p);
-            const uint32_t cls = byte_class(b);
+        // The walk over the words of two bytes or more. Each wave takes a
+        // contiguous share of them; a lane without a word takes the wave's
+        // next one (ballot + mbcnt), so lanes stay busy until the share is
+        // done. A lane follows its word's chain of longest matches, one
+        // trie step per round: the byte from the LDS copy, one 8-byte load
+        // of the slot it leads to. A word ends at the next start in s_sb;
+        // the tile's last word ends at the first start past the tile, or is
+        // open (it may run past the copy, and is then finished from global
+        // memory after the loop).
+        {
+            const uint32_t lim = nrel < CAP ? nrel : CAP;
+            const uint32_t last_end = s_after < lim ? s_after : lim;
+            const bool last_open = s_after >= CAP && lim < nrel;
+            constexpr uint32_t NWAVE = TPB / 64u;
+            const uint32_t wave = tid >> 6;
+            const uint32_t share = (nwords + NWAVE - 1u) / NWAVE;
+            const uint32_t w_hi = min(nwords, (wave + 1u) * share);
+            uint32_t next = min(nwords, wave * share);  // the wave's next word (uniform)
+            uint32_t p = 0, j = 0, slot = 0, best = 0, blen = 0, wend = 0, gp = NO_OVF;
+            unsigned long long e = 0ull;
+            bool act = false;
+            auto begin_match = [&](uint32_t q) {
+                const uint32_t b = lbyte(q);
+                e = s_root[b];
+                slot = root_base + b;
+                best = tr_tok1(e) - 1u;  // every byte is a token
+                blen = 1u;
+                j = 1u;
+                p = q;
+            };
             for (;;) {
-                uint32_t tok, len;
-                bool cut;
-                longest_match(da, s_root, root_base, p, lim, b, cls, lbyte, &tok, &len, &cut);
-                if (cut) {
-                    finish_word_global(text, t0, nrel, p, cls, da, s_root, root_base, CAP, s_flag, s_tok,
-                                       &s_ovf_pos, &s_ovf_n);
-                    break;
+                const unsigned long long need = __ballot(!act);
+                if (need) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(need >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)need, 0u));
+                    if (!act && next + below < w_hi) {
+                        const uint32_t q = s_aux[next + below];
+                        // the word's end: the next start after q
+                        wend = last_end;
+                        for (uint32_t x = q + 1u; x < TILE;) {
+                            const uint32_t m = s_sb[x >> 5] & (0xFFFFFFFFu << (x & 31u));
+                            if (m) {
+                                wend = (x & ~31u) + (__ffs(m) - 1);
+                                break;
+                            }
+                            x = (x & ~31u) + 32u;
+                        }
+                        begin_match(q);
+                        act = true;
+                    }
+                    next += (uint32_t)__popcll(need);
                 }
-                atomicOr(&s_flag[p >> 5], 1u << (p & 31u));
-                s_tok[p] = (uint16_t)tok;
-                p += len;
-                if (p >= lim) {
-                    if (p < nrel && byte_class(text[t0 + p]) == cls)
-                        finish_word_global(text, t0, nrel, p, cls, da, s_root, root_base, CAP, s_flag, s_tok,
-                                           &s_ovf_pos, &s_ovf_n);
-                    break;
+                if (__ballot(act) == 0ull) break;
+                if (act) {
+                    const uint32_t base = tr_base(e);
+                    const uint32_t q = p + j;
+                    const bool go = base != 0u && q < wend;
+                    const uint32_t addr = go ? base + lbyte(q) : 0u;
+                    const unsigned long long e2 = da[addr];
+                    if (go && tr_check(e2) == slot + 1u) {
+                        slot = addr;
+                        e = e2;
+                        const uint32_t t1 = tr_tok1(e2);
+                        if (t1) {
+                            best = t1 - 1u;
+                            blen = j + 1u;
+                        }
+                        ++j;
+                    } else {
+                        const bool open = last_open && wend == last_end;
+                        if (open && base != 0u && q >= lim) {
+                            gp = p;  // the match may go on past the LDS copy
+                            act = false;
+                        } else {
+                            atomicOr(&s_flag[p >> 5], 1u << (p & 31u));
+                            s_tok[p] = (uint16_t)best;
+                            const uint32_t np = p + blen;
+                            if (np < wend) {
+                                begin_match(np);
+                            } else {
+                                if (open && np < nrel && byte_class(text[t0 + np]) == byte_class(lbyte(p))) gp = np;
+                                act = false;
+                            }
+                        }
+                    }
                 }
-                b = lbyte(p);
-                if (byte_class(b) != cls) break;
+            }
+            if (gp != NO_OVF) {
+                const uint32_t cls = byte_class(gp < lim ? lbyte(gp) : (uint32_t)text[t0 + gp]);
+                finish_word_global(text, t0, nrel, gp, cls, da, s_root, root_base, CAP, s_flag, s_tok, &s_ovf_pos,
+                                   &s_ovf_n);
             }
         }
         __syncthreads();
@@ -284,21 +382,41 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
 
 // ---------------------------------------------------------------- pass 2: scan
 // One workgroup: pfx[t] = tokens of all tiles below t (cnt + ovf_n), and
-// *total = all of them.
+// *total = all of them. The arrays hold npad entries (a multiple of 4 TPB;
+// entries past ntiles are ignored); thread i scans entries [i per, i per +
+// per) with 16-byte loads.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_trie_scan(const uint32_t* __restrict__ cnt,
                                                    const uint32_t* __restrict__ ovf_n, uint32_t* __restrict__ pfx,
-                                                   uint32_t ntiles, uint32_t* total) {
+                                                   uint32_t ntiles, uint32_t npad, uint32_t* total) {
     __shared__ uint32_t s_w[TPB / 64];
-    const uint32_t per = (ntiles + TPB - 1u) / TPB;
-    const uint32_t lo = threadIdx.x * per, hi = lo + per < ntiles ? lo + per : ntiles;
+    const uint32_t per = npad / TPB;
+    const uint32_t lo = threadIdx.x * per;
+    const uint4* c4 = reinterpret_cast<const uint4*>(cnt + lo);
+    const uint4* o4 = reinterpret_cast<const uint4*>(ovf_n + lo);
     uint32_t sum = 0;
-    for (uint32_t t = lo; t < hi; ++t) sum += cnt[t] + ovf_n[t];
+    for (uint32_t v = 0; v < per / 4u; ++v) {
+        const uint4 c = c4[v], o = o4[v];
+        const uint32_t i = lo + 4u * v;
+        sum += (i < ntiles ? c.x + o.x : 0u) + (i + 1u < ntiles ? c.y + o.y : 0u) +
+               (i + 2u < ntiles ? c.z + o.z : 0u) + (i + 3u < ntiles ? c.w + o.w : 0u);
+    }
     uint32_t all;
     uint32_t run = block_exclusive_sum<TPB>(sum, s_w, &all);
-    for (uint32_t t = lo; t < hi; ++t) {
-        pfx[t] = run;
-        run += cnt[t] + ovf_n[t];
+    uint4* p4 = reinterpret_cast<uint4*>(pfx + lo);
+    for (uint32_t v = 0; v < per / 4u; ++v) {
+        const uint4 c = c4[v], o = o4[v];
+        const uint32_t i = lo + 4u * v;
+        uint4 r;
+        r.x = run;
+        run += i < ntiles ? c.x + o.x : 0u;
+        r.y = run;
+        run += i + 1u < ntiles ? c.y + o.y : 0u;
+        r.z = run;
+        run += i + 2u < ntiles ? c.z + o.z : 0u;
+        r.w = run;
+        run += i + 3u < ntiles ? c.w + o.w : 0u;
+        p4[v] = r;
     }
     if (threadIdx.x == 0) *total = all;
 }
