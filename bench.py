@@ -74,6 +74,64 @@ def pct(a, q):
     return float(np.percentile(a, q)) if len(a) else 0.0
 
 
+def inference_leg(args, bpe, spec, data, d, m, np, torch, time, log, source="learned above"):
+    """Greedy longest-match inference of the corpus (device-resident) with
+    the trie of merges m, timed per kernel; returns the report object."""
+    k = int(m.shape[0])
+    log("inference: trie of the %d learned merges over the same corpus, %d launches"
+        % (k, args.inference_reps))
+    with bpe.Trie(m) as tr:
+        slots, longest = tr.info()
+        n_tok, ms = tr.profile(d, args.inference_reps)
+        sample_n = min(spec.n_bytes, 16 << 20)
+        gpu_sample = None
+        if not args.no_cpu_baseline:
+            gpu_sample = tr.encode(d[:sample_n]).cpu().numpy().astype(np.uint32)
+    ms = ms.astype(np.float64)
+    per_kernel = ms.mean(axis=0)
+    ms = ms.sum(axis=1)
+    avg_ms = float(ms.mean())
+    inf_bytes = float(spec.n_bytes) + 4.0 * n_tok
+    inf_gbps = inf_bytes / (avg_ms / 1e3) / 1e9
+    inf_traffic = measured_traffic(spec.name, "trie")
+    inf_cpu = None
+    if gpu_sample is not None:
+        import oracle
+        t0 = time.perf_counter()
+        ot = oracle.trie_encode(data[:sample_n], m.cpu().numpy())
+        cpu_s = time.perf_counter() - t0
+        inf_cpu = {"value": round(sample_n / cpu_s, 1), "unit": "bytes/s", "cores": 1, "kind": "oracle",
+                   "sample": "the first %d bytes of the corpus through the C oracle (oracle/bpe_oracle.c, "
+                             "trie_encode, pointer trie), one thread, %.2f s; GPU tokens of the same bytes "
+                             "identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample)))}
+        log("inference oracle: %.2f s on %d bytes, identical: %s"
+            % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
+    inference = {
+        "metric": "trie greedy longest-match tokenization, input bytes/s",
+        "value": round(spec.n_bytes / (avg_ms / 1e3), 1),
+        "unit": "bytes/s",
+        "workload": "%s corpus (%d bytes), vocabulary of the %d merges %s (trie %d slots, "
+                    "longest string %d bytes)" % (spec.name, spec.n_bytes, k, source, slots, longest),
+        "tokens": int(n_tok),
+        "runs": len(ms),
+        "ms_per_run": {"mean": round(avg_ms, 4), "min": round(float(ms.min()), 4),
+                       "max": round(float(ms.max()), 4)},
+        "kernels_ms_per_run": {"k_trie_walk": round(float(per_kernel[0]), 4),
+                               "k_trie_scan": round(float(per_kernel[1]), 4),
+                               "k_trie_copy": round(float(per_kernel[2]), 4)},
+        "roofline": {"bound": "hbm", "kernel": "all three passes", "achieved": round(inf_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(inf_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": (round(inf_traffic["fetch_bytes_per_launch"] + inf_traffic["write_bytes_per_launch"])
+                                 if inf_traffic else None),
+                     "bytes_per_launch": round(inf_bytes), "avg_launch_ms": round(avg_ms, 5)},
+        "cpu_baseline": inf_cpu,
+    }
+    log("inference: %.3f ms per run (walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, %d tokens"
+        % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], inf_gbps, n_tok))
+
+    return inference
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +142,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="write per-iteration details to this JSON file")
     ap.add_argument("--no-inference", action="store_true", help="skip the trie inference leg")
+    ap.add_argument("--save-merges", default=None, metavar="PATH", help="write the learned merges (.npy)")
+    ap.add_argument("--inference-only", default=None, metavar="PATH",
+                    help="skip training: time inference with the merges saved in PATH (.npy) by --save-merges")
     ap.add_argument("--inference-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
@@ -121,6 +182,17 @@ def main() -> int:
     sha = corpus.sha256(data)
     d = torch.from_numpy(data).to("cuda:0")
     torch.cuda.synchronize()
+
+    if args.inference_only:
+        m = torch.from_numpy(np.load(args.inference_only, allow_pickle=False)).to("cuda:0")
+        inf = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log,
+                            source="learned by an earlier run on the same corpus")
+        out = dict(inf)
+        out.update({"n_gpus": 1, "steps": inf["runs"], "warmup": 1, "higher_is_better": True, "scaling": "weak",
+                    "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+                    "config": {"workload": inf["workload"], "corpus_bytes": spec.n_bytes}})
+        print(json.dumps(out), flush=True)
+        return 0
 
     def step(profiled: bool):
         t0 = time.perf_counter()
@@ -197,55 +269,11 @@ def main() -> int:
                          "GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, same)}
         log("oracle: %.2f s, bit-identical to the GPU result: %s" % (cpu_s, same))
 
+    if args.save_merges:
+        np.save(args.save_merges, m.cpu().numpy())
     inference = None
     if not args.no_inference:
-        log("inference: trie of the %d learned merges over the same corpus, %d launches"
-            % (k, args.inference_reps))
-        with bpe.Trie(m) as tr:
-            slots, longest = tr.info()
-            n_tok, ms = tr.profile(d, args.inference_reps)
-            sample_n = min(spec.n_bytes, 16 << 20)
-            gpu_sample = None
-            if not args.no_cpu_baseline:
-                gpu_sample = tr.encode(d[:sample_n]).cpu().numpy().astype(np.uint32)
-        ms = ms.astype(np.float64)
-        per_kernel = ms.mean(axis=0)
-        ms = ms.sum(axis=1)
-        avg_ms = float(ms.mean())
-        inf_bytes = float(spec.n_bytes) + 4.0 * n_tok
-        inf_gbps = inf_bytes / (avg_ms / 1e3) / 1e9
-        inf_cpu = None
-        if gpu_sample is not None:
-            import oracle
-            t0 = time.perf_counter()
-            ot = oracle.trie_encode(data[:sample_n], m.cpu().numpy())
-            cpu_s = time.perf_counter() - t0
-            inf_cpu = {"value": round(sample_n / cpu_s, 1), "unit": "bytes/s", "cores": 1, "kind": "oracle",
-                       "sample": "the first %d bytes of the corpus through the C oracle (oracle/bpe_oracle.c, "
-                                 "trie_encode, pointer trie), one thread, %.2f s; GPU tokens of the same bytes "
-                                 "identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample)))}
-            log("inference oracle: %.2f s on %d bytes, identical: %s"
-                % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
-        inference = {
-            "metric": "trie greedy longest-match tokenization, input bytes/s",
-            "value": round(spec.n_bytes / (avg_ms / 1e3), 1),
-            "unit": "bytes/s",
-            "workload": "%s corpus (%d bytes), vocabulary of the %d merges learned above (trie %d slots, "
-                        "longest string %d bytes)" % (spec.name, spec.n_bytes, k, slots, longest),
-            "tokens": int(n_tok),
-            "runs": len(ms),
-            "ms_per_run": {"mean": round(avg_ms, 4), "min": round(float(ms.min()), 4),
-                           "max": round(float(ms.max()), 4)},
-            "kernels_ms_per_run": {"k_trie_walk": round(float(per_kernel[0]), 4),
-                                   "k_trie_scan": round(float(per_kernel[1]), 4),
-                                   "k_trie_copy": round(float(per_kernel[2]), 4)},
-            "roofline": {"bound": "hbm", "kernel": "all three passes", "achieved": round(inf_gbps, 1),
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(inf_gbps / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "bytes_per_launch": round(inf_bytes), "avg_launch_ms": round(avg_ms, 5)},
-            "cpu_baseline": inf_cpu,
-        }
-        log("inference: %.3f ms per run (walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, %d tokens"
-            % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], inf_gbps, n_tok))
+        inference = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log)
 
     out = {
         "metric": "BPE train merges/sec + symbols/sec per merge, 256 MiB/32k merges; HBM GB/s",
