@@ -25,6 +25,9 @@ trie's stream. Its algorithmic bytes are the text read once (1 byte per
 input byte) plus the token ids written once (4 bytes per token); trie nodes
 are read from cache, and the per-tile slices are implementation traffic:
 timed, not credited.
+
+"encoding" reports encoding of the same corpus with the same merges (a
+learned list applied to new text, word by word), with the same accounting.
 """
 from __future__ import annotations
 
@@ -132,6 +135,54 @@ def inference_leg(args, bpe, spec, data, d, m, np, torch, time, log, source="lea
     return inference
 
 
+def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above"):
+    """Encoding of the corpus (device-resident) with merges m, word by word,
+    timed per kernel; returns the report object."""
+    k = int(m.shape[0])
+    log("encoding: the %d merges over the same corpus, %d runs" % (k, args.inference_reps))
+    with bpe.Encoder(m) as enc:
+        n_tok, ms = enc.profile(d, args.inference_reps)
+        sample_n = min(spec.n_bytes, 128 << 10)
+        gpu_sample = None
+        if not args.no_cpu_baseline:
+            gpu_sample = enc.encode(d[:sample_n]).cpu().numpy().astype(np.uint32)
+    ms = ms.astype(np.float64)
+    per_kernel = ms.mean(axis=0)
+    ms = ms.sum(axis=1)
+    avg_ms = float(ms.mean())
+    enc_bytes = float(spec.n_bytes) + 4.0 * n_tok
+    enc_gbps = enc_bytes / (avg_ms / 1e3) / 1e9
+    cpu = None
+    if gpu_sample is not None:
+        import oracle
+        t0 = time.perf_counter()
+        _, ot = oracle.encode(data[:sample_n], m.cpu().numpy())
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(sample_n / cpu_s, 1), "unit": "bytes/s", "cores": 1, "kind": "oracle",
+               "sample": "the first %d bytes of the corpus through the C oracle (oracle/bpe_oracle.c, encode: "
+                         "every merge applied over the whole text in order), one thread, %.2f s; GPU tokens of "
+                         "the same bytes identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample)))}
+        log("encoding oracle: %.2f s on %d bytes, identical: %s" % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
+    log("encoding: %.3f ms per run (walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, %d tokens"
+        % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], enc_gbps, n_tok))
+    return {
+        "metric": "BPE encoding of new text with a merge list, input bytes/s",
+        "value": round(spec.n_bytes / (avg_ms / 1e3), 1),
+        "unit": "bytes/s",
+        "workload": "%s corpus (%d bytes), the %d merges %s" % (spec.name, spec.n_bytes, k, source),
+        "tokens": int(n_tok),
+        "runs": len(ms),
+        "ms_per_run": {"mean": round(avg_ms, 4), "min": round(float(ms.min()), 4), "max": round(float(ms.max()), 4)},
+        "kernels_ms_per_run": {"k_enc_walk": round(float(per_kernel[0]), 4),
+                               "k_trie_scan": round(float(per_kernel[1]), 4),
+                               "k_enc_copy": round(float(per_kernel[2]), 4)},
+        "roofline": {"bound": "hbm", "kernel": "all three passes", "achieved": round(enc_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": round(enc_bytes), "avg_launch_ms": round(avg_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,7 +192,7 @@ def main() -> int:
     ap.add_argument("--merges", type=int, default=None, help="override the merge count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="write per-iteration details to this JSON file")
-    ap.add_argument("--no-inference", action="store_true", help="skip the trie inference leg")
+    ap.add_argument("--no-inference", action="store_true", help="skip the inference and encoding legs")
     ap.add_argument("--save-merges", default=None, metavar="PATH", help="write the learned merges (.npy)")
     ap.add_argument("--inference-only", default=None, metavar="PATH",
                     help="skip training: time inference with the merges saved in PATH (.npy) by --save-merges")
@@ -272,8 +323,10 @@ def main() -> int:
     if args.save_merges:
         np.save(args.save_merges, m.cpu().numpy())
     inference = None
+    encoding = None
     if not args.no_inference:
         inference = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log)
+        encoding = encode_leg(args, bpe, spec, data, d, m, np, time, log)
 
     out = {
         "metric": "BPE train merges/sec + symbols/sec per merge, 256 MiB/32k merges; HBM GB/s",
@@ -318,6 +371,7 @@ def main() -> int:
                      "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
         "inference": inference,
+        "encoding": encoding,
     }
     if args.report:
         with open(args.report, "w") as fh:

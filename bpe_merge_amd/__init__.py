@@ -75,6 +75,10 @@ _SIGS = {
     "bpe_trie_encode": (ctypes.c_int, [_vp, _vp, _sz, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_trie_profile": (ctypes.c_int, [_vp, _vp, _sz, _u32, _vp, ctypes.POINTER(_sz)]),
     "bpe_trie_free": (None, [_vp]),
+    "bpe_encoder_build": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(_vp)]),
+    "bpe_encoder_encode": (ctypes.c_int, [_vp, _vp, _sz, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_encoder_profile": (ctypes.c_int, [_vp, _vp, _sz, _u32, _vp, ctypes.POINTER(_sz)]),
+    "bpe_encoder_free": (None, [_vp]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "bpe_last_error": (ctypes.c_char_p, []),
@@ -173,7 +177,8 @@ def _merge_list(merges, device):
 def encode(data, merges, table_log2: int | None = None):
     """bpe_encode on a uint8 CUDA tensor with a merge list ([k, 2] or [k, 3];
     merge i creates id 256 + i). Returns the int32 CUDA tensor of final
-    symbols (id | 0x10000 on word starts)."""
+    symbols (id | 0x10000 on word starts). table_log2 is accepted for the
+    bpe_config but not used by encoding."""
     torch = _torch()
     if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
         raise TypeError("data must be a uint8 CUDA tensor")
@@ -190,6 +195,66 @@ def encode(data, merges, table_log2: int | None = None):
     _check(_lib.bpe_encode(data.data_ptr(), n, m.data_ptr(), m.shape[0], ctypes.byref(cfg), tokens.data_ptr(),
                            tokens.numel(), ctypes.byref(n_tok)), "bpe_encode")
     return tokens[: n_tok.value]
+
+
+class Encoder:
+    """bpe_encoder_build ... bpe_encoder_free: a merge list ([k, 2] or [k, 3];
+    merge i is id 256 + i) applied to new text word by word, lowest rank
+    first, on the current CUDA device. Tokens carry 0x10000 on word starts."""
+
+    def __init__(self, merges):
+        torch = _torch()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        m = _merge_list(merges, dev)
+        self.device = dev
+        self._h = _vp(None)
+        _check(_lib.bpe_encoder_build(m.data_ptr() if m.numel() else None, m.shape[0], ctypes.byref(self._h)),
+               "bpe_encoder_build")
+
+    def encode(self, data, out=None):
+        """Encode a uint8 CUDA tensor on the current stream; returns the int32
+        CUDA tensor of tokens (a prefix of ``out`` if given)."""
+        torch = _torch()
+        if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+            raise TypeError("data must be a uint8 CUDA tensor")
+        data = data.contiguous().reshape(-1)
+        n = data.numel()
+        if out is None:
+            out = torch.empty(max(n, 1), dtype=torch.int32, device=data.device)
+        if not (out.is_cuda and out.dtype == torch.int32 and out.is_contiguous() and out.numel() >= n):
+            raise ValueError("out must be a contiguous int32 CUDA tensor with room for n tokens")
+        n_tok = _sz(0)
+        _check(_lib.bpe_encoder_encode(self._h, data.data_ptr() if n else None, n, _stream_handle(data.device),
+                                       out.data_ptr(), out.numel(), ctypes.byref(n_tok)), "bpe_encoder_encode")
+        return out[: n_tok.value]
+
+    def profile(self, data, reps: int):
+        """bpe_encoder_profile: (n_tokens, device ms of shape [reps, 3]: walk,
+        scan and copy of each run)."""
+        import numpy as np
+        data = data.contiguous().reshape(-1)
+        ms = np.zeros(3 * max(reps, 1), dtype=np.float32)
+        n_tok = _sz(0)
+        _check(_lib.bpe_encoder_profile(self._h, data.data_ptr(), data.numel(), reps, ms.ctypes.data,
+                                        ctypes.byref(n_tok)), "bpe_encoder_profile")
+        return n_tok.value, ms[: 3 * reps].reshape(reps, 3)
+
+    def free(self) -> None:
+        if self._h:
+            _lib.bpe_encoder_free(self._h)
+            self._h = _vp(None)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
 
 
 class Trie:

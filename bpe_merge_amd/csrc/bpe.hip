@@ -26,6 +26,7 @@
 #include "kernels.hpp"
 #include "merge.hpp"
 #include "trie.hpp"
+#include "encode.hpp"
 
 using bpek::Ctl;
 
@@ -685,33 +686,6 @@ bpe_status bpe_train(const uint8_t* bytes, size_t n, uint32_t n_merges, const bp
     return st;
 }
 
-bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, uint32_t n_merges,
-                      const bpe_config* cfg, uint32_t* tokens, size_t tokens_cap, size_t* n_tokens) {
-    g_err.clear();
-    if (!n_tokens || (!merges && n_merges) || (n && !bytes)) {
-        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_tokens must be non-NULL");
-        return BPE_EINVAL;
-    }
-    if (n_merges > BPE_MAX_MERGES) {
-        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
-        return BPE_EIDSPACE;
-    }
-    if (!config_ok(n, cfg)) return BPE_EINVAL;
-    if (tokens && tokens_cap < n) {
-        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
-        return BPE_EINVAL;
-    }
-    *n_tokens = 0;
-    if (n == 0) return BPE_OK;
-    bpe_state* s = nullptr;
-    bpe_status st = bpe_init(bytes, n, cfg, &s);
-    if (st != BPE_OK) return st;
-    st = bpe_replay(s, merges, n_merges);
-    if (st == BPE_OK) st = bpe_tokens(s, tokens, tokens ? tokens_cap : 0, n_tokens);
-    bpe_free(s);
-    return st;
-}
-
 }  // extern "C"
 
 // ======================================================================== inference
@@ -1144,6 +1118,289 @@ void bpe_trie_free(bpe_trie* t) {
     if (t->tok_buf) (void)hipFree(t->tok_buf);
     if (t->stream) (void)hipStreamDestroy(t->stream);
     delete t;
+}
+
+}  // extern "C"
+
+// ======================================================================== encoding
+// A merge list applied to new text word by word, lowest rank first (equal
+// to applying its merges in learned order over the whole text; page "bpe -
+// GPU BPE Tokenizer Pipeline", "Nedir bu ya?").
+
+struct bpe_encoder {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    unsigned long long* rt = nullptr;   // rank table
+    uint32_t rt_mask = 0, rt_probes = 0;
+    uint32_t* status = nullptr;         // total, error flags, scratch used
+    uint32_t* slices = nullptr;         // per-tile token slices
+    size_t slices_cap = 0;
+    uint32_t* tiles = nullptr;          // cnt, ovf_pos, ovf_n, pfx
+    size_t tiles_cap = 0;
+    uint16_t* sym_g = nullptr;          // scratch of words too long for a tile's LDS
+    size_t sym_cap = 0;
+    uint32_t* nx_g = nullptr;
+    size_t nx_cap = 0;
+    uint16_t* rk_g = nullptr;
+    size_t rk_cap = 0;
+    uint32_t* ovf = nullptr;
+    size_t ovf_cap = 0;
+    uint8_t* text_buf = nullptr;
+    size_t text_cap = 0;
+    uint32_t* tok_buf = nullptr;
+    size_t tok_cap = 0;
+    int walk_grid = 0, copy_grid = 0;
+};
+
+namespace {
+
+constexpr int ENC_TPB = 256;
+constexpr uint32_t ENC_TILE = ENC_TPB * 16;
+constexpr uint32_t ENC_CAP = ENC_TILE + ENC_TPB * bpek::TRIE_HALO_PER_THREAD;
+constexpr size_t ENC_SCRATCH_MAX = size_t(1) << 24;  // positions of long words per call
+
+size_t enc_scratch_cap(size_t n) { return std::min(n, ENC_SCRATCH_MAX); }
+
+bpe_status enc_pools(bpe_encoder* e, size_t n) {
+    const size_t ntiles = (n + ENC_TILE - 1) / ENC_TILE;
+    const size_t sc = enc_scratch_cap(n);
+    bpe_status st = pool_grow(&e->slices, &e->slices_cap, ntiles * ENC_CAP, false);
+    if (st == BPE_OK) st = pool_grow(&e->tiles, &e->tiles_cap, 4 * size_t(trie_npad(uint32_t(ntiles))), false);
+    if (st == BPE_OK) st = pool_grow(&e->sym_g, &e->sym_cap, sc, false);
+    if (st == BPE_OK) st = pool_grow(&e->nx_g, &e->nx_cap, sc, false);
+    if (st == BPE_OK) st = pool_grow(&e->rk_g, &e->rk_cap, sc, false);
+    if (st == BPE_OK) st = pool_grow(&e->ovf, &e->ovf_cap, sc, false);
+    return st;
+}
+
+bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t* dst, hipStream_t s,
+                       hipEvent_t* ev) {
+    const uint32_t ntiles = (n + ENC_TILE - 1) / ENC_TILE;
+    const uint32_t npad = trie_npad(ntiles);
+    uint32_t* cnt = e->tiles;
+    uint32_t* ovf_pos = cnt + npad;
+    uint32_t* ovf_n = ovf_pos + npad;
+    uint32_t* pfx = ovf_n + npad;
+    const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes};
+    hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
+    hipLaunchKernelGGL(bpek::k_enc_walk<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->walk_grid)), dim3(ENC_TPB), 0,
+                       s, src, n, rt, e->slices, cnt, ovf_pos, ovf_n, ntiles, e->sym_g, e->nx_g, e->rk_g, e->ovf,
+                       e->status + 2, uint32_t(enc_scratch_cap(n)), e->status + 1);
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    hipLaunchKernelGGL(bpek::k_trie_scan<TRIE_SCAN_TPB>, dim3(1), dim3(TRIE_SCAN_TPB), 0, s, cnt, ovf_n, pfx,
+                       ntiles, npad, e->status);
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    hipLaunchKernelGGL(bpek::k_enc_copy<TRIE_COPY_TPB>, dim3(std::min<uint32_t>(ntiles, e->copy_grid)),
+                       dim3(TRIE_COPY_TPB), 0, s, e->slices, cnt, ovf_pos, ovf_n, pfx, e->ovf, dst, ntiles, ENC_CAP);
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    HIP_TRY(hipGetLastError());
+    return BPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_encoder** out) {
+    g_err.clear();
+    if (!out || (!merges && n_merges)) {
+        set_err("out must be non-NULL, and merges non-NULL when n_merges > 0");
+        return BPE_EINVAL;
+    }
+    *out = nullptr;
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    std::vector<bpe_merge> hm(n_merges);
+    if (n_merges) HIP_TRY(hipMemcpy(hm.data(), merges, sizeof(bpe_merge) * n_merges, hipMemcpyDefault));
+    // rank table: pair -> first rank; open addressing at most half full
+    size_t slots = 1024;
+    while (slots < 2 * size_t(n_merges)) slots *= 2;
+    std::vector<unsigned long long> table(slots, ~0ull);
+    uint32_t probes = 1;
+    for (uint32_t r = 0; r < n_merges; ++r) {
+        const uint32_t l = hm[r].left, rr = hm[r].right, lim = bpek::BASE + r;
+        if (l >= lim || rr >= lim) {
+            set_err("merge %u (%u, %u) names an id that does not exist before it (ids < %u)", r, l, rr, lim);
+            return BPE_EINVAL;
+        }
+        const uint32_t key = (l << 16) | rr;
+        uint32_t h = bpek::mix32(key) & uint32_t(slots - 1), p = 0;
+        bool dup = false;
+        while (table[h] != ~0ull) {
+            if (uint32_t(table[h] >> 32) == key) {
+                dup = true;  // a repeat never occurs again after the first merge of the pair
+                break;
+            }
+            h = (h + 1) & uint32_t(slots - 1);
+            ++p;
+        }
+        if (dup) continue;
+        table[h] = (static_cast<unsigned long long>(key) << 32) | r;
+        probes = std::max(probes, p + 1);
+    }
+    bpe_encoder* e = new (std::nothrow) bpe_encoder();
+    if (!e) {
+        set_err("out of host memory");
+        return BPE_ENOMEM;
+    }
+    auto fail = [&](bpe_status st) {
+        bpe_encoder_free(e);
+        return st;
+    };
+    int cus = 0, per_cu = 0;
+    if (hipGetDevice(&e->device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_enc_walk<ENC_TPB>, ENC_TPB, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        set_err("cannot query the device");
+        return fail(BPE_EHIP);
+    }
+    e->walk_grid = cus * per_cu;
+    e->copy_grid = cus * 8;
+    e->rt_mask = uint32_t(slots - 1);
+    e->rt_probes = probes;
+    if (hipStreamCreateWithFlags(&e->stream, hipStreamNonBlocking) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&e->rt), slots * sizeof(unsigned long long)) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&e->status), 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMemcpy(e->rt, table.data(), slots * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("allocating or uploading the rank table failed");
+        return fail(BPE_ENOMEM);
+    }
+    *out = e;
+    return BPE_OK;
+}
+
+bpe_status bpe_encoder_encode(bpe_encoder* e, const uint8_t* bytes, size_t n, void* stream, uint32_t* tokens,
+                              size_t tokens_cap, size_t* n_tokens) {
+    g_err.clear();
+    if (!e || !n_tokens || (n && !bytes)) {
+        set_err("encoder and n_tokens must be non-NULL, and bytes non-NULL when n > 0");
+        return BPE_EINVAL;
+    }
+    if (n > BPE_MAX_BYTES) {
+        set_err("n = %zu exceeds the limit of %llu bytes", n, (unsigned long long)BPE_MAX_BYTES);
+        return BPE_EINVAL;
+    }
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    HIP_TRY(hipSetDevice(e->device));
+    hipStream_t s = stream ? reinterpret_cast<hipStream_t>(stream) : e->stream;
+    bpe_status st = enc_pools(e, n);
+    if (st != BPE_OK) return st;
+    const uint8_t* src = bytes;
+    if (!is_device_pointer(bytes)) {
+        st = pool_grow(&e->text_buf, &e->text_cap, n, false);
+        if (st != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(e->text_buf, bytes, n, hipMemcpyHostToDevice, s));
+        src = e->text_buf;
+    }
+    uint32_t* dst = tokens;
+    if (!tokens || !is_device_pointer(tokens)) {
+        st = pool_grow(&e->tok_buf, &e->tok_cap, n, false);
+        if (st != BPE_OK) return st;
+        dst = e->tok_buf;
+    }
+    st = enc_enqueue(e, src, uint32_t(n), dst, s, nullptr);
+    if (st != BPE_OK) return st;
+    uint32_t h[4] = {0, 0, 0, 0};
+    HIP_TRY(hipMemcpyAsync(h, e->status, sizeof h, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (h[1]) {
+        set_err("words too long for the encoder's scratch (%zu positions per call)", enc_scratch_cap(n));
+        return BPE_ENOMEM;
+    }
+    if (h[0] > n) {
+        set_err("device reported %u tokens for %zu bytes", h[0], n);
+        return BPE_ESTATE;
+    }
+    *n_tokens = h[0];
+    if (tokens && dst != tokens) HIP_TRY(hipMemcpy(tokens, dst, sizeof(uint32_t) * size_t(h[0]), hipMemcpyDefault));
+    return BPE_OK;
+}
+
+bpe_status bpe_encoder_profile(bpe_encoder* e, const uint8_t* bytes, size_t n, uint32_t reps, float* ms,
+                               size_t* n_tokens) {
+    g_err.clear();
+    if (!e || !n_tokens || !bytes || n == 0 || reps == 0 || n > BPE_MAX_BYTES) {
+        set_err("encoder, bytes and n_tokens must be non-NULL, 0 < n <= BPE_MAX_BYTES and reps > 0");
+        return BPE_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(e->device));
+    if (!is_device_pointer(bytes)) {
+        set_err("bpe_encoder_profile reads device bytes only");
+        return BPE_EINVAL;
+    }
+    size_t first = 0;
+    bpe_status st = bpe_encoder_encode(e, bytes, n, nullptr, nullptr, 0, &first);
+    if (st != BPE_OK) return st;
+    std::vector<hipEvent_t>* ev = nullptr;
+    st = event_pool(e->device, 3 * size_t(reps) + 1, &ev);
+    if (st != BPE_OK) return st;
+    std::vector<hipEvent_t>& evs = *ev;
+    HIP_TRY(hipEventRecord(evs[0], e->stream));
+    for (uint32_t r = 0; r < reps; ++r) {
+        st = enc_enqueue(e, bytes, uint32_t(n), e->tok_buf, e->stream, &evs[3 * size_t(r) + 1]);
+        if (st != BPE_OK) return st;
+    }
+    uint32_t h[4] = {0, 0, 0, 0};
+    HIP_TRY(hipMemcpyAsync(h, e->status, sizeof h, hipMemcpyDeviceToHost, e->stream));
+    HIP_TRY(hipStreamSynchronize(e->stream));
+    if (h[1] || h[0] != first) {
+        set_err("repeated runs disagree (%u tokens vs %zu, error flags %u)", h[0], first, h[1]);
+        return BPE_ESTATE;
+    }
+    for (size_t i = 0; i < 3 * size_t(reps); ++i) {
+        float a = 0.f;
+        HIP_TRY(hipEventElapsedTime(&a, evs[i], evs[i + 1]));
+        if (ms) ms[i] = a;
+    }
+    *n_tokens = first;
+    return BPE_OK;
+}
+
+void bpe_encoder_free(bpe_encoder* e) {
+    if (!e) return;
+    (void)hipSetDevice(e->device);
+    if (e->stream) (void)hipStreamSynchronize(e->stream);
+    for (void* p : {(void*)e->rt, (void*)e->status, (void*)e->slices, (void*)e->tiles, (void*)e->sym_g,
+                    (void*)e->nx_g, (void*)e->rk_g, (void*)e->ovf, (void*)e->text_buf, (void*)e->tok_buf})
+        if (p) (void)hipFree(p);
+    if (e->stream) (void)hipStreamDestroy(e->stream);
+    delete e;
+}
+
+bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, uint32_t n_merges,
+                      const bpe_config* cfg, uint32_t* tokens, size_t tokens_cap, size_t* n_tokens) {
+    g_err.clear();
+    if (!n_tokens || (!merges && n_merges) || (n && !bytes)) {
+        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_tokens must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    if (!config_ok(n, cfg)) return BPE_EINVAL;
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    bpe_encoder* e = nullptr;
+    bpe_status st = bpe_encoder_build(merges, n_merges, &e);
+    if (st != BPE_OK) return st;
+    st = bpe_encoder_encode(e, bytes, n, cfg ? cfg->stream : nullptr, tokens, tokens_cap, n_tokens);
+    bpe_encoder_free(e);
+    return st;
 }
 
 }  // extern "C"

@@ -1,0 +1,375 @@
+// Encoding new text with a learned merge list, word by word (page "bpe -
+// GPU BPE Tokenizer Pipeline", "Nedir bu ya?": a learned list is applied to
+// text in the order its merges were learned; "Ne Yapar? 1": merges never
+// cross a word start).
+//
+// Applying merge k over the whole text, k = 0, 1, ..., equals merging,
+// inside each word (maximal run of one byte class), the pair of lowest rank
+// again and again, each time at all its non-overlapping occurrences left to
+// right: a pair containing id 256 + k has rank > k, so a merge never
+// creates a pair of lower rank than its own, and words never interact. One
+// pass over the text then replaces one pass per merge. The decomposition
+// is the inference kernels' (trie.hpp): a workgroup takes a tile and owns
+// the words starting in it, one-byte words are final at once, the longer
+// ones are taken by the lanes of a wave from a queue. A lane runs one
+// iteration of its word per round: find the lowest-rank pair on the word's
+// live list, merge it everywhere in the word, look up the ranks of the
+// pairs the merges made. Ranks come from a hash table of the list (pair ->
+// first rank of that pair; a repeated pair never occurs again after its
+// first merge, so later copies are dead). The output is the training
+// format: id | 0x10000 on the first token of each word.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+#include "trie.hpp"
+
+namespace bpek {
+
+constexpr uint32_t RK_NONE = 0xFFFFu;   // no such pair in the list
+constexpr uint32_t RK_STALE = 0xFFFEu;  // a pair a merge made, rank not yet looked up
+constexpr uint32_t NIL = 0xFFFFFFFFu;
+
+// Rank table: 64-bit slots key << 32 | rank, empty = all ones (the key
+// 0xFFFFFFFF = (65535, 65535) never appears in a list: an entry's ids are
+// below 256 + its index <= 65534). Linear probing, at most probes slots.
+struct RankTable {
+    const unsigned long long* slot;
+    uint32_t mask;
+    uint32_t probes;
+};
+
+__host__ __device__ __forceinline__ uint32_t rank_of(const RankTable& rt, uint32_t key) {
+    uint32_t h = mix32(key) & rt.mask;
+    for (uint32_t p = 0; p < rt.probes; ++p) {
+        const unsigned long long v = rt.slot[h];
+        const uint32_t k = (uint32_t)(v >> 32);
+        if (k == key) return (uint32_t)(v & 0xFFFFull);
+        if (k == 0xFFFFFFFFu) break;
+        h = (h + 1u) & rt.mask;
+    }
+    return RK_NONE;
+}
+
+// A word's live list: sym, next live position and rank of the pair
+// starting at each position, in LDS (16-bit, positions relative to the
+// tile) or in global scratch (positions relative to the word).
+struct LdsWord {
+    uint16_t* sym;
+    uint16_t* nx;
+    uint16_t* rk;
+    __host__ __device__ uint32_t s(uint32_t i) const { return sym[i]; }
+    __host__ __device__ uint32_t n(uint32_t i) const { return nx[i]; }
+    __host__ __device__ uint32_t r(uint32_t i) const { return rk[i]; }
+    __host__ __device__ void set_s(uint32_t i, uint32_t v) const { sym[i] = (uint16_t)v; }
+    __host__ __device__ void set_n(uint32_t i, uint32_t v) const { nx[i] = (uint16_t)v; }
+    __host__ __device__ void set_r(uint32_t i, uint32_t v) const { rk[i] = (uint16_t)v; }
+};
+struct GlobalWord {
+    uint16_t* sym;
+    uint32_t* nx;
+    uint16_t* rk;
+    __host__ __device__ uint32_t s(uint32_t i) const { return sym[i]; }
+    __host__ __device__ uint32_t n(uint32_t i) const { return nx[i]; }
+    __host__ __device__ uint32_t r(uint32_t i) const { return rk[i]; }
+    __host__ __device__ void set_s(uint32_t i, uint32_t v) const { sym[i] = (uint16_t)v; }
+    __host__ __device__ void set_n(uint32_t i, uint32_t v) const { nx[i] = v; }
+    __host__ __device__ void set_r(uint32_t i, uint32_t v) const { rk[i] = (uint16_t)v; }
+};
+
+// One iteration on the live list of a word [q, wend): the lowest-rank pair
+// (its first occurrence, from the left); if there is none the word is
+// final and this returns true. Otherwise its occurrences are merged left to
+// right (the left symbol becomes 256 + rank, the right one leaves the list;
+// after a merge the scan goes on past the new symbol, so a run of one
+// symbol is paired from its left end), and the pairs the merges made get
+// their ranks.
+template <class W>
+__host__ __device__ __forceinline__ bool merge_iteration(const W& a, uint32_t q, uint32_t wend, const RankTable& rt) {
+    uint32_t best = RK_NONE, bi = q, bprev = NIL;
+    for (uint32_t i = q, prev = NIL;;) {
+        const uint32_t j = a.n(i);
+        if (j >= wend) break;
+        const uint32_t r = a.r(i);
+        if (r < best) {
+            best = r;
+            bi = i;
+            bprev = prev;
+        }
+        prev = i;
+        i = j;
+    }
+    if (best == RK_NONE) return true;
+    const uint32_t X = BASE + best;
+    for (uint32_t i = bi, pv = bprev;;) {
+        const uint32_t j = a.n(i);
+        if (j >= wend) break;
+        if (a.r(i) == best) {
+            const uint32_t k = a.n(j);
+            a.set_s(i, X);
+            a.set_n(i, k);
+            a.set_r(i, RK_STALE);
+            if (pv != NIL) a.set_r(pv, RK_STALE);
+            pv = i;
+            i = k;
+            if (i >= wend) break;
+        } else {
+            pv = i;
+            i = j;
+        }
+    }
+    for (uint32_t i = bprev != NIL ? bprev : bi;;) {
+        const uint32_t j = a.n(i);
+        if (j >= wend) break;
+        if (a.r(i) == RK_STALE) a.set_r(i, rank_of(rt, (a.s(i) << 16) | a.s(j)));
+        i = j;
+    }
+    return false;
+}
+
+// A word from global scratch, by one thread: the bytes text[w0, w0 + len)
+// (relative positions 0 .. len) are encoded in the scratch arrays at base;
+// its tokens (id | WS on the first) are written to tok. Returns the token
+// count.
+__device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* __restrict__ text, size_t w0,
+                                                                 uint32_t len, uint16_t* sym, uint32_t* nx,
+                                                                 uint16_t* rk, RankTable rt, uint32_t* tok) {
+    const GlobalWord a{sym, nx, rk};
+    for (uint32_t i = 0; i < len; ++i) {
+        sym[i] = text[w0 + i];
+        nx[i] = i + 1u;
+    }
+    for (uint32_t i = 0; i + 1u < len; ++i) rk[i] = (uint16_t)rank_of(rt, ((uint32_t)sym[i] << 16) | sym[i + 1u]);
+    while (!merge_iteration(a, 0u, len, rt)) {
+    }
+    uint32_t c = 0;
+    for (uint32_t i = 0; i < len; i = nx[i]) tok[c++] = sym[i] | (i == 0u ? WS : 0u);
+    return c;
+}
+
+// ---------------------------------------------------------------- pass 1
+// Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x, ...
+// Outputs for tile t: tok32[t * CAP + i], i < cnt[t], the tokens of the
+// words starting in the tile that end within CAP bytes of its start; for a
+// last word running further, its tokens at ovf + ovf_pos[t] (ovf_n[t] of
+// them; NO_OVF / 0 otherwise), encoded in scratch reserved from *scratch_used
+// (capacity scratch_cap positions; past it *err is set and the word is
+// skipped). sym_g, nx_g, rk_g: the scratch arrays.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ text, uint32_t n, RankTable rt,
+                                                  uint32_t* __restrict__ tok32, uint32_t* __restrict__ cnt,
+                                                  uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
+                                                  uint32_t ntiles, uint16_t* sym_g, uint32_t* nx_g, uint16_t* rk_g,
+                                                  uint32_t* ovf, uint32_t* scratch_used, uint32_t scratch_cap,
+                                                  uint32_t* err) {
+    constexpr uint32_t TILE = TPB * 16u;
+    constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
+    constexpr uint32_t CAP = TILE + HALO;
+    constexpr uint32_t PER = CAP / TPB;
+    constexpr uint32_t NCH = (CAP + 32u) / 16u;
+    static_assert(CAP % TPB == 0 && PER <= 32, "compaction covers CAP positions, at most 32 per thread");
+
+    __shared__ __align__(16) uint8_t s_txt[NCH * 16u];  // s_txt[p + 16 + mis] = text[t0 + p]
+    __shared__ uint32_t s_flag[CAP / 32u];             // token starts
+    __shared__ uint32_t s_sb[TILE / 32u];              // word starts in the tile
+    __shared__ uint16_t s_sym[CAP], s_nx[CAP], s_rk[CAP];
+    __shared__ uint32_t s_aux[CAP];                    // word list, then staged output
+    __shared__ uint32_t s_w[TPB / 64];
+    __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after;
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t mis = (uint32_t)((uintptr_t)text & 15u);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
+    const LdsWord lw{s_sym, s_nx, s_rk};
+
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        if (tid == 0) {
+            s_ovf_pos = NO_OVF;
+            s_ovf_n = 0u;
+            s_after = CAP;
+        }
+        for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
+        for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
+        const uint32_t t0 = t * TILE;
+        const uint32_t nrel = n - t0;
+        for (uint32_t k = tid; k < NCH; k += TPB) {
+            typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+            const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
+            *reinterpret_cast<v4*>(s_txt + 16u * k) = v;
+        }
+        __syncthreads();
+        const uint32_t sh = 16u + mis;
+        auto lbyte = [&](uint32_t q) -> uint32_t { return s_txt[q + sh]; };  // q < CAP
+
+        // word starts: one-byte words are final here, the others listed
+        uint32_t multi;
+        {
+            const uint32_t p0 = 16u * tid;
+            uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+            uint32_t starts = 0, bnd = 0;
+#pragma unroll
+            for (int k = 0; k <= 16; ++k) {
+                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+                const bool inside = p0 + k < nrel;
+                const bool change = c != pc || t0 + p0 + k == 0u;
+                if (k < 16) starts |= ((inside && change) ? 1u : 0u) << k;
+                if (k >= 1) bnd |= ((!inside || change) ? 1u : 0u) << k;
+                pc = c;
+            }
+            const uint32_t single = starts & (bnd >> 1);
+            multi = starts & ~single;
+            const uint32_t sb = p0 & 31u;
+            if (starts) atomicOr(&s_sb[p0 >> 5], starts << sb);
+            if (single) {
+                atomicOr(&s_flag[p0 >> 5], single << sb);
+                for (uint32_t m = single; m; m &= m - 1u) {
+                    const uint32_t k = __ffs(m) - 1;
+                    s_sym[p0 + k] = (uint16_t)lbyte(p0 + k);
+                }
+            }
+        }
+        {
+            uint32_t after = CAP;
+            const uint32_t p0 = TILE + TRIE_HALO_PER_THREAD * tid;
+            uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+#pragma unroll
+            for (int k = 0; k < (int)TRIE_HALO_PER_THREAD; ++k) {
+                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+                if (p0 + k < nrel && c != pc && after == CAP) after = p0 + k;
+                pc = c;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) after = min(after, (uint32_t)__shfl_xor(after, o));
+            if ((tid & 63u) == 0u) atomicMin(&s_after, after);
+        }
+        uint32_t nwords;
+        uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
+        for (uint32_t m = multi; m; m &= m - 1u) s_aux[woff++] = 16u * tid + (__ffs(m) - 1);
+        __syncthreads();
+
+        // the words of two bytes or more: a wave queue, one iteration of a
+        // lane's word per round
+        {
+            const uint32_t lim = nrel < CAP ? nrel : CAP;
+            const uint32_t last_end = s_after < lim ? s_after : lim;
+            const bool last_open = s_after >= CAP && lim < nrel;
+            constexpr uint32_t NWAVE = TPB / 64u;
+            const uint32_t wave = tid >> 6;
+            const uint32_t share = (nwords + NWAVE - 1u) / NWAVE;
+            const uint32_t w_hi = min(nwords, (wave + 1u) * share);
+            uint32_t next = min(nwords, wave * share);
+            uint32_t q = 0, wend = 0, gq = NO_OVF;
+            bool act = false;
+            for (;;) {
+                const unsigned long long need = __ballot(!act);
+                if (need) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(need >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)need, 0u));
+                    if (!act && next + below < w_hi) {
+                        q = s_aux[next + below];
+                        wend = last_end;
+                        for (uint32_t x = q + 1u; x < TILE;) {
+                            const uint32_t m = s_sb[x >> 5] & (0xFFFFFFFFu << (x & 31u));
+                            if (m) {
+                                wend = (x & ~31u) + (__ffs(m) - 1);
+                                break;
+                            }
+                            x = (x & ~31u) + 32u;
+                        }
+                        if (last_open && wend == last_end) {
+                            gq = q;  // runs past the copy: encoded from global memory below
+                        } else {
+                            for (uint32_t i = q; i < wend; ++i) {
+                                s_sym[i] = (uint16_t)lbyte(i);
+                                s_nx[i] = (uint16_t)(i + 1u);
+                            }
+                            for (uint32_t i = q; i + 1u < wend; ++i)
+                                s_rk[i] = (uint16_t)rank_of(rt, (lbyte(i) << 16) | lbyte(i + 1u));
+                            act = true;
+                        }
+                    }
+                    next += (uint32_t)__popcll(need);
+                }
+                if (__ballot(act) == 0ull) break;
+                if (act && merge_iteration(lw, q, wend, rt)) {
+                    for (uint32_t i = q; i < wend; i = s_nx[i]) atomicOr(&s_flag[i >> 5], 1u << (i & 31u));
+                    act = false;
+                }
+            }
+            if (gq != NO_OVF) {
+                // the word's end: the first class change past the copy
+                const uint32_t cls = byte_class(lbyte(gq));
+                uint32_t e = lim;
+                while (e < nrel && byte_class(text[(size_t)t0 + e]) == cls) ++e;
+                const uint32_t len = e - gq;
+                const uint32_t at = atomicAdd(scratch_used, len);
+                if (at + len > scratch_cap || at + len < at) {
+                    atomicOr(err, 1u);
+                } else {
+                    s_ovf_pos = at;
+                    s_ovf_n = encode_word_global(text, (size_t)t0 + gq, len, sym_g + at, nx_g + at, rk_g + at, rt,
+                                                 ovf + at);
+                }
+            }
+        }
+        __syncthreads();
+
+        // compaction: final symbols at the recorded starts, WS on word starts
+        uint32_t bits;
+        {
+            const uint32_t lo = PER * tid, wi = lo >> 5, sb = lo & 31u;
+            const uint32_t w0 = s_flag[wi];
+            const uint32_t w1 = (wi + 1u < CAP / 32u) ? s_flag[wi + 1u] : 0u;
+            const unsigned long long both = ((unsigned long long)w1 << 32) | w0;
+            bits = (uint32_t)(both >> sb) & (uint32_t)((1ull << PER) - 1ull);
+        }
+        uint32_t nlds;
+        uint32_t off = block_exclusive_sum<TPB>(__popc(bits), s_w, &nlds);
+        for (uint32_t m = bits; m; m &= m - 1u) {
+            const uint32_t i = PER * tid + (__ffs(m) - 1);
+            const bool ws = i < TILE && ((s_sb[i >> 5] >> (i & 31u)) & 1u);
+            s_aux[off++] = (uint32_t)s_sym[i] | (ws ? WS : 0u);
+        }
+        __syncthreads();
+        uint32_t* dst = tok32 + (size_t)t * CAP;
+        for (uint32_t i = tid; i < nlds; i += TPB) dst[i] = s_aux[i];
+        if (tid == 0) {
+            cnt[t] = nlds;
+            ovf_pos[t] = s_ovf_pos;
+            ovf_n[t] = s_ovf_n;
+        }
+    }
+}
+
+// status[0] total tokens (written by the scan), status[1] error flags,
+// status[2] scratch positions reserved
+__global__ void k_enc_init(uint32_t* status) {
+    if (threadIdx.x < 4u && blockIdx.x == 0) status[threadIdx.x] = 0u;
+}
+
+// ---------------------------------------------------------------- pass 3: copy
+// Tile slices to their places in out, then the tokens of a tile's long last
+// word from the overflow area.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ tok32,
+                                                  const uint32_t* __restrict__ cnt,
+                                                  const uint32_t* __restrict__ ovf_pos,
+                                                  const uint32_t* __restrict__ ovf_n,
+                                                  const uint32_t* __restrict__ pfx, const uint32_t* __restrict__ ovf,
+                                                  uint32_t* __restrict__ out, uint32_t ntiles, uint32_t cap) {
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint32_t c = cnt[t], base = pfx[t], no = ovf_n[t];
+        const uint32_t* src = tok32 + (size_t)t * cap;
+        for (uint32_t i = threadIdx.x; i < c; i += TPB) out[base + i] = src[i];
+        if (no) {
+            const uint32_t* o = ovf + ovf_pos[t];
+            for (uint32_t i = threadIdx.x; i < no; i += TPB) out[base + c + i] = o[i];
+        }
+    }
+}
+
+}  // namespace bpek

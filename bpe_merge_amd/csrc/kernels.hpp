@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
 
 // Murmur3 32-bit finalizer: spreads packed pair keys; the low bits pick an
 // LDS bucket, the top 8 bits the partition.
-__device__ __forceinline__ uint32_t mix32(uint32_t h) {
+__host__ __device__ __forceinline__ uint32_t mix32(uint32_t h) {
     h ^= h >> 16;
     h *= 0x85ebca6bu;
     h ^= h >> 13;

@@ -164,11 +164,50 @@ bpe_status bpe_pair_counts(bpe_state *s, uint32_t *keys, uint32_t *counts, size_
    error), BPE_ETABLE, BPE_EHIP. */
 bpe_status bpe_replay(bpe_state *s, const bpe_merge *merges, uint32_t k);
 
-/* Encode bytes[0..n) with a learned merge list: bpe_init, bpe_replay of all
-   n_merges merges, then the final symbols (id | 0x10000 on word starts) to
-   tokens (host or device, capacity tokens_cap >= n, or NULL to get only
-   the length in *n_tokens). Equal to training's tokens when the list was
-   learned on the same bytes. Errors as bpe_init and bpe_replay. */
+/* ---------------------------------------------------------------- encoding
+   Encoding text with a learned merge list (page "bpe - GPU BPE Tokenizer
+   Pipeline", "Nedir bu ya?": the list is applied in the order it was
+   learned; "Ne Yapar? 1": no merge crosses a word start). The result equals
+   applying merge k, k = 0, 1, ..., to every non-overlapping occurrence left
+   to right over the whole tagged text, and is computed word by word, the
+   lowest-rank pair first. Tokens are in the training format: id | 0x10000 on
+   the first token of each word. A pair listed twice acts at its first rank
+   (it never occurs again after that merge). */
+typedef struct bpe_encoder bpe_encoder;
+
+/* Build the rank table of merges[0..n_merges) (host or device; counts are
+   not read) on the current device and create the encoder's stream.
+   Errors: BPE_EINVAL (NULL out, an id that does not exist before its
+   merge), BPE_EIDSPACE (above 65,280 merges), BPE_ENOMEM, BPE_EHIP. */
+bpe_status bpe_encoder_build(const bpe_merge *merges, uint32_t n_merges, bpe_encoder **out);
+
+/* Encode bytes[0..n) (host or device) on stream (a hipStream_t, or NULL for
+   the encoder's own). tokens (host or device, capacity tokens_cap >= n, or
+   NULL for the count only) receive the tokens, *n_tokens their count.
+   Three kernels (walk, scan, copy), a wait for the total and a sized copy
+   for host tokens. Device buffers are pooled in the encoder (about 6 bytes
+   per input byte, plus scratch of 12 bytes per position for words that do
+   not fit a tile's LDS, at most 2^24 positions per call), so calls on one
+   encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
+   NULL bytes with n > 0, n > BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM
+   (also: words past a tile's LDS longer than the scratch in total),
+   BPE_EHIP. */
+bpe_status bpe_encoder_encode(bpe_encoder *e, const uint8_t *bytes, size_t n, void *stream, uint32_t *tokens,
+                              size_t tokens_cap, size_t *n_tokens);
+
+/* Time the encoder's kernels: bpe_encoder_encode of device bytes once, then
+   reps runs back to back on the encoder's stream with a HIP event after
+   each kernel; ms (3 * reps entries, or NULL): walk (with its small init
+   kernel), scan and copy times of each run. */
+bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, uint32_t reps, float *ms,
+                               size_t *n_tokens);
+
+/* Release the encoder and its buffers. NULL is a no-op. */
+void bpe_encoder_free(bpe_encoder *e);
+
+/* One-shot encoding: bpe_encoder_build, bpe_encoder_encode on cfg's stream
+   (cfg may be NULL; its table size and workspace are not used),
+   bpe_encoder_free. Errors as those calls, and BPE_EINVAL for a bad cfg. */
 bpe_status bpe_encode(const uint8_t *bytes, size_t n, const bpe_merge *merges, uint32_t n_merges,
                       const bpe_config *cfg, uint32_t *tokens, size_t tokens_cap, size_t *n_tokens);
 

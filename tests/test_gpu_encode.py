@@ -99,3 +99,44 @@ def test_replay_rejects_an_unknown_id_and_the_state_stays_usable(bpe):
         om, ot, _ = oracle.train_chunks(d, 10)
         assert np.array_equal(_np(st.merges()).astype(np.int64), om)
         assert np.array_equal(_np(st.tokens()).astype(np.uint32), ot)
+
+
+def test_encoder_object_repeated_calls_and_count(bpe):
+    learn = corpus.generate(corpus.CONFIGS[4].scaled(300_000, seed=71))
+    om, _, _ = oracle.train_chunks(learn, 700)
+    with bpe.Encoder(om) as e:
+        for i, n in enumerate((5, 1_500_000, 4095, 4096, 4097, 5121, 70_000)):
+            text = corpus.generate(corpus.CONFIGS[4].scaled(n, seed=720 + i))
+            _say("encoder call %d n=%d" % (i, n))
+            _, ot = oracle.encode(text, om)
+            got = _np(e.encode(_dev(text))).astype(np.uint32)
+            assert np.array_equal(got, ot), (i, n)
+
+
+def test_encoder_words_longer_than_a_tile(bpe):
+    # runs past a tile's LDS range are encoded from global scratch
+    merges = [(97, 97), (256, 256), (257, 257), (258, 97), (98, 98), (260, 260), (256, 97)]
+    parts = [b"x" * 3, b"a" * 20_001, b" ", b"b" * 7_000, b"ab" * 3_000, b" ", b"a" * 5_000, b"1" * 9_999]
+    text = np.frombuffer(b"".join(parts), np.uint8)
+    with bpe.Encoder(merges) as e:
+        for shift in (0, 7, 4090):
+            tt = np.concatenate([np.full(shift, 32, np.uint8), text])
+            _say("encoder long words shift=%d" % shift)
+            _, ot = oracle.encode(tt, merges)
+            assert np.array_equal(_np(e.encode(_dev(tt))).astype(np.uint32), ot), shift
+
+
+def test_encoder_host_input_and_output_through_the_abi(bpe):
+    import ctypes
+    learn = corpus.generate(corpus.CONFIGS[2].scaled(100_000, seed=81))
+    om, _, _ = oracle.train_chunks(learn, 300)
+    text = corpus.generate(corpus.CONFIGS[2].scaled(40_000, seed=82))
+    _, ot = oracle.encode(text, om)
+    with bpe.Encoder(om) as e:
+        out = np.zeros(text.size, np.uint32)
+        n_tok = ctypes.c_size_t(0)
+        st = bpe._lib.bpe_encoder_encode(e._h, text.ctypes.data, text.size, None, out.ctypes.data, out.size,
+                                         ctypes.byref(n_tok))
+        assert st == 0 and np.array_equal(out[: n_tok.value], ot)
+        st = bpe._lib.bpe_encoder_encode(e._h, text.ctypes.data, text.size, None, None, 0, ctypes.byref(n_tok))
+        assert st == 0 and n_tok.value == ot.size
