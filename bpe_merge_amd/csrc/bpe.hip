@@ -1131,6 +1131,7 @@ struct bpe_encoder {
     int device = 0;
     hipStream_t stream = nullptr;
     unsigned long long* rt = nullptr;   // rank table
+    uint16_t* rt_bytes = nullptr;       // rank of every byte pair
     uint32_t rt_mask = 0, rt_probes = 0;
     uint32_t* status = nullptr;         // total, error flags, scratch used
     uint32_t* slices = nullptr;         // per-tile token slices
@@ -1181,7 +1182,7 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
     uint32_t* ovf_pos = cnt + npad;
     uint32_t* ovf_n = ovf_pos + npad;
     uint32_t* pfx = ovf_n + npad;
-    const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes};
+    const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes, e->rt_bytes};
     hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
     hipLaunchKernelGGL(bpek::k_enc_walk<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->walk_grid)), dim3(ENC_TPB), 0,
                        s, src, n, rt, e->slices, cnt, ovf_pos, ovf_n, ntiles, e->sym_g, e->nx_g, e->rk_g, e->ovf,
@@ -1218,6 +1219,7 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
     size_t slots = 1024;
     while (slots < 2 * size_t(n_merges)) slots *= 2;
     std::vector<unsigned long long> table(slots, ~0ull);
+    std::vector<uint16_t> byte_ranks(65536, uint16_t(bpek::RK_NONE));
     uint32_t probes = 1;
     for (uint32_t r = 0; r < n_merges; ++r) {
         const uint32_t l = hm[r].left, rr = hm[r].right, lim = bpek::BASE + r;
@@ -1239,6 +1241,7 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
         if (dup) continue;
         table[h] = (static_cast<unsigned long long>(key) << 32) | r;
         probes = std::max(probes, p + 1);
+        if (l < bpek::BASE && rr < bpek::BASE) byte_ranks[(l << 8) | rr] = uint16_t(r);
     }
     bpe_encoder* e = new (std::nothrow) bpe_encoder();
     if (!e) {
@@ -1265,7 +1268,9 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
     if (hipStreamCreateWithFlags(&e->stream, hipStreamNonBlocking) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&e->rt), slots * sizeof(unsigned long long)) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&e->status), 4 * sizeof(uint32_t)) != hipSuccess ||
-        hipMemcpy(e->rt, table.data(), slots * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess) {
+        hipMalloc(reinterpret_cast<void**>(&e->rt_bytes), 65536 * sizeof(uint16_t)) != hipSuccess ||
+        hipMemcpy(e->rt, table.data(), slots * sizeof(unsigned long long), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(e->rt_bytes, byte_ranks.data(), 65536 * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipGetLastError();
         set_err("allocating or uploading the rank table failed");
         return fail(BPE_ENOMEM);
@@ -1370,7 +1375,7 @@ void bpe_encoder_free(bpe_encoder* e) {
     if (!e) return;
     (void)hipSetDevice(e->device);
     if (e->stream) (void)hipStreamSynchronize(e->stream);
-    for (void* p : {(void*)e->rt, (void*)e->status, (void*)e->slices, (void*)e->tiles, (void*)e->sym_g,
+    for (void* p : {(void*)e->rt, (void*)e->rt_bytes, (void*)e->status, (void*)e->slices, (void*)e->tiles, (void*)e->sym_g,
                     (void*)e->nx_g, (void*)e->rk_g, (void*)e->ovf, (void*)e->text_buf, (void*)e->tok_buf})
         if (p) (void)hipFree(p);
     if (e->stream) (void)hipStreamDestroy(e->stream);

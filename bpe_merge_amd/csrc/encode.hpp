@@ -40,6 +40,7 @@ struct RankTable {
     const unsigned long long* slot;
     uint32_t mask;
     uint32_t probes;
+    const uint16_t* bytes;  // rank of every byte pair, 256 x 256 (RK_NONE if absent)
 };
 
 __host__ __device__ __forceinline__ uint32_t rank_of(const RankTable& rt, uint32_t key) {
@@ -142,7 +143,7 @@ __device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* 
         sym[i] = text[w0 + i];
         nx[i] = i + 1u;
     }
-    for (uint32_t i = 0; i + 1u < len; ++i) rk[i] = (uint16_t)rank_of(rt, ((uint32_t)sym[i] << 16) | sym[i + 1u]);
+    for (uint32_t i = 0; i + 1u < len; ++i) rk[i] = rt.bytes[((uint32_t)sym[i] << 8) | sym[i + 1u]];
     while (!merge_iteration(a, 0u, len, rt)) {
     }
     uint32_t c = 0;
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
     __shared__ uint32_t s_flag[CAP / 32u];             // token starts
     __shared__ uint32_t s_sb[TILE / 32u];              // word starts in the tile
     __shared__ uint16_t s_sym[CAP], s_nx[CAP], s_rk[CAP];
-    __shared__ uint32_t s_aux[CAP];                    // word list, then staged output
+    __shared__ uint16_t s_aux[CAP];                    // word list, then staged output ids
+    __shared__ uint32_t s_ws[CAP / 32u];               // staged output: word-start bits
     __shared__ uint32_t s_w[TPB / 64];
     __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after;
 
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
         }
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
         for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
+        for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_ws[i] = 0u;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
         for (uint32_t k = tid; k < NCH; k += TPB) {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
         }
         uint32_t nwords;
         uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
-        for (uint32_t m = multi; m; m &= m - 1u) s_aux[woff++] = 16u * tid + (__ffs(m) - 1);
+        for (uint32_t m = multi; m; m &= m - 1u) s_aux[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
         __syncthreads();
 
         // the words of two bytes or more: a wave queue, one iteration of a
@@ -287,8 +290,18 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                                 s_sym[i] = (uint16_t)lbyte(i);
                                 s_nx[i] = (uint16_t)(i + 1u);
                             }
-                            for (uint32_t i = q; i + 1u < wend; ++i)
-                                s_rk[i] = (uint16_t)rank_of(rt, (lbyte(i) << 16) | lbyte(i + 1u));
+                            // ranks of the byte pairs: eight loads in flight, then the stores
+                            for (uint32_t i = q; i + 1u < wend; i += 8u) {
+                                uint32_t r[8];
+#pragma unroll
+                                for (int u = 0; u < 8; ++u) {
+                                    const uint32_t p = i + (uint32_t)u;
+                                    r[u] = p + 1u < wend ? rt.bytes[(lbyte(p) << 8) | lbyte(p + 1u)] : 0u;
+                                }
+#pragma unroll
+                                for (int u = 0; u < 8; ++u)
+                                    if (i + (uint32_t)u + 1u < wend) s_rk[i + u] = (uint16_t)r[u];
+                            }
                             act = true;
                         }
                     }
@@ -331,12 +344,12 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
         uint32_t off = block_exclusive_sum<TPB>(__popc(bits), s_w, &nlds);
         for (uint32_t m = bits; m; m &= m - 1u) {
             const uint32_t i = PER * tid + (__ffs(m) - 1);
-            const bool ws = i < TILE && ((s_sb[i >> 5] >> (i & 31u)) & 1u);
-            s_aux[off++] = (uint32_t)s_sym[i] | (ws ? WS : 0u);
+            if (i < TILE && ((s_sb[i >> 5] >> (i & 31u)) & 1u)) atomicOr(&s_ws[off >> 5], 1u << (off & 31u));
+            s_aux[off++] = s_sym[i];
         }
         __syncthreads();
         uint32_t* dst = tok32 + (size_t)t * CAP;
-        for (uint32_t i = tid; i < nlds; i += TPB) dst[i] = s_aux[i];
+        for (uint32_t i = tid; i < nlds; i += TPB) dst[i] = (uint32_t)s_aux[i] | (((s_ws[i >> 5] >> (i & 31u)) & 1u) << 16);
         if (tid == 0) {
             cnt[t] = nlds;
             ovf_pos[t] = s_ovf_pos;
