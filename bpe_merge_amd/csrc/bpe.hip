@@ -878,6 +878,18 @@ bpe_status build_double_array(const std::vector<bpe_merge>& hm, std::vector<unsi
     return BPE_OK;
 }
 
+// A merge list from host or device memory into host memory: host lists are
+// copied without touching the device, so a bad list is rejected before any
+// device call.
+bpe_status copy_merges(const bpe_merge* merges, uint32_t n_merges, bpe_merge* out) {
+    if (!n_merges) return BPE_OK;
+    if (is_device_pointer(merges))
+        HIP_TRY(hipMemcpy(out, merges, sizeof(bpe_merge) * n_merges, hipMemcpyDeviceToHost));
+    else
+        std::memcpy(out, merges, sizeof(bpe_merge) * n_merges);
+    return BPE_OK;
+}
+
 template <typename T>
 bpe_status pool_grow(T** p, size_t* cap, size_t need, bool zero) {
     if (*cap >= need) return BPE_OK;
@@ -911,10 +923,11 @@ bpe_status bpe_trie_build(const bpe_merge* merges, uint32_t n_merges, bpe_trie**
         return BPE_EIDSPACE;
     }
     std::vector<bpe_merge> hm(n_merges);
-    if (n_merges) HIP_TRY(hipMemcpy(hm.data(), merges, sizeof(bpe_merge) * n_merges, hipMemcpyDefault));
+    bpe_status st = copy_merges(merges, n_merges, hm.data());
+    if (st != BPE_OK) return st;
     std::vector<unsigned long long> da;
     uint32_t root_base = 0, max_len = 0;
-    bpe_status st = build_double_array(hm, &da, &root_base, &max_len);
+    st = build_double_array(hm, &da, &root_base, &max_len);
     if (st != BPE_OK) return st;
 
     bpe_trie* t = new (std::nothrow) bpe_trie();
@@ -1214,7 +1227,8 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
         return BPE_EIDSPACE;
     }
     std::vector<bpe_merge> hm(n_merges);
-    if (n_merges) HIP_TRY(hipMemcpy(hm.data(), merges, sizeof(bpe_merge) * n_merges, hipMemcpyDefault));
+    const bpe_status cst = copy_merges(merges, n_merges, hm.data());
+    if (cst != BPE_OK) return cst;
     // rank table: pair -> first rank; open addressing at most half full
     size_t slots = 1024;
     while (slots < 2 * size_t(n_merges)) slots *= 2;

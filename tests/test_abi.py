@@ -140,3 +140,37 @@ def test_encode_and_replay_argument_validation_before_any_device_call(bpe):
     # an empty text is valid and needs no device
     assert lib.bpe_encode(None, 0, ctypes.addressof(merges), 1, None, None, 0, ctypes.byref(n_tok)) == bpe.OK
     assert n_tok.value == 0
+
+
+def _merges(bpe, pairs):
+    arr = (bpe.Merge * max(len(pairs), 1))()
+    for i, (left, right) in enumerate(pairs):
+        arr[i].left, arr[i].right, arr[i].count = left, right, 0
+    return arr
+
+
+def test_trie_and_encoder_reject_bad_lists_before_any_device_call(bpe):
+    lib = bpe._lib
+    h = ctypes.c_void_p()
+    for build in (lib.bpe_trie_build, lib.bpe_encoder_build):
+        assert build(None, 1, ctypes.byref(h)) == bpe.EINVAL                       # NULL merges
+        assert build(ctypes.addressof(_merges(bpe, [(97, 98)])), 1, None) == bpe.EINVAL  # NULL out
+        assert build(ctypes.addressof(_merges(bpe, [(97, 256)])), 1, ctypes.byref(h)) == bpe.EINVAL
+        assert build(ctypes.addressof(_merges(bpe, [(97, 98), (300, 97)])), 2, ctypes.byref(h)) == bpe.EINVAL
+        assert build(ctypes.addressof(_merges(bpe, [(97, 98)])), 65281, ctypes.byref(h)) == bpe.EIDSPACE
+        assert not h.value
+    # a merge joining two byte classes cannot be part of a longest-match vocabulary
+    assert lib.bpe_trie_build(ctypes.addressof(_merges(bpe, [(97, 32)])), 1, ctypes.byref(h)) == bpe.EINVAL
+    assert "byte classes" in lib.bpe_last_error().decode()
+
+
+def test_trie_and_encoder_encode_argument_validation(bpe):
+    lib = bpe._lib
+    buf = (ctypes.c_uint8 * 16)()
+    n_tok = ctypes.c_size_t(7)
+    for enc in (lib.bpe_trie_encode, lib.bpe_encoder_encode):
+        assert enc(None, ctypes.addressof(buf), 16, None, None, 0, ctypes.byref(n_tok)) == bpe.EINVAL
+    for prof in (lib.bpe_trie_profile, lib.bpe_encoder_profile):
+        assert prof(None, ctypes.addressof(buf), 16, 1, None, ctypes.byref(n_tok)) == bpe.EINVAL
+    lib.bpe_trie_free(None)
+    lib.bpe_encoder_free(None)
