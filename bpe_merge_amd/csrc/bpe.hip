@@ -33,7 +33,7 @@ using bpek::Ctl;
 namespace {
 
 // launch shapes
-constexpr int MERGE_TPB = 512;
+constexpr int MERGE_TPB = 1024;
 constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
 constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
 constexpr int TAG_TPB = 256;
