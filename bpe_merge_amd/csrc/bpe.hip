@@ -33,9 +33,15 @@ using bpek::Ctl;
 namespace {
 
 // launch shapes
-constexpr int MERGE_TPB = 1024;
+// The merge pass runs 1024-thread workgroups on 16384-symbol tiles (one per
+// CU, half the look-backs and tile-counter atomics per symbol), or, when a
+// corpus has fewer than two such tiles per CU, 512-thread workgroups on
+// 8192-symbol tiles (two per CU) so that more of the chip takes part.
+constexpr int MERGE_TPB_BIG = 1024;
+constexpr int MERGE_TPB_SMALL = 512;
 constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
-constexpr int TILE = MERGE_TPB * 16;       // symbols per scan tile (16 per thread)
+constexpr int TILE = MERGE_TPB_BIG * 16;   // the larger tile: symbol buffers are padded to it
+constexpr int TILE_SMALL = MERGE_TPB_SMALL * 16;
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 constexpr int FIND_TPB = 256;
@@ -75,9 +81,9 @@ uint32_t table_log2_for(size_t n, const bpe_config* cfg) {
     return std::min<uint32_t>(22, std::max<uint32_t>(12, l));
 }
 
-// Workgroups of the merge and tag passes: enough to fill the chip, never
-// more than there are tiles to hand out.
-size_t grid_bound(size_t n) { return (n + TILE - 1) / TILE + 1; }
+// Workgroups of the tag pass: enough to fill the chip, never more than
+// there are chunks to hand out.
+size_t tag_grid_bound(size_t n) { return (n + TAG_TPB * 16 - 1) / (TAG_TPB * 16) + 1; }
 
 // The global table counts as full at 7/8 load (linear probing stays short).
 uint32_t table_limit(uint32_t tlog2) { return uint32_t((1ull << tlog2) - (1ull << tlog2) / 8); }
@@ -102,7 +108,7 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     L.table = a;
     a = align_up(a + 8 * (size_t(1) << tlog2), 256);
     // at least 512 words: the look-back copies a 512-word window from index 0
-    L.max_tiles = std::max<uint32_t>(uint32_t((n + TILE - 1) / TILE) + 1, 512);
+    L.max_tiles = std::max<uint32_t>(uint32_t((n + TILE_SMALL - 1) / TILE_SMALL) + 1, 512);
     L.status = a;
     a = align_up(a + 8 * size_t(L.max_tiles), 256);
     L.merges = a;
@@ -165,6 +171,7 @@ struct bpe_state {
     uint32_t* fpairs = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
     int merge_grid = 0, tag_grid = 0, fill_grid = 0, find_grid = 0;
+    int merge_tpb = MERGE_TPB_BIG;
     bool poisoned = false;   // a device error was seen
 
     uint32_t slots() const { return 1u << tlog2; }
@@ -179,9 +186,14 @@ void launch_find_max(bpe_state* s) {
 }
 
 void launch_merge(bpe_state* s) {
-    hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB), 0, s->stream,
-                       s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                       uint32_t(s->find_grid), s->merges);
+    if (s->merge_tpb == MERGE_TPB_BIG)
+        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG), 0,
+                           s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           uint32_t(s->find_grid), s->merges);
+    else
+        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_SMALL),
+                           0, s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           uint32_t(s->find_grid), s->merges);
 }
 
 void launch_force(bpe_state* s) {
@@ -348,11 +360,17 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         return fail(BPE_EHIP);
     }
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB, MERGE_LT>,
-                                                     MERGE_TPB, 0);
+    s->merge_tpb = (n + TILE - 1) / TILE >= 2 * size_t(cus) ? MERGE_TPB_BIG : MERGE_TPB_SMALL;
+    if (s->merge_tpb == MERGE_TPB_BIG)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>,
+                                                         MERGE_TPB_BIG, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>,
+                                                         MERGE_TPB_SMALL, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, grid_bound(n)));
-    s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, grid_bound(n)));
+    const size_t merge_tile = size_t(s->merge_tpb) * 16;
+    s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));
+    s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, tag_grid_bound(n)));
     s->fill_grid = cus * 4;
     // four sweep workgroups per CU (one round of loads each on the largest
     // default table), fewer for small tables; each merge workgroup reads

@@ -205,3 +205,14 @@ def test_bench_launch_path_matches_train(bpe):
         assert np.array_equal(st.tokens().cpu().numpy().astype(np.uint32), gt)
     om, ot, _ = oracle.train_chunks(d, 300)
     assert np.array_equal(gm, om) and np.array_equal(gt, ot)
+
+
+def test_large_corpus_uses_the_large_tiles_and_matches(bpe):
+    # above 2 x 256 tiles of 16384 symbols the merge pass runs 1024-thread
+    # workgroups on 16384-symbol tiles; below, 512 threads on 8192
+    d = corpus.generate(corpus.CONFIGS[3].scaled(10_000_000, seed=91))
+    _say("train 10 MB, 400 merges")
+    gm, gt = bpe.train(_dev(d), 400, 21)
+    om, ot, _ = oracle.train_chunks(d, 400)
+    assert np.array_equal(gm.cpu().numpy().astype(np.int64), om)
+    assert np.array_equal(gt.cpu().numpy().astype(np.uint32), ot)
