@@ -72,6 +72,36 @@ def measured_traffic(workload: str, kernel: str):
     return t
 
 
+def cpu_facts() -> dict:
+    """The host CPU model and core count, for the CPU baseline."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cores": os.cpu_count()}
+
+
+class one_core:
+    """Pin this process to one core while the oracle is timed (it is
+    single-threaded), and restore the previous affinity afterwards."""
+
+    def __enter__(self):
+        self.prev = None
+        if hasattr(os, "sched_getaffinity"):
+            self.prev = os.sched_getaffinity(0)
+            os.sched_setaffinity(0, {min(self.prev)})
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            os.sched_setaffinity(0, self.prev)
+
+
 def pct(a, q):
     import numpy as np
     return float(np.percentile(a, q)) if len(a) else 0.0
@@ -100,13 +130,16 @@ def inference_leg(args, bpe, spec, data, d, m, np, torch, time, log, source="lea
     inf_cpu = None
     if gpu_sample is not None:
         import oracle
-        t0 = time.perf_counter()
-        ot = oracle.trie_encode(data[:sample_n], m.cpu().numpy())
-        cpu_s = time.perf_counter() - t0
+        mh = m.cpu().numpy()
+        with one_core():
+            t0 = time.perf_counter()
+            ot = oracle.trie_encode(data[:sample_n], mh)
+            cpu_s = time.perf_counter() - t0
         inf_cpu = {"value": round(sample_n / cpu_s, 1), "unit": "bytes/s", "cores": 1, "kind": "oracle",
                    "sample": "the first %d bytes of the corpus through the C oracle (oracle/bpe_oracle.c, "
                              "trie_encode, pointer trie), one thread, %.2f s; GPU tokens of the same bytes "
-                             "identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample)))}
+                             "identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample))),
+                   "pinned": "one core (sched_setaffinity)", **cpu_facts()}
         log("inference oracle: %.2f s on %d bytes, identical: %s"
             % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
     inference = {
@@ -155,13 +188,16 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
     cpu = None
     if gpu_sample is not None:
         import oracle
-        t0 = time.perf_counter()
-        _, ot = oracle.encode(data[:sample_n], m.cpu().numpy())
-        cpu_s = time.perf_counter() - t0
+        mh = m.cpu().numpy()
+        with one_core():
+            t0 = time.perf_counter()
+            _, ot = oracle.encode(data[:sample_n], mh)
+            cpu_s = time.perf_counter() - t0
         cpu = {"value": round(sample_n / cpu_s, 1), "unit": "bytes/s", "cores": 1, "kind": "oracle",
                "sample": "the first %d bytes of the corpus through the C oracle (oracle/bpe_oracle.c, encode: "
                          "every merge applied over the whole text in order), one thread, %.2f s; GPU tokens of "
-                         "the same bytes identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample)))}
+                         "the same bytes identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample))),
+               "pinned": "one core (sched_setaffinity)", **cpu_facts()}
         log("encoding oracle: %.2f s on %d bytes, identical: %s" % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
     log("encoding: %.3f ms per run (walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, %d tokens"
         % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], enc_gbps, n_tok))
@@ -309,15 +345,17 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         log("timing the CPU oracle (chunk-multiset, single thread) on the same corpus")
-        t0 = time.perf_counter()
-        om, ot, _ = oracle.train_chunks(data, n_merges)
-        cpu_s = time.perf_counter() - t0
+        with one_core():
+            t0 = time.perf_counter()
+            om, ot, _ = oracle.train_chunks(data, n_merges)
+            cpu_s = time.perf_counter() - t0
         same = np.array_equal(om, m.cpu().numpy().astype(np.int64)) and \
             np.array_equal(ot, t.cpu().numpy().astype(np.uint32))
         cpu = {"value": round(len(om) / cpu_s, 3), "unit": "merges/s", "cores": 1, "kind": "oracle",
                "sample": "the whole workload (%d bytes, %d merges) through the chunk-multiset C oracle "
                          "(oracle/bpe_oracle.c, train_chunks), one thread, %.2f s including chunking; "
-                         "GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, same)}
+                         "GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, same),
+               "pinned": "one core (sched_setaffinity)", **cpu_facts()}
         log("oracle: %.2f s, bit-identical to the GPU result: %s" % (cpu_s, same))
 
     if args.save_merges:

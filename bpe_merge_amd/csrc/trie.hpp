@@ -52,12 +52,6 @@ __host__ __device__ __forceinline__ unsigned long long tr_pack(uint32_t check, u
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // Exclusive prefix sum over the workgroup (TPB threads); the total goes to
 // *total. Uses s_w (TPB / 64 words); ends with a barrier.
 template <int TPB>

@@ -130,3 +130,17 @@ def test_bytes_only_vocabulary_and_rejections(bpe):
         bpe.Trie([(97, 300)])                      # id 300 does not exist before merge 0
     with pytest.raises(bpe.BpeError):
         bpe.Trie([(97, 32)])                       # letter + space: crosses a class change
+
+
+def test_profile_calls_agree_with_encode(bpe, vocabs):
+    m = vocabs[1]
+    text = corpus.generate(corpus.CONFIGS[1].scaled(200_000, seed=31))
+    d = _dev(text)
+    with bpe.Trie(m) as t:
+        n_tok, ms = t.profile(d, 3)
+        assert n_tok == t.count(d) == oracle.trie_encode(text, m).size
+        assert ms.shape == (3, 3) and (ms > 0).all()
+    with bpe.Encoder(m) as e:
+        n_tok, ms = e.profile(d, 3)
+        assert n_tok == oracle.encode(text, m)[1].size
+        assert ms.shape == (3, 3) and (ms > 0).all()
