@@ -344,18 +344,34 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        log("timing the CPU oracle (chunk-multiset, single thread) on the same corpus")
-        with one_core():
-            t0 = time.perf_counter()
-            om, ot, _ = oracle.train_chunks(data, n_merges)
-            cpu_s = time.perf_counter() - t0
+        # the large workloads once, the others three times (median)
+        reps = 1 if spec.n_bytes >= (256 << 20) else 3
+        log("timing the CPU oracle (chunk-multiset, single thread) on the same corpus, %d run(s)" % reps)
+        times = []
+        for _ in range(reps):
+            with one_core():
+                t0 = time.perf_counter()
+                om, ot, _ = oracle.train_chunks(data, n_merges)
+                times.append(time.perf_counter() - t0)
+        cpu_s = float(np.median(times))
         same = np.array_equal(om, m.cpu().numpy().astype(np.int64)) and \
             np.array_equal(ot, t.cpu().numpy().astype(np.uint32))
         cpu = {"value": round(len(om) / cpu_s, 3), "unit": "merges/s", "cores": 1, "kind": "oracle",
                "sample": "the whole workload (%d bytes, %d merges) through the chunk-multiset C oracle "
-                         "(oracle/bpe_oracle.c, train_chunks), one thread, %.2f s including chunking; "
-                         "GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, same),
+                         "(oracle/bpe_oracle.c, train_chunks), one thread, %.2f s including chunking (median "
+                         "of %d); GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, reps, same),
                "pinned": "one core (sched_setaffinity)", **cpu_facts()}
+        if spec.n_bytes <= (1 << 20):
+            # the literal definition (a full recount every iteration) is
+            # feasible only on the smallest workload
+            with one_core():
+                t0 = time.perf_counter()
+                lm, lt, _ = oracle.train_literal(data, n_merges)
+                lit_s = time.perf_counter() - t0
+            cpu["literal"] = {"value": round(len(lm) / lit_s, 3), "unit": "merges/s",
+                              "sample": "the literal C oracle (train_literal: full recount each iteration), "
+                                        "one thread, %.2f s; equal to the chunk oracle: %s"
+                                        % (lit_s, bool(np.array_equal(lm, om) and np.array_equal(lt, ot)))}
         log("oracle: %.2f s, bit-identical to the GPU result: %s" % (cpu_s, same))
 
     if args.save_merges:
