@@ -436,7 +436,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
     __shared__ uint32_t s_stage[2 * SST];
     __shared__ uint32_t s_wagg[NW];
-    __shared__ uint32_t s_tile[2], s_off[2], s_sel;
+    __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now;
     __shared__ unsigned long long s_best[NW];
     __shared__ __align__(16) unsigned long long s_win[LB_WIN];
 
@@ -603,91 +603,164 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             t = tn;
         }
     } else {
-        for (uint32_t round = 1; t < ntiles; ++round) {
-            const uint32_t g0 = t * TILE + tid * V;
-            uint32_t a1, a2, b1;
-            fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
-            uint32_t occ, valid;
-            occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
-
-            // ---- this thread's tuple, then inclusive scans over the wave and the waves
-            uint32_t tup;
-            {
-                uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
+        // L == R: the selection of a position depends on the one before it
+        // (run-length parity), so a tile's selection depends on the state it
+        // is entered with, but only through its leading chain of
+        // occurrences: the first position that is not an occurrence resets
+        // it. When neither the tile's first position nor the one before it
+        // (whose selection decides the pair across the boundary for the
+        // counts) is an occurrence, the entry state is known to be "not
+        // selected": the tile is staged at once and pipelined like the
+        // L != R path (its look-back, a round later, only supplies the
+        // output offset). Otherwise the tile runs its look-back at once, as
+        // its staging needs the entry state, and is stored in the next round
+        // with no second look-back. Tile 0 (entered with nothing selected)
+        // publishes its inclusive prefix as soon as it is staged: a
+        // workgroup's immediate look-back never waits for its own pending
+        // tile, whose aggregate is out, but would wait for tile 0's prefix.
+        // Aggregates are the selection tuples.
+        uint32_t tp = ntiles, kp = 0, cur = 0, agg_p = TUP_ID, off_p = 0;
+        bool done_p = false;  // the pending tile's prefix is out (offset off_p)
+        uint32_t grab = 0;
+        if (tid == 0) grab = atomicAdd(tile_ctr, 1u);
+        store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
+        for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
+            uint32_t tn = ntiles, tile_kept = 0, tile_agg = TUP_ID, off_t = 0;
+            bool dep = false;
+            const long long lb_top = (long long)tp - 1;
+            const long long lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
+            const bool lb_pending = tp < ntiles && !done_p;  // tile 0 is always done
+            if (w == 0 && lb_pending) {
 #pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    const uint32_t o = (occ >> j) & 1u, v = (valid >> j) & 1u;
-                    s0 = o & ~s0 & 1u;
-                    s1 = o & ~s1 & 1u;
-                    c0 += v & ~s0 & 1u;
-                    c1 += v & ~s1 & 1u;
-                }
-                tup = tup_make(c0, c1 - c0, s0, s1);
+                for (int q = 0; q < LB_WIN / 128; ++q)
+                    __builtin_amdgcn_global_load_lds(status + lb_base + 2 * (lane + 64 * q),
+                                                     (__attribute__((address_space(3))) void*)(s_win + 128 * q),
+                                                     16, 0, LDS_DMA_SC1);
             }
-            uint32_t incl = tup;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t u = __shfl_up(incl, o);
-                if (lane >= (uint32_t)o) incl = tup_then(u, incl);
-            }
-            uint32_t lane_excl = __shfl_up(incl, 1);
-            if (lane == 0) lane_excl = TUP_ID;
-            if (lane == 63) s_wagg[w] = incl;
-            lds_barrier();
-            uint32_t wave_excl = TUP_ID, tile_agg = TUP_ID;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                if (i == (int)w) wave_excl = tile_agg;
-                tile_agg = tup_then(tile_agg, s_wagg[i]);
-            }
+            if (t < ntiles) {  // uniform
+                const uint32_t g0 = t * TILE + tid * V;
+                uint32_t a1, a2, b1;
+                fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
+                uint32_t occ, valid;
+                occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
 
-            // ---- decoupled look-back (wave 0)
-            if (w == 0) {
-                uint32_t off = 0, sel = 0;
-                if (t != 0) {
-                    if (lane == 0) st_store(status + t, st_pack(ST_AGG, epoch, tile_agg));
-                    unsigned long long lbw[4];
-                    lookback_window<4>(status, (long long)t - 1, epoch, lane, lbw);
-                    lookback<4>(status, t, epoch, lane, ctl, lbw, off, sel);
-                }
-                if (lane == 0) {
-                    const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
-                    st_store(status + t, st_pack(ST_PRE, epoch, (off + kept) | (tup_o(tile_agg, sel) << 31)));
-                    s_off[0] = off;
-                    s_sel = sel;
-                }
-            }
-            lds_barrier();
-            const uint32_t tile_off = s_off[0], tile_sel = s_sel;
-            const uint32_t texcl = tup_then(wave_excl, lane_excl);
-            const uint32_t my_local = tup_c0(texcl) + (tile_sel ? tup_d(texcl) : 0u);
-            const uint32_t sel_in = tup_o(texcl, tile_sel);
-            const uint32_t tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
-
-            // ---- resolve sel, stage, count changes
-            uint32_t selbits = 0;
-            {
-                uint32_t s = sel_in;
+                // ---- this thread's tuple, then inclusive scans over the wave and the waves
+                uint32_t tup;
+                {
+                    uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
 #pragma unroll
-                for (int j = 0; j <= V; ++j) {
-                    s = (occ >> j) & ~s & 1u;
-                    selbits |= s << j;
+                    for (int j = 0; j < V; ++j) {
+                        const uint32_t o = (occ >> j) & 1u, v = (valid >> j) & 1u;
+                        s0 = o & ~s0 & 1u;
+                        s1 = o & ~s1 & 1u;
+                        c0 += v & ~s0 & 1u;
+                        c1 += v & ~s1 & 1u;
+                    }
+                    tup = tup_make(c0, c1 - c0, s0, s1);
                 }
-            }
-            stage<V>(s_stage, my_local, x, valid, selbits, X);
-            if (do_count && (occ | sel_in)) {
-                const Changes<V> ch(x, selbits, sel_in);
-                count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, selbits, sel_in, a1, s_stage, my_local,
-                                  valid & ~selbits, L, R, X);
-            }
+                uint32_t incl = tup;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t u = __shfl_up(incl, o);
+                    if (lane >= (uint32_t)o) incl = tup_then(u, incl);
+                }
+                uint32_t lane_excl = __shfl_up(incl, 1);
+                if (lane == 0) lane_excl = TUP_ID;
+                if (lane == 63) s_wagg[w] = incl;
+                if (tid == 0) {
+                    s_tile[round & 1u] = grab - tile_base;
+                    s_dep = (occ & 1u) | (uint32_t)((a2 & IDM) == L && (a1 & (WS | IDM)) == L);
+                }
+                lds_barrier();
+                uint32_t wave_excl = TUP_ID;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    if (i == (int)w) wave_excl = tile_agg;
+                    tile_agg = tup_then(tile_agg, s_wagg[i]);
+                }
+                dep = s_dep != 0u;  // uniform
+                // the tile's aggregate (tile 0: prefix) goes out before anything else is done
+                if (tid == 0)
+                    st_store(status + t, t != 0 ? st_pack(ST_AGG, epoch, tile_agg)
+                                                : st_pack(ST_PRE, epoch, tup_c0(tile_agg) | (tup_o(tile_agg, 0u) << 31)));
+                uint32_t tile_sel = 0;
+                if (dep) {  // uniform: the entry state is needed now
+                    if (w == 0) {
+                        uint32_t off = 0, sel = 0;
+                        unsigned long long lbw[4];
+                        lookback_window<4>(status, (long long)t - 1, epoch, lane, lbw);
+                        lookback<4>(status, t, epoch, lane, ctl, lbw, off, sel);
+                        if (lane == 0) {
+                            const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
+                            st_store(status + t,
+                                     st_pack(ST_PRE, epoch, (off + kept) | (tup_o(tile_agg, sel) << 31)));
+                            s_off_now = off;
+                            s_sel = sel;
+                        }
+                    }
+                    lds_barrier();
+                    tile_sel = s_sel;
+                    off_t = s_off_now;
+                }
+                const uint32_t texcl = tup_then(wave_excl, lane_excl);
+                const uint32_t my_local = tup_c0(texcl) + (tile_sel ? tup_d(texcl) : 0u);
+                const uint32_t sel_in = tup_o(texcl, tile_sel);
+                tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
 
-            // ---- next tile, then write this one
-            if (tid == 0) s_tile[round & 1u] = atomicAdd(tile_ctr, 1u) - tile_base;
-            lds_barrier();
-            const uint32_t tn = s_tile[round & 1u];
+                // ---- resolve sel, stage, count changes
+                uint32_t selbits = 0;
+                {
+                    uint32_t sv = sel_in;
+#pragma unroll
+                    for (int j = 0; j <= V; ++j) {
+                        sv = (occ >> j) & ~sv & 1u;
+                        selbits |= sv << j;
+                    }
+                }
+                uint32_t* st = s_stage + cur * SST;
+                stage<V>(st, my_local, x, valid, selbits, X);
+                if (do_count && (occ | sel_in)) {
+                    const Changes<V> ch(x, selbits, sel_in);
+                    count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, selbits, sel_in, a1, st, my_local,
+                                      valid & ~selbits, L, R, X);
+                }
+                tn = s_tile[round & 1u];
+            }
+            // ---- the next tile's loads (an empty resource when there is none)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
-            store_tile<TPB, TILE>(out, s_stage, tile_off, tile_kept);
-            if (t == ntiles - 1 && tid == 0) finish_iteration(ctl, lengths, it, tile_off + tile_kept);
+            // ---- the previous tile: its offset (unless its look-back is done)
+            if (tp < ntiles && w == 0) {
+                uint32_t off = off_p, sel = 0;
+                if (!done_p) {  // tp != 0
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM7);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    unsigned long long lbw[LB_PL];
+#pragma unroll
+                    for (int q = 0; q < LB_PL; ++q) {
+                        const long long idx = lb_top - (long long)(LB_PL * lane + q);
+                        lbw[q] = idx >= 0 ? s_win[idx - lb_base] : st_pack(ST_PRE, epoch, 0u);
+                    }
+                    lookback<LB_PL>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
+                    if (lane == 0)
+                        st_store(status + tp, st_pack(ST_PRE, epoch, (off + kp) | (tup_o(agg_p, sel) << 31)));
+                }
+                if (lane == 0) s_off[round & 1u] = off;
+            }
+            lds_barrier();
+            if (tid == 0 && tn < ntiles) grab = atomicAdd(tile_ctr, 1u);
+            const uint32_t tile_off = tp < ntiles ? s_off[round & 1u] : 0u;
+            store_tile<TPB, TILE>(out, s_stage + (cur ^ 1u) * SST, tile_off, tp < ntiles ? kp : 0u);
+            if (tp == ntiles - 1 && tid == 0) finish_iteration(ctl, lengths, it, tile_off + kp);
+            if (t < ntiles) {
+                tp = t;
+                kp = tile_kept;
+                agg_p = tile_agg;
+                done_p = dep || t == 0;
+                off_p = off_t;
+                cur ^= 1u;
+            } else {
+                tp = ntiles;
+            }
             t = tn;
         }
     }

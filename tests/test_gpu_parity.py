@@ -210,9 +210,12 @@ def test_bench_launch_path_matches_train(bpe):
 def test_large_corpus_uses_the_large_tiles_and_matches(bpe):
     # above 2 x 256 tiles of 16384 symbols the merge pass runs 1024-thread
     # workgroups on 16384-symbol tiles; below, 512 threads on 8192
-    d = corpus.generate(corpus.CONFIGS[3].scaled(10_000_000, seed=91))
-    _say("train 10 MB, 400 merges")
-    gm, gt = bpe.train(_dev(d), 400, 21)
-    om, ot, _ = oracle.train_chunks(d, 400)
-    assert np.array_equal(gm.cpu().numpy().astype(np.int64), om)
-    assert np.array_equal(gt.cpu().numpy().astype(np.uint32), ot)
+    # words (unequal pairs mostly), then runs (every merge an equal pair,
+    # many tiles entered inside a chain of occurrences)
+    for cfg, seed in [(3, 91), (5, 92)]:
+        d = corpus.generate(corpus.CONFIGS[cfg].scaled(10_000_000, seed=seed))
+        _say("train 10 MB of %s, 400 merges" % corpus.CONFIGS[cfg].kind)
+        gm, gt = bpe.train(_dev(d), 400, 21)
+        om, ot, _ = oracle.train_chunks(d, 400)
+        assert np.array_equal(gm.cpu().numpy().astype(np.int64), om), cfg
+        assert np.array_equal(gt.cpu().numpy().astype(np.uint32), ot), cfg
