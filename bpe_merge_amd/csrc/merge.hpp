@@ -83,6 +83,30 @@ __device__ __forceinline__ bool st_valid(unsigned long long s, uint32_t epoch) {
     return (s >> 62) != 0ull && (uint32_t)((s >> 32) & 0x3FFFFFFFull) == epoch;
 }
 
+// Cross-lane moves by DPP (data-parallel primitives of the GCN/CDNA vector
+// ALU): v from another lane per CTRL, ident where that lane is outside the
+// row or wave, or the row is masked off (row_mask RM). No LDS round trip.
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_WAVE_SHL1 = 0x130, DPP_WAVE_SHR1 = 0x138, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t ident, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, RM, 0xF, false);
+}
+// Inclusive scan over the 64 lanes of a wave with an associative op(a, b)
+// (a then b; ident its identity): shifts of 1, 2, 4, 8 within rows of 16,
+// then row 0's last lane into row 1 and row 2's into row 3, then lane 31
+// into rows 2 and 3.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t ident, Op op) {
+    v = op(dpp<DPP_ROW_SHR1>(ident, v), v);
+    v = op(dpp<DPP_ROW_SHR2>(ident, v), v);
+    v = op(dpp<DPP_ROW_SHR4>(ident, v), v);
+    v = op(dpp<DPP_ROW_SHR8>(ident, v), v);
+    v = op(dpp<DPP_ROW_BCAST15, 0xA>(ident, v), v);
+    v = op(dpp<DPP_ROW_BCAST31, 0xC>(ident, v), v);
+    return v;
+}
+
 // Decoupled look-back, run by one wave: the exclusive prefix of tile t (kept
 // symbols before it, sel of the position before it). Each round reads the
 // status words of the 64 * PL tiles below the current window top at once
@@ -94,11 +118,11 @@ __device__ __forceinline__ bool st_valid(unsigned long long s, uint32_t epoch) {
 // zero prefix. Every lane issues its PL loads (tile 0's word stands in for
 // indexes below 0), so that the number of loads is fixed.
 template <int PL>
-__device__ __forceinline__ void lookback_window(const unsigned long long* status, long long top, uint32_t epoch,
+__device__ __forceinline__ void lookback_window(const unsigned long long* status, int top, uint32_t epoch,
                                                 uint32_t lane, unsigned long long (&st)[PL]) {
 #pragma unroll
     for (int q = 0; q < PL; ++q) {
-        const long long idx = top - (long long)(PL * lane + q);
+        const int idx = top - (int)(PL * lane + q);
         const unsigned long long v = st_load(status + (idx >= 0 ? idx : 0));
         st[q] = (idx >= 0) ? v : st_pack(ST_PRE, epoch, 0u);
     }
@@ -111,13 +135,13 @@ __device__ __forceinline__ void lookback_window(const unsigned long long* status
 // in LDS; later windows that lie inside it are read from there. A stale
 // copy is fine: a word only ever moves from invalid to aggregate to prefix
 // within an epoch, and invalid words are read again from global memory.
-template <int PL>
+template <int PL, bool SUM>
 __device__ __forceinline__ void lookback(const unsigned long long* status, uint32_t t, uint32_t epoch,
                                          uint32_t lane, Ctl* ctl, const unsigned long long (&first)[PL],
                                          uint32_t& off, uint32_t& sel, const unsigned long long* lwin = nullptr,
-                                         long long lbase = 0, long long nwin = 0) {
-    Span acc{0u, 0u, 0u, 1u};
-    long long top = (long long)t - 1;
+                                         int lbase = 0, int nwin = 0) {
+    Span acc{0u, 0u, 0u, 1u};  // SUM: acc.c0 alone
+    int top = (int)t - 1;
     uint32_t spins = 0;
     for (bool at_first = true;; at_first = false) {
         unsigned long long st[PL];
@@ -126,12 +150,12 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
             for (int q = 0; q < PL; ++q) st[q] = first[q];
         } else if (lwin && top - (64 * PL - 1) >= lbase && top < lbase + nwin) {
 #pragma unroll
-            for (int q = 0; q < PL; ++q) st[q] = lwin[top - (long long)(PL * lane + q) - lbase];
+            for (int q = 0; q < PL; ++q) st[q] = lwin[top - (int)(PL * lane + q) - lbase];
         } else {
             lookback_window<PL>(status, top, epoch, lane, st);
         }
         int fq;          // this lane's first q holding a prefix (PL if none)
-        uint32_t plane;  // first lane holding a prefix (64 if none)
+        uint32_t plane;  // first lane holding a prefix (64 if none); uniform
         for (;;) {
             fq = PL;
             bool all_valid = true, valid_below_fq = true;
@@ -160,32 +184,44 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int q = 0; q < PL; ++q) {
-                const long long idx = top - (long long)(PL * lane + q);
+                const int idx = top - (int)(PL * lane + q);
                 if (idx >= 0 && !st_valid(st[q], epoch)) st[q] = st_load(status + idx);
             }
         }
-        // fold this lane's aggregates, lowest tile first
-        uint32_t a = TUP_ID;
+        // fold this lane's aggregates, lowest tile (highest q) first, then
+        // across the lanes, highest lane (lowest tiles) first: an upward
+        // scan with the operands swapped, read at lane 63. For L != R every
+        // aggregate is a plain kept count and the fold is a sum.
+        uint32_t a = SUM ? 0u : TUP_ID;
         uint32_t pay = 0;
 #pragma unroll
         for (int q = PL - 1; q >= 0; --q) {
             const bool inc = (lane < plane) || (lane == plane && q < fq);
-            if (inc) a = tup_then(a, (uint32_t)(st[q] & 0xFFFFFFFFull));
-            if (q == fq) pay = (uint32_t)(st[q] & 0xFFFFFFFFull);
+            const uint32_t v = (uint32_t)(st[q] & 0xFFFFFFFFull);
+            if (SUM) {
+                a += inc ? v : 0u;
+            } else if (inc) {
+                a = tup_then(a, v);
+            }
+            if (q == fq) pay = v;
         }
-        // fold across lanes: higher lanes hold lower tiles and come first
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t other = __shfl_down(a, o);
-            if (lane + o < 64) a = tup_then(other, a);
+        if (SUM) {
+            a = wave_scan(a, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+            acc.c0 += (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
+        } else {
+            a = wave_scan(a, TUP_ID, [](uint32_t x, uint32_t y) { return tup_then(y, x); });
+            acc = span_after((uint32_t)__builtin_amdgcn_readlane((int)a, 63), acc);
         }
-        a = __shfl(a, 0);
-        acc = span_after(a, acc);
         if (plane < 64) {
-            const uint32_t p = __shfl(pay, (int)plane);
+            const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pay, (int)plane);
             const uint32_t base = p & 0x7FFFFFFFu, bsel = p >> 31;
-            off = base + acc.c0 + (bsel ? acc.d : 0u);
-            sel = bsel ? acc.o1 : acc.o0;
+            if (SUM) {
+                off = base + acc.c0;
+                sel = 0u;
+            } else {
+                off = base + acc.c0 + (bsel ? acc.d : 0u);
+                sel = bsel ? acc.o1 : acc.o0;
+            }
             return;
         }
         top -= 64 * PL;
@@ -193,7 +229,9 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
 }
 
 // LDS index skew for staged output (thread-contiguous runs spread over banks)
-__device__ __forceinline__ uint32_t skew(uint32_t i) { return i + (i >> 5); }
+__host__ __device__ constexpr uint32_t skew(uint32_t i) { return i + (i >> 5); }
+
+
 
 // Count changes of one thread's positions (bit j: position g0 + j).
 // sel holds sel for positions g0 .. g0 + V (bit V: the next thread's first),
@@ -302,9 +340,9 @@ __device__ __forceinline__ void fix_tile(uint32_t (&x)[16], uint32_t h1, uint32_
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? x[j] : WS;
     }
-    a1 = __shfl_up(x[15], 1);
-    a2 = __shfl_up(x[14], 1);
-    b1 = __shfl_down(x[0], 1);
+    a1 = dpp<DPP_WAVE_SHR1>(WS, x[15]);  // from lane - 1
+    a2 = dpp<DPP_WAVE_SHR1>(WS, x[14]);
+    b1 = dpp<DPP_WAVE_SHL1>(WS, x[0]);  // from lane + 1
     if (lane == 0) {
         a1 = g0 >= 1u ? h1 : WS;
         a2 = g0 >= 2u ? h2 : WS;
@@ -321,15 +359,17 @@ __device__ __forceinline__ void occurrences(const uint32_t (&x)[V], uint32_t a1,
     // bitwise, not short-circuit: no branch per position. A position
     // past n holds WS, and position 0 always carries WS, so the tag test
     // also rules those out.
+    // Symbols hold bits 0-16 only (id and WS), so x == R tests the id and
+    // the absence of the tag at once.
     occ = 0;
     uint32_t prev = a1;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const uint32_t o = (uint32_t)((prev & IDM) == L) & (uint32_t)((x[j] & (WS | IDM)) == R);
+        const uint32_t o = (uint32_t)((prev & IDM) == L) & (uint32_t)(x[j] == R);
         occ |= o << j;
         prev = x[j];
     }
-    occ |= ((uint32_t)((x[V - 1] & IDM) == L) & (uint32_t)((b1 & (WS | IDM)) == R)) << V;
+    occ |= ((uint32_t)((x[V - 1] & IDM) == L) & (uint32_t)(b1 == R)) << V;
     valid = (g0 >= n) ? 0u : (n - g0 >= (uint32_t)V ? (1u << V) - 1u : (1u << (n - g0)) - 1u);
 }
 
@@ -357,13 +397,23 @@ __device__ __forceinline__ void store_tile(uint32_t* __restrict__ out, const uin
         const uint32_t i = on ? tid : 0u;
         __builtin_amdgcn_raw_buffer_store_b32(st[skew(i)], rs, on ? 4u * i : BUF_OOB, 0, 0);
     }
+    // Group q of the thread holds symbols b + 4 * TPB * q .. + 3 with
+    // b = head + 4 * tid. A step of 4 * TPB symbols (a multiple of 32) moves
+    // every skewed index by the same amount, so the four LDS addresses are
+    // formed once and the groups add a constant. A group past the body
+    // still reads inside the (padded) staging buffer; its store is dropped.
+    constexpr uint32_t QSTEP = skew(4 * TPB);
+    static_assert((4 * TPB) % 32 == 0, "groups keep their offset within 32 symbols");
+    const uint32_t b = head + 4u * tid;
+    const uint32_t* p0 = st + skew(b);
+    const uint32_t* p1 = st + skew(b + 1u);
+    const uint32_t* p2 = st + skew(b + 2u);
+    const uint32_t* p3 = st + skew(b + 3u);
 #pragma unroll
     for (int q = 0; q < TILE / 4 / TPB; ++q) {
-        const uint32_t g = tid + q * TPB;
-        const bool on = g < body;
-        const uint32_t b = on ? head + 4 * g : 0u;
-        const v4u32 v = {st[skew(b)], st[skew(b + 1)], st[skew(b + 2)], st[skew(b + 3)]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * b : BUF_OOB, 0, BUF_NT);
+        const bool on = tid + q * TPB < body;
+        const v4u32 v = {p0[q * QSTEP], p1[q * QSTEP], p2[q * QSTEP], p3[q * QSTEP]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * (b + 4u * TPB * q) : BUF_OOB, 0, BUF_NT);
     }
     {
         const bool on = tid < tile_kept - rest;
@@ -377,11 +427,23 @@ __device__ __forceinline__ void store_tile(uint32_t* __restrict__ out, const uin
 template <int V>
 __device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
                                       uint32_t sel, uint32_t X) {
+    constexpr uint32_t VM = (1u << V) - 1u;
+    if (valid == VM && (sel & ((VM << 1) | 1u)) == 0u) {
+        // nothing dropped or replaced (most threads): symbol j goes to
+        // skew(o + j) = o + (o >> 5) + j, one further once o + j reaches
+        // the next multiple of 32 (at most once in V < 32 symbols)
+        uint32_t* p0 = st + skew(o);
+        uint32_t* p1 = p0 + 1;
+        const uint32_t r = o & 31u;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
-            st[skew(o)] = ((sel >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
-            ++o;
+        for (int j = 0; j < V; ++j) (r + j >= 32u ? p1 : p0)[j] = x[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
+                st[skew(o)] = ((sel >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
+                ++o;
+            }
         }
     }
 }
@@ -400,7 +462,6 @@ __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, ui
 // global_load_lds.
 constexpr int LB_PL = 4;
 constexpr int LB_WIN = 2 * 64 * LB_PL;
-constexpr int LDS_DMA_SC1 = 16;  // cache policy sc1: agent-coherent, like st_load
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= 7, expcnt and lgkmcnt untouched
 constexpr int WAIT_VM7 = 0x0F77;
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
@@ -421,6 +482,54 @@ static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 // L == R: the selection carries along runs (sel_i = occ_i and not
 // sel_{i-1}) and a tile's selection can depend on every tile before it, so
 // staging waits for the look-back's sel as well.
+// Prefixes over the workgroup's NW <= 16 wave totals tot[] in LDS, for the
+// calling wave w (uniform): the combination of the totals of waves 0 .. w-1
+// (ident for wave 0) and of all NW. Lane i of each 16-lane row takes total
+// i, a row scan by DPP row shifts combines them (lanes shifted in from
+// outside the row take ident), and two single lanes are read: a handful of
+// instructions in place of a select per wave. op(a, b) is a then b.
+template <int NW, typename Op>
+__device__ __forceinline__ void waves_prefix(const uint32_t* tot, uint32_t w, uint32_t lane, uint32_t ident, Op op,
+                                             uint32_t& before, uint32_t& all) {
+    static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes");
+    const uint32_t i = lane & 15u;
+    uint32_t v = i < (uint32_t)NW ? tot[i] : ident;
+    // DPP row_shr:1, 2, 4, 8 (row and bank masks all on; no bound control)
+    v = op((uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x111, 0xF, 0xF, false), v);
+    v = op((uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x112, 0xF, 0xF, false), v);
+    v = op((uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x114, 0xF, 0xF, false), v);
+    v = op((uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x118, 0xF, 0xF, false), v);
+    all = (uint32_t)__builtin_amdgcn_readlane((int)v, NW - 1);
+    before = w ? (uint32_t)__builtin_amdgcn_readlane((int)v, (int)w - 1) : ident;
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds + 16 * lane, with cache policy sc1 (agent-coherent, like st_load).
+// Inline assembly, so that the compiler does not track the copy: it would
+// otherwise drain every vector memory operation at each later barrier and
+// before each later LDS access it cannot tell apart from the destination.
+// The caller waits for the copy (vmcnt) before reading the destination,
+// and nothing else accesses that LDS range.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
+__device__ __forceinline__ void lds_copy16(const unsigned long long* src, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Values loaded by load_tile that a round does not consume: an empty use,
+// so that the compiler waits for their loads in that round and not when
+// the registers are next loaded.
+__device__ __forceinline__ void retire(const uint32_t (&x)[16], uint32_t h1, uint32_t h2, uint32_t hr) {
+    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+                 "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]),
+                 "v"(h1), "v"(h2), "v"(hr));
+}
+
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
@@ -434,7 +543,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     constexpr uint32_t VM = (1u << V) - 1u;
     constexpr uint32_t SST = TILE + TILE / 32;  // one staging buffer (skewed)
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
-    __shared__ uint32_t s_stage[2 * SST];
+    __shared__ uint32_t s_stage[2 * SST + 4];  // + 4: reads of dropped store groups stay inside
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now;
     __shared__ unsigned long long s_best[NW];
@@ -451,7 +560,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     // X == 65535 is the last possible id: no later iteration reads counts,
     // and the pair (X, X) would collide with the empty key
     const bool do_count = X != IDM;
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: in a scalar register
     uint32_t* tile_ctr = &ctl->tile_ctr;
     const uint32_t tile_base = sw->tile_base;
 
@@ -514,14 +624,12 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // words below it), copied straight into LDS before anything else
             // of the round, so that it has arrived by the time wave 0
             // examines it and occupies no registers meanwhile
-            const long long lb_top = (long long)tp - 1;
-            const long long lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
+            const int lb_top = (int)tp - 1;
+            const int lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
             if (w == 0 && tp < ntiles && tp != 0) {
 #pragma unroll
                 for (int q = 0; q < LB_WIN / 128; ++q)
-                    __builtin_amdgcn_global_load_lds(status + lb_base + 2 * (lane + 64 * q),
-                                                     (__attribute__((address_space(3))) void*)(s_win + 128 * q),
-                                                     16, 0, LDS_DMA_SC1);
+                    lds_copy16(status + lb_base + 2 * (lane + 64 * q), s_win + 128 * q);
             }
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
@@ -534,21 +642,14 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
 
                 // ---- kept counts: wave scan, then across the waves
                 const uint32_t kept = __popc(valid & ~occ & VM);
-                uint32_t incl = kept;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t u = __shfl_up(incl, o);
-                    if (lane >= (uint32_t)o) incl += u;
-                }
+                const uint32_t incl = wave_scan(kept, 0u, [](uint32_t a, uint32_t b) { return a + b; });
                 if (lane == 63) s_wagg[w] = incl;
                 if (tid == 0) s_tile[round & 1u] = grab - tile_base;
                 lds_barrier();
-                uint32_t my_local = incl - kept;
-#pragma unroll
-                for (int i = 0; i < NW; ++i) {
-                    if (i < (int)w) my_local += s_wagg[i];
-                    tile_kept += s_wagg[i];
-                }
+                uint32_t before;
+                waves_prefix<NW>(s_wagg, w, lane, 0u, [](uint32_t a, uint32_t b) { return a + b; }, before,
+                                 tile_kept);
+                const uint32_t my_local = incl - kept + before;
                 // the tile's aggregate goes out before anything else is done
                 if (tid == 0 && t != 0)
                     st_store(status + t, st_pack(ST_AGG, epoch, tup_make(tile_kept, 0u, 0u, 0u)));
@@ -561,6 +662,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                                       valid & ~occ, L, R, X);
                 }
                 tn = s_tile[round & 1u];
+            } else {
+                retire(x, h1, h2, hr);
             }
             // ---- the next tile's loads (an empty resource when there is none)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
@@ -575,10 +678,10 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     unsigned long long lbw[LB_PL];
 #pragma unroll
                     for (int q = 0; q < LB_PL; ++q) {
-                        const long long idx = lb_top - (long long)(LB_PL * lane + q);
+                        const int idx = lb_top - (int)(LB_PL * lane + q);
                         lbw[q] = idx >= 0 ? s_win[idx - lb_base] : st_pack(ST_PRE, epoch, 0u);
                     }
-                    lookback<LB_PL>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
+                    lookback<LB_PL, true>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
                 }
                 if (lane == 0) {
                     st_store(status + tp, st_pack(ST_PRE, epoch, off + kp));
@@ -627,15 +730,13 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0, tile_agg = TUP_ID, off_t = 0;
             bool dep = false;
-            const long long lb_top = (long long)tp - 1;
-            const long long lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
+            const int lb_top = (int)tp - 1;
+            const int lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
             const bool lb_pending = tp < ntiles && !done_p;  // tile 0 is always done
             if (w == 0 && lb_pending) {
 #pragma unroll
                 for (int q = 0; q < LB_WIN / 128; ++q)
-                    __builtin_amdgcn_global_load_lds(status + lb_base + 2 * (lane + 64 * q),
-                                                     (__attribute__((address_space(3))) void*)(s_win + 128 * q),
-                                                     16, 0, LDS_DMA_SC1);
+                    lds_copy16(status + lb_base + 2 * (lane + 64 * q), s_win + 128 * q);
             }
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
@@ -658,26 +759,17 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     }
                     tup = tup_make(c0, c1 - c0, s0, s1);
                 }
-                uint32_t incl = tup;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t u = __shfl_up(incl, o);
-                    if (lane >= (uint32_t)o) incl = tup_then(u, incl);
-                }
-                uint32_t lane_excl = __shfl_up(incl, 1);
-                if (lane == 0) lane_excl = TUP_ID;
+                const uint32_t incl = wave_scan(tup, TUP_ID, [](uint32_t a, uint32_t b) { return tup_then(a, b); });
+                const uint32_t lane_excl = dpp<DPP_WAVE_SHR1>(TUP_ID, incl);
                 if (lane == 63) s_wagg[w] = incl;
                 if (tid == 0) {
                     s_tile[round & 1u] = grab - tile_base;
                     s_dep = (occ & 1u) | (uint32_t)((a2 & IDM) == L && (a1 & (WS | IDM)) == L);
                 }
                 lds_barrier();
-                uint32_t wave_excl = TUP_ID;
-#pragma unroll
-                for (int i = 0; i < NW; ++i) {
-                    if (i == (int)w) wave_excl = tile_agg;
-                    tile_agg = tup_then(tile_agg, s_wagg[i]);
-                }
+                uint32_t wave_excl;
+                waves_prefix<NW>(s_wagg, w, lane, TUP_ID, [](uint32_t a, uint32_t b) { return tup_then(a, b); },
+                                 wave_excl, tile_agg);
                 dep = s_dep != 0u;  // uniform
                 // the tile's aggregate (tile 0: prefix) goes out before anything else is done
                 if (tid == 0)
@@ -688,8 +780,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     if (w == 0) {
                         uint32_t off = 0, sel = 0;
                         unsigned long long lbw[4];
-                        lookback_window<4>(status, (long long)t - 1, epoch, lane, lbw);
-                        lookback<4>(status, t, epoch, lane, ctl, lbw, off, sel);
+                        lookback_window<4>(status, (int)t - 1, epoch, lane, lbw);
+                        lookback<4, false>(status, t, epoch, lane, ctl, lbw, off, sel);
                         if (lane == 0) {
                             const uint32_t kept = tup_c0(tile_agg) + (sel ? tup_d(tile_agg) : 0u);
                             st_store(status + t,
@@ -725,6 +817,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                                       valid & ~selbits, L, R, X);
                 }
                 tn = s_tile[round & 1u];
+            } else {
+                retire(x, h1, h2, hr);
             }
             // ---- the next tile's loads (an empty resource when there is none)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
@@ -737,10 +831,10 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                     unsigned long long lbw[LB_PL];
 #pragma unroll
                     for (int q = 0; q < LB_PL; ++q) {
-                        const long long idx = lb_top - (long long)(LB_PL * lane + q);
+                        const int idx = lb_top - (int)(LB_PL * lane + q);
                         lbw[q] = idx >= 0 ? s_win[idx - lb_base] : st_pack(ST_PRE, epoch, 0u);
                     }
-                    lookback<LB_PL>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
+                    lookback<LB_PL, false>(status, tp, epoch, lane, ctl, lbw, off, sel, s_win, lb_base, LB_WIN);
                     if (lane == 0)
                         st_store(status + tp, st_pack(ST_PRE, epoch, (off + kp) | (tup_o(agg_p, sel) << 31)));
                 }
