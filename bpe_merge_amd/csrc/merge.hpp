@@ -256,6 +256,14 @@ struct Changes {
     }
 };
 
+// The arguments of count_changes, held from a tile's staging until after
+// the next tile's loads are issued (gone = born = 0: nothing to count).
+struct CountArgs {
+    uint32_t gone, born, sel, sel_in, left;
+    const uint32_t* st;
+    uint32_t o, kept;
+};
+
 // Apply one thread's count changes (masks from Changes) to the workgroup's
 // LDS table (the global table when LDS has no room), one changed pair per
 // loop turn, so that the insert code exists once. The old symbol at a
@@ -620,6 +628,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0;
+            CountArgs cc{};
             // the previous tile's first look-back window (the 512 status
             // words below it), copied straight into LDS before anything else
             // of the round, so that it has arrived by the time wave 0
@@ -658,15 +667,18 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                 stage<V>(st, my_local, x, valid, occ, X);
                 if (do_count && (occ | sel_in)) {
                     const Changes<V> ch(x, occ, sel_in);
-                    count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, occ, sel_in, a1, st, my_local,
-                                      valid & ~occ, L, R, X);
+                    cc = CountArgs{ch.gone, ch.born, occ, sel_in, a1, st, my_local, valid & ~occ};
                 }
                 tn = s_tile[round & 1u];
             } else {
                 retire(x, h1, h2, hr);
             }
-            // ---- the next tile's loads (an empty resource when there is none)
+            // ---- the next tile's loads (an empty resource when there is none), then this
+            // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
+            if (cc.gone | cc.born)
+                count_changes<LT>(tab, gt, ctl, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                                  L, R, X);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
@@ -729,6 +741,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0, tile_agg = TUP_ID, off_t = 0;
+            CountArgs cc{};
             bool dep = false;
             const int lb_top = (int)tp - 1;
             const int lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
@@ -813,15 +826,18 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
                 stage<V>(st, my_local, x, valid, selbits, X);
                 if (do_count && (occ | sel_in)) {
                     const Changes<V> ch(x, selbits, sel_in);
-                    count_changes<LT>(tab, gt, ctl, ch.gone, ch.born, selbits, sel_in, a1, st, my_local,
-                                      valid & ~selbits, L, R, X);
+                    cc = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, my_local, valid & ~selbits};
                 }
                 tn = s_tile[round & 1u];
             } else {
                 retire(x, h1, h2, hr);
             }
-            // ---- the next tile's loads (an empty resource when there is none)
+            // ---- the next tile's loads (an empty resource when there is none), then this
+            // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
+            if (cc.gone | cc.born)
+                count_changes<LT>(tab, gt, ctl, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                                  L, R, X);
             // ---- the previous tile: its offset (unless its look-back is done)
             if (tp < ntiles && w == 0) {
                 uint32_t off = off_p, sel = 0;
