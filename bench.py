@@ -1,22 +1,25 @@
 """Benchmark: BPE training on one MI355X, one JSON line on stdout.
 
 A step is one whole training job on device-resident bytes: tag + count
-into the global pair table (bpe_init), every merge iteration (table sweep
-for the argmax, then merge + compaction + count update of the new
-sequence), and the copy-out of merges and tokens. The default workload is the 256 MiB ASCII corpus with 32,000 merges
-and a 2^22-slot pair table. Warm-up steps run without per-kernel events;
-timed steps run with a HIP event between consecutive kernels on the
-library's stream (one host wait per step), which gives both the wall-clock
-value and the per-kernel times behind the roofline figures.
+into the global pair table (bpe_init), every merge iteration (one launch:
+selection of the merge from the candidate list, or by a sweep of the
+table, then merge + compaction + count update of the new sequence), and
+the copy-out of merges and tokens. The default workload is the 256 MiB
+ASCII corpus with 32,000 merges and a 2^22-slot pair table. Warm-up steps
+run without events; timed steps run with a HIP event after each
+iteration's launch on the library's stream (one host wait per step), which
+gives both the wall-clock value and the per-iteration times behind the
+roofline figures.
 
 Algorithmic bytes of iteration k (n_k symbols before it, n_{k+1} after,
 T table slots of 8 bytes):
   4 n_k + 4 n_{k+1}: the merge pass reads the symbols once and writes the
   compacted result once (the roofline figure of k_merge);
-  + 8 T: the argmax sweep reads the table once. The table is never reset
+  + 16 T in an iteration that sweeps the table (for the maximum, then for
+  the candidates; "table_sweeps" counts them). The table is never reset
   (its counts are updated in place), so no reset write is credited. Count
-  updates and look-back status words are implementation overhead: timed,
-  not credited.
+  updates, candidate-list reads and look-back status words are
+  implementation overhead: timed, not credited.
 
 After training, the line also reports inference ("inference"): greedy
 longest-match tokenization of the same corpus with the trie of the merges
@@ -320,19 +323,22 @@ def main() -> int:
         log("timed step %d: %.3f s, %d merges" % (i + 1, dt, m.shape[0]))
 
     m, t, lengths, prof = last
-    r, f_ms, m_ms = prof
+    r, m_ms = prof
     k = m.shape[0]
     n_k = lengths[:k].astype(np.float64)
     n_k1 = lengths[1: k + 1].astype(np.float64)
-    f_ms = f_ms[:k].astype(np.float64)
     m_ms = m_ms[:k].astype(np.float64)
-    it_s = (f_ms + m_ms) / 1e3
+    it_s = m_ms / 1e3
     merge_bytes = 4.0 * n_k + 4.0 * n_k1
-    iter_bytes = merge_bytes + 8.0 * T
+    # an iteration that sweeps the pair table reads it twice (maximum, then
+    # candidates); the others read only the candidate list's slots (not
+    # credited). Per-iteration figures leave the sweeps out.
+    iter_bytes = merge_bytes
+    sweep_bytes = 2 * 8.0 * T * r.sweeps
     total_wall = float(sum(wall))
     value = k * len(wall) / total_wall
     sym_per_s_agg = float(n_k.sum() / it_s.sum())
-    hbm_agg = float(iter_bytes.sum() / it_s.sum() / 1e9)
+    hbm_agg = float((iter_bytes.sum() + sweep_bytes) / it_s.sum() / 1e9)
     merge_gbps = float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9)
     per_it_sym = n_k / it_s
     per_it_gbps = iter_bytes / it_s / 1e9
@@ -409,8 +415,8 @@ def main() -> int:
         "hbm_gbps_per_iteration": {"aggregate": round(hbm_agg, 1), "frac_of_peak": round(hbm_agg / HBM_PEAK_GBPS, 4),
                                    "p10": round(pct(per_it_gbps, 10), 1), "p50": round(pct(per_it_gbps, 50), 1),
                                    "p90": round(pct(per_it_gbps, 90), 1)},
-        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_find_max": round(float(f_ms.sum()), 3),
-                                "k_merge_gbps": round(merge_gbps, 1)},
+        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_merge_gbps": round(merge_gbps, 1),
+                                "table_sweeps": int(r.sweeps)},
         "warmup_unprofiled_s": [round(x, 3) for x in warm_s],
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -429,8 +435,7 @@ def main() -> int:
     }
     if args.report:
         with open(args.report, "w") as fh:
-            json.dump({"summary": out, "lengths": lengths.tolist(), "find_max_ms": f_ms.tolist(),
-                       "merge_ms": m_ms.tolist()}, fh)
+            json.dump({"summary": out, "lengths": lengths.tolist(), "merge_ms": m_ms.tolist()}, fh)
     print(json.dumps(out), flush=True)
     return 0
 

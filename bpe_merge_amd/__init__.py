@@ -49,8 +49,8 @@ class Merge(ctypes.Structure):
 
 
 class ProfileResult(ctypes.Structure):
-    _fields_ = [("find_max_ms", ctypes.c_double), ("merge_ms", ctypes.c_double),
-                ("launches", ctypes.c_uint32), ("merges_done", ctypes.c_uint32)]
+    _fields_ = [("merge_ms", ctypes.c_double), ("launches", ctypes.c_uint32), ("merges_done", ctypes.c_uint32),
+                ("sweeps", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 _vp, _sz, _u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
@@ -67,7 +67,7 @@ _SIGS = {
     "bpe_tokens": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_lengths": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
     "bpe_pair_counts": (ctypes.c_int, [_vp, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
-    "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp, _vp]),
+    "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp]),
     "bpe_replay": (ctypes.c_int, [_vp, _vp, _u32]),
     "bpe_encode": (ctypes.c_int, [_vp, _sz, _vp, _u32, _cfgp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_trie_build": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(_vp)]),
@@ -408,14 +408,13 @@ class State:
         return keys[o], cnts[o]
 
     def profile(self, n_merges: int, per_iteration: bool = False):
-        """bpe_profile; with per_iteration also (find_ms, merge_ms) float32 arrays."""
+        """bpe_profile; with per_iteration also the per-iteration times (ms, float32)."""
         import numpy as np
         r = ProfileResult()
-        f = np.zeros(max(n_merges, 1), dtype=np.float32) if per_iteration else None
         m = np.zeros(max(n_merges, 1), dtype=np.float32) if per_iteration else None
-        _check(_lib.bpe_profile(self._h, n_merges, ctypes.byref(r), f.ctypes.data if per_iteration else None,
-                                m.ctypes.data if per_iteration else None), "bpe_profile")
-        return (r, f[:n_merges], m[:n_merges]) if per_iteration else r
+        _check(_lib.bpe_profile(self._h, n_merges, ctypes.byref(r), m.ctypes.data if per_iteration else None),
+               "bpe_profile")
+        return (r, m[:n_merges]) if per_iteration else r
 
     def free(self) -> None:
         if self._h:

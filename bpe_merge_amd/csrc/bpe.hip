@@ -1,11 +1,11 @@
 // Host driver and C ABI of the BPE training library (include/bpe.h).
 //
 // The whole merge loop is enqueued on one stream with no host round trip
-// between iterations: each iteration is a sweep of the global pair table
-// for the maximum (k_find_max) followed by the fused merge / compaction /
-// count-update pass (k_merge); both read the iteration
-// number, the merge and the sequence length from the device control block,
-// and do nothing once training has stopped. The host reads back a few bytes
+// between iterations: each iteration is one launch of the fused selection /
+// merge / compaction / count-update pass (k_merge), which reads the
+// iteration number, the merge and the sequence length from device state
+// prepared by the launch before it, and does nothing once training has
+// stopped. The host reads back a few bytes
 // of status at the end, then copies only the merges and tokens that exist,
 // in the spirit of the page's single submit with a sized readback ("Host
 // Mimarisi 4", page "bpe - GPU BPE Tokenizer Pipeline").
@@ -44,8 +44,6 @@ constexpr int TILE = MERGE_TPB_BIG * 16;   // the larger tile: symbol buffers ar
 constexpr int TILE_SMALL = MERGE_TPB_SMALL * 16;
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
-constexpr int FIND_TPB = 256;
-constexpr int FIND_U = 8;                  // 16-byte loads in flight per sweep thread
 
 thread_local std::string g_err;
 
@@ -170,7 +168,7 @@ struct bpe_state {
     uint32_t* lengths = nullptr;
     uint32_t* fpairs = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
-    int merge_grid = 0, tag_grid = 0, fill_grid = 0, find_grid = 0;
+    int merge_grid = 0, tag_grid = 0, fill_grid = 0;
     int merge_tpb = MERGE_TPB_BIG;
     bool poisoned = false;   // a device error was seen
 
@@ -180,29 +178,22 @@ struct bpe_state {
 
 namespace {
 
-void launch_find_max(bpe_state* s) {
-    hipLaunchKernelGGL((bpek::k_find_max<FIND_TPB, FIND_U>), dim3(s->find_grid), dim3(FIND_TPB), 0, s->stream,
-                       s->ctl, s->table, s->slots(), s->sweep);
-}
-
 void launch_merge(bpe_state* s) {
     if (s->merge_tpb == MERGE_TPB_BIG)
         hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG), 0,
                            s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           uint32_t(s->find_grid), s->merges);
+                           s->merges);
     else
         hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_SMALL),
                            0, s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           uint32_t(s->find_grid), s->merges);
+                           s->merges);
 }
 
 void launch_force(bpe_state* s) {
-    hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(bpek::FORCE_TPB), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs,
-                       uint32_t(s->find_grid));
+    hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(64), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs);
 }
 
 bpe_status launch_iteration(bpe_state* s) {
-    launch_find_max(s);
     launch_merge(s);
     return BPE_OK;
 }
@@ -250,7 +241,7 @@ bpe_status enqueue_run(bpe_state* s, uint32_t n_merges) {
         return BPE_EIDSPACE;
     }
     s->requested += n_merges;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->requested);
+    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
     return BPE_OK;
 }
 
@@ -372,11 +363,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, tag_grid_bound(n)));
     s->fill_grid = cus * 4;
-    // four sweep workgroups per CU (one round of loads each on the largest
-    // default table), fewer for small tables; each merge workgroup reads
-    // every sweep workgroup's maximum
-    s->find_grid = int(std::min<size_t>(std::min<size_t>(size_t(cus) * 4, bpek::SWEEP_MAX_BLOCKS),
-                                        std::max<size_t>(1, s->slots() / 2 / (FIND_TPB * FIND_U))));
+    // every merge workgroup takes part in a sweep of the table and in its
+    // barrier, so the grid must fit in the sweep maxima
+    if (s->merge_grid > int(bpek::SWEEP_MAX_BLOCKS)) s->merge_grid = int(bpek::SWEEP_MAX_BLOCKS);
 
     // input bytes: device memory is read in place, host memory is uploaded
     // into the second symbol buffer first (4n bytes hold n bytes)
@@ -460,7 +449,7 @@ bpe_status bpe_step(bpe_state* s, bpe_merge* out) {
         return BPE_EIDSPACE;
     }
     s->requested = before.k + 1;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->requested);
+    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
     launch_iteration(s);
     HIP_TRY(hipGetLastError());
     Ctl after;
@@ -563,8 +552,7 @@ bpe_status bpe_pair_counts(bpe_state* s, uint32_t* keys, uint32_t* counts, size_
     return BPE_OK;
 }
 
-bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res, float* find_ms,
-                       float* merge_ms) {
+bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res, float* merge_ms) {
     g_err.clear();
     if (!s || !res) {
         set_err("state and out must be non-NULL");
@@ -577,33 +565,33 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res,
     HIP_TRY(hipSetDevice(s->device));
     std::memset(res, 0, sizeof *res);
     std::vector<hipEvent_t>* ev = nullptr;
-    bpe_status st = event_pool(s->device, 2 * size_t(n_merges) + 1, &ev);
+    bpe_status st = event_pool(s->device, size_t(n_merges) + 1, &ev);
     if (st != BPE_OK) return st;
+    uint32_t sweeps0 = 0, sweeps1 = 0;
+    HIP_TRY(hipStreamSynchronize(s->stream));
+    HIP_TRY(hipMemcpy(&sweeps0, &s->sweep->sweeps, 4, hipMemcpyDeviceToHost));
     st = enqueue_run(s, n_merges);
     if (st != BPE_OK) return st;
     std::vector<hipEvent_t>& e = *ev;
     HIP_TRY(hipEventRecord(e[0], s->stream));
     for (uint32_t i = 0; i < n_merges; ++i) {
-        launch_find_max(s);
-        HIP_TRY(hipEventRecord(e[2 * size_t(i) + 1], s->stream));
         launch_merge(s);
-        HIP_TRY(hipEventRecord(e[2 * size_t(i) + 2], s->stream));
+        HIP_TRY(hipEventRecord(e[size_t(i) + 1], s->stream));
     }
     HIP_TRY(hipGetLastError());
-    HIP_TRY(hipEventSynchronize(e[2 * size_t(n_merges)]));
+    HIP_TRY(hipEventSynchronize(e[size_t(n_merges)]));
     for (uint32_t i = 0; i < n_merges; ++i) {
-        float a = 0.f, c = 0.f;
-        HIP_TRY(hipEventElapsedTime(&a, e[2 * size_t(i)], e[2 * size_t(i) + 1]));
-        HIP_TRY(hipEventElapsedTime(&c, e[2 * size_t(i) + 1], e[2 * size_t(i) + 2]));
-        res->find_max_ms += a;
+        float c = 0.f;
+        HIP_TRY(hipEventElapsedTime(&c, e[size_t(i)], e[size_t(i) + 1]));
         res->merge_ms += c;
-        if (find_ms) find_ms[i] = a;
         if (merge_ms) merge_ms[i] = c;
     }
     res->launches = n_merges;
     Ctl h;
     st = read_ctl(s, &h);
     res->merges_done = h.k;
+    HIP_TRY(hipMemcpy(&sweeps1, &s->sweep->sweeps, 4, hipMemcpyDeviceToHost));
+    res->sweeps = sweeps1 - sweeps0;
     return st;
 }
 
@@ -647,7 +635,7 @@ bpe_status bpe_replay(bpe_state* s, const bpe_merge* merges, uint32_t k) {
     HIP_TRY(hipMemcpyAsync(s->fpairs + 2 * size_t(m0), pairs.data(), 4 * pairs.size(), hipMemcpyHostToDevice,
                            s->stream));
     s->requested = m0 + k;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->requested);
+    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
     for (uint32_t i = 0; i < k; ++i) {
         launch_force(s);
         launch_merge(s);

@@ -10,14 +10,13 @@
 // How the work is laid out here (not the page's WGSL dispatch plan):
 //   k_tag_count  bytes -> tagged uint32 symbols, and the pair counts of
 //                iteration 0 in the global table (LDS aggregation first).
-//   k_find_max   one sweep of the global table for the maximum; the last
-//                workgroup to finish records the merge (device-resident, no
-//                host round trip).
-//   k_merge      (merge.hpp) one persistent pass over the symbols that
-//                applies the merge, compacts with a single-pass decoupled
-//                look-back scan, and updates the global table by the pairs
-//                the merge destroyed and created: the symbols are read once
-//                and written once per iteration.
+//   k_merge      (merge.hpp) one persistent pass per iteration that selects
+//                the merge (from a candidate list, or by a sweep of the
+//                global table when the list cannot vouch for the maximum),
+//                applies it, compacts with a single-pass decoupled look-back
+//                scan, and updates the global table by the pairs the merge
+//                destroyed and created: the symbols are read once and
+//                written once per iteration, with no host round trip.
 // The global table always holds the exact pair counts of the current
 // sequence, as a full recount would give them. A merge changes only the
 // pairs at its own sites: every other adjacency of the new sequence is an
@@ -55,24 +54,51 @@ struct alignas(64) Ctl {
     uint32_t err;         // ERR_* bits
     uint32_t n[2];        // symbol counts; n[m & 1] is the current one
     uint32_t L, R, X;     // merge being applied: (L, R) -> X
-    uint32_t tile_ctr;    // tiles handed out by k_merge, counted across iterations (mod 2^32)
+    uint32_t tile_ctr[2];  // tiles handed out by k_merge, per iteration parity (cleared one iteration ahead)
     uint32_t used;        // claimed slots of the global table
 };
 
-// What a k_find_max launch leaves for the k_merge launch after it: one
-// maximum per sweep workgroup (the kernel boundary publishes them, so the
-// sweep needs no atomics or fences), and the iteration it swept for
-// (NO_ITER if training had stopped), and the tile counter's value before
-// the iteration (tile numbers are counter values minus this base, modulo
-// 2^32, so the counter never needs a reset). k_merge reads the iteration from here,
-// never from the live counters in Ctl, so that all its workgroups agree on
-// it even if one starts after the last tile was written.
-constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;
+// Selection state, carried from one iteration's merge pass to the next.
+//
+// The merge of an iteration is the maximum over the global table of the
+// packed value count << 32 | ~key (highest count, ties to the smallest
+// (left, right), whatever the order of evaluation). A candidate list holds
+// every slot whose count is at least a threshold theta; whenever the
+// largest count on the list reaches theta, no slot off the list can beat
+// it and the maximum is taken over the list alone. The list stays complete
+// because the count of an existing pair only falls (every new adjacency
+// involves the newest id), and a new pair whose count the merge pass lifts
+// across theta is appended by the add that does it. When the list's
+// maximum falls below theta (or the list overflowed), the iteration sweeps
+// the whole table (every workgroup a share, one grid-wide barrier) and
+// rebuilds the list with theta = max - (max >> shift), the shift adapted
+// to the list sizes seen.
+//
+// Every workgroup of a merge launch makes the same selection at its start,
+// from the list and the table as the previous launch left them; no
+// workgroup changes the table until all have made theirs (started[]).
+// Counters are kept per iteration parity and cleared one iteration ahead,
+// so none needs a reset at the end of a launch.
+constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;  // workgroups that can take part in a sweep
 constexpr uint32_t NO_ITER = 0xFFFFFFFFu;
+constexpr uint32_t CAND_MAX = 16384;
+constexpr uint32_t CAND_TARGET = 2048;  // list size the shift steers towards
+constexpr uint32_t SHIFT_DEFAULT = 3;   // theta = 7/8 of the maximum
+constexpr uint32_t SHIFT_MAX = 16;
 struct Sweep {
-    unsigned long long bmax[SWEEP_MAX_BLOCKS];
-    uint32_t iter;
-    uint32_t tile_base;
+    unsigned long long bmax[SWEEP_MAX_BLOCKS];  // per-workgroup maxima of a sweep
+    unsigned long long best;                    // the replayed merge, packed
+    uint32_t iter;                              // the iteration the next launch runs (NO_ITER: none)
+    uint32_t force;                             // 1 + the iteration whose merge is best (0: none)
+    uint32_t theta;                             // the list's threshold
+    uint32_t shift;                             // of the last sweep (0: none yet)
+    uint32_t cand_n;                            // entries appended (above CAND_MAX: overflowed)
+    uint32_t cand_ok;                           // the list holds every slot with count >= theta
+    uint32_t started[2];                        // workgroups past their selection, per parity
+    uint32_t arrived[2];                        // workgroups at the sweep barrier, per parity
+    uint32_t sweeps;                            // iterations that swept the table
+    uint32_t pad;
+    uint32_t cand[CAND_MAX];  // slot indexes
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -134,10 +160,10 @@ __device__ __forceinline__ void fail_table(Ctl* ctl) {
     atomicExch(&ctl->done, 1u);
 }
 
-// Add delta (two's complement, so negative deltas work) to the count of key
-// in the global table, claiming a slot for a new key. Within one launch a
-// key only ever receives deltas of one sign, so no count goes below zero.
-__device__ __forceinline__ void gt_add(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl) {
+// The slot of key in the global table, claimed if the key is new; NO_SLOT
+// (and ERR_TABLE) if the table is full.
+constexpr uint32_t NO_SLOT = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t gt_slot(const GTable& gt, uint32_t key, Ctl* ctl) {
     uint32_t h = mix32(key) & gt.mask;
     for (uint32_t p = 0; p < GT_PROBES; ++p) {
         unsigned long long* slot = gt.slot + h;
@@ -151,13 +177,41 @@ __device__ __forceinline__ void gt_add(const GTable& gt, uint32_t key, uint32_t 
                 cur = (uint32_t)old;
             }
         }
-        if (cur == key) {
-            atomicAdd(slot, (unsigned long long)(long long)(int)delta << 32);
-            return;
-        }
+        if (cur == key) return h;
         h = (h + 1) & gt.mask;
     }
     fail_table(ctl);
+    return NO_SLOT;
+}
+
+// Add delta (two's complement, so negative deltas work) to the count of key
+// in the global table, claiming a slot for a new key. Within one launch a
+// key only ever receives deltas of one sign, so no count goes below zero.
+__device__ __forceinline__ void gt_add(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl) {
+    const uint32_t h = gt_slot(gt, key, ctl);
+    if (h != NO_SLOT) atomicAdd(gt.slot + h, (unsigned long long)(long long)(int)delta << 32);
+}
+
+// Append a slot to the candidate list (its entry is dropped past CAND_MAX;
+// the overflow shows in cand_n).
+__device__ __forceinline__ void cand_append(Sweep* sw, uint32_t slot) {
+    const uint32_t i = atomicAdd(&sw->cand_n, 1u);
+    if (i < CAND_MAX) __hip_atomic_store(&sw->cand[i], slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// gt_add for the merge pass: an increase that lifts the count from below
+// theta to theta or more appends the slot to the candidate list.
+__device__ __forceinline__ void gt_add_sel(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl, Sweep* sw,
+                                           uint32_t theta) {
+    const uint32_t h = gt_slot(gt, key, ctl);
+    if (h == NO_SLOT) return;
+    const unsigned long long d = (unsigned long long)(long long)(int)delta << 32;
+    if ((int)delta > 0) {
+        const uint32_t old = (uint32_t)(atomicAdd(gt.slot + h, d) >> 32);
+        if (old < theta && old + delta >= theta) cand_append(sw, h);
+    } else {
+        atomicAdd(gt.slot + h, d);
+    }
 }
 
 // ---------------------------------------------------------------- LDS table
@@ -315,13 +369,19 @@ __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
         ctl->k = 0; ctl->m = 0; ctl->limit = 0; ctl->done = 0; ctl->err = 0;
         ctl->n[0] = n; ctl->n[1] = 0;
         ctl->L = 0; ctl->R = 0; ctl->X = 0;
-        ctl->tile_ctr = 0; ctl->used = 0;
+        ctl->tile_ctr[0] = 0; ctl->tile_ctr[1] = 0; ctl->used = 0;
         lengths[0] = n;
     }
 }
 
-__global__ void k_set_limit(Ctl* ctl, uint32_t limit) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) ctl->limit = limit;
+// Set the number of iterations allowed in total, and with it the next
+// iteration to run (none once training has stopped or the limit is reached).
+__global__ void k_set_limit(Ctl* ctl, Sweep* sw, uint32_t limit) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        ctl->limit = limit;
+        const uint32_t m = ctl->m;
+        sw->iter = (!ctl->done && m < limit) ? m : NO_ITER;
+    }
 }
 
 // fill a buffer of 64-bit words with one value (status words, table slots)
@@ -404,13 +464,8 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
 }
 
 // ---------------------------------------------------------------- maximum
-// Sweep of the global table for the maximum of the packed value
-// (count << 32 | ~key) over slots with a nonzero count: highest count, ties
-// to the smallest (left, right), whatever the order of the sweep. Each
-// workgroup stores its maximum in Sweep; the merge pass that follows takes
-// the maximum of those, records the merge, or marks training done when no
-// pair has a nonzero count. Workgroup 0 also records the iteration and the
-// tile counter's base for it.
+// Packed candidates (count << 32 | ~key) of table slots, compared as
+// unsigned 64-bit values: highest count, ties to the smallest key.
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -428,56 +483,13 @@ __device__ __forceinline__ unsigned long long candidate(unsigned long long v) {
     return (v >> 32) ? (v ^ 0xFFFFFFFFull) : 0ull;
 }
 
-// U 16-byte loads in flight per thread; gridDim.x <= SWEEP_MAX_BLOCKS
-template <int TPB, int U>
-__global__ __launch_bounds__(TPB) void k_find_max(Ctl* ctl, const unsigned long long* __restrict__ table,
-                                                  uint32_t slots, Sweep* sw) {
-    __shared__ unsigned long long s_best[TPB / 64];
-    const uint32_t done = ld_relaxed(&ctl->done);
-    const uint32_t m = ld_relaxed(&ctl->m);
-    const uint32_t limit = ld_relaxed(&ctl->limit);
-    const bool active = !done && m < limit;  // uniform over the grid
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        sw->iter = active ? m : NO_ITER;
-        sw->tile_base = ld_relaxed(&ctl->tile_ctr);  // no k_merge runs during the sweep
-    }
-    if (!active) return;
-
-    // two slots per 16-byte load (slots is a power of two >= 1024)
-    const ulonglong2* t2 = reinterpret_cast<const ulonglong2*>(table);
-    const uint32_t n2 = slots / 2;
-    unsigned long long best = 0ull;
-    for (uint32_t i0 = blockIdx.x * (TPB * U) + threadIdx.x; i0 < n2; i0 += gridDim.x * (TPB * U)) {
-        ulonglong2 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = (i0 + u * TPB < n2) ? t2[i0 + u * TPB] : make_ulonglong2(0ull, 0ull);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const unsigned long long a = candidate(v[u].x), c = candidate(v[u].y);
-            best = a > best ? a : best;
-            best = c > best ? c : best;
-        }
-    }
-    best = wave_max_u64(best);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) s_best[w] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long b = 0ull;
-        for (int i = 0; i < TPB / 64; ++i) b = s_best[i] > b ? s_best[i] : b;
-        sw->bmax[blockIdx.x] = b;
-    }
-}
-
 // ---------------------------------------------------------------- replay
 // A replayed iteration: the merge is the given pair pairs[2m], pairs[2m+1]
 // for iteration m (a learned merge list applied in order, "Nedir bu ya?"),
-// not the table's maximum. It takes the sweep's place: the pair, with its
-// count looked up in the table, becomes the only nonzero per-workgroup
-// maximum, so the merge pass picks it through its ordinary reduction (the
-// value is never 0 since ~key != 0 for 16-bit ids, so a pair that does not
-// occur still counts as a merge: count 0, nothing changes, id 256 + m is
-// used up).
+// not the table's maximum, with its count looked up in the table (a pair
+// that does not occur still counts as a merge: count 0, nothing changes,
+// id 256 + m is used up; the packed value is never 0 since ~key != 0 for
+// 16-bit ids). The candidate list stays valid through it.
 
 __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     uint32_t h = mix32(key) & gt.mask;
@@ -492,29 +504,15 @@ __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     return 0u;
 }
 
-// One workgroup of FORCE_TPB threads; nsweep (<= SWEEP_MAX_BLOCKS) is the
-// number of maxima the merge pass reduces.
-constexpr int FORCE_TPB = 256;
-__global__ __launch_bounds__(FORCE_TPB) void k_force(Ctl* ctl, GTable gt, Sweep* sw,
-                                                     const uint32_t* __restrict__ pairs, uint32_t nsweep) {
-    if (blockIdx.x != 0) return;
-    const uint32_t done = ld_relaxed(&ctl->done);
-    const uint32_t m = ld_relaxed(&ctl->m);
-    const uint32_t limit = ld_relaxed(&ctl->limit);
-    const bool active = !done && m < limit;
-    if (threadIdx.x == 0) {
-        sw->iter = active ? m : NO_ITER;
-        sw->tile_base = ld_relaxed(&ctl->tile_ctr);
-    }
+__global__ void k_force(Ctl* ctl, GTable gt, Sweep* sw, const uint32_t* __restrict__ pairs) {
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    const uint32_t m = ctl->m;
+    const bool active = !ctl->done && m < ctl->limit;
+    sw->iter = active ? m : NO_ITER;
     if (!active) return;
-    for (uint32_t i = threadIdx.x; i < nsweep; i += FORCE_TPB) {
-        unsigned long long v = 0ull;
-        if (i == 0) {
-            const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
-            v = ((unsigned long long)gt_count(gt, key) << 32) | (uint32_t)~key;
-        }
-        sw->bmax[i] = v;
-    }
+    const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
+    sw->best = ((unsigned long long)gt_count(gt, key) << 32) | (uint32_t)~key;
+    sw->force = m + 1u;
 }
 
 }  // namespace bpek

@@ -1,7 +1,8 @@
 // Merge + compaction + count update: one pass over the symbols per
 // training iteration (gfx950, wave64).
 //
-// For the merge (L, R) -> X chosen by k_find_max, the pass
+// For the merge (L, R) -> X (the table's maximum, selected at the start of
+// the pass from a candidate list or by a sweep of the table), the pass
 //   1. applies the merge left to right without overlap (page "bpe - GPU BPE
 //      Tokenizer Pipeline", "Nedir bu ya?"; chains of identical pairs
 //      resolved by run-length parity),
@@ -264,6 +265,20 @@ struct CountArgs {
     uint32_t o, kept;
 };
 
+// Bounded wait until every workgroup of the launch has made
+// its selection: the table and the list may change only after that.
+__device__ __forceinline__ void wait_all_started(const Sweep* sw, uint32_t p, Ctl* ctl) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(&sw->started[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+        if (++spins > SPIN_LIMIT) {
+            atomicOr(&ctl->err, ERR_SPIN);
+            atomicExch(&ctl->done, 1u);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Apply one thread's count changes (masks from Changes) to the workgroup's
 // LDS table (the global table when LDS has no room), one changed pair per
 // loop turn, so that the insert code exists once. The old symbol at a
@@ -272,10 +287,10 @@ struct CountArgs {
 // kept unchanged and already staged in LDS (st, at the thread's offset o
 // plus the number of kept positions before j). left: old symbol at g0 - 1.
 template <int LT>
-__device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, uint32_t gone,
-                                              uint32_t born, uint32_t sel, uint32_t sel_in, uint32_t left,
-                                              const uint32_t* st, uint32_t o, uint32_t kept, uint32_t L,
-                                              uint32_t R, uint32_t X) {
+__device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, Sweep* sw,
+                                              uint32_t p, uint32_t theta, uint32_t gone, uint32_t born, uint32_t sel,
+                                              uint32_t sel_in, uint32_t left, const uint32_t* st, uint32_t o,
+                                              uint32_t kept, uint32_t L, uint32_t R, uint32_t X) {
     auto old_id = [&](uint32_t j) -> uint32_t {
         if ((sel >> j) & 1u) return R;
         if ((sel >> (j + 1)) & 1u) return L;
@@ -296,7 +311,10 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
             delta = 1u;
             born &= born - 1u;
         }
-        if (!tab.insert(key, delta)) gt_add(gt, key, delta, ctl);
+        if (!tab.insert(key, delta)) {  // the LDS table is full: straight to the global one
+            wait_all_started(sw, p, ctl);
+            gt_add_sel(gt, key, delta, ctl, sw, theta);
+        }
     }
 }
 
@@ -457,12 +475,13 @@ __device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (
 }
 
 // The last tile publishes the new length and advances the iteration.
+// Nothing in this launch reads these; the next launch and the host read
+// them after the kernel boundary.
 __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, uint32_t it, uint32_t total) {
     ctl->n[(it + 1) & 1u] = total;
     lengths[it + 1] = total;
     ctl->k = it + 1;
-    __threadfence();
-    atomicExch(&ctl->m, it + 1);
+    ctl->m = it + 1;
 }
 
 // Look-back of the pipelined path: windows of 64 * LB_PL status words; the
@@ -538,13 +557,135 @@ __device__ __forceinline__ void retire(const uint32_t (&x)[16], uint32_t h1, uin
                  "v"(h1), "v"(h2), "v"(hr));
 }
 
+// ---------------------------------------------------------------- selection
+constexpr int SWEEP_UNROLL = 8;  // table loads in flight per thread
+
+// The largest packed candidate in this workgroup's share of the table
+// (slots blockIdx.x * TPB + tid + k * gridDim.x * TPB), or, with COLLECT,
+// the share's slots whose count is theta or more appended to the
+// candidate list. Plain loads: while the maximum is taken no workgroup
+// changes the table; while candidates are collected one may, but a count
+// read before an increase that crosses theta is covered by the append of
+// that increase, and counts of existing pairs only fall.
+template <int TPB, bool COLLECT>
+__device__ __forceinline__ unsigned long long sweep_share(const GTable& gt, Sweep* sw, uint32_t theta) {
+    const uint32_t slots = gt.mask + 1u;
+    const uint32_t stride = gridDim.x * TPB;
+    unsigned long long best = 0ull;
+    for (uint32_t s0 = blockIdx.x * TPB + threadIdx.x; s0 < slots; s0 += SWEEP_UNROLL * stride) {
+        unsigned long long v[SWEEP_UNROLL];
+#pragma unroll
+        for (int k = 0; k < SWEEP_UNROLL; ++k) {
+            const uint32_t i = s0 + k * stride;
+            v[k] = i < slots ? gt.slot[i] : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < SWEEP_UNROLL; ++k) {
+            if (COLLECT) {
+                if ((uint32_t)(v[k] >> 32) >= theta) cand_append(sw, s0 + k * stride);  // 0 past the end
+            } else {
+                const unsigned long long c = candidate(v[k]);
+                best = c > best ? c : best;
+            }
+        }
+    }
+    return best;
+}
+
+// Maximum of v over the workgroup (every thread gets it). s_best: NW slots.
+template <int NW>
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* s_best,
+                                                             uint32_t lane, uint32_t w) {
+    v = wave_max_u64(v);
+    if (lane == 0) s_best[w] = v;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) v = s_best[i] > v ? s_best[i] : v;
+    lds_barrier();  // s_best free again
+    return v;
+}
+
+// The largest packed candidate among the list's first n entries whose
+// count is theta or more (0 if none). Every workgroup reads the same list
+// and table, left by the previous launch (plain loads, cached per XCD).
+template <int TPB>
+__device__ __forceinline__ unsigned long long list_max(const GTable& gt, const Sweep* sw, uint32_t n, uint32_t theta,
+                                                        unsigned long long* s_best, uint32_t lane, uint32_t w) {
+    unsigned long long best = 0ull;
+    for (uint32_t i = threadIdx.x; i < n; i += TPB) {
+        const unsigned long long v = gt.slot[sw->cand[i] & gt.mask];
+        const unsigned long long c = (uint32_t)(v >> 32) >= theta ? candidate(v) : 0ull;
+        best = c > best ? c : best;
+    }
+    return block_max_u64<TPB / 64>(best, s_best, lane, w);
+}
+
+// An iteration that sweeps the table: every workgroup takes the maximum of
+// its share and publishes it; the last to arrive empties the list (every
+// workgroup arrives after its selection, so no one reads the list any
+// more) and then releases the others; all take the maximum of all
+// maxima. (The workgroups of the persistent grid all run at once, as for
+// the look-back; the wait is bounded, ERR_SPIN.) Then theta = max - (max
+// >> shift), and every workgroup appends its share's slots at or above it.
+template <int TPB>
+__device__ __forceinline__ unsigned long long sweep_select(const GTable& gt, Sweep* sw, Ctl* ctl, uint32_t p,
+                                                            uint32_t shift, unsigned long long* s_best,
+                                                            uint32_t lane, uint32_t w, uint32_t& theta) {
+    constexpr int NW = TPB / 64;
+    unsigned long long best = block_max_u64<NW>(sweep_share<TPB, false>(gt, sw, 0u), s_best, lane, w);
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&sw->bmax[blockIdx.x], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t a = __hip_atomic_fetch_add(&sw->arrived[p], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (a + 1u == gridDim.x) {
+            __hip_atomic_store(&sw->cand_n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&sw->arrived[p], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&sw->arrived[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <= gridDim.x) {
+            if (++spins > SPIN_LIMIT) {
+                atomicOr(&ctl->err, ERR_SPIN);
+                atomicExch(&ctl->done, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    lds_barrier();
+    best = 0ull;
+    for (uint32_t i = threadIdx.x; i < gridDim.x; i += TPB) {
+        const unsigned long long b = __hip_atomic_load(&sw->bmax[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        best = b > best ? b : best;
+    }
+    best = block_max_u64<NW>(best, s_best, lane, w);
+    const uint32_t m = (uint32_t)(best >> 32);
+    theta = m - (m >> shift);
+    if (best != 0ull) sweep_share<TPB, true>(gt, sw, theta);
+    return best;
+}
+
+// The per-workgroup flush of count changes (flush_table) with the merge
+// pass's table adds.
+template <int LT>
+__device__ __forceinline__ void flush_table_sel(LdsTable<LT>& tab, int tpb, const GTable& gt, Ctl* ctl, Sweep* sw,
+                                                uint32_t theta) {
+    for (int i = threadIdx.x; i < LT; i += tpb) {
+        const uint32_t key = tab.keys[i], c = tab.cnts[i];
+        if (key != EMPTY && c != 0u) gt_add_sel(gt, key, c, ctl, sw, theta);
+        tab.keys[i] = EMPTY;
+        tab.cnts[i] = 0u;
+    }
+    if (threadIdx.x == 0) {
+        tab.used = 0u;
+        tab.qn = 0u;
+    }
+}
+
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
                                                uint32_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
-                                               uint32_t* lengths, const Sweep* sw, uint32_t nsweep,
-                                               uint32_t* merges) {
+                                               uint32_t* lengths, Sweep* sw, uint32_t* merges) {
     constexpr int V = 16;  // symbols per thread: four 16-byte loads
     constexpr int TILE = TPB * V;
     constexpr int NW = TPB / 64;
@@ -557,8 +698,9 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     __shared__ unsigned long long s_best[NW];
     __shared__ __align__(16) unsigned long long s_win[LB_WIN];
 
-    const uint32_t it = sw->iter;  // written by the sweep before this launch
-    if (it == NO_ITER) return;     // training has stopped (uniform)
+    const uint32_t it = sw->iter;  // prepared by the previous launch (or k_set_limit, k_force)
+    if (it == NO_ITER || ctl->done) return;  // training has stopped (uniform)
+    const uint32_t p = it & 1u;                 // parity of the per-iteration counters
     const uint32_t n = ctl->n[it & 1u];
     const uint32_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
     uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
@@ -570,19 +712,14 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     const bool do_count = X != IDM;
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: in a scalar register
-    uint32_t* tile_ctr = &ctl->tile_ctr;
-    const uint32_t tile_base = sw->tile_base;
-
-    // ---- the merge: the maximum of the sweep's per-workgroup maxima. These
-    // loads go first: waiting for them then does not wait for the tile's.
-    unsigned long long best = 0ull;
-    {
-        // nsweep <= SWEEP_MAX_BLOCKS = 2 * TPB
-        const unsigned long long b0 = tid < nsweep ? sw->bmax[tid] : 0ull;
-        const unsigned long long b1 = tid + TPB < nsweep ? sw->bmax[tid + TPB] : 0ull;
-        best = b0 > b1 ? b0 : b1;
+    uint32_t* tile_ctr = &ctl->tile_ctr[p];
+    constexpr uint32_t tile_base = 0u;
+    if (blockIdx.x == 0 && tid == 0) {
+        // the counters of the next iteration (the previous one's are done with)
+        __hip_atomic_store(&ctl->tile_ctr[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&sw->started[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&sw->arrived[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    static_assert(SWEEP_MAX_BLOCKS <= 2 * TPB, "two sweep maxima per thread");
 
     tab.clear(TPB);
     if (tid == 0) s_tile[0] = atomicAdd(tile_ctr, 1u) - tile_base;
@@ -592,11 +729,34 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
     load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
 
-    best = wave_max_u64(best);
-    if (lane == 0) s_best[w] = best;
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NW; ++i) best = s_best[i] > best ? s_best[i] : best;
+    // ---- the merge: a replayed pair, the list's maximum, or a sweep's. All
+    // workgroups read the same state, so all take the same branch.
+    unsigned long long best = 0ull;
+    uint32_t theta = sw->theta;
+    uint32_t shift = sw->shift ? sw->shift : SHIFT_DEFAULT;
+    bool sweep = false;
+    if (sw->force == it + 1u) {
+        best = sw->best;
+    } else {
+        const uint32_t nc = sw->cand_n;
+        const bool ok = sw->cand_ok != 0u;
+        if (ok && nc <= CAND_MAX) best = list_max<TPB>(gt, sw, nc, theta, s_best, lane, w);
+        sweep = best == 0ull;  // the list is invalid, overflowed or below theta
+        // steer the next list's size: more than the target (or an overflow)
+        // narrows the window, a small list widens it
+        if (ok && nc > CAND_TARGET) shift = min(shift + 1u, SHIFT_MAX);
+        else if (ok && nc < CAND_TARGET / 16u && shift > 1u) shift = shift - 1u;
+    }
+    if (tid == 0) atomicAdd(&sw->started[p], 1u);  // this workgroup's reads of the list are done
+    if (sweep) {  // uniform
+        best = sweep_select<TPB>(gt, sw, ctl, p, shift, s_best, lane, w, theta);
+        if (blockIdx.x == 0 && tid == 0) {  // every workgroup has read the old values
+            sw->theta = theta;
+            sw->shift = shift;
+            sw->cand_ok = 1u;
+            sw->sweeps += 1u;
+        }
+    }
     if (best == 0ull) {  // uniform: no countable pair is left
         if (blockIdx.x == 0 && tid == 0) ctl->done = 1u;
         return;
@@ -677,7 +837,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                count_changes<LT>(tab, gt, ctl, sw, p, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
                                   L, R, X);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
@@ -836,7 +996,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                count_changes<LT>(tab, gt, ctl, sw, p, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
                                   L, R, X);
             // ---- the previous tile: its offset (unless its look-back is done)
             if (tp < ntiles && w == 0) {
@@ -874,8 +1034,10 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             t = tn;
         }
     }
+    if (tid == 0) wait_all_started(sw, p, ctl);  // before the table changes
     lds_barrier();
-    if (tab.used) flush_table(tab, TPB, gt, ctl);  // uniform: read after the barrier
+    if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
+    if (blockIdx.x == 0 && tid == 0) sw->iter = it + 1u < ctl->limit ? it + 1u : NO_ITER;  // all have read it
 }
 
 }  // namespace bpek

@@ -262,22 +262,24 @@ bpe_status bpe_trie_profile(bpe_trie *t, const uint8_t *bytes, size_t n, uint32_
 /* Release the trie and its buffers. NULL is a no-op. */
 void bpe_trie_free(bpe_trie *t);
 
-/* Per-kernel device time of the iterations run by bpe_profile. */
+/* Device time of the iterations run by bpe_profile. */
 typedef struct {
-    double find_max_ms;      /* total time of the table sweep + argmax launches      */
-    double merge_ms;         /* total time of the fused merge/compact/count launches */
-    uint32_t launches;       /* number of iterations timed (each has one of each)    */
-    uint32_t merges_done;    /* merges produced by the state after the run           */
+    double merge_ms;         /* total time of the iteration launches (selection, merge,
+                                compaction and count update: one launch each)        */
+    uint32_t launches;       /* number of iterations timed                            */
+    uint32_t merges_done;    /* merges produced by the state after the run            */
+    uint32_t sweeps;         /* iterations among them that swept the whole pair table
+                                (the others took the merge from the candidate list)   */
+    uint32_t reserved;       /* 0 */
 } bpe_profile_result;
 
 /* Like bpe_run followed by bpe_sync, but with a HIP event recorded on the
-   state's stream between consecutive kernel launches, to time each kernel.
-   find_ms / merge_ms (host, n_merges entries each, or NULL) receive the
-   per-iteration times; iterations after training stopped take ~0 ms. One
-   host wait at the end, as in bpe_run + bpe_sync. The events are created
-   once per device and kept until the process ends. */
-bpe_status bpe_profile(bpe_state *s, uint32_t n_merges, bpe_profile_result *out, float *find_ms,
-                       float *merge_ms);
+   state's stream after each iteration's launch, to time it. merge_ms (host,
+   n_merges entries, or NULL) receives the per-iteration times; iterations
+   after training stopped take ~0 ms. One host wait at the end, as in
+   bpe_run + bpe_sync. The events are created once per device and kept until
+   the process ends. */
+bpe_status bpe_profile(bpe_state *s, uint32_t n_merges, bpe_profile_result *out, float *merge_ms);
 
 /* Release the state and everything it owns (not a caller workspace). NULL is a no-op. */
 void bpe_free(bpe_state *s);

@@ -111,7 +111,7 @@ def test_state_calls_reject_null(bpe):
     assert lib.bpe_merges(None, None, 0, None) == bpe.EINVAL
     assert lib.bpe_lengths(None, None, 0, None) == bpe.EINVAL
     assert lib.bpe_pair_counts(None, None, None, 0, None) == bpe.EINVAL
-    assert lib.bpe_profile(None, 1, None, None, None) == bpe.EINVAL
+    assert lib.bpe_profile(None, 1, None, None) == bpe.EINVAL
     lib.bpe_free(None)  # no-op
 
 
