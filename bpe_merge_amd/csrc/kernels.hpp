@@ -201,18 +201,17 @@ __device__ __forceinline__ void cand_append(Sweep* sw, uint32_t slot) {
 
 // gt_add for the merge pass: an increase that lifts the count from below
 // theta to theta or more appends the slot to the candidate list.
-// The returned count is consumed right away on every path (the empty asm):
-// a returning atomic left pending on some path makes the compiler drain
-// all vector memory operations before the register is next written, far
-// from here (on gfx9 one in-order counter covers loads and stores).
 __device__ __forceinline__ void gt_add_sel(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl, Sweep* sw,
                                            uint32_t theta) {
     const uint32_t h = gt_slot(gt, key, ctl);
     if (h == NO_SLOT) return;
     const unsigned long long d = (unsigned long long)(long long)(int)delta << 32;
-    const uint32_t old = (uint32_t)(atomicAdd(gt.slot + h, d) >> 32);
-    asm volatile("" ::"v"(old));
-    if ((int)delta > 0 && old < theta && old + delta >= theta) cand_append(sw, h);
+    if ((int)delta > 0) {
+        const uint32_t old = (uint32_t)(atomicAdd(gt.slot + h, d) >> 32);
+        if (old < theta && old + delta >= theta) cand_append(sw, h);
+    } else {
+        atomicAdd(gt.slot + h, d);
+    }
 }
 
 // ---------------------------------------------------------------- LDS table
