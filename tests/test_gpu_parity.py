@@ -219,3 +219,40 @@ def test_large_corpus_uses_the_large_tiles_and_matches(bpe):
         om, ot, _ = oracle.train_chunks(d, 400)
         assert np.array_equal(gm.cpu().numpy().astype(np.int64), om), cfg
         assert np.array_equal(gt.cpu().numpy().astype(np.uint32), ot), cfg
+
+
+def test_interleaved_state_calls_match_training(bpe):
+    # run, step, profile and run again on one state: the merge of every
+    # iteration is selected on the device from state the previous launch
+    # left (candidate list or table sweep), whatever call enqueued it
+    d = corpus.generate(corpus.CONFIGS[3].scaled(3_000_000, seed=17))
+    om, ot, _ = oracle.train_chunks(d, 200)
+    with bpe.State(_dev(d), table_log2=20) as st:
+        r = st.profile(20)
+        assert r.launches == 20 and r.merges_done == 20
+        assert 1 <= r.sweeps <= 20  # a fresh state has no candidate list yet
+        st.run(30)
+        assert st.sync() == 50
+        for k in range(50, 60):
+            assert st.step() == tuple(int(x) for x in om[k]), k
+        st.run(40)
+        r = st.profile(30)
+        assert r.launches == 30 and r.merges_done == 130 and 0 <= r.sweeps <= 30
+        st.run(70)
+        assert st.sync() == 200
+        assert np.array_equal(st.merges().cpu().numpy().astype(np.int64), om)
+        assert np.array_equal(st.tokens().cpu().numpy().astype(np.uint32), ot)
+
+
+def test_words_of_uniform_letters_many_near_ties(bpe):
+    # flat pair counts: hundreds of pairs within a few percent of the
+    # maximum keep the candidate list long and its threshold busy
+    rng = np.random.default_rng(23)
+    letters = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz", dtype=np.uint8)
+    words = [letters[rng.integers(0, 26, int(rng.integers(2, 9)))].tobytes() for _ in range(3000)]
+    text = b" ".join(words[int(i)] for i in rng.integers(0, 3000, 120_000))
+    d = np.frombuffer(text, dtype=np.uint8)
+    _say("uniform letters n=%d" % d.size)
+    gm, gt = gpu_train(bpe, d, 600, table_log2=18)
+    om, ot, _ = oracle.train_chunks(d, 600)
+    assert np.array_equal(gm, om) and np.array_equal(gt, ot)
