@@ -30,7 +30,8 @@ are read from cache, and the per-tile slices are implementation traffic:
 timed, not credited.
 
 "encoding" reports encoding of the same corpus with the same merges (a
-learned list applied to new text, word by word), with the same accounting.
+learned list applied to new text, word by word, each distinct word encoded
+once), with the same accounting.
 """
 from __future__ import annotations
 
@@ -171,13 +172,21 @@ def inference_leg(args, bpe, spec, data, d, m, np, torch, time, log, source="lea
     return inference
 
 
-def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above"):
+def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above", train_tokens=None):
     """Encoding of the corpus (device-resident) with merges m, word by word,
-    timed per kernel; returns the report object."""
+    timed per kernel; returns the report object. With the training run's
+    tokens given, the whole encoding is compared with them (encoding a
+    training corpus with its own merges must give its training tokens)."""
     k = int(m.shape[0])
     log("encoding: the %d merges over the same corpus, %d runs" % (k, args.inference_reps))
+    same_as_training = None
     with bpe.Encoder(m) as enc:
         n_tok, ms = enc.profile(d, args.inference_reps)
+        if train_tokens is not None:
+            whole = enc.encode(d)
+            same_as_training = bool(whole.shape == train_tokens.shape and bool((whole == train_tokens).all()))
+            del whole
+            log("encoding: whole corpus identical to the training tokens: %s" % same_as_training)
         sample_n = min(spec.n_bytes, 128 << 10)
         gpu_sample = None
         if not args.no_cpu_baseline:
@@ -202,20 +211,22 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
                          "the same bytes identical: %s" % (sample_n, cpu_s, bool(np.array_equal(ot, gpu_sample))),
                "pinned": "one core (sched_setaffinity)", **cpu_facts()}
         log("encoding oracle: %.2f s on %d bytes, identical: %s" % (cpu_s, sample_n, np.array_equal(ot, gpu_sample)))
-    log("encoding: %.3f ms per run (walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, %d tokens"
-        % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], enc_gbps, n_tok))
+    log("encoding: %.3f ms per run (word cache %.3f, walk %.3f, scan %.3f, copy %.3f), %.1f GB/s algorithmic, "
+        "%d tokens" % (avg_ms, per_kernel[0], per_kernel[1], per_kernel[2], per_kernel[3], enc_gbps, n_tok))
     return {
         "metric": "BPE encoding of new text with a merge list, input bytes/s",
         "value": round(spec.n_bytes / (avg_ms / 1e3), 1),
         "unit": "bytes/s",
         "workload": "%s corpus (%d bytes), the %d merges %s" % (spec.name, spec.n_bytes, k, source),
         "tokens": int(n_tok),
+        "identical_to_training_tokens": same_as_training,
         "runs": len(ms),
         "ms_per_run": {"mean": round(avg_ms, 4), "min": round(float(ms.min()), 4), "max": round(float(ms.max()), 4)},
-        "kernels_ms_per_run": {"k_enc_walk": round(float(per_kernel[0]), 4),
-                               "k_trie_scan": round(float(per_kernel[1]), 4),
-                               "k_enc_copy": round(float(per_kernel[2]), 4)},
-        "roofline": {"bound": "hbm", "kernel": "all three passes", "achieved": round(enc_gbps, 1),
+        "kernels_ms_per_run": {"word_cache": round(float(per_kernel[0]), 4),
+                               "k_enc_walk": round(float(per_kernel[1]), 4),
+                               "k_trie_scan": round(float(per_kernel[2]), 4),
+                               "k_enc_copy": round(float(per_kernel[3]), 4)},
+        "roofline": {"bound": "hbm", "kernel": "all passes", "achieved": round(enc_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": round(enc_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
@@ -386,7 +397,7 @@ def main() -> int:
     encoding = None
     if not args.no_inference:
         inference = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log)
-        encoding = encode_leg(args, bpe, spec, data, d, m, np, time, log)
+        encoding = encode_leg(args, bpe, spec, data, d, m, np, time, log, train_tokens=t)
 
     out = {
         "metric": "BPE train merges/sec + symbols/sec per merge, 256 MiB/32k merges; HBM GB/s",

@@ -79,6 +79,7 @@ _SIGS = {
     "bpe_encoder_encode": (ctypes.c_int, [_vp, _vp, _sz, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_encoder_profile": (ctypes.c_int, [_vp, _vp, _sz, _u32, _vp, ctypes.POINTER(_sz)]),
     "bpe_encoder_free": (None, [_vp]),
+    "bpe_encoder_cache": (ctypes.c_int, [_vp, _u32, _u32]),
     "bpe_free": (None, [_vp]),
     "bpe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "bpe_last_error": (ctypes.c_char_p, []),
@@ -229,15 +230,24 @@ class Encoder:
         return out[: n_tok.value]
 
     def profile(self, data, reps: int):
-        """bpe_encoder_profile: (n_tokens, device ms of shape [reps, 3]: walk,
-        scan and copy of each run)."""
+        """bpe_encoder_profile: (n_tokens, device ms of shape [reps, 4]: word
+        cache, walk, scan and copy of each run)."""
         import numpy as np
         data = data.contiguous().reshape(-1)
-        ms = np.zeros(3 * max(reps, 1), dtype=np.float32)
+        ms = np.zeros(4 * max(reps, 1), dtype=np.float32)
         n_tok = _sz(0)
         _check(_lib.bpe_encoder_profile(self._h, data.data_ptr(), data.numel(), reps, ms.ctypes.data,
                                         ctypes.byref(n_tok)), "bpe_encoder_profile")
-        return n_tok.value, ms[: 3 * reps].reshape(reps, 3)
+        return n_tok.value, ms[: 4 * reps].reshape(reps, 4)
+
+    CACHE_AUTO = 0xFFFFFFFF
+    CACHE_KEY_BITS = 58
+
+    def cache(self, log2_slots=CACHE_AUTO, key_bits=CACHE_KEY_BITS):
+        """bpe_encoder_cache: word-cache size for later calls (CACHE_AUTO, 0 =
+        off, or 8..24) and key bits (fewer share keys more; a testing aid)."""
+        _check(_lib.bpe_encoder_cache(self._h, log2_slots, key_bits), "bpe_encoder_cache")
+        return self
 
     def free(self) -> None:
         if self._h:

@@ -1169,17 +1169,38 @@ struct bpe_encoder {
     size_t text_cap = 0;
     uint32_t* tok_buf = nullptr;
     size_t tok_cap = 0;
-    int walk_grid = 0, copy_grid = 0;
+    // word cache: keys, positions and the claim list per slot, records
+    unsigned long long* wc_key = nullptr;
+    size_t wc_key_cap = 0;
+    uint32_t* wc_pos = nullptr;
+    size_t wc_pos_cap = 0;
+    uint32_t* wc_list = nullptr;
+    size_t wc_list_cap = 0;
+    uint32_t* wc_rec = nullptr;
+    size_t wc_rec_cap = 0;
+    uint32_t wc_log2 = 0, wc_key_bits = BPE_CACHE_KEY_BITS;  // no word cache until asked for
+    int walk_grid = 0, copy_grid = 0, insert_grid = 0, fill_grid = 0, clear_grid = 0;
 };
 
 namespace {
 
 constexpr int ENC_TPB = 256;
+constexpr int WC_FILL_TPB = 256;
+constexpr uint32_t WC_AUTO_MAX_LOG2 = 22;  // automatic size: 2^22 slots at most (512 MiB of records)
 constexpr uint32_t ENC_TILE = ENC_TPB * 16;
 constexpr uint32_t ENC_CAP = ENC_TILE + ENC_TPB * bpek::TRIE_HALO_PER_THREAD;
 constexpr size_t ENC_SCRATCH_MAX = size_t(1) << 24;  // positions of long words per call
 
 size_t enc_scratch_cap(size_t n) { return std::min(n, ENC_SCRATCH_MAX); }
+
+// Slots of the word cache for n bytes (0: no cache). Automatic: one slot
+// per 128 input bytes, a power of two in [2^10, 2^22]; claims stop at half.
+uint32_t enc_wc_log2(const bpe_encoder* e, size_t n) {
+    if (e->wc_log2 != BPE_CACHE_AUTO) return e->wc_log2;
+    uint32_t l = 10;
+    while (l < WC_AUTO_MAX_LOG2 && (size_t(1) << l) < n / 128) ++l;
+    return l;
+}
 
 bpe_status enc_pools(bpe_encoder* e, size_t n) {
     const size_t ntiles = (n + ENC_TILE - 1) / ENC_TILE;
@@ -1190,6 +1211,14 @@ bpe_status enc_pools(bpe_encoder* e, size_t n) {
     if (st == BPE_OK) st = pool_grow(&e->nx_g, &e->nx_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->rk_g, &e->rk_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->ovf, &e->ovf_cap, sc, false);
+    const uint32_t l = enc_wc_log2(e, n);
+    if (l) {
+        const size_t slots = size_t(1) << l;
+        if (st == BPE_OK) st = pool_grow(&e->wc_key, &e->wc_key_cap, slots, false);
+        if (st == BPE_OK) st = pool_grow(&e->wc_pos, &e->wc_pos_cap, slots, false);
+        if (st == BPE_OK) st = pool_grow(&e->wc_list, &e->wc_list_cap, slots, false);
+        if (st == BPE_OK) st = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, false);
+    }
     return st;
 }
 
@@ -1202,17 +1231,30 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
     uint32_t* ovf_n = ovf_pos + npad;
     uint32_t* pfx = ovf_n + npad;
     const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes, e->rt_bytes};
+    const uint32_t l = enc_wc_log2(e, n);
+    bpek::WordCache wc{};
     hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
+    if (l) {
+        const uint32_t slots = 1u << l;
+        wc = bpek::WordCache{e->wc_key, e->wc_pos, e->wc_list, e->wc_rec, e->status + 3, slots - 1, slots / 2,
+                             e->wc_key_bits ? ~0ull << (64 - e->wc_key_bits) : 0ull};
+        hipLaunchKernelGGL(bpek::k_wc_clear, dim3(std::min<uint32_t>((slots + 255) / 256, e->clear_grid)), dim3(256),
+                           0, s, wc, slots);
+        hipLaunchKernelGGL(bpek::k_wc_insert<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->insert_grid)),
+                           dim3(ENC_TPB), 0, s, src, n, ntiles, wc);
+        hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>, dim3(e->fill_grid), dim3(WC_FILL_TPB), 0, s, src, wc, rt);
+    }
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     hipLaunchKernelGGL(bpek::k_enc_walk<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->walk_grid)), dim3(ENC_TPB), 0,
                        s, src, n, rt, e->slices, cnt, ovf_pos, ovf_n, ntiles, e->sym_g, e->nx_g, e->rk_g, e->ovf,
-                       e->status + 2, uint32_t(enc_scratch_cap(n)), e->status + 1);
-    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+                       e->status + 2, uint32_t(enc_scratch_cap(n)), e->status + 1, wc);
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     hipLaunchKernelGGL(bpek::k_trie_scan<TRIE_SCAN_TPB>, dim3(1), dim3(TRIE_SCAN_TPB), 0, s, cnt, ovf_n, pfx,
                        ntiles, npad, e->status);
-    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     hipLaunchKernelGGL(bpek::k_enc_copy<TRIE_COPY_TPB>, dim3(std::min<uint32_t>(ntiles, e->copy_grid)),
                        dim3(TRIE_COPY_TPB), 0, s, e->slices, cnt, ovf_pos, ovf_n, pfx, e->ovf, dst, ntiles, ENC_CAP);
-    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
     HIP_TRY(hipGetLastError());
     return BPE_OK;
 }
@@ -1272,16 +1314,23 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
         bpe_encoder_free(e);
         return st;
     };
-    int cus = 0, per_cu = 0;
+    int cus = 0, per_cu = 0, per_cu_ins = 0, per_cu_fill = 0;
     if (hipGetDevice(&e->device) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_enc_walk<ENC_TPB>, ENC_TPB, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_ins, bpek::k_wc_insert<ENC_TPB>, ENC_TPB, 0) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fill, bpek::k_wc_fill<WC_FILL_TPB>, WC_FILL_TPB, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0 || per_cu_ins <= 0 || per_cu_fill <= 0) {
         (void)hipGetLastError();
         set_err("cannot query the device");
         return fail(BPE_EHIP);
     }
     e->walk_grid = cus * per_cu;
+    e->insert_grid = cus * per_cu_ins;
+    e->fill_grid = cus * per_cu_fill;
+    e->clear_grid = cus * 8;
     e->copy_grid = cus * 8;
     e->rt_mask = uint32_t(slots - 1);
     e->rt_probes = probes;
@@ -1367,12 +1416,12 @@ bpe_status bpe_encoder_profile(bpe_encoder* e, const uint8_t* bytes, size_t n, u
     bpe_status st = bpe_encoder_encode(e, bytes, n, nullptr, nullptr, 0, &first);
     if (st != BPE_OK) return st;
     std::vector<hipEvent_t>* ev = nullptr;
-    st = event_pool(e->device, 3 * size_t(reps) + 1, &ev);
+    st = event_pool(e->device, 4 * size_t(reps) + 1, &ev);
     if (st != BPE_OK) return st;
     std::vector<hipEvent_t>& evs = *ev;
     HIP_TRY(hipEventRecord(evs[0], e->stream));
     for (uint32_t r = 0; r < reps; ++r) {
-        st = enc_enqueue(e, bytes, uint32_t(n), e->tok_buf, e->stream, &evs[3 * size_t(r) + 1]);
+        st = enc_enqueue(e, bytes, uint32_t(n), e->tok_buf, e->stream, &evs[4 * size_t(r) + 1]);
         if (st != BPE_OK) return st;
     }
     uint32_t h[4] = {0, 0, 0, 0};
@@ -1382,7 +1431,7 @@ bpe_status bpe_encoder_profile(bpe_encoder* e, const uint8_t* bytes, size_t n, u
         set_err("repeated runs disagree (%u tokens vs %zu, error flags %u)", h[0], first, h[1]);
         return BPE_ESTATE;
     }
-    for (size_t i = 0; i < 3 * size_t(reps); ++i) {
+    for (size_t i = 0; i < 4 * size_t(reps); ++i) {
         float a = 0.f;
         HIP_TRY(hipEventElapsedTime(&a, evs[i], evs[i + 1]));
         if (ms) ms[i] = a;
@@ -1391,12 +1440,26 @@ bpe_status bpe_encoder_profile(bpe_encoder* e, const uint8_t* bytes, size_t n, u
     return BPE_OK;
 }
 
+bpe_status bpe_encoder_cache(bpe_encoder* e, uint32_t log2_slots, uint32_t key_bits) {
+    g_err.clear();
+    if (!e || !(log2_slots == BPE_CACHE_AUTO || log2_slots == 0 || (log2_slots >= 8 && log2_slots <= 24)) ||
+        key_bits > BPE_CACHE_KEY_BITS) {
+        set_err("encoder must be non-NULL, log2_slots BPE_CACHE_AUTO, 0 or 8..24, key_bits at most %u",
+                BPE_CACHE_KEY_BITS);
+        return BPE_EINVAL;
+    }
+    e->wc_log2 = log2_slots;
+    e->wc_key_bits = key_bits;
+    return BPE_OK;
+}
+
 void bpe_encoder_free(bpe_encoder* e) {
     if (!e) return;
     (void)hipSetDevice(e->device);
     if (e->stream) (void)hipStreamSynchronize(e->stream);
     for (void* p : {(void*)e->rt, (void*)e->rt_bytes, (void*)e->status, (void*)e->slices, (void*)e->tiles, (void*)e->sym_g,
-                    (void*)e->nx_g, (void*)e->rk_g, (void*)e->ovf, (void*)e->text_buf, (void*)e->tok_buf})
+                    (void*)e->nx_g, (void*)e->rk_g, (void*)e->ovf, (void*)e->text_buf, (void*)e->tok_buf,
+                    (void*)e->wc_key, (void*)e->wc_pos, (void*)e->wc_list, (void*)e->wc_rec})
         if (p) (void)hipFree(p);
     if (e->stream) (void)hipStreamDestroy(e->stream);
     delete e;

@@ -151,6 +151,288 @@ __device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* 
     return c;
 }
 
+// ---------------------------------------------------------------- word cache
+// A word's encoding depends on its bytes alone, and a text repeats few
+// distinct words many times, so each distinct word can be encoded once: the
+// insert pass puts every word of 2 .. WC_MAXLEN bytes into a hash table
+// (first claim of a slot wins and lists it), the fill pass encodes each
+// listed word into its slot's record, and the walk takes a word's tokens
+// from its record after comparing the bytes. A word that finds no record
+// (table at its claim limit, probes used up, or a key shared with another
+// word) is encoded by the walk itself, so the table never decides a token.
+constexpr uint32_t WC_MAXLEN = 32;   // longest cached word
+constexpr uint32_t WC_REC = 32;      // u32 per record (128 bytes)
+constexpr uint32_t WC_TOK = 8;       // record: bytes [0, 8), token ids [8, 24) (two per u32), token starts [24]
+constexpr uint32_t WC_MASKW = 24;
+constexpr uint32_t WC_PROBES = 32;
+
+struct WordCache {
+    unsigned long long* key;   // per slot: 0 = free, else hash bits | length (a slot changes once)
+    uint32_t* pos;             // per slot: text position of one occurrence of its word
+    uint32_t* list;            // claimed slots, in claim order
+    uint32_t* rec;             // WC_REC words per slot
+    uint32_t* n_list;          // claims so far
+    uint32_t mask;             // slots - 1
+    uint32_t limit;            // no new claims at or past this count
+    unsigned long long kmask;  // hash bits kept in a key (fewer bits, more words sharing a key)
+};
+
+// Bytes s[a, a + len), len <= WC_MAXLEN, little-endian in w[0..7], zero
+// past len. s is 4-byte aligned; reads at most 36 bytes from s + (a & ~3).
+__device__ __forceinline__ void wc_pack_lds(const uint8_t* s, uint32_t a, uint32_t len, uint32_t (&w)[8]) {
+    const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s);
+    const uint32_t b = a >> 2, r = a & 3u;
+    uint32_t lo = s32[b];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint32_t v = 0u;
+        if (4u * (uint32_t)k < len) {
+            const uint32_t hi = s32[b + (uint32_t)k + 1u];
+            v = __builtin_amdgcn_alignbyte(hi, lo, r);
+            lo = hi;
+            const uint32_t rem = len - 4u * (uint32_t)k;
+            if (rem < 4u) v &= (1u << (8u * rem)) - 1u;
+        }
+        w[k] = v;
+    }
+}
+
+// 64-bit hash of a packed word: a multiply-xorshift step per 4 bytes, then
+// the SplitMix64 finaliser (Steele, Lea and Flood, 2014).
+__device__ __forceinline__ unsigned long long wc_hash(const uint32_t (&w)[8], uint32_t len) {
+    unsigned long long h = 0x9E3779B97F4A7C15ull * (unsigned long long)(len + 1u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (4u * (uint32_t)k < len) {
+            h ^= w[k];
+            h *= 0xBF58476D1CE4E5B9ull;
+            h ^= h >> 31;
+        }
+    }
+    h ^= h >> 30;
+    h *= 0xBF58476D1CE4E5B9ull;
+    h ^= h >> 27;
+    h *= 0x94D049BB133111EBull;
+    h ^= h >> 31;
+    return h;
+}
+
+__device__ __forceinline__ unsigned long long wc_key(const WordCache& wc, unsigned long long h, uint32_t len) {
+    return (h & wc.kmask & ~63ull) | len;  // len >= 2: never 0
+}
+__device__ __forceinline__ uint32_t wc_slot(const WordCache& wc, unsigned long long h) {
+    return (uint32_t)(h >> 32) & wc.mask;
+}
+
+// Linear probing from slot: stop at the key (someone claimed the word, or
+// a word with the same key) or claim a free slot, list it and record pos.
+// Plain loads see a slot either free (then the CAS decides) or final.
+__device__ __forceinline__ void wc_insert(const WordCache& wc, unsigned long long key, uint32_t slot, uint32_t pos) {
+    for (uint32_t p = 0; p < WC_PROBES; ++p) {
+        unsigned long long v = wc.key[slot];
+        if (v == 0ull) {
+            if (ld_relaxed(wc.n_list) >= wc.limit) return;
+            v = atomicCAS(wc.key + slot, 0ull, key);
+            if (v == 0ull) {
+                wc.pos[slot] = pos;
+                wc.list[atomicAdd(wc.n_list, 1u)] = slot;
+                return;
+            }
+        }
+        if (v == key) return;
+        slot = (slot + 1u) & wc.mask;
+    }
+}
+
+// The record of the packed word w (key, probing from slot), into r; false
+// if no slot on its probe path holds these bytes. Each probe loads the
+// slot's key and record together.
+__device__ __forceinline__ bool wc_lookup(const WordCache& wc, unsigned long long key, uint32_t slot,
+                                          const uint32_t (&w)[8], uint32_t (&r)[WC_MASKW + 1]) {
+    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    for (uint32_t p = 0; p < WC_PROBES; ++p) {
+        const unsigned long long v = wc.key[slot];
+        const uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
+#pragma unroll
+        for (int k = 0; k < (int)WC_MASKW / 4; ++k) {
+            const v4 x = *reinterpret_cast<const v4*>(rp + 4 * k);
+            r[4 * k] = x.x;
+            r[4 * k + 1] = x.y;
+            r[4 * k + 2] = x.z;
+            r[4 * k + 3] = x.w;
+        }
+        r[WC_MASKW] = rp[WC_MASKW];
+        if (v == key) {
+            uint32_t d = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) d |= w[k] ^ r[k];
+            if (d == 0u) return true;
+        } else if (v == 0ull) {
+            return false;
+        }
+        slot = (slot + 1u) & wc.mask;
+    }
+    return false;
+}
+
+// Free every slot and the claim count (before the insert pass).
+__global__ void k_wc_clear(WordCache wc, uint32_t slots) {
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gridDim.x * blockDim.x) wc.key[i] = 0ull;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *wc.n_list = 0u;
+}
+
+// Fill pass: every listed word, one per thread, encoded in the thread's
+// LDS range of WC_MAXLEN positions; the record gets the word's bytes (zero
+// past its length), its token ids and the offsets where its tokens start.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ text, WordCache wc, RankTable rt) {
+    __shared__ uint16_t s_sym[TPB * WC_MAXLEN], s_nx[TPB * WC_MAXLEN], s_rk[TPB * WC_MAXLEN];
+    const LdsWord lw{s_sym, s_nx, s_rk};
+    const uint32_t nl = ld_relaxed(wc.n_list);
+    const uint32_t b = threadIdx.x * WC_MAXLEN;
+    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < nl; i += gridDim.x * TPB) {
+        const uint32_t slot = wc.list[i];
+        const uint32_t len = (uint32_t)(wc.key[slot] & 63ull);
+        const uint8_t* src = text + wc.pos[slot];
+        uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t v = 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t j = 4u * (uint32_t)k + (uint32_t)u;
+                if (j < len) v |= (uint32_t)src[j] << (8 * u);
+            }
+            rp[k] = v;
+        }
+        for (uint32_t j = 0; j < len; ++j) {
+            s_sym[b + j] = src[j];
+            s_nx[b + j] = (uint16_t)(b + j + 1u);
+        }
+        for (uint32_t j = 0; j + 1u < len; ++j)
+            s_rk[b + j] = rt.bytes[((uint32_t)s_sym[b + j] << 8) | s_sym[b + j + 1u]];
+        while (!merge_iteration(lw, b, b + len, rt)) {
+        }
+        uint16_t* tp = reinterpret_cast<uint16_t*>(rp + WC_TOK);
+        uint32_t m = 0u, c = 0u;
+        for (uint32_t x = b; x < b + len; x = s_nx[x]) {
+            m |= 1u << (x - b);
+            tp[c++] = s_sym[x];
+        }
+        rp[WC_MASKW] = m;
+    }
+}
+
+// The text of tile t in LDS (s_txt[p + 16 + mis] = text[t0 + p], TILE bytes
+// and the halo), the word starts inside the tile in s_sb, and *s_after,
+// the first class change in the halo (CAP if none). Returns this thread's
+// starts (bit k: position 16 tid + k) of words of two bytes or more and, in
+// *single, those of one-byte words. The caller clears *s_after to CAP
+// before; this clears s_sb and ends with the starts recorded.
+template <int TPB, uint32_t TILE, uint32_t CAP, uint32_t NCH>
+__device__ __forceinline__ uint32_t tile_words(__amdgpu_buffer_rsrc_t rs, uint32_t t0, uint32_t nrel, uint32_t sh,
+                                               uint8_t* s_txt, uint32_t* s_sb, uint32_t* s_after, uint32_t* single) {
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
+    for (uint32_t k = tid; k < NCH; k += TPB) {
+        typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+        const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
+        *reinterpret_cast<v4*>(s_txt + 16u * k) = v;
+    }
+    __syncthreads();
+    uint32_t multi;
+    {
+        const uint32_t p0 = 16u * tid;
+        uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+        uint32_t starts = 0, bnd = 0;
+#pragma unroll
+        for (int k = 0; k <= 16; ++k) {
+            const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+            const bool inside = p0 + k < nrel;
+            const bool change = c != pc || t0 + p0 + k == 0u;
+            if (k < 16) starts |= ((inside && change) ? 1u : 0u) << k;
+            if (k >= 1) bnd |= ((!inside || change) ? 1u : 0u) << k;
+            pc = c;
+        }
+        *single = starts & (bnd >> 1);
+        multi = starts & ~*single;
+        if (starts) atomicOr(&s_sb[p0 >> 5], starts << (p0 & 31u));
+    }
+    {
+        uint32_t after = CAP;
+        const uint32_t p0 = TILE + TRIE_HALO_PER_THREAD * tid;
+        uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
+#pragma unroll
+        for (int k = 0; k < (int)TRIE_HALO_PER_THREAD; ++k) {
+            const uint32_t c = byte_class(s_txt[p0 + k + sh]);
+            if (p0 + k < nrel && c != pc && after == CAP) after = p0 + k;
+            pc = c;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) after = min(after, (uint32_t)__shfl_xor(after, o));
+        if ((tid & 63u) == 0u) atomicMin(s_after, after);
+    }
+    return multi;
+}
+
+// End of the word starting at q (< TILE): the next start in the tile, else
+// last_end.
+template <uint32_t TILE>
+__device__ __forceinline__ uint32_t word_end(const uint32_t* s_sb, uint32_t q, uint32_t last_end) {
+    for (uint32_t x = q + 1u; x < TILE;) {
+        const uint32_t m = s_sb[x >> 5] & (0xFFFFFFFFu << (x & 31u));
+        if (m) return (x & ~31u) + (__ffs(m) - 1);
+        x = (x & ~31u) + 32u;
+    }
+    return last_end;
+}
+
+// Insert pass: the walk's tiles, every word of 2 .. WC_MAXLEN bytes
+// starting in a tile put into the cache.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ text, uint32_t n, uint32_t ntiles,
+                                                   WordCache wc) {
+    constexpr uint32_t TILE = TPB * 16u;
+    constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
+    constexpr uint32_t CAP = TILE + HALO;
+    constexpr uint32_t NCH = (CAP + 32u) / 16u;
+    static_assert(HALO > WC_MAXLEN, "a cached word ends inside the copy");
+    __shared__ __align__(16) uint8_t s_txt[NCH * 16u];
+    __shared__ uint32_t s_sb[TILE / 32u];
+    __shared__ uint16_t s_list[TILE];
+    __shared__ uint32_t s_w[TPB / 64];
+    __shared__ uint32_t s_after;
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t mis = (uint32_t)((uintptr_t)text & 15u);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
+    const uint32_t sh = 16u + mis;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        if (tid == 0) s_after = CAP;
+        const uint32_t t0 = t * TILE;
+        const uint32_t nrel = n - t0;
+        uint32_t single;
+        const uint32_t multi = tile_words<TPB, TILE, CAP, NCH>(rs, t0, nrel, sh, s_txt, s_sb, &s_after, &single);
+        uint32_t nwords;
+        uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
+        for (uint32_t m = multi; m; m &= m - 1u) s_list[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
+        lds_barrier();
+        const uint32_t lim = nrel < CAP ? nrel : CAP;
+        const uint32_t last_end = s_after < lim ? s_after : lim;
+        for (uint32_t i = tid; i < nwords; i += TPB) {
+            const uint32_t q = s_list[i];
+            const uint32_t len = word_end<TILE>(s_sb, q, last_end) - q;
+            if (len > WC_MAXLEN) continue;  // also a word running past the copy (its length here >= HALO)
+            uint32_t w[8];
+            wc_pack_lds(s_txt, q + sh, len, w);
+            const unsigned long long h = wc_hash(w, len);
+            wc_insert(wc, wc_key(wc, h, len), wc_slot(wc, h), t0 + q);
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- pass 1
 // Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x, ...
 // Outputs for tile t: tok32[t * CAP + i], i < cnt[t], the tokens of the
@@ -165,7 +447,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                                                   uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
                                                   uint32_t ntiles, uint16_t* sym_g, uint32_t* nx_g, uint16_t* rk_g,
                                                   uint32_t* ovf, uint32_t* scratch_used, uint32_t scratch_cap,
-                                                  uint32_t* err) {
+                                                  uint32_t* err, WordCache wc) {
     constexpr uint32_t TILE = TPB * 16u;
     constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
     constexpr uint32_t CAP = TILE + HALO;
@@ -187,6 +469,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
     const LdsWord lw{s_sym, s_nx, s_rk};
+    const uint32_t sh = 16u + mis;
 
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         if (tid == 0) {
@@ -195,59 +478,23 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
             s_after = CAP;
         }
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
-        for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
-        for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_ws[i] = 0u;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
-        for (uint32_t k = tid; k < NCH; k += TPB) {
-            typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-            const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
-            *reinterpret_cast<v4*>(s_txt + 16u * k) = v;
-        }
-        __syncthreads();
-        const uint32_t sh = 16u + mis;
         auto lbyte = [&](uint32_t q) -> uint32_t { return s_txt[q + sh]; };  // q < CAP
 
         // word starts: one-byte words are final here, the others listed
-        uint32_t multi;
-        {
+        uint32_t single;
+        const uint32_t multi = tile_words<TPB, TILE, CAP, NCH>(rs, t0, nrel, sh, s_txt, s_sb, &s_after, &single);
+        // s_ws is read by the previous tile's last loop: cleared only past
+        // the barrier in tile_words
+        for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_ws[i] = 0u;
+        if (single) {
             const uint32_t p0 = 16u * tid;
-            uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
-            uint32_t starts = 0, bnd = 0;
-#pragma unroll
-            for (int k = 0; k <= 16; ++k) {
-                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
-                const bool inside = p0 + k < nrel;
-                const bool change = c != pc || t0 + p0 + k == 0u;
-                if (k < 16) starts |= ((inside && change) ? 1u : 0u) << k;
-                if (k >= 1) bnd |= ((!inside || change) ? 1u : 0u) << k;
-                pc = c;
+            atomicOr(&s_flag[p0 >> 5], single << (p0 & 31u));
+            for (uint32_t m = single; m; m &= m - 1u) {
+                const uint32_t k = __ffs(m) - 1;
+                s_sym[p0 + k] = (uint16_t)lbyte(p0 + k);
             }
-            const uint32_t single = starts & (bnd >> 1);
-            multi = starts & ~single;
-            const uint32_t sb = p0 & 31u;
-            if (starts) atomicOr(&s_sb[p0 >> 5], starts << sb);
-            if (single) {
-                atomicOr(&s_flag[p0 >> 5], single << sb);
-                for (uint32_t m = single; m; m &= m - 1u) {
-                    const uint32_t k = __ffs(m) - 1;
-                    s_sym[p0 + k] = (uint16_t)lbyte(p0 + k);
-                }
-            }
-        }
-        {
-            uint32_t after = CAP;
-            const uint32_t p0 = TILE + TRIE_HALO_PER_THREAD * tid;
-            uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
-#pragma unroll
-            for (int k = 0; k < (int)TRIE_HALO_PER_THREAD; ++k) {
-                const uint32_t c = byte_class(s_txt[p0 + k + sh]);
-                if (p0 + k < nrel && c != pc && after == CAP) after = p0 + k;
-                pc = c;
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) after = min(after, (uint32_t)__shfl_xor(after, o));
-            if ((tid & 63u) == 0u) atomicMin(&s_after, after);
         }
         uint32_t nwords;
         uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
@@ -274,18 +521,36 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)need, 0u));
                     if (!act && next + below < w_hi) {
                         q = s_aux[next + below];
-                        wend = last_end;
-                        for (uint32_t x = q + 1u; x < TILE;) {
-                            const uint32_t m = s_sb[x >> 5] & (0xFFFFFFFFu << (x & 31u));
-                            if (m) {
-                                wend = (x & ~31u) + (__ffs(m) - 1);
-                                break;
+                        wend = word_end<TILE>(s_sb, q, last_end);
+                        bool cached = false;
+                        if (wc.key && wend - q <= WC_MAXLEN) {
+                            // a cached word: its tokens from the record
+                            const uint32_t len = wend - q;
+                            uint32_t w[8], r[WC_MASKW + 1];
+                            wc_pack_lds(s_txt, q + sh, len, w);
+                            const unsigned long long h = wc_hash(w, len);
+                            if (wc_lookup(wc, wc_key(wc, h, len), wc_slot(wc, h), w, r)) {
+                                uint32_t m = r[WC_MASKW];
+                                const uint32_t o = q & 31u;
+                                atomicOr(&s_flag[q >> 5], m << o);
+                                if (o && (m >> (32u - o))) atomicOr(&s_flag[(q >> 5) + 1u], m >> (32u - o));
+#pragma unroll
+                                for (int k = 0; k < (int)WC_MAXLEN / 2; ++k) {
+                                    const uint32_t two = r[WC_TOK + k];
+#pragma unroll
+                                    for (int u = 0; u < 2; ++u) {
+                                        if (m) {
+                                            s_sym[q + __ffs(m) - 1] = (uint16_t)(two >> (16 * u));
+                                            m &= m - 1u;
+                                        }
+                                    }
+                                }
+                                cached = true;
                             }
-                            x = (x & ~31u) + 32u;
                         }
-                        if (last_open && wend == last_end) {
+                        if (!cached && last_open && wend == last_end) {
                             gq = q;  // runs past the copy: encoded from global memory below
-                        } else {
+                        } else if (!cached) {
                             for (uint32_t i = q; i < wend; ++i) {
                                 s_sym[i] = (uint16_t)lbyte(i);
                                 s_nx[i] = (uint16_t)(i + 1u);
@@ -307,7 +572,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                     }
                     next += (uint32_t)__popcll(need);
                 }
-                if (__ballot(act) == 0ull) break;
+                if (__ballot(act) == 0ull && next >= w_hi) break;
                 if (act && merge_iteration(lw, q, wend, rt)) {
                     for (uint32_t i = q; i < wend; i = s_nx[i]) atomicOr(&s_flag[i >> 5], 1u << (i & 31u));
                     act = false;

@@ -184,11 +184,13 @@ bpe_status bpe_encoder_build(const bpe_merge *merges, uint32_t n_merges, bpe_enc
 /* Encode bytes[0..n) (host or device) on stream (a hipStream_t, or NULL for
    the encoder's own). tokens (host or device, capacity tokens_cap >= n, or
    NULL for the count only) receive the tokens, *n_tokens their count.
-   Three kernels (walk, scan, copy), a wait for the total and a sized copy
-   for host tokens. Device buffers are pooled in the encoder (about 6 bytes
-   per input byte, plus scratch of 12 bytes per position for words that do
-   not fit a tile's LDS, at most 2^24 positions per call), so calls on one
-   encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
+   With the word cache (bpe_encoder_cache; off by default) three kernels
+   first collect the distinct words of 2..32 bytes and encode each once;
+   then three kernels (walk, scan, copy), a wait for the total and a sized
+   copy for host tokens. Device buffers are pooled in the encoder (about 6
+   bytes per input byte, the cache's 144 bytes per slot, plus scratch of 12
+   bytes per position for words that do not fit a tile's LDS, at most 2^24
+   positions per call), so calls on one encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
    NULL bytes with n > 0, n > BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM
    (also: words past a tile's LDS longer than the scratch in total),
    BPE_EHIP. */
@@ -196,11 +198,26 @@ bpe_status bpe_encoder_encode(bpe_encoder *e, const uint8_t *bytes, size_t n, vo
                               size_t tokens_cap, size_t *n_tokens);
 
 /* Time the encoder's kernels: bpe_encoder_encode of device bytes once, then
-   reps runs back to back on the encoder's stream with a HIP event after
-   each kernel; ms (3 * reps entries, or NULL): walk (with its small init
-   kernel), scan and copy times of each run. */
+   reps runs back to back on the encoder's stream with HIP events between
+   the stages; ms (4 * reps entries, or NULL): the word cache's three
+   kernels (with the small init kernel), walk, scan and copy times of each
+   run. */
 bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, uint32_t reps, float *ms,
                                size_t *n_tokens);
+
+/* Size of the encoder's word cache for later calls. Every occurrence of a
+   word encodes alike, so each distinct word of 2..32 bytes is encoded once
+   per call into a hash table (linear probing over 2^log2_slots slots,
+   claims stop at half of them) and its occurrences copy the result after
+   comparing their bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
+   (one slot per 128 input bytes, 2^10..2^22), 0 (no cache) or 8..24.
+   key_bits (at most BPE_CACHE_KEY_BITS): hash bits in a slot's key; fewer
+   bits make distinct words share keys, which only sends more words down
+   the uncached path (a testing aid). Tokens never depend on either
+   setting. A new encoder has no cache (log2_slots 0). Errors: BPE_EINVAL. */
+#define BPE_CACHE_AUTO 0xFFFFFFFFu
+#define BPE_CACHE_KEY_BITS 58u
+bpe_status bpe_encoder_cache(bpe_encoder *e, uint32_t log2_slots, uint32_t key_bits);
 
 /* Release the encoder and its buffers. NULL is a no-op. */
 void bpe_encoder_free(bpe_encoder *e);

@@ -40,6 +40,22 @@ def test_encoding_the_training_corpus_gives_training_tokens(bpe):
     assert np.array_equal(_np(tokens).astype(np.uint32), ot)
 
 
+@pytest.mark.parametrize("c", [3, 5])
+def test_encoding_a_large_training_corpus_gives_training_tokens(bpe, c):
+    # many tiles per workgroup: LDS reuse from one tile to the next (the
+    # staged word-start bits of a tile were once cleared by the next tile
+    # while its output was still being written)
+    spec = corpus.CONFIGS[c].scaled(48 << 20, n_merges=600, seed=77)
+    d = _dev(corpus.generate(spec))
+    _say("encode large training corpus c=%d" % c)
+    gm, gt = bpe.train(d, spec.n_merges, 22)
+    with bpe.Encoder(gm) as e:
+        for slots in (0, 0xFFFFFFFF):
+            e.cache(slots)
+            got = e.encode(d)
+            assert got.shape == gt.shape and bool((got == gt).all()), (c, slots)
+
+
 @pytest.mark.parametrize("c", [1, 2, 4, 5])
 @pytest.mark.parametrize("n", [1, 3, 8191, 8193, 70_001])
 def test_encode_new_text_matches_oracle(bpe, c, n):
@@ -140,3 +156,61 @@ def test_encoder_host_input_and_output_through_the_abi(bpe):
         assert st == 0 and np.array_equal(out[: n_tok.value], ot)
         st = bpe._lib.bpe_encoder_encode(e._h, text.ctypes.data, text.size, None, None, 0, ctypes.byref(n_tok))
         assert st == 0 and n_tok.value == ot.size
+
+
+# word cache: (log2 slots, key bits). 8 slots-log2 stops claims at 128
+# words, so most words take the uncached path; 0 key bits give every word
+# of one length the same key, 4 bits nearly so (probing past keys whose
+# bytes differ); 0 slots turn the cache off.
+CACHE_SETTINGS = [(0xFFFFFFFF, 58), (0, 58), (8, 58), (10, 0), (12, 4), (16, 58)]
+
+
+@pytest.mark.parametrize("c", [2, 3, 5])
+def test_word_cache_settings_do_not_change_tokens(bpe, c):
+    learn = corpus.generate(corpus.CONFIGS[c].scaled(200_000, seed=900 + c))
+    om, _, _ = oracle.train_chunks(learn, 400)
+    text = corpus.generate(corpus.CONFIGS[c].scaled(300_001, seed=910 + c))
+    _, ot = oracle.encode(text, om)
+    d = _dev(text)
+    with bpe.Encoder(om) as e:
+        for slots, bits in CACHE_SETTINGS:
+            _say("word cache c=%d slots=%d bits=%d" % (c, slots, bits))
+            e.cache(slots, bits)
+            got = _np(e.encode(d)).astype(np.uint32)
+            assert np.array_equal(got, ot), (c, slots, bits)
+
+
+def test_word_cache_lengths_and_alignments(bpe):
+    # words of 2..40 letters (the cache takes 2..32) at every offset modulo
+    # 32 of a tile, some across tile edges, with merges that make tokens of
+    # several lengths inside them
+    rng = np.random.default_rng(5)
+    words = [bytes(rng.choice(list(b"abcd"), size=L).tolist()) for L in range(2, 41) for _ in range(3)]
+    parts = []
+    for i in range(4000):
+        w = words[rng.integers(len(words))]
+        parts.append(w)
+        parts.append(b" " * int(rng.integers(1, 4)))
+        if i % 97 == 0:
+            parts.append(b"7" * int(rng.integers(1, 40)))
+    text = np.frombuffer(b"".join(parts), np.uint8)
+    om, _, _ = oracle.train_chunks(text, 120)
+    with bpe.Encoder(om) as e:
+        for shift in (0, 1, 13, 31):
+            tt = np.concatenate([np.full(shift, 32, np.uint8), text])
+            _, ot = oracle.encode(tt, om)
+            d = _dev(tt)
+            for slots, bits in CACHE_SETTINGS:
+                _say("word cache lengths shift=%d slots=%d bits=%d" % (shift, slots, bits))
+                e.cache(slots, bits)
+                assert np.array_equal(_np(e.encode(d)).astype(np.uint32), ot), (shift, slots, bits)
+
+
+def test_word_cache_rejects_bad_settings(bpe):
+    with bpe.Encoder([(97, 98)]) as e:
+        for slots, bits in ((7, 58), (25, 58), (16, 59)):
+            with pytest.raises(bpe.BpeError):
+                e.cache(slots, bits)
+        e.cache(8, 0)
+        text = np.frombuffer(b"ab abab ba " * 100, np.uint8)
+        assert np.array_equal(_np(e.encode(_dev(text))).astype(np.uint32), oracle.encode(text, [(97, 98)])[1])

@@ -143,4 +143,4 @@ def test_profile_calls_agree_with_encode(bpe, vocabs):
     with bpe.Encoder(m) as e:
         n_tok, ms = e.profile(d, 3)
         assert n_tok == oracle.encode(text, m)[1].size
-        assert ms.shape == (3, 3) and (ms > 0).all()
+        assert ms.shape == (3, 4) and (ms > 0).all()
