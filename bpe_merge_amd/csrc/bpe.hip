@@ -1169,16 +1169,14 @@ struct bpe_encoder {
     size_t text_cap = 0;
     uint32_t* tok_buf = nullptr;
     size_t tok_cap = 0;
-    // word cache: keys, positions and the claim list per slot, records
+    // word cache: key, position and record per slot
     unsigned long long* wc_key = nullptr;
     size_t wc_key_cap = 0;
     uint32_t* wc_pos = nullptr;
     size_t wc_pos_cap = 0;
-    uint32_t* wc_list = nullptr;
-    size_t wc_list_cap = 0;
     uint32_t* wc_rec = nullptr;
     size_t wc_rec_cap = 0;
-    uint32_t wc_log2 = 0, wc_key_bits = BPE_CACHE_KEY_BITS;  // no word cache until asked for
+    uint32_t wc_log2 = BPE_CACHE_AUTO, wc_key_bits = BPE_CACHE_KEY_BITS;
     int walk_grid = 0, copy_grid = 0, insert_grid = 0, fill_grid = 0, clear_grid = 0;
 };
 
@@ -1194,11 +1192,11 @@ constexpr size_t ENC_SCRATCH_MAX = size_t(1) << 24;  // positions of long words 
 size_t enc_scratch_cap(size_t n) { return std::min(n, ENC_SCRATCH_MAX); }
 
 // Slots of the word cache for n bytes (0: no cache). Automatic: one slot
-// per 128 input bytes, a power of two in [2^10, 2^22]; claims stop at half.
+// per 256 input bytes, a power of two in [2^10, 2^22].
 uint32_t enc_wc_log2(const bpe_encoder* e, size_t n) {
     if (e->wc_log2 != BPE_CACHE_AUTO) return e->wc_log2;
     uint32_t l = 10;
-    while (l < WC_AUTO_MAX_LOG2 && (size_t(1) << l) < n / 128) ++l;
+    while (l < WC_AUTO_MAX_LOG2 && (size_t(1) << l) < n / 256) ++l;
     return l;
 }
 
@@ -1216,7 +1214,6 @@ bpe_status enc_pools(bpe_encoder* e, size_t n) {
         const size_t slots = size_t(1) << l;
         if (st == BPE_OK) st = pool_grow(&e->wc_key, &e->wc_key_cap, slots, false);
         if (st == BPE_OK) st = pool_grow(&e->wc_pos, &e->wc_pos_cap, slots, false);
-        if (st == BPE_OK) st = pool_grow(&e->wc_list, &e->wc_list_cap, slots, false);
         if (st == BPE_OK) st = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, false);
     }
     return st;
@@ -1236,13 +1233,15 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
     hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
     if (l) {
         const uint32_t slots = 1u << l;
-        wc = bpek::WordCache{e->wc_key, e->wc_pos, e->wc_list, e->wc_rec, e->status + 3, slots - 1, slots / 2,
+        wc = bpek::WordCache{e->wc_key, e->wc_pos, e->wc_rec, slots - 1,
                              e->wc_key_bits ? ~0ull << (64 - e->wc_key_bits) : 0ull};
         hipLaunchKernelGGL(bpek::k_wc_clear, dim3(std::min<uint32_t>((slots + 255) / 256, e->clear_grid)), dim3(256),
                            0, s, wc, slots);
         hipLaunchKernelGGL(bpek::k_wc_insert<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->insert_grid)),
                            dim3(ENC_TPB), 0, s, src, n, ntiles, wc);
-        hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>, dim3(e->fill_grid), dim3(WC_FILL_TPB), 0, s, src, wc, rt);
+        hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>, dim3(std::min<uint32_t>((slots + WC_FILL_TPB - 1) / WC_FILL_TPB,
+                                                                                  e->fill_grid)),
+                           dim3(WC_FILL_TPB), 0, s, src, n, wc, rt, slots);
     }
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     hipLaunchKernelGGL(bpek::k_enc_walk<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->walk_grid)), dim3(ENC_TPB), 0,
@@ -1459,7 +1458,7 @@ void bpe_encoder_free(bpe_encoder* e) {
     if (e->stream) (void)hipStreamSynchronize(e->stream);
     for (void* p : {(void*)e->rt, (void*)e->rt_bytes, (void*)e->status, (void*)e->slices, (void*)e->tiles, (void*)e->sym_g,
                     (void*)e->nx_g, (void*)e->rk_g, (void*)e->ovf, (void*)e->text_buf, (void*)e->tok_buf,
-                    (void*)e->wc_key, (void*)e->wc_pos, (void*)e->wc_list, (void*)e->wc_rec})
+                    (void*)e->wc_key, (void*)e->wc_pos, (void*)e->wc_rec})
         if (p) (void)hipFree(p);
     if (e->stream) (void)hipStreamDestroy(e->stream);
     delete e;

@@ -154,37 +154,49 @@ __device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* 
 // ---------------------------------------------------------------- word cache
 // A word's encoding depends on its bytes alone, and a text repeats few
 // distinct words many times, so each distinct word can be encoded once: the
-// insert pass puts every word of 2 .. WC_MAXLEN bytes into a hash table
-// (first claim of a slot wins and lists it), the fill pass encodes each
-// listed word into its slot's record, and the walk takes a word's tokens
-// from its record after comparing the bytes. A word that finds no record
-// (table at its claim limit, probes used up, or a key shared with another
-// word) is encoded by the walk itself, so the table never decides a token.
+// insert pass puts the words of 2 .. WC_MAXLEN bytes into a hash table, the
+// fill pass encodes the word of every used slot into the slot's record, and
+// the walk takes a word's tokens from a record holding the same bytes.
+//
+// A slot is claimed by a CAS on its key and the claimer stores a text
+// position of its word. Nothing else is shared: device-scope atomics on one
+// address serialise at memory (about 10 ns each), so a claim counter or a
+// list of claimed slots, touched by every new word, would cost more than
+// the rest of the pass; the fill pass scans all slots instead. A record is
+// built from the bytes it encodes (those at the slot's position, over the
+// key's length) and stores them, and the walk uses a record only when those
+// bytes and that length equal the word's own; a word that finds no such
+// record (probes used up, a different word under its key) is encoded by the
+// walk itself.
+// A record is 32 u32 in two halves of 64 bytes; the first serves words of
+// up to WC_SHORT bytes alone: bytes 0-15 [0, 4), token ids 0-15 [4, 12)
+// (two per u32), token starts [12] (bit k: a token starts at offset k),
+// length [13] (0: the slot's position did not hold that many bytes); the
+// second holds bytes 16-31 [16, 20) and token ids 16-31 [20, 28).
 constexpr uint32_t WC_MAXLEN = 32;   // longest cached word
+constexpr uint32_t WC_SHORT = 16;    // longest word served by the first half
 constexpr uint32_t WC_REC = 32;      // u32 per record (128 bytes)
-constexpr uint32_t WC_TOK = 8;       // record: bytes [0, 8), token ids [8, 24) (two per u32), token starts [24]
-constexpr uint32_t WC_MASKW = 24;
-constexpr uint32_t WC_PROBES = 32;
+constexpr uint32_t WC_HALF = 16;
+constexpr uint32_t WC_T0 = 4, WC_MASKW = 12, WC_LENW = 13, WC_B1 = 16, WC_T1 = 20;
+constexpr uint32_t WC_PROBES = 8;
 
 struct WordCache {
-    unsigned long long* key;   // per slot: 0 = free, else hash bits | length (a slot changes once)
-    uint32_t* pos;             // per slot: text position of one occurrence of its word
-    uint32_t* list;            // claimed slots, in claim order
+    unsigned long long* key;   // per slot: 0 = free, else hash bits | length
+    uint32_t* pos;             // per slot: a text position of a word with that key
     uint32_t* rec;             // WC_REC words per slot
-    uint32_t* n_list;          // claims so far
     uint32_t mask;             // slots - 1
-    uint32_t limit;            // no new claims at or past this count
     unsigned long long kmask;  // hash bits kept in a key (fewer bits, more words sharing a key)
 };
 
-// Bytes s[a, a + len), len <= WC_MAXLEN, little-endian in w[0..7], zero
-// past len. s is 4-byte aligned; reads at most 36 bytes from s + (a & ~3).
-__device__ __forceinline__ void wc_pack_lds(const uint8_t* s, uint32_t a, uint32_t len, uint32_t (&w)[8]) {
+// Bytes s[a, a + len), len <= 4 NW, little-endian in w[0, NW), zero past
+// len. s is 4-byte aligned; reads at most 4 NW + 4 bytes from s + (a & ~3).
+template <int NW>
+__device__ __forceinline__ void wc_pack_lds(const uint8_t* s, uint32_t a, uint32_t len, uint32_t (&w)[NW]) {
     const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s);
     const uint32_t b = a >> 2, r = a & 3u;
     uint32_t lo = s32[b];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NW; ++k) {
         uint32_t v = 0u;
         if (4u * (uint32_t)k < len) {
             const uint32_t hi = s32[b + (uint32_t)k + 1u];
@@ -197,12 +209,14 @@ __device__ __forceinline__ void wc_pack_lds(const uint8_t* s, uint32_t a, uint32
     }
 }
 
-// 64-bit hash of a packed word: a multiply-xorshift step per 4 bytes, then
-// the SplitMix64 finaliser (Steele, Lea and Flood, 2014).
-__device__ __forceinline__ unsigned long long wc_hash(const uint32_t (&w)[8], uint32_t len) {
+// 64-bit hash of a packed word (len <= 4 NW; the same value for any such
+// NW): a multiply-xorshift step per 4 bytes, then the SplitMix64 finaliser
+// (Steele, Lea and Flood, 2014).
+template <int NW>
+__device__ __forceinline__ unsigned long long wc_hash(const uint32_t (&w)[NW], uint32_t len) {
     unsigned long long h = 0x9E3779B97F4A7C15ull * (unsigned long long)(len + 1u);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NW; ++k) {
         if (4u * (uint32_t)k < len) {
             h ^= w[k];
             h *= 0xBF58476D1CE4E5B9ull;
@@ -224,18 +238,16 @@ __device__ __forceinline__ uint32_t wc_slot(const WordCache& wc, unsigned long l
     return (uint32_t)(h >> 32) & wc.mask;
 }
 
-// Linear probing from slot: stop at the key (someone claimed the word, or
-// a word with the same key) or claim a free slot, list it and record pos.
-// Plain loads see a slot either free (then the CAS decides) or final.
+// Linear probing from slot: stop at the key, or claim the first free slot
+// (CAS; the claimer records its position); give up after WC_PROBES slots.
+// A plain load that still shows a slot free only costs the CAS.
 __device__ __forceinline__ void wc_insert(const WordCache& wc, unsigned long long key, uint32_t slot, uint32_t pos) {
     for (uint32_t p = 0; p < WC_PROBES; ++p) {
         unsigned long long v = wc.key[slot];
         if (v == 0ull) {
-            if (ld_relaxed(wc.n_list) >= wc.limit) return;
             v = atomicCAS(wc.key + slot, 0ull, key);
             if (v == 0ull) {
                 wc.pos[slot] = pos;
-                wc.list[atomicAdd(wc.n_list, 1u)] = slot;
                 return;
             }
         }
@@ -244,57 +256,80 @@ __device__ __forceinline__ void wc_insert(const WordCache& wc, unsigned long lon
     }
 }
 
-// The record of the packed word w (key, probing from slot), into r; false
-// if no slot on its probe path holds these bytes. Each probe loads the
-// slot's key and record together.
-__device__ __forceinline__ bool wc_lookup(const WordCache& wc, unsigned long long key, uint32_t slot,
-                                          const uint32_t (&w)[8], uint32_t (&r)[WC_MASKW + 1]) {
+// One probe: the slot's key into *v and the first NW words of its record
+// into r, loaded together.
+template <uint32_t NW>
+__device__ __forceinline__ void wc_probe(const WordCache& wc, uint32_t slot, unsigned long long* v,
+                                         uint32_t (&r)[NW]) {
     typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    *v = wc.key[slot];
+    const uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
+#pragma unroll
+    for (int k = 0; k < (int)NW / 4; ++k) {
+        const v4 x = *reinterpret_cast<const v4*>(rp + 4 * k);
+        r[4 * k] = x.x;
+        r[4 * k + 1] = x.y;
+        r[4 * k + 2] = x.z;
+        r[4 * k + 3] = x.w;
+    }
+}
+
+// Whether a probed slot (key v, record r: its first half, or all of it)
+// holds the packed word w of length len under key; with the first half
+// only, len <= WC_SHORT and w has 4 words.
+template <uint32_t NW, int NB>
+__device__ __forceinline__ bool wc_match(unsigned long long key, unsigned long long v, const uint32_t (&w)[NB],
+                                         uint32_t len, const uint32_t (&r)[NW]) {
+    static_assert(NB == (NW == WC_REC ? 8 : 4), "packed bytes match the record part");
+    uint32_t d = r[WC_LENW] ^ len;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d |= w[k] ^ r[k];
+#pragma unroll
+    for (int k = 4; k < NB; ++k) d |= w[k] ^ r[WC_B1 + (k - 4)];
+    return v == key && d == 0u;
+}
+
+// The record holding the packed word w of length len (key, probing from
+// slot), into r; false if none before a free slot, within WC_PROBES slots.
+__device__ __forceinline__ bool wc_lookup(const WordCache& wc, unsigned long long key, uint32_t slot,
+                                          const uint32_t (&w)[8], uint32_t len, uint32_t (&r)[WC_REC]) {
     for (uint32_t p = 0; p < WC_PROBES; ++p) {
-        const unsigned long long v = wc.key[slot];
-        const uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
-#pragma unroll
-        for (int k = 0; k < (int)WC_MASKW / 4; ++k) {
-            const v4 x = *reinterpret_cast<const v4*>(rp + 4 * k);
-            r[4 * k] = x.x;
-            r[4 * k + 1] = x.y;
-            r[4 * k + 2] = x.z;
-            r[4 * k + 3] = x.w;
-        }
-        r[WC_MASKW] = rp[WC_MASKW];
-        if (v == key) {
-            uint32_t d = 0u;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) d |= w[k] ^ r[k];
-            if (d == 0u) return true;
-        } else if (v == 0ull) {
-            return false;
-        }
+        unsigned long long v;
+        wc_probe<WC_REC>(wc, slot, &v, r);
+        if (wc_match(key, v, w, len, r)) return true;
+        if (v == 0ull) return false;
         slot = (slot + 1u) & wc.mask;
     }
     return false;
 }
 
-// Free every slot and the claim count (before the insert pass).
+// Free every slot (before the insert pass).
 __global__ void k_wc_clear(WordCache wc, uint32_t slots) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gridDim.x * blockDim.x) wc.key[i] = 0ull;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *wc.n_list = 0u;
 }
 
-// Fill pass: every listed word, one per thread, encoded in the thread's
-// LDS range of WC_MAXLEN positions; the record gets the word's bytes (zero
-// past its length), its token ids and the offsets where its tokens start.
+// Fill pass: every used slot, one per thread, its key's length of bytes
+// from its position (n bytes of text) encoded in the thread's LDS range of
+// WC_MAXLEN positions. The record gets those bytes (zero past the length),
+// the token ids, the offsets where tokens start and the length; a range
+// past the text's end gets length 0, which no lookup accepts.
 template <int TPB>
-__global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ text, WordCache wc, RankTable rt) {
+__global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ text, uint32_t n, WordCache wc,
+                                                 RankTable rt, uint32_t slots) {
     __shared__ uint16_t s_sym[TPB * WC_MAXLEN], s_nx[TPB * WC_MAXLEN], s_rk[TPB * WC_MAXLEN];
     const LdsWord lw{s_sym, s_nx, s_rk};
-    const uint32_t nl = ld_relaxed(wc.n_list);
     const uint32_t b = threadIdx.x * WC_MAXLEN;
-    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < nl; i += gridDim.x * TPB) {
-        const uint32_t slot = wc.list[i];
-        const uint32_t len = (uint32_t)(wc.key[slot] & 63ull);
-        const uint8_t* src = text + wc.pos[slot];
+    for (uint32_t slot = blockIdx.x * TPB + threadIdx.x; slot < slots; slot += gridDim.x * TPB) {
+        const unsigned long long key = wc.key[slot];
+        if (key == 0ull) continue;
+        const uint32_t len = (uint32_t)(key & 63ull);
+        const uint32_t at = wc.pos[slot];
         uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
+        if (len > WC_MAXLEN || at > n || n - at < len) {
+            rp[WC_LENW] = 0u;
+            continue;
+        }
+        const uint8_t* src = text + at;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t v = 0u;
@@ -303,7 +338,7 @@ __global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ tex
                 const uint32_t j = 4u * (uint32_t)k + (uint32_t)u;
                 if (j < len) v |= (uint32_t)src[j] << (8 * u);
             }
-            rp[k] = v;
+            rp[k < 4 ? k : WC_B1 + (k - 4)] = v;
         }
         for (uint32_t j = 0; j < len; ++j) {
             s_sym[b + j] = src[j];
@@ -313,13 +348,18 @@ __global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ tex
             s_rk[b + j] = rt.bytes[((uint32_t)s_sym[b + j] << 8) | s_sym[b + j + 1u]];
         while (!merge_iteration(lw, b, b + len, rt)) {
         }
-        uint16_t* tp = reinterpret_cast<uint16_t*>(rp + WC_TOK);
+        uint16_t* t0 = reinterpret_cast<uint16_t*>(rp + WC_T0);
+        uint16_t* t1 = reinterpret_cast<uint16_t*>(rp + WC_T1);
         uint32_t m = 0u, c = 0u;
-        for (uint32_t x = b; x < b + len; x = s_nx[x]) {
+        for (uint32_t x = b; x < b + len; x = s_nx[x], ++c) {
             m |= 1u << (x - b);
-            tp[c++] = s_sym[x];
+            if (c < 16u)
+                t0[c] = s_sym[x];
+            else
+                t1[c - 16u] = s_sym[x];
         }
         rp[WC_MASKW] = m;
+        rp[WC_LENW] = len;
     }
 }
 
@@ -442,7 +482,7 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
 // (capacity scratch_cap positions; past it *err is set and the word is
 // skipped). sym_g, nx_g, rk_g: the scratch arrays.
 template <int TPB>
-__global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ text, uint32_t n, RankTable rt,
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k_enc_walk(const uint8_t* __restrict__ text, uint32_t n, RankTable rt,
                                                   uint32_t* __restrict__ tok32, uint32_t* __restrict__ cnt,
                                                   uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
                                                   uint32_t ntiles, uint16_t* sym_g, uint32_t* nx_g, uint16_t* rk_g,
@@ -462,7 +502,11 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
     __shared__ uint16_t s_aux[CAP];                    // word list, then staged output ids
     __shared__ uint32_t s_ws[CAP / 32u];               // staged output: word-start bits
     __shared__ uint32_t s_w[TPB / 64];
-    __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after;
+    __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after, s_nq;
+    constexpr uint32_t DLIST = TILE / 2;  // with the cache: the queue's words at s_aux[DLIST..)
+    constexpr uint32_t RETRY = 0x8000u;   // flag on a queued position (positions < CAP < RETRY)
+    static_assert(CAP < RETRY, "positions leave the flag bit free");
+    static_assert(DLIST + TILE / 2 <= CAP, "word list and queue fit s_aux");
 
     const uint32_t tid = threadIdx.x;
     const uint32_t mis = (uint32_t)((uintptr_t)text & 15u);
@@ -476,6 +520,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
             s_ovf_pos = NO_OVF;
             s_ovf_n = 0u;
             s_after = CAP;
+            s_nq = 0u;
         }
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_flag[i] = 0u;
         const uint32_t t0 = t * TILE;
@@ -501,17 +546,104 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
         for (uint32_t m = multi; m; m &= m - 1u) s_aux[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
         __syncthreads();
 
-        // the words of two bytes or more: a wave queue, one iteration of a
-        // lane's word per round
+        const uint32_t lim = nrel < CAP ? nrel : CAP;
+        const uint32_t last_end = s_after < lim ? s_after : lim;
+        const bool last_open = s_after >= CAP && lim < nrel;
+
+        // live list of the word [q, wend) from its bytes, with the ranks of
+        // its byte pairs (eight loads in flight, then the stores)
+        auto init_word = [&](uint32_t q, uint32_t wend) {
+            for (uint32_t i = q; i < wend; ++i) {
+                s_sym[i] = (uint16_t)lbyte(i);
+                s_nx[i] = (uint16_t)(i + 1u);
+            }
+            for (uint32_t i = q; i + 1u < wend; i += 8u) {
+                uint32_t r[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t p = i + (uint32_t)u;
+                    r[u] = p + 1u < wend ? rt.bytes[(lbyte(p) << 8) | lbyte(p + 1u)] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (i + (uint32_t)u + 1u < wend) s_rk[i + u] = (uint16_t)r[u];
+            }
+        };
+        auto flag_tokens = [&](uint32_t q, uint32_t wend) {
+            for (uint32_t i = q; i < wend; i = s_nx[i]) atomicOr(&s_flag[i >> 5], 1u << (i & 31u));
+        };
+        // a cached word at q: the token starts and ids of its record r (the
+        // first half for a word of up to WC_SHORT bytes)
+        auto put_tokens = [&](uint32_t q, const auto& r) {
+            constexpr uint32_t NT = sizeof(r) / sizeof(r[0]) == WC_REC ? WC_MAXLEN : WC_SHORT;
+            uint32_t m = r[WC_MASKW];
+            const uint32_t o = q & 31u;
+            atomicOr(&s_flag[q >> 5], m << o);
+            if (o && (m >> (32u - o))) atomicOr(&s_flag[(q >> 5) + 1u], m >> (32u - o));
+#pragma unroll
+            for (int k = 0; k < (int)NT; ++k) {
+                if (m) {
+                    const uint32_t two = k < 16 ? r[WC_T0 + k / 2] : r[WC_T1 + (k - 16) / 2];
+                    s_sym[q + __ffs(m) - 1] = (uint16_t)(two >> (16 * (k & 1)));
+                    m &= m - 1u;
+                }
+            }
+        };
+
+        // with the cache: every word of 2 .. WC_SHORT bytes takes its tokens
+        // from the first half of its home slot's record, two words per thread
+        // with their loads in flight together; the other words are listed
+        // for the queue, with RETRY for those the queue should look up (longer
+        // cached words, and short ones whose home slot holds another key)
+        const uint16_t* ql = s_aux;
+        uint32_t nq = nwords;
+        if (wc.key) {
+            for (uint32_t i0 = tid; i0 < nwords; i0 += 2u * TPB) {
+                uint32_t q[2], len[2], slot[2], w[2][4], r[2][WC_HALF];
+                unsigned long long key[2], v[2];
+                bool cand[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t i = i0 + (uint32_t)u * TPB;
+                    cand[u] = false;
+                    if (i < nwords) {
+                        q[u] = s_aux[i];
+                        len[u] = word_end<TILE>(s_sb, q[u], last_end) - q[u];
+                        cand[u] = len[u] <= WC_SHORT;
+                    }
+                    if (cand[u]) {
+                        wc_pack_lds(s_txt, q[u] + sh, len[u], w[u]);
+                        const unsigned long long h = wc_hash(w[u], len[u]);
+                        key[u] = wc_key(wc, h, len[u]);
+                        slot[u] = wc_slot(wc, h);
+                        wc_probe<WC_HALF>(wc, slot[u], &v[u], r[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t i = i0 + (uint32_t)u * TPB;
+                    if (i >= nwords) continue;
+                    if (cand[u] && wc_match(key[u], v[u], w[u], len[u], r[u]))
+                        put_tokens(q[u], r[u]);
+                    else if (cand[u])
+                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (v[u] ? RETRY : 0u));
+                    else
+                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (len[u] <= WC_MAXLEN ? RETRY : 0u));
+                }
+            }
+            lds_barrier();
+            ql = s_aux + DLIST;
+            nq = s_nq;
+        }
+
+        // the listed words: a wave queue, one iteration of a lane's word per
+        // round
         {
-            const uint32_t lim = nrel < CAP ? nrel : CAP;
-            const uint32_t last_end = s_after < lim ? s_after : lim;
-            const bool last_open = s_after >= CAP && lim < nrel;
             constexpr uint32_t NWAVE = TPB / 64u;
             const uint32_t wave = tid >> 6;
-            const uint32_t share = (nwords + NWAVE - 1u) / NWAVE;
-            const uint32_t w_hi = min(nwords, (wave + 1u) * share);
-            uint32_t next = min(nwords, wave * share);
+            const uint32_t share = (nq + NWAVE - 1u) / NWAVE;
+            const uint32_t w_hi = min(nq, (wave + 1u) * share);
+            uint32_t next = min(nq, wave * share);
             uint32_t q = 0, wend = 0, gq = NO_OVF;
             bool act = false;
             for (;;) {
@@ -519,54 +651,28 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                 if (need) {
                     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(need >> 32),
                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)need, 0u));
-                    if (!act && next + below < w_hi) {
-                        q = s_aux[next + below];
-                        wend = word_end<TILE>(s_sb, q, last_end);
+                    const uint32_t wi = next + below;
+                    if (!act && wi < w_hi) {
+                        q = ql[wi];
                         bool cached = false;
-                        if (wc.key && wend - q <= WC_MAXLEN) {
-                            // a cached word: its tokens from the record
+                        if (q & RETRY) {
+                            q &= ~RETRY;
+                            wend = word_end<TILE>(s_sb, q, last_end);
                             const uint32_t len = wend - q;
-                            uint32_t w[8], r[WC_MASKW + 1];
+                            uint32_t w[8], r[WC_REC];
                             wc_pack_lds(s_txt, q + sh, len, w);
                             const unsigned long long h = wc_hash(w, len);
-                            if (wc_lookup(wc, wc_key(wc, h, len), wc_slot(wc, h), w, r)) {
-                                uint32_t m = r[WC_MASKW];
-                                const uint32_t o = q & 31u;
-                                atomicOr(&s_flag[q >> 5], m << o);
-                                if (o && (m >> (32u - o))) atomicOr(&s_flag[(q >> 5) + 1u], m >> (32u - o));
-#pragma unroll
-                                for (int k = 0; k < (int)WC_MAXLEN / 2; ++k) {
-                                    const uint32_t two = r[WC_TOK + k];
-#pragma unroll
-                                    for (int u = 0; u < 2; ++u) {
-                                        if (m) {
-                                            s_sym[q + __ffs(m) - 1] = (uint16_t)(two >> (16 * u));
-                                            m &= m - 1u;
-                                        }
-                                    }
-                                }
+                            if (wc_lookup(wc, wc_key(wc, h, len), wc_slot(wc, h), w, len, r)) {
+                                put_tokens(q, r);
                                 cached = true;
                             }
                         }
-                        if (!cached && last_open && wend == last_end) {
+                        wend = word_end<TILE>(s_sb, q, last_end);
+                        if (cached) {
+                        } else if (last_open && wend == last_end) {
                             gq = q;  // runs past the copy: encoded from global memory below
-                        } else if (!cached) {
-                            for (uint32_t i = q; i < wend; ++i) {
-                                s_sym[i] = (uint16_t)lbyte(i);
-                                s_nx[i] = (uint16_t)(i + 1u);
-                            }
-                            // ranks of the byte pairs: eight loads in flight, then the stores
-                            for (uint32_t i = q; i + 1u < wend; i += 8u) {
-                                uint32_t r[8];
-#pragma unroll
-                                for (int u = 0; u < 8; ++u) {
-                                    const uint32_t p = i + (uint32_t)u;
-                                    r[u] = p + 1u < wend ? rt.bytes[(lbyte(p) << 8) | lbyte(p + 1u)] : 0u;
-                                }
-#pragma unroll
-                                for (int u = 0; u < 8; ++u)
-                                    if (i + (uint32_t)u + 1u < wend) s_rk[i + u] = (uint16_t)r[u];
-                            }
+                        } else {
+                            init_word(q, wend);
                             act = true;
                         }
                     }
@@ -574,7 +680,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                 }
                 if (__ballot(act) == 0ull && next >= w_hi) break;
                 if (act && merge_iteration(lw, q, wend, rt)) {
-                    for (uint32_t i = q; i < wend; i = s_nx[i]) atomicOr(&s_flag[i >> 5], 1u << (i & 31u));
+                    flag_tokens(q, wend);
                     act = false;
                 }
             }
@@ -594,6 +700,7 @@ __global__ __launch_bounds__(TPB) void k_enc_walk(const uint8_t* __restrict__ te
                 }
             }
         }
+
         __syncthreads();
 
         // compaction: final symbols at the recorded starts, WS on word starts

@@ -184,11 +184,11 @@ bpe_status bpe_encoder_build(const bpe_merge *merges, uint32_t n_merges, bpe_enc
 /* Encode bytes[0..n) (host or device) on stream (a hipStream_t, or NULL for
    the encoder's own). tokens (host or device, capacity tokens_cap >= n, or
    NULL for the count only) receive the tokens, *n_tokens their count.
-   With the word cache (bpe_encoder_cache; off by default) three kernels
+   With the word cache (bpe_encoder_cache; on by default) three kernels
    first collect the distinct words of 2..32 bytes and encode each once;
    then three kernels (walk, scan, copy), a wait for the total and a sized
    copy for host tokens. Device buffers are pooled in the encoder (about 6
-   bytes per input byte, the cache's 144 bytes per slot, plus scratch of 12
+   bytes per input byte, the cache's 140 bytes per slot, plus scratch of 12
    bytes per position for words that do not fit a tile's LDS, at most 2^24
    positions per call), so calls on one encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
    NULL bytes with n > 0, n > BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM
@@ -205,16 +205,18 @@ bpe_status bpe_encoder_encode(bpe_encoder *e, const uint8_t *bytes, size_t n, vo
 bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, uint32_t reps, float *ms,
                                size_t *n_tokens);
 
-/* Size of the encoder's word cache for later calls. Every occurrence of a
-   word encodes alike, so each distinct word of 2..32 bytes is encoded once
-   per call into a hash table (linear probing over 2^log2_slots slots,
-   claims stop at half of them) and its occurrences copy the result after
-   comparing their bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
-   (one slot per 128 input bytes, 2^10..2^22), 0 (no cache) or 8..24.
+/* Size of the encoder's word cache for later calls. Words are encoded each
+   on its own (page "bpe - GPU BPE Tokenizer Pipeline", "Nedir bu ya?" and
+   "Ne Yapar? 1": merges never cross a word start), so every occurrence of a
+   word encodes alike and each distinct word of 2..32 bytes is encoded once
+   per call into a hash table (linear probing over 2^log2_slots slots, at
+   most 8 probes) and its occurrences copy the result after comparing their
+   bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
+   (one slot per 256 input bytes, 2^10..2^22), 0 (no cache) or 8..24.
    key_bits (at most BPE_CACHE_KEY_BITS): hash bits in a slot's key; fewer
    bits make distinct words share keys, which only sends more words down
    the uncached path (a testing aid). Tokens never depend on either
-   setting. A new encoder has no cache (log2_slots 0). Errors: BPE_EINVAL. */
+   setting. A new encoder has the automatic size. Errors: BPE_EINVAL. */
 #define BPE_CACHE_AUTO 0xFFFFFFFFu
 #define BPE_CACHE_KEY_BITS 58u
 bpe_status bpe_encoder_cache(bpe_encoder *e, uint32_t log2_slots, uint32_t key_bits);

@@ -158,10 +158,10 @@ def test_encoder_host_input_and_output_through_the_abi(bpe):
         assert st == 0 and n_tok.value == ot.size
 
 
-# word cache: (log2 slots, key bits). 8 slots-log2 stops claims at 128
-# words, so most words take the uncached path; 0 key bits give every word
-# of one length the same key, 4 bits nearly so (probing past keys whose
-# bytes differ); 0 slots turn the cache off.
+# word cache: (log2 slots, key bits). 2^8 slots fill up, so most words
+# take the uncached path; 0 key bits give every word of one length the same
+# key, 4 bits nearly so (records whose bytes differ, probing past them); 0
+# slots turn the cache off.
 CACHE_SETTINGS = [(0xFFFFFFFF, 58), (0, 58), (8, 58), (10, 0), (12, 4), (16, 58)]
 
 
