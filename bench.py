@@ -245,7 +245,8 @@ def main() -> int:
     ap.add_argument("--no-inference", action="store_true", help="skip the inference and encoding legs")
     ap.add_argument("--save-merges", default=None, metavar="PATH", help="write the learned merges (.npy)")
     ap.add_argument("--inference-only", default=None, metavar="PATH",
-                    help="skip training: time inference with the merges saved in PATH (.npy) by --save-merges")
+                    help="skip training: time inference and encoding with the merges saved in PATH (.npy) "
+                         "by --save-merges")
     ap.add_argument("--inference-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
@@ -288,7 +289,10 @@ def main() -> int:
         m = torch.from_numpy(np.load(args.inference_only, allow_pickle=False)).to("cuda:0")
         inf = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log,
                             source="learned by an earlier run on the same corpus")
+        enc = encode_leg(args, bpe, spec, data, d, m, np, time, log,
+                         source="learned by an earlier run on the same corpus")
         out = dict(inf)
+        out["encoding"] = enc
         out.update({"n_gpus": 1, "steps": inf["runs"], "warmup": 1, "higher_is_better": True, "scaling": "weak",
                     "vs_baseline": None, "dtype": "u8", "data": "synthetic",
                     "config": {"workload": inf["workload"], "corpus_bytes": spec.n_bytes}})
