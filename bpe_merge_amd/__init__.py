@@ -241,7 +241,7 @@ class Encoder:
         return n_tok.value, ms[: 4 * reps].reshape(reps, 4)
 
     CACHE_AUTO = 0xFFFFFFFF
-    CACHE_KEY_BITS = 58
+    CACHE_KEY_BITS = 32
 
     def cache(self, log2_slots=CACHE_AUTO, key_bits=CACHE_KEY_BITS):
         """bpe_encoder_cache: word-cache size for later calls (CACHE_AUTO, 0 =

@@ -1234,7 +1234,7 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
     if (l) {
         const uint32_t slots = 1u << l;
         wc = bpek::WordCache{e->wc_key, e->wc_pos, e->wc_rec, slots - 1,
-                             e->wc_key_bits ? ~0ull << (64 - e->wc_key_bits) : 0ull};
+                             e->wc_key_bits ? ~0u << (32 - e->wc_key_bits) : 0u};
         hipLaunchKernelGGL(bpek::k_wc_clear, dim3(std::min<uint32_t>((slots + 255) / 256, e->clear_grid)), dim3(256),
                            0, s, wc, slots);
         hipLaunchKernelGGL(bpek::k_wc_insert<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->insert_grid)),

@@ -179,13 +179,14 @@ constexpr uint32_t WC_REC = 32;      // u32 per record (128 bytes)
 constexpr uint32_t WC_HALF = 16;
 constexpr uint32_t WC_T0 = 4, WC_MASKW = 12, WC_LENW = 13, WC_B1 = 16, WC_T1 = 20;
 constexpr uint32_t WC_PROBES = 8;
+constexpr uint32_t WC_BATCH = 2;     // words a walk thread looks up with their loads in flight together
 
 struct WordCache {
-    unsigned long long* key;   // per slot: 0 = free, else hash bits | length
+    unsigned long long* key;   // per slot: 0 = free, else hash bits << 6 | length
     uint32_t* pos;             // per slot: a text position of a word with that key
     uint32_t* rec;             // WC_REC words per slot
     uint32_t mask;             // slots - 1
-    unsigned long long kmask;  // hash bits kept in a key (fewer bits, more words sharing a key)
+    uint32_t kmask;            // hash bits kept in a key (fewer bits, more words sharing a key)
 };
 
 // Bytes s[a, a + len), len <= 4 NW, little-endian in w[0, NW), zero past
@@ -209,34 +210,30 @@ __device__ __forceinline__ void wc_pack_lds(const uint8_t* s, uint32_t a, uint32
     }
 }
 
-// 64-bit hash of a packed word (len <= 4 NW; the same value for any such
-// NW): a multiply-xorshift step per 4 bytes, then the SplitMix64 finaliser
-// (Steele, Lea and Flood, 2014).
+// 32-bit hash of a packed word (len <= 4 NW; the same value for any such
+// NW): per 4 bytes an xor, a multiply and an xorshift, then the Murmur3
+// finaliser. A key only has to tell apart the words that meet in one probe
+// run (a record is used only after comparing bytes), so 32 bits suffice,
+// and 32-bit multiplies keep the hash cheap: it runs once per word in the
+// insert pass and again in the walk.
 template <int NW>
-__device__ __forceinline__ unsigned long long wc_hash(const uint32_t (&w)[NW], uint32_t len) {
-    unsigned long long h = 0x9E3779B97F4A7C15ull * (unsigned long long)(len + 1u);
+__device__ __forceinline__ uint32_t wc_hash(const uint32_t (&w)[NW], uint32_t len) {
+    uint32_t h = 0x9E3779B9u ^ len;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         if (4u * (uint32_t)k < len) {
             h ^= w[k];
-            h *= 0xBF58476D1CE4E5B9ull;
-            h ^= h >> 31;
+            h *= 0x85EBCA6Bu;
+            h ^= h >> 13;
         }
     }
-    h ^= h >> 30;
-    h *= 0xBF58476D1CE4E5B9ull;
-    h ^= h >> 27;
-    h *= 0x94D049BB133111EBull;
-    h ^= h >> 31;
-    return h;
+    return mix32(h);
 }
 
-__device__ __forceinline__ unsigned long long wc_key(const WordCache& wc, unsigned long long h, uint32_t len) {
-    return (h & wc.kmask & ~63ull) | len;  // len >= 2: never 0
+__device__ __forceinline__ unsigned long long wc_key(const WordCache& wc, uint32_t h, uint32_t len) {
+    return ((unsigned long long)(h & wc.kmask) << 6) | len;  // len >= 2: never 0
 }
-__device__ __forceinline__ uint32_t wc_slot(const WordCache& wc, unsigned long long h) {
-    return (uint32_t)(h >> 32) & wc.mask;
-}
+__device__ __forceinline__ uint32_t wc_slot(const WordCache& wc, uint32_t h) { return h & wc.mask; }
 
 // Linear probing from slot: stop at the key, or claim the first free slot
 // (CAS; the claimer records its position); give up after WC_PROBES slots.
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
             if (len > WC_MAXLEN) continue;  // also a word running past the copy (its length here >= HALO)
             uint32_t w[8];
             wc_pack_lds(s_txt, q + sh, len, w);
-            const unsigned long long h = wc_hash(w, len);
+            const uint32_t h = wc_hash(w, len);
             wc_insert(wc, wc_key(wc, h, len), wc_slot(wc, h), t0 + q);
         }
         __syncthreads();
@@ -591,19 +588,19 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         };
 
         // with the cache: every word of 2 .. WC_SHORT bytes takes its tokens
-        // from the first half of its home slot's record, two words per thread
-        // with their loads in flight together; the other words are listed
+        // from the first half of its home slot's record, WC_BATCH words per
+        // thread with their loads in flight together; the other words are listed
         // for the queue, with RETRY for those the queue should look up (longer
         // cached words, and short ones whose home slot holds another key)
         const uint16_t* ql = s_aux;
         uint32_t nq = nwords;
         if (wc.key) {
-            for (uint32_t i0 = tid; i0 < nwords; i0 += 2u * TPB) {
-                uint32_t q[2], len[2], slot[2], w[2][4], r[2][WC_HALF];
-                unsigned long long key[2], v[2];
-                bool cand[2];
+            for (uint32_t i0 = tid; i0 < nwords; i0 += WC_BATCH * TPB) {
+                uint32_t q[WC_BATCH], len[WC_BATCH], slot[WC_BATCH], w[WC_BATCH][4], r[WC_BATCH][WC_HALF];
+                unsigned long long key[WC_BATCH], v[WC_BATCH];
+                bool cand[WC_BATCH];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < (int)WC_BATCH; ++u) {
                     const uint32_t i = i0 + (uint32_t)u * TPB;
                     cand[u] = false;
                     if (i < nwords) {
@@ -613,14 +610,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                     }
                     if (cand[u]) {
                         wc_pack_lds(s_txt, q[u] + sh, len[u], w[u]);
-                        const unsigned long long h = wc_hash(w[u], len[u]);
+                        const uint32_t h = wc_hash(w[u], len[u]);
                         key[u] = wc_key(wc, h, len[u]);
                         slot[u] = wc_slot(wc, h);
                         wc_probe<WC_HALF>(wc, slot[u], &v[u], r[u]);
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < (int)WC_BATCH; ++u) {
                     const uint32_t i = i0 + (uint32_t)u * TPB;
                     if (i >= nwords) continue;
                     if (cand[u] && wc_match(key[u], v[u], w[u], len[u], r[u]))
@@ -661,7 +658,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                             const uint32_t len = wend - q;
                             uint32_t w[8], r[WC_REC];
                             wc_pack_lds(s_txt, q + sh, len, w);
-                            const unsigned long long h = wc_hash(w, len);
+                            const uint32_t h = wc_hash(w, len);
                             if (wc_lookup(wc, wc_key(wc, h, len), wc_slot(wc, h), w, len, r)) {
                                 put_tokens(q, r);
                                 cached = true;

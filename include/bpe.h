@@ -218,7 +218,7 @@ bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, u
    the uncached path (a testing aid). Tokens never depend on either
    setting. A new encoder has the automatic size. Errors: BPE_EINVAL. */
 #define BPE_CACHE_AUTO 0xFFFFFFFFu
-#define BPE_CACHE_KEY_BITS 58u
+#define BPE_CACHE_KEY_BITS 32u
 bpe_status bpe_encoder_cache(bpe_encoder *e, uint32_t log2_slots, uint32_t key_bits);
 
 /* Release the encoder and its buffers. NULL is a no-op. */

@@ -172,6 +172,6 @@ def test_trie_and_encoder_encode_argument_validation(bpe):
         assert enc(None, ctypes.addressof(buf), 16, None, None, 0, ctypes.byref(n_tok)) == bpe.EINVAL
     for prof in (lib.bpe_trie_profile, lib.bpe_encoder_profile):
         assert prof(None, ctypes.addressof(buf), 16, 1, None, ctypes.byref(n_tok)) == bpe.EINVAL
-    assert lib.bpe_encoder_cache(None, 0xFFFFFFFF, 58) == bpe.EINVAL
+    assert lib.bpe_encoder_cache(None, 0xFFFFFFFF, 32) == bpe.EINVAL
     lib.bpe_trie_free(None)
     lib.bpe_encoder_free(None)

@@ -162,7 +162,7 @@ def test_encoder_host_input_and_output_through_the_abi(bpe):
 # take the uncached path; 0 key bits give every word of one length the same
 # key, 4 bits nearly so (records whose bytes differ, probing past them); 0
 # slots turn the cache off.
-CACHE_SETTINGS = [(0xFFFFFFFF, 58), (0, 58), (8, 58), (10, 0), (12, 4), (16, 58)]
+CACHE_SETTINGS = [(0xFFFFFFFF, 32), (0, 32), (8, 32), (10, 0), (12, 4), (16, 32)]
 
 
 @pytest.mark.parametrize("c", [2, 3, 5])
@@ -208,7 +208,7 @@ def test_word_cache_lengths_and_alignments(bpe):
 
 def test_word_cache_rejects_bad_settings(bpe):
     with bpe.Encoder([(97, 98)]) as e:
-        for slots, bits in ((7, 58), (25, 58), (16, 59)):
+        for slots, bits in ((7, 32), (25, 32), (16, 33)):
             with pytest.raises(bpe.BpeError):
                 e.cache(slots, bits)
         e.cache(8, 0)
