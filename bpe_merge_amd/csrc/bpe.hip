@@ -1177,6 +1177,7 @@ struct bpe_encoder {
     uint32_t* wc_rec = nullptr;
     size_t wc_rec_cap = 0;
     uint32_t wc_log2 = BPE_CACHE_AUTO, wc_key_bits = BPE_CACHE_KEY_BITS;
+    uint32_t wc_call_log2 = 0;  // the size the current call runs with (0: none)
     int walk_grid = 0, copy_grid = 0, insert_grid = 0, fill_grid = 0, clear_grid = 0;
 };
 
@@ -1209,13 +1210,20 @@ bpe_status enc_pools(bpe_encoder* e, size_t n) {
     if (st == BPE_OK) st = pool_grow(&e->nx_g, &e->nx_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->rk_g, &e->rk_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->ovf, &e->ovf_cap, sc, false);
-    const uint32_t l = enc_wc_log2(e, n);
-    if (l) {
+    // the cache never decides a token: without memory for it, the call
+    // runs without it
+    uint32_t l = enc_wc_log2(e, n);
+    if (st == BPE_OK && l) {
         const size_t slots = size_t(1) << l;
-        if (st == BPE_OK) st = pool_grow(&e->wc_key, &e->wc_key_cap, slots, false);
-        if (st == BPE_OK) st = pool_grow(&e->wc_pos, &e->wc_pos_cap, slots, false);
-        if (st == BPE_OK) st = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, false);
+        bpe_status cs = pool_grow(&e->wc_key, &e->wc_key_cap, slots, false);
+        if (cs == BPE_OK) cs = pool_grow(&e->wc_pos, &e->wc_pos_cap, slots, false);
+        if (cs == BPE_OK) cs = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, false);
+        if (cs != BPE_OK) {
+            g_err.clear();
+            l = 0;
+        }
     }
+    e->wc_call_log2 = l;
     return st;
 }
 
@@ -1228,7 +1236,7 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
     uint32_t* ovf_n = ovf_pos + npad;
     uint32_t* pfx = ovf_n + npad;
     const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes, e->rt_bytes};
-    const uint32_t l = enc_wc_log2(e, n);
+    const uint32_t l = e->wc_call_log2;  // set by enc_pools for this n
     bpek::WordCache wc{};
     hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
     if (l) {

@@ -216,7 +216,8 @@ bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, u
    key_bits (at most BPE_CACHE_KEY_BITS): hash bits in a slot's key; fewer
    bits make distinct words share keys, which only sends more words down
    the uncached path (a testing aid). Tokens never depend on either
-   setting. A new encoder has the automatic size. Errors: BPE_EINVAL. */
+   setting. A new encoder has the automatic size; a call that cannot
+   allocate the cache's memory runs without it. Errors: BPE_EINVAL. */
 #define BPE_CACHE_AUTO 0xFFFFFFFFu
 #define BPE_CACHE_KEY_BITS 32u
 bpe_status bpe_encoder_cache(bpe_encoder *e, uint32_t log2_slots, uint32_t key_bits);
