@@ -154,9 +154,10 @@ __device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* 
 // ---------------------------------------------------------------- word cache
 // A word's encoding depends on its bytes alone, and a text repeats few
 // distinct words many times, so each distinct word can be encoded once: the
-// insert pass puts the words of 2 .. WC_MAXLEN bytes into a hash table, the
-// fill pass encodes the word of every used slot into the slot's record, and
-// the walk takes a word's tokens from a record holding the same bytes.
+// insert pass puts the words of 2 .. WC_MAXLEN bytes of a sample of the
+// tiles into a hash table, the fill pass encodes the word of every used
+// slot into the slot's record, and the walk takes a word's tokens from a
+// record holding the same bytes.
 //
 // A slot is claimed by a CAS on its key and the claimer stores a text
 // position of its word. Nothing else is shared: device-scope atomics on one
@@ -424,11 +425,11 @@ __device__ __forceinline__ uint32_t word_end(const uint32_t* s_sb, uint32_t q, u
     return last_end;
 }
 
-// Insert pass: the walk's tiles, every word of 2 .. WC_MAXLEN bytes
-// starting in a tile put into the cache.
+// Insert pass: every stride-th tile of the walk's (tiles 0, stride, ...),
+// every word of 2 .. WC_MAXLEN bytes starting in it put into the cache.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ text, uint32_t n, uint32_t ntiles,
-                                                   WordCache wc) {
+                                                   uint32_t stride, WordCache wc) {
     constexpr uint32_t TILE = TPB * 16u;
     constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
     constexpr uint32_t CAP = TILE + HALO;
@@ -445,7 +446,8 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
     const uint32_t sh = 16u + mis;
-    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (uint32_t tt = blockIdx.x; tt < (ntiles + stride - 1u) / stride; tt += gridDim.x) {
+        const uint32_t t = tt * stride;
         if (tid == 0) s_after = CAP;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;

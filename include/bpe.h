@@ -208,10 +208,10 @@ bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, u
 /* Size of the encoder's word cache for later calls. Words are encoded each
    on its own (page "bpe - GPU BPE Tokenizer Pipeline", "Nedir bu ya?" and
    "Ne Yapar? 1": merges never cross a word start), so every occurrence of a
-   word encodes alike and each distinct word of 2..32 bytes is encoded once
-   per call into a hash table (linear probing over 2^log2_slots slots, at
-   most 8 probes) and its occurrences copy the result after comparing their
-   bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
+   word encodes alike and each distinct word of 2..32 bytes found in every
+   second 4 KiB tile is encoded once per call into a hash table (linear
+   probing over 2^log2_slots slots, at most 8 probes); its occurrences copy
+   the result after comparing their bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
    (one slot per 256 input bytes, 2^10..2^22), 0 (no cache) or 8..24.
    key_bits (at most BPE_CACHE_KEY_BITS): hash bits in a slot's key; fewer
    bits make distinct words share keys, which only sends more words down
