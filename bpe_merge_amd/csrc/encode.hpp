@@ -748,7 +748,18 @@ __global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ t
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const uint32_t c = cnt[t], base = pfx[t], no = ovf_n[t];
         const uint32_t* src = tok32 + (size_t)t * cap;
-        for (uint32_t i = threadIdx.x; i < c; i += TPB) out[base + i] = src[i];
+        {
+            // four loads in flight per thread, then their stores
+            uint32_t i = threadIdx.x;
+            for (; i + 3u * TPB < c; i += 4u * TPB) {
+                const uint32_t a0 = src[i], a1 = src[i + TPB], a2 = src[i + 2u * TPB], a3 = src[i + 3u * TPB];
+                out[base + i] = a0;
+                out[base + i + TPB] = a1;
+                out[base + i + 2u * TPB] = a2;
+                out[base + i + 3u * TPB] = a3;
+            }
+            for (; i < c; i += TPB) out[base + i] = src[i];
+        }
         if (no) {
             const uint32_t* o = ovf + ovf_pos[t];
             for (uint32_t i = threadIdx.x; i < no; i += TPB) out[base + c + i] = o[i];

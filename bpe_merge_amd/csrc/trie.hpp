@@ -315,16 +315,16 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
                     const bool go = base != 0u && q < wend;
                     const uint32_t addr = go ? base + lbyte(q) : 0u;
                     const unsigned long long e2 = da[addr];
-                    if (go && tr_check(e2) == slot + 1u) {
-                        slot = addr;
-                        e = e2;
-                        const uint32_t t1 = tr_tok1(e2);
-                        if (t1) {
-                            best = t1 - 1u;
-                            blen = j + 1u;
-                        }
-                        ++j;
-                    } else {
+                    // a step down the trie, as selects (fewer register copies
+                    // than branches: the walk is bound by vector issue)
+                    const bool adv = go && tr_check(e2) == slot + 1u;
+                    const uint32_t t1 = adv ? tr_tok1(e2) : 0u;
+                    best = t1 ? t1 - 1u : best;
+                    blen = t1 ? j + 1u : blen;
+                    slot = adv ? addr : slot;
+                    e = adv ? e2 : e;
+                    j += adv ? 1u : 0u;
+                    if (!adv) {
                         const bool open = last_open && wend == last_end;
                         if (open && base != 0u && q >= lim) {
                             gp = p;  // the match may go on past the LDS copy
@@ -431,7 +431,18 @@ __global__ __launch_bounds__(TPB) void k_trie_copy(const uint8_t* __restrict__ t
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const uint32_t c = cnt[t], base = pfx[t];
         const uint16_t* src = tok16 + (size_t)t * cap;
-        for (uint32_t i = threadIdx.x; i < c; i += TPB) out[base + i] = src[i];
+        {
+            // four loads in flight per thread, then their stores
+            uint32_t i = threadIdx.x;
+            for (; i + 3u * TPB < c; i += 4u * TPB) {
+                const uint32_t a0 = src[i], a1 = src[i + TPB], a2 = src[i + 2u * TPB], a3 = src[i + 3u * TPB];
+                out[base + i] = a0;
+                out[base + i + TPB] = a1;
+                out[base + i + 2u * TPB] = a2;
+                out[base + i + 3u * TPB] = a3;
+            }
+            for (; i < c; i += TPB) out[base + i] = src[i];
+        }
         const uint32_t no = ovf_n[t];
         if (threadIdx.x == 0 && no) {
             const uint32_t t0 = t * tile, nrel = n - t0;
