@@ -1254,8 +1254,8 @@ bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t*
         hipLaunchKernelGGL(bpek::k_wc_insert<ENC_TPB>,
                            dim3(std::min<uint32_t>((ntiles + stride - 1) / stride, e->insert_grid)), dim3(ENC_TPB),
                            0, s, src, n, ntiles, stride, wc);
-        hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>, dim3(std::min<uint32_t>((slots + WC_FILL_TPB - 1) / WC_FILL_TPB,
-                                                                                  e->fill_grid)),
+        hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>,
+                           dim3(std::min<uint32_t>((slots + 4 * WC_FILL_TPB - 1) / (4 * WC_FILL_TPB), e->fill_grid)),
                            dim3(WC_FILL_TPB), 0, s, src, n, wc, rt, slots);
     }
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));

@@ -306,58 +306,79 @@ __global__ void k_wc_clear(WordCache wc, uint32_t slots) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gridDim.x * blockDim.x) wc.key[i] = 0ull;
 }
 
-// Fill pass: every used slot, one per thread, its key's length of bytes
-// from its position (n bytes of text) encoded in the thread's LDS range of
-// WC_MAXLEN positions. The record gets those bytes (zero past the length),
-// the token ids, the offsets where tokens start and the length; a range
-// past the text's end gets length 0, which no lookup accepts.
+// Fill pass: every used slot's word, its key's length of bytes from its
+// position (n bytes of text), encoded in a thread's LDS range of WC_MAXLEN
+// positions. A workgroup takes chunks of FILL_CHUNK slots, lists the used
+// ones in LDS (a block scan: a used slot is one in five or so, and a wave
+// waits for its slowest lane's word) and encodes them one per thread. The
+// record gets those bytes (zero past the length), the token ids, the
+// offsets where tokens start and the length; a range past the text's end
+// gets length 0, which no lookup accepts.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ text, uint32_t n, WordCache wc,
                                                  RankTable rt, uint32_t slots) {
+    constexpr uint32_t PER = 4;
+    constexpr uint32_t FILL_CHUNK = TPB * PER;
+    static_assert(FILL_CHUNK <= 65536, "chunk offsets fit 16 bits");
     __shared__ uint16_t s_sym[TPB * WC_MAXLEN], s_nx[TPB * WC_MAXLEN], s_rk[TPB * WC_MAXLEN];
+    __shared__ uint16_t s_used[FILL_CHUNK];
+    __shared__ uint32_t s_w[TPB / 64];
     const LdsWord lw{s_sym, s_nx, s_rk};
-    const uint32_t b = threadIdx.x * WC_MAXLEN;
-    for (uint32_t slot = blockIdx.x * TPB + threadIdx.x; slot < slots; slot += gridDim.x * TPB) {
-        const unsigned long long key = wc.key[slot];
-        if (key == 0ull) continue;
-        const uint32_t len = (uint32_t)(key & 63ull);
-        const uint32_t at = wc.pos[slot];
-        uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
-        if (len > WC_MAXLEN || at > n || n - at < len) {
-            rp[WC_LENW] = 0u;
-            continue;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t b = tid * WC_MAXLEN;
+    for (uint32_t c0 = blockIdx.x * FILL_CHUNK; c0 < slots; c0 += gridDim.x * FILL_CHUNK) {
+        uint32_t used = 0u;
+#pragma unroll
+        for (uint32_t k = 0; k < PER; ++k) {
+            const uint32_t slot = c0 + tid * PER + k;
+            used |= (slot < slots && wc.key[slot] != 0ull) ? 1u << k : 0u;
         }
-        const uint8_t* src = text + at;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint32_t v = 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t j = 4u * (uint32_t)k + (uint32_t)u;
-                if (j < len) v |= (uint32_t)src[j] << (8 * u);
+        uint32_t nused;
+        uint32_t off = block_exclusive_sum<TPB>(__popc(used), s_w, &nused);
+        for (uint32_t m = used; m; m &= m - 1u) s_used[off++] = (uint16_t)(tid * PER + (__ffs(m) - 1));
+        lds_barrier();
+        for (uint32_t i = tid; i < nused; i += TPB) {
+            const uint32_t slot = c0 + s_used[i];
+            const uint32_t len = (uint32_t)(wc.key[slot] & 63ull);
+            const uint32_t at = wc.pos[slot];
+            uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
+            if (len > WC_MAXLEN || at > n || n - at < len) {
+                rp[WC_LENW] = 0u;
+                continue;
             }
-            rp[k < 4 ? k : WC_B1 + (k - 4)] = v;
+            const uint8_t* src = text + at;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                uint32_t v = 0u;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t j = 4u * (uint32_t)k + (uint32_t)u;
+                    if (j < len) v |= (uint32_t)src[j] << (8 * u);
+                }
+                rp[k < 4 ? k : WC_B1 + (k - 4)] = v;
+            }
+            for (uint32_t j = 0; j < len; ++j) {
+                s_sym[b + j] = src[j];
+                s_nx[b + j] = (uint16_t)(b + j + 1u);
+            }
+            for (uint32_t j = 0; j + 1u < len; ++j)
+                s_rk[b + j] = rt.bytes[((uint32_t)s_sym[b + j] << 8) | s_sym[b + j + 1u]];
+            while (!merge_iteration(lw, b, b + len, rt)) {
+            }
+            uint16_t* t0 = reinterpret_cast<uint16_t*>(rp + WC_T0);
+            uint16_t* t1 = reinterpret_cast<uint16_t*>(rp + WC_T1);
+            uint32_t m = 0u, c = 0u;
+            for (uint32_t x = b; x < b + len; x = s_nx[x], ++c) {
+                m |= 1u << (x - b);
+                if (c < 16u)
+                    t0[c] = s_sym[x];
+                else
+                    t1[c - 16u] = s_sym[x];
+            }
+            rp[WC_MASKW] = m;
+            rp[WC_LENW] = len;
         }
-        for (uint32_t j = 0; j < len; ++j) {
-            s_sym[b + j] = src[j];
-            s_nx[b + j] = (uint16_t)(b + j + 1u);
-        }
-        for (uint32_t j = 0; j + 1u < len; ++j)
-            s_rk[b + j] = rt.bytes[((uint32_t)s_sym[b + j] << 8) | s_sym[b + j + 1u]];
-        while (!merge_iteration(lw, b, b + len, rt)) {
-        }
-        uint16_t* t0 = reinterpret_cast<uint16_t*>(rp + WC_T0);
-        uint16_t* t1 = reinterpret_cast<uint16_t*>(rp + WC_T1);
-        uint32_t m = 0u, c = 0u;
-        for (uint32_t x = b; x < b + len; x = s_nx[x], ++c) {
-            m |= 1u << (x - b);
-            if (c < 16u)
-                t0[c] = s_sym[x];
-            else
-                t1[c - 16u] = s_sym[x];
-        }
-        rp[WC_MASKW] = m;
-        rp[WC_LENW] = len;
+        lds_barrier();
     }
 }
 
