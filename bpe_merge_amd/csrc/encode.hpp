@@ -524,8 +524,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
     __shared__ uint32_t s_w[TPB / 64];
     __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after, s_nq;
     constexpr uint32_t DLIST = TILE / 2;  // with the cache: the queue's words at s_aux[DLIST..)
-    constexpr uint32_t RETRY = 0x8000u;   // flag on a queued position (positions < CAP < RETRY)
-    static_assert(CAP < RETRY, "positions leave the flag bit free");
+    // flags on a queued position: look the word up from its home slot (a
+    // word of more than WC_SHORT bytes), or from the slot after it (its home
+    // slot holds another key)
+    constexpr uint32_t RETRY = 0x8000u, RETRY_NEXT = 0x4000u;
+    static_assert(CAP < RETRY_NEXT, "positions leave the flag bits free");
     static_assert(DLIST + TILE / 2 <= CAP, "word list and queue fit s_aux");
 
     const uint32_t tid = threadIdx.x;
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         // with the cache: every word of 2 .. WC_SHORT bytes takes its tokens
         // from the first half of its home slot's record, WC_BATCH words per
         // thread with their loads in flight together; the other words are listed
-        // for the queue, with RETRY for those the queue should look up (longer
+        // for the queue, flagged when the queue should look them up (longer
         // cached words, and short ones whose home slot holds another key)
         const uint16_t* ql = s_aux;
         uint32_t nq = nwords;
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                     if (cand[u] && wc_match(key[u], v[u], w[u], len[u], r[u]))
                         put_tokens(q[u], r[u]);
                     else if (cand[u])
-                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (v[u] ? RETRY : 0u));
+                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (v[u] ? RETRY | RETRY_NEXT : 0u));
                     else
                         s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (len[u] <= WC_MAXLEN ? RETRY : 0u));
                 }
@@ -676,13 +679,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                         q = ql[wi];
                         bool cached = false;
                         if (q & RETRY) {
-                            q &= ~RETRY;
+                            const uint32_t from = (q & RETRY_NEXT) ? 1u : 0u;
+                            q &= ~(RETRY | RETRY_NEXT);
                             wend = word_end<TILE>(s_sb, q, last_end);
                             const uint32_t len = wend - q;
                             uint32_t w[8], r[WC_REC];
                             wc_pack_lds(s_txt, q + sh, len, w);
                             const uint32_t h = wc_hash(w, len);
-                            if (wc_lookup(wc, wc_key(wc, h, len), wc_slot(wc, h), w, len, r)) {
+                            if (wc_lookup(wc, wc_key(wc, h, len), (wc_slot(wc, h) + from) & wc.mask, w, len, r)) {
                                 put_tokens(q, r);
                                 cached = true;
                             }
