@@ -495,8 +495,10 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
 
 // ---------------------------------------------------------------- pass 1
 // Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x, ...
-// Outputs for tile t: tok32[t * CAP + i], i < cnt[t], the tokens of the
-// words starting in the tile that end within CAP bytes of its start; for a
+// Outputs for tile t, in its region of CAP words at tok32 + t * CAP: the
+// 16-bit ids of the tokens (i < cnt[t]) of the words starting in the tile
+// that end within CAP bytes of its start, and from word CAP / 2 on the bits
+// marking word starts among them; for a
 // last word running further, its tokens at ovf + ovf_pos[t] (ovf_n[t] of
 // them; NO_OVF / 0 otherwise), encoded in scratch reserved from *scratch_used
 // (capacity scratch_cap positions; past it *err is set and the word is
@@ -744,8 +746,12 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
             s_aux[off++] = s_sym[i];
         }
         __syncthreads();
-        uint32_t* dst = tok32 + (size_t)t * CAP;
-        for (uint32_t i = tid; i < nlds; i += TPB) dst[i] = (uint32_t)s_aux[i] | (((s_ws[i >> 5] >> (i & 31u)) & 1u) << 16);
+        // the tile's region of CAP words: 16-bit ids from its start, the
+        // word-start bits from word CAP / 2
+        uint16_t* d16 = reinterpret_cast<uint16_t*>(tok32 + (size_t)t * CAP);
+        uint32_t* dws = tok32 + (size_t)t * CAP + CAP / 2u;
+        for (uint32_t i = tid; i < nlds; i += TPB) d16[i] = s_aux[i];
+        for (uint32_t i = tid; i < (nlds + 31u) / 32u; i += TPB) dws[i] = s_ws[i];
         if (tid == 0) {
             cnt[t] = nlds;
             ovf_pos[t] = s_ovf_pos;
@@ -761,8 +767,9 @@ __global__ void k_enc_init(uint32_t* status) {
 }
 
 // ---------------------------------------------------------------- pass 3: copy
-// Tile slices to their places in out, then the tokens of a tile's long last
-// word from the overflow area.
+// Tile slices (16-bit ids and word-start bits, as the walk leaves them) to
+// their places in out as 32-bit tokens, then the tokens of a tile's long
+// last word from the overflow area.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ tok32,
                                                   const uint32_t* __restrict__ cnt,
@@ -772,18 +779,20 @@ __global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ t
                                                   uint32_t* __restrict__ out, uint32_t ntiles, uint32_t cap) {
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const uint32_t c = cnt[t], base = pfx[t], no = ovf_n[t];
-        const uint32_t* src = tok32 + (size_t)t * cap;
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(tok32 + (size_t)t * cap);
+        const uint32_t* sws = tok32 + (size_t)t * cap + cap / 2u;
+        auto tok = [&](uint32_t i) -> uint32_t { return (uint32_t)s16[i] | (((sws[i >> 5] >> (i & 31u)) & 1u) << 16); };
         {
-            // four loads in flight per thread, then their stores
+            // four tokens in flight per thread, then their stores
             uint32_t i = threadIdx.x;
             for (; i + 3u * TPB < c; i += 4u * TPB) {
-                const uint32_t a0 = src[i], a1 = src[i + TPB], a2 = src[i + 2u * TPB], a3 = src[i + 3u * TPB];
+                const uint32_t a0 = tok(i), a1 = tok(i + TPB), a2 = tok(i + 2u * TPB), a3 = tok(i + 3u * TPB);
                 out[base + i] = a0;
                 out[base + i + TPB] = a1;
                 out[base + i + 2u * TPB] = a2;
                 out[base + i + 3u * TPB] = a3;
             }
-            for (; i < c; i += TPB) out[base + i] = src[i];
+            for (; i < c; i += TPB) out[base + i] = tok(i);
         }
         if (no) {
             const uint32_t* o = ovf + ovf_pos[t];
