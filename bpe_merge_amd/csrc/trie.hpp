@@ -377,40 +377,63 @@ __global__ __launch_bounds__(TPB) void k_trie_walk(const uint8_t* __restrict__ t
 // ---------------------------------------------------------------- pass 2: scan
 // One workgroup: pfx[t] = tokens of all tiles below t (cnt + ovf_n), and
 // *total = all of them. The arrays hold npad entries (a multiple of 4 TPB;
-// entries past ntiles are ignored); thread i scans entries [i per, i per +
-// per) with 16-byte loads.
+// entries past ntiles are ignored). Wave w owns a contiguous segment; its
+// lanes read consecutive groups of four entries (16-byte loads, coalesced
+// across the wave): a first pass sums the segment, a second writes the
+// prefixes, each group's offset from a wave scan of the group sums.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_trie_scan(const uint32_t* __restrict__ cnt,
                                                    const uint32_t* __restrict__ ovf_n, uint32_t* __restrict__ pfx,
                                                    uint32_t ntiles, uint32_t npad, uint32_t* total) {
-    __shared__ uint32_t s_w[TPB / 64];
-    const uint32_t per = npad / TPB;
-    const uint32_t lo = threadIdx.x * per;
-    const uint4* c4 = reinterpret_cast<const uint4*>(cnt + lo);
-    const uint4* o4 = reinterpret_cast<const uint4*>(ovf_n + lo);
+    constexpr uint32_t NWAVE = TPB / 64u;
+    __shared__ uint32_t s_w[NWAVE];
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint32_t seg = npad / NWAVE;  // a multiple of 256
+    const uint32_t lo = w * seg;
+    auto group = [&](uint32_t i, uint32_t (&g)[4]) {
+        const uint4 c = *reinterpret_cast<const uint4*>(cnt + i);
+        const uint4 o = *reinterpret_cast<const uint4*>(ovf_n + i);
+        g[0] = i < ntiles ? c.x + o.x : 0u;
+        g[1] = i + 1u < ntiles ? c.y + o.y : 0u;
+        g[2] = i + 2u < ntiles ? c.z + o.z : 0u;
+        g[3] = i + 3u < ntiles ? c.w + o.w : 0u;
+    };
     uint32_t sum = 0;
-    for (uint32_t v = 0; v < per / 4u; ++v) {
-        const uint4 c = c4[v], o = o4[v];
-        const uint32_t i = lo + 4u * v;
-        sum += (i < ntiles ? c.x + o.x : 0u) + (i + 1u < ntiles ? c.y + o.y : 0u) +
-               (i + 2u < ntiles ? c.z + o.z : 0u) + (i + 3u < ntiles ? c.w + o.w : 0u);
+#pragma unroll 4
+    for (uint32_t v = 0; v < seg; v += 256u) {
+        uint32_t g[4];
+        group(lo + v + 4u * lane, g);
+        sum += g[0] + g[1] + g[2] + g[3];
     }
-    uint32_t all;
-    uint32_t run = block_exclusive_sum<TPB>(sum, s_w, &all);
-    uint4* p4 = reinterpret_cast<uint4*>(pfx + lo);
-    for (uint32_t v = 0; v < per / 4u; ++v) {
-        const uint4 c = c4[v], o = o4[v];
-        const uint32_t i = lo + 4u * v;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0u) s_w[w] = sum;
+    __syncthreads();
+    uint32_t run = 0, all = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < NWAVE; ++k) {
+        const uint32_t x = s_w[k];
+        run += k < w ? x : 0u;
+        all += x;
+    }
+    for (uint32_t v = 0; v < seg; v += 256u) {
+        const uint32_t i = lo + v + 4u * lane;
+        uint32_t g[4];
+        group(i, g);
+        const uint32_t gs = g[0] + g[1] + g[2] + g[3];
+        uint32_t incl = gs;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (lane >= (uint32_t)o) incl += y;
+        }
         uint4 r;
-        r.x = run;
-        run += i < ntiles ? c.x + o.x : 0u;
-        r.y = run;
-        run += i + 1u < ntiles ? c.y + o.y : 0u;
-        r.z = run;
-        run += i + 2u < ntiles ? c.z + o.z : 0u;
-        r.w = run;
-        run += i + 3u < ntiles ? c.w + o.w : 0u;
-        p4[v] = r;
+        r.x = run + incl - gs;
+        r.y = r.x + g[0];
+        r.z = r.y + g[1];
+        r.w = r.z + g[2];
+        *reinterpret_cast<uint4*>(pfx + i) = r;
+        run += __shfl(incl, 63);
     }
     if (threadIdx.x == 0) *total = all;
 }
