@@ -783,7 +783,9 @@ __global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ t
         const uint32_t* sws = tok32 + (size_t)t * cap + cap / 2u;
         auto tok = [&](uint32_t i) -> uint32_t { return (uint32_t)s16[i] | (((sws[i >> 5] >> (i & 31u)) & 1u) << 16); };
         {
-            // four tokens in flight per thread, then their stores
+            // four tokens in flight per thread, then their stores (consecutive
+            // lanes on consecutive tokens: 16-byte stores of four tokens per
+            // lane measured slower here, the id and bit loads then spread)
             uint32_t i = threadIdx.x;
             for (; i + 3u * TPB < c; i += 4u * TPB) {
                 const uint32_t a0 = tok(i), a1 = tok(i + TPB), a2 = tok(i + 2u * TPB), a3 = tok(i + 3u * TPB);

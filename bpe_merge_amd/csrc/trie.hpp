@@ -439,6 +439,32 @@ __global__ __launch_bounds__(TPB) void k_trie_scan(const uint32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- pass 3: copy
+// Tokens tok(0) .. tok(c - 1) of one tile to out[base ..]: a scalar head up
+// to a 16-byte boundary of out, then four tokens per thread and 16-byte
+// store (two groups in flight), then a scalar tail.
+template <int TPB, typename Tok>
+__device__ __forceinline__ void copy_tokens(uint32_t* __restrict__ out, uint32_t base, uint32_t c, Tok tok) {
+    const uint32_t mis = (uint32_t)(((uintptr_t)(out + base) >> 2) & 3u);  // out is 4-byte aligned
+    const uint32_t head = min(c, (4u - mis) & 3u);
+    if (threadIdx.x < head) out[base + threadIdx.x] = tok(threadIdx.x);
+    const uint32_t ng = (c - head) / 4u;
+    uint4* o4 = reinterpret_cast<uint4*>(out + base + head);
+    uint32_t g = threadIdx.x;
+    for (; g + TPB < ng; g += 2u * TPB) {
+        const uint32_t i = head + 4u * g, k = i + 4u * TPB;
+        const uint4 a = make_uint4(tok(i), tok(i + 1u), tok(i + 2u), tok(i + 3u));
+        const uint4 b = make_uint4(tok(k), tok(k + 1u), tok(k + 2u), tok(k + 3u));
+        o4[g] = a;
+        o4[g + TPB] = b;
+    }
+    for (; g < ng; g += TPB) {
+        const uint32_t i = head + 4u * g;
+        o4[g] = make_uint4(tok(i), tok(i + 1u), tok(i + 2u), tok(i + 3u));
+    }
+    const uint32_t done = head + 4u * ng;
+    if (threadIdx.x < c - done) out[base + done + threadIdx.x] = tok(done + threadIdx.x);
+}
+
 // Tile slices to their places in out (16-bit ids widened to 32 bits); the
 // tokens of a tile's last word past its recorded range are walked again,
 // from global memory, by one thread.
@@ -454,18 +480,7 @@ __global__ __launch_bounds__(TPB) void k_trie_copy(const uint8_t* __restrict__ t
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const uint32_t c = cnt[t], base = pfx[t];
         const uint16_t* src = tok16 + (size_t)t * cap;
-        {
-            // four loads in flight per thread, then their stores
-            uint32_t i = threadIdx.x;
-            for (; i + 3u * TPB < c; i += 4u * TPB) {
-                const uint32_t a0 = src[i], a1 = src[i + TPB], a2 = src[i + 2u * TPB], a3 = src[i + 3u * TPB];
-                out[base + i] = a0;
-                out[base + i + TPB] = a1;
-                out[base + i + 2u * TPB] = a2;
-                out[base + i + 3u * TPB] = a3;
-            }
-            for (; i < c; i += TPB) out[base + i] = src[i];
-        }
+        copy_tokens<TPB>(out, base, c, [&](uint32_t i) -> uint32_t { return src[i]; });
         const uint32_t no = ovf_n[t];
         if (threadIdx.x == 0 && no) {
             const uint32_t t0 = t * tile, nrel = n - t0;

@@ -214,3 +214,27 @@ def test_word_cache_rejects_bad_settings(bpe):
         e.cache(8, 0)
         text = np.frombuffer(b"ab abab ba " * 100, np.uint8)
         assert np.array_equal(_np(e.encode(_dev(text))).astype(np.uint32), oracle.encode(text, [(97, 98)])[1])
+
+
+def test_outputs_at_every_word_offset(bpe):
+    # the copy passes store four tokens at a time from a 16-byte boundary of
+    # the output: views of one buffer starting 0..3 words in, with texts
+    # whose tiles end at every residue of the token count
+    import torch
+    learn = corpus.generate(corpus.CONFIGS[2].scaled(100_000, seed=91))
+    om, _, _ = oracle.train_chunks(learn, 250)
+    big = torch.zeros(300_000, dtype=torch.int32, device="cuda:0")
+    with bpe.Encoder(om) as e, bpe.Trie(om) as tr:
+        for k, n in enumerate((5, 4099, 70_003, 250_001)):
+            text = corpus.generate(corpus.CONFIGS[2].scaled(n, seed=930 + k))
+            d = _dev(text)
+            _, oe = oracle.encode(text, om)
+            ot = oracle.trie_encode(text, om)
+            for off in range(4):
+                _say("outputs at offset %d n=%d" % (off, n))
+                big.fill_(-1)
+                got = _np(e.encode(d, out=big[off:])).astype(np.uint32)
+                assert np.array_equal(got, oe), (off, n)
+                assert int(big[off + oe.size:].max()) == -1 if off + oe.size < big.numel() else True
+                got = _np(tr.encode(d, out=big[off:])).astype(np.uint32)
+                assert np.array_equal(got, ot.astype(np.uint32)), (off, n)
