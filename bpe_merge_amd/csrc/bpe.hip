@@ -1197,11 +1197,16 @@ constexpr size_t ENC_SCRATCH_MAX = size_t(1) << 24;  // positions of long words 
 
 size_t enc_scratch_cap(size_t n) { return std::min(n, ENC_SCRATCH_MAX); }
 
-// Slots of the word cache for n bytes (0: no cache). Automatic: one slot
-// per 256 input bytes, a power of two in [2^10, 2^22].
+// Slots of the word cache for n bytes (0: no cache). Automatic: none below
+// 1 MiB (the walk is bound by launches there, and the cache's three kernels
+// cost more than they save: 64 KiB, 0.094 ms without, 0.124 with); above,
+// one slot per 256 input bytes, a power of two in [2^18, 2^22] (a table
+// too small for a text's distinct words fills up: 16 MiB of Turkish-like
+// text, 2^16 slots 0.86 ms, 2^18 0.61 ms; 256 MiB, 2^20 1.91 ms, 2^22 1.95).
 uint32_t enc_wc_log2(const bpe_encoder* e, size_t n) {
     if (e->wc_log2 != BPE_CACHE_AUTO) return e->wc_log2;
-    uint32_t l = 10;
+    if (n < (size_t(1) << 20)) return 0;
+    uint32_t l = 18;
     while (l < WC_AUTO_MAX_LOG2 && (size_t(1) << l) < n / 256) ++l;
     return l;
 }

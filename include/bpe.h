@@ -211,8 +211,9 @@ bpe_status bpe_encoder_profile(bpe_encoder *e, const uint8_t *bytes, size_t n, u
    word encodes alike and each distinct word of 2..32 bytes found in every
    second 4 KiB tile is encoded once per call into a hash table (linear
    probing over 2^log2_slots slots, at most 8 probes); its occurrences copy
-   the result after comparing their bytes with the cached word's. log2_slots: BPE_CACHE_AUTO
-   (one slot per 256 input bytes, 2^10..2^22), 0 (no cache) or 8..24.
+   the result after comparing their bytes with the cached word's. log2_slots:
+   BPE_CACHE_AUTO (none below 1 MiB of input, else one slot per 256 input
+   bytes, 2^18..2^22), 0 (no cache) or 8..24.
    key_bits (at most BPE_CACHE_KEY_BITS): hash bits in a slot's key; fewer
    bits make distinct words share keys, which only sends more words down
    the uncached path (a testing aid). Tokens never depend on either
