@@ -10,14 +10,16 @@
 // creates a pair of lower rank than its own, and words never interact. One
 // pass over the text then replaces one pass per merge. The decomposition
 // is the inference kernels' (trie.hpp): a workgroup takes a tile and owns
-// the words starting in it, one-byte words are final at once, the longer
-// ones are taken by the lanes of a wave from a queue. A lane runs one
-// iteration of its word per round: find the lowest-rank pair on the word's
-// live list, merge it everywhere in the word, look up the ranks of the
-// pairs the merges made. Ranks come from a hash table of the list (pair ->
-// first rank of that pair; a repeated pair never occurs again after its
-// first merge, so later copies are dead). The output is the training
-// format: id | 0x10000 on the first token of each word.
+// the words starting in it, one-byte words are final at once. Since a word's
+// tokens depend on its bytes alone, the distinct words are encoded once,
+// into a word cache (below), and the walk copies their tokens; the words
+// the cache does not hold are taken by the lanes of a wave from a queue. A
+// lane runs one iteration of its word per round: find the lowest-rank pair
+// on the word's live list, merge it everywhere in the word, look up the
+// ranks of the pairs the merges made. Ranks come from a hash table of the
+// list (pair -> first rank of that pair; a repeated pair never occurs again
+// after its first merge, so later copies are dead). The output is the
+// training format: id | 0x10000 on the first token of each word.
 #pragma once
 
 #include <hip/hip_runtime.h>
