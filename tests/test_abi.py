@@ -175,3 +175,16 @@ def test_trie_and_encoder_encode_argument_validation(bpe):
     assert lib.bpe_encoder_cache(None, 0xFFFFFFFF, 32) == bpe.EINVAL
     lib.bpe_trie_free(None)
     lib.bpe_encoder_free(None)
+
+
+def test_bench_refuses_more_than_one_gpu_before_touching_one():
+    # the measurement is one GPU's: --gpus N > 1 (or a multi-rank launch)
+    # exits with a message, before importing torch or the library
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           timeout=60, env={**os.environ, **env})
+        assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == "", (args, env, r.stderr)
