@@ -238,3 +238,18 @@ def test_outputs_at_every_word_offset(bpe):
                 assert int(big[off + oe.size:].max()) == -1 if off + oe.size < big.numel() else True
                 got = _np(tr.encode(d, out=big[off:])).astype(np.uint32)
                 assert np.array_equal(got, ot.astype(np.uint32)), (off, n)
+
+
+def test_encoder_reports_long_words_past_its_scratch(bpe):
+    # one word longer than the 2^24 positions of scratch a call may use for
+    # words past a tile's LDS copy: BPE_ENOMEM (the walk skips the word, so
+    # nothing is written past the scratch), and the encoder stays usable
+    merges = [(97, 97), (256, 256)]
+    text = np.full((1 << 24) + 5000, 97, np.uint8)
+    small = np.frombuffer(b"aaaa ab " * 500, np.uint8)
+    with bpe.Encoder(merges) as e:
+        _say("encoder scratch overflow")
+        with pytest.raises(bpe.BpeError) as ei:
+            e.encode(_dev(text))
+        assert ei.value.status == bpe.ENOMEM
+        assert np.array_equal(_np(e.encode(_dev(small))).astype(np.uint32), oracle.encode(small, merges)[1])
