@@ -184,13 +184,14 @@ bpe_status bpe_encoder_build(const bpe_merge *merges, uint32_t n_merges, bpe_enc
 /* Encode bytes[0..n) (host or device) on stream (a hipStream_t, or NULL for
    the encoder's own). tokens (host or device, capacity tokens_cap >= n, or
    NULL for the count only) receive the tokens, *n_tokens their count.
-   With the word cache (bpe_encoder_cache; on by default) three kernels
-   first collect the distinct words of 2..32 bytes and encode each once;
-   then three kernels (walk, scan, copy), a wait for the total and a sized
-   copy for host tokens. Device buffers are pooled in the encoder (about 6
-   bytes per input byte, the cache's 140 bytes per slot, plus scratch of 12
-   bytes per position for words that do not fit a tile's LDS, at most 2^24
-   positions per call), so calls on one encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
+   With the word cache (bpe_encoder_cache; on by default from 1 MiB) three
+   kernels first collect the distinct words of 2..32 bytes of every second
+   4 KiB tile and encode each once; then three kernels (walk, scan, copy),
+   a wait for the total and a sized copy for host tokens. Device buffers
+   are pooled in the encoder (about 5 bytes per input byte, the cache's 140
+   bytes per slot, plus scratch of 12 bytes per position for words that do
+   not fit a tile's LDS, at most 2^24 positions per call), so calls on one
+   encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
    NULL bytes with n > 0, n > BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM
    (also: words past a tile's LDS longer than the scratch in total),
    BPE_EHIP. */
