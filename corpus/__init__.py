@@ -23,8 +23,15 @@ _LIB_PATH = os.path.join(_HERE, "libcorpus.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile gen.c into libcorpus.so with gcc (host code only)."""
+def build(force: bool = True, sanitize: bool = False, out_dir: str | None = None) -> str:
+    """Compile gen.c into libcorpus.so with gcc (host code only).
+
+    With ``sanitize``, build the sanitizer checker that links gen.c with the
+    C oracle under AddressSanitizer and UndefinedBehaviorSanitizer (see
+    ``oracle.build``) and return the executable's path."""
+    if sanitize:
+        import oracle
+        return oracle.build(force=force, sanitize=True, out_dir=out_dir)
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])

@@ -39,8 +39,27 @@ BASE = 256
 MAX_MERGES = 0x10000 - BASE
 
 
-def build(force: bool = True) -> str:
-    """Compile bpe_oracle.c into liboracle.so with gcc."""
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+_CHECK_SRC = os.path.join(_HERE, "sanitize_check.c")
+_GEN_SRC = os.path.join(os.path.dirname(_HERE), "corpus", "gen.c")
+
+
+def build(force: bool = True, sanitize: bool = False, out_dir: str | None = None) -> str:
+    """Compile bpe_oracle.c into liboracle.so with gcc.
+
+    With ``sanitize``, build instead the executable sanitize_check (the C
+    oracle, the corpus generator and sanitize_check.c, which runs the
+    brute-force pins through them) with AddressSanitizer and
+    UndefinedBehaviorSanitizer, into ``out_dir`` (default: this directory),
+    and return its path."""
+    if sanitize:
+        exe = os.path.join(out_dir or _HERE, "sanitize_check")
+        if force or not os.path.exists(exe):
+            tmp = exe + ".tmp%d" % os.getpid()
+            subprocess.check_call(["gcc", "-O1", "-std=c11", "-Wall", *SANITIZE_FLAGS, "-o", tmp, _CHECK_SRC, _SRC,
+                                   _GEN_SRC, "-lm"])
+            os.replace(tmp, exe)
+        return exe
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", "-o", tmp, _SRC])
