@@ -64,14 +64,25 @@
 #define O_BASE 256u
 #define O_MAX_MERGES (0x10000u - O_BASE)
 
+/* The page's byte classes ("Satir Satir Analiz 1)") as a table filled from
+   the class members: ASCII letters and every byte >= 0x80 (UTF-8 letters stay
+   letters) 0, ASCII digits 1, space 2, newline 4, all other bytes 3. */
+static uint8_t class_of[256];
+static int classes_ready;
+
+static void fill_classes(void) {
+    for (int b = 0; b < 256; b++) class_of[b] = 3;
+    for (int b = 0; b < 26; b++) class_of['A' + b] = class_of['a' + b] = 0;
+    for (int b = 0x80; b < 256; b++) class_of[b] = 0;
+    for (int b = 0; b < 10; b++) class_of['0' + b] = 1;
+    class_of[' '] = 2;
+    class_of['\n'] = 4;
+    classes_ready = 1;
+}
+
 uint32_t oracle_char_class(uint32_t x) {
-    if (x == 0x0A) return 4;
-    if (x == 0x20) return 2;
-    if (x >= 0x30 && x <= 0x39) return 1;
-    if (x >= 0x80) return 0;
-    if (x >= 0x61 && x <= 0x7A) return 0;
-    if (x >= 0x41 && x <= 0x5A) return 0;
-    return 3;
+    if (!classes_ready) fill_classes();
+    return x < 256 ? class_of[x] : 0;
 }
 
 void oracle_tag(const uint8_t *b, uint64_t n, uint32_t *s) {

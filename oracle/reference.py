@@ -43,22 +43,23 @@ BASE = 256            # byte-level base vocabulary: new ids start here
 MAX_MERGES = 0x10000 - BASE   # ids must fit in 16 bits
 
 
+# Byte classes of the page's char_class ("Satir Satir Analiz 1)"), as sets:
+# letters are the ASCII letters and every byte of a multi-byte UTF-8
+# sequence (so UTF-8 letters stay letters); 3 is everything not listed.
+_CLASS_MEMBERS = {
+    0: set(range(ord("A"), ord("Z") + 1)) | set(range(ord("a"), ord("z") + 1)) | set(range(0x80, 0x100)),
+    1: set(range(ord("0"), ord("9") + 1)),
+    2: {ord(" ")},
+    4: {ord("\n")},
+}
+
+
 def char_class(x: int) -> int:
-    """Character class of one byte, as the page's char_class prints it:
-    newline 4, space 2, ASCII digit 1, any byte >= 0x80 and ASCII letters 0,
-    everything else 3."""
-    if x == 0x0A:
-        return 4
-    if x == 0x20:
-        return 2
-    if 0x30 <= x <= 0x39:
-        return 1
-    if x >= 0x80:
-        return 0
-    if 0x61 <= x <= 0x7A:
-        return 0
-    if 0x41 <= x <= 0x5A:
-        return 0
+    """Character class of one byte: newline 4, space 2, ASCII digit 1, any
+    byte >= 0x80 and ASCII letters 0, everything else 3."""
+    for cls, members in _CLASS_MEMBERS.items():
+        if x in members:
+            return cls
     return 3
 
 

@@ -13,22 +13,17 @@ BASE = 256
 
 
 def byte_class(x: int) -> int:
-    """Class of a byte in the unsigned-wrap form the page prints for
-    char_class: (tok - base) <= range as a 32-bit unsigned comparison."""
-    u = lambda v: v & 0xFFFFFFFF  # noqa: E731
-    if x == 0x0A:
-        return 4
-    if x == 0x20:
-        return 2
-    if u(x - 0x30) <= 9:
+    """Class of a byte as the page states it for char_class ("Satir Satir
+    Analiz 1)"): a line break is 4, a space 2, an ASCII digit 1, an ASCII
+    letter or any byte of a multi-byte UTF-8 sequence (0x80 and above) 0,
+    anything else 3. Written with Python's character predicates, not with
+    the oracle's range tests."""
+    c = chr(x)
+    if x >= 0x80 or (c.isascii() and c.isalpha()):
+        return 0
+    if c.isascii() and c.isdigit():
         return 1
-    if x >= 0x80:
-        return 0
-    if u(x - 0x61) <= 25:
-        return 0
-    if u(x - 0x41) <= 25:
-        return 0
-    return 3
+    return {" ": 2, "\n": 4}.get(c, 3)
 
 
 CLASS = np.array([byte_class(b) for b in range(256)], dtype=np.int8)

@@ -25,9 +25,9 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json
 
 # ---------------------------------------------------------------- classes
 
-def test_char_class_matches_printed_unsigned_wrap_form():
-    # the page prints char_class with unsigned (tok - base) <= range tests;
-    # the oracles write the same classes as plain range comparisons
+def test_char_class_matches_the_stated_classes():
+    # the class the page states for every byte, written with Python's
+    # character predicates (tests/checks.py), against both oracles' tables
     for b in range(256):
         assert ref.char_class(b) == byte_class(b), b
         assert oracle.char_class(b) == byte_class(b), b
