@@ -957,7 +957,10 @@ bpe_status bpe_trie_build(const bpe_merge* merges, uint32_t n_merges, bpe_trie**
     }
     t->walk_grid = cus * per_cu;
     t->copy_grid = cus * 8;
-    if (hipStreamCreateWithFlags(&t->stream, hipStreamNonBlocking) != hipSuccess) {
+    // a blocking stream: a call with no stream of its own is then ordered
+    // after work on the legacy default stream (the producer of its input,
+    // the last user of its output)
+    if (hipStreamCreate(&t->stream) != hipSuccess) {
         (void)hipGetLastError();
         set_err("hipStreamCreate failed");
         return fail(BPE_EHIP);
@@ -1353,7 +1356,8 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
     e->copy_grid = cus * 8;
     e->rt_mask = uint32_t(slots - 1);
     e->rt_probes = probes;
-    if (hipStreamCreateWithFlags(&e->stream, hipStreamNonBlocking) != hipSuccess ||
+    // blocking, as the trie's: ordered after the legacy default stream
+    if (hipStreamCreate(&e->stream) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&e->rt), slots * sizeof(unsigned long long)) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&e->status), 4 * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&e->rt_bytes), 65536 * sizeof(uint16_t)) != hipSuccess ||
