@@ -14,8 +14,9 @@
 //      sums these changes in an LDS table and adds the sums to the global
 //      table at the end.
 // The page runs these as separate dispatches with a three-pass scan; here
-// the scan is a single-pass decoupled look-back over 8192-symbol tiles, so
-// the symbols are read once and written once per iteration.
+// the scan is a single-pass decoupled look-back over tiles of 16384 symbols
+// (1024-thread workgroups) or 8192 (512-thread workgroups, on small
+// corpora), so the symbols are read once and written once per iteration.
 #pragma once
 
 #include "kernels.hpp"
@@ -493,8 +494,8 @@ constexpr int LB_WIN = 2 * 64 * LB_PL;
 constexpr int WAIT_VM7 = 0x0F77;
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 
-// One persistent pass per iteration. Workgroups take 8192-symbol tiles from
-// a counter, in order, so every tile a look-back waits for is held by a
+// One persistent pass per iteration. Workgroups take tiles from a counter,
+// in order, so every tile a look-back waits for is held by a
 // running workgroup that has already published or is about to publish its
 // aggregate.
 //

@@ -81,7 +81,8 @@ typedef struct {
                                 0 = automatic; otherwise 10..30                       */
     uint32_t flags;          /* reserved, must be 0                                    */
     void *stream;            /* hipStream_t all work is ordered on; NULL = the state
-                                creates and owns a non-default stream                  */
+                                creates and owns a blocking stream (ordered after the
+                                legacy default stream)                                 */
     void *workspace;         /* device memory of at least bpe_workspace_bytes();
                                 NULL = the state allocates its own                     */
     size_t workspace_bytes;  /* size of workspace (ignored when workspace is NULL)     */
@@ -94,7 +95,11 @@ typedef struct bpe_state bpe_state;
 size_t bpe_workspace_bytes(size_t n, const bpe_config *cfg);
 
 /*
- * Train up to n_merges merges on bytes[0..n) and return the result.
+ * Train up to n_merges merges on bytes[0..n) and return the result: the loop
+ * of "Nedir bu ya?" (most frequent adjacent pair -> one new symbol) run
+ * n_merges times over the symbols tagged as in "Ne Yapar? 1", each
+ * iteration the training pipeline of the page head (count, deterministic
+ * maximum, merge, prefix-scan compaction of "Ne Yapar? 3").
  *   merges    out, n_merges entries (host or device); merge i creates id 256 + i
  *   n_done    out (host): merges produced; < n_merges if no pair was left
  *   tokens    out (host or device) or NULL: final symbols, id | tag
@@ -109,9 +114,11 @@ bpe_status bpe_train(const uint8_t *bytes, size_t n, uint32_t n_merges, const bp
                      bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
                      size_t *n_tokens);
 
-/* Create a training state: tag bytes[0..n) (n >= 1) into symbols and count
-   the pairs of iteration 0. Asynchronous on the state's stream; bytes must
-   stay valid until the next synchronising call (bpe_sync, bpe_step, ...). */
+/* Create a training state: tag bytes[0..n) (n >= 1) into symbols with the
+   character classes of "Ne Yapar? 1" ("Satir Satir Analiz 1)") and count the
+   pairs of iteration 0 into the global pair table ("Ne Yapar? 2").
+   Asynchronous on the state's stream; bytes must stay valid until the next
+   synchronising call (bpe_sync, bpe_step, ...). */
 bpe_status bpe_init(const uint8_t *bytes, size_t n, const bpe_config *cfg, bpe_state **out);
 
 /* Enqueue up to n_merges more iterations without waiting and without any
@@ -123,15 +130,20 @@ bpe_status bpe_run(bpe_state *s, uint32_t n_merges);
    Returns BPE_ETABLE / BPE_ESTATE if the device reported an error. */
 bpe_status bpe_sync(bpe_state *s, uint32_t *n_done);
 
-/* One iteration, synchronously: *out = the merge made. BPE_DONE (and *out
-   untouched) when no countable pair is left. */
+/* One iteration of "Nedir bu ya?", synchronously: *out = the merge made.
+   BPE_DONE (and *out untouched) when no countable pair is left;
+   BPE_EIDSPACE once all BPE_MAX_MERGES ids are used. */
 bpe_status bpe_step(bpe_state *s, bpe_merge *out);
 
 /* Copy the merges produced so far (up to cap) to out; *n_out = how many exist. */
 bpe_status bpe_merges(bpe_state *s, bpe_merge *out, uint32_t cap, uint32_t *n_out);
 
-/* Copy the current symbol sequence to out; *n_out = its length. With out NULL
-   or cap 0 only the length is returned; cap below the length is BPE_EINVAL. */
+/* Copy the current symbol sequence to out; *n_out = its length. After the
+   last merge these are the training corpus's tokens: the sequence the
+   merges of "Nedir bu ya?" have rewritten, each symbol id | 0x10000 where
+   a word starts ("Ne Yapar? 1"; a merged symbol keeps its left part's bit,
+   "Ne Yapar? 3"). With out NULL or cap 0 only the length is returned; cap
+   below the length is BPE_EINVAL. */
 bpe_status bpe_tokens(bpe_state *s, uint32_t *out, size_t cap, size_t *n_out);
 
 /* Sequence length before each merge so far, then the current length:
