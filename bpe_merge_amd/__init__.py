@@ -28,6 +28,7 @@ ID_MASK = 0xFFFF
 BASE_VOCAB = 256
 MAX_MERGES = 65280
 MAX_BYTES = 0x7FFFFFFF
+FLAG_OVERSUBSCRIBE = 1  # testing aid: merge passes with 4x the resident workgroups
 
 
 class BpeError(RuntimeError):
@@ -98,10 +99,10 @@ def _check(st: int, where: str) -> int:
     return st
 
 
-def _config(table_log2=None, stream=None, workspace=None) -> Config:
+def _config(table_log2=None, stream=None, workspace=None, flags=0) -> Config:
     c = Config()
     c.table_log2 = int(table_log2 or 0)
-    c.flags = 0
+    c.flags = int(flags)
     c.stream = stream
     if workspace is not None:
         c.workspace = workspace.data_ptr()
@@ -135,7 +136,7 @@ def _workspace(n, table_log2, device):
     return ws[shift: shift + nbytes]
 
 
-def train(data, n_merges: int, table_log2: int | None = None):
+def train(data, n_merges: int, table_log2: int | None = None, flags: int = 0):
     """bpe_train on a uint8 CUDA tensor.
 
     Returns (merges, tokens): int32 CUDA tensors of shape [k, 3] (left,
@@ -152,7 +153,7 @@ def train(data, n_merges: int, table_log2: int | None = None):
     if n == 0:
         return merges[:0], tokens[:0]
     ws = _workspace(n, table_log2, dev)
-    cfg = _config(table_log2, _stream_handle(dev), ws)
+    cfg = _config(table_log2, _stream_handle(dev), ws, flags)
     n_done = _u32(0)
     n_tok = _sz(0)
     st = _lib.bpe_train(data.data_ptr(), n, n_merges, ctypes.byref(cfg), merges.data_ptr(), ctypes.byref(n_done),
@@ -348,7 +349,7 @@ class Trie:
 class State:
     """bpe_init ... bpe_free on a uint8 CUDA tensor, with a torch workspace."""
 
-    def __init__(self, data, table_log2: int | None = None):
+    def __init__(self, data, table_log2: int | None = None, flags: int = 0):
         torch = _torch()
         if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
             raise TypeError("data must be a uint8 CUDA tensor")
@@ -356,7 +357,7 @@ class State:
         self.n = self.data.numel()
         self.device = self.data.device
         self.ws = _workspace(self.n, table_log2, self.device)
-        self.cfg = _config(table_log2, _stream_handle(self.device), self.ws)
+        self.cfg = _config(table_log2, _stream_handle(self.device), self.ws, flags)
         self._h = _vp(None)
         _check(_lib.bpe_init(self.data.data_ptr(), self.n, ctypes.byref(self.cfg), ctypes.byref(self._h)),
                "bpe_init")

@@ -125,8 +125,8 @@ bool config_ok(size_t n, const bpe_config* cfg) {
         return false;
     }
     if (cfg) {
-        if (cfg->flags != 0) {
-            set_err("bpe_config.flags must be 0");
+        if (cfg->flags & ~uint32_t(BPE_FLAG_OVERSUBSCRIBE)) {
+            set_err("bpe_config.flags holds an unknown bit (0x%x)", cfg->flags);
             return false;
         }
         if (cfg->table_log2 && (cfg->table_log2 < 10 || cfg->table_log2 > 30)) {
@@ -178,14 +178,18 @@ struct bpe_state {
 
 namespace {
 
-void launch_merge(bpe_state* s) {
+// The merge pass of iteration it (one launch per iteration; a pass after
+// training has stopped does nothing). Plain launches: no workgroup of the
+// pass waits for one that has not started, so the grid need not be
+// resident all at once.
+void launch_merge(bpe_state* s, uint32_t it) {
     if (s->merge_tpb == MERGE_TPB_BIG)
         hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG), 0,
-                           s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
                            s->merges);
     else
         hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_SMALL),
-                           0, s->stream, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           0, s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
                            s->merges);
 }
 
@@ -193,10 +197,6 @@ void launch_force(bpe_state* s) {
     hipLaunchKernelGGL(bpek::k_force, dim3(1), dim3(64), 0, s->stream, s->ctl, s->gtable(), s->sweep, s->fpairs);
 }
 
-bpe_status launch_iteration(bpe_state* s) {
-    launch_merge(s);
-    return BPE_OK;
-}
 
 bpe_status read_ctl(bpe_state* s, Ctl* h) {
     HIP_TRY(hipStreamSynchronize(s->stream));
@@ -235,13 +235,15 @@ bpe_status event_pool(int device, size_t count, std::vector<hipEvent_t>** out) {
     return BPE_OK;
 }
 
-bpe_status enqueue_run(bpe_state* s, uint32_t n_merges) {
+// Iterations requested .. requested + n_merges - 1, which the passes are
+// told; once training stops (no pair left) the later passes do nothing.
+bpe_status enqueue_run(bpe_state* s, uint32_t n_merges, uint32_t* first) {
     if (size_t(s->requested) + n_merges > BPE_MAX_MERGES) {
         set_err("%u + %u merges exceed the id space (%u merges)", s->requested, n_merges, BPE_MAX_MERGES);
         return BPE_EIDSPACE;
     }
+    *first = s->requested;
     s->requested += n_merges;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
     return BPE_OK;
 }
 
@@ -363,9 +365,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, tag_grid_bound(n)));
     s->fill_grid = cus * 4;
-    // every merge workgroup takes part in a sweep of the table and in its
-    // barrier, so the grid must fit in the sweep maxima
-    if (s->merge_grid > int(bpek::SWEEP_MAX_BLOCKS)) s->merge_grid = int(bpek::SWEEP_MAX_BLOCKS);
+    // testing aid: four times the workgroups that can be resident at once,
+    // so that most of them start only when earlier ones have finished
+    if (cfg && (cfg->flags & BPE_FLAG_OVERSUBSCRIBE)) s->merge_grid = int(size_t(cus) * per_cu * 4);
 
     // input bytes: device memory is read in place, host memory is uploaded
     // into the second symbol buffer first (4n bytes hold n bytes)
@@ -378,9 +380,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         }
         src = reinterpret_cast<const uint8_t*>(s->sym1);
     }
-    hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s->stream,
                        reinterpret_cast<unsigned long long*>(s->sweep), sizeof(bpek::Sweep) / 8, 0ull);
+    hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->table, size_t(s->slots()),
                        bpek::GT_EMPTY);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->status,
@@ -407,9 +409,10 @@ bpe_status bpe_run(bpe_state* s, uint32_t n_merges) {
         return BPE_ESTATE;
     }
     HIP_TRY(hipSetDevice(s->device));
-    bpe_status st = enqueue_run(s, n_merges);
+    uint32_t it0 = 0;
+    bpe_status st = enqueue_run(s, n_merges, &it0);
     if (st != BPE_OK) return st;
-    for (uint32_t i = 0; i < n_merges; ++i) launch_iteration(s);
+    for (uint32_t i = 0; i < n_merges; ++i) launch_merge(s, it0 + i);
     HIP_TRY(hipGetLastError());
     return BPE_OK;
 }
@@ -449,8 +452,7 @@ bpe_status bpe_step(bpe_state* s, bpe_merge* out) {
         return BPE_EIDSPACE;
     }
     s->requested = before.k + 1;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
-    launch_iteration(s);
+    launch_merge(s, before.k);
     HIP_TRY(hipGetLastError());
     Ctl after;
     st = read_ctl(s, &after);
@@ -570,12 +572,13 @@ bpe_status bpe_profile(bpe_state* s, uint32_t n_merges, bpe_profile_result* res,
     uint32_t sweeps0 = 0, sweeps1 = 0;
     HIP_TRY(hipStreamSynchronize(s->stream));
     HIP_TRY(hipMemcpy(&sweeps0, &s->sweep->sweeps, 4, hipMemcpyDeviceToHost));
-    st = enqueue_run(s, n_merges);
+    uint32_t it0 = 0;
+    st = enqueue_run(s, n_merges, &it0);
     if (st != BPE_OK) return st;
     std::vector<hipEvent_t>& e = *ev;
     HIP_TRY(hipEventRecord(e[0], s->stream));
     for (uint32_t i = 0; i < n_merges; ++i) {
-        launch_merge(s);
+        launch_merge(s, it0 + i);
         HIP_TRY(hipEventRecord(e[size_t(i) + 1], s->stream));
     }
     HIP_TRY(hipGetLastError());
@@ -635,10 +638,9 @@ bpe_status bpe_replay(bpe_state* s, const bpe_merge* merges, uint32_t k) {
     HIP_TRY(hipMemcpyAsync(s->fpairs + 2 * size_t(m0), pairs.data(), 4 * pairs.size(), hipMemcpyHostToDevice,
                            s->stream));
     s->requested = m0 + k;
-    hipLaunchKernelGGL(bpek::k_set_limit, dim3(1), dim3(64), 0, s->stream, s->ctl, s->sweep, s->requested);
     for (uint32_t i = 0; i < k; ++i) {
         launch_force(s);
-        launch_merge(s);
+        launch_merge(s, m0 + i);
     }
     HIP_TRY(hipGetLastError());
     st = read_ctl(s, &h);  // also keeps pairs alive until the copy has run

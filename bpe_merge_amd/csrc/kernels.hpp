@@ -39,17 +39,20 @@ constexpr uint32_t EMPTY = 0xFFFFFFFFu;  // empty key (the pair 65535,65535 is n
 constexpr uint32_t BASE = 256u;
 
 constexpr uint32_t ERR_TABLE = 1u;  // the global pair table is full
-constexpr uint32_t ERR_SPIN = 2u;   // a look-back wait exceeded its bound
+// A bounded wait of the merge pass exceeded its bound: the look-back of the
+// scan (for a lower tile's status) or a table sweep (for the maximum of all
+// chunks). Both wait only for work a workgroup that is already running has
+// taken on, so only a fault can make them fail.
+constexpr uint32_t ERR_SPIN = 2u;
 
 constexpr uint32_t LDS_PROBES = 16;        // buckets probed before giving up on an LDS table
 constexpr uint32_t GT_PROBES = 4096;       // slots probed before giving up on the global table
-constexpr uint32_t SPIN_LIMIT = 1u << 22;  // polls of one look-back before giving up
+constexpr uint32_t SPIN_LIMIT = 1u << 22;  // polls of one wait before giving up
 
 // Device-resident control block; one per training state.
 struct alignas(64) Ctl {
     uint32_t k;           // merges chosen so far
     uint32_t m;           // merges applied so far (m == k between iterations)
-    uint32_t limit;       // iterations allowed in total
     uint32_t done;        // 1 once no pair is left (or after a device error)
     uint32_t err;         // ERR_* bits
     uint32_t n[2];        // symbol counts; n[m & 1] is the current one
@@ -70,35 +73,50 @@ struct alignas(64) Ctl {
 // involves the newest id), and a new pair whose count the merge pass lifts
 // across theta is appended by the add that does it. When the list's
 // maximum falls below theta (or the list overflowed), the iteration sweeps
-// the whole table (every workgroup a share, one grid-wide barrier) and
-// rebuilds the list with theta = max - (max >> shift), the shift adapted
-// to the list sizes seen.
+// the whole table and rebuilds the list with theta = max - (max >> shift),
+// the shift adapted to the list sizes seen.
 //
-// Every workgroup of a merge launch makes the same selection at its start,
-// from the list and the table as the previous launch left them; no
-// workgroup changes the table until all have made theirs (started[]).
-// Counters are kept per iteration parity and cleared one iteration ahead,
-// so none needs a reset at the end of a launch.
-constexpr uint32_t SWEEP_MAX_BLOCKS = 1024;  // workgroups that can take part in a sweep
-constexpr uint32_t NO_ITER = 0xFFFFFFFFu;
+// The workgroup that draws the pass's first ticket from the tile counter
+// (so it is running; ticket 0 is this job, not a tile) selects the merge:
+// the maximum over the list, or a mark that the pass sweeps, or the pair a
+// replay lists, before it issues any load of its own tile, while the other
+// workgroups load theirs. It publishes the result to PUB_COPIES copies
+// (value, then epoch = iteration + 1), one read by each group of
+// workgroups, so that their polls do not pile up on one address. No workgroup changes the
+// table before it has read the publication, which follows every read of the
+// selection, and a workgroup that starts late reads only the publication:
+// no wait in the pass is on a workgroup that has not started, so the pass
+// needs no co-residency of its grid. A sweep is split into chunks of the
+// table that running workgroups claim from a counter; the workgroup that
+// finishes the last chunk of the maximum publishes it (spub), and the
+// candidates are collected from chunks claimed the same way. Counters are
+// kept per iteration parity and cleared one iteration ahead.
 constexpr uint32_t CAND_MAX = 16384;
 constexpr uint32_t CAND_TARGET = 2048;  // list size the shift steers towards
 constexpr uint32_t SHIFT_DEFAULT = 3;   // theta = 7/8 of the maximum
 constexpr uint32_t SHIFT_MAX = 16;
+constexpr uint32_t SWEEP_CHUNK = 16384;           // table slots per sweep chunk
+constexpr unsigned long long SEL_SWEEP = ~0ull;  // the pass sweeps (never a packed maximum)
+constexpr uint32_t PUB_COPIES = 256;              // copies of a published merge
 struct Sweep {
-    unsigned long long bmax[SWEEP_MAX_BLOCKS];  // per-workgroup maxima of a sweep
-    unsigned long long best;                    // the replayed merge, packed
-    uint32_t iter;                              // the iteration the next launch runs (NO_ITER: none)
-    uint32_t force;                             // 1 + the iteration whose merge is best (0: none)
-    uint32_t theta;                             // the list's threshold
-    uint32_t shift;                             // of the last sweep (0: none yet)
-    uint32_t cand_n;                            // entries appended (above CAND_MAX: overflowed)
-    uint32_t cand_ok;                           // the list holds every slot with count >= theta
-    uint32_t started[2];                        // workgroups past their selection, per parity
-    uint32_t arrived[2];                        // workgroups at the sweep barrier, per parity
-    uint32_t sweeps;                            // iterations that swept the table
-    uint32_t pad;
-    uint32_t cand[CAND_MAX];  // slot indexes
+    unsigned long long pub[2][PUB_COPIES];  // per parity: the pass's merge (packed maximum,
+                                            // or SEL_SWEEP), published by tile 0's workgroup
+    uint32_t pub_epoch[2][PUB_COPIES];      // per parity: 1 + the iteration pub holds
+    unsigned long long force_val;  // a replayed iteration's merge, packed
+    uint32_t force_epoch;          // 1 + the iteration force_val is for (0: none)
+    uint32_t pad0;
+    unsigned long long smax[2];  // per parity: maximum over the sweep's finished chunks
+    unsigned long long spub[2];  // per parity: the sweep's maximum, published
+    uint32_t spub_epoch[2];      // per parity: 1 + the iteration whose maximum spub holds
+    uint32_t c1[2];              // per parity: chunks claimed for the maximum
+    uint32_t c1done[2];          // per parity: chunks whose maximum is in smax
+    uint32_t c2[2];              // per parity: chunks claimed for the candidates
+    uint32_t theta;              // the list's threshold
+    uint32_t shift;              // for the next sweep (0: none yet)
+    uint32_t cand_n;             // entries appended (above CAND_MAX: overflowed)
+    uint32_t cand_ok;            // the list holds every slot with count >= theta
+    uint32_t sweeps;             // iterations that swept the table
+    uint32_t cand[CAND_MAX];     // slot indexes
 };
 
 // Global pair table: open addressing with linear probing over 64-bit slots
@@ -126,6 +144,19 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Agent-coherent load and store (relaxed atomics at agent scope: sc1 on
+// gfx950), for state that workgroups on other XCDs change during a pass:
+// an sc1 store is visible on every XCD once it has completed, and an sc1
+// load never returns a stale line of this XCD's L2.
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Murmur3 32-bit finalizer: spreads packed pair keys; the low bits pick an
@@ -366,21 +397,11 @@ __device__ __forceinline__ void flush_table(LdsTable<LT>& tab, int tpb, const GT
 
 __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
-        ctl->k = 0; ctl->m = 0; ctl->limit = 0; ctl->done = 0; ctl->err = 0;
+        ctl->k = 0; ctl->m = 0; ctl->done = 0; ctl->err = 0;
         ctl->n[0] = n; ctl->n[1] = 0;
         ctl->L = 0; ctl->R = 0; ctl->X = 0;
         ctl->tile_ctr[0] = 0; ctl->tile_ctr[1] = 0; ctl->used = 0;
         lengths[0] = n;
-    }
-}
-
-// Set the number of iterations allowed in total, and with it the next
-// iteration to run (none once training has stopped or the limit is reached).
-__global__ void k_set_limit(Ctl* ctl, Sweep* sw, uint32_t limit) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        ctl->limit = limit;
-        const uint32_t m = ctl->m;
-        sw->iter = (!ctl->done && m < limit) ? m : NO_ITER;
     }
 }
 
@@ -484,12 +505,12 @@ __device__ __forceinline__ unsigned long long candidate(unsigned long long v) {
 }
 
 // ---------------------------------------------------------------- replay
-// A replayed iteration: the merge is the given pair pairs[2m], pairs[2m+1]
-// for iteration m (a learned merge list applied in order, "Nedir bu ya?"),
-// not the table's maximum, with its count looked up in the table (a pair
-// that does not occur still counts as a merge: count 0, nothing changes,
-// id 256 + m is used up; the packed value is never 0 since ~key != 0 for
-// 16-bit ids). The candidate list stays valid through it.
+// A replayed iteration m merges the listed pair pairs[2m], pairs[2m+1] (a
+// learned merge list applied in order, "Nedir bu ya?"), not the table's
+// maximum; its count is looked up in the table. A pair that does not occur
+// still counts as a merge: count 0, nothing changes, id 256 + m is used up.
+// The packed value is never 0 or SEL_SWEEP (~key != 0 for 16-bit ids), and
+// the candidate list stays valid through the iteration.
 
 __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     uint32_t h = mix32(key) & gt.mask;
@@ -504,15 +525,14 @@ __device__ __forceinline__ uint32_t gt_count(const GTable& gt, uint32_t key) {
     return 0u;
 }
 
+// Launched before the merge pass of a replayed iteration: its merge is the
+// listed pair, not the table's maximum.
 __global__ void k_force(Ctl* ctl, GTable gt, Sweep* sw, const uint32_t* __restrict__ pairs) {
-    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    if (blockIdx.x != 0 || threadIdx.x != 0 || ctl->done) return;
     const uint32_t m = ctl->m;
-    const bool active = !ctl->done && m < ctl->limit;
-    sw->iter = active ? m : NO_ITER;
-    if (!active) return;
     const uint32_t key = (pairs[2 * m] << 16) | pairs[2 * m + 1];
-    sw->best = ((unsigned long long)gt_count(gt, key) << 32) | (uint32_t)~key;
-    sw->force = m + 1u;
+    sw->force_val = ((unsigned long long)gt_count(gt, key) << 32) | (uint32_t)~key;
+    sw->force_epoch = m + 1u;
 }
 
 }  // namespace bpek

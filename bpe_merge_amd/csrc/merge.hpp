@@ -266,20 +266,6 @@ struct CountArgs {
     uint32_t o, kept;
 };
 
-// Bounded wait until every workgroup of the launch has made
-// its selection: the table and the list may change only after that.
-__device__ __forceinline__ void wait_all_started(const Sweep* sw, uint32_t p, Ctl* ctl) {
-    uint32_t spins = 0;
-    while (__hip_atomic_load(&sw->started[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
-        if (++spins > SPIN_LIMIT) {
-            atomicOr(&ctl->err, ERR_SPIN);
-            atomicExch(&ctl->done, 1u);
-            return;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-}
-
 // Apply one thread's count changes (masks from Changes) to the workgroup's
 // LDS table (the global table when LDS has no room), one changed pair per
 // loop turn, so that the insert code exists once. The old symbol at a
@@ -289,7 +275,7 @@ __device__ __forceinline__ void wait_all_started(const Sweep* sw, uint32_t p, Ct
 // plus the number of kept positions before j). left: old symbol at g0 - 1.
 template <int LT>
 __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, Sweep* sw,
-                                              uint32_t p, uint32_t theta, uint32_t gone, uint32_t born, uint32_t sel,
+                                              uint32_t theta, uint32_t gone, uint32_t born, uint32_t sel,
                                               uint32_t sel_in, uint32_t left, const uint32_t* st, uint32_t o,
                                               uint32_t kept, uint32_t L, uint32_t R, uint32_t X) {
     auto old_id = [&](uint32_t j) -> uint32_t {
@@ -312,10 +298,8 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
             delta = 1u;
             born &= born - 1u;
         }
-        if (!tab.insert(key, delta)) {  // the LDS table is full: straight to the global one
-            wait_all_started(sw, p, ctl);
+        if (!tab.insert(key, delta))  // the LDS table is full: straight to the global one
             gt_add_sel(gt, key, delta, ctl, sw, theta);
-        }
     }
 }
 
@@ -561,38 +545,6 @@ __device__ __forceinline__ void retire(const uint32_t (&x)[16], uint32_t h1, uin
 // ---------------------------------------------------------------- selection
 constexpr int SWEEP_UNROLL = 8;  // table loads in flight per thread
 
-// The largest packed candidate in this workgroup's share of the table
-// (slots blockIdx.x * TPB + tid + k * gridDim.x * TPB), or, with COLLECT,
-// the share's slots whose count is theta or more appended to the
-// candidate list. Plain loads: while the maximum is taken no workgroup
-// changes the table; while candidates are collected one may, but a count
-// read before an increase that crosses theta is covered by the append of
-// that increase, and counts of existing pairs only fall.
-template <int TPB, bool COLLECT>
-__device__ __forceinline__ unsigned long long sweep_share(const GTable& gt, Sweep* sw, uint32_t theta) {
-    const uint32_t slots = gt.mask + 1u;
-    const uint32_t stride = gridDim.x * TPB;
-    unsigned long long best = 0ull;
-    for (uint32_t s0 = blockIdx.x * TPB + threadIdx.x; s0 < slots; s0 += SWEEP_UNROLL * stride) {
-        unsigned long long v[SWEEP_UNROLL];
-#pragma unroll
-        for (int k = 0; k < SWEEP_UNROLL; ++k) {
-            const uint32_t i = s0 + k * stride;
-            v[k] = i < slots ? gt.slot[i] : 0ull;
-        }
-#pragma unroll
-        for (int k = 0; k < SWEEP_UNROLL; ++k) {
-            if (COLLECT) {
-                if ((uint32_t)(v[k] >> 32) >= theta) cand_append(sw, s0 + k * stride);  // 0 past the end
-            } else {
-                const unsigned long long c = candidate(v[k]);
-                best = c > best ? c : best;
-            }
-        }
-    }
-    return best;
-}
-
 // Maximum of v over the workgroup (every thread gets it). s_best: NW slots.
 template <int NW>
 __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* s_best,
@@ -606,9 +558,114 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
     return v;
 }
 
+// A chunk counter claimed by the workgroup: thread 0 takes the next chunk,
+// every thread gets its number.
+__device__ __forceinline__ uint32_t claim_chunk(uint32_t* ctr, uint32_t* s_u32) {
+    if (threadIdx.x == 0) *s_u32 = atomicAdd(ctr, 1u);
+    lds_barrier();
+    const uint32_t c = *s_u32;
+    lds_barrier();  // s_u32 free again
+    return c;
+}
+
+// The largest packed candidate (COLLECT false) of this thread's slots of
+// chunk c, or (COLLECT true) the chunk's slots whose count is theta or more
+// appended to the candidate list. Agent-coherent loads: other workgroups'
+// table adds reach memory, not this XCD's L2.
+template <int TPB, bool COLLECT>
+__device__ __forceinline__ unsigned long long sweep_chunk(const GTable& gt, Sweep* sw, uint32_t c, uint32_t theta) {
+    const uint32_t slots = gt.mask + 1u;
+    const uint32_t end = min(slots, (c + 1u) * SWEEP_CHUNK);
+    unsigned long long best = 0ull;
+    for (uint32_t s0 = c * SWEEP_CHUNK + threadIdx.x; s0 < end; s0 += SWEEP_UNROLL * TPB) {
+        unsigned long long v[SWEEP_UNROLL];
+#pragma unroll
+        for (int k = 0; k < SWEEP_UNROLL; ++k) {
+            const uint32_t i = s0 + k * TPB;
+            v[k] = i < end ? ld_agent(gt.slot + i) : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < SWEEP_UNROLL; ++k) {
+            if (COLLECT) {
+                if ((uint32_t)(v[k] >> 32) >= theta) cand_append(sw, s0 + k * TPB);  // 0 past the end
+            } else {
+                const unsigned long long cv = candidate(v[k]);
+                best = cv > best ? cv : best;
+            }
+        }
+    }
+    return best;
+}
+
+// An iteration that sweeps the table. Running workgroups claim chunks of
+// the table and fold each chunk's maximum into smax; the workgroup whose
+// chunks complete the count of finished chunks has every chunk's maximum in
+// smax: it empties the candidate list, stores the new threshold and
+// publishes the maximum. Every workgroup waits for the publication (it
+// comes from a workgroup that is running), then all claim chunks again to
+// collect the slots at or above the threshold (no one waits for that: the
+// merge pass's own adds append what they lift across theta, and counts of
+// existing pairs only fall). A workgroup that starts after the chunks are
+// gone only reads the publication.
+template <int TPB>
+__device__ __forceinline__ unsigned long long sweep_select(const GTable& gt, Sweep* sw, Ctl* ctl, uint32_t p,
+                                                            uint32_t it, unsigned long long* s_best,
+                                                            uint32_t* s_u32, uint32_t lane, uint32_t w,
+                                                            uint32_t& theta) {
+    constexpr int NW = TPB / 64;
+    const uint32_t nch = (gt.mask + SWEEP_CHUNK) / SWEEP_CHUNK;
+    uint32_t mine = 0;
+    unsigned long long part = 0ull;
+    for (uint32_t c; (c = claim_chunk(&sw->c1[p], s_u32)) < nch; ++mine) {
+        const unsigned long long m = sweep_chunk<TPB, false>(gt, sw, c, 0u);
+        part = m > part ? m : part;
+    }
+    const unsigned long long wbest = block_max_u64<NW>(part, s_best, lane, w);
+    const uint32_t shift_now = ld_agent(&sw->shift);
+    const uint32_t shift = shift_now ? shift_now : SHIFT_DEFAULT;
+    if (threadIdx.x == 0) {
+        if (mine) {
+            // the maximum is in smax before the chunks count as finished
+            const unsigned long long o = atomicMax(&sw->smax[p], wbest);
+            asm volatile("" ::"v"(o));
+            if (atomicAdd(&sw->c1done[p], mine) + mine == nch) {
+                const unsigned long long m = ld_agent(&sw->smax[p]);
+                const uint32_t mc = (uint32_t)(m >> 32);
+                st_agent(&sw->cand_n, 0u);
+                st_agent(&sw->theta, mc - (mc >> shift));
+                st_agent(&sw->shift, shift);
+                st_agent(&sw->cand_ok, 1u);
+                st_agent(&sw->sweeps, ld_agent(&sw->sweeps) + 1u);
+                st_agent(&sw->spub[p], m);
+                __builtin_amdgcn_s_waitcnt(0);  // the stores above are complete before the epoch
+                st_agent(&sw->spub_epoch[p], it + 1u);
+            }
+        }
+        uint32_t spins = 0;
+        while (ld_agent(&sw->spub_epoch[p]) != it + 1u) {
+            if (++spins > SPIN_LIMIT) {
+                atomicOr(&ctl->err, ERR_SPIN);
+                atomicExch(&ctl->done, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s_best[0] = ld_agent(&sw->spub[p]);
+    }
+    lds_barrier();
+    const unsigned long long best = s_best[0];
+    lds_barrier();  // s_best free again
+    const uint32_t mc = (uint32_t)(best >> 32);
+    theta = mc - (mc >> shift);
+    if (best != 0ull)
+        for (uint32_t c; (c = claim_chunk(&sw->c2[p], s_u32)) < nch;) sweep_chunk<TPB, true>(gt, sw, c, theta);
+    return best;
+}
+
 // The largest packed candidate among the list's first n entries whose
-// count is theta or more (0 if none). Every workgroup reads the same list
-// and table, left by the previous launch (plain loads, cached per XCD).
+// count is theta or more (0 if none). Plain loads: the list and the table
+// are as the previous launch left them, and nothing changes them before
+// the selection is published.
 template <int TPB>
 __device__ __forceinline__ unsigned long long list_max(const GTable& gt, const Sweep* sw, uint32_t n, uint32_t theta,
                                                         unsigned long long* s_best, uint32_t lane, uint32_t w) {
@@ -619,49 +676,6 @@ __device__ __forceinline__ unsigned long long list_max(const GTable& gt, const S
         best = c > best ? c : best;
     }
     return block_max_u64<TPB / 64>(best, s_best, lane, w);
-}
-
-// An iteration that sweeps the table: every workgroup takes the maximum of
-// its share and publishes it; the last to arrive empties the list (every
-// workgroup arrives after its selection, so no one reads the list any
-// more) and then releases the others; all take the maximum of all
-// maxima. (The workgroups of the persistent grid all run at once, as for
-// the look-back; the wait is bounded, ERR_SPIN.) Then theta = max - (max
-// >> shift), and every workgroup appends its share's slots at or above it.
-template <int TPB>
-__device__ __forceinline__ unsigned long long sweep_select(const GTable& gt, Sweep* sw, Ctl* ctl, uint32_t p,
-                                                            uint32_t shift, unsigned long long* s_best,
-                                                            uint32_t lane, uint32_t w, uint32_t& theta) {
-    constexpr int NW = TPB / 64;
-    unsigned long long best = block_max_u64<NW>(sweep_share<TPB, false>(gt, sw, 0u), s_best, lane, w);
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&sw->bmax[blockIdx.x], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t a = __hip_atomic_fetch_add(&sw->arrived[p], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        if (a + 1u == gridDim.x) {
-            __hip_atomic_store(&sw->cand_n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&sw->arrived[p], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        uint32_t spins = 0;
-        while (__hip_atomic_load(&sw->arrived[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <= gridDim.x) {
-            if (++spins > SPIN_LIMIT) {
-                atomicOr(&ctl->err, ERR_SPIN);
-                atomicExch(&ctl->done, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    lds_barrier();
-    best = 0ull;
-    for (uint32_t i = threadIdx.x; i < gridDim.x; i += TPB) {
-        const unsigned long long b = __hip_atomic_load(&sw->bmax[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        best = b > best ? b : best;
-    }
-    best = block_max_u64<NW>(best, s_best, lane, w);
-    const uint32_t m = (uint32_t)(best >> 32);
-    theta = m - (m >> shift);
-    if (best != 0ull) sweep_share<TPB, true>(gt, sw, theta);
-    return best;
 }
 
 // The per-workgroup flush of count changes (flush_table) with the merge
@@ -681,9 +695,83 @@ __device__ __forceinline__ void flush_table_sel(LdsTable<LT>& tab, int tpb, cons
     }
 }
 
+// The merge of iteration it, selected by the workgroup that drew ticket 0
+// (every thread of it calls this): the replayed pair if k_force listed one, else
+// the maximum over the candidate list if the list vouches for it, else
+// SEL_SWEEP (with the shift for that sweep steered by the list's size: a
+// list longer than the target narrows the next window, a small one widens
+// it). Then published: each of the first PUB_COPIES threads writes its
+// copy's value and, once that store is complete, its epoch.
+template <int TPB>
+__device__ __forceinline__ void select_and_publish(const GTable& gt, Sweep* sw, uint32_t p, uint32_t it,
+                                                   uint32_t theta, unsigned long long* s_best, uint32_t lane,
+                                                   uint32_t w) {
+    unsigned long long sel;
+    if (sw->force_epoch == it + 1u) {
+        sel = sw->force_val;
+    } else {
+        const uint32_t nc = sw->cand_n;
+        const bool ok = sw->cand_ok != 0u;
+        unsigned long long best = 0ull;
+        if (ok && nc <= CAND_MAX) best = list_max<TPB>(gt, sw, nc, theta, s_best, lane, w);
+        sel = best ? best : SEL_SWEEP;
+        if (!best && threadIdx.x == 0) {
+            uint32_t shift = sw->shift ? sw->shift : SHIFT_DEFAULT;
+            if (ok && nc > CAND_TARGET) shift = min(shift + 1u, SHIFT_MAX);
+            else if (ok && nc < CAND_TARGET / 16u && shift > 1u) shift = shift - 1u;
+            st_agent(&sw->shift, shift);  // read by the sweep, after the publication
+        }
+    }
+    static_assert(PUB_COPIES <= TPB, "one copy per thread");
+    __syncthreads();  // the shift above is complete before any copy is published
+    if (threadIdx.x < PUB_COPIES) {
+        st_agent(&sw->pub[p][threadIdx.x], sel);
+        __builtin_amdgcn_s_waitcnt(0);  // the value is visible before its epoch
+        st_agent(&sw->pub_epoch[p][threadIdx.x], it + 1u);
+    }
+}
+
+// The published merge of iteration it, from this workgroup's copy (a
+// bounded wait for the workgroup that drew ticket 0, which is running). Every thread of the workgroup calls this.
+__device__ __forceinline__ unsigned long long read_publication(Sweep* sw, Ctl* ctl, uint32_t p, uint32_t it,
+                                                               unsigned long long* s_best) {
+    if (threadIdx.x == 0) {
+        const uint32_t c = blockIdx.x % PUB_COPIES;
+        uint32_t spins = 0;
+        while (ld_agent(&sw->pub_epoch[p][c]) != it + 1u) {
+            if (++spins > SPIN_LIMIT) {
+                atomicOr(&ctl->err, ERR_SPIN);
+                atomicExch(&ctl->done, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        s_best[0] = ld_agent(&sw->pub[p][c]);
+    }
+    lds_barrier();
+    const unsigned long long v = s_best[0];
+    lds_barrier();  // s_best free again
+    return v;
+}
+
+// Once this workgroup has written its last tile: add its summed count
+// changes to the global table (it has read the publication, so every read
+// of the selection is done). Every thread of the workgroup calls this once
+// per pass.
+template <int TPB, int LT>
+__device__ __forceinline__ void finish_counts(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, Sweep* sw,
+                                              uint32_t theta) {
+    lds_barrier();  // every count change of the workgroup is in LDS
+    if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
+}
+
+// One launch per iteration it (the host passes it; a launch after training
+// has stopped does nothing). The workgroup that draws ticket 0 selects the
+// merge and publishes it; the others read the publication while their
+// first tile's loads are in flight.
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
-__global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict__ buf0,
+__global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_t* __restrict__ buf0,
                                                uint32_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
                                                uint32_t* lengths, Sweep* sw, uint32_t* merges) {
@@ -695,13 +783,13 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
     __shared__ uint32_t s_stage[2 * SST + 4];  // + 4: reads of dropped store groups stay inside
     __shared__ uint32_t s_wagg[NW];
-    __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now;
+    __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now, s_u32;
     __shared__ unsigned long long s_best[NW];
     __shared__ __align__(16) unsigned long long s_win[LB_WIN];
 
-    const uint32_t it = sw->iter;  // prepared by the previous launch (or k_set_limit, k_force)
-    if (it == NO_ITER || ctl->done) return;  // training has stopped (uniform)
-    const uint32_t p = it & 1u;                 // parity of the per-iteration counters
+    // state the previous launch left (plain, uniform loads: scalar, cached)
+    if (ctl->done) return;  // training has stopped
+    const uint32_t p = it & 1u;  // parity of the per-iteration counters
     const uint32_t n = ctl->n[it & 1u];
     const uint32_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
     uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
@@ -714,52 +802,39 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: in a scalar register
     uint32_t* tile_ctr = &ctl->tile_ctr[p];
-    constexpr uint32_t tile_base = 0u;
+    // ticket 0 of the tile counter is the selection of the merge, not a
+    // tile: ticket k > 0 is tile k - 1
+    constexpr uint32_t tile_base = 1u;
     if (blockIdx.x == 0 && tid == 0) {
         // the counters of the next iteration (the previous one's are done with)
         __hip_atomic_store(&ctl->tile_ctr[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&sw->started[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&sw->arrived[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_agent(&sw->c1[p ^ 1u], 0u);
+        st_agent(&sw->c1done[p ^ 1u], 0u);
+        st_agent(&sw->c2[p ^ 1u], 0u);
+        st_agent(&sw->smax[p ^ 1u], 0ull);
     }
 
     tab.clear(TPB);
-    if (tid == 0) s_tile[0] = atomicAdd(tile_ctr, 1u) - tile_base;
+    if (tid == 0) s_tile[0] = atomicAdd(tile_ctr, 1u);
+    uint32_t theta = sw->theta;  // the list's threshold, as the previous launch left it
     lds_barrier();
-    uint32_t t = s_tile[0];
+    // ---- the merge: selected by the workgroup that drew ticket 0 (it is
+    // running), before it issues any tile load, and published to all
+    if (s_tile[0] == 0u) {  // uniform
+        select_and_publish<TPB>(gt, sw, p, it, theta, s_best, lane, w);
+        if (tid == 0) s_tile[1] = atomicAdd(tile_ctr, 1u);
+        lds_barrier();
+        if (tid == 0) s_tile[0] = s_tile[1];
+        lds_barrier();
+    }
+    uint32_t t = s_tile[0] - tile_base;
     uint32_t x[V], h1, h2, hr;
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
     load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
-
-    // ---- the merge: a replayed pair, the list's maximum, or a sweep's. All
-    // workgroups read the same state, so all take the same branch.
-    unsigned long long best = 0ull;
-    uint32_t theta = sw->theta;
-    uint32_t shift = sw->shift ? sw->shift : SHIFT_DEFAULT;
-    bool sweep = false;
-    if (sw->force == it + 1u) {
-        best = sw->best;
-    } else {
-        const uint32_t nc = sw->cand_n;
-        const bool ok = sw->cand_ok != 0u;
-        if (ok && nc <= CAND_MAX) best = list_max<TPB>(gt, sw, nc, theta, s_best, lane, w);
-        sweep = best == 0ull;  // the list is invalid, overflowed or below theta
-        // steer the next list's size: more than the target (or an overflow)
-        // narrows the window, a small list widens it
-        if (ok && nc > CAND_TARGET) shift = min(shift + 1u, SHIFT_MAX);
-        else if (ok && nc < CAND_TARGET / 16u && shift > 1u) shift = shift - 1u;
-    }
-    if (tid == 0) atomicAdd(&sw->started[p], 1u);  // this workgroup's reads of the list are done
-    if (sweep) {  // uniform
-        best = sweep_select<TPB>(gt, sw, ctl, p, shift, s_best, lane, w, theta);
-        if (blockIdx.x == 0 && tid == 0) {  // every workgroup has read the old values
-            sw->theta = theta;
-            sw->shift = shift;
-            sw->cand_ok = 1u;
-            sw->sweeps += 1u;
-        }
-    }
+    unsigned long long best = read_publication(sw, ctl, p, it, s_best);
+    if (best == SEL_SWEEP) best = sweep_select<TPB>(gt, sw, ctl, p, it, s_best, &s_u32, lane, w, theta);  // uniform
     if (best == 0ull) {  // uniform: no countable pair is left
-        if (blockIdx.x == 0 && tid == 0) ctl->done = 1u;
+        if (blockIdx.x == 0 && tid == 0) st_agent(&ctl->done, 1u);
         return;
     }
     // uniform: keep the merge in scalar registers
@@ -838,7 +913,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, sw, p, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
                                   L, R, X);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
@@ -997,7 +1072,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             // tile's count changes (they need the old symbols only as masks and staged values)
             load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
             if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, sw, p, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
+                count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
                                   L, R, X);
             // ---- the previous tile: its offset (unless its look-back is done)
             if (tp < ntiles && w == 0) {
@@ -1035,10 +1110,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(Ctl* ctl, uint32_t* __restrict
             t = tn;
         }
     }
-    if (tid == 0) wait_all_started(sw, p, ctl);  // before the table changes
-    lds_barrier();
-    if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
-    if (blockIdx.x == 0 && tid == 0) sw->iter = it + 1u < ctl->limit ? it + 1u : NO_ITER;  // all have read it
+    finish_counts<TPB, LT>(tab, gt, ctl, sw, theta);
 }
 
 }  // namespace bpek

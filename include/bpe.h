@@ -79,7 +79,7 @@ typedef struct {
 typedef struct {
     uint32_t table_log2;     /* global pair table of 2^table_log2 slots (8 B each);
                                 0 = automatic; otherwise 10..30                       */
-    uint32_t flags;          /* reserved, must be 0                                    */
+    uint32_t flags;          /* 0, or BPE_FLAG_OVERSUBSCRIBE (a testing aid)           */
     void *stream;            /* hipStream_t all work is ordered on; NULL = the state
                                 creates and owns a blocking stream (ordered after the
                                 legacy default stream)                                 */
@@ -87,6 +87,13 @@ typedef struct {
                                 NULL = the state allocates its own                     */
     size_t workspace_bytes;  /* size of workspace (ignored when workspace is NULL)     */
 } bpe_config;
+
+/* Testing aid for bpe_config.flags: launch each merge pass with four times
+   as many workgroups as the device can hold at once, so that most of them
+   start only after earlier ones have finished. Results do not change: no
+   workgroup of a pass ever waits for one that has not started (see
+   bpe_run). Slower; for tests only. */
+#define BPE_FLAG_OVERSUBSCRIBE 1u
 
 typedef struct bpe_state bpe_state;
 
@@ -121,9 +128,19 @@ bpe_status bpe_train(const uint8_t *bytes, size_t n, uint32_t n_merges, const bp
    synchronising call (bpe_sync, bpe_step, ...). */
 bpe_status bpe_init(const uint8_t *bytes, size_t n, const bpe_config *cfg, bpe_state **out);
 
-/* Enqueue up to n_merges more iterations without waiting and without any
-   host round trip between iterations. Iterations after the last countable
-   pair do nothing. BPE_EIDSPACE if the total would exceed BPE_MAX_MERGES. */
+/* Enqueue up to n_merges more iterations of "Nedir bu ya?" without waiting
+   and without any host round trip between iterations: one plain kernel
+   launch per iteration, each reading the merge the previous one prepared
+   on the device. Iterations after the last countable pair do nothing.
+   Shared devices: a pass never needs its whole grid resident at once.
+   Its workgroups wait for one another only for work a running workgroup
+   has already taken on (the scan's look-back waits for lower tiles, which
+   are handed out in order; a table sweep waits for chunks already
+   claimed), so any subset of resident workgroups completes the pass, and
+   other kernels on the device only slow it down. Each wait is bounded all
+   the same; one that gives up marks the state BPE_ESTATE (device error
+   bit 2), which only a fault can cause. BPE_EIDSPACE if the total would
+   exceed BPE_MAX_MERGES. */
 bpe_status bpe_run(bpe_state *s, uint32_t n_merges);
 
 /* Wait for the enqueued work; *n_done (may be NULL) = merges produced so far.

@@ -87,7 +87,7 @@ def test_train_argument_validation_before_any_device_call(bpe):
     cfg = bpe.Config(); cfg.table_log2 = 5
     assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
                          ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
-    cfg = bpe.Config(); cfg.flags = 1
+    cfg = bpe.Config(); cfg.flags = 2  # an unknown flag bit (1 is the oversubscription testing aid)
     assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
                          ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
     # an empty corpus is valid and needs no device

@@ -256,3 +256,19 @@ def test_words_of_uniform_letters_many_near_ties(bpe):
     gm, gt = gpu_train(bpe, d, 600, table_log2=18)
     om, ot, _ = oracle.train_chunks(d, 600)
     assert np.array_equal(gm, om) and np.array_equal(gt, ot)
+
+
+def test_oversubscribed_grid_needs_no_coresidency(bpe):
+    # merge passes launched with four times the workgroups the device holds
+    # at once: most start only after earlier ones have finished. No
+    # workgroup waits for one that has not started (tiles are handed out in
+    # order; table sweeps are claimed in chunks; the next merge is prepared
+    # by the last workgroup to finish), so results are unchanged.
+    cases = [(1, 65_536, 60), (3, 3_000_000, 150), (5, 2_000_000, 120), (2, 1_000_000, 200)]
+    for cfg, n, k in cases:
+        d = corpus.generate(corpus.CONFIGS[cfg].scaled(n, seed=200 + cfg))
+        _say("oversubscribed grid: recipe %d, %d bytes, %d merges" % (cfg, n, k))
+        m, t = bpe.train(_dev(d), k, 18, flags=bpe.FLAG_OVERSUBSCRIBE)
+        om, ot, _ = oracle.train_chunks(d, k)
+        assert np.array_equal(m.cpu().numpy().astype(np.int64), om), cfg
+        assert np.array_equal(t.cpu().numpy().astype(np.uint32), ot), cfg
