@@ -60,6 +60,8 @@ _SIGS = {
     "bpe_workspace_bytes": (_sz, [_sz, _cfgp]),
     "bpe_train": (ctypes.c_int, [_vp, _sz, _u32, _cfgp, _vp, ctypes.POINTER(_u32), _vp, _sz,
                                  ctypes.POINTER(_sz)]),
+    "bpe_train_static": (ctypes.c_int, [_vp, _sz, _u32, _u32, _vp, _vp, ctypes.POINTER(_u32), _vp, _sz,
+                                        ctypes.POINTER(_sz)]),
     "bpe_init": (ctypes.c_int, [_vp, _sz, _cfgp, ctypes.POINTER(_vp)]),
     "bpe_run": (ctypes.c_int, [_vp, _u32]),
     "bpe_sync": (ctypes.c_int, [_vp, ctypes.POINTER(_u32)]),
@@ -159,6 +161,33 @@ def train(data, n_merges: int, table_log2: int | None = None, flags: int = 0):
     st = _lib.bpe_train(data.data_ptr(), n, n_merges, ctypes.byref(cfg), merges.data_ptr(), ctypes.byref(n_done),
                         tokens.data_ptr(), tokens.numel(), ctypes.byref(n_tok))
     _check(st, "bpe_train")
+    return merges[: n_done.value], tokens[: n_tok.value]
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+STATIC_MAX_BYTES = 2 << 20
+STATIC_MAX_TABLE_LOG2 = 20
+
+
+def train_static(data, n_merges: int, table_log2: int | None = None):
+    """bpe_train_static on a uint8 CUDA tensor: training in the library's own
+    static workspace (no device allocation by the library; at most
+    STATIC_MAX_BYTES bytes). Returns (merges, tokens) as train() does; the
+    output tensors are allocated here, by torch, before the call."""
+    torch = _torch()
+    if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+        raise TypeError("data must be a uint8 CUDA tensor")
+    data = data.contiguous().reshape(-1)
+    n = data.numel()
+    dev = data.device
+    merges = torch.empty((max(n_merges, 1), 3), dtype=torch.int32, device=dev)
+    tokens = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    n_done = _u32(0)
+    n_tok = _sz(0)
+    st = _lib.bpe_train_static(data.data_ptr() if n else None, n, n_merges, int(table_log2 or 0),
+                               _stream_handle(dev), merges.data_ptr(), ctypes.byref(n_done), tokens.data_ptr(),
+                               tokens.numel(), ctypes.byref(n_tok))
+    _check(st, "bpe_train_static")
     return merges[: n_done.value], tokens[: n_tok.value]
 
 

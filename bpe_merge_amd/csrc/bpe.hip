@@ -153,6 +153,7 @@ struct bpe_state {
     int device = 0;
     hipStream_t stream = nullptr;
     bool own_stream = false;
+    bool null_stream = false;  // work goes to the null stream (a caller's NULL, without allocation)
     void* ws = nullptr;
     bool own_ws = false;
     size_t n = 0;
@@ -237,6 +238,10 @@ bpe_status event_pool(int device, size_t count, std::vector<hipEvent_t>** out) {
 
 // Iterations requested .. requested + n_merges - 1, which the passes are
 // told; once training stops (no pair left) the later passes do nothing.
+bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_config* cfg, uint32_t tlog2,
+                       const Layout& lay, bool may_allocate);
+void state_release(bpe_state* s);
+
 bpe_status enqueue_run(bpe_state* s, uint32_t n_merges, uint32_t* first) {
     if (size_t(s->requested) + n_merges > BPE_MAX_MERGES) {
         set_err("%u + %u merges exceed the id space (%u merges)", s->requested, n_merges, BPE_MAX_MERGES);
@@ -300,10 +305,27 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         set_err("host allocation failed");
         return BPE_ENOMEM;
     }
-    auto fail = [&](bpe_status st) {
+    const bpe_status st = state_setup(s, bytes, n, cfg, tlog2, lay, true);
+    if (st != BPE_OK) {
         bpe_free(s);
         return st;
-    };
+    }
+    *out = s;
+    return BPE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Fill a default-constructed state for bytes[0..n) (validated by the
+// caller) and enqueue tagging and the first count. With may_allocate, a
+// missing stream or workspace is created and owned by the state; without,
+// the state uses the caller's stream (NULL: the null stream) and workspace
+// and creates nothing. On failure the caller releases the state.
+bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_config* cfg, uint32_t tlog2,
+                       const Layout& lay, bool may_allocate) {
+    auto fail = [](bpe_status st) { return st; };
     hipError_t e = hipGetDevice(&s->device);
     if (e != hipSuccess) {
         set_err("hipGetDevice failed: %s", hipGetErrorString(e));
@@ -312,8 +334,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     s->n = n;
     s->tlog2 = tlog2;
     s->lay = lay;
-    if (cfg && cfg->stream) {
-        s->stream = static_cast<hipStream_t>(cfg->stream);
+    if ((cfg && cfg->stream) || !may_allocate) {
+        s->stream = static_cast<hipStream_t>(cfg ? cfg->stream : nullptr);
+        s->null_stream = s->stream == nullptr;
     } else {
         // a blocking stream: it still orders after work on the legacy
         // default stream that produced the input
@@ -326,6 +349,9 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     }
     if (cfg && cfg->workspace) {
         s->ws = cfg->workspace;
+    } else if (!may_allocate) {
+        set_err("no workspace given");
+        return BPE_EINVAL;
     } else {
         e = hipMalloc(&s->ws, lay.total);
         if (e != hipSuccess) {
@@ -394,9 +420,23 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         set_err("kernel launch failed: %s", hipGetErrorString(e));
         return fail(BPE_EHIP);
     }
-    *out = s;
     return BPE_OK;
 }
+
+// Wait for the state's work and release what it owns (not the state).
+void state_release(bpe_state* s) {
+    (void)hipSetDevice(s->device);
+    if (s->stream || s->null_stream) (void)hipStreamSynchronize(s->stream);
+    if (s->own_ws && s->ws) (void)hipFree(s->ws);
+    if (s->own_stream && s->stream) (void)hipStreamDestroy(s->stream);
+    s->ws = nullptr;
+    s->stream = nullptr;
+    s->own_ws = s->own_stream = false;
+}
+
+}  // namespace
+
+extern "C" {
 
 bpe_status bpe_run(bpe_state* s, uint32_t n_merges) {
     g_err.clear();
@@ -654,10 +694,7 @@ bpe_status bpe_replay(bpe_state* s, const bpe_merge* merges, uint32_t k) {
 
 void bpe_free(bpe_state* s) {
     if (!s) return;
-    (void)hipSetDevice(s->device);
-    if (s->stream) (void)hipStreamSynchronize(s->stream);
-    if (s->own_ws && s->ws) (void)hipFree(s->ws);
-    if (s->own_stream && s->stream) (void)hipStreamDestroy(s->stream);
+    state_release(s);
     delete s;
 }
 
@@ -691,6 +728,105 @@ bpe_status bpe_train(const uint8_t* bytes, size_t n, uint32_t n_merges, const bp
     if (st == BPE_OK && (tokens || n_tokens)) st = bpe_tokens(s, tokens, tokens ? tokens_cap : 0, n_tokens);
     if (st == BPE_OK) *n_done = done;
     bpe_free(s);
+    return st;
+}
+
+}  // extern "C"
+
+// ======================================================================== training without allocation
+// bpe_train_static: bpe_train on a workspace in the library's own device
+// memory, for callers that cannot allocate. The workspace is a file-scope
+// device array; host code uses the address hipGetSymbolAddress returns for
+// the current device (each device holds its own copy), never the array's
+// name, which in host code is only a stand-in.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[BPE_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The address of this device's copy of scratch, looked up once per device
+// (with that device current, as it is on every call).
+bpe_status static_scratch(int device, void** out) {
+    if (device < 0 || device >= 64) {
+        set_err("device index %d out of range", device);
+        return BPE_EINVAL;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            set_err("hipGetSymbolAddress of the static workspace failed: %s", hipGetErrorString(e));
+            return BPE_EHIP;
+        }
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return BPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpe_status bpe_train_static(const uint8_t* bytes, size_t n, uint32_t n_merges, uint32_t table_log2, void* stream,
+                            bpe_merge* merges, uint32_t* n_done, uint32_t* tokens, size_t tokens_cap,
+                            size_t* n_tokens) {
+    g_err.clear();
+    if (!n_done || (!merges && n_merges) || (n && !bytes)) {
+        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_done must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    if (n > BPE_STATIC_MAX_BYTES) {
+        set_err("n = %zu exceeds the %u bytes the static workspace takes", n, BPE_STATIC_MAX_BYTES);
+        return BPE_EINVAL;
+    }
+    if (table_log2 && (table_log2 < 10 || table_log2 > BPE_STATIC_MAX_TABLE_LOG2)) {
+        set_err("table_log2 = %u is outside 10..%u for the static workspace", table_log2,
+                BPE_STATIC_MAX_TABLE_LOG2);
+        return BPE_EINVAL;
+    }
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_done = 0;
+    if (n_tokens) *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    const uint32_t tlog2 =
+        table_log2 ? table_log2 : std::min<uint32_t>(BPE_STATIC_MAX_TABLE_LOG2, table_log2_for(n, nullptr));
+    const Layout lay = layout_for(n, tlog2);
+    if (lay.total > BPE_STATIC_SCRATCH_BYTES) {
+        set_err("%zu bytes of workspace needed, the static workspace holds %u", lay.total, BPE_STATIC_SCRATCH_BYTES);
+        return BPE_EINVAL;
+    }
+    int device = 0;
+    HIP_TRY(hipGetDevice(&device));
+    void* ws = nullptr;
+    bpe_status st = static_scratch(device, &ws);
+    if (st != BPE_OK) return st;
+    bpe_config cfg{};
+    cfg.table_log2 = tlog2;
+    cfg.stream = stream;
+    cfg.workspace = ws;
+    cfg.workspace_bytes = BPE_STATIC_SCRATCH_BYTES;
+    bpe_state s;  // on the stack: nothing is allocated, on the host or the device
+    st = state_setup(&s, bytes, n, &cfg, tlog2, lay, false);
+    if (st == BPE_OK) st = bpe_run(&s, n_merges);
+    uint32_t done = 0;
+    if (st == BPE_OK) st = bpe_sync(&s, &done);
+    if (st == BPE_OK && done) st = bpe_merges(&s, merges, done, nullptr);
+    if (st == BPE_OK && (tokens || n_tokens)) st = bpe_tokens(&s, tokens, tokens ? tokens_cap : 0, n_tokens);
+    if (st == BPE_OK) *n_done = done;
+    state_release(&s);
     return st;
 }
 

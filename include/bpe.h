@@ -121,6 +121,27 @@ bpe_status bpe_train(const uint8_t *bytes, size_t n, uint32_t n_merges, const bp
                      bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
                      size_t *n_tokens);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): bpe_train
+   on a workspace that lives in the library itself, a file-scope device
+   array of BPE_STATIC_SCRATCH_BYTES that every device the library runs on
+   holds until the process ends. Nothing is allocated on the device or the
+   host (no stream is created: stream is the caller's hipStream_t, NULL for
+   the null stream; the workspace is cleared by kernels at the start of
+   each call). Limits: n <= BPE_STATIC_MAX_BYTES and a pair table of at most
+   2^BPE_STATIC_MAX_TABLE_LOG2 slots (table_log2 0 = automatic, capped
+   there); beyond them BPE_EINVAL with a message. All calls on one device
+   share the array, which keeps the last call's contents: calls that
+   overlap on one device (from two threads, or on two streams) race and
+   must not be made. Pointers and results as bpe_train; blocks until done.
+   Errors as bpe_train. */
+#define BPE_STATIC_SCRATCH_BYTES (32u << 20)
+#define BPE_STATIC_MAX_BYTES (2u << 20)
+#define BPE_STATIC_MAX_TABLE_LOG2 20u
+bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, uint32_t table_log2, void *stream,
+                            bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
+                            size_t *n_tokens);
+
 /* Create a training state: tag bytes[0..n) (n >= 1) into symbols with the
    character classes of "Ne Yapar? 1" ("Satir Satir Analiz 1)") and count the
    pairs of iteration 0 into the global pair table ("Ne Yapar? 2").
