@@ -32,6 +32,12 @@ timed, not credited.
 "encoding" reports encoding of the same corpus with the same merges (a
 learned list applied to new text, word by word, each distinct word encoded
 once), with the same accounting.
+
+"configs" reports the other four workloads (64 KiB, 16 MiB, 128 MiB and
+1 GiB corpora, each with its own merge count and table size): one timed
+job each, merges/s, the merge pass's GB/s and fraction of peak, and
+whether the result is bit-identical to the chunk-multiset CPU oracle on
+the same bytes (timed beside it, one core).
 """
 from __future__ import annotations
 
@@ -233,14 +239,110 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
     }
 
 
+def traffic_windows(workload: str, kernel: str):
+    """Measured HBM bytes of a kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (one or more windows of launches), only if
+    it was taken on the kernel sources as they are now."""
+    t = measured_traffic(workload, kernel)
+    if t is None:
+        return None
+    wins = t.get("windows") or [t]
+    out = []
+    for w in wins:
+        meas = w["fetch_bytes_per_launch"] + w["write_bytes_per_launch"]
+        alg = w["algorithmic_bytes_per_launch"]
+        out.append({"launches": w.get("launches"), "iterations": w.get("iterations"),
+                    "read": round(w["fetch_bytes_per_launch"]), "write": round(w["write_bytes_per_launch"]),
+                    "measured": round(meas), "algorithmic_same_launches": round(alg),
+                    "ratio": round(meas / alg, 4)})
+    return out
+
+
+def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0):
+    """Train spec's workload: warmup unprofiled jobs, then `steps` jobs with
+    a HIP event after each iteration's launch. Returns the measurements, the
+    last job's merges and tokens, and (cpu_reps > 0) the CPU oracle's timing
+    on the same bytes with the bit-identity check."""
+    log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
+    data = corpus.generate(spec)
+    sha = corpus.sha256(data)
+    d = torch.from_numpy(data).to("cuda:0")
+    torch.cuda.synchronize()
+    n_merges, tlog2 = spec.n_merges, spec.table_log2
+
+    def step(profiled: bool):
+        t0 = time.perf_counter()
+        st = bpe.State(d, table_log2=tlog2)
+        prof = None
+        if profiled:
+            prof = st.profile(n_merges, per_iteration=True)
+        else:
+            st.run(n_merges)
+            st.sync()
+        merges = st.merges()
+        tokens = st.tokens()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        lengths = st.lengths().cpu().numpy().astype(np.int64)
+        st.free()
+        return t1 - t0, merges, tokens, lengths, prof
+
+    warm_s = []
+    for i in range(warmup):
+        dt, m, t, _, _ = step(False)
+        warm_s.append(dt)
+        log("%s warmup step %d: %.3f s, %d merges, %d tokens" % (spec.name, i + 1, dt, m.shape[0], t.shape[0]))
+    wall, last, ref = [], None, None
+    for i in range(steps):
+        torch.cuda.synchronize()
+        dt, m, t, lengths, prof = step(True)
+        wall.append(dt)
+        last = (m, t, lengths, prof)
+        sig = (m.cpu().numpy().tobytes(), t.shape[0])
+        if ref is None:
+            ref = sig
+        elif sig != ref:
+            raise RuntimeError("timed steps of %s disagree" % spec.name)
+        log("%s timed step %d: %.3f s, %d merges" % (spec.name, i + 1, dt, m.shape[0]))
+    m, t, lengths, (r, m_ms) = last
+    k = m.shape[0]
+    n_k = lengths[:k].astype(np.float64)
+    n_k1 = lengths[1: k + 1].astype(np.float64)
+    m_ms = m_ms[:k].astype(np.float64)
+    merge_bytes = 4.0 * n_k + 4.0 * n_k1
+    total_wall = float(sum(wall))
+    res = {"spec": spec, "data": data, "d": d, "sha": sha, "merges": m, "tokens": t, "lengths": lengths,
+           "k": int(k), "wall": wall, "warm_s": warm_s, "value": k * len(wall) / total_wall,
+           "ms_per_step": 1e3 * total_wall / len(wall), "m_ms": m_ms, "n_k": n_k, "merge_bytes": merge_bytes,
+           "sweeps": int(r.sweeps), "merge_ms_sum": float(m_ms.sum()),
+           "merge_gbps": float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9) if k else 0.0}
+    if cpu_reps:
+        import oracle
+        log("timing the CPU oracle (chunk-multiset, single thread) on %s, %d run(s)" % (spec.name, cpu_reps))
+        times = []
+        for _ in range(cpu_reps):
+            with one_core():
+                t0 = time.perf_counter()
+                om, ot, _ = oracle.train_chunks(data, n_merges)
+                times.append(time.perf_counter() - t0)
+        cpu_s = float(np.median(times))
+        same = bool(np.array_equal(om, m.cpu().numpy().astype(np.int64)) and
+                    np.array_equal(ot, t.cpu().numpy().astype(np.uint32)))
+        res.update({"cpu_s": cpu_s, "cpu_merges_s": len(om) / cpu_s, "cpu_reps": cpu_reps, "identical": same})
+        log("%s oracle: %.2f s, bit-identical to the GPU result: %s" % (spec.name, cpu_s, same))
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 256 MiB, 32k merges)")
     ap.add_argument("--merges", type=int, default=None, help="override the merge count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other four workloads (one job each, with the oracle check)")
     ap.add_argument("--report", default=None, help="write per-iteration details to this JSON file")
     ap.add_argument("--no-inference", action="store_true", help="skip the inference and encoding legs")
     ap.add_argument("--save-merges", default=None, metavar="PATH", help="write the learned merges (.npy)")
@@ -279,13 +381,11 @@ def main() -> int:
         spec = spec.scaled(spec.n_bytes, n_merges=args.merges)
     n_merges, tlog2 = spec.n_merges, spec.table_log2
     T = 1 << tlog2
-    log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
-    data = corpus.generate(spec)
-    sha = corpus.sha256(data)
-    d = torch.from_numpy(data).to("cuda:0")
-    torch.cuda.synchronize()
 
     if args.inference_only:
+        log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
+        data = corpus.generate(spec)
+        d = torch.from_numpy(data).to("cuda:0")
         m = torch.from_numpy(np.load(args.inference_only, allow_pickle=False)).to("cuda:0")
         inf = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log,
                             source="learned by an earlier run on the same corpus")
@@ -299,101 +399,47 @@ def main() -> int:
         print(json.dumps(out), flush=True)
         return 0
 
-    def step(profiled: bool):
-        t0 = time.perf_counter()
-        st = bpe.State(d, table_log2=tlog2)
-        prof = None
-        if profiled:
-            prof = st.profile(n_merges, per_iteration=True)
-        else:
-            st.run(n_merges)
-            st.sync()
-        merges = st.merges()
-        tokens = st.tokens()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        lengths = st.lengths().cpu().numpy().astype(np.int64)
-        st.free()
-        return t1 - t0, merges, tokens, lengths, prof
-
-    warm_s = []
-    for i in range(args.warmup):
-        dt, m, t, _, _ = step(False)
-        warm_s.append(dt)
-        log("warmup step %d: %.3f s, %d merges, %d tokens" % (i + 1, dt, m.shape[0], t.shape[0]))
-    wall = []
-    last = None
-    ref = None
-    for i in range(args.steps):
-        torch.cuda.synchronize()
-        dt, m, t, lengths, prof = step(True)
-        wall.append(dt)
-        last = (m, t, lengths, prof)
-        sig = (m.cpu().numpy().tobytes(), t.shape[0])
-        if ref is None:
-            ref = sig
-        elif sig != ref:
-            log("ERROR: timed steps disagree")
-            return 1
-        log("timed step %d: %.3f s, %d merges" % (i + 1, dt, m.shape[0]))
-
-    m, t, lengths, prof = last
-    r, m_ms = prof
-    k = m.shape[0]
-    n_k = lengths[:k].astype(np.float64)
-    n_k1 = lengths[1: k + 1].astype(np.float64)
-    m_ms = m_ms[:k].astype(np.float64)
+    # the large workloads once, the others three times (median)
+    cpu_reps = 0 if args.no_cpu_baseline else (1 if spec.n_bytes >= (256 << 20) else 3)
+    res = train_leg(bpe, corpus, spec, args.steps, args.warmup, np, torch, time, log, cpu_reps)
+    m, t, lengths, k = res["merges"], res["tokens"], res["lengths"], res["k"]
+    m_ms, n_k, merge_bytes = res["m_ms"], res["n_k"], res["merge_bytes"]
+    data, d, sha = res["data"], res["d"], res["sha"]
     it_s = m_ms / 1e3
-    merge_bytes = 4.0 * n_k + 4.0 * n_k1
     # an iteration that sweeps the pair table reads it twice (maximum, then
     # candidates); the others read only the candidate list's slots (not
     # credited). Per-iteration figures leave the sweeps out.
-    iter_bytes = merge_bytes
-    sweep_bytes = 2 * 8.0 * T * r.sweeps
-    total_wall = float(sum(wall))
-    value = k * len(wall) / total_wall
+    sweep_bytes = 2 * 8.0 * T * res["sweeps"]
     sym_per_s_agg = float(n_k.sum() / it_s.sum())
-    hbm_agg = float((iter_bytes.sum() + sweep_bytes) / it_s.sum() / 1e9)
-    merge_gbps = float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9)
+    hbm_agg = float((merge_bytes.sum() + sweep_bytes) / it_s.sum() / 1e9)
+    merge_gbps = res["merge_gbps"]
     per_it_sym = n_k / it_s
-    per_it_gbps = iter_bytes / it_s / 1e9
-    dominant = "k_merge"  # the merge pass takes >90% of the time (see kernels_ms_per_step)
+    per_it_gbps = merge_bytes / it_s / 1e9
+    dominant = "k_merge"  # the merge pass takes >95% of the time (see kernels_ms_per_step)
     achieved, avg_bytes, avg_ms = merge_gbps, float(merge_bytes.mean()), float(m_ms.mean())
-
-    traffic = measured_traffic(spec.name, dominant)
+    windows = traffic_windows(spec.name, dominant)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        # the large workloads once, the others three times (median)
-        reps = 1 if spec.n_bytes >= (256 << 20) else 3
-        log("timing the CPU oracle (chunk-multiset, single thread) on the same corpus, %d run(s)" % reps)
-        times = []
-        for _ in range(reps):
-            with one_core():
-                t0 = time.perf_counter()
-                om, ot, _ = oracle.train_chunks(data, n_merges)
-                times.append(time.perf_counter() - t0)
-        cpu_s = float(np.median(times))
-        same = np.array_equal(om, m.cpu().numpy().astype(np.int64)) and \
-            np.array_equal(ot, t.cpu().numpy().astype(np.uint32))
-        cpu = {"value": round(len(om) / cpu_s, 3), "unit": "merges/s", "cores": 1, "kind": "oracle",
+    if cpu_reps:
+        cpu = {"value": round(res["cpu_merges_s"], 3), "unit": "merges/s", "cores": 1, "kind": "oracle",
                "sample": "the whole workload (%d bytes, %d merges) through the chunk-multiset C oracle "
                          "(oracle/bpe_oracle.c, train_chunks), one thread, %.2f s including chunking (median "
-                         "of %d); GPU result bit-identical: %s" % (spec.n_bytes, n_merges, cpu_s, reps, same),
+                         "of %d); GPU result bit-identical: %s"
+                         % (spec.n_bytes, n_merges, res["cpu_s"], cpu_reps, res["identical"]),
                "pinned": "one core (sched_setaffinity)", **cpu_facts()}
         if spec.n_bytes <= (1 << 20):
             # the literal definition (a full recount every iteration) is
             # feasible only on the smallest workload
+            import oracle
             with one_core():
                 t0 = time.perf_counter()
                 lm, lt, _ = oracle.train_literal(data, n_merges)
                 lit_s = time.perf_counter() - t0
+            om, ot, _ = oracle.train_chunks(data, n_merges)
             cpu["literal"] = {"value": round(len(lm) / lit_s, 3), "unit": "merges/s",
                               "sample": "the literal C oracle (train_literal: full recount each iteration), "
                                         "one thread, %.2f s; equal to the chunk oracle: %s"
                                         % (lit_s, bool(np.array_equal(lm, om) and np.array_equal(lt, ot)))}
-        log("oracle: %.2f s, bit-identical to the GPU result: %s" % (cpu_s, same))
 
     if args.save_merges:
         np.save(args.save_merges, m.cpu().numpy())
@@ -403,14 +449,46 @@ def main() -> int:
         inference = inference_leg(args, bpe, spec, data, d, m, np, torch, time, log)
         encoding = encode_leg(args, bpe, spec, data, d, m, np, time, log, train_tokens=t)
 
+    # the other workloads: one timed job each (after one unprofiled job on
+    # the small ones), with the oracle's result on the same bytes
+    configs = None
+    if not args.no_configs and args.merges is None:
+        configs = {}
+        del d, res["d"]
+        for c in sorted(corpus.CONFIGS):
+            if c == args.config:
+                continue
+            cs = corpus.CONFIGS[c]
+            small = cs.n_bytes < (256 << 20)
+            r = train_leg(bpe, corpus, cs, 1, 1 if small else 0, np, torch, time, log,
+                          0 if args.no_cpu_baseline else 1)
+            frac = r["merge_gbps"] / HBM_PEAK_GBPS
+            configs[cs.name] = {
+                "workload": "%d-byte seeded corpus (%s), %d merges, pair table 2^%d, sha256 %s"
+                            % (cs.n_bytes, cs.kind, cs.n_merges, cs.table_log2, r["sha"][:16]),
+                "merges_done": r["k"], "merges_per_s": round(r["value"], 1), "s_per_job": round(r["ms_per_step"] / 1e3, 4),
+                "k_merge_ms": round(r["merge_ms_sum"], 3), "k_merge_gbps": round(r["merge_gbps"], 1),
+                "k_merge_frac_of_peak": round(frac, 4), "table_sweeps": r["sweeps"],
+                "final_tokens": int(r["tokens"].shape[0]),
+                "cpu_oracle_merges_per_s": round(r["cpu_merges_s"], 1) if "cpu_merges_s" in r else None,
+                "bit_identical_to_oracle": r.get("identical"),
+                "note": ("launch- and latency-bound: the roofline fraction is not meaningful"
+                         if cs.n_bytes <= (1 << 20) else
+                         "the 64 MiB symbol array and 16 MiB table fit the 256 MB last-level cache; GB/s is "
+                         "effective" if cs.n_bytes <= (16 << 20) else "HBM-bound"),
+            }
+            log("%s: %.1f merges/s, k_merge %.1f GB/s (%.1f%% of peak), bit-identical: %s"
+                % (cs.name, r["value"], r["merge_gbps"], 100 * frac, r.get("identical")))
+            del r
+
     out = {
         "metric": "BPE train merges/sec + symbols/sec per merge, 256 MiB/32k merges; HBM GB/s",
-        "value": round(value, 3),
+        "value": round(res["value"], 3),
         "unit": "merges/s",
         "n_gpus": 1,
-        "steps": len(wall),
+        "steps": len(res["wall"]),
         "warmup": args.warmup,
-        "ms_per_step": round(1e3 * total_wall / len(wall), 3),
+        "ms_per_step": round(res["ms_per_step"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -430,21 +508,19 @@ def main() -> int:
         "hbm_gbps_per_iteration": {"aggregate": round(hbm_agg, 1), "frac_of_peak": round(hbm_agg / HBM_PEAK_GBPS, 4),
                                    "p10": round(pct(per_it_gbps, 10), 1), "p50": round(pct(per_it_gbps, 50), 1),
                                    "p90": round(pct(per_it_gbps, 90), 1)},
-        "kernels_ms_per_step": {"k_merge": round(float(m_ms.sum()), 3), "k_merge_gbps": round(merge_gbps, 1),
-                                "table_sweeps": int(r.sweeps)},
-        "warmup_unprofiled_s": [round(x, 3) for x in warm_s],
+        "kernels_ms_per_step": {"k_merge": round(res["merge_ms_sum"], 3), "k_merge_gbps": round(merge_gbps, 1),
+                                "table_sweeps": res["sweeps"]},
+        "warmup_unprofiled_s": [round(x, 3) for x in res["warm_s"]],
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": (round(traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"])
-                                 if traffic else None),
-                     "traffic_detail": ({"read": round(traffic["fetch_bytes_per_launch"]),
-                                         "write": round(traffic["write_bytes_per_launch"]),
-                                         "launches": traffic["launches"],
-                                         "algorithmic_same_launches": round(traffic["algorithmic_bytes_per_launch"]),
-                                         "source": "profiles/traffic_%s_%s.json" % (dominant, spec.name)}
-                                        if traffic else None),
+                     # measured bytes per launch over the last committed window (the
+                     # steady state), beside the algorithmic bytes of the same launches
+                     "traffic": windows[-1]["measured"] if windows else None,
+                     "traffic_windows": windows,
+                     "traffic_source": ("profiles/traffic_%s_%s.json" % (dominant, spec.name)) if windows else None,
                      "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
+        "configs": configs,
         "inference": inference,
         "encoding": encoding,
     }
