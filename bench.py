@@ -58,12 +58,16 @@ def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(files=None) -> str:
+    """SHA-256 of the kernel sources: the given files of bpe_merge_amd/csrc,
+    or every header plus bpe.hip."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bpe_merge_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hpp"))) + [os.path.join(csrc, "bpe.hip")]:
+    paths = ([os.path.join(csrc, f) for f in files] if files else
+             sorted(glob.glob(os.path.join(csrc, "*.hpp"))) + [os.path.join(csrc, "bpe.hip")])
+    for f in paths:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -71,13 +75,13 @@ def kernel_sources_sha256() -> str:
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, only if it was taken on the kernel sources as they are now."""
+    summary, only if it was taken on the kernel's sources as they are now."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if t.get("kernel_sources_sha256") != kernel_sources_sha256(t.get("kernel_sources")):
         return None
     return t
 
@@ -258,11 +262,12 @@ def traffic_windows(workload: str, kernel: str):
     return out
 
 
-def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0):
+def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0, events=True, chunk=0):
     """Train spec's workload: warmup unprofiled jobs, then `steps` jobs with
-    a HIP event after each iteration's launch. Returns the measurements, the
-    last job's merges and tokens, and (cpu_reps > 0) the CPU oracle's timing
-    on the same bytes with the bit-identity check."""
+    a HIP event after each iteration's launch (without events: timed by the
+    wall clock only, for runs under a profiler). Returns the measurements,
+    the last job's merges and tokens, and (cpu_reps > 0) the CPU oracle's
+    timing on the same bytes with the bit-identity check."""
     log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
     data = corpus.generate(spec)
     sha = corpus.sha256(data)
@@ -276,6 +281,12 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
         prof = None
         if profiled:
             prof = st.profile(n_merges, per_iteration=True)
+        elif chunk:
+            # at most `chunk` launches in flight (a profiler that serialises
+            # dispatches keeps one record per queued launch)
+            for i in range(0, n_merges, chunk):
+                st.run(min(chunk, n_merges - i))
+                st.sync()
         else:
             st.run(n_merges)
             st.sync()
@@ -295,7 +306,7 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     wall, last, ref = [], None, None
     for i in range(steps):
         torch.cuda.synchronize()
-        dt, m, t, lengths, prof = step(True)
+        dt, m, t, lengths, prof = step(events)
         wall.append(dt)
         last = (m, t, lengths, prof)
         sig = (m.cpu().numpy().tobytes(), t.shape[0])
@@ -304,8 +315,13 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
         elif sig != ref:
             raise RuntimeError("timed steps of %s disagree" % spec.name)
         log("%s timed step %d: %.3f s, %d merges" % (spec.name, i + 1, dt, m.shape[0]))
-    m, t, lengths, (r, m_ms) = last
+    m, t, lengths, prof = last
     k = m.shape[0]
+    if prof is None:  # no per-iteration events: the job's wall time stands in
+        r = type("NoEvents", (), {"sweeps": -1})()
+        m_ms = np.full(k, 1e3 * wall[-1] / max(k, 1))
+    else:
+        r, m_ms = prof
     n_k = lengths[:k].astype(np.float64)
     n_k1 = lengths[1: k + 1].astype(np.float64)
     m_ms = m_ms[:k].astype(np.float64)
@@ -350,6 +366,10 @@ def main() -> int:
                     help="skip training: time inference and encoding with the merges saved in PATH (.npy) "
                          "by --save-merges")
     ap.add_argument("--inference-reps", type=int, default=20)
+    ap.add_argument("--no-iteration-events", action="store_true",
+                    help="time whole jobs only (no HIP event per iteration; for runs under a profiler)")
+    ap.add_argument("--run-chunk", type=int, default=0, metavar="K",
+                    help="with --no-iteration-events: enqueue K iterations at a time, waiting in between")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
     args = ap.parse_args()
@@ -401,7 +421,8 @@ def main() -> int:
 
     # the large workloads once, the others three times (median)
     cpu_reps = 0 if args.no_cpu_baseline else (1 if spec.n_bytes >= (256 << 20) else 3)
-    res = train_leg(bpe, corpus, spec, args.steps, args.warmup, np, torch, time, log, cpu_reps)
+    res = train_leg(bpe, corpus, spec, args.steps, args.warmup, np, torch, time, log, cpu_reps,
+                    events=not args.no_iteration_events, chunk=args.run_chunk)
     m, t, lengths, k = res["merges"], res["tokens"], res["lengths"], res["k"]
     m_ms, n_k, merge_bytes = res["m_ms"], res["n_k"], res["merge_bytes"]
     data, d, sha = res["data"], res["d"], res["sha"]
@@ -513,9 +534,10 @@ def main() -> int:
         "warmup_unprofiled_s": [round(x, 3) for x in res["warm_s"]],
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     # measured bytes per launch over the last committed window (the
-                     # steady state), beside the algorithmic bytes of the same launches
-                     "traffic": windows[-1]["measured"] if windows else None,
+                     # measured bytes per launch over the whole run (committed
+                     # rocprofv3 counters), beside the windows it was taken in
+                     "traffic": (next((w["measured"] for w in windows if w["launches"] == k), windows[-1]["measured"])
+                                 if windows else None),
                      "traffic_windows": windows,
                      "traffic_source": ("profiles/traffic_%s_%s.json" % (dominant, spec.name)) if windows else None,
                      "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
