@@ -275,6 +275,8 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     torch.cuda.synchronize()
     n_merges, tlog2 = spec.n_merges, spec.table_log2
 
+    usage = [0, 0, 0]
+
     def step(profiled: bool):
         t0 = time.perf_counter()
         st = bpe.State(d, table_log2=tlog2)
@@ -295,6 +297,7 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         lengths = st.lengths().cpu().numpy().astype(np.int64)
+        usage[:] = st.table_usage()
         st.free()
         return t1 - t0, merges, tokens, lengths, prof
 
@@ -330,7 +333,7 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     res = {"spec": spec, "data": data, "d": d, "sha": sha, "merges": m, "tokens": t, "lengths": lengths,
            "k": int(k), "wall": wall, "warm_s": warm_s, "value": k * len(wall) / total_wall,
            "ms_per_step": 1e3 * total_wall / len(wall), "m_ms": m_ms, "n_k": n_k, "merge_bytes": merge_bytes,
-           "sweeps": int(r.sweeps), "merge_ms_sum": float(m_ms.sum()),
+           "sweeps": int(r.sweeps), "merge_ms_sum": float(m_ms.sum()), "table_usage": list(usage),
            "merge_gbps": float(merge_bytes.sum() / (m_ms.sum() / 1e3) / 1e9) if k else 0.0}
     if cpu_reps:
         import oracle
@@ -490,6 +493,7 @@ def main() -> int:
                 "merges_done": r["k"], "merges_per_s": round(r["value"], 1), "s_per_job": round(r["ms_per_step"] / 1e3, 4),
                 "k_merge_ms": round(r["merge_ms_sum"], 3), "k_merge_gbps": round(r["merge_gbps"], 1),
                 "k_merge_frac_of_peak": round(frac, 4), "table_sweeps": r["sweeps"],
+                "table_slots_claimed": r["table_usage"][1], "table_claim_limit": r["table_usage"][2],
                 "final_tokens": int(r["tokens"].shape[0]),
                 "cpu_oracle_merges_per_s": round(r["cpu_merges_s"], 1) if "cpu_merges_s" in r else None,
                 "bit_identical_to_oracle": r.get("identical"),
@@ -522,6 +526,7 @@ def main() -> int:
             "n_merges": n_merges,
             "merges_done": int(k),
             "table_slots": T,
+            "table_slots_claimed": res["table_usage"][1],
             "final_tokens": int(t.shape[0]),
         },
         "symbols_per_s_per_merge": {"aggregate": sym_per_s_agg, "p10": pct(per_it_sym, 10),

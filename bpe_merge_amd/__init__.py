@@ -70,6 +70,7 @@ _SIGS = {
     "bpe_tokens": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "bpe_lengths": (ctypes.c_int, [_vp, _vp, _u32, ctypes.POINTER(_u32)]),
     "bpe_pair_counts": (ctypes.c_int, [_vp, _vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "bpe_table_usage": (ctypes.c_int, [_vp, ctypes.POINTER(_u32), ctypes.POINTER(_u32), ctypes.POINTER(_u32)]),
     "bpe_profile": (ctypes.c_int, [_vp, _u32, ctypes.POINTER(ProfileResult), _vp]),
     "bpe_replay": (ctypes.c_int, [_vp, _vp, _u32]),
     "bpe_encode": (ctypes.c_int, [_vp, _sz, _vp, _u32, _cfgp, _vp, _sz, ctypes.POINTER(_sz)]),
@@ -433,6 +434,12 @@ class State:
         out = torch.empty(max(c.value, 1), dtype=torch.int32, device=self.device)
         _check(_lib.bpe_lengths(self._h, out.data_ptr(), c.value, ctypes.byref(c)), "bpe_lengths")
         return out[: c.value]
+
+    def table_usage(self):
+        """bpe_table_usage: (slots, claimed slots, claim limit) of the pair table."""
+        a, b, c = _u32(0), _u32(0), _u32(0)
+        _check(_lib.bpe_table_usage(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "bpe_table_usage")
+        return a.value, b.value, c.value
 
     def pair_counts(self):
         """(keys, counts) int64 host arrays of the current pair table, sorted by key."""

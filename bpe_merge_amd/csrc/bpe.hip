@@ -73,10 +73,18 @@ uint32_t ceil_log2(size_t v) {
     return r;
 }
 
-uint32_t table_log2_for(size_t n, const bpe_config* cfg) {
+// The automatic table size for n bytes and up to n_merges merges. Claimed
+// slots (one per distinct pair the sequence ever holds) stay below 3n:
+// n - 1 pairs at the start, and at most two new ones per merge site, of
+// which there are at most n - 1 in all. Measured growth is far smaller:
+// 10-25 new keys per merge on word corpora, about 350 on runs of random
+// bytes; 512 per merge plus the 65,536 byte pairs bounds both. The table
+// is sized so that the smaller estimate stays under its 7/8 limit.
+uint32_t table_log2_for(size_t n, const bpe_config* cfg, uint32_t n_merges = BPE_MAX_MERGES) {
     if (cfg && cfg->table_log2) return cfg->table_log2;
-    uint32_t l = ceil_log2(n ? n : 1) + 1;
-    return std::min<uint32_t>(22, std::max<uint32_t>(12, l));
+    const uint64_t est = std::min<uint64_t>(3ull * (n ? n : 1), 65536ull + 512ull * n_merges);
+    const uint32_t l = ceil_log2(size_t(est + est / 7 + 1));
+    return std::min<uint32_t>(30, std::max<uint32_t>(12, l));
 }
 
 // Workgroups of the tag pass: enough to fill the chip, never more than
@@ -241,6 +249,7 @@ bpe_status event_pool(int device, size_t count, std::vector<hipEvent_t>** out) {
 bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_config* cfg, uint32_t tlog2,
                        const Layout& lay, bool may_allocate);
 void state_release(bpe_state* s);
+bpe_status init_state(const uint8_t* bytes, size_t n, const bpe_config* cfg, uint32_t n_merges, bpe_state** out);
 
 bpe_status enqueue_run(bpe_state* s, uint32_t n_merges, uint32_t* first) {
     if (size_t(s->requested) + n_merges > BPE_MAX_MERGES) {
@@ -279,6 +288,16 @@ const char* bpe_last_error(void) { return g_err.c_str(); }
 
 bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_state** out) {
     g_err.clear();
+    return init_state(bytes, n, cfg, BPE_MAX_MERGES, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+// bpe_init with the number of merges the caller will ask for (it sizes an
+// automatic table; BPE_MAX_MERGES if unknown).
+bpe_status init_state(const uint8_t* bytes, size_t n, const bpe_config* cfg, uint32_t n_merges, bpe_state** out) {
     if (!out) {
         set_err("out is NULL");
         return BPE_EINVAL;
@@ -289,7 +308,7 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
         return BPE_EINVAL;
     }
     if (!config_ok(n, cfg)) return BPE_EINVAL;
-    const uint32_t tlog2 = table_log2_for(n, cfg);
+    const uint32_t tlog2 = table_log2_for(n, cfg, n_merges);
     const Layout lay = layout_for(n, tlog2);
     if (cfg && cfg->workspace && cfg->workspace_bytes < lay.total) {
         set_err("workspace of %zu bytes is smaller than the %zu bytes needed", cfg->workspace_bytes, lay.total);
@@ -313,10 +332,6 @@ bpe_status bpe_init(const uint8_t* bytes, size_t n, const bpe_config* cfg, bpe_s
     *out = s;
     return BPE_OK;
 }
-
-}  // extern "C"
-
-namespace {
 
 // Fill a default-constructed state for bytes[0..n) (validated by the
 // caller) and enqueue tagging and the first count. With may_allocate, a
@@ -560,6 +575,21 @@ bpe_status bpe_lengths(bpe_state* s, uint32_t* out, uint32_t cap, uint32_t* n_ou
     return BPE_OK;
 }
 
+bpe_status bpe_table_usage(bpe_state* s, uint32_t* slots, uint32_t* claimed, uint32_t* limit) {
+    g_err.clear();
+    if (!s) {
+        set_err("state is NULL");
+        return BPE_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(s->device));
+    Ctl h;
+    const bpe_status st = read_ctl(s, &h);
+    if (slots) *slots = s->slots();
+    if (claimed) *claimed = h.used;
+    if (limit) *limit = table_limit(s->tlog2);
+    return st;
+}
+
 bpe_status bpe_pair_counts(bpe_state* s, uint32_t* keys, uint32_t* counts, size_t cap, size_t* n_out) {
     g_err.clear();
     if (!s || (cap && (!keys || !counts))) {
@@ -719,7 +749,7 @@ bpe_status bpe_train(const uint8_t* bytes, size_t n, uint32_t n_merges, const bp
     if (n_tokens) *n_tokens = 0;
     if (n == 0) return BPE_OK;
     bpe_state* s = nullptr;
-    bpe_status st = bpe_init(bytes, n, cfg, &s);
+    bpe_status st = init_state(bytes, n, cfg, n_merges, &s);
     if (st != BPE_OK) return st;
     st = bpe_run(s, n_merges);
     uint32_t done = 0;
@@ -802,7 +832,8 @@ bpe_status bpe_train_static(const uint8_t* bytes, size_t n, uint32_t n_merges, u
     if (n_tokens) *n_tokens = 0;
     if (n == 0) return BPE_OK;
     const uint32_t tlog2 =
-        table_log2 ? table_log2 : std::min<uint32_t>(BPE_STATIC_MAX_TABLE_LOG2, table_log2_for(n, nullptr));
+        table_log2 ? table_log2
+                   : std::min<uint32_t>(BPE_STATIC_MAX_TABLE_LOG2, table_log2_for(n, nullptr, n_merges));
     const Layout lay = layout_for(n, tlog2);
     if (lay.total > BPE_STATIC_SCRATCH_BYTES) {
         set_err("%zu bytes of workspace needed, the static workspace holds %u", lay.total, BPE_STATIC_SCRATCH_BYTES);

@@ -78,7 +78,12 @@ typedef struct {
 
 typedef struct {
     uint32_t table_log2;     /* global pair table of 2^table_log2 slots (8 B each);
-                                0 = automatic; otherwise 10..30                       */
+                                otherwise 10..30; 0 = automatic: room under the 7/8
+                                limit for min(3n, 65536 + 512 * merges) keys, where
+                                merges is bpe_train's n_merges (BPE_MAX_MERGES for
+                                bpe_init and bpe_workspace_bytes). Claimed keys never
+                                exceed 3n; an overflow is BPE_ETABLE, never a dropped
+                                count.                                                 */
     uint32_t flags;          /* 0, or BPE_FLAG_OVERSUBSCRIBE (a testing aid)           */
     void *stream;            /* hipStream_t all work is ordered on; NULL = the state
                                 creates and owns a blocking stream (ordered after the
@@ -98,7 +103,9 @@ typedef struct {
 typedef struct bpe_state bpe_state;
 
 /* Device workspace needed for a corpus of n bytes with this config (cfg may be
-   NULL for defaults). Host arithmetic only; 0 if n or the config is invalid. */
+   NULL for defaults; an automatic table is sized for up to BPE_MAX_MERGES
+   merges, so the result also suffices for bpe_train with any n_merges).
+   Host arithmetic only; 0 if n or the config is invalid. */
 size_t bpe_workspace_bytes(size_t n, const bpe_config *cfg);
 
 /*
@@ -194,6 +201,13 @@ bpe_status bpe_lengths(bpe_state *s, uint32_t *out, uint32_t cap, uint32_t *n_ou
    out), in table order; *n_out = number of distinct pairs. Both arrays are host or device, cap entries each; with cap
    0 only the number is returned, with cap below it BPE_EINVAL. */
 bpe_status bpe_pair_counts(bpe_state *s, uint32_t *keys, uint32_t *counts, size_t cap, size_t *n_out);
+
+/* The global pair table's size and use: *slots = 2^table_log2, *claimed =
+   slots holding a key (a key keeps its slot for the life of the state, so
+   this only grows, with the distinct pairs the corpus and its merges have
+   produced), *limit = the claims at which the table counts as full
+   (BPE_ETABLE). Any pointer may be NULL. Waits for the enqueued work. */
+bpe_status bpe_table_usage(bpe_state *s, uint32_t *slots, uint32_t *claimed, uint32_t *limit);
 
 /* Apply a given merge list as the state's next k iterations, in order
    (page "bpe - GPU BPE Tokenizer Pipeline", "Nedir bu ya?": a learned merge

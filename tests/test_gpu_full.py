@@ -125,6 +125,28 @@ def test_training_to_the_last_id(bpe, cfg, n_bytes):
                     oracle.trie_encode(text, om))
 
 
+@pytest.mark.timeout(600)
+def test_automatic_table_holds_a_corpus_past_the_old_default(bpe):
+    # 32 MiB of byte runs and random bytes trained to 20,000 merges claims
+    # about 4.6M pair-table slots, past the 3.67M a 2^22 table holds (the
+    # largest automatic size before it depended on the merge count)
+    spec = corpus.CONFIGS[5].scaled(32 << 20, n_merges=20000, seed=400 + 20000 % 97)
+    data = corpus.generate(spec)
+    _say("automatic table: %d bytes of runs, %d merges" % (spec.n_bytes, spec.n_merges))
+    d = _dev(data)
+    gm, gt = bpe.train(d, spec.n_merges)  # table_log2 0: automatic, from n and n_merges
+    om, ot, _ = oracle.train_chunks(data, spec.n_merges)
+    assert_same("merges", gm.cpu().numpy().astype(np.int64), om)
+    assert_same("tokens", gt.cpu().numpy().astype(np.uint32), ot)
+    with bpe.State(d) as st:  # bpe_init: automatic size for up to 65,280 merges
+        st.run(spec.n_merges)
+        assert st.sync() == spec.n_merges
+        slots, claimed, limit = st.table_usage()
+        _say("  slots %d, claimed %d, limit %d" % (slots, claimed, limit))
+        assert 3_670_016 < claimed <= limit < slots
+        assert_same("merges through bpe_init", st.merges().cpu().numpy().astype(np.int64), om)
+
+
 def _busy(torch):
     """Queue a few milliseconds of work on the current stream."""
     a = torch.randn(2048, 2048, device="cuda:0")
