@@ -1327,7 +1327,7 @@ struct bpe_encoder {
     uint32_t* status = nullptr;         // total, error flags, scratch used
     uint32_t* slices = nullptr;         // per-tile token slices
     size_t slices_cap = 0;
-    uint32_t* tiles = nullptr;          // cnt, ovf_pos, ovf_n, pfx
+    uint32_t* tiles = nullptr;          // cnt, ovf_pos, ovf_n, group sums
     size_t tiles_cap = 0;
     uint16_t* sym_g = nullptr;          // scratch of words too long for a tile's LDS
     size_t sym_cap = 0;
@@ -1355,15 +1355,25 @@ struct bpe_encoder {
 
 namespace {
 
-constexpr int ENC_TPB = 256;
+// The walk runs one wave per workgroup on 1 KiB tiles: its phases are
+// chained by barriers, and with one wave a barrier waits for nothing else
+// (256 MiB corpus: 256 threads on 4 KiB tiles 1.00 ms per walk, 128 on 2
+// KiB 0.92, 64 on 1 KiB 0.85). The insert pass keeps 256 threads on 4 KiB
+// tiles (faster there: 0.30 ms against 0.35 with 64).
+constexpr int ENC_TPB = 64;
+constexpr int INS_TPB = 256;
+constexpr int ENC_SCAN_TPB = 1024;
+constexpr int ENC_COPY_TPB = 256;
 constexpr int WC_FILL_TPB = 256;
-// The insert pass takes every WC_SAMPLE-th tile: frequent words occur in
-// most tiles, a word missed falls back to the walk's own encoding, and on
-// the 256 MiB corpus 2 measured best (1: 2.35 ms per run, 2: 2.11, 3: 2.16,
-// 4: 2.25; wider strides miss more words than they save in inserts).
+// The insert pass takes every WC_SAMPLE-th of its tiles: frequent words
+// occur in most tiles, a word missed falls back to the walk's own encoding,
+// and on the 256 MiB corpus 2 measured best (1: 2.35 ms per run, 2: 2.11,
+// 3: 2.16, 4: 2.25; wider strides miss more words than they save in
+// inserts).
 constexpr uint32_t WC_SAMPLE = 2;
-constexpr uint32_t WC_AUTO_MAX_LOG2 = 22;  // automatic size: 2^22 slots at most (512 MiB of records)
+constexpr uint32_t WC_AUTO_MAX_LOG2 = 22;  // automatic size: 2^22 slots at most (256 MiB of records)
 constexpr uint32_t ENC_TILE = ENC_TPB * 16;
+constexpr uint32_t INS_TILE = INS_TPB * 16;
 constexpr uint32_t ENC_CAP = ENC_TILE + ENC_TPB * bpek::TRIE_HALO_PER_THREAD;
 constexpr size_t ENC_SCRATCH_MAX = size_t(1) << 24;  // positions of long words per call
 
@@ -1386,8 +1396,9 @@ uint32_t enc_wc_log2(const bpe_encoder* e, size_t n) {
 bpe_status enc_pools(bpe_encoder* e, size_t n) {
     const size_t ntiles = (n + ENC_TILE - 1) / ENC_TILE;
     const size_t sc = enc_scratch_cap(n);
+    const size_t ngroups = (ntiles + bpek::ENC_GROUP - 1) / bpek::ENC_GROUP;
     bpe_status st = pool_grow(&e->slices, &e->slices_cap, ntiles * ENC_CAP, false);
-    if (st == BPE_OK) st = pool_grow(&e->tiles, &e->tiles_cap, 4 * size_t(trie_npad(uint32_t(ntiles))), false);
+    if (st == BPE_OK) st = pool_grow(&e->tiles, &e->tiles_cap, 3 * ntiles + ngroups, false);
     if (st == BPE_OK) st = pool_grow(&e->sym_g, &e->sym_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->nx_g, &e->nx_cap, sc, false);
     if (st == BPE_OK) st = pool_grow(&e->rk_g, &e->rk_cap, sc, false);
@@ -1399,7 +1410,8 @@ bpe_status enc_pools(bpe_encoder* e, size_t n) {
         const size_t slots = size_t(1) << l;
         bpe_status cs = pool_grow(&e->wc_key, &e->wc_key_cap, slots, false);
         if (cs == BPE_OK) cs = pool_grow(&e->wc_pos, &e->wc_pos_cap, slots, false);
-        if (cs == BPE_OK) cs = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, false);
+        // records start zeroed (never filled) and are never cleared
+        if (cs == BPE_OK) cs = pool_grow(&e->wc_rec, &e->wc_rec_cap, slots * bpek::WC_REC, true);
         if (cs != BPE_OK) {
             g_err.clear();
             l = 0;
@@ -1409,42 +1421,46 @@ bpe_status enc_pools(bpe_encoder* e, size_t n) {
     return st;
 }
 
+// The passes of one call on stream s: status init, the word cache's clear,
+// insert and fill (with a cache), the walk, the scan of the group sums and
+// the copy of the tokens to dst (their total to status[0]). ev, if given,
+// gets an event after the cache passes, the walk, the scan and the copy.
 bpe_status enc_enqueue(bpe_encoder* e, const uint8_t* src, uint32_t n, uint32_t* dst, hipStream_t s,
                        hipEvent_t* ev) {
     const uint32_t ntiles = (n + ENC_TILE - 1) / ENC_TILE;
-    const uint32_t npad = trie_npad(ntiles);
+    const uint32_t ngroups = (ntiles + bpek::ENC_GROUP - 1) / bpek::ENC_GROUP;
     uint32_t* cnt = e->tiles;
-    uint32_t* ovf_pos = cnt + npad;
-    uint32_t* ovf_n = ovf_pos + npad;
-    uint32_t* pfx = ovf_n + npad;
+    uint32_t* ovf_pos = cnt + ntiles;
+    uint32_t* ovf_n = ovf_pos + ntiles;
+    uint32_t* gsum = ovf_n + ntiles;
     const bpek::RankTable rt{e->rt, e->rt_mask, e->rt_probes, e->rt_bytes};
     const uint32_t l = e->wc_call_log2;  // set by enc_pools for this n
     bpek::WordCache wc{};
-    hipLaunchKernelGGL(bpek::k_enc_init, dim3(1), dim3(64), 0, s, e->status);
+    hipLaunchKernelGGL(bpek::k_enc_init, dim3(std::min<uint32_t>((ngroups + 255) / 256, e->clear_grid)), dim3(256),
+                       0, s, e->status, gsum, ngroups);
     if (l) {
         const uint32_t slots = 1u << l;
         wc = bpek::WordCache{e->wc_key, e->wc_pos, e->wc_rec, slots - 1,
                              e->wc_key_bits ? ~0u << (32 - e->wc_key_bits) : 0u};
         hipLaunchKernelGGL(bpek::k_wc_clear, dim3(std::min<uint32_t>((slots + 255) / 256, e->clear_grid)), dim3(256),
                            0, s, wc, slots);
-        const uint32_t stride = WC_SAMPLE;
-        hipLaunchKernelGGL(bpek::k_wc_insert<ENC_TPB>,
-                           dim3(std::min<uint32_t>((ntiles + stride - 1) / stride, e->insert_grid)), dim3(ENC_TPB),
-                           0, s, src, n, ntiles, stride, wc);
+        const uint32_t itiles = (n + INS_TILE - 1) / INS_TILE, stride = WC_SAMPLE;
+        hipLaunchKernelGGL(bpek::k_wc_insert<INS_TPB>,
+                           dim3(std::min<uint32_t>((itiles + stride - 1) / stride, e->insert_grid)), dim3(INS_TPB),
+                           0, s, src, n, itiles, stride, wc);
         hipLaunchKernelGGL(bpek::k_wc_fill<WC_FILL_TPB>,
                            dim3(std::min<uint32_t>((slots + 4 * WC_FILL_TPB - 1) / (4 * WC_FILL_TPB), e->fill_grid)),
                            dim3(WC_FILL_TPB), 0, s, src, n, wc, rt, slots);
     }
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     hipLaunchKernelGGL(bpek::k_enc_walk<ENC_TPB>, dim3(std::min<uint32_t>(ntiles, e->walk_grid)), dim3(ENC_TPB), 0,
-                       s, src, n, rt, e->slices, cnt, ovf_pos, ovf_n, ntiles, e->sym_g, e->nx_g, e->rk_g, e->ovf,
-                       e->status + 2, uint32_t(enc_scratch_cap(n)), e->status + 1, wc);
+                       s, src, n, rt, e->slices, cnt, ovf_pos, ovf_n, gsum, ntiles, e->sym_g, e->nx_g, e->rk_g,
+                       e->ovf, e->status, uint32_t(enc_scratch_cap(n)), wc);
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
-    hipLaunchKernelGGL(bpek::k_trie_scan<TRIE_SCAN_TPB>, dim3(1), dim3(TRIE_SCAN_TPB), 0, s, cnt, ovf_n, pfx,
-                       ntiles, npad, e->status);
+    hipLaunchKernelGGL(bpek::k_enc_gscan<ENC_SCAN_TPB>, dim3(1), dim3(ENC_SCAN_TPB), 0, s, gsum, ngroups, e->status);
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
-    hipLaunchKernelGGL(bpek::k_enc_copy<TRIE_COPY_TPB>, dim3(std::min<uint32_t>(ntiles, e->copy_grid)),
-                       dim3(TRIE_COPY_TPB), 0, s, e->slices, cnt, ovf_pos, ovf_n, pfx, e->ovf, dst, ntiles, ENC_CAP);
+    hipLaunchKernelGGL(bpek::k_enc_copy<ENC_COPY_TPB>, dim3(std::min<uint32_t>(ngroups, e->copy_grid)),
+                       dim3(ENC_COPY_TPB), 0, s, e->slices, cnt, ovf_pos, ovf_n, gsum, e->ovf, dst, ntiles, ENC_CAP);
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
     HIP_TRY(hipGetLastError());
     return BPE_OK;
@@ -1509,7 +1525,7 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
     if (hipGetDevice(&e->device) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, e->device) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_enc_walk<ENC_TPB>, ENC_TPB, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_ins, bpek::k_wc_insert<ENC_TPB>, ENC_TPB, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_ins, bpek::k_wc_insert<INS_TPB>, INS_TPB, 0) !=
             hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_fill, bpek::k_wc_fill<WC_FILL_TPB>, WC_FILL_TPB, 0) !=
             hipSuccess ||

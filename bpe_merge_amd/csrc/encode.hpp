@@ -171,18 +171,28 @@ __device__ __attribute__((noinline)) uint32_t encode_word_global(const uint8_t* 
 // bytes and that length equal the word's own; a word that finds no such
 // record (probes used up, a different word under its key) is encoded by the
 // walk itself.
-// A record is 32 u32 in two halves of 64 bytes; the first serves words of
-// up to WC_SHORT bytes alone: bytes 0-15 [0, 4), token ids 0-15 [4, 12)
-// (two per u32), token starts [12] (bit k: a token starts at offset k),
-// length [13] (0: the slot's position did not hold that many bytes); the
-// second holds bytes 16-31 [16, 20) and token ids 16-31 [20, 28).
-constexpr uint32_t WC_MAXLEN = 32;   // longest cached word
-constexpr uint32_t WC_SHORT = 16;    // longest word served by the first half
-constexpr uint32_t WC_REC = 32;      // u32 per record (128 bytes)
-constexpr uint32_t WC_HALF = 16;
-constexpr uint32_t WC_T0 = 4, WC_MASKW = 12, WC_LENW = 13, WC_B1 = 16, WC_T1 = 20;
+// The walk reads records only, never keys: one cache line per probe. A
+// record holds a word and its tokens under the encoder's merge list, so it
+// stays right for every later call and records are never cleared; the
+// record memory starts zeroed, and a record whose token-start word is 0
+// was never filled and ends a probe run, as a free slot ends the insert's.
+// A record is 16 u32 in two halves of 32 bytes; the first serves words of
+// up to WC_SHORT bytes with up to WC_TOK_SHORT tokens alone: bytes 0-15
+// [0, 4), length [4] (0: not cached: the slot's position did not hold that
+// many bytes, or the word has more than WC_TOK tokens), token starts [5]
+// (bit k: a token starts at offset k), token ids 0-3 [6, 8) (two per u32);
+// the second holds bytes 16-31 [8, 12) and token ids 4-11 [12, 16). A
+// short record keeps the records of a text's frequent words within the
+// caches: a walk lookup reads 32 bytes.
+constexpr uint32_t WC_MAXLEN = 32;    // longest cached word
+constexpr uint32_t WC_SHORT = 16;     // longest word served by the first half
+constexpr uint32_t WC_TOK = 12;       // most tokens a record holds
+constexpr uint32_t WC_TOK_SHORT = 4;  // tokens in the first half
+constexpr uint32_t WC_REC = 16;       // u32 per record (64 bytes)
+constexpr uint32_t WC_HALF = 8;
+constexpr uint32_t WC_LENW = 4, WC_MASKW = 5, WC_T0 = 6, WC_B1 = 8, WC_T1 = 12;
 constexpr uint32_t WC_PROBES = 8;
-constexpr uint32_t WC_BATCH = 2;     // words a walk thread looks up with their loads in flight together
+constexpr uint32_t WC_BATCH = 3;     // words a walk thread looks up with their loads in flight together
 
 struct WordCache {
     unsigned long long* key;   // per slot: 0 = free, else hash bits << 6 | length
@@ -256,13 +266,10 @@ __device__ __forceinline__ void wc_insert(const WordCache& wc, unsigned long lon
     }
 }
 
-// One probe: the slot's key into *v and the first NW words of its record
-// into r, loaded together.
+// One probe: the first NW words of the slot's record into r.
 template <uint32_t NW>
-__device__ __forceinline__ void wc_probe(const WordCache& wc, uint32_t slot, unsigned long long* v,
-                                         uint32_t (&r)[NW]) {
+__device__ __forceinline__ void wc_probe(const WordCache& wc, uint32_t slot, uint32_t (&r)[NW]) {
     typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-    *v = wc.key[slot];
     const uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
 #pragma unroll
     for (int k = 0; k < (int)NW / 4; ++k) {
@@ -274,30 +281,29 @@ __device__ __forceinline__ void wc_probe(const WordCache& wc, uint32_t slot, uns
     }
 }
 
-// Whether a probed slot (key v, record r: its first half, or all of it)
-// holds the packed word w of length len under key; with the first half
-// only, len <= WC_SHORT and w has 4 words.
+// Whether a probed record r (its first half, or all of it) holds the
+// packed word w of length len; with the first half only, len <= WC_SHORT
+// and w has 4 words.
 template <uint32_t NW, int NB>
-__device__ __forceinline__ bool wc_match(unsigned long long key, unsigned long long v, const uint32_t (&w)[NB],
-                                         uint32_t len, const uint32_t (&r)[NW]) {
+__device__ __forceinline__ bool wc_match(const uint32_t (&w)[NB], uint32_t len, const uint32_t (&r)[NW]) {
     static_assert(NB == (NW == WC_REC ? 8 : 4), "packed bytes match the record part");
     uint32_t d = r[WC_LENW] ^ len;
 #pragma unroll
     for (int k = 0; k < 4; ++k) d |= w[k] ^ r[k];
 #pragma unroll
     for (int k = 4; k < NB; ++k) d |= w[k] ^ r[WC_B1 + (k - 4)];
-    return v == key && d == 0u;
+    return d == 0u;
 }
 
-// The record holding the packed word w of length len (key, probing from
-// slot), into r; false if none before a free slot, within WC_PROBES slots.
-__device__ __forceinline__ bool wc_lookup(const WordCache& wc, unsigned long long key, uint32_t slot,
-                                          const uint32_t (&w)[8], uint32_t len, uint32_t (&r)[WC_REC]) {
+// The record holding the packed word w of length len (probing from slot),
+// into r; false if none before a never-filled record, within WC_PROBES
+// slots.
+__device__ __forceinline__ bool wc_lookup(const WordCache& wc, uint32_t slot, const uint32_t (&w)[8], uint32_t len,
+                                          uint32_t (&r)[WC_REC]) {
     for (uint32_t p = 0; p < WC_PROBES; ++p) {
-        unsigned long long v;
-        wc_probe<WC_REC>(wc, slot, &v, r);
-        if (wc_match(key, v, w, len, r)) return true;
-        if (v == 0ull) return false;
+        wc_probe<WC_REC>(wc, slot, r);
+        if (wc_match(w, len, r)) return true;
+        if (r[WC_MASKW] == 0u) return false;
         slot = (slot + 1u) & wc.mask;
     }
     return false;
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ tex
             uint32_t* rp = wc.rec + (size_t)slot * WC_REC;
             if (len > WC_MAXLEN || at > n || n - at < len) {
                 rp[WC_LENW] = 0u;
+                rp[WC_MASKW] = 1u;  // filled, matching no word
                 continue;
             }
             const uint8_t* src = text + at;
@@ -372,34 +379,56 @@ __global__ __launch_bounds__(TPB) void k_wc_fill(const uint8_t* __restrict__ tex
             uint32_t m = 0u, c = 0u;
             for (uint32_t x = b; x < b + len; x = s_nx[x], ++c) {
                 m |= 1u << (x - b);
-                if (c < 16u)
+                if (c < WC_TOK_SHORT)
                     t0[c] = s_sym[x];
-                else
-                    t1[c - 16u] = s_sym[x];
+                else if (c < WC_TOK)
+                    t1[c - WC_TOK_SHORT] = s_sym[x];
             }
             rp[WC_MASKW] = m;
-            rp[WC_LENW] = len;
+            rp[WC_LENW] = c <= WC_TOK ? len : 0u;  // more tokens than a record holds: not cached
         }
         lds_barrier();
     }
 }
 
-// The text of tile t in LDS (s_txt[p + 16 + mis] = text[t0 + p], TILE bytes
-// and the halo), the word starts inside the tile in s_sb, and *s_after,
-// the first class change in the halo (CAP if none). Returns this thread's
-// starts (bit k: position 16 tid + k) of words of two bytes or more and, in
-// *single, those of one-byte words. The caller clears *s_after to CAP
-// before; this clears s_sb and ends with the starts recorded.
-template <int TPB, uint32_t TILE, uint32_t CAP, uint32_t NCH>
-__device__ __forceinline__ uint32_t tile_words(__amdgpu_buffer_rsrc_t rs, uint32_t t0, uint32_t nrel, uint32_t sh,
-                                               uint8_t* s_txt, uint32_t* s_sb, uint32_t* s_after, uint32_t* single) {
+// A tile's text copy, [t0 - 16, t0 + 16 NCH - 16) in 16-byte chunks (zero
+// outside the text), held in registers from its load to its store into
+// LDS: a workgroup loads the next tile's text as it starts a tile, so the
+// load's latency passes while the tile is worked on.
+template <int TPB, uint32_t NCH>
+struct TileText {
+    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    static constexpr uint32_t R = (NCH + TPB - 1) / TPB;
+    v4 v[R];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t t0) {
+#pragma unroll
+        for (uint32_t j = 0; j < R; ++j) {
+            const uint32_t k = threadIdx.x + j * TPB;
+            if (k < NCH) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
+        }
+    }
+    // s_txt[16 k + i] = byte i of chunk k
+    __device__ __forceinline__ void store(uint8_t* s_txt) const {
+#pragma unroll
+        for (uint32_t j = 0; j < R; ++j) {
+            const uint32_t k = threadIdx.x + j * TPB;
+            if (k < NCH) *reinterpret_cast<v4*>(s_txt + 16u * k) = v[j];
+        }
+    }
+};
+
+// With the text of tile t stored in LDS (s_txt[p + 16 + mis] = text[t0 +
+// p], TILE bytes and the halo), the word starts inside the tile in s_sb,
+// and *s_after, the first class change in the halo (CAP if none). Returns
+// this thread's starts (bit k: position 16 tid + k) of words of two bytes
+// or more and, in *single, those of one-byte words. The caller clears
+// *s_after to CAP before; this clears s_sb and ends with the starts
+// recorded.
+template <int TPB, uint32_t TILE, uint32_t CAP>
+__device__ __forceinline__ uint32_t tile_words(uint32_t t0, uint32_t nrel, uint32_t sh, const uint8_t* s_txt,
+                                               uint32_t* s_sb, uint32_t* s_after, uint32_t* single) {
     const uint32_t tid = threadIdx.x;
     for (uint32_t i = tid; i < TILE / 32u; i += TPB) s_sb[i] = 0u;
-    for (uint32_t k = tid; k < NCH; k += TPB) {
-        typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-        const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, t0 - 16u + 16u * k, 0, 0);
-        *reinterpret_cast<v4*>(s_txt + 16u * k) = v;
-    }
     __syncthreads();
     uint32_t multi;
     {
@@ -469,13 +498,20 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
     const uint32_t sh = 16u + mis;
-    for (uint32_t tt = blockIdx.x; tt < (ntiles + stride - 1u) / stride; tt += gridDim.x) {
+    const uint32_t nsamp = (ntiles + stride - 1u) / stride;
+    for (uint32_t tt = blockIdx.x; tt < nsamp; tt += gridDim.x) {
         const uint32_t t = tt * stride;
         if (tid == 0) s_after = CAP;
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
+        {
+            // the previous tile's reads of s_txt ended before its last barrier
+            TileText<TPB, NCH> tx;
+            tx.load(rs, t0);
+            tx.store(s_txt);
+        }
         uint32_t single;
-        const uint32_t multi = tile_words<TPB, TILE, CAP, NCH>(rs, t0, nrel, sh, s_txt, s_sb, &s_after, &single);
+        const uint32_t multi = tile_words<TPB, TILE, CAP>(t0, nrel, sh, s_txt, s_sb, &s_after, &single);
         uint32_t nwords;
         uint32_t woff = block_exclusive_sum<TPB>(__popc(multi), s_w, &nwords);
         for (uint32_t m = multi; m; m &= m - 1u) s_list[woff++] = (uint16_t)(16u * tid + (__ffs(m) - 1));
@@ -495,23 +531,29 @@ __global__ __launch_bounds__(TPB) void k_wc_insert(const uint8_t* __restrict__ t
     }
 }
 
-// ---------------------------------------------------------------- pass 1
-// Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x, ...
-// Outputs for tile t, in its region of CAP words at tok32 + t * CAP: the
-// 16-bit ids of the tokens (i < cnt[t]) of the words starting in the tile
-// that end within CAP bytes of its start, and from word CAP / 2 on the bits
-// marking word starts among them; for a
-// last word running further, its tokens at ovf + ovf_pos[t] (ovf_n[t] of
-// them; NO_OVF / 0 otherwise), encoded in scratch reserved from *scratch_used
-// (capacity scratch_cap positions; past it *err is set and the word is
-// skipped). sym_g, nx_g, rk_g: the scratch arrays.
+// ---------------------------------------------------------------- the walk
+// Error flag of a call (status[1]): long words need more scratch than the
+// call has.
+constexpr uint32_t ENC_ERR_SCRATCH = 1u;
+constexpr uint32_t ENC_GROUP = 64;  // tiles per group sum
+
+// Tiles of TILE = 16 TPB bytes, t = blockIdx.x, blockIdx.x + gridDim.x,
+// ... A tile's tokens are those of the words starting in it: the words
+// ending within CAP bytes of its start are encoded in LDS, a last word
+// running further in scratch reserved from status[2] (capacity scratch_cap
+// positions; past it ENC_ERR_SCRATCH is set in status[1] and the word is
+// skipped; sym_g, nx_g, rk_g: the scratch arrays). Outputs for tile t, in
+// its region of CAP words at tok32 + t * CAP: the 16-bit ids of the cnt[t]
+// tokens encoded in LDS, and from word CAP / 2 on the bits marking word
+// starts among them; the long last word's tokens at ovf + ovf_pos[t]
+// (ovf_n[t] of them; NO_OVF / 0 otherwise). The tile's token count is
+// added to gsum[t / ENC_GROUP].
 template <int TPB>
-__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k_enc_walk(const uint8_t* __restrict__ text, uint32_t n, RankTable rt,
-                                                  uint32_t* __restrict__ tok32, uint32_t* __restrict__ cnt,
-                                                  uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
-                                                  uint32_t ntiles, uint16_t* sym_g, uint32_t* nx_g, uint16_t* rk_g,
-                                                  uint32_t* ovf, uint32_t* scratch_used, uint32_t scratch_cap,
-                                                  uint32_t* err, WordCache wc) {
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k_enc_walk(
+    const uint8_t* __restrict__ text, uint32_t n, RankTable rt, uint32_t* __restrict__ tok32,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ ovf_pos, uint32_t* __restrict__ ovf_n,
+    uint32_t* __restrict__ gsum, uint32_t ntiles, uint16_t* sym_g, uint32_t* nx_g, uint16_t* rk_g, uint32_t* ovf,
+    uint32_t* status, uint32_t scratch_cap, WordCache wc) {
     constexpr uint32_t TILE = TPB * 16u;
     constexpr uint32_t HALO = TPB * TRIE_HALO_PER_THREAD;
     constexpr uint32_t CAP = TILE + HALO;
@@ -529,8 +571,8 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
     __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after, s_nq;
     constexpr uint32_t DLIST = TILE / 2;  // with the cache: the queue's words at s_aux[DLIST..)
     // flags on a queued position: look the word up from its home slot (a
-    // word of more than WC_SHORT bytes), or from the slot after it (its home
-    // slot holds another key)
+    // word of more than WC_SHORT bytes or WC_TOK_SHORT tokens), or from the
+    // second slot after it (its home slot and the next hold other words)
     constexpr uint32_t RETRY = 0x8000u, RETRY_NEXT = 0x4000u;
     static_assert(CAP < RETRY_NEXT, "positions leave the flag bits free");
     static_assert(DLIST + TILE / 2 <= CAP, "word list and queue fit s_aux");
@@ -541,6 +583,8 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         const_cast<uint8_t*>(text - mis), 0, (int)((n + mis + 15u) & ~15u), 0x00020000);
     const LdsWord lw{s_sym, s_nx, s_rk};
     const uint32_t sh = 16u + mis;
+    uint32_t* const err = status + 1;
+    uint32_t* const scratch_used = status + 2;
 
     for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         if (tid == 0) {
@@ -553,10 +597,16 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         const uint32_t t0 = t * TILE;
         const uint32_t nrel = n - t0;
         auto lbyte = [&](uint32_t q) -> uint32_t { return s_txt[q + sh]; };  // q < CAP
+        {
+            // the previous tile's reads of s_txt ended before its compaction
+            TileText<TPB, NCH> tx;
+            tx.load(rs, t0);
+            tx.store(s_txt);
+        }
 
         // word starts: one-byte words are final here, the others listed
         uint32_t single;
-        const uint32_t multi = tile_words<TPB, TILE, CAP, NCH>(rs, t0, nrel, sh, s_txt, s_sb, &s_after, &single);
+        const uint32_t multi = tile_words<TPB, TILE, CAP>(t0, nrel, sh, s_txt, s_sb, &s_after, &single);
         // s_ws is read by the previous tile's last loop: cleared only past
         // the barrier in tile_words
         for (uint32_t i = tid; i < CAP / 32u; i += TPB) s_ws[i] = 0u;
@@ -600,9 +650,9 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (uint32_t i = q; i < wend; i = s_nx[i]) atomicOr(&s_flag[i >> 5], 1u << (i & 31u));
         };
         // a cached word at q: the token starts and ids of its record r (the
-        // first half for a word of up to WC_SHORT bytes)
+        // first half for a word of up to WC_SHORT bytes and WC_TOK_SHORT tokens)
         auto put_tokens = [&](uint32_t q, const auto& r) {
-            constexpr uint32_t NT = sizeof(r) / sizeof(r[0]) == WC_REC ? WC_MAXLEN : WC_SHORT;
+            constexpr uint32_t NT = sizeof(r) / sizeof(r[0]) == WC_REC ? WC_TOK : WC_TOK_SHORT;
             uint32_t m = r[WC_MASKW];
             const uint32_t o = q & 31u;
             atomicOr(&s_flag[q >> 5], m << o);
@@ -610,7 +660,8 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
             for (int k = 0; k < (int)NT; ++k) {
                 if (m) {
-                    const uint32_t two = k < 16 ? r[WC_T0 + k / 2] : r[WC_T1 + (k - 16) / 2];
+                    const uint32_t two = k < (int)WC_TOK_SHORT ? r[WC_T0 + k / 2]
+                                                               : r[WC_T1 + (k - (int)WC_TOK_SHORT) / 2];
                     s_sym[q + __ffs(m) - 1] = (uint16_t)(two >> (16 * (k & 1)));
                     m &= m - 1u;
                 }
@@ -618,16 +669,17 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         };
 
         // with the cache: every word of 2 .. WC_SHORT bytes takes its tokens
-        // from the first half of its home slot's record, WC_BATCH words per
-        // thread with their loads in flight together; the other words are listed
-        // for the queue, flagged when the queue should look them up (longer
-        // cached words, and short ones whose home slot holds another key)
+        // from the first half of the record in its home slot or the slot
+        // after it (where most words that lost their home slot to another
+        // went), WC_BATCH words per thread with their loads in flight
+        // together; the other words are listed for the queue, flagged when
+        // the queue should look them up (longer cached words, and short ones
+        // whose first two slots hold other words)
         const uint16_t* ql = s_aux;
         uint32_t nq = nwords;
         if (wc.key) {
             for (uint32_t i0 = tid; i0 < nwords; i0 += WC_BATCH * TPB) {
-                uint32_t q[WC_BATCH], len[WC_BATCH], slot[WC_BATCH], w[WC_BATCH][4], r[WC_BATCH][WC_HALF];
-                unsigned long long key[WC_BATCH], v[WC_BATCH];
+                uint32_t q[WC_BATCH], len[WC_BATCH], w[WC_BATCH][4], r[WC_BATCH][WC_HALF], r1[WC_BATCH][WC_HALF];
                 bool cand[WC_BATCH];
 #pragma unroll
                 for (int u = 0; u < (int)WC_BATCH; ++u) {
@@ -640,20 +692,26 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                     }
                     if (cand[u]) {
                         wc_pack_lds(s_txt, q[u] + sh, len[u], w[u]);
-                        const uint32_t h = wc_hash(w[u], len[u]);
-                        key[u] = wc_key(wc, h, len[u]);
-                        slot[u] = wc_slot(wc, h);
-                        wc_probe<WC_HALF>(wc, slot[u], &v[u], r[u]);
+                        const uint32_t home = wc_slot(wc, wc_hash(w[u], len[u]));
+                        wc_probe<WC_HALF>(wc, home, r[u]);
+                        wc_probe<WC_HALF>(wc, (home + 1u) & wc.mask, r1[u]);
                     }
                 }
 #pragma unroll
                 for (int u = 0; u < (int)WC_BATCH; ++u) {
                     const uint32_t i = i0 + (uint32_t)u * TPB;
                     if (i >= nwords) continue;
-                    if (cand[u] && wc_match(key[u], v[u], w[u], len[u], r[u]))
+                    const bool hit = cand[u] && wc_match(w[u], len[u], r[u]);
+                    const bool hit1 = cand[u] && !hit && r[u][WC_MASKW] && wc_match(w[u], len[u], r1[u]);
+                    if (hit && __popc(r[u][WC_MASKW]) <= WC_TOK_SHORT)
                         put_tokens(q[u], r[u]);
-                    else if (cand[u])
-                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (v[u] ? RETRY | RETRY_NEXT : 0u));
+                    else if (hit1 && __popc(r1[u][WC_MASKW]) <= WC_TOK_SHORT)
+                        put_tokens(q[u], r1[u]);
+                    else if (hit || hit1)  // more tokens than the first half holds: the whole record
+                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | RETRY);
+                    else if (cand[u])  // a never-filled record ends the probe run
+                        s_aux[DLIST + atomicAdd(&s_nq, 1u)] =
+                            (uint16_t)(q[u] | (r[u][WC_MASKW] && r1[u][WC_MASKW] ? RETRY | RETRY_NEXT : 0u));
                     else
                         s_aux[DLIST + atomicAdd(&s_nq, 1u)] = (uint16_t)(q[u] | (len[u] <= WC_MAXLEN ? RETRY : 0u));
                 }
@@ -683,14 +741,14 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                         q = ql[wi];
                         bool cached = false;
                         if (q & RETRY) {
-                            const uint32_t from = (q & RETRY_NEXT) ? 1u : 0u;
+                            const uint32_t from = (q & RETRY_NEXT) ? 2u : 0u;
                             q &= ~(RETRY | RETRY_NEXT);
                             wend = word_end<TILE>(s_sb, q, last_end);
                             const uint32_t len = wend - q;
                             uint32_t w[8], r[WC_REC];
                             wc_pack_lds(s_txt, q + sh, len, w);
                             const uint32_t h = wc_hash(w, len);
-                            if (wc_lookup(wc, wc_key(wc, h, len), (wc_slot(wc, h) + from) & wc.mask, w, len, r)) {
+                            if (wc_lookup(wc, (wc_slot(wc, h) + from) & wc.mask, w, len, r)) {
                                 put_tokens(q, r);
                                 cached = true;
                             }
@@ -712,15 +770,45 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
                     act = false;
                 }
             }
+            const unsigned long long gm = __ballot(gq != NO_OVF);
+            uint32_t e = 0u;
+            if (gm) {
+                // the open word's end: the first position past the copy with
+                // another class, or the text's end, searched by the wave 1 KiB
+                // at a time; the search stops once the word is longer than
+                // any call's scratch
+                const uint32_t g = (uint32_t)__shfl((int)gq, (int)(__ffsll((long long)gm) - 1));
+                const uint32_t cls = byte_class(lbyte(g));
+                const uint32_t lane = tid & 63u;
+                const uint32_t a0 = t0 + mis + lim;  // offset of position lim from text - mis
+                for (uint32_t c = a0 >> 4;; c += 64u) {
+                    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+                    const uint32_t ac = (c + lane) << 4;
+                    const v4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, ac, 0, 0);
+                    uint32_t stop = 0xFFFFFFFFu;
+#pragma unroll
+                    for (int k = 15; k >= 0; --k) {
+                        const uint32_t a = ac + (uint32_t)k;
+                        const uint32_t b = (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                        if (a >= a0 && (a - mis - t0 >= nrel || byte_class(b) != cls)) stop = a - mis - t0;
+                    }
+                    const unsigned long long sm = __ballot(stop != 0xFFFFFFFFu);
+                    if (sm) {
+                        e = (uint32_t)__shfl((int)stop, (int)(__ffsll((long long)sm) - 1));
+                        break;
+                    }
+                    const uint32_t past = ((c + 64u) << 4) - mis - t0;  // every position below is in the word
+                    if (past - g > scratch_cap) {
+                        e = past;
+                        break;
+                    }
+                }
+            }
             if (gq != NO_OVF) {
-                // the word's end: the first class change past the copy
-                const uint32_t cls = byte_class(lbyte(gq));
-                uint32_t e = lim;
-                while (e < nrel && byte_class(text[(size_t)t0 + e]) == cls) ++e;
                 const uint32_t len = e - gq;
                 const uint32_t at = atomicAdd(scratch_used, len);
                 if (at + len > scratch_cap || at + len < at) {
-                    atomicOr(err, 1u);
+                    atomicOr(err, ENC_ERR_SCRATCH);
                 } else {
                     s_ovf_pos = at;
                     s_ovf_n = encode_word_global(text, (size_t)t0 + gq, len, sym_g + at, nx_g + at, rk_g + at, rt,
@@ -741,11 +829,28 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
             bits = (uint32_t)(both >> sb) & (uint32_t)((1ull << PER) - 1ull);
         }
         uint32_t nlds;
-        uint32_t off = block_exclusive_sum<TPB>(__popc(bits), s_w, &nlds);
-        for (uint32_t m = bits; m; m &= m - 1u) {
-            const uint32_t i = PER * tid + (__ffs(m) - 1);
-            if (i < TILE && ((s_sb[i >> 5] >> (i & 31u)) & 1u)) atomicOr(&s_ws[off >> 5], 1u << (off & 31u));
-            s_aux[off++] = s_sym[i];
+        const uint32_t off = block_exclusive_sum<TPB>(__popc(bits), s_w, &nlds);
+        {
+            // the word starts among this thread's positions (none past the tile)
+            const uint32_t lo = PER * tid, wi = lo >> 5, sb = lo & 31u;
+            uint32_t wsp = 0u;
+            if (lo < TILE) {
+                const uint32_t w0 = s_sb[wi];
+                const uint32_t w1 = (wi + 1u < TILE / 32u) ? s_sb[wi + 1u] : 0u;
+                wsp = (uint32_t)((((unsigned long long)w1 << 32) | w0) >> sb);
+            }
+            // bit k of ws: this thread's k-th token starts a word
+            uint32_t ws = 0u, k = 0u;
+            for (uint32_t m = bits; m; m &= m - 1u, ++k) {
+                const uint32_t b = __ffs(m) - 1;
+                ws |= ((wsp >> b) & 1u) << k;
+                s_aux[off + k] = s_sym[PER * tid + b];
+            }
+            if (ws) {
+                const uint32_t o = off & 31u;
+                atomicOr(&s_ws[off >> 5], ws << o);
+                if (o && (ws >> (32u - o))) atomicOr(&s_ws[(off >> 5) + 1u], ws >> (32u - o));
+            }
         }
         __syncthreads();
         // the tile's region of CAP words: 16-bit ids from its start, the
@@ -758,50 +863,127 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
             cnt[t] = nlds;
             ovf_pos[t] = s_ovf_pos;
             ovf_n[t] = s_ovf_n;
+            atomicAdd(gsum + t / ENC_GROUP, nlds + s_ovf_n);
         }
     }
 }
 
-// status[0] total tokens (written by the scan), status[1] error flags,
-// status[2] scratch positions reserved
-__global__ void k_enc_init(uint32_t* status) {
-    if (threadIdx.x < 4u && blockIdx.x == 0) status[threadIdx.x] = 0u;
+// status[0..3] (total, error flags, scratch used, spare) and the group sums
+// gsum[0, ngroups) cleared.
+__global__ void k_enc_init(uint32_t* status, uint32_t* gsum, uint32_t ngroups) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 4u) status[i] = 0u;
+    for (uint32_t g = i; g < ngroups; g += gridDim.x * blockDim.x) gsum[g] = 0u;
 }
 
-// ---------------------------------------------------------------- pass 3: copy
+// Exclusive scan of the group sums in place (one workgroup, each thread a
+// contiguous run of them); the total into *total.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_enc_gscan(uint32_t* __restrict__ gsum, uint32_t ngroups, uint32_t* total) {
+    __shared__ uint32_t s_w[TPB / 64];
+    const uint32_t per = (ngroups + TPB - 1u) / TPB;
+    const uint32_t lo = min(ngroups, threadIdx.x * per), hi = min(ngroups, lo + per);
+    uint32_t sum = 0u;
+    for (uint32_t g = lo; g < hi; ++g) sum += gsum[g];
+    uint32_t all;
+    uint32_t run = block_exclusive_sum<TPB>(sum, s_w, &all);
+    for (uint32_t g = lo; g < hi; ++g) {
+        const uint32_t x = gsum[g];
+        gsum[g] = run;
+        run += x;
+    }
+    if (threadIdx.x == 0) *total = all;
+}
+
 // Tile slices (16-bit ids and word-start bits, as the walk leaves them) to
-// their places in out as 32-bit tokens, then the tokens of a tile's long
-// last word from the overflow area.
+// their places in out as 32-bit tokens, each tile's long last word's
+// tokens after its own from the overflow area. A workgroup takes a group
+// of ENC_GROUP tiles at a time: the tiles' counts and offsets within the
+// group into LDS, then every (tile, 8 of its first CPT tokens) pair of the
+// group, U pairs per thread with their loads in flight (consecutive
+// threads on consecutive pairs of a tile: 16-byte id loads); tokens past
+// CPT in a tile and the overflow tokens after.
 template <int TPB>
 __global__ __launch_bounds__(TPB) void k_enc_copy(const uint32_t* __restrict__ tok32,
                                                   const uint32_t* __restrict__ cnt,
                                                   const uint32_t* __restrict__ ovf_pos,
                                                   const uint32_t* __restrict__ ovf_n,
-                                                  const uint32_t* __restrict__ pfx, const uint32_t* __restrict__ ovf,
+                                                  const uint32_t* __restrict__ gpfx, const uint32_t* __restrict__ ovf,
                                                   uint32_t* __restrict__ out, uint32_t ntiles, uint32_t cap) {
-    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint32_t c = cnt[t], base = pfx[t], no = ovf_n[t];
-        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(tok32 + (size_t)t * cap);
-        const uint32_t* sws = tok32 + (size_t)t * cap + cap / 2u;
-        auto tok = [&](uint32_t i) -> uint32_t { return (uint32_t)s16[i] | (((sws[i >> 5] >> (i & 31u)) & 1u) << 16); };
-        {
-            // four tokens in flight per thread, then their stores (consecutive
-            // lanes on consecutive tokens: 16-byte stores of four tokens per
-            // lane measured slower here, the id and bit loads then spread)
-            uint32_t i = threadIdx.x;
-            for (; i + 3u * TPB < c; i += 4u * TPB) {
-                const uint32_t a0 = tok(i), a1 = tok(i + TPB), a2 = tok(i + 2u * TPB), a3 = tok(i + 3u * TPB);
-                out[base + i] = a0;
-                out[base + i + TPB] = a1;
-                out[base + i + 2u * TPB] = a2;
-                out[base + i + 3u * TPB] = a3;
+    static_assert(ENC_GROUP == 64 && TPB >= 64, "a group's counts are scanned by one wave");
+    constexpr uint32_t CPT = 512, PPT = CPT / 8u;  // tokens and pairs per tile in the main pass
+    constexpr uint32_t U = 4;
+    static_assert((ENC_GROUP * PPT) % (TPB * U) == 0, "pairs split evenly");
+    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t v4u __attribute__((ext_vector_type(4), aligned(4)));  // output: 4-byte aligned only
+    __shared__ uint32_t s_off[ENC_GROUP], s_c[ENC_GROUP], s_no[ENC_GROUP], s_op[ENC_GROUP];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t ngroups = (ntiles + ENC_GROUP - 1u) / ENC_GROUP;
+    for (uint32_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+        const uint32_t t0 = g * ENC_GROUP;
+        if (tid < 64u) {
+            const uint32_t t = t0 + tid;
+            const uint32_t c = t < ntiles ? cnt[t] : 0u, no = t < ntiles ? ovf_n[t] : 0u;
+            uint32_t x = c + no;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_up((int)x, o);
+                if (tid >= (uint32_t)o) x += y;
             }
-            for (; i < c; i += TPB) out[base + i] = tok(i);
+            s_off[tid] = x - c - no;
+            s_c[tid] = c;
+            s_no[tid] = no;
+            s_op[tid] = no ? ovf_pos[t] : 0u;
         }
-        if (no) {
-            const uint32_t* o = ovf + ovf_pos[t];
-            for (uint32_t i = threadIdx.x; i < no; i += TPB) out[base + c + i] = o[i];
+        __syncthreads();
+        uint32_t* o = out + gpfx[g];
+        for (uint32_t p0 = tid; p0 < ENC_GROUP * PPT; p0 += TPB * U) {
+            v4 ids[U];
+            uint32_t ws[U];
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) {
+                const uint32_t p = p0 + TPB * u, j = p / PPT, k = 8u * (p % PPT);
+                if (k < s_c[j]) {
+                    const uint32_t* r = tok32 + (size_t)(t0 + j) * cap;
+                    ids[u] = *reinterpret_cast<const v4*>(r + k / 2u);
+                    ws[u] = r[cap / 2u + k / 32u] >> (k & 31u);
+                }
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) {
+                const uint32_t p = p0 + TPB * u, j = p / PPT, k = 8u * (p % PPT);
+                const uint32_t c = s_c[j];
+                if (k < c) {
+                    uint32_t tk[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        tk[q] = ((ids[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu) | (((ws[u] >> q) & 1u) << 16);
+                    uint32_t* d = o + s_off[j] + k;
+                    if (k + 8u <= c) {
+                        *reinterpret_cast<v4u*>(d) = v4u{tk[0], tk[1], tk[2], tk[3]};
+                        *reinterpret_cast<v4u*>(d + 4) = v4u{tk[4], tk[5], tk[6], tk[7]};
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            if (k + (uint32_t)q < c) d[q] = tk[q];
+                    }
+                }
+            }
         }
+        // tokens past CPT (rare: a tile of mostly one-byte words), then the
+        // long words' tokens: one wave per tile
+        for (uint32_t j = tid >> 6; j < ENC_GROUP; j += TPB / 64u) {
+            const uint32_t c = s_c[j], no = s_no[j];
+            if (c <= CPT && !no) continue;
+            const uint16_t* s16 = reinterpret_cast<const uint16_t*>(tok32 + (size_t)(t0 + j) * cap);
+            const uint32_t* sws = tok32 + (size_t)(t0 + j) * cap + cap / 2u;
+            uint32_t* d = o + s_off[j];
+            for (uint32_t i = CPT + (tid & 63u); i < c; i += 64u)
+                d[i] = (uint32_t)s16[i] | (((sws[i >> 5] >> (i & 31u)) & 1u) << 16);
+            const uint32_t* ov = ovf + s_op[j];
+            for (uint32_t i = tid & 63u; i < no; i += 64u) d[c + i] = ov[i];
+        }
+        __syncthreads();
     }
 }
 

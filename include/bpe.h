@@ -250,15 +250,16 @@ bpe_status bpe_encoder_build(const bpe_merge *merges, uint32_t n_merges, bpe_enc
    NULL for the count only) receive the tokens, *n_tokens their count.
    With the word cache (bpe_encoder_cache; on by default from 1 MiB) three
    kernels first collect the distinct words of 2..32 bytes of every second
-   4 KiB tile and encode each once; then three kernels (walk, scan, copy),
-   a wait for the total and a sized copy for host tokens. Device buffers
-   are pooled in the encoder (about 5 bytes per input byte, the cache's 140
-   bytes per slot, plus scratch of 12 bytes per position for words that do
-   not fit a tile's LDS, at most 2^24 positions per call), so calls on one
-   encoder must not overlap. Errors: BPE_EINVAL (NULL encoder or n_tokens,
-   NULL bytes with n > 0, n > BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM
-   (also: words past a tile's LDS longer than the scratch in total),
-   BPE_EHIP. */
+   4 KiB tile and encode each once; then three kernels (the walk over 1 KiB
+   tiles, a scan of the token counts of groups of 64 tiles, the copy of
+   each tile's tokens to its place), a wait for the total and a sized copy
+   for host tokens. Device buffers are pooled in the encoder (about 5 bytes
+   per input byte, the cache's 76 bytes per slot, plus scratch of 12 bytes
+   per position for words that do not fit a tile's LDS, at most 2^24
+   positions per call), so calls on one encoder must not overlap. Errors:
+   BPE_EINVAL (NULL encoder or n_tokens, NULL bytes with n > 0, n >
+   BPE_MAX_BYTES, tokens_cap < n), BPE_ENOMEM (also: words past a tile's
+   LDS longer than the scratch in total), BPE_EHIP. */
 bpe_status bpe_encoder_encode(bpe_encoder *e, const uint8_t *bytes, size_t n, void *stream, uint32_t *tokens,
                               size_t tokens_cap, size_t *n_tokens);
 
