@@ -352,6 +352,92 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     return res
 
 
+def distinct_chunks(data, np):
+    """The distinct words of two bytes or more of a corpus (words: maximal
+    runs of one byte class), with their occurrence counts, by a 64-bit hash
+    of each word's bytes (up to 32 bytes; longer words are kept one per
+    occurrence). Returns (list of distinct words as bytes, counts array,
+    number of words of two bytes or more)."""
+    import oracle
+    cls = np.array([oracle.char_class(x) for x in range(256)], dtype=np.uint8)[data]
+    starts = np.flatnonzero(np.concatenate([[True], cls[1:] != cls[:-1]]))
+    lens = np.diff(np.append(starts, data.size))
+    multi = lens >= 2
+    st, ln = starts[multi], lens[multi]
+    short = ln <= 32
+    ss, sl = st[short], ln[short]
+    h = np.full(ss.size, np.uint64(1469598103934665603), dtype=np.uint64)
+    prime = np.uint64(1099511628211)
+    for k in range(32):
+        live = sl > k
+        b = np.where(live, data[np.minimum(ss + k, data.size - 1)], 0).astype(np.uint64)
+        h = np.where(live, (h ^ b) * prime, h)
+    h ^= sl.astype(np.uint64) << np.uint64(56)
+    _, first, counts = np.unique(h, return_index=True, return_counts=True)
+    words = [bytes(data[ss[i]: ss[i] + sl[i]]) for i in first]
+    longs = [bytes(data[a: a + b]) for a, b in zip(st[~short], ln[~short])]
+    return words + longs, np.concatenate([counts, np.ones(len(longs), dtype=counts.dtype)]), int(st.size)
+
+
+def chunk_study(args, bpe, corpus, spec, np, torch) -> dict:
+    """Design study: training over the distinct words of the corpus (each
+    once) instead of the whole symbol array. The GPU trains on the text of
+    the distinct words, each followed by a one-byte separator of another
+    class (the separators form no pairs), unweighted: the merge loop on an
+    array of that size is what a weighted version would run (one more
+    weight per symbol), so its per-merge time is measured here; the
+    weighted counts, and so the merges, would differ from this unweighted
+    run. The estimate adds a pass that finds the distinct words on the GPU
+    (the encoder's word-cache passes over the corpus, measured) and the
+    final tokens through the encoder (a learned list applied to its own
+    training text gives the training tokens; measured)."""
+    log("chunk study: generating %s" % spec.name)
+    data = corpus.generate(spec)
+    t0 = time.perf_counter()
+    words, counts, n_multi = distinct_chunks(data, np)
+    host_s = time.perf_counter() - t0
+    log("chunk study: %d words of 2+ bytes, %d distinct (host dedup %.1f s)" % (n_multi, len(words), host_s))
+    import oracle
+    seps = [ord(c) for c in "\n !0a"]
+    parts, prev = [], None
+    for w in words:
+        c = oracle.char_class(w[0])
+        if prev is not None:
+            parts.append(bytes([next(x for x in seps if oracle.char_class(x) not in (prev, c))]))
+        parts.append(w)
+        prev = c
+    text = np.frombuffer(b"".join(parts), dtype=np.uint8).copy()
+    d = torch.from_numpy(text).to("cuda:0")
+    k_req = spec.n_merges
+    runs = []
+    for i in range(1 + args.steps):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        with bpe.State(d) as st:
+            st.run(k_req)
+            k = st.sync()
+            m = st.merges()
+        torch.cuda.synchronize()
+        if i:
+            runs.append(time.perf_counter() - t1)
+    train_s = float(np.median(runs))
+    log("chunk study: %d merges on %d bytes in %.3f s (%.1f us per merge)" % (k, text.size, train_s,
+                                                                              1e6 * train_s / max(k, 1)))
+    d_full = torch.from_numpy(data).to("cuda:0")
+    with bpe.Encoder(m) as enc:
+        _, ms = enc.profile(d_full, 5)
+    ms = np.median(ms.astype(np.float64), axis=0)
+    dedup_ms, encode_ms = float(ms[0]), float(ms.sum())
+    total_s = dedup_ms / 1e3 + train_s + encode_ms / 1e3
+    return {"study": "training over the distinct words (chunk multiset), %s" % spec.name,
+            "words_2plus": n_multi, "distinct_words": len(words), "chunk_text_bytes": int(text.size),
+            "merges": int(k), "train_s": round(train_s, 4), "us_per_merge": round(1e6 * train_s / max(k, 1), 2),
+            "dedup_ms_gpu_stand_in": round(dedup_ms, 4), "final_encode_ms": round(encode_ms, 4),
+            "estimate_merges_s": round(k / total_s, 1),
+            "note": "unweighted training on the distinct-word text; dedup and final encoding measured with the "
+                    "encoder's passes; host dedup (numpy) %.1f s is not part of the estimate" % host_s}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,6 +459,8 @@ def main() -> int:
                     help="time whole jobs only (no HIP event per iteration; for runs under a profiler)")
     ap.add_argument("--run-chunk", type=int, default=0, metavar="K",
                     help="with --no-iteration-events: enqueue K iterations at a time, waiting in between")
+    ap.add_argument("--chunk-study", action="store_true",
+                    help="design study: time GPU training over the corpus's distinct words and print its JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
     args = ap.parse_args()
@@ -404,6 +492,10 @@ def main() -> int:
         spec = spec.scaled(spec.n_bytes, n_merges=args.merges)
     n_merges, tlog2 = spec.n_merges, spec.table_log2
     T = 1 << tlog2
+
+    if args.chunk_study:
+        print(json.dumps(chunk_study(args, bpe, corpus, spec, np, torch)), flush=True)
+        return 0
 
     if args.inference_only:
         log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))

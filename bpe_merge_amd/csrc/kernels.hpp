@@ -230,6 +230,37 @@ __device__ __forceinline__ void cand_append(Sweep* sw, uint32_t slot) {
     if (i < CAND_MAX) __hip_atomic_store(&sw->cand[i], slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// cand_append for the slots slot0 + k * stride (k < N) whose bit k of take
+// is set, for every lane of a wave at once, with one counter atomic per
+// wave (a sweep over a table of many equal small counts appends tens of
+// thousands of slots, and the list's counter is one address). Called by
+// all 64 lanes of the wave.
+template <int N>
+__device__ __forceinline__ void cand_append_wave(Sweep* sw, uint32_t slot0, uint32_t stride, uint32_t take) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t mine = (uint32_t)__popc(take);
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
+        if (lane >= (uint32_t)o) incl += y;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63);
+    if (total == 0u) return;
+    uint32_t base = 0u;
+    if (lane == 63u) base = atomicAdd(&sw->cand_n, total);
+    base = (uint32_t)__shfl((int)base, 63) + incl - mine;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if ((take >> k) & 1u) {
+            if (base < CAND_MAX)
+                __hip_atomic_store(&sw->cand[base], slot0 + (uint32_t)k * stride, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            ++base;
+        }
+    }
+}
+
 // gt_add for the merge pass: an increase that lifts the count from below
 // theta to theta or more appends the slot to the candidate list.
 __device__ __forceinline__ void gt_add_sel(const GTable& gt, uint32_t key, uint32_t delta, Ctl* ctl, Sweep* sw,

@@ -572,8 +572,11 @@ __device__ __forceinline__ uint32_t claim_chunk(uint32_t* ctr, uint32_t* s_u32) 
 // chunk c, or (COLLECT true) the chunk's slots whose count is theta or more
 // appended to the candidate list. Agent-coherent loads: other workgroups'
 // table adds reach memory, not this XCD's L2.
+// (Table sizes are powers of two of at least 1024 slots, so a wave's lanes
+// run the same rounds.)
 template <int TPB, bool COLLECT>
 __device__ __forceinline__ unsigned long long sweep_chunk(const GTable& gt, Sweep* sw, uint32_t c, uint32_t theta) {
+    static_assert(SWEEP_CHUNK % (64 * SWEEP_UNROLL) == 0, "whole waves per round");
     const uint32_t slots = gt.mask + 1u;
     const uint32_t end = min(slots, (c + 1u) * SWEEP_CHUNK);
     unsigned long long best = 0ull;
@@ -584,11 +587,14 @@ __device__ __forceinline__ unsigned long long sweep_chunk(const GTable& gt, Swee
             const uint32_t i = s0 + k * TPB;
             v[k] = i < end ? ld_agent(gt.slot + i) : 0ull;
         }
+        if (COLLECT) {
+            uint32_t take = 0u;  // slots past the end hold 0, below theta
 #pragma unroll
-        for (int k = 0; k < SWEEP_UNROLL; ++k) {
-            if (COLLECT) {
-                if ((uint32_t)(v[k] >> 32) >= theta) cand_append(sw, s0 + k * TPB);  // 0 past the end
-            } else {
+            for (int k = 0; k < SWEEP_UNROLL; ++k) take |= ((uint32_t)(v[k] >> 32) >= theta ? 1u : 0u) << k;
+            cand_append_wave<SWEEP_UNROLL>(sw, s0, TPB, take);
+        } else {
+#pragma unroll
+            for (int k = 0; k < SWEEP_UNROLL; ++k) {
                 const unsigned long long cv = candidate(v[k]);
                 best = cv > best ? cv : best;
             }
