@@ -207,6 +207,7 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
     avg_ms = float(ms.mean())
     enc_bytes = float(spec.n_bytes) + 4.0 * n_tok
     enc_gbps = enc_bytes / (avg_ms / 1e3) / 1e9
+    enc_traffic = measured_traffic(spec.name, "encode")
     cpu = None
     if gpu_sample is not None:
         import oracle
@@ -238,7 +239,10 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
                                "k_enc_copy": round(float(per_kernel[3]), 4)},
         "roofline": {"bound": "hbm", "kernel": "all passes", "achieved": round(enc_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": round(enc_bytes), "avg_launch_ms": round(avg_ms, 5)},
+                     "traffic": (round(enc_traffic["fetch_bytes_per_launch"] + enc_traffic["write_bytes_per_launch"])
+                                 if enc_traffic else None),
+                     "traffic_source": "profiles/traffic_encode_%s.json" % spec.name if enc_traffic else None,
+                     "bytes_per_launch": round(enc_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
     }
 
