@@ -235,7 +235,7 @@ def encode_leg(args, bpe, spec, data, d, m, np, time, log, source="learned above
         "ms_per_run": {"mean": round(avg_ms, 4), "min": round(float(ms.min()), 4), "max": round(float(ms.max()), 4)},
         "kernels_ms_per_run": {"word_cache": round(float(per_kernel[0]), 4),
                                "k_enc_walk": round(float(per_kernel[1]), 4),
-                               "k_trie_scan": round(float(per_kernel[2]), 4),
+                               "k_enc_gscan": round(float(per_kernel[2]), 4),
                                "k_enc_copy": round(float(per_kernel[3]), 4)},
         "roofline": {"bound": "hbm", "kernel": "all passes", "achieved": round(enc_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
