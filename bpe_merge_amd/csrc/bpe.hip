@@ -1538,7 +1538,7 @@ bpe_status bpe_encoder_build(const bpe_merge* merges, uint32_t n_merges, bpe_enc
     e->insert_grid = cus * per_cu_ins;
     e->fill_grid = cus * per_cu_fill;
     e->clear_grid = cus * 8;
-    e->copy_grid = cus * 8;
+    e->copy_grid = cus * 16;
     e->rt_mask = uint32_t(slots - 1);
     e->rt_probes = probes;
     // blocking, as the trie's: ordered after the legacy default stream

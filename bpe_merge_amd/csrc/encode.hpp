@@ -192,7 +192,7 @@ constexpr uint32_t WC_REC = 16;       // u32 per record (64 bytes)
 constexpr uint32_t WC_HALF = 8;
 constexpr uint32_t WC_LENW = 4, WC_MASKW = 5, WC_T0 = 6, WC_B1 = 8, WC_T1 = 12;
 constexpr uint32_t WC_PROBES = 8;
-constexpr uint32_t WC_BATCH = 3;     // words a walk thread looks up with their loads in flight together
+constexpr uint32_t WC_BATCH = 3;     // words a thread of the insert pass or the walk handles with their loads in flight together
 
 struct WordCache {
     unsigned long long* key;   // per slot: 0 = free, else hash bits << 6 | length
@@ -417,6 +417,21 @@ struct TileText {
     }
 };
 
+// The byte_class value of each byte of x, four at a time. Range tests are
+// subtractions on bytes that first get bit 7, so no borrow crosses a byte;
+// a byte of 0x80 or more is a letter whatever its low bits say.
+__device__ __forceinline__ uint32_t byte_class4(uint32_t x) {
+    const uint32_t H = 0x80808080u;
+    const uint32_t hi = x & H, lo = x & 0x7F7F7F7Fu;
+    const uint32_t t = lo | 0x20202020u | H, l = lo | H;  // t: ASCII letters in lower case
+    const uint32_t letter = hi | ((t - 0x61616161u) & ~(t - 0x7B7B7B7Bu) & H);
+    const uint32_t digit = (l - 0x30303030u) & ~(l - 0x3A3A3A3Au) & ~hi & H;
+    const uint32_t space = ~(((lo ^ 0x20202020u) | H) - 0x01010101u) & ~hi & H;
+    const uint32_t nl = ~(((lo ^ 0x0A0A0A0Au) | H) - 0x01010101u) & ~hi & H;
+    const uint32_t other = H & ~(letter | digit | space | nl);
+    return (digit >> 7) | (space >> 6) | (nl >> 5) | ((other >> 7) * 3u);
+}
+
 // With the text of tile t stored in LDS (s_txt[p + 16 + mis] = text[t0 +
 // p], TILE bytes and the halo), the word starts inside the tile in s_sb,
 // and *s_after, the first class change in the halo (CAP if none). Returns
@@ -432,18 +447,30 @@ __device__ __forceinline__ uint32_t tile_words(uint32_t t0, uint32_t nrel, uint3
     __syncthreads();
     uint32_t multi;
     {
+        // bit k of ch (k = 0..16): a class change between positions p0 + k - 1
+        // and p0 + k (or the text's first byte), from the classes of
+        // positions p0 .. p0 + 15 four at a time (aligned LDS words, shifted
+        // into place) and of the bytes on either side
         const uint32_t p0 = 16u * tid;
-        uint32_t pc = byte_class(s_txt[p0 - 1u + sh]);
-        uint32_t starts = 0, bnd = 0;
+        const uint32_t a = p0 + sh;  // LDS offset of position p0
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(s_txt) + (a >> 2);
+        uint32_t prev = byte_class(s_txt[a - 1u]), ch = 0u, lo = w[0];
 #pragma unroll
-        for (int k = 0; k <= 16; ++k) {
-            const uint32_t c = byte_class(s_txt[p0 + k + sh]);
-            const bool inside = p0 + k < nrel;
-            const bool change = c != pc || t0 + p0 + k == 0u;
-            if (k < 16) starts |= ((inside && change) ? 1u : 0u) << k;
-            if (k >= 1) bnd |= ((!inside || change) ? 1u : 0u) << k;
-            pc = c;
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t hi = w[j + 1];
+            const uint32_t code = byte_class4(__builtin_amdgcn_alignbyte(hi, lo, a & 3u));
+            lo = hi;
+            const uint32_t d = code ^ ((code << 8) | prev);            // bytes 0..7
+            const uint32_t nz = (d + 0x7F7F7F7Fu) & 0x80808080u;       // bit 7: byte nonzero
+            ch |= ((((nz >> 7) * 0x204081u) >> 21) & 0xFu) << (4 * j);  // the four bit 7s, packed
+            prev = code >> 24;
         }
+        ch |= (byte_class(s_txt[a + 16u]) != prev ? 1u : 0u) << 16;
+        if (t0 + p0 == 0u) ch |= 1u;
+        const uint32_t lim = nrel > p0 ? min(nrel - p0, 17u) : 0u;
+        const uint32_t inside = (1u << lim) - 1u;  // positions before the text's end
+        const uint32_t starts = inside & ch & 0xFFFFu;
+        const uint32_t bnd = (~inside | ch) & 0x1FFFEu;  // bit k: position p0 + k starts a word or is past the end
         *single = starts & (bnd >> 1);
         multi = starts & ~*single;
         if (starts) atomicOr(&s_sb[p0 >> 5], starts << (p0 & 31u));
@@ -479,9 +506,10 @@ __device__ __forceinline__ uint32_t word_end(const uint32_t* s_sb, uint32_t q, u
 
 // Insert pass: every stride-th tile of the walk's (tiles 0, stride, ...),
 // every word of 2 .. WC_MAXLEN bytes starting in it put into the cache.
-// (six waves per SIMD: the pass waits on its loads and claims; 256 MiB
-// corpus, 0.35 ms per pass with the compiler's register budget, 0.28 ms
-// with this one)
+// (six waves per SIMD and three words per thread with their loads in
+// flight: the pass waits on its loads and claims; 256 MiB corpus, 0.35 ms
+// per pass with the compiler's register budget and one word at a time,
+// 0.27-0.29 ms with both)
 template <int TPB>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6))) void k_wc_insert(const uint8_t* __restrict__ text, uint32_t n, uint32_t ntiles,
                                                    uint32_t stride, WordCache wc) {
@@ -521,14 +549,34 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(6))) void k
         lds_barrier();
         const uint32_t lim = nrel < CAP ? nrel : CAP;
         const uint32_t last_end = s_after < lim ? s_after : lim;
-        for (uint32_t i = tid; i < nwords; i += TPB) {
-            const uint32_t q = s_list[i];
-            const uint32_t len = word_end<TILE>(s_sb, q, last_end) - q;
-            if (len > WC_MAXLEN) continue;  // also a word running past the copy (its length here >= HALO)
-            uint32_t w[8];
-            wc_pack_lds(s_txt, q + sh, len, w);
-            const uint32_t h = wc_hash(w, len);
-            wc_insert(wc, wc_key(wc, h, len), wc_slot(wc, h), t0 + q);
+        // WC_BATCH words per thread with their home slots' keys loaded
+        // together; a word already in its home slot (most occurrences of
+        // frequent words) needs nothing more
+        for (uint32_t i0 = tid; i0 < nwords; i0 += WC_BATCH * TPB) {
+            uint32_t q[WC_BATCH], slot[WC_BATCH];
+            unsigned long long key[WC_BATCH], v[WC_BATCH];
+#pragma unroll
+            for (int u = 0; u < (int)WC_BATCH; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * TPB;
+                key[u] = 0ull;
+                if (i < nwords) {
+                    q[u] = s_list[i];
+                    const uint32_t len = word_end<TILE>(s_sb, q[u], last_end) - q[u];
+                    // a longer word (also one running past the copy: its
+                    // length here is at least HALO) is not cached
+                    if (len <= WC_MAXLEN) {
+                        uint32_t w[8];
+                        wc_pack_lds(s_txt, q[u] + sh, len, w);
+                        const uint32_t h = wc_hash(w, len);
+                        key[u] = wc_key(wc, h, len);
+                        slot[u] = wc_slot(wc, h);
+                        v[u] = wc.key[slot[u]];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < (int)WC_BATCH; ++u)
+                if (key[u] && v[u] != key[u]) wc_insert(wc, key[u], slot[u], t0 + q[u]);
         }
         __syncthreads();
     }
@@ -568,10 +616,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
     __shared__ uint32_t s_flag[CAP / 32u];             // token starts
     __shared__ uint32_t s_sb[TILE / 32u];              // word starts in the tile
     __shared__ uint16_t s_sym[CAP], s_nx[CAP], s_rk[CAP];
-    __shared__ uint16_t s_aux[CAP];                    // word list, then staged output ids
+    __shared__ __align__(4) uint16_t s_aux[CAP];       // word list, then staged output ids
     __shared__ uint32_t s_ws[CAP / 32u];               // staged output: word-start bits
     __shared__ uint32_t s_w[TPB / 64];
     __shared__ uint32_t s_ovf_pos, s_ovf_n, s_after, s_nq;
+    static_assert(CAP % 2u == 0, "ids are stored two at a time");
     constexpr uint32_t DLIST = TILE / 2;  // with the cache: the queue's words at s_aux[DLIST..)
     // flags on a queued position: look the word up from its home slot (a
     // word of more than WC_SHORT bytes or WC_TOK_SHORT tokens), or from the
@@ -858,9 +907,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(3))) void k
         __syncthreads();
         // the tile's region of CAP words: 16-bit ids from its start, the
         // word-start bits from word CAP / 2
-        uint16_t* d16 = reinterpret_cast<uint16_t*>(tok32 + (size_t)t * CAP);
+        // (two ids per 4-byte store; the one past an odd count lies inside
+        // the ids' part)
+        uint32_t* d16 = tok32 + (size_t)t * CAP;
         uint32_t* dws = tok32 + (size_t)t * CAP + CAP / 2u;
-        for (uint32_t i = tid; i < nlds; i += TPB) d16[i] = s_aux[i];
+        for (uint32_t i = tid; 2u * i < nlds; i += TPB) d16[i] = reinterpret_cast<const uint32_t*>(s_aux)[i];
         for (uint32_t i = tid; i < (nlds + 31u) / 32u; i += TPB) dws[i] = s_ws[i];
         if (tid == 0) {
             cnt[t] = nlds;
