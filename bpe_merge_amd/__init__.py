@@ -60,6 +60,8 @@ _SIGS = {
     "bpe_workspace_bytes": (_sz, [_sz, _cfgp]),
     "bpe_train": (ctypes.c_int, [_vp, _sz, _u32, _cfgp, _vp, ctypes.POINTER(_u32), _vp, _sz,
                                  ctypes.POINTER(_sz)]),
+    "bpe_train_chunked": (ctypes.c_int, [_vp, _sz, _u32, _cfgp, _vp, ctypes.POINTER(_u32), _vp, _sz,
+                                         ctypes.POINTER(_sz)]),
     "bpe_train_static": (ctypes.c_int, [_vp, _sz, _u32, _u32, _vp, _vp, ctypes.POINTER(_u32), _vp, _sz,
                                         ctypes.POINTER(_sz)]),
     "bpe_init": (ctypes.c_int, [_vp, _sz, _cfgp, ctypes.POINTER(_vp)]),
@@ -163,6 +165,28 @@ def train(data, n_merges: int, table_log2: int | None = None, flags: int = 0):
                         tokens.data_ptr(), tokens.numel(), ctypes.byref(n_tok))
     _check(st, "bpe_train")
     return merges[: n_done.value], tokens[: n_tok.value]
+
+
+def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bool = True):
+    """bpe_train_chunked on a uint8 CUDA tensor: training over the corpus's
+    distinct words, each weighted by its frequency. Returns (merges, tokens)
+    as train() does (tokens is None when tokens=False)."""
+    torch = _torch()
+    if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
+        raise TypeError("data must be a uint8 CUDA tensor")
+    data = data.contiguous().reshape(-1)
+    n = data.numel()
+    dev = data.device
+    merges = torch.empty((max(n_merges, 1), 3), dtype=torch.int32, device=dev)
+    tok = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if tokens else None
+    cfg = _config(table_log2, _stream_handle(dev))
+    n_done = _u32(0)
+    n_tok = _sz(0)
+    st = _lib.bpe_train_chunked(data.data_ptr() if n else None, n, n_merges, ctypes.byref(cfg), merges.data_ptr(),
+                                ctypes.byref(n_done), tok.data_ptr() if tokens else None,
+                                tok.numel() if tokens else 0, ctypes.byref(n_tok) if tokens else None)
+    _check(st, "bpe_train_chunked")
+    return merges[: n_done.value], (tok[: n_tok.value] if tokens else None)
 
 
 STATIC_SCRATCH_BYTES = 32 << 20

@@ -27,6 +27,7 @@
 #include "merge.hpp"
 #include "trie.hpp"
 #include "encode.hpp"
+#include "chunks.hpp"
 
 using bpek::Ctl;
 
@@ -1697,6 +1698,231 @@ bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, u
     st = bpe_encoder_encode(e, bytes, n, cfg ? cfg->stream : nullptr, tokens, tokens_cap, n_tokens);
     bpe_encoder_free(e);
     return st;
+}
+
+}  // extern "C"
+
+// ======================================================================== training over distinct words
+// bpe_train_chunked: bpe_train's results from the corpus's distinct words,
+// each once with its frequency (chunks.hpp). One call: the chunk passes, a
+// host wait for the chunk sizes, the chunk arrays, the weighted pair
+// counts, one launch per iteration, and the tokens from the encoder.
+
+namespace {
+
+// Device buffers of one call, freed together.
+struct DevBufs {
+    std::vector<void*> p;
+    template <typename T>
+    bpe_status get(T** out, size_t count) {
+        *out = nullptr;
+        if (!count) count = 1;
+        if (hipMalloc(reinterpret_cast<void**>(out), count * sizeof(T)) != hipSuccess) {
+            (void)hipGetLastError();
+            set_err("hipMalloc of %zu bytes failed", count * sizeof(T));
+            return BPE_ENOMEM;
+        }
+        p.push_back(*out);
+        return BPE_OK;
+    }
+    ~DevBufs() {
+        for (void* q : p) (void)hipFree(q);
+    }
+};
+
+constexpr int CK_TPB = 256;
+constexpr int CK_LT = 2048;   // LDS sums per workgroup (slots, or pairs)
+constexpr int CK_MERGE_TPB = 256;
+constexpr uint32_t CK_TILE = CK_TPB * 16;  // k_ck_count's tile
+
+// Word-table slots for n bytes: one per 128 bytes, a power of two in
+// [2^16, 2^24] (a word that finds no slot within the probe limit is kept
+// as a chunk of its own, so the size only moves work, never a result).
+uint32_t ck_table_log2(size_t n) {
+    uint32_t l = 16;
+    while (l < 24 && (size_t(1) << l) < n / 128) ++l;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, const bpe_config* cfg,
+                             bpe_merge* merges, uint32_t* n_done, uint32_t* tokens, size_t tokens_cap,
+                             size_t* n_tokens) {
+    g_err.clear();
+    if (!n_done || (!merges && n_merges) || (n && !bytes)) {
+        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_done must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    if (!config_ok(n, cfg)) return BPE_EINVAL;
+    if (cfg && cfg->workspace) {
+        set_err("bpe_train_chunked allocates its own memory (bpe_config.workspace must be NULL)");
+        return BPE_EINVAL;
+    }
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_done = 0;
+    if (n_tokens) *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    int dev = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    DevBufs mem;  // released last, after the stream has drained
+    hipStream_t s = cfg && cfg->stream ? reinterpret_cast<hipStream_t>(cfg->stream) : nullptr;
+    hipStream_t own = nullptr;
+    if (!s) {
+        HIP_TRY(hipStreamCreate(&own));  // blocking: ordered after the legacy default stream
+        s = own;
+    }
+    struct StreamGuard {
+        hipStream_t s, own;
+        ~StreamGuard() {
+            (void)hipStreamSynchronize(s);
+            if (own) (void)hipStreamDestroy(own);
+        }
+    } guard{s, own};
+    bpe_status st = BPE_OK;
+    auto launch_ok = [&]() -> bpe_status {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            set_err("kernel launch failed: %s", hipGetErrorString(e));
+            return BPE_EHIP;
+        }
+        return BPE_OK;
+    };
+
+    // the corpus on the device
+    const uint8_t* text = bytes;
+    if (!is_device_pointer(bytes)) {
+        uint8_t* t = nullptr;
+        if ((st = mem.get(&t, n)) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(t, bytes, n, hipMemcpyHostToDevice, s));
+        text = t;
+    }
+
+    // ---- the distinct words and their counts
+    const uint32_t wl = ck_table_log2(n), slots = 1u << wl;
+    unsigned long long* wkey = nullptr;
+    uint32_t *wpos = nullptr, *wrec = nullptr, *wcnt = nullptr, *lpos = nullptr, *llen = nullptr, *small = nullptr;
+    size_t lcap = n / 64 + 1024;  // listed words kept; the count runs again with room for all when more
+    if ((st = mem.get(&wkey, slots)) != BPE_OK || (st = mem.get(&wpos, slots)) != BPE_OK ||
+        (st = mem.get(&wrec, size_t(slots) * 8)) != BPE_OK || (st = mem.get(&wcnt, slots)) != BPE_OK ||
+        (st = mem.get(&lpos, lcap)) != BPE_OK || (st = mem.get(&llen, lcap)) != BPE_OK ||
+        (st = mem.get(&small, 8)) != BPE_OK)
+        return st;
+    const bpek::WordCache wc{wkey, wpos, wrec, slots - 1u, ~0u};  // 8 u32 of bytes per record here
+    const uint32_t ins_tiles = uint32_t((n + INS_TILE - 1) / INS_TILE);
+    const uint32_t ck_tiles = uint32_t((n + CK_TILE - 1) / CK_TILE);
+    const uint32_t sgrid = std::min<uint32_t>((slots + 255) / 256, cus * 8);
+    hipLaunchKernelGGL(bpek::k_wc_clear, dim3(sgrid), dim3(256), 0, s, wc, slots);
+    hipLaunchKernelGGL(bpek::k_wc_insert<INS_TPB>, dim3(std::min<uint32_t>(ins_tiles, cus * 8)), dim3(INS_TPB), 0, s,
+                       text, uint32_t(n), ins_tiles, 1u, wc);
+    hipLaunchKernelGGL(bpek::k_ck_record, dim3(sgrid), dim3(256), 0, s, text, uint32_t(n), wc, slots);
+    uint32_t h[4] = {0, 0, 0, 0};  // table chunks, their symbols, listed words
+    for (;;) {
+        const bpek::CkList list{lpos, llen, small + 2, uint32_t(lcap)};
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(sgrid), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(wcnt),
+                           size_t(slots / 2), 0ull);
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small),
+                           size_t(4), 0ull);
+        hipLaunchKernelGGL((bpek::k_ck_count<CK_TPB, CK_LT>), dim3(std::min<uint32_t>(ck_tiles, cus * 4)),
+                           dim3(CK_TPB), 0, s, text, uint32_t(n), ck_tiles, wc, wcnt, list);
+        hipLaunchKernelGGL(bpek::k_ck_size, dim3(sgrid), dim3(256), 0, s, wc, wcnt, slots, small);
+        if ((st = launch_ok()) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(h, small, sizeof h, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        if (h[2] <= lcap) break;
+        lcap = h[2];  // the same words again: the count is exact
+        if ((st = mem.get(&lpos, lcap)) != BPE_OK || (st = mem.get(&llen, lcap)) != BPE_OK) return st;
+    }
+    const bpek::CkList list{lpos, llen, small + 2, uint32_t(lcap)};
+    const uint32_t n_table = h[0], sym_table = h[1], n_list = h[2];
+    // the listed words' symbol offsets: their lengths, scanned in place
+    uint32_t* loff = nullptr;
+    if ((st = mem.get(&loff, size_t(n_list) + 1)) != BPE_OK) return st;
+    uint32_t sym_list = 0;
+    if (n_list) {
+        HIP_TRY(hipMemcpyAsync(loff, llen, sizeof(uint32_t) * n_list, hipMemcpyDeviceToDevice, s));
+        hipLaunchKernelGGL(bpek::k_enc_gscan<ENC_SCAN_TPB>, dim3(1), dim3(ENC_SCAN_TPB), 0, s, loff, n_list,
+                           small + 4);
+        if ((st = launch_ok()) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(&sym_list, small + 4, sizeof sym_list, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+    }
+    const size_t n_chunks = size_t(n_table) + n_list, n_sym = size_t(sym_table) + sym_list;
+    bpek::Chunks ck{};
+    if ((st = mem.get(&ck.sym, n_sym)) != BPE_OK || (st = mem.get(&ck.off, n_chunks)) != BPE_OK ||
+        (st = mem.get(&ck.len, n_chunks)) != BPE_OK || (st = mem.get(&ck.w, n_chunks)) != BPE_OK)
+        return st;
+    ck.n = uint32_t(n_chunks);
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small + 6),
+                       size_t(1), 0ull);
+    hipLaunchKernelGGL(bpek::k_ck_build, dim3(sgrid), dim3(256), 0, s,
+                       text, wc, wcnt, slots, list, loff, n_table, sym_table, ck, small + 6);
+    if ((st = launch_ok()) != BPE_OK) return st;
+
+    // ---- training state: control block, selection state, pair table, merges
+    const uint32_t tlog2 = table_log2_for(n, cfg, n_merges);
+    const size_t tslots = size_t(1) << tlog2;
+    Ctl* ctl = nullptr;
+    bpek::Sweep* sw = nullptr;
+    unsigned long long* table = nullptr;
+    uint32_t *dmerges = nullptr, *lengths = nullptr;
+    if ((st = mem.get(&ctl, 1)) != BPE_OK || (st = mem.get(&sw, 1)) != BPE_OK ||
+        (st = mem.get(&table, tslots)) != BPE_OK || (st = mem.get(&dmerges, 3 * size_t(BPE_MAX_MERGES))) != BPE_OK ||
+        (st = mem.get(&lengths, 2)) != BPE_OK)
+        return st;
+    const bpek::GTable gt{table, uint32_t(tslots - 1), table_limit(tlog2)};
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(sw),
+                       sizeof(bpek::Sweep) / 8, 0ull);
+    hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, table, tslots, bpek::GT_EMPTY);
+    hipLaunchKernelGGL((bpek::k_ck_pairs<CK_TPB, CK_LT>),
+                       dim3(std::max<uint32_t>(1, std::min<uint32_t>((ck.n + CK_TPB - 1) / CK_TPB, cus * 4))),
+                       dim3(CK_TPB), 0, s, ck, gt, ctl);
+    const uint32_t mgrid =
+        std::max<uint32_t>(1, std::min<uint32_t>((ck.n + CK_MERGE_TPB - 1) / CK_MERGE_TPB, cus * 4));
+    for (uint32_t it = 0; it < n_merges; ++it)
+        hipLaunchKernelGGL((bpek::k_ck_merge<CK_MERGE_TPB, CK_LT>), dim3(mgrid), dim3(CK_MERGE_TPB), 0, s, it, ctl,
+                           ck, gt, sw, dmerges);
+    if ((st = launch_ok()) != BPE_OK) return st;
+    Ctl hc;
+    HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (hc.err) {
+        if (hc.err & bpek::ERR_TABLE) {
+            set_err("the global pair table is full (%u of %zu slots claimed; give a larger table_log2)",
+                    table_limit(tlog2), tslots);
+            return BPE_ETABLE;
+        }
+        set_err("device error bits 0x%x", hc.err);
+        return BPE_ESTATE;
+    }
+    const uint32_t done = hc.k;
+    if (done) HIP_TRY(hipMemcpy(merges, dmerges, sizeof(bpe_merge) * done, hipMemcpyDefault));
+    *n_done = done;
+    // ---- the tokens: the learned list applied to its own training text
+    if (tokens || n_tokens) {
+        size_t nt = 0;
+        bpe_encoder* e = nullptr;
+        std::vector<bpe_merge> hm(done);
+        if (done) HIP_TRY(hipMemcpy(hm.data(), dmerges, sizeof(bpe_merge) * done, hipMemcpyDeviceToHost));
+        st = bpe_encoder_build(hm.data(), done, &e);
+        if (st != BPE_OK) return st;
+        st = bpe_encoder_encode(e, text, n, s, tokens, tokens ? tokens_cap : 0, &nt);
+        bpe_encoder_free(e);
+        if (st != BPE_OK) return st;
+        if (n_tokens) *n_tokens = nt;
+    }
+    return BPE_OK;
 }
 
 }  // extern "C"

@@ -149,6 +149,30 @@ bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, u
                             bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
                             size_t *n_tokens);
 
+/*
+ * bpe_train's results computed from the corpus's distinct words. Pairs are
+ * counted within words and merges never cross a word start (page "bpe - GPU
+ * BPE Tokenizer Pipeline", "Ne Yapar? 1" and "Nedir bu ya?"), so all
+ * occurrences of a word are rewritten alike and a pair's count is the sum,
+ * over the distinct words holding it, of the word's frequency times the
+ * pair's occurrences in it. Training runs on each distinct word of 2..32
+ * bytes once, with that weight (a word the word table cannot hold, longer
+ * ones included, is kept once per occurrence): the same counts, so the same
+ * merges, ties and counts included. The tokens are the learned list applied
+ * to the same bytes by the encoder (bpe_encoder_encode), which gives the
+ * training tokens. Arguments and results as bpe_train: merges (host or
+ * device), n_done (host), tokens (host or device, or NULL), tokens_cap,
+ * n_tokens (host, or NULL); cfg->table_log2 sizes the pair table as for
+ * bpe_train, cfg->stream orders the work (NULL: a stream of its own),
+ * cfg->flags are ignored and cfg->workspace must be NULL: the call allocates
+ * its own device memory (the word table, about 2 bytes of chunk symbols per
+ * distinct-word byte, the pair table) and frees it before returning. Blocks
+ * until done. Errors as bpe_train, and as bpe_encoder_encode for the tokens.
+ */
+bpe_status bpe_train_chunked(const uint8_t *bytes, size_t n, uint32_t n_merges, const bpe_config *cfg,
+                             bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
+                             size_t *n_tokens);
+
 /* Create a training state: tag bytes[0..n) (n >= 1) into symbols with the
    character classes of "Ne Yapar? 1" ("Satir Satir Analiz 1)") and count the
    pairs of iteration 0 into the global pair table ("Ne Yapar? 2").

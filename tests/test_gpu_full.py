@@ -8,6 +8,9 @@ all work is integer). The same corpus is then encoded with the learned list
 by the GPU encoder, which must give the oracle's training tokens (a learned
 list applied to its own training text reproduces training's result).
 
+Training over the distinct words (bpe_train_chunked) must give the same
+merges and tokens at every full size.
+
 The id-space test trains to the last id (65,535 = 256 + 65,279) on corpora
 small enough for the oracle to follow, checks that nothing more can be
 merged (BPE_EIDSPACE), and builds the encoder and the trie from the full
@@ -82,6 +85,12 @@ def test_full_size_workload_matches_oracle(bpe, cfg):
     with bpe.Encoder(gm) as enc:
         et = enc.encode(d).cpu().numpy().astype(np.uint32)
     assert_same("encoding of %s with its own merges" % spec.name, et, ot)
+    del gt, et
+    # training over the distinct words, each weighted by its frequency, gives the same
+    cm, ct = bpe.train_chunked(d, spec.n_merges, spec.table_log2)
+    _say("  chunked: %d merges, %d tokens" % (cm.shape[0], ct.shape[0]))
+    assert_same("chunked merges of %s" % spec.name, cm.cpu().numpy().astype(np.int64), om)
+    assert_same("chunked tokens of %s" % spec.name, ct.cpu().numpy().astype(np.uint32), ot)
 
 
 @pytest.mark.timeout(600)
