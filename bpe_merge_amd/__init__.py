@@ -29,6 +29,7 @@ BASE_VOCAB = 256
 MAX_MERGES = 65280
 MAX_BYTES = 0x7FFFFFFF
 FLAG_OVERSUBSCRIBE = 1  # testing aid: merge passes with 4x the resident workgroups
+FLAG_ALWAYS_CHUNKS = 2  # train_chunked: over the distinct words even where that saves no work
 
 
 class BpeError(RuntimeError):
@@ -167,10 +168,13 @@ def train(data, n_merges: int, table_log2: int | None = None, flags: int = 0):
     return merges[: n_done.value], tokens[: n_tok.value]
 
 
-def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bool = True):
+def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bool = True,
+                  always_chunks: bool = False):
     """bpe_train_chunked on a uint8 CUDA tensor: training over the corpus's
-    distinct words, each weighted by its frequency. Returns (merges, tokens)
-    as train() does (tokens is None when tokens=False)."""
+    distinct words, each weighted by its frequency (or over the full symbol
+    array where the distinct words would not save work, unless
+    always_chunks). Returns (merges, tokens) as train() does (tokens is
+    None when tokens=False)."""
     torch = _torch()
     if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):
         raise TypeError("data must be a uint8 CUDA tensor")
@@ -179,7 +183,7 @@ def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bo
     dev = data.device
     merges = torch.empty((max(n_merges, 1), 3), dtype=torch.int32, device=dev)
     tok = torch.empty(max(n, 1), dtype=torch.int32, device=dev) if tokens else None
-    cfg = _config(table_log2, _stream_handle(dev))
+    cfg = _config(table_log2, _stream_handle(dev), flags=FLAG_ALWAYS_CHUNKS if always_chunks else 0)
     n_done = _u32(0)
     n_tok = _sz(0)
     st = _lib.bpe_train_chunked(data.data_ptr() if n else None, n, n_merges, ctypes.byref(cfg), merges.data_ptr(),

@@ -134,7 +134,7 @@ bool config_ok(size_t n, const bpe_config* cfg) {
         return false;
     }
     if (cfg) {
-        if (cfg->flags & ~uint32_t(BPE_FLAG_OVERSUBSCRIBE)) {
+        if (cfg->flags & ~uint32_t(BPE_FLAG_OVERSUBSCRIBE | BPE_FLAG_ALWAYS_CHUNKS)) {
             set_err("bpe_config.flags holds an unknown bit (0x%x)", cfg->flags);
             return false;
         }
@@ -1704,9 +1704,12 @@ bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, u
 
 // ======================================================================== training over distinct words
 // bpe_train_chunked: bpe_train's results from the corpus's distinct words,
-// each once with its frequency (chunks.hpp). One call: the chunk passes, a
-// host wait for the chunk sizes, the chunk arrays, the weighted pair
-// counts, one launch per iteration, and the tokens from the encoder.
+// each once with its frequency (chunks.hpp). One call: the word passes, a
+// host wait for the chunk sizes, the chunks, the weighted pair counts, one
+// launch per iteration, and the tokens from the encoder. Where the chunks
+// would take more memory traffic per iteration than a quarter of the full
+// symbol array's first iteration (incompressible text: few repeated
+// words), bpe_train runs instead, unless BPE_FLAG_ALWAYS_CHUNKS is set.
 
 namespace {
 
@@ -1731,7 +1734,7 @@ struct DevBufs {
 };
 
 constexpr int CK_TPB = 256;
-constexpr int CK_LT = 2048;   // LDS sums per workgroup (slots, or pairs)
+constexpr int CK_LT = 2048;  // LDS sums per workgroup (slots, or pairs)
 constexpr int CK_MERGE_TPB = 256;
 constexpr uint32_t CK_TILE = CK_TPB * 16;  // k_ck_count's tile
 
@@ -1744,34 +1747,11 @@ uint32_t ck_table_log2(size_t n) {
     return l;
 }
 
-}  // namespace
-
-extern "C" {
-
-bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, const bpe_config* cfg,
-                             bpe_merge* merges, uint32_t* n_done, uint32_t* tokens, size_t tokens_cap,
-                             size_t* n_tokens) {
-    g_err.clear();
-    if (!n_done || (!merges && n_merges) || (n && !bytes)) {
-        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_done must be non-NULL");
-        return BPE_EINVAL;
-    }
-    if (n_merges > BPE_MAX_MERGES) {
-        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
-        return BPE_EIDSPACE;
-    }
-    if (!config_ok(n, cfg)) return BPE_EINVAL;
-    if (cfg && cfg->workspace) {
-        set_err("bpe_train_chunked allocates its own memory (bpe_config.workspace must be NULL)");
-        return BPE_EINVAL;
-    }
-    if (tokens && tokens_cap < n) {
-        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
-        return BPE_EINVAL;
-    }
-    *n_done = 0;
-    if (n_tokens) *n_tokens = 0;
-    if (n == 0) return BPE_OK;
+// The work of bpe_train_chunked on the device; *full set (and nothing
+// else done) when the full-array path is to run instead.
+bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, const bpe_config* cfg,
+                         bpe_merge* merges, uint32_t* n_done, uint32_t* tokens, size_t tokens_cap,
+                         size_t* n_tokens, bool* full) {
     int dev = 0, cus = 0;
     HIP_TRY(hipGetDevice(&dev));
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
@@ -1798,6 +1778,7 @@ bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, 
         }
         return BPE_OK;
     };
+    const bool always = cfg && (cfg->flags & BPE_FLAG_ALWAYS_CHUNKS);
 
     // the corpus on the device
     const uint8_t* text = bytes;
@@ -1816,7 +1797,7 @@ bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, 
     if ((st = mem.get(&wkey, slots)) != BPE_OK || (st = mem.get(&wpos, slots)) != BPE_OK ||
         (st = mem.get(&wrec, size_t(slots) * 8)) != BPE_OK || (st = mem.get(&wcnt, slots)) != BPE_OK ||
         (st = mem.get(&lpos, lcap)) != BPE_OK || (st = mem.get(&llen, lcap)) != BPE_OK ||
-        (st = mem.get(&small, 8)) != BPE_OK)
+        (st = mem.get(&small, 16)) != BPE_OK)
         return st;
     const bpek::WordCache wc{wkey, wpos, wrec, slots - 1u, ~0u};  // 8 u32 of bytes per record here
     const uint32_t ins_tiles = uint32_t((n + INS_TILE - 1) / INS_TILE);
@@ -1826,47 +1807,45 @@ bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, 
     hipLaunchKernelGGL(bpek::k_wc_insert<INS_TPB>, dim3(std::min<uint32_t>(ins_tiles, cus * 8)), dim3(INS_TPB), 0, s,
                        text, uint32_t(n), ins_tiles, 1u, wc);
     hipLaunchKernelGGL(bpek::k_ck_record, dim3(sgrid), dim3(256), 0, s, text, uint32_t(n), wc, slots);
-    uint32_t h[4] = {0, 0, 0, 0};  // table chunks, their symbols, listed words
+    // small: [0] the table's chunks, [2..4] listed words (all, long ones,
+    // their bytes), [8..10] the build's counters
+    uint32_t h[5] = {0, 0, 0, 0, 0};
     for (;;) {
         const bpek::CkList list{lpos, llen, small + 2, uint32_t(lcap)};
         hipLaunchKernelGGL(bpek::k_fill64, dim3(sgrid), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(wcnt),
                            size_t(slots / 2), 0ull);
         hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small),
-                           size_t(4), 0ull);
+                           size_t(8), 0ull);
         hipLaunchKernelGGL((bpek::k_ck_count<CK_TPB, CK_LT>), dim3(std::min<uint32_t>(ck_tiles, cus * 4)),
                            dim3(CK_TPB), 0, s, text, uint32_t(n), ck_tiles, wc, wcnt, list);
-        hipLaunchKernelGGL(bpek::k_ck_size, dim3(sgrid), dim3(256), 0, s, wc, wcnt, slots, small);
+        hipLaunchKernelGGL(bpek::k_ck_size<256>, dim3(sgrid), dim3(256), 0, s, wcnt, slots, small);
         if ((st = launch_ok()) != BPE_OK) return st;
         HIP_TRY(hipMemcpyAsync(h, small, sizeof h, hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
+        // records of 64 bytes, long chunks' 16-bit symbols; against 8 bytes
+        // per symbol of the full array's first iteration
+        const size_t n_rec = size_t(h[0]) + (h[2] - h[3]);
+        if (!always && 64 * n_rec + 2 * size_t(h[4]) > 2 * n) {
+            *full = true;
+            return BPE_OK;
+        }
         if (h[2] <= lcap) break;
         lcap = h[2];  // the same words again: the count is exact
         if ((st = mem.get(&lpos, lcap)) != BPE_OK || (st = mem.get(&llen, lcap)) != BPE_OK) return st;
     }
     const bpek::CkList list{lpos, llen, small + 2, uint32_t(lcap)};
-    const uint32_t n_table = h[0], sym_table = h[1], n_list = h[2];
-    // the listed words' symbol offsets: their lengths, scanned in place
-    uint32_t* loff = nullptr;
-    if ((st = mem.get(&loff, size_t(n_list) + 1)) != BPE_OK) return st;
-    uint32_t sym_list = 0;
-    if (n_list) {
-        HIP_TRY(hipMemcpyAsync(loff, llen, sizeof(uint32_t) * n_list, hipMemcpyDeviceToDevice, s));
-        hipLaunchKernelGGL(bpek::k_enc_gscan<ENC_SCAN_TPB>, dim3(1), dim3(ENC_SCAN_TPB), 0, s, loff, n_list,
-                           small + 4);
-        if ((st = launch_ok()) != BPE_OK) return st;
-        HIP_TRY(hipMemcpyAsync(&sym_list, small + 4, sizeof sym_list, hipMemcpyDeviceToHost, s));
-        HIP_TRY(hipStreamSynchronize(s));
-    }
-    const size_t n_chunks = size_t(n_table) + n_list, n_sym = size_t(sym_table) + sym_list;
+    const uint32_t n_list = h[2];
     bpek::Chunks ck{};
-    if ((st = mem.get(&ck.sym, n_sym)) != BPE_OK || (st = mem.get(&ck.off, n_chunks)) != BPE_OK ||
-        (st = mem.get(&ck.len, n_chunks)) != BPE_OK || (st = mem.get(&ck.w, n_chunks)) != BPE_OK)
+    ck.nr = h[0] + (h[2] - h[3]);
+    ck.nl = h[3];
+    if ((st = mem.get(&ck.rec, 4 * size_t(ck.nr))) != BPE_OK || (st = mem.get(&ck.rlen, ck.nr)) != BPE_OK ||
+        (st = mem.get(&ck.rw, ck.nr)) != BPE_OK || (st = mem.get(&ck.lsym, h[4])) != BPE_OK ||
+        (st = mem.get(&ck.loff, ck.nl)) != BPE_OK || (st = mem.get(&ck.llen, ck.nl)) != BPE_OK)
         return st;
-    ck.n = uint32_t(n_chunks);
-    hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small + 6),
-                       size_t(1), 0ull);
-    hipLaunchKernelGGL(bpek::k_ck_build, dim3(sgrid), dim3(256), 0, s,
-                       text, wc, wcnt, slots, list, loff, n_table, sym_table, ck, small + 6);
+    hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small + 8),
+                       size_t(2), 0ull);
+    hipLaunchKernelGGL(bpek::k_ck_build<256>, dim3(sgrid), dim3(256), 0, s, text, wc, wcnt, slots, list, n_list, ck,
+                       small + 8);
     if ((st = launch_ok()) != BPE_OK) return st;
 
     // ---- training state: control block, selection state, pair table, merges
@@ -1885,13 +1864,13 @@ bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, 
                        sizeof(bpek::Sweep) / 8, 0ull);
     hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, table, tslots, bpek::GT_EMPTY);
-    hipLaunchKernelGGL((bpek::k_ck_pairs<CK_TPB, CK_LT>),
-                       dim3(std::max<uint32_t>(1, std::min<uint32_t>((ck.n + CK_TPB - 1) / CK_TPB, cus * 4))),
-                       dim3(CK_TPB), 0, s, ck, gt, ctl);
-    const uint32_t mgrid =
-        std::max<uint32_t>(1, std::min<uint32_t>((ck.n + CK_MERGE_TPB - 1) / CK_MERGE_TPB, cus * 4));
+    // one workgroup per CU: more only add to the selection's wait and the
+    // publication's polls (each thread has CK_PF records in flight anyway)
+    const uint32_t nmax = std::max(ck.nr, ck.nl);
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>((nmax + CK_MERGE_TPB - 1) / CK_MERGE_TPB, cus));
+    hipLaunchKernelGGL((bpek::k_ck_pairs<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, ck, gt, ctl);
     for (uint32_t it = 0; it < n_merges; ++it)
-        hipLaunchKernelGGL((bpek::k_ck_merge<CK_MERGE_TPB, CK_LT>), dim3(mgrid), dim3(CK_MERGE_TPB), 0, s, it, ctl,
+        hipLaunchKernelGGL((bpek::k_ck_merge<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, it, ctl,
                            ck, gt, sw, dmerges);
     if ((st = launch_ok()) != BPE_OK) return st;
     Ctl hc;
@@ -1923,6 +1902,41 @@ bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, 
         if (n_tokens) *n_tokens = nt;
     }
     return BPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpe_status bpe_train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, const bpe_config* cfg,
+                             bpe_merge* merges, uint32_t* n_done, uint32_t* tokens, size_t tokens_cap,
+                             size_t* n_tokens) {
+    g_err.clear();
+    if (!n_done || (!merges && n_merges) || (n && !bytes)) {
+        set_err("bytes (when n > 0), merges (when n_merges > 0) and n_done must be non-NULL");
+        return BPE_EINVAL;
+    }
+    if (n_merges > BPE_MAX_MERGES) {
+        set_err("%u merges exceed the id space (%u merges)", n_merges, BPE_MAX_MERGES);
+        return BPE_EIDSPACE;
+    }
+    if (!config_ok(n, cfg)) return BPE_EINVAL;
+    if (cfg && cfg->workspace) {
+        set_err("bpe_train_chunked allocates its own memory (bpe_config.workspace must be NULL)");
+        return BPE_EINVAL;
+    }
+    if (tokens && tokens_cap < n) {
+        set_err("tokens_cap %zu is below n = %zu", tokens_cap, n);
+        return BPE_EINVAL;
+    }
+    *n_done = 0;
+    if (n_tokens) *n_tokens = 0;
+    if (n == 0) return BPE_OK;
+    bool full = false;
+    const bpe_status st = train_chunked(bytes, n, n_merges, cfg, merges, n_done, tokens, tokens_cap, n_tokens, &full);
+    if (st != BPE_OK || !full) return st;
+    // the chunk buffers are freed: the full-array path, same results
+    return bpe_train(bytes, n, n_merges, cfg, merges, n_done, tokens, tokens_cap, n_tokens);
 }
 
 }  // extern "C"

@@ -15,16 +15,20 @@
 //     counts there (summed per workgroup in LDS first); a word without one
 //     (longer, or lost to the probe limit) goes to a list of its own, one
 //     chunk per occurrence;
-//   k_ck_size, k_ck_build: the chunks (slots with a count, then the listed
-//     words) with their symbols, lengths and weights.
+//   k_ck_size, k_ck_build: the chunks with their symbols and weights. A
+//     chunk of at most CK_MAXW symbols (the table's words, weighted by
+//     their counts, and the short listed words) is a 64-byte record of
+//     16-bit symbols, zero past its length, which one thread reads with
+//     four 16-byte loads; a longer one (weight 1) lies in an array of its
+//     own.
 // k_ck_pairs counts the chunks' pairs into the global pair table, and
 // k_ck_merge runs one iteration: the selection of merge.hpp (ticket 0 of a
-// counter selects from the candidate list or calls a sweep, and publishes),
-// then every chunk containing the pair is rewritten in place (left to
-// right, without overlap) and its count changes are summed in LDS and
-// added to the table. The tokens of the whole corpus come from the
-// encoder afterwards: a learned list applied to its own training text
-// gives the training tokens.
+// counter selects from the candidate list or calls a sweep, and publishes;
+// the other workgroups load their first records meanwhile), then every
+// chunk containing the pair is rewritten in place (left to right, without
+// overlap) and its count changes are summed in LDS and added to the table.
+// The tokens of the whole corpus come from the encoder afterwards: a
+// learned list applied to its own training text gives the training tokens.
 #pragma once
 
 #include "encode.hpp"
@@ -33,9 +37,11 @@
 namespace bpek {
 
 constexpr uint32_t CK_MAXW = WC_MAXLEN;  // longest word kept in the table
+constexpr int CK_PF = 3;                 // records a thread of the merge pass has in flight
 
 // The listed words (one chunk per occurrence): text positions and lengths,
-// *n of them (entries past cap are counted but not stored).
+// n[0] of them (entries past cap are counted but not stored); n[1] of them
+// are longer than CK_MAXW, with n[2] bytes in all.
 struct CkList {
     uint32_t* pos;
     uint32_t* len;
@@ -43,18 +49,31 @@ struct CkList {
     uint32_t cap;
 };
 
-// The chunks: symbols of chunk c at sym[off[c] .. off[c] + len[c]) (16-bit
-// ids; a chunk only shrinks, in place), weight w[c] = its occurrences.
+// The chunks. Record chunks c < nr: symbols in rec[4c .. 4c + 4) (two per
+// 32-bit word, the first in the low half; zero past the length when
+// built), length rlen[c], weight rw[c]. Long chunks c < nl: symbols at
+// lsym[loff[c] .. loff[c] + llen[c]), weight 1. A chunk only shrinks, in
+// place.
 struct Chunks {
-    uint16_t* sym;
-    uint32_t* off;
-    uint32_t* len;
-    uint32_t* w;
-    uint32_t n;
+    uint4* rec;
+    uint32_t* rlen;
+    uint32_t* rw;
+    uint32_t nr;
+    uint16_t* lsym;
+    uint32_t* loff;
+    uint32_t* llen;
+    uint32_t nl;
 };
 
-// Appends the lanes' entries with take set, one counter atomic per wave.
-// Called by all active lanes of the wave.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
+    return v;
+}
+
+// Appends the lanes' entries with take set, one counter atomic per wave
+// (and two more when long words are among them). Called by all active
+// lanes of the wave.
 __device__ __forceinline__ void ck_list_append(const CkList& l, bool take, uint32_t pos, uint32_t len) {
     const unsigned long long m = __ballot(take);
     if (!m) return;
@@ -67,6 +86,15 @@ __device__ __forceinline__ void ck_list_append(const CkList& l, bool take, uint3
     if (take && base + below < l.cap) {
         l.pos[base + below] = pos;
         l.len[base + below] = len;
+    }
+    const bool lg = take && len > CK_MAXW;
+    const unsigned long long ml = __ballot(lg);
+    if (ml) {
+        const uint32_t bytes = wave_sum(lg ? len : 0u);
+        if ((int)(threadIdx.x & 63u) == lead) {
+            atomicAdd(l.n + 1, (uint32_t)__popcll(ml));
+            atomicAdd(l.n + 2, bytes);
+        }
     }
 }
 
@@ -208,73 +236,143 @@ __global__ __launch_bounds__(TPB) void k_ck_count(const uint8_t* __restrict__ te
     }
 }
 
-// sizes[0] += chunks of the table (slots with a count), sizes[1] += their
-// symbols; one atomic pair per wave.
-__global__ void k_ck_size(WordCache wc, const uint32_t* __restrict__ cnt, uint32_t slots, uint32_t* sizes) {
-    uint32_t c = 0u, s = 0u;
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gridDim.x * blockDim.x)
-        if (cnt[i]) {
-            ++c;
-            s += (uint32_t)(wc.key[i] & 63ull);
-        }
+// sizes[0] += the slots with a count (the table's chunks); one atomic per
+// workgroup.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_ck_size(const uint32_t* __restrict__ cnt, uint32_t slots, uint32_t* sizes) {
+    __shared__ uint32_t s_w[TPB / 64];
+    uint32_t c = 0u;
+    for (uint32_t i = blockIdx.x * TPB + threadIdx.x; i < slots; i += gridDim.x * TPB) c += cnt[i] ? 1u : 0u;
+    c = wave_sum(c);
+    if ((threadIdx.x & 63u) == 0u) s_w[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0u;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        c += (uint32_t)__shfl_xor((int)c, o);
-        s += (uint32_t)__shfl_xor((int)s, o);
-    }
-    if ((threadIdx.x & 63u) == 0u && (c | s)) {
-        atomicAdd(sizes + 0, c);
-        atomicAdd(sizes + 1, s);
+        for (int k = 0; k < TPB / 64; ++k) t += s_w[k];
+        if (t) atomicAdd(sizes, t);
     }
 }
 
-// The chunks, in any order (the counts and the merges do not depend on it):
-// table chunks take their index and symbol range from two counters ctr[0],
-// ctr[1] (zero before; one atomic pair per wave); the listed words follow
-// as chunks n_table.., their symbols at list_base + list_off[k] (list_off:
-// exclusive sums of the listed lengths).
-__global__ void k_ck_build(const uint8_t* __restrict__ text, WordCache wc, const uint32_t* __restrict__ cnt,
-                           uint32_t slots, CkList list, const uint32_t* __restrict__ list_off, uint32_t n_table,
-                           uint32_t list_base, Chunks ck, uint32_t* ctr) {
-    const uint32_t lane = threadIdx.x & 63u;
-    for (uint32_t i0 = blockIdx.x * blockDim.x; i0 < slots; i0 += gridDim.x * blockDim.x) {
-        const uint32_t i = i0 + threadIdx.x;
-        const uint32_t c = i < slots ? cnt[i] : 0u;
-        const uint32_t len = c ? (uint32_t)(wc.key[i] & 63ull) : 0u;
-        // wave-wide exclusive sums of the chunk flags and lengths
-        uint32_t ci = c ? 1u : 0u, li = len;
+// Four bytes (little-endian in x) as four 16-bit symbols in two words.
+__device__ __forceinline__ uint2 ck_widen(uint32_t x) {
+    return make_uint2((x & 0xFFu) | ((x & 0xFF00u) << 8), ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u));
+}
+
+// The chunks, in any order (the counts and the merges do not depend on
+// it). Each workgroup takes a contiguous range of the slots and one of the
+// nlist listed words, counts the chunks of each kind its range makes, and
+// takes their places with one atomic per counter: ctr[0] record chunks,
+// ctr[1] long chunks, ctr[2] long chunks' symbols (all zero before).
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_ck_build(const uint8_t* __restrict__ text, WordCache wc,
+                                                  const uint32_t* __restrict__ cnt, uint32_t slots, CkList list,
+                                                  uint32_t nlist, Chunks ck, uint32_t* ctr) {
+    __shared__ uint32_t s_w[TPB / 64];
+    __shared__ uint32_t s_base[3];
+    const uint32_t tid = threadIdx.x;
+    {  // the table's words: the record's bytes widened, weight = count
+        const uint32_t per = (slots + gridDim.x - 1u) / gridDim.x;
+        const uint32_t lo = min(slots, blockIdx.x * per), hi = min(slots, lo + per);
+        uint32_t mine = 0u;
+        for (uint32_t i = lo + tid; i < hi; i += TPB) mine += cnt[i] ? 1u : 0u;
+        uint32_t all;
+        const uint32_t off = block_exclusive_sum<TPB>(mine, s_w, &all);
+        if (tid == 0) s_base[0] = all ? atomicAdd(ctr, all) : 0u;
+        __syncthreads();
+        uint32_t c = s_base[0] + off;
+        for (uint32_t i = lo + tid; i < hi; i += TPB) {
+            const uint32_t k = cnt[i];
+            if (!k) continue;
+            const uint4* src = reinterpret_cast<const uint4*>(wc.rec + (size_t)i * 8u);
+            const uint4 a = src[0], b = src[1];
+            const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint4* dst = ck.rec + 4u * (size_t)c;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t a = (uint32_t)__shfl_up((int)ci, o), b = (uint32_t)__shfl_up((int)li, o);
-            if (lane >= (uint32_t)o) {
-                ci += a;
-                li += b;
+            for (int j = 0; j < 4; ++j) {
+                const uint2 lo2 = ck_widen(wds[2 * j]), hi2 = ck_widen(wds[2 * j + 1]);
+                dst[j] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+            }
+            ck.rlen[c] = (uint32_t)(wc.key[i] & 63ull);
+            ck.rw[c] = k;
+            ++c;
+        }
+        __syncthreads();  // s_base is reused below
+    }
+    {  // the listed words, weight 1: short ones as records, long ones as they are
+        const uint32_t per = (nlist + gridDim.x - 1u) / gridDim.x;
+        const uint32_t lo = min(nlist, blockIdx.x * per), hi = min(nlist, lo + per);
+        uint32_t ns = 0u, nl = 0u, nb = 0u;
+        for (uint32_t i = lo + tid; i < hi; i += TPB) {
+            const uint32_t len = list.len[i];
+            if (len > CK_MAXW) {
+                ++nl;
+                nb += len;
+            } else {
+                ++ns;
             }
         }
-        const uint32_t tc = (uint32_t)__shfl((int)ci, 63), tl = (uint32_t)__shfl((int)li, 63);
-        uint32_t bc = 0u, bl = 0u;
-        if (lane == 63u && tc) {
-            bc = atomicAdd(ctr + 0, tc);
-            bl = atomicAdd(ctr + 1, tl);
+        uint32_t as, al, ab;
+        uint32_t os = block_exclusive_sum<TPB>(ns, s_w, &as);
+        uint32_t ol = block_exclusive_sum<TPB>(nl, s_w, &al);
+        uint32_t ob = block_exclusive_sum<TPB>(nb, s_w, &ab);
+        if (tid == 0) {
+            s_base[0] = as ? atomicAdd(ctr + 0, as) : 0u;
+            s_base[1] = al ? atomicAdd(ctr + 1, al) : 0u;
+            s_base[2] = ab ? atomicAdd(ctr + 2, ab) : 0u;
         }
-        bc = (uint32_t)__shfl((int)bc, 63) + ci - (c ? 1u : 0u);
-        bl = (uint32_t)__shfl((int)bl, 63) + li - len;
-        if (c) {
-            const uint32_t* rp = wc.rec + (size_t)i * 8u;
-            for (uint32_t j = 0; j < len; ++j) ck.sym[bl + j] = (uint16_t)((rp[j >> 2] >> (8u * (j & 3u))) & 0xFFu);
-            ck.off[bc] = bl;
-            ck.len[bc] = len;
-            ck.w[bc] = c;
+        __syncthreads();
+        os += s_base[0];
+        ol += s_base[1];
+        ob += s_base[2];
+        for (uint32_t i = lo + tid; i < hi; i += TPB) {
+            const uint32_t at = list.pos[i], len = list.len[i];
+            if (len > CK_MAXW) {
+                for (uint32_t j = 0; j < len; ++j) ck.lsym[ob + j] = text[at + j];
+                ck.loff[ol] = ob;
+                ck.llen[ol] = len;
+                ++ol;
+                ob += len;
+            } else {
+                uint32_t wds[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t q = 2u * (uint32_t)j;
+                    wds[j] = (q < len ? (uint32_t)text[at + q] : 0u) |
+                             (q + 1u < len ? (uint32_t)text[at + q + 1u] << 16 : 0u);
+                }
+                uint4* dst = ck.rec + 4u * (size_t)os;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[j] = make_uint4(wds[4 * j], wds[4 * j + 1], wds[4 * j + 2], wds[4 * j + 3]);
+                ck.rlen[os] = len;
+                ck.rw[os] = 1u;
+                ++os;
+            }
         }
     }
-    const uint32_t nl = min(*list.n, list.cap);
-    for (uint32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < nl; k += gridDim.x * blockDim.x) {
-        const uint32_t c = n_table + k, at = list.pos[k], len = list.len[k], o = list_base + list_off[k];
-        for (uint32_t j = 0; j < len; ++j) ck.sym[o + j] = text[at + j];
-        ck.off[c] = o;
-        ck.len[c] = len;
-        ck.w[c] = 1u;
+}
+
+// A record's 32 symbols, in 16 words.
+struct CkRec {
+    uint32_t v[16];
+    __device__ __forceinline__ void load(const Chunks& ck, uint32_t c) {
+        const uint4* rp = ck.rec + 4u * (size_t)c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 q = rp[j];
+            v[4 * j] = q.x;
+            v[4 * j + 1] = q.y;
+            v[4 * j + 2] = q.z;
+            v[4 * j + 3] = q.w;
+        }
     }
+    // symbol i (i a constant after unrolling)
+    __device__ __forceinline__ uint32_t sym(int i) const { return (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; }
+};
+
+// Bits 1 .. len - 1: the pairs (i - 1, i) of a chunk of len symbols.
+__device__ __forceinline__ uint32_t ck_pair_mask(uint32_t len) {
+    return len >= 32u ? 0xFFFFFFFEu : (len >= 2u ? (1u << len) - 2u : 0u);
 }
 
 // Every adjacent pair of every chunk, weighted by the chunk's count, into
@@ -284,15 +382,27 @@ __global__ __launch_bounds__(TPB) void k_ck_pairs(Chunks ck, GTable gt, Ctl* ctl
     __shared__ LdsTable<LT> tab;
     tab.clear(TPB);
     lds_barrier();
-    for (uint32_t c = blockIdx.x * TPB + threadIdx.x; c < ck.n; c += gridDim.x * TPB) {
-        const uint32_t o = ck.off[c], len = ck.len[c], w = ck.w[c];
-        if (len < 2u) continue;
-        uint32_t prev = ck.sym[o];
+    const uint32_t stride = gridDim.x * TPB;
+    for (uint32_t c = blockIdx.x * TPB + threadIdx.x; c < ck.nr; c += stride) {
+        CkRec r;
+        r.load(ck, c);
+        const uint32_t pm = ck_pair_mask(ck.rlen[c]), w = ck.rw[c];
+#pragma unroll
+        for (int i = 1; i < 32; ++i)
+            if ((pm >> i) & 1u) {
+                const uint32_t key = (r.sym(i - 1) << 16) | r.sym(i);
+                if (!tab.insert(key, w)) gt_add(gt, key, w, ctl);
+            }
+    }
+    for (uint32_t c = blockIdx.x * TPB + threadIdx.x; c < ck.nl; c += stride) {
+        const uint16_t* s = ck.lsym + ck.loff[c];
+        const uint32_t len = ck.llen[c];
+        uint32_t prev = s[0];
         for (uint32_t j = 1; j < len; ++j) {
-            const uint32_t s = ck.sym[o + j];
-            const uint32_t key = (prev << 16) | s;
-            if (!tab.insert(key, w)) gt_add(gt, key, w, ctl);
-            prev = s;
+            const uint32_t x = s[j];
+            const uint32_t key = (prev << 16) | x;
+            if (!tab.insert(key, 1u)) gt_add(gt, key, 1u, ctl);
+            prev = x;
         }
     }
     lds_barrier();
@@ -306,20 +416,22 @@ __global__ __launch_bounds__(TPB) void k_ck_pairs(Chunks ck, GTable gt, Ctl* ctl
 // training has stopped does nothing). The selection is merge.hpp's: the
 // workgroup that draws ticket 0 of the iteration's counter selects and
 // publishes, every workgroup reads the publication (and joins a sweep when
-// it says so). Then each thread rewrites its chunks that contain the merged
-// pair: in place, left to right without overlap, each occurrence of (L, R)
-// becoming X. With the chunk's weight, every old pair with a side inside a
-// merged occurrence is taken out and every new pair with a side X is put
-// in; the other pairs map one to one onto each other (X is a new id), so
-// this is the chunk's exact recount. The keys taken out all hold L or R and
-// those put in all hold X, so a key only falls or only rises in a launch,
-// as the candidate list requires. The changes are summed in LDS and go to
-// the table once the workgroup is done.
+// it says so); a thread's first record is loaded before that wait. Then
+// each thread rewrites its chunks that contain the merged pair: in place,
+// left to right without overlap, each occurrence of (L, R) becoming X.
+// With the chunk's weight, every old pair with a side inside a merged
+// occurrence is taken out and every new pair with a side X is put in; the
+// other pairs map one to one onto each other (X is a new id), so this is
+// the chunk's exact recount. The keys taken out all hold L or R and those
+// put in all hold X, so a key only falls or only rises in a launch, as the
+// candidate list requires. The changes are summed in LDS and go to the
+// table once the workgroup is done.
 template <int TPB, int LT>
 __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks ck, GTable gt, Sweep* sw,
                                                   uint32_t* merges) {
     __shared__ LdsTable<LT> tab;
-    __shared__ uint32_t s_tile[2], s_u32;
+    __shared__ uint32_t s_rec[TPB * 17];  // a thread's record being rewritten (rows padded: no bank conflicts)
+    __shared__ uint32_t s_tile[2], s_u32, s_w[TPB / 64];
     __shared__ unsigned long long s_best[TPB / 64];
     if (ctl->done) return;
     const uint32_t p = it & 1u;
@@ -328,6 +440,8 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t* tick = &ctl->tile_ctr[p];
+    uint32_t* const my_rec = s_rec + 17u * tid;
+    const uint16_t* const my_sym = reinterpret_cast<const uint16_t*>(my_rec);
     if (blockIdx.x == 0 && tid == 0) {
         // the counters of the next iteration (the previous one's are done with)
         __hip_atomic_store(&ctl->tile_ctr[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -341,6 +455,23 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
     uint32_t theta = sw->theta;
     lds_barrier();
     if (s_tile[0] == 0u) select_and_publish<TPB>(gt, sw, p, it, theta, s_best, lane, w);  // uniform
+    const uint32_t stride = gridDim.x * TPB;
+    uint32_t c = blockIdx.x * TPB + tid;
+    // a pipeline of CK_PF records per thread, the first CK_PF in flight
+    // during the wait for the publication
+    CkRec r[CK_PF];
+    uint32_t rl[CK_PF], rw[CK_PF];
+#pragma unroll
+    for (int k = 0; k < CK_PF; ++k) {
+        const uint32_t ci = c + (uint32_t)k * stride;
+        rl[k] = 0u;
+        rw[k] = 0u;
+        if (ci < ck.nr) {
+            r[k].load(ck, ci);
+            rl[k] = ck.rlen[ci];
+            rw[k] = ck.rw[ci];
+        }
+    }
     unsigned long long best = read_publication(sw, ctl, p, it, s_best);
     if (best == SEL_SWEEP) best = sweep_select<TPB>(gt, sw, ctl, p, it, s_best, &s_u32, lane, w, theta);
     if (best == 0ull) {  // uniform: no countable pair is left
@@ -359,27 +490,88 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
         ctl->k = it + 1;
         ctl->m = it + 1;
     }
-    for (uint32_t c = blockIdx.x * TPB + tid; c < ck.n; c += gridDim.x * TPB) {
-        const uint32_t len = ck.len[c];
-        if (len < 2u) continue;
-        uint16_t* s = ck.sym + ck.off[c];
+    auto add = [&](uint32_t a, uint32_t b, uint32_t d) {
+        const uint32_t k = (a << 16) | b;
+        if (!tab.insert(k, d)) gt_add_sel(gt, k, d, ctl, sw, theta);
+    };
+    for (; c < ck.nr; c += stride) {
+        const CkRec cur = r[0];
+        const uint32_t len = rl[0], wt = rw[0];
+#pragma unroll
+        for (int k = 0; k + 1 < CK_PF; ++k) {
+            r[k] = r[k + 1];
+            rl[k] = rl[k + 1];
+            rw[k] = rw[k + 1];
+        }
+        {
+            const uint32_t ci = c + (uint32_t)CK_PF * stride;
+            if (ci < ck.nr) {
+                r[CK_PF - 1].load(ck, ci);
+                rl[CK_PF - 1] = ck.rlen[ci];
+                rw[CK_PF - 1] = ck.rw[ci];
+            }
+        }
+        const uint32_t pm = ck_pair_mask(len);
+        uint32_t occ = 0u;  // bit i: the pair (i - 1, i) is (L, R)
+#pragma unroll
+        for (int i = 1; i < 32; ++i) occ |= (cur.sym(i - 1) == L && cur.sym(i) == R) ? 1u << i : 0u;
+        occ &= pm;
+        if (occ) {
+            // bit i of sel: (i - 1, i) is merged (left to right without
+            // overlap: in a run of occurrences of (L, L), every other one)
+            uint32_t sel = occ;
+            if (L == R) {
+                sel = 0u;
+                uint32_t prev = 0u;
+#pragma unroll
+                for (int i = 1; i < 32; ++i) {
+                    const uint32_t b = (occ >> i) & 1u & (prev ^ 1u);
+                    sel |= b << i;
+                    prev = b;
+                }
+            }
+            const uint32_t site = sel | (sel >> 1);              // positions in a merged occurrence
+            const uint32_t changed = (site | (site << 1)) & pm;  // old pairs with a side in one
+            const uint32_t minus = (uint32_t)(-(int)wt);
+            // the old symbols, read at variable positions below
+#pragma unroll
+            for (int j = 0; j < 16; ++j) my_rec[j] = cur.v[j];
+            if (do_count)
+                for (uint32_t m = changed; m; m &= m - 1u) {
+                    const uint32_t i = (uint32_t)__ffs(m) - 1u;
+                    add(my_sym[i - 1u], my_sym[i], minus);
+                }
+            uint16_t* dst = reinterpret_cast<uint16_t*>(ck.rec + 4u * (size_t)c);
+            uint32_t o = 0u, pv = 0u;
+#pragma unroll 1
+            for (uint32_t i = 0; i < len; ++i) {
+                if ((sel >> i) & 1u) continue;  // the right half of a merged occurrence
+                const bool mx = i < 31u && ((sel >> (i + 1u)) & 1u);
+                const uint32_t cur = mx ? X : (uint32_t)my_sym[i];
+                dst[o] = (uint16_t)cur;
+                if (do_count && o && (pv == X || cur == X)) add(pv, cur, wt);
+                pv = cur;
+                ++o;
+            }
+            ck.rlen[c] = o;
+        }
+    }
+    for (uint32_t cl = blockIdx.x * TPB + tid; cl < ck.nl; cl += stride) {
+        const uint32_t n = ck.llen[cl];
+        uint16_t* s = ck.lsym + ck.loff[cl];
         // a quick look first: most chunks do not hold the pair
         bool has = false;
-        for (uint32_t j = 1; j < len && !has; ++j) has = s[j - 1] == L && s[j] == R;
+        for (uint32_t j = 1; j < n && !has; ++j) has = s[j - 1] == L && s[j] == R;
         if (!has) continue;
-        const uint32_t wt = ck.w[c], minus = (uint32_t)(-(int)wt);
-        auto add = [&](uint32_t a, uint32_t b, uint32_t d) {
-            const uint32_t k = (a << 16) | b;
-            if (!tab.insert(k, d)) gt_add_sel(gt, k, d, ctl, sw, theta);
-        };
+        const uint32_t minus = 0xFFFFFFFFu;  // weight 1
         // old pair (j-1, j) is looked at when j is reached; prev is the old
         // symbol at j-1 (the output may have overwritten it), in_site says
         // whether j-1 was inside a merged occurrence
         uint32_t o = 0, prev = 0u;
         bool in_site = false;
-        for (uint32_t j = 0; j < len;) {
+        for (uint32_t j = 0; j < n;) {
             const uint32_t a = s[j];
-            if (a == L && j + 1u < len && s[j + 1u] == R) {
+            if (a == L && j + 1u < n && s[j + 1u] == R) {
                 if (do_count) {
                     if (j) add(prev, L, minus);
                     add(L, R, minus);
@@ -396,12 +588,28 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
                 j += 1u;
             }
         }
-        ck.len[c] = o;
+        ck.llen[cl] = o;
         if (do_count)
             for (uint32_t j = 1; j < o; ++j)
-                if (s[j - 1] == X || s[j] == X) add(s[j - 1], s[j], wt);
+                if (s[j - 1] == X || s[j] == X) add(s[j - 1], s[j], 1u);
     }
-    finish_counts<TPB, LT>(tab, gt, ctl, sw, theta);
+    // the summed changes, one per thread at a time: the non-empty entries
+    // first gathered (in the record rows, free now), so that no thread adds
+    // several of them one after another while others idle
+    lds_barrier();
+    uint32_t mine = 0u;
+    for (uint32_t i = tid; i < (uint32_t)LT; i += TPB) mine += (tab.keys[i] != EMPTY && tab.cnts[i] != 0u) ? 1u : 0u;
+    uint32_t total;
+    uint32_t at = block_exclusive_sum<TPB>(mine, s_w, &total);
+    static_assert(2 * LT <= 17 * TPB, "the gathered entries fit the record rows");
+    for (uint32_t i = tid; i < (uint32_t)LT; i += TPB)
+        if (tab.keys[i] != EMPTY && tab.cnts[i] != 0u) {
+            s_rec[2u * at] = tab.keys[i];
+            s_rec[2u * at + 1u] = tab.cnts[i];
+            ++at;
+        }
+    lds_barrier();
+    for (uint32_t i = tid; i < total; i += TPB) gt_add_sel(gt, s_rec[2u * i], s_rec[2u * i + 1u], ctl, sw, theta);
 }
 
 }  // namespace bpek

@@ -100,6 +100,10 @@ typedef struct {
    bpe_run). Slower; for tests only. */
 #define BPE_FLAG_OVERSUBSCRIBE 1u
 
+/* For bpe_train_chunked (other calls ignore it): always train over the
+   distinct words, also where they would not save work (testing aid). */
+#define BPE_FLAG_ALWAYS_CHUNKS 2u
+
 typedef struct bpe_state bpe_state;
 
 /* Device workspace needed for a corpus of n bytes with this config (cfg may be

@@ -87,13 +87,40 @@ def test_train_argument_validation_before_any_device_call(bpe):
     cfg = bpe.Config(); cfg.table_log2 = 5
     assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
                          ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
-    cfg = bpe.Config(); cfg.flags = 2  # an unknown flag bit (1 is the oversubscription testing aid)
+    cfg = bpe.Config(); cfg.flags = 4  # an unknown flag bit (1 and 2 are testing aids)
     assert lib.bpe_train(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges),
                          ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
     # an empty corpus is valid and needs no device
     n_done.value = 9
     assert lib.bpe_train(None, 0, 4, None, ctypes.addressof(merges), ctypes.byref(n_done), None, 0,
                          ctypes.byref(n_tok)) == bpe.OK
+    assert n_done.value == 0 and n_tok.value == 0
+
+
+def test_chunked_training_argument_validation_before_any_device_call(bpe):
+    lib = bpe._lib
+    buf = (ctypes.c_uint8 * 16)()
+    merges = (ctypes.c_uint32 * 12)()
+    toks = (ctypes.c_uint32 * 16)()
+    n_done = ctypes.c_uint32(7)
+    n_tok = ctypes.c_size_t(7)
+    call = lib.bpe_train_chunked
+    assert call(ctypes.addressof(buf), 16, bpe.MAX_MERGES + 1, None, ctypes.addressof(merges),
+                ctypes.byref(n_done), None, 0, None) == bpe.EIDSPACE
+    assert call(None, 16, 4, None, ctypes.addressof(merges), ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
+    assert call(ctypes.addressof(buf), 16, 4, None, None, ctypes.byref(n_done), None, 0, None) == bpe.EINVAL
+    assert call(ctypes.addressof(buf), 16, 4, None, ctypes.addressof(merges), None, None, 0, None) == bpe.EINVAL
+    assert call(ctypes.addressof(buf), 16, 4, None, ctypes.addressof(merges), ctypes.byref(n_done),
+                ctypes.addressof(toks), 15, ctypes.byref(n_tok)) == bpe.EINVAL
+    cfg = bpe.Config(); cfg.flags = 4
+    assert call(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges), ctypes.byref(n_done),
+                None, 0, None) == bpe.EINVAL
+    cfg = bpe.Config(); cfg.workspace = ctypes.addressof(buf); cfg.workspace_bytes = 16
+    assert call(ctypes.addressof(buf), 16, 4, ctypes.byref(cfg), ctypes.addressof(merges), ctypes.byref(n_done),
+                None, 0, None) == bpe.EINVAL
+    assert b"workspace" in lib.bpe_last_error()
+    assert call(None, 0, 4, None, ctypes.addressof(merges), ctypes.byref(n_done), None, 0,
+                ctypes.byref(n_tok)) == bpe.OK
     assert n_done.value == 0 and n_tok.value == 0
 
 

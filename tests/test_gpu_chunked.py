@@ -4,10 +4,13 @@ through the C ABI) against the chunk-multiset C oracle.
 The merge list (pairs and counts) and the final tokens must be identical to
 the oracle's: on every workload recipe at ragged sizes, on the degenerate
 inputs (empty, no pair at all, one word), on words at and past the longest
-the word table keeps, on a corpus with more distinct words than the word
+a 64-byte record holds, on a corpus with more distinct words than the word
 table holds (so that most words are kept once per occurrence and the list
-of such words outgrows its first allocation), and with host buffers. The
-full-size workloads are compared in test_gpu_full.py."""
+of such words outgrows its first allocation), and with host buffers. These
+run over the chunks whatever their size (BPE_FLAG_ALWAYS_CHUNKS); one test
+also checks the default, which takes the full-array path where the chunks
+would not save work. The full-size workloads are compared in
+test_gpu_full.py."""
 import ctypes
 import sys
 
@@ -38,9 +41,9 @@ def _dev(data):
     return torch.from_numpy(np.ascontiguousarray(data, dtype=np.uint8)).to("cuda:0")
 
 
-def _check(bpe, data, n_merges, what, table_log2=None):
+def _check(bpe, data, n_merges, what, table_log2=None, always=True):
     _say("chunked: %s (%d bytes, %d merges)" % (what, data.size, n_merges))
-    gm, gt = bpe.train_chunked(_dev(data), n_merges, table_log2)
+    gm, gt = bpe.train_chunked(_dev(data), n_merges, table_log2, always_chunks=always)
     om, ot, _ = oracle.train_chunks(data, n_merges)
     gm = gm.cpu().numpy().astype(np.int64)
     gt = gt.cpu().numpy().astype(np.uint32)
@@ -64,13 +67,13 @@ def test_merge_counts_zero_and_one(bpe):
     d = corpus.generate(corpus.CONFIGS[3].scaled(100_000, seed=531))
     _check(bpe, d, 0, "no merges")
     _check(bpe, d, 1, "one merge")
-    m, t = bpe.train_chunked(_dev(d), 200, tokens=False)
+    m, t = bpe.train_chunked(_dev(d), 200, tokens=False, always_chunks=True)
     om, _, _ = oracle.train_chunks(d, 200, want_tokens=False)
     assert t is None and np.array_equal(m.cpu().numpy().astype(np.int64), om)
 
 
 def test_degenerate_inputs(bpe):
-    m, t = bpe.train_chunked(_dev(np.zeros(0, np.uint8)), 10)
+    m, t = bpe.train_chunked(_dev(np.zeros(0, np.uint8)), 10, always_chunks=True)
     assert m.shape[0] == 0 and t.shape[0] == 0
     # every word one byte long (letters and punctuation alternate): no pair
     one = np.frombuffer(b"a.b,c;d:" * 5000, dtype=np.uint8)
@@ -124,8 +127,17 @@ def test_host_buffers_through_the_c_abi(bpe):
     n_done = ctypes.c_uint32(0)
     n_tok = ctypes.c_size_t(0)
     cfg = bpe.Config()
+    cfg.flags = bpe.FLAG_ALWAYS_CHUNKS
     st = bpe._lib.bpe_train_chunked(d.ctypes.data, d.size, k, ctypes.byref(cfg), merges.ctypes.data,
                                     ctypes.byref(n_done), tokens.ctypes.data, tokens.size, ctypes.byref(n_tok))
     assert st == 0, bpe._lib.bpe_last_error()
     assert np.array_equal(merges[: n_done.value].astype(np.int64), om)
     assert np.array_equal(tokens[: n_tok.value], ot)
+
+
+def test_default_path_choice_gives_the_same_results(bpe):
+    # text of repeated words runs over the chunks; bytes with few repeated
+    # words (the runs recipe) over the full array: the same results either way
+    for cfg, n in ((3, 1_000_003), (5, 1_000_003), (2, 300_001)):
+        spec = corpus.CONFIGS[cfg].scaled(n, seed=540 + cfg)
+        _check(bpe, corpus.generate(spec), 1200, "default path, %s" % spec.kind, always=False)
