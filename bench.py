@@ -33,11 +33,17 @@ timed, not credited.
 learned list applied to new text, word by word, each distinct word encoded
 once), with the same accounting.
 
+"chunked" reports training over the corpus's distinct words
+(bpe_train_chunked: each distinct word once with its frequency, the same
+merges and tokens by another route), whole jobs timed by the wall clock and
+compared with the full-array result; the headline stays the full-array
+path, whose merge pass is the HBM-bound kernel of the roofline figures.
+
 "configs" reports the other four workloads (64 KiB, 16 MiB, 128 MiB and
 1 GiB corpora, each with its own merge count and table size): one timed
-job each, merges/s, the merge pass's GB/s and fraction of peak, and
-whether the result is bit-identical to the chunk-multiset CPU oracle on
-the same bytes (timed beside it, one core).
+job each, merges/s, the merge pass's GB/s and fraction of peak, whether
+the result is bit-identical to the chunk-multiset CPU oracle on the same
+bytes (timed beside it, one core), and the distinct-word training's job.
 """
 from __future__ import annotations
 
@@ -356,90 +362,39 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     return res
 
 
-def distinct_chunks(data, np):
-    """The distinct words of two bytes or more of a corpus (words: maximal
-    runs of one byte class), with their occurrence counts, by a 64-bit hash
-    of each word's bytes (up to 32 bytes; longer words are kept one per
-    occurrence). Returns (list of distinct words as bytes, counts array,
-    number of words of two bytes or more)."""
-    import oracle
-    cls = np.array([oracle.char_class(x) for x in range(256)], dtype=np.uint8)[data]
-    starts = np.flatnonzero(np.concatenate([[True], cls[1:] != cls[:-1]]))
-    lens = np.diff(np.append(starts, data.size))
-    multi = lens >= 2
-    st, ln = starts[multi], lens[multi]
-    short = ln <= 32
-    ss, sl = st[short], ln[short]
-    h = np.full(ss.size, np.uint64(1469598103934665603), dtype=np.uint64)
-    prime = np.uint64(1099511628211)
-    for k in range(32):
-        live = sl > k
-        b = np.where(live, data[np.minimum(ss + k, data.size - 1)], 0).astype(np.uint64)
-        h = np.where(live, (h ^ b) * prime, h)
-    h ^= sl.astype(np.uint64) << np.uint64(56)
-    _, first, counts = np.unique(h, return_index=True, return_counts=True)
-    words = [bytes(data[ss[i]: ss[i] + sl[i]]) for i in first]
-    longs = [bytes(data[a: a + b]) for a, b in zip(st[~short], ln[~short])]
-    return words + longs, np.concatenate([counts, np.ones(len(longs), dtype=counts.dtype)]), int(st.size)
-
-
-def chunk_study(args, bpe, corpus, spec, np, torch) -> dict:
-    """Design study: training over the distinct words of the corpus (each
-    once) instead of the whole symbol array. The GPU trains on the text of
-    the distinct words, each followed by a one-byte separator of another
-    class (the separators form no pairs), unweighted: the merge loop on an
-    array of that size is what a weighted version would run (one more
-    weight per symbol), so its per-merge time is measured here; the
-    weighted counts, and so the merges, would differ from this unweighted
-    run. The estimate adds a pass that finds the distinct words on the GPU
-    (the encoder's word-cache passes over the corpus, measured) and the
-    final tokens through the encoder (a learned list applied to its own
-    training text gives the training tokens; measured)."""
-    log("chunk study: generating %s" % spec.name)
-    data = corpus.generate(spec)
-    t0 = time.perf_counter()
-    words, counts, n_multi = distinct_chunks(data, np)
-    host_s = time.perf_counter() - t0
-    log("chunk study: %d words of 2+ bytes, %d distinct (host dedup %.1f s)" % (n_multi, len(words), host_s))
-    import oracle
-    seps = [ord(c) for c in "\n !0a"]
-    parts, prev = [], None
-    for w in words:
-        c = oracle.char_class(w[0])
-        if prev is not None:
-            parts.append(bytes([next(x for x in seps if oracle.char_class(x) not in (prev, c))]))
-        parts.append(w)
-        prev = c
-    text = np.frombuffer(b"".join(parts), dtype=np.uint8).copy()
-    d = torch.from_numpy(text).to("cuda:0")
-    k_req = spec.n_merges
-    runs = []
-    for i in range(1 + args.steps):
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        with bpe.State(d) as st:
-            st.run(k_req)
-            k = st.sync()
-            m = st.merges()
-        torch.cuda.synchronize()
-        if i:
-            runs.append(time.perf_counter() - t1)
-    train_s = float(np.median(runs))
-    log("chunk study: %d merges on %d bytes in %.3f s (%.1f us per merge)" % (k, text.size, train_s,
-                                                                              1e6 * train_s / max(k, 1)))
-    d_full = torch.from_numpy(data).to("cuda:0")
-    with bpe.Encoder(m) as enc:
-        _, ms = enc.profile(d_full, 5)
-    ms = np.median(ms.astype(np.float64), axis=0)
-    dedup_ms, encode_ms = float(ms[0]), float(ms.sum())
-    total_s = dedup_ms / 1e3 + train_s + encode_ms / 1e3
-    return {"study": "training over the distinct words (chunk multiset), %s" % spec.name,
-            "words_2plus": n_multi, "distinct_words": len(words), "chunk_text_bytes": int(text.size),
-            "merges": int(k), "train_s": round(train_s, 4), "us_per_merge": round(1e6 * train_s / max(k, 1), 2),
-            "dedup_ms_gpu_stand_in": round(dedup_ms, 4), "final_encode_ms": round(encode_ms, 4),
-            "estimate_merges_s": round(k / total_s, 1),
-            "note": "unweighted training on the distinct-word text; dedup and final encoding measured with the "
-                    "encoder's passes; host dedup (numpy) %.1f s is not part of the estimate" % host_s}
+def chunked_leg(bpe, spec, d, ref_m, ref_t, ref_oracle, steps, warmup, np, torch, time, log):
+    """Training over the corpus's distinct words (bpe_train_chunked): each
+    distinct word once with its frequency, the tokens through the encoder.
+    Whole jobs on the device-resident corpus, timed by the wall clock (word
+    passes, merges, tokens and the copy-out included); the result is
+    compared with the full-array path's (ref_m, ref_t), and so with the
+    oracle where that was (ref_oracle). Timed twice: as called (where the
+    distinct words would not save work the call runs the full-array path)
+    and with BPE_FLAG_ALWAYS_CHUNKS."""
+    out = {}
+    for always in (False, True):
+        def job():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m, t = bpe.train_chunked(d, spec.n_merges, spec.table_log2, always_chunks=always)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0, m, t
+        for _ in range(warmup):
+            job()
+        walls, m, t = [], None, None
+        for _ in range(steps):
+            dt, m, t = job()
+            walls.append(dt)
+        same = bool(torch.equal(m, ref_m) and torch.equal(t, ref_t))
+        k = int(m.shape[0])
+        rate = k * len(walls) / sum(walls)
+        key = "over_chunks" if always else "as_called"
+        out[key] = {"merges_per_s": round(rate, 1), "s_per_job": round(float(np.median(walls)), 4),
+                    "jobs": steps, "identical_to_full_array_path": same,
+                    "bit_identical_to_oracle": (same and ref_oracle) if ref_oracle is not None else None}
+        log("%s chunked (%s): %.1f merges/s, %.3f s per job, identical to the full-array path: %s"
+            % (spec.name, key, rate, float(np.median(walls)), same))
+    return out
 
 
 def main() -> int:
@@ -463,8 +418,8 @@ def main() -> int:
                     help="time whole jobs only (no HIP event per iteration; for runs under a profiler)")
     ap.add_argument("--run-chunk", type=int, default=0, metavar="K",
                     help="with --no-iteration-events: enqueue K iterations at a time, waiting in between")
-    ap.add_argument("--chunk-study", action="store_true",
-                    help="design study: time GPU training over the corpus's distinct words and print its JSON")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the legs that train over the distinct words (bpe_train_chunked)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
     args = ap.parse_args()
@@ -496,10 +451,6 @@ def main() -> int:
         spec = spec.scaled(spec.n_bytes, n_merges=args.merges)
     n_merges, tlog2 = spec.n_merges, spec.table_log2
     T = 1 << tlog2
-
-    if args.chunk_study:
-        print(json.dumps(chunk_study(args, bpe, corpus, spec, np, torch)), flush=True)
-        return 0
 
     if args.inference_only:
         log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
@@ -561,6 +512,10 @@ def main() -> int:
                                         "one thread, %.2f s; equal to the chunk oracle: %s"
                                         % (lit_s, bool(np.array_equal(lm, om) and np.array_equal(lt, ot)))}
 
+    chunked = None
+    if not args.no_chunked:
+        chunked = chunked_leg(bpe, spec, d, m, t, res.get("identical"), 3, 1, np, torch, time, log)
+
     if args.save_merges:
         np.save(args.save_merges, m.cpu().numpy())
     inference = None
@@ -583,6 +538,10 @@ def main() -> int:
             r = train_leg(bpe, corpus, cs, 1, 1 if small else 0, np, torch, time, log,
                           0 if args.no_cpu_baseline else 1)
             frac = r["merge_gbps"] / HBM_PEAK_GBPS
+            ck = None
+            if not args.no_chunked:
+                ck = chunked_leg(bpe, cs, r["d"], r["merges"], r["tokens"], r.get("identical"), 1,
+                                 1 if small else 0, np, torch, time, log)
             configs[cs.name] = {
                 "workload": "%d-byte seeded corpus (%s), %d merges, pair table 2^%d, sha256 %s"
                             % (cs.n_bytes, cs.kind, cs.n_merges, cs.table_log2, r["sha"][:16]),
@@ -593,6 +552,7 @@ def main() -> int:
                 "final_tokens": int(r["tokens"].shape[0]),
                 "cpu_oracle_merges_per_s": round(r["cpu_merges_s"], 1) if "cpu_merges_s" in r else None,
                 "bit_identical_to_oracle": r.get("identical"),
+                "chunked": ck,
                 "note": ("launch- and latency-bound: the roofline fraction is not meaningful"
                          if cs.n_bytes <= (1 << 20) else
                          "the 64 MiB symbol array and 16 MiB table fit the 256 MB last-level cache; GB/s is "
@@ -643,6 +603,7 @@ def main() -> int:
                      "traffic_source": ("profiles/traffic_%s_%s.json" % (dominant, spec.name)) if windows else None,
                      "bytes_per_launch": round(avg_bytes), "avg_launch_ms": round(avg_ms, 5)},
         "cpu_baseline": cpu,
+        "chunked": chunked,
         "configs": configs,
         "inference": inference,
         "encoding": encoding,
