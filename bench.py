@@ -420,6 +420,8 @@ def main() -> int:
                     help="with --no-iteration-events: enqueue K iterations at a time, waiting in between")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the legs that train over the distinct words (bpe_train_chunked)")
+    ap.add_argument("--chunked-only", action="store_true",
+                    help="only time training over the distinct words on the workload (for profiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device-to-device copy of BYTES bytes (hardware-counter reference)")
     args = ap.parse_args()
@@ -451,6 +453,29 @@ def main() -> int:
         spec = spec.scaled(spec.n_bytes, n_merges=args.merges)
     n_merges, tlog2 = spec.n_merges, spec.table_log2
     T = 1 << tlog2
+
+    if args.chunked_only:
+        log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))
+        data = corpus.generate(spec)
+        d = torch.from_numpy(data).to("cuda:0")
+        walls, k = [], 0
+        for i in range(args.warmup + args.steps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m, t = bpe.train_chunked(d, n_merges, tlog2)
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                walls.append(time.perf_counter() - t0)
+            k = int(m.shape[0])
+            log("%s chunked job %d: %.3f s, %d merges" % (spec.name, i + 1, time.perf_counter() - t0, k))
+        out = {"metric": "BPE train merges/sec over the distinct words", "value": round(k * len(walls) / sum(walls), 1),
+               "unit": "merges/s", "n_gpus": 1, "steps": len(walls), "warmup": args.warmup,
+               "ms_per_step": round(1e3 * sum(walls) / len(walls), 3), "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "u16", "data": "synthetic",
+               "config": {"workload": "%s: %d-byte seeded corpus (%s), %d merges, pair table 2^%d"
+                                      % (spec.name, spec.n_bytes, spec.kind, n_merges, tlog2)}}
+        print(json.dumps(out), flush=True)
+        return 0
 
     if args.inference_only:
         log("generating %s (%d bytes)" % (spec.name, spec.n_bytes))

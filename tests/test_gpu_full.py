@@ -86,11 +86,14 @@ def test_full_size_workload_matches_oracle(bpe, cfg):
         et = enc.encode(d).cpu().numpy().astype(np.uint32)
     assert_same("encoding of %s with its own merges" % spec.name, et, ot)
     del gt, et
-    # training over the distinct words, each weighted by its frequency, gives the same
-    cm, ct = bpe.train_chunked(d, spec.n_merges, spec.table_log2)
-    _say("  chunked: %d merges, %d tokens" % (cm.shape[0], ct.shape[0]))
-    assert_same("chunked merges of %s" % spec.name, cm.cpu().numpy().astype(np.int64), om)
-    assert_same("chunked tokens of %s" % spec.name, ct.cpu().numpy().astype(np.uint32), ot)
+    # training over the distinct words, each weighted by its frequency, gives
+    # the same (as called: runs128m takes the full-array path; and forced)
+    for always in (False, True):
+        cm, ct = bpe.train_chunked(d, spec.n_merges, spec.table_log2, always_chunks=always)
+        _say("  chunked (always %s): %d merges, %d tokens" % (always, cm.shape[0], ct.shape[0]))
+        assert_same("chunked merges of %s" % spec.name, cm.cpu().numpy().astype(np.int64), om)
+        assert_same("chunked tokens of %s" % spec.name, ct.cpu().numpy().astype(np.uint32), ot)
+        del cm, ct
 
 
 @pytest.mark.timeout(600)
@@ -122,6 +125,11 @@ def test_training_to_the_last_id(bpe, cfg, n_bytes):
     m2, t2 = bpe.train(d, bpe.MAX_MERGES, 22)
     assert_same("bpe_train merges", m2.cpu().numpy().astype(np.int64), om)
     assert_same("bpe_train tokens", t2.cpu().numpy().astype(np.uint32), ot)
+    # and so does training over the distinct words (its last merge, X = 0xFFFF, updates no counts)
+    for always in (True, False):
+        m3, t3 = bpe.train_chunked(d, bpe.MAX_MERGES, 22, always_chunks=always)
+        assert_same("bpe_train_chunked merges (always %s)" % always, m3.cpu().numpy().astype(np.int64), om)
+        assert_same("bpe_train_chunked tokens (always %s)" % always, t3.cpu().numpy().astype(np.uint32), ot)
     # the full list drives the encoder and the trie
     text = corpus.generate(corpus.CONFIGS[cfg].scaled(300_000, seed=78))
     dt = _dev(text)
