@@ -1839,7 +1839,7 @@ bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, cons
     ck.nr = h[0] + (h[2] - h[3]);
     ck.nl = h[3];
     if ((st = mem.get(&ck.rec, 4 * size_t(ck.nr))) != BPE_OK || (st = mem.get(&ck.rlen, ck.nr)) != BPE_OK ||
-        (st = mem.get(&ck.rw, ck.nr)) != BPE_OK || (st = mem.get(&ck.lsym, h[4])) != BPE_OK ||
+        (st = mem.get(&ck.rw, ck.nr)) != BPE_OK || (st = mem.get(&ck.rbloom, ck.nr)) != BPE_OK || (st = mem.get(&ck.lsym, h[4])) != BPE_OK ||
         (st = mem.get(&ck.loff, ck.nl)) != BPE_OK || (st = mem.get(&ck.llen, ck.nl)) != BPE_OK)
         return st;
     hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small + 8),

@@ -37,7 +37,8 @@
 namespace bpek {
 
 constexpr uint32_t CK_MAXW = WC_MAXLEN;  // longest word kept in the table
-constexpr int CK_PF = 3;                 // records a thread of the merge pass has in flight
+constexpr int CK_PF = 3;                 // records a thread of the merge pass loads during the selection
+constexpr int CK_NB = 16;                // symbol filters a thread of the merge pass reads at once
 
 // The listed words (one chunk per occurrence): text positions and lengths,
 // n[0] of them (entries past cap are counted but not stored); n[1] of them
@@ -51,19 +52,33 @@ struct CkList {
 
 // The chunks. Record chunks c < nr: symbols in rec[4c .. 4c + 4) (two per
 // 32-bit word, the first in the low half; zero past the length when
-// built), length rlen[c], weight rw[c]. Long chunks c < nl: symbols at
-// lsym[loff[c] .. loff[c] + llen[c]), weight 1. A chunk only shrinks, in
-// place.
+// built), length rlen[c], weight rw[c], and a filter of the symbols it
+// holds, rbloom[c] (bit ck_bit(s) set for each symbol s). Long chunks
+// c < nl: symbols at lsym[loff[c] .. loff[c] + llen[c]), weight 1. A chunk
+// only shrinks, in place.
 struct Chunks {
     uint4* rec;
     uint32_t* rlen;
     uint32_t* rw;
+    unsigned long long* rbloom;
     uint32_t nr;
     uint16_t* lsym;
     uint32_t* loff;
     uint32_t* llen;
     uint32_t nl;
 };
+
+// A symbol's bit in a chunk's filter (Fibonacci hashing to 6 bits).
+__device__ __forceinline__ unsigned long long ck_bit(uint32_t s) { return 1ull << ((s * 0x9E3779B1u) >> 26); }
+
+// The filter of the first len symbols of a record's 16 words.
+__device__ __forceinline__ unsigned long long ck_filter(const uint32_t (&wds)[16], uint32_t len) {
+    unsigned long long f = 0ull;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        if ((uint32_t)i < len) f |= ck_bit((wds[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
+    return f;
+}
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 #pragma unroll
@@ -286,15 +301,21 @@ __global__ __launch_bounds__(TPB) void k_ck_build(const uint8_t* __restrict__ te
             if (!k) continue;
             const uint4* src = reinterpret_cast<const uint4*>(wc.rec + (size_t)i * 8u);
             const uint4 a = src[0], b = src[1];
-            const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint32_t bytes[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t wds[16];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint2 x = ck_widen(bytes[j]);
+                wds[2 * j] = x.x;
+                wds[2 * j + 1] = x.y;
+            }
             uint4* dst = ck.rec + 4u * (size_t)c;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint2 lo2 = ck_widen(wds[2 * j]), hi2 = ck_widen(wds[2 * j + 1]);
-                dst[j] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
-            }
-            ck.rlen[c] = (uint32_t)(wc.key[i] & 63ull);
+            for (int j = 0; j < 4; ++j) dst[j] = make_uint4(wds[4 * j], wds[4 * j + 1], wds[4 * j + 2], wds[4 * j + 3]);
+            const uint32_t len = (uint32_t)(wc.key[i] & 63ull);
+            ck.rlen[c] = len;
             ck.rw[c] = k;
+            ck.rbloom[c] = ck_filter(wds, len);
             ++c;
         }
         __syncthreads();  // s_base is reused below
@@ -346,6 +367,7 @@ __global__ __launch_bounds__(TPB) void k_ck_build(const uint8_t* __restrict__ te
                 for (int j = 0; j < 4; ++j) dst[j] = make_uint4(wds[4 * j], wds[4 * j + 1], wds[4 * j + 2], wds[4 * j + 3]);
                 ck.rlen[os] = len;
                 ck.rw[os] = 1u;
+                ck.rbloom[os] = ck_filter(wds, len);
                 ++os;
             }
         }
@@ -412,6 +434,25 @@ __global__ __launch_bounds__(TPB) void k_ck_pairs(Chunks ck, GTable gt, Ctl* ctl
     }
 }
 
+// Bit k: chunk c0 + k stride (below ck->nr) may hold both symbols of need
+// (two filter bits; both set is necessary, not sufficient). With ck, the
+// CK_NB filters are read into bl first (all loads in flight together);
+// without it, bl already holds them.
+__device__ __forceinline__ uint32_t ck_hits(unsigned long long (&bl)[CK_NB], unsigned long long need,
+                                            const Chunks* ck, uint32_t c0, uint32_t stride) {
+    if (ck) {
+#pragma unroll
+        for (int k = 0; k < CK_NB; ++k) {
+            const uint32_t ci = c0 + (uint32_t)k * stride;
+            bl[k] = ci < ck->nr ? ck->rbloom[ci] : 0ull;
+        }
+    }
+    uint32_t hits = 0u;
+#pragma unroll
+    for (int k = 0; k < CK_NB; ++k) hits |= (bl[k] & need) == need ? 1u << k : 0u;
+    return hits;
+}
+
 // One training iteration over the chunks (launch it; a launch after
 // training has stopped does nothing). The selection is merge.hpp's: the
 // workgroup that draws ticket 0 of the iteration's counter selects and
@@ -457,8 +498,16 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
     if (s_tile[0] == 0u) select_and_publish<TPB>(gt, sw, p, it, theta, s_best, lane, w);  // uniform
     const uint32_t stride = gridDim.x * TPB;
     uint32_t c = blockIdx.x * TPB + tid;
-    // a pipeline of CK_PF records per thread, the first CK_PF in flight
-    // during the wait for the publication
+    // A thread's record chunks are c, c + stride, ..., taken in batches of
+    // CK_NB whose filters are read together; a record is read only when its
+    // filter holds both L and R. The first batch's filters and its first
+    // CK_PF records are in flight during the wait for the publication.
+    unsigned long long bl[CK_NB];
+#pragma unroll
+    for (int k = 0; k < CK_NB; ++k) {
+        const uint32_t ci = c + (uint32_t)k * stride;
+        bl[k] = ci < ck.nr ? ck.rbloom[ci] : 0ull;
+    }
     CkRec r[CK_PF];
     uint32_t rl[CK_PF], rw[CK_PF];
 #pragma unroll
@@ -494,22 +543,26 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
         const uint32_t k = (a << 16) | b;
         if (!tab.insert(k, d)) gt_add_sel(gt, k, d, ctl, sw, theta);
     };
-    for (; c < ck.nr; c += stride) {
-        const CkRec cur = r[0];
-        const uint32_t len = rl[0], wt = rw[0];
+    const unsigned long long need = ck_bit(L) | ck_bit(R);
+    for (uint32_t b0 = 0u; c + b0 * stride < ck.nr; b0 += (uint32_t)CK_NB)
+    for (uint32_t hits = ck_hits(bl, need, b0 ? &ck : nullptr, c + b0 * stride, stride); hits; hits &= hits - 1u) {
+        const uint32_t k = (uint32_t)__ffs(hits) - 1u;
+        const uint32_t cc = c + (b0 + k) * stride;
+        CkRec cur;
+        uint32_t len = 0u, wt = 0u;
+        bool got = false;
 #pragma unroll
-        for (int k = 0; k + 1 < CK_PF; ++k) {
-            r[k] = r[k + 1];
-            rl[k] = rl[k + 1];
-            rw[k] = rw[k + 1];
-        }
-        {
-            const uint32_t ci = c + (uint32_t)CK_PF * stride;
-            if (ci < ck.nr) {
-                r[CK_PF - 1].load(ck, ci);
-                rl[CK_PF - 1] = ck.rlen[ci];
-                rw[CK_PF - 1] = ck.rw[ci];
+        for (int j = 0; j < CK_PF; ++j)
+            if (b0 == 0u && k == (uint32_t)j) {
+                cur = r[j];
+                len = rl[j];
+                wt = rw[j];
+                got = true;
             }
+        if (!got) {
+            cur.load(ck, cc);
+            len = ck.rlen[cc];
+            wt = ck.rw[cc];
         }
         const uint32_t pm = ck_pair_mask(len);
         uint32_t occ = 0u;  // bit i: the pair (i - 1, i) is (L, R)
@@ -541,19 +594,22 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
                     const uint32_t i = (uint32_t)__ffs(m) - 1u;
                     add(my_sym[i - 1u], my_sym[i], minus);
                 }
-            uint16_t* dst = reinterpret_cast<uint16_t*>(ck.rec + 4u * (size_t)c);
+            uint16_t* dst = reinterpret_cast<uint16_t*>(ck.rec + 4u * (size_t)cc);
             uint32_t o = 0u, pv = 0u;
+            unsigned long long f = 0ull;
 #pragma unroll 1
             for (uint32_t i = 0; i < len; ++i) {
                 if ((sel >> i) & 1u) continue;  // the right half of a merged occurrence
                 const bool mx = i < 31u && ((sel >> (i + 1u)) & 1u);
                 const uint32_t cur = mx ? X : (uint32_t)my_sym[i];
                 dst[o] = (uint16_t)cur;
+                f |= ck_bit(cur);
                 if (do_count && o && (pv == X || cur == X)) add(pv, cur, wt);
                 pv = cur;
                 ++o;
             }
-            ck.rlen[c] = o;
+            ck.rlen[cc] = o;
+            ck.rbloom[cc] = f;
         }
     }
     for (uint32_t cl = blockIdx.x * TPB + tid; cl < ck.nl; cl += stride) {
