@@ -141,3 +141,33 @@ def test_default_path_choice_gives_the_same_results(bpe):
     for cfg, n in ((3, 1_000_003), (5, 1_000_003), (2, 300_001)):
         spec = corpus.CONFIGS[cfg].scaled(n, seed=540 + cfg)
         _check(bpe, corpus.generate(spec), 1200, "default path, %s" % spec.kind, always=False)
+
+
+def test_a_full_pair_table_is_reported(bpe):
+    # a 2^10-slot pair table cannot hold this corpus's pairs: BPE_ETABLE,
+    # never a result with a count missing; a large table trains bit-exactly
+    d = corpus.generate(corpus.CONFIGS[5].scaled(200_000, seed=545))
+    with pytest.raises(bpe.BpeError) as e:
+        bpe.train_chunked(_dev(d), 30, 10, always_chunks=True)
+    assert e.value.status == bpe.ETABLE
+    _check(bpe, d, 30, "the same corpus with a large table", table_log2=22)
+
+
+def test_default_stream_work_is_ordered_before_and_after(bpe):
+    # the corpus is produced by torch kernels on the default stream, queued
+    # behind other work, with no synchronisation before the call
+    import torch
+    data = corpus.generate(corpus.CONFIGS[3].scaled(1 << 20, seed=546))
+    om, ot, _ = oracle.train_chunks(data, 500)
+    src = torch.from_numpy(data.copy()).pin_memory()
+    torch.cuda.synchronize()
+    a = torch.randn(2048, 2048, device="cuda:0")
+    for _ in range(20):
+        a = a @ a
+        a = a / a.abs().amax()
+    d = torch.empty(data.size, dtype=torch.uint8, device="cuda:0")
+    d.copy_(src, non_blocking=True)
+    d = d ^ (a[0, 0] * 0).to(torch.uint8)  # a kernel that waits for the busy work
+    m, t = bpe.train_chunked(d, 500, always_chunks=True)
+    assert np.array_equal(m.cpu().numpy().astype(np.int64), om)
+    assert np.array_equal(t.cpu().numpy().astype(np.uint32), ot)
