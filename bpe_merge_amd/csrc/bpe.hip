@@ -1737,6 +1737,8 @@ constexpr int CK_TPB = 256;
 constexpr int CK_LT = 2048;  // LDS sums per workgroup (slots, or pairs)
 constexpr int CK_MERGE_TPB = 256;
 constexpr uint32_t CK_TILE = CK_TPB * 16;  // k_ck_count's tile
+constexpr int CK_SMALL_TPB = 1024;          // k_ck_small: at most this many record chunks, no long ones
+constexpr int CK_SMALL_LT = 8192;           // its LDS pair table
 
 // Word-table slots for n bytes: one per 128 bytes, a power of two in
 // [2^16, 2^24] (a word that finds no slot within the probe limit is kept
@@ -1860,22 +1862,36 @@ bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, cons
         (st = mem.get(&lengths, 2)) != BPE_OK)
         return st;
     const bpek::GTable gt{table, uint32_t(tslots - 1), table_limit(tlog2)};
-    hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(sw),
-                       sizeof(bpek::Sweep) / 8, 0ull);
-    hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
-    hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, table, tslots, bpek::GT_EMPTY);
-    // one workgroup per CU: more only add to the selection's wait and the
-    // publication's polls (each thread has CK_PF records in flight anyway)
-    const uint32_t nmax = std::max(ck.nr, ck.nl);
-    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>((nmax + CK_MERGE_TPB - 1) / CK_MERGE_TPB, cus));
-    hipLaunchKernelGGL((bpek::k_ck_pairs<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, ck, gt, ctl);
-    for (uint32_t it = 0; it < n_merges; ++it)
-        hipLaunchKernelGGL((bpek::k_ck_merge<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, it, ctl,
-                           ck, gt, sw, dmerges);
-    if ((st = launch_ok()) != BPE_OK) return st;
     Ctl hc;
-    HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
+    bool small_done = false;
+    if (ck.nr <= uint32_t(CK_SMALL_TPB) && ck.nl == 0 && n_merges > 0) {
+        // every iteration in one workgroup and one launch; its LDS table
+        // may fill, and then the workgroups below train instead
+        hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
+        hipLaunchKernelGGL((bpek::k_ck_small<CK_SMALL_TPB, CK_SMALL_LT>), dim3(1), dim3(CK_SMALL_TPB), 0, s, ck,
+                           n_merges, dmerges, ctl);
+        if ((st = launch_ok()) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        small_done = !(hc.err & bpek::ERR_LDS_FULL);
+    }
+    if (!small_done) {
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(sw),
+                           sizeof(bpek::Sweep) / 8, 0ull);
+        hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, table, tslots, bpek::GT_EMPTY);
+        // one workgroup per CU: more only add to the selection's wait and the
+        // publication's polls (each thread has CK_PF records in flight anyway)
+        const uint32_t nmax = std::max(ck.nr, ck.nl);
+        const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>((nmax + CK_MERGE_TPB - 1) / CK_MERGE_TPB, cus));
+        hipLaunchKernelGGL((bpek::k_ck_pairs<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, ck, gt, ctl);
+        for (uint32_t it = 0; it < n_merges; ++it)
+            hipLaunchKernelGGL((bpek::k_ck_merge<CK_MERGE_TPB, CK_LT>), dim3(grid), dim3(CK_MERGE_TPB), 0, s, it, ctl,
+                               ck, gt, sw, dmerges);
+        if ((st = launch_ok()) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+    }
     if (hc.err) {
         if (hc.err & bpek::ERR_TABLE) {
             set_err("the global pair table is full (%u of %zu slots claimed; give a larger table_log2)",

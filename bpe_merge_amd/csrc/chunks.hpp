@@ -392,6 +392,17 @@ struct CkRec {
     __device__ __forceinline__ uint32_t sym(int i) const { return (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; }
 };
 
+// Symbol i of a record row in LDS, and its replacement. The row is only
+// ever accessed as 32-bit words, so that no access through another type
+// can be reordered around the row's stores.
+__device__ __forceinline__ uint32_t row_sym(const uint32_t* row, uint32_t i) {
+    return (row[i >> 1] >> ((i & 1u) * 16u)) & 0xFFFFu;
+}
+__device__ __forceinline__ void row_set(uint32_t* row, uint32_t i, uint32_t v) {
+    const uint32_t sh = (i & 1u) * 16u;
+    row[i >> 1] = (row[i >> 1] & ~(0xFFFFu << sh)) | (v << sh);
+}
+
 // Bits 1 .. len - 1: the pairs (i - 1, i) of a chunk of len symbols.
 __device__ __forceinline__ uint32_t ck_pair_mask(uint32_t len) {
     return len >= 32u ? 0xFFFFFFFEu : (len >= 2u ? (1u << len) - 2u : 0u);
@@ -482,7 +493,6 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t* tick = &ctl->tile_ctr[p];
     uint32_t* const my_rec = s_rec + 17u * tid;
-    const uint16_t* const my_sym = reinterpret_cast<const uint16_t*>(my_rec);
     if (blockIdx.x == 0 && tid == 0) {
         // the counters of the next iteration (the previous one's are done with)
         __hip_atomic_store(&ctl->tile_ctr[p ^ 1u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -592,7 +602,7 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
             if (do_count)
                 for (uint32_t m = changed; m; m &= m - 1u) {
                     const uint32_t i = (uint32_t)__ffs(m) - 1u;
-                    add(my_sym[i - 1u], my_sym[i], minus);
+                    add(row_sym(my_rec, i - 1u), row_sym(my_rec, i), minus);
                 }
             uint16_t* dst = reinterpret_cast<uint16_t*>(ck.rec + 4u * (size_t)cc);
             uint32_t o = 0u, pv = 0u;
@@ -601,7 +611,7 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
             for (uint32_t i = 0; i < len; ++i) {
                 if ((sel >> i) & 1u) continue;  // the right half of a merged occurrence
                 const bool mx = i < 31u && ((sel >> (i + 1u)) & 1u);
-                const uint32_t cur = mx ? X : (uint32_t)my_sym[i];
+                const uint32_t cur = mx ? X : row_sym(my_rec, i);
                 dst[o] = (uint16_t)cur;
                 f |= ck_bit(cur);
                 if (do_count && o && (pv == X || cur == X)) add(pv, cur, wt);
@@ -666,6 +676,136 @@ __global__ __launch_bounds__(TPB) void k_ck_merge(uint32_t it, Ctl* ctl, Chunks 
         }
     lds_barrier();
     for (uint32_t i = tid; i < total; i += TPB) gt_add_sel(gt, s_rec[2u * i], s_rec[2u * i + 1u], ctl, sw, theta);
+}
+
+// ---------------------------------------------------------------- one workgroup, every iteration
+// Training over at most TPB record chunks (no long ones) in one workgroup
+// and one launch: each thread holds one chunk's record in registers for the
+// whole run, the weighted pair counts live in an LDS hash table of LT
+// slots (linear probing; a claimed slot keeps its key), and an iteration is
+// a maximum over that table, the rewrite of the chunks that hold the pair
+// with their count changes (the same exact recount as k_ck_merge), and a
+// barrier. The maximum is the same packed value as the multi-workgroup
+// path's (count << 32 | ~key over the nonzero counts), so the merges are
+// the same. If the LDS table fills, ERR_LDS_FULL is set and nothing of the
+// run is used: the caller trains with the multi-workgroup path instead.
+constexpr uint32_t ERR_LDS_FULL = 4u;
+
+template <int TPB, int LT>
+__global__ __launch_bounds__(TPB) void k_ck_small(Chunks ck, uint32_t n_merges, uint32_t* merges, Ctl* ctl) {
+    static_assert((LT & (LT - 1)) == 0 && LT % TPB == 0, "LT: a power of two, a multiple of TPB");
+    __shared__ uint32_t t_key[LT], t_cnt[LT];
+    __shared__ uint32_t s_rec[TPB * 17];  // a thread's record being rewritten (rows padded: no bank conflicts)
+    __shared__ unsigned long long s_best[TPB / 64];
+    __shared__ uint32_t s_full;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+    for (uint32_t i = tid; i < (uint32_t)LT; i += TPB) {
+        t_key[i] = EMPTY;
+        t_cnt[i] = 0u;
+    }
+    if (tid == 0) s_full = 0u;
+    const bool mine = tid < ck.nr;
+    CkRec r;
+    uint32_t len = 0u, wt = 0u;
+    if (mine) {
+        r.load(ck, tid);
+        len = ck.rlen[tid];
+        wt = ck.rw[tid];
+    }
+    uint32_t* const my_rec = s_rec + 17u * tid;
+    auto add = [&](uint32_t a, uint32_t b, uint32_t d) {
+        const uint32_t key = (a << 16) | b;
+        uint32_t h = mix32(key) & (uint32_t)(LT - 1);
+        for (uint32_t p = 0; p < (uint32_t)LT; ++p, h = (h + 1u) & (uint32_t)(LT - 1)) {
+            uint32_t cur = __hip_atomic_load(&t_key[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (cur == EMPTY) {
+                cur = atomicCAS(&t_key[h], EMPTY, key);
+                if (cur == EMPTY) cur = key;
+            }
+            if (cur == key) {
+                atomicAdd(&t_cnt[h], d);
+                return;
+            }
+        }
+        s_full = 1u;
+    };
+    __syncthreads();
+    if (mine) {
+        const uint32_t pm = ck_pair_mask(len);
+#pragma unroll
+        for (int i = 1; i < 32; ++i)
+            if ((pm >> i) & 1u) add(r.sym(i - 1), r.sym(i), wt);
+    }
+    __syncthreads();
+    uint32_t it = 0;
+    for (; it < n_merges && !s_full; ++it) {  // s_full: read after a barrier, uniform
+        unsigned long long best = 0ull;
+        for (uint32_t i = tid; i < (uint32_t)LT; i += TPB) {
+            const uint32_t c = t_cnt[i];
+            const unsigned long long v = c ? ((unsigned long long)c << 32) | (uint32_t)~t_key[i] : 0ull;
+            best = v > best ? v : best;
+        }
+        best = block_max_u64<TPB / 64>(best, s_best, lane, w);
+        if (best == 0ull) break;  // uniform: no pair is left
+        const uint32_t key = ~(uint32_t)best;
+        const uint32_t L = key >> 16, R = key & IDM, X = BASE + it;
+        const bool do_count = X != IDM;
+        if (tid == 0) {
+            merges[3 * it + 0] = L;
+            merges[3 * it + 1] = R;
+            merges[3 * it + 2] = (uint32_t)(best >> 32);
+        }
+        const uint32_t pm = ck_pair_mask(len);
+        uint32_t occ = 0u;
+#pragma unroll
+        for (int i = 1; i < 32; ++i) occ |= (r.sym(i - 1) == L && r.sym(i) == R) ? 1u << i : 0u;
+        occ &= pm;
+        if (occ) {
+            uint32_t sel = occ;
+            if (L == R) {
+                sel = 0u;
+                uint32_t prev = 0u;
+#pragma unroll
+                for (int i = 1; i < 32; ++i) {
+                    const uint32_t b = (occ >> i) & 1u & (prev ^ 1u);
+                    sel |= b << i;
+                    prev = b;
+                }
+            }
+            const uint32_t site = sel | (sel >> 1);
+            const uint32_t changed = (site | (site << 1)) & pm;
+            const uint32_t minus = (uint32_t)(-(int)wt);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) my_rec[j] = r.v[j];
+            if (do_count)
+                for (uint32_t m = changed; m; m &= m - 1u) {
+                    const uint32_t i = (uint32_t)__ffs(m) - 1u;
+                    add(row_sym(my_rec, i - 1u), row_sym(my_rec, i), minus);
+                }
+            // in place in the row: position o <= i is written after i is read
+            uint32_t o = 0u, pv = 0u;
+#pragma unroll 1
+            for (uint32_t i = 0; i < len; ++i) {
+                if ((sel >> i) & 1u) continue;
+                const bool mx = i < 31u && ((sel >> (i + 1u)) & 1u);
+                const uint32_t cur = mx ? X : row_sym(my_rec, i);
+                row_set(my_rec, o, cur);
+                if (do_count && o && (pv == X || cur == X)) add(pv, cur, wt);
+                pv = cur;
+                ++o;
+            }
+            len = o;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) r.v[j] = my_rec[j];
+        }
+        __syncthreads();  // every count change is in before the next maximum
+    }
+    if (tid == 0) {
+        ctl->k = it;
+        ctl->m = it;
+        ctl->done = 1u;
+        if (s_full) ctl->err |= ERR_LDS_FULL;
+    }
 }
 
 }  // namespace bpek
