@@ -28,6 +28,7 @@
 #include "trie.hpp"
 #include "encode.hpp"
 #include "chunks.hpp"
+#include "chunks_solo.hpp"
 
 using bpek::Ctl;
 
@@ -1739,6 +1740,9 @@ constexpr int CK_MERGE_TPB = 256;
 constexpr uint32_t CK_TILE = CK_TPB * 16;  // k_ck_count's tile
 constexpr int CK_SMALL_TPB = 1024;          // k_ck_small: at most this many record chunks, no long ones
 constexpr int CK_SMALL_LT = 8192;           // its LDS pair table
+constexpr int CK_SOLO_TPB = 1024;           // k_ck_solo: one workgroup, every iteration
+constexpr int CK_SOLO_CT = 2048;            // its candidate table
+constexpr int CK_SOLO_KT = 2048;            // its per-iteration change table
 
 // Word-table slots for n bytes: one per 128 bytes, a power of two in
 // [2^16, 2^24] (a word that finds no slot within the probe limit is kept
@@ -1874,6 +1878,47 @@ bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, cons
         HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
         small_done = !(hc.err & bpek::ERR_LDS_FULL);
+    }
+    if (!small_done && ck.nl == 0 && n_merges > 0) {
+        // one workgroup, every iteration, with occurrence lists: the
+        // weighted counts into the pair table, each pair's list of chunks
+        const bpek::OccLists ol0{};
+        bpek::OccLists ol = ol0;
+        bpek::PairIds pid{};
+        uint2* scratch = nullptr;
+        ol.cap = uint32_t(std::min<size_t>(64 * size_t(ck.nr) + 4096, 0xFFFFFFF0u));
+        const uint32_t scratch_cap = uint32_t(std::min<size_t>(2 * size_t(ck.nr) + 65536, 0xFFFFFFF0u));
+        if ((st = mem.get(&ol.off, tslots)) != BPE_OK || (st = mem.get(&ol.len, tslots)) != BPE_OK ||
+            (st = mem.get(&ol.pool, ol.cap)) != BPE_OK || (st = mem.get(&pid.slot, tslots)) != BPE_OK ||
+            (st = mem.get(&pid.key, tslots)) != BPE_OK || (st = mem.get(&pid.cnt, tslots)) != BPE_OK ||
+            (st = mem.get(&pid.id_of, tslots)) != BPE_OK || (st = mem.get(&scratch, scratch_cap)) != BPE_OK)
+            return st;
+        hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s, ctl, uint32_t(n), lengths);
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, table, tslots, bpek::GT_EMPTY);
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(cus * 4), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(ol.len),
+                           tslots / 2, 0ull);
+        hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned long long*>(small + 12),
+                           size_t(1), 0ull);
+        const uint32_t pgrid = std::max<uint32_t>(1, std::min<uint32_t>((ck.nr + 255) / 256, cus * 4));
+        hipLaunchKernelGGL((bpek::k_ck_pairs<CK_MERGE_TPB, CK_LT>), dim3(pgrid), dim3(CK_MERGE_TPB), 0, s, ck, gt, ctl);
+        hipLaunchKernelGGL((bpek::k_occ_scan<256, false>), dim3(pgrid), dim3(256), 0, s, ck, gt, ol);
+        hipLaunchKernelGGL(bpek::k_occ_place<256>, dim3(std::min<uint32_t>(uint32_t((tslots + 255) / 256), cus * 8)),
+                           dim3(256), 0, s, gt, ol, pid, small + 12);
+        hipLaunchKernelGGL((bpek::k_occ_scan<256, true>), dim3(pgrid), dim3(256), 0, s, ck, gt, ol);
+        hipLaunchKernelGGL((bpek::k_ck_solo<CK_SOLO_TPB, CK_SOLO_CT, CK_SOLO_KT>), dim3(1), dim3(CK_SOLO_TPB), 0, s,
+                           ck, gt, ol, small + 12, pid, small + 13, scratch, scratch_cap, n_merges, dmerges, ctl);
+        if ((st = launch_ok()) != BPE_OK) return st;
+        HIP_TRY(hipMemcpyAsync(&hc, ctl, sizeof hc, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        small_done = !(hc.err & bpek::ERR_SOLO);
+        if (!small_done) {
+            // the records were rewritten: built again for the passes below
+            hipLaunchKernelGGL(bpek::k_fill64, dim3(1), dim3(64), 0, s,
+                               reinterpret_cast<unsigned long long*>(small + 8), size_t(2), 0ull);
+            hipLaunchKernelGGL(bpek::k_ck_build<256>, dim3(sgrid), dim3(256), 0, s, text, wc, wcnt, slots, list,
+                               n_list, ck, small + 8);
+            if ((st = launch_ok()) != BPE_OK) return st;
+        }
     }
     if (!small_done) {
         hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(sw),
