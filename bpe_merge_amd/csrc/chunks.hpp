@@ -21,12 +21,17 @@
 //     16-bit symbols, zero past its length, which one thread reads with
 //     four 16-byte loads; a longer one (weight 1) lies in an array of its
 //     own.
-// k_ck_pairs counts the chunks' pairs into the global pair table, and
-// k_ck_merge runs one iteration: the selection of merge.hpp (ticket 0 of a
-// counter selects from the candidate list or calls a sweep, and publishes;
-// the other workgroups load their first records meanwhile), then every
-// chunk containing the pair is rewritten in place (left to right, without
-// overlap) and its count changes are summed in LDS and added to the table.
+// The iterations take one of three routes: k_ck_small (at most 1,024
+// record chunks, no long ones: every iteration in one workgroup, the pair
+// counts in LDS); k_ck_solo (chunks_solo.hpp: no long chunks; every
+// iteration in one workgroup, touching only the chunks on the merged
+// pair's occurrence list); or k_ck_pairs, which counts the chunks' pairs
+// into the global pair table, and k_ck_merge per iteration: the selection
+// of merge.hpp (ticket 0 of a counter selects from the candidate list or
+// calls a sweep, and publishes; the other workgroups load their first
+// records meanwhile), then every chunk containing the pair is rewritten in
+// place (left to right, without overlap) and its count changes are summed
+// in LDS and added to the table.
 // The tokens of the whole corpus come from the encoder afterwards: a
 // learned list applied to its own training text gives the training tokens.
 #pragma once

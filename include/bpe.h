@@ -167,11 +167,19 @@ bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, u
  * training tokens. Arguments and results as bpe_train: merges (host or
  * device), n_done (host), tokens (host or device, or NULL), tokens_cap,
  * n_tokens (host, or NULL); cfg->table_log2 sizes the pair table as for
- * bpe_train, cfg->stream orders the work (NULL: a stream of its own),
- * cfg->flags are ignored and cfg->workspace must be NULL: the call allocates
- * its own device memory (the word table, about 2 bytes of chunk symbols per
- * distinct-word byte, the pair table) and frees it before returning. Blocks
- * until done. Errors as bpe_train, and as bpe_encoder_encode for the tokens.
+ * bpe_train (a corpus of at most 1,024 distinct words, none longer than 32
+ * bytes, is trained in one workgroup's LDS, without it), cfg->stream
+ * orders the work (NULL: a stream of its own), cfg->flags may hold
+ * BPE_FLAG_ALWAYS_CHUNKS (other bits as for bpe_train), and cfg->workspace
+ * must be NULL: the call allocates its own device memory (the word table,
+ * 76 bytes per distinct word of at most 32 bytes, 2 bytes per symbol of a
+ * longer word, the pair table with about 20 bytes per slot for the pairs'
+ * chunk lists, and up to 256 bytes per distinct word for the lists
+ * themselves) and frees it before returning. Where the distinct words'
+ * records would take more than a quarter of the full array's first-
+ * iteration bytes (incompressible bytes), it runs bpe_train instead.
+ * Blocks until done. Errors as bpe_train, and as bpe_encoder_encode for the
+ * tokens.
  */
 bpe_status bpe_train_chunked(const uint8_t *bytes, size_t n, uint32_t n_merges, const bpe_config *cfg,
                              bpe_merge *merges, uint32_t *n_done, uint32_t *tokens, size_t tokens_cap,
