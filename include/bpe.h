@@ -173,7 +173,7 @@ bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, u
  * BPE_FLAG_ALWAYS_CHUNKS (other bits as for bpe_train), and cfg->workspace
  * must be NULL: the call allocates its own device memory (the word table,
  * 76 bytes per distinct word of at most 32 bytes, 2 bytes per symbol of a
- * longer word, the pair table with about 20 bytes per slot for the pairs'
+ * longer word, the pair table with 24 more bytes per slot for the pairs'
  * chunk lists, and up to 256 bytes per distinct word for the lists
  * themselves) and frees it before returning. Where the distinct words'
  * records would take more than a quarter of the full array's first-
