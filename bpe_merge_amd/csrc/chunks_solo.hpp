@@ -196,6 +196,7 @@ __global__ __launch_bounds__(TPB) void k_ck_solo(Chunks ck, GTable gt, OccLists 
     __shared__ uint32_t k_key[KT], k_d[KT], k_n[KT], k_base[KT];
     __shared__ uint32_t s_rec[TPB * 17];
     __shared__ unsigned long long s_best[TPB / 64];
+    __shared__ uint32_t s_bidx[TPB / 64], s_nge[TPB / 64];
     // scalars: 0 theta, 1 shift, 2 candidates held, 3 candidates complete,
     // 4 pool used, 5 claimed slots, 6 scratch entries, 7 error bits,
     // 8 the merged pair's slot, 9 pair-table claims, 10 collected,
@@ -222,8 +223,11 @@ __global__ __launch_bounds__(TPB) void k_ck_solo(Chunks ck, GTable gt, OccLists 
     uint32_t* const my_rec = s_rec + 17u * tid;
     __syncthreads();
 
-    // a slot into the candidate table (count updated if it is there); false if full
+    // a slot into the candidate table (count updated if it is there); false
+    // if the table is more than half full (not probed then) or no free slot
+    // is found
     auto cand_put = [&](uint32_t slot, uint32_t key, uint32_t cnt, uint32_t off, uint32_t len) -> bool {
+        if (s_v[2] > (uint32_t)CT / 2u) return false;
         uint32_t h = mix32(slot) & (uint32_t)(CT - 1);
         for (uint32_t p = 0; p < (uint32_t)CT / 4u; ++p, h = (h + 1u) & (uint32_t)(CT - 1)) {
             uint32_t cur = __hip_atomic_load(&c_slot[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -294,28 +298,54 @@ __global__ __launch_bounds__(TPB) void k_ck_solo(Chunks ck, GTable gt, OccLists 
             }
         }
         if (best == 0ull) {
-            // a sweep over the pairs' counts by id: the top count, then the
-            // candidates (eight loads in flight per thread); the merge is the
-            // maximum over the candidates, which hold every pair of the top count
-            const uint32_t nc = s_v[5];
-            uint32_t top = 0u;
+            // a sweep over the pairs' counts by id (eight loads in flight
+            // per thread): the top count and how many pairs hold at least
+            // the current theta; then the maximum (the top count's pair of
+            // the smallest key) and where it is, from a second pass that
+            // refills the candidates (theta = top - (top >> shift)), or, when
+            // theta already equals the top count and more pairs hold it than
+            // the table may, from one over the pairs of the top count only
+            // (every merge then sweeps until that changes)
+            const uint32_t nc = s_v[5], theta0 = s_v[0];
+            uint32_t top = 0u, nge = 0u;
             for (uint32_t i0 = tid; i0 < nc; i0 += 8u * TPB) {
                 uint32_t c[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) c[u] = i0 + (uint32_t)u * TPB < nc ? pid.cnt[i0 + (uint32_t)u * TPB] : 0u;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) top = max(top, c[u]);
-            }
-            top = (uint32_t)(block_max64<TPB / 64>(top, s_best, lane, w));
-            if (top == 0u) break;  // uniform: no pair is left
-            for (uint32_t shift = s_v[1];; ++shift) {
-                const uint32_t theta = shift >= 31u ? top : top - (top >> shift);
-                for (uint32_t i = tid; i < (uint32_t)CT; i += TPB) c_slot[i] = EMPTY;
-                if (tid == 0) {
-                    s_v[2] = 0u;
-                    s_v[10] = 0u;
+                for (int u = 0; u < 8; ++u) {
+                    top = max(top, c[u]);
+                    nge += c[u] && c[u] >= theta0 ? 1u : 0u;
                 }
-                lds_barrier();
+            }
+            top = (uint32_t)wave_max64(top);
+            nge = wave_sum(nge);
+            if (lane == 0) {
+                s_best[w] = top;
+                s_nge[w] = nge;
+            }
+            lds_barrier();
+            top = 0u;
+            nge = 0u;
+#pragma unroll
+            for (int i = 0; i < TPB / 64; ++i) {
+                top = max(top, (uint32_t)s_best[i]);
+                nge += s_nge[i];
+            }
+            lds_barrier();
+            if (top == 0u) break;  // uniform: no pair is left
+            const bool flat = theta0 == top && nge > (uint32_t)CT / 2u;
+            for (uint32_t shift = s_v[1];; ++shift) {
+                const uint32_t theta = flat || shift >= 31u ? top : top - (top >> shift);
+                if (!flat) {
+                    for (uint32_t i = tid; i < (uint32_t)CT; i += TPB) c_slot[i] = EMPTY;
+                    if (tid == 0) {
+                        s_v[2] = 0u;
+                        s_v[10] = 0u;
+                    }
+                    lds_barrier();
+                }
+                uint32_t bid = 0u;
                 best = 0ull;
                 for (uint32_t i0 = tid; i0 < nc; i0 += 8u * TPB) {
                     uint32_t c[8];
@@ -325,48 +355,52 @@ __global__ __launch_bounds__(TPB) void k_ck_solo(Chunks ck, GTable gt, OccLists 
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
                         if (c[u] >= theta && c[u]) {
-                            const uint32_t id = i0 + (uint32_t)u * TPB;
-                            const uint32_t sl = pid.slot[id], kk = pid.key[id];
-                            if (!cand_put(sl, kk, c[u], ol.off[sl], ol.len[sl])) atomicOr(&s_v[10], 1u);
-                            best = max(best, ((unsigned long long)c[u] << 32) | (uint32_t)~kk);
+                            const uint32_t id = i0 + (uint32_t)u * TPB, kk = pid.key[id];
+                            if (!flat) {
+                                const uint32_t sl = pid.slot[id];
+                                if (!cand_put(sl, kk, c[u], ol.off[sl], ol.len[sl])) atomicOr(&s_v[10], 1u);
+                            }
+                            const unsigned long long v = ((unsigned long long)c[u] << 32) | (uint32_t)~kk;
+                            if (v > best) {
+                                best = v;
+                                bid = id;
+                            }
                         }
                 }
-                best = block_max64<TPB / 64>(best, s_best, lane, w);
+                const unsigned long long wb = wave_max64(best);
+                const unsigned long long m = __ballot(best == wb);
+                if (lane == (uint32_t)(__ffsll((long long)m) - 1)) {
+                    s_best[w] = wb;
+                    s_bidx[w] = bid;
+                }
+                lds_barrier();
+                best = 0ull;
+#pragma unroll
+                for (int i = 0; i < TPB / 64; ++i)
+                    if (s_best[i] > best) {
+                        best = s_best[i];
+                        bid = s_bidx[i];
+                    }
                 // at most half full, so that the pairs this run adds find room
-                const bool ok = !s_v[10] && s_v[2] <= (uint32_t)CT / 2u;
+                const bool ok = !flat && !s_v[10] && s_v[2] <= (uint32_t)CT / 2u;
                 const uint32_t held = s_v[2];
                 lds_barrier();  // every thread has read the counts before they change
-                if (ok || theta == top) {  // uniform
+                if (flat || ok || theta == top) {  // uniform
                     if (tid == 0) {
-                        s_v[0] = theta;
-                        s_v[3] = ok ? 1u : 0u;
-                        // steer the next window towards a quarter of the table
-                        s_v[1] = held > (uint32_t)CT / 4u ? min(shift + 1u, SHIFT_MAX)
-                                                          : (shift > 1u ? shift - 1u : 1u);
-                    }
-                    break;
-                }
-            }
-            // the merged pair's place: a candidate now (top count, theta <= top), unless
-            // the table overflowed; then from its id
-            if (tid == 0) s_v[13] = 0u;
-            lds_barrier();
-            for (uint32_t i = tid; i < (uint32_t)CT; i += TPB)
-                if (c_slot[i] != EMPTY && c_cnt[i] == (uint32_t)(best >> 32) && c_key[i] == ~(uint32_t)best) {
-                    s_v[8] = c_slot[i];
-                    s_v[11] = c_off[i];
-                    s_v[12] = c_len[i];
-                    s_v[13] = 1u;
-                }
-            lds_barrier();
-            if (!s_v[13]) {  // uniform
-                for (uint32_t i0 = tid; i0 < nc; i0 += TPB)
-                    if (pid.cnt[i0] == (uint32_t)(best >> 32) && pid.key[i0] == ~(uint32_t)best) {
-                        const uint32_t sl = pid.slot[i0];
+                        const uint32_t sl = pid.slot[bid];
                         s_v[8] = sl;
                         s_v[11] = ol.off[sl];
                         s_v[12] = ol.len[sl];
+                        s_v[3] = ok ? 1u : 0u;
+                        if (!flat) {
+                            s_v[0] = theta;
+                            // steer the next window towards a quarter of the table
+                            s_v[1] = held > (uint32_t)CT / 4u ? min(shift + 1u, SHIFT_MAX)
+                                                              : (shift > 1u ? shift - 1u : 1u);
+                        }
                     }
+                    break;
+                }
             }
         }
         lds_barrier();
