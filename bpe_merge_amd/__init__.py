@@ -29,7 +29,7 @@ BASE_VOCAB = 256
 MAX_MERGES = 65280
 MAX_BYTES = 0x7FFFFFFF
 FLAG_OVERSUBSCRIBE = 1  # testing aid: merge passes with 4x the resident workgroups
-FLAG_ALWAYS_CHUNKS = 2  # train_chunked: over the distinct words even where that saves no work
+FLAG_ALWAYS_CHUNKS = 2  # train_chunked: over the distinct words whatever memory their records take
 
 
 class BpeError(RuntimeError):
@@ -172,8 +172,8 @@ def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bo
                   always_chunks: bool = False):
     """bpe_train_chunked on a uint8 CUDA tensor: training over the corpus's
     distinct words, each weighted by its frequency (or over the full symbol
-    array where the distinct words would not save work, unless
-    always_chunks). Returns (merges, tokens) as train() does (tokens is
+    array where their records would take more than 16 bytes per input
+    byte, unless always_chunks). Returns (merges, tokens) as train() does (tokens is
     None when tokens=False)."""
     torch = _torch()
     if not (isinstance(data, torch.Tensor) and data.is_cuda and data.dtype == torch.uint8):

@@ -1707,10 +1707,10 @@ bpe_status bpe_encode(const uint8_t* bytes, size_t n, const bpe_merge* merges, u
 // bpe_train_chunked: bpe_train's results from the corpus's distinct words,
 // each once with its frequency (chunks.hpp). One call: the word passes, a
 // host wait for the chunk sizes, the chunks, the weighted pair counts, one
-// launch per iteration, and the tokens from the encoder. Where the chunks
-// would take more memory traffic per iteration than a quarter of the full
-// symbol array's first iteration (incompressible text: few repeated
-// words), bpe_train runs instead, unless BPE_FLAG_ALWAYS_CHUNKS is set.
+// launch per iteration, and the tokens from the encoder. Where the chunks'
+// records would take more than 16 bytes per input byte (bytes with almost
+// no repeated word), bpe_train runs instead, unless BPE_FLAG_ALWAYS_CHUNKS
+// is set.
 
 namespace {
 
@@ -1828,10 +1828,12 @@ bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, cons
         if ((st = launch_ok()) != BPE_OK) return st;
         HIP_TRY(hipMemcpyAsync(h, small, sizeof h, hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
-        // records of 64 bytes, long chunks' 16-bit symbols; against 8 bytes
-        // per symbol of the full array's first iteration
+        // records of 64 bytes, long chunks' 16-bit symbols: a memory bound
+        // (the iterations read 8 bytes of filter per record and the records
+        // that hold the merged pair, against 8 bytes per symbol of the full
+        // array, so the chunks are faster wherever they fit)
         const size_t n_rec = size_t(h[0]) + (h[2] - h[3]);
-        if (!always && 64 * n_rec + 2 * size_t(h[4]) > 2 * n) {
+        if (!always && 64 * n_rec + 2 * size_t(h[4]) > 16 * n) {
             *full = true;
             return BPE_OK;
         }

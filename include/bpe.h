@@ -101,7 +101,7 @@ typedef struct {
 #define BPE_FLAG_OVERSUBSCRIBE 1u
 
 /* For bpe_train_chunked (other calls ignore it): always train over the
-   distinct words, also where they would not save work (testing aid). */
+   distinct words, whatever memory their records take (testing aid). */
 #define BPE_FLAG_ALWAYS_CHUNKS 2u
 
 typedef struct bpe_state bpe_state;
@@ -176,8 +176,8 @@ bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, u
  * longer word, the pair table with 24 more bytes per slot for the pairs'
  * chunk lists, and up to 256 bytes per distinct word for the lists
  * themselves) and frees it before returning. Where the distinct words'
- * records would take more than a quarter of the full array's first-
- * iteration bytes (incompressible bytes), it runs bpe_train instead.
+ * records would take more than 16 bytes per input byte (bytes with almost
+ * no repeated word), it runs bpe_train instead.
  * Blocks until done. Errors as bpe_train, and as bpe_encoder_encode for the
  * tokens.
  */

@@ -7,10 +7,9 @@ inputs (empty, no pair at all, one word), on words at and past the longest
 a 64-byte record holds, on a corpus with more distinct words than the word
 table holds (so that most words are kept once per occurrence and the list
 of such words outgrows its first allocation), and with host buffers. These
-run over the chunks whatever their size (BPE_FLAG_ALWAYS_CHUNKS); one test
-also checks the default, which takes the full-array path where the chunks
-would not save work. The full-size workloads are compared in
-test_gpu_full.py."""
+run over the chunks whatever memory their records take
+(BPE_FLAG_ALWAYS_CHUNKS); one test also checks the default. The full-size
+workloads are compared in test_gpu_full.py."""
 import ctypes
 import sys
 
@@ -38,7 +37,7 @@ def bpe():
 
 def _dev(data):
     import torch
-    return torch.from_numpy(np.ascontiguousarray(data, dtype=np.uint8)).to("cuda:0")
+    return torch.from_numpy(np.array(data, dtype=np.uint8)).to("cuda:0")  # a writable copy
 
 
 def _check(bpe, data, n_merges, what, table_log2=None, always=True):
@@ -136,8 +135,7 @@ def test_host_buffers_through_the_c_abi(bpe):
 
 
 def test_default_path_choice_gives_the_same_results(bpe):
-    # text of repeated words runs over the chunks; bytes with few repeated
-    # words (the runs recipe) over the full array: the same results either way
+    # as called (the full array only past a memory bound that these stay under)
     for cfg, n in ((3, 1_000_003), (5, 1_000_003), (2, 300_001)):
         spec = corpus.CONFIGS[cfg].scaled(n, seed=540 + cfg)
         _check(bpe, corpus.generate(spec), 1200, "default path, %s" % spec.kind, always=False)

@@ -87,7 +87,7 @@ def test_full_size_workload_matches_oracle(bpe, cfg):
     assert_same("encoding of %s with its own merges" % spec.name, et, ot)
     del gt, et
     # training over the distinct words, each weighted by its frequency, gives
-    # the same (as called: runs128m takes the full-array path; and forced)
+    # the same (as called, and forced past the memory bound it checks)
     for always in (False, True):
         cm, ct = bpe.train_chunked(d, spec.n_merges, spec.table_log2, always_chunks=always)
         _say("  chunked (always %s): %d merges, %d tokens" % (always, cm.shape[0], ct.shape[0]))
