@@ -73,6 +73,37 @@ struct Chunks {
     uint32_t nl;
 };
 
+// Maximum of a 64-bit value over the wave (every lane gets it): DPP row
+// shifts, then the row broadcasts, on the two halves; no LDS round trip.
+__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
+    auto step = [&](uint32_t lo, uint32_t hi) {
+        const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+        v = o > v ? o : v;
+    };
+    step(dpp<DPP_ROW_SHR1>(0u, (uint32_t)v), dpp<DPP_ROW_SHR1>(0u, (uint32_t)(v >> 32)));
+    step(dpp<DPP_ROW_SHR2>(0u, (uint32_t)v), dpp<DPP_ROW_SHR2>(0u, (uint32_t)(v >> 32)));
+    step(dpp<DPP_ROW_SHR4>(0u, (uint32_t)v), dpp<DPP_ROW_SHR4>(0u, (uint32_t)(v >> 32)));
+    step(dpp<DPP_ROW_SHR8>(0u, (uint32_t)v), dpp<DPP_ROW_SHR8>(0u, (uint32_t)(v >> 32)));
+    step(dpp<DPP_ROW_BCAST15, 0xA>(0u, (uint32_t)v), dpp<DPP_ROW_BCAST15, 0xA>(0u, (uint32_t)(v >> 32)));
+    step(dpp<DPP_ROW_BCAST31, 0xC>(0u, (uint32_t)v), dpp<DPP_ROW_BCAST31, 0xC>(0u, (uint32_t)(v >> 32)));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// ... and over the workgroup (NW waves; s_best holds NW values; two barriers).
+template <int NW>
+__device__ __forceinline__ unsigned long long block_max64(unsigned long long v, unsigned long long* s_best,
+                                                          uint32_t lane, uint32_t w) {
+    v = wave_max64(v);
+    if (lane == 0) s_best[w] = v;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) v = s_best[i] > v ? s_best[i] : v;
+    lds_barrier();
+    return v;
+}
+
 // A symbol's bit in a chunk's filter (Fibonacci hashing to 6 bits).
 __device__ __forceinline__ unsigned long long ck_bit(uint32_t s) { return 1ull << ((s * 0x9E3779B1u) >> 26); }
 
@@ -750,7 +781,7 @@ __global__ __launch_bounds__(TPB) void k_ck_small(Chunks ck, uint32_t n_merges, 
             const unsigned long long v = c ? ((unsigned long long)c << 32) | (uint32_t)~t_key[i] : 0ull;
             best = v > best ? v : best;
         }
-        best = block_max_u64<TPB / 64>(best, s_best, lane, w);
+        best = block_max64<TPB / 64>(best, s_best, lane, w);
         if (best == 0ull) break;  // uniform: no pair is left
         const uint32_t key = ~(uint32_t)best;
         const uint32_t L = key >> 16, R = key & IDM, X = BASE + it;

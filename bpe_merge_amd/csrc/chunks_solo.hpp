@@ -40,37 +40,6 @@ struct PairIds {
 
 constexpr uint32_t ERR_SOLO = 8u;  // an LDS table, the pool or the scratch filled: the run is not used
 
-// Maximum of a 64-bit value over the wave (every lane gets it): DPP row
-// shifts, then the row broadcasts, on the two halves; no LDS round trip.
-__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
-    auto step = [&](uint32_t lo, uint32_t hi) {
-        const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-        v = o > v ? o : v;
-    };
-    step(dpp<DPP_ROW_SHR1>(0u, (uint32_t)v), dpp<DPP_ROW_SHR1>(0u, (uint32_t)(v >> 32)));
-    step(dpp<DPP_ROW_SHR2>(0u, (uint32_t)v), dpp<DPP_ROW_SHR2>(0u, (uint32_t)(v >> 32)));
-    step(dpp<DPP_ROW_SHR4>(0u, (uint32_t)v), dpp<DPP_ROW_SHR4>(0u, (uint32_t)(v >> 32)));
-    step(dpp<DPP_ROW_SHR8>(0u, (uint32_t)v), dpp<DPP_ROW_SHR8>(0u, (uint32_t)(v >> 32)));
-    step(dpp<DPP_ROW_BCAST15, 0xA>(0u, (uint32_t)v), dpp<DPP_ROW_BCAST15, 0xA>(0u, (uint32_t)(v >> 32)));
-    step(dpp<DPP_ROW_BCAST31, 0xC>(0u, (uint32_t)v), dpp<DPP_ROW_BCAST31, 0xC>(0u, (uint32_t)(v >> 32)));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-// ... and over the workgroup (NW waves; s_best holds NW values; two barriers).
-template <int NW>
-__device__ __forceinline__ unsigned long long block_max64(unsigned long long v, unsigned long long* s_best,
-                                                          uint32_t lane, uint32_t w) {
-    v = wave_max64(v);
-    if (lane == 0) s_best[w] = v;
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NW; ++i) v = s_best[i] > v ? s_best[i] : v;
-    lds_barrier();
-    return v;
-}
-
 // The slot of a key that is in the table (NO_SLOT if it is not).
 __device__ __forceinline__ uint32_t gt_find(const GTable& gt, uint32_t key) {
     uint32_t h = mix32(key) & gt.mask;
