@@ -169,3 +169,21 @@ def test_default_stream_work_is_ordered_before_and_after(bpe):
     m, t = bpe.train_chunked(d, 500, always_chunks=True)
     assert np.array_equal(m.cpu().numpy().astype(np.int64), om)
     assert np.array_equal(t.cpu().numpy().astype(np.uint32), ot)
+
+
+def test_a_merge_with_more_count_changes_than_the_one_workgroup_route_holds(bpe):
+    # 3,000 words "uv" (3,001 times each) and "uvab" (once each): the first
+    # 3,000 merges make each "uv" one symbol, then merging (a, b) changes the
+    # counts of about 6,000 pairs (each "uv" symbol next to a, and next to
+    # the new one), past the one-workgroup route's change table: it gives up
+    # and the multi-workgroup passes train from the start, with the same result
+    import oracle as orc
+    letters = [c for c in range(256) if orc.char_class(c) == 0 and c not in (ord("a"), ord("b"))]
+    pairs = [(u, v) for u in letters for v in letters][:3000]
+    parts = []
+    for u, v in pairs:
+        parts.append(bytes([u, v, 32]) * 3001)
+        parts.append(bytes([u, v, ord("a"), ord("b"), 32]))
+    d = np.frombuffer(b"".join(parts), dtype=np.uint8)
+    om = _check(bpe, d, 3002, "a wide merge")
+    assert om[3000].tolist() == [ord("a"), ord("b"), 3000]
