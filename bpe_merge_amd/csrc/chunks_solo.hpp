@@ -249,19 +249,37 @@ __global__ __launch_bounds__(TPB) void k_ck_solo(Chunks ck, GTable gt, OccLists 
         // ---- 1. the merge
         unsigned long long best = 0ull;
         if (s_v[3]) {
+            unsigned long long b = 0ull;
+            uint32_t bi = 0u;
             for (uint32_t i = tid; i < (uint32_t)CT; i += TPB) {
                 const uint32_t c = c_cnt[i];
-                if (c_slot[i] != EMPTY && c)
-                    best = max(best, ((unsigned long long)c << 32) | (uint32_t)~c_key[i]);
+                const unsigned long long v =
+                    c_slot[i] != EMPTY && c ? ((unsigned long long)c << 32) | (uint32_t)~c_key[i] : 0ull;
+                if (v > b) {
+                    b = v;
+                    bi = i;
+                }
             }
-            best = block_max64<TPB / 64>(best, s_best, lane, w);
+            const unsigned long long wb = wave_max64(b);
+            const unsigned long long m = __ballot(b == wb);
+            if (lane == (uint32_t)(__ffsll((long long)m) - 1)) {
+                s_best[w] = wb;
+                s_bidx[w] = bi;
+            }
+            lds_barrier();
+            uint32_t at = 0u;
+#pragma unroll
+            for (int i = 0; i < TPB / 64; ++i)
+                if (s_best[i] > best) {
+                    best = s_best[i];
+                    at = s_bidx[i];
+                }
             if (best && (uint32_t)(best >> 32) >= s_v[0]) {
-                for (uint32_t i = tid; i < (uint32_t)CT; i += TPB)
-                    if (c_slot[i] != EMPTY && c_cnt[i] == (uint32_t)(best >> 32) && c_key[i] == ~(uint32_t)best) {
-                        s_v[8] = c_slot[i];
-                        s_v[11] = c_off[i];
-                        s_v[12] = c_len[i];
-                    }
+                if (tid == 0) {
+                    s_v[8] = c_slot[at];
+                    s_v[11] = c_off[at];
+                    s_v[12] = c_len[at];
+                }
             } else {
                 best = 0ull;
             }
