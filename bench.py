@@ -13,8 +13,10 @@ roofline figures.
 
 Algorithmic bytes of iteration k (n_k symbols before it, n_{k+1} after,
 T table slots of 8 bytes):
-  4 n_k + 4 n_{k+1}: the merge pass reads the symbols once and writes the
-  compacted result once (the roofline figure of k_merge);
+  2 n_k + 2 n_{k+1}: the merge pass reads the symbols (16-bit ids; a word
+  start is a change of byte class between neighbours, so no tag is stored)
+  once and writes the compacted result once (the roofline figure of
+  k_merge);
   + 16 T in an iteration that sweeps the table (for the maximum, then for
   the candidates; "table_sweeps" counts them). The table is never reset
   (its counts are updated in place), so no reset write is credited. Count
@@ -338,7 +340,7 @@ def train_leg(bpe, corpus, spec, steps, warmup, np, torch, time, log, cpu_reps=0
     n_k = lengths[:k].astype(np.float64)
     n_k1 = lengths[1: k + 1].astype(np.float64)
     m_ms = m_ms[:k].astype(np.float64)
-    merge_bytes = 4.0 * n_k + 4.0 * n_k1
+    merge_bytes = 2.0 * n_k + 2.0 * n_k1
     total_wall = float(sum(wall))
     res = {"spec": spec, "data": data, "d": d, "sha": sha, "merges": m, "tokens": t, "lengths": lengths,
            "k": int(k), "wall": wall, "warm_s": warm_s, "value": k * len(wall) / total_wall,
@@ -598,7 +600,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": "u16",
         "data": "synthetic",
         "config": {
             "workload": "%s: %d-byte seeded corpus (%s), %d merges, pair table 2^%d, sha256 %s"

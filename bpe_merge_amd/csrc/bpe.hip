@@ -97,7 +97,7 @@ size_t tag_grid_bound(size_t n) { return (n + TAG_TPB * 16 - 1) / (TAG_TPB * 16)
 uint32_t table_limit(uint32_t tlog2) { return uint32_t((1ull << tlog2) - (1ull << tlog2) / 8); }
 
 struct Layout {
-    size_t ctl, sweep, sym0, sym1, table, status, merges, lengths, fpairs, total;
+    size_t ctl, sweep, sym0, sym1, table, status, merges, lengths, fpairs, cls, cmask, total;
     uint32_t max_tiles;
 };
 
@@ -109,10 +109,10 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     L.sweep = a;
     a = align_up(a + sizeof(bpek::Sweep), 256);
     const size_t sym_elems = align_up(n ? n : 1, TILE) + 64;
-    L.sym0 = a;
-    a = align_up(a + 4 * sym_elems, 256);
+    L.sym0 = a;  // 16-bit ids
+    a = align_up(a + 2 * sym_elems, 256);
     L.sym1 = a;
-    a = align_up(a + 4 * sym_elems, 256);
+    a = align_up(a + 2 * sym_elems, 256);
     L.table = a;
     a = align_up(a + 8 * (size_t(1) << tlog2), 256);
     // at least 512 words: the look-back copies a 512-word window from index 0
@@ -125,6 +125,10 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     a = align_up(a + 4 * (size_t(BPE_MAX_MERGES) + 1), 256);
     L.fpairs = a;  // pairs of replayed iterations, indexed by iteration
     a = align_up(a + 8 * size_t(BPE_MAX_MERGES), 256);
+    L.cls = a;  // class of every id
+    a = align_up(a + 65536, 256);
+    L.cmask = a;  // per class, the bit mask of its ids
+    a = align_up(a + 4 * size_t(bpek::N_CLASSES) * bpek::CLASS_WORDS, 256);
     L.total = a;
     return L;
 }
@@ -171,8 +175,10 @@ struct bpe_state {
     Layout lay{};
     Ctl* ctl = nullptr;
     bpek::Sweep* sweep = nullptr;
-    uint32_t* sym0 = nullptr;
-    uint32_t* sym1 = nullptr;
+    uint16_t* sym0 = nullptr;
+    uint16_t* sym1 = nullptr;
+    uint8_t* cls = nullptr;
+    uint32_t* cmask = nullptr;
     unsigned long long* table = nullptr;
     unsigned long long* status = nullptr;
     uint32_t* merges = nullptr;
@@ -195,13 +201,13 @@ namespace {
 // resident all at once.
 void launch_merge(bpe_state* s, uint32_t it) {
     if (s->merge_tpb == MERGE_TPB_BIG)
-        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG), 0,
-                           s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           s->merges);
+        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG),
+                           bpek::cmask_lds_bytes(it), s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           s->merges, s->cls, s->cmask);
     else
         hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_SMALL),
-                           0, s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           s->merges);
+                           bpek::cmask_lds_bytes(it), s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                           s->merges, s->cls, s->cmask);
 }
 
 void launch_force(bpe_state* s) {
@@ -381,8 +387,10 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
     char* base = static_cast<char*>(s->ws);
     s->ctl = reinterpret_cast<Ctl*>(base + lay.ctl);
     s->sweep = reinterpret_cast<bpek::Sweep*>(base + lay.sweep);
-    s->sym0 = reinterpret_cast<uint32_t*>(base + lay.sym0);
-    s->sym1 = reinterpret_cast<uint32_t*>(base + lay.sym1);
+    s->sym0 = reinterpret_cast<uint16_t*>(base + lay.sym0);
+    s->sym1 = reinterpret_cast<uint16_t*>(base + lay.sym1);
+    s->cls = reinterpret_cast<uint8_t*>(base + lay.cls);
+    s->cmask = reinterpret_cast<uint32_t*>(base + lay.cmask);
     s->table = reinterpret_cast<unsigned long long*>(base + lay.table);
     s->status = reinterpret_cast<unsigned long long*>(base + lay.status);
     s->merges = reinterpret_cast<uint32_t*>(base + lay.merges);
@@ -413,7 +421,7 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
     if (cfg && (cfg->flags & BPE_FLAG_OVERSUBSCRIBE)) s->merge_grid = int(size_t(cus) * per_cu * 4);
 
     // input bytes: device memory is read in place, host memory is uploaded
-    // into the second symbol buffer first (4n bytes hold n bytes)
+    // into the second symbol buffer first (2n bytes hold n bytes)
     const uint8_t* src = bytes;
     if (!is_device_pointer(bytes)) {
         e = hipMemcpyAsync(s->sym1, bytes, n, hipMemcpyHostToDevice, s->stream);
@@ -426,6 +434,7 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
     hipLaunchKernelGGL(bpek::k_fill64, dim3(4), dim3(256), 0, s->stream,
                        reinterpret_cast<unsigned long long*>(s->sweep), sizeof(bpek::Sweep) / 8, 0ull);
     hipLaunchKernelGGL(bpek::k_init_ctl, dim3(1), dim3(64), 0, s->stream, s->ctl, uint32_t(n), s->lengths);
+    hipLaunchKernelGGL(bpek::k_init_classes, dim3(256), dim3(256), 0, s->stream, s->cls, s->cmask);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->table, size_t(s->slots()),
                        bpek::GT_EMPTY);
     hipLaunchKernelGGL(bpek::k_fill64, dim3(s->fill_grid), dim3(256), 0, s->stream, s->status,
@@ -556,8 +565,27 @@ bpe_status bpe_tokens(bpe_state* s, uint32_t* out, size_t cap, size_t* n_out) {
         set_err("tokens capacity %zu is below the %zu symbols", cap, len);
         return BPE_EINVAL;
     }
-    const uint32_t* src = (h.m & 1u) ? s->sym1 : s->sym0;
-    if (len) HIP_TRY(hipMemcpy(out, src, 4 * len, hipMemcpyDefault));
+    // the ids with their word starts (k_expand), written straight into
+    // device memory; for host memory through the free symbol buffer (2
+    // bytes per symbol: the tokens in two halves), which the next pass
+    // overwrites anyway
+    const uint16_t* src = (h.m & 1u) ? s->sym1 : s->sym0;
+    uint16_t* freebuf = (h.m & 1u) ? s->sym0 : s->sym1;
+    const bool dev = is_device_pointer(out);
+    const size_t part = dev ? len : (len + 1) / 2;
+    for (size_t b = 0; b < len; b += part) {
+        const size_t cnt = std::min(part, len - b);
+        uint32_t* dst = dev ? out + b : reinterpret_cast<uint32_t*>(freebuf);
+        const unsigned grid = unsigned(std::min<size_t>((cnt + 255) / 256, 4096));
+        hipLaunchKernelGGL(bpek::k_expand, dim3(grid), dim3(256), 0, s->stream, src, uint32_t(b), uint32_t(cnt),
+                           s->cls, dst);
+        HIP_TRY(hipGetLastError());
+        if (!dev) {
+            HIP_TRY(hipMemcpyAsync(out + b, dst, 4 * cnt, hipMemcpyDeviceToHost, s->stream));
+            HIP_TRY(hipStreamSynchronize(s->stream));
+        }
+    }
+    if (dev) HIP_TRY(hipStreamSynchronize(s->stream));
     return BPE_OK;
 }
 

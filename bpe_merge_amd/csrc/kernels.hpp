@@ -33,8 +33,10 @@
 
 namespace bpek {
 
-constexpr uint32_t WS = 0x10000u;        // word-start bit of a symbol
-constexpr uint32_t IDM = 0xFFFFu;        // id field of a symbol
+constexpr uint32_t WS = 0x10000u;        // word-start bit of a token at the boundary
+constexpr uint32_t IDM = 0xFFFFu;        // id field of a token
+constexpr uint32_t N_CLASSES = 5;        // byte classes (byte_class)
+constexpr uint32_t CLASS_WORDS = 2048;   // words of a class's bit mask: one bit per 16-bit id
 constexpr uint32_t EMPTY = 0xFFFFFFFFu;  // empty key (the pair 65535,65535 is never counted)
 constexpr uint32_t BASE = 256u;
 
@@ -44,6 +46,7 @@ constexpr uint32_t ERR_TABLE = 1u;  // the global pair table is full
 // chunks). Both wait only for work a workgroup that is already running has
 // taken on, so only a fault can make them fail.
 constexpr uint32_t ERR_SPIN = 2u;
+constexpr uint32_t ERR_CLASS = 16u;  // a merge names an id with no class (ids below X always have one)
 
 constexpr uint32_t LDS_PROBES = 16;        // buckets probed before giving up on an LDS table
 constexpr uint32_t GT_PROBES = 4096;       // slots probed before giving up on the global table
@@ -436,6 +439,34 @@ __global__ void k_init_ctl(Ctl* ctl, uint32_t n, uint32_t* lengths) {
     }
 }
 
+// The class of every id (a byte: its byte class; a merged id: written by
+// the pass that creates it) and, per class, the bit mask of its ids.
+// Launched over at least 65,536 threads.
+__global__ void k_init_classes(uint8_t* __restrict__ cls, uint32_t* __restrict__ cmask) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 65536u) cls[i] = i < BASE ? (uint8_t)byte_class(i) : (uint8_t)0xFFu;
+    if (i < N_CLASSES * CLASS_WORDS) {
+        const uint32_t c = i / CLASS_WORDS, wd = i % CLASS_WORDS;
+        uint32_t m = 0;
+        if (wd < BASE / 32u)
+            for (uint32_t b = 0; b < 32u; ++b) m |= (byte_class(32u * wd + b) == c ? 1u : 0u) << b;
+        cmask[i] = m;
+    }
+}
+
+// Tokens in the boundary's format from the 16-bit ids sym[begin ..
+// begin + count): id | WS on the first token of each word, that is at
+// position 0 and wherever the class changes from the token before (words
+// are maximal runs of one class, and every token lies inside one).
+__global__ void k_expand(const uint16_t* __restrict__ sym, uint32_t begin, uint32_t count,
+                         const uint8_t* __restrict__ cls, uint32_t* __restrict__ out) {
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) {
+        const uint32_t p = begin + i, v = sym[p];
+        const bool start = p == 0u || cls[v] != cls[sym[p - 1u]];
+        out[i] = v | (start ? WS : 0u);
+    }
+}
+
 // fill a buffer of 64-bit words with one value (status words, table slots)
 __global__ void k_fill64(unsigned long long* p, size_t count, unsigned long long v) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count;
@@ -445,13 +476,15 @@ __global__ void k_fill64(unsigned long long* p, size_t count, unsigned long long
 
 // ---------------------------------------------------------------- tag + count (iteration 0)
 // Blocks take chunks of TPB * 16 bytes in turn; a thread covers 16
-// consecutive bytes (one 16-byte load when the input is aligned, four
-// 16-byte stores of symbols). The chunk loop is uniform over the block so
+// consecutive bytes (one 16-byte load when the input is aligned, two
+// 16-byte stores of 16-bit symbols). The word starts decide which pairs
+// are counted; the symbol array holds the ids alone (a word start is a
+// change of class between neighbours). The chunk loop is uniform over the block so
 // that the LDS table can be flushed between chunks.
 
 template <int TPB, int LT>
 __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ bytes, uint32_t n,
-                                                   uint32_t* __restrict__ sym, GTable gt, Ctl* ctl) {
+                                                   uint16_t* __restrict__ sym, GTable gt, Ctl* ctl) {
     constexpr uint32_t CH = TPB * 16;
     constexpr uint32_t QCAP = TPB * 8;
     __shared__ LdsTable<LT> tab;
@@ -485,10 +518,12 @@ __global__ __launch_bounds__(TPB) void k_tag_count(const uint8_t* __restrict__ b
         if (base + 16 <= n) {
             uint4* o = reinterpret_cast<uint4*>(sym + base);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = make_uint4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+            for (int q = 0; q < 2; ++q)
+                o[q] = make_uint4(b[8 * q] | (b[8 * q + 1] << 16), b[8 * q + 2] | (b[8 * q + 3] << 16),
+                                  b[8 * q + 4] | (b[8 * q + 5] << 16), b[8 * q + 6] | (b[8 * q + 7] << 16));
         } else {
             for (int j = 0; j < 16; ++j)
-                if (base + j < n) sym[base + j] = s[j];
+                if (base + j < n) sym[base + j] = (uint16_t)b[j];
         }
         // pairs whose right symbol starts no word; equal keys folded into one add
         uint32_t keys[16];

@@ -17,6 +17,17 @@
 // the scan is a single-pass decoupled look-back over tiles of 16384 symbols
 // (1024-thread workgroups) or 8192 (512-thread workgroups, on small
 // corpora), so the symbols are read once and written once per iteration.
+//
+// The symbol array holds 16-bit ids and no word-start bit. The page tags
+// the first symbol of each word ("Ne Yapar? 1"); here that tag is implied:
+// a word is a maximal run of one byte class, every token lies inside one
+// word, so a token has its first byte's class, and two neighbouring words
+// always differ in class. A pair of neighbours therefore straddles a word
+// start exactly when their classes differ, and the merge (L, R), a counted
+// pair, has both ids in one class: any neighbouring L, R lie in one word.
+// The class of every id is kept in a byte table (the class of X is that of
+// L), and per class a bit mask of the ids in it; a pass copies the mask of
+// its merge's class into LDS for the few pairs whose counts change.
 #pragma once
 
 #include "kernels.hpp"
@@ -24,8 +35,9 @@
 namespace bpek {
 
 // Selection recurrence. An occurrence at position i (right symbol of the
-// pair) is occ_i = (no tag on s_i) and id(s_{i-1}) == L and id(s_i) == R;
-// the left-to-right scan merges it iff sel_i = occ_i and not sel_{i-1}.
+// pair) is occ_i = (s_{i-1} == L and s_i == R; no word start lies between
+// them, as L and R share a class); the left-to-right scan merges it iff
+// sel_i = occ_i and not sel_{i-1}.
 // A segment's effect on this recurrence and on the number of symbols it
 // keeps is a 4-tuple, composed associatively across lanes, waves and tiles:
 //   c0      symbols kept when the segment is entered with sel = 0
@@ -237,24 +249,22 @@ __host__ __device__ constexpr uint32_t skew(uint32_t i) { return i + (i >> 5); }
 
 // Count changes of one thread's positions (bit j: position g0 + j).
 // sel holds sel for positions g0 .. g0 + V (bit V: the next thread's first),
-// sel_in the sel of position g0 - 1; x the old symbols, left the old symbol
-// at g0 - 1. Position i changes if it is dropped (sel_i) or becomes X
-// (sel_{i+1}). An old pair (i - 1, i), counted when i carries no word-start
-// tag, is gone if i - 1 or i changes. A kept position i with no tag forms
-// the new pair (left neighbour, value) and it is new if either side is an X:
-// the left neighbour is X when i - 1 was dropped (sel_{i-1}), otherwise the
-// unchanged old symbol i - 1; the value is X when sel_{i+1}.
+// sel_in the sel of position g0 - 1, valid the positions below n. Position
+// i changes if it is dropped (sel_i) or becomes X (sel_{i+1}). An old pair
+// (i - 1, i) is gone if i - 1 or i changes. A kept position i forms the new
+// pair (left neighbour, value) and it is new if either side is an X: the
+// left neighbour is X when i - 1 was dropped (sel_{i-1}), otherwise the
+// unchanged old symbol i - 1; the value is X when sel_{i+1}. Both masks
+// hold candidates: a pair counts only if its ids share a class (no word
+// start between them), which count_changes tests.
 template <int V>
 struct Changes {
     uint32_t gone, born;  // position masks
-    __device__ __forceinline__ Changes(const uint32_t (&x)[V], uint32_t sel, uint32_t sel_in) {
+    __device__ __forceinline__ Changes(uint32_t sel, uint32_t sel_in, uint32_t valid) {
         constexpr uint32_t VM = (1u << V) - 1u;
-        uint32_t untagged = 0;
-#pragma unroll
-        for (int j = 0; j < V; ++j) untagged |= (uint32_t)!(x[j] & WS) << j;  // positions past n carry WS
         const uint32_t sm1 = ((sel << 1) | sel_in) & VM, s0 = sel & VM, sp1 = (sel >> 1) & VM;
-        gone = (sm1 | s0 | sp1) & untagged;
-        born = ~s0 & (sm1 | sp1) & untagged & VM;
+        gone = (sm1 | s0 | sp1) & valid;
+        born = ~s0 & (sm1 | sp1) & valid & VM;
     }
 };
 
@@ -272,34 +282,41 @@ struct CountArgs {
 // position j of the thread is needed without indexing registers: a dropped
 // position held R, one that becomes X held L, and any other position is
 // kept unchanged and already staged in LDS (st, at the thread's offset o
-// plus the number of kept positions before j). left: old symbol at g0 - 1.
+// plus the number of kept positions before j). left: old symbol at g0 - 1
+// (NOSYM before the first position). cm: the bit mask of the ids below X
+// in the merge's class, in LDS; X is in that class, NOSYM in none.
 template <int LT>
 __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, Sweep* sw,
                                               uint32_t theta, uint32_t gone, uint32_t born, uint32_t sel,
                                               uint32_t sel_in, uint32_t left, const uint32_t* st, uint32_t o,
-                                              uint32_t kept, uint32_t L, uint32_t R, uint32_t X) {
+                                              uint32_t kept, uint32_t L, uint32_t R, uint32_t X, const uint32_t* cm) {
     auto old_id = [&](uint32_t j) -> uint32_t {
         if ((sel >> j) & 1u) return R;
         if ((sel >> (j + 1)) & 1u) return L;
-        return st[skew(o + __popc(kept & ((1u << j) - 1u)))] & IDM;
+        return st[skew(o + __popc(kept & ((1u << j) - 1u)))];
     };
+    auto in_class = [&](uint32_t v) -> bool { return v == X || (v < X && ((cm[v >> 5] >> (v & 31u)) & 1u)); };
     const uint32_t sm1 = (sel << 1) | sel_in;  // bit j: sel of position j - 1
     while (gone | born) {
         const bool is_gone = gone != 0u;
         const uint32_t j = __ffs(is_gone ? gone : born) - 1;
         const uint32_t xl = j ? old_id(j - 1) : left;
-        uint32_t key, delta;
+        uint32_t a, b, delta;
         if (is_gone) {
-            key = pair_key(xl, old_id(j));
+            a = xl;
+            b = old_id(j);
             delta = 0xFFFFFFFFu;
             gone &= gone - 1u;
         } else {
-            key = pair_key(((sm1 >> j) & 1u) ? X : xl, ((sel >> (j + 1)) & 1u) ? X : old_id(j));
+            a = ((sm1 >> j) & 1u) ? X : xl;
+            b = ((sel >> (j + 1)) & 1u) ? X : old_id(j);
             delta = 1u;
             born &= born - 1u;
         }
-        if (!tab.insert(key, delta))  // the LDS table is full: straight to the global one
-            gt_add_sel(gt, key, delta, ctl, sw, theta);
+        // one id of the pair is L, R or X: the pair lies in one word iff
+        // the other id has the merge's class too
+        if (in_class(a) && in_class(b) && !tab.insert(pair_key(a, b), delta))
+            gt_add_sel(gt, pair_key(a, b), delta, ctl, sw, theta);  // the LDS table is full
     }
 }
 
@@ -310,55 +327,67 @@ constexpr uint32_t BUF_OOB = 0x80000000u;   // an offset past any buffer: the st
 // them back long after this pass has streamed the rest of the array)
 constexpr int BUF_NT = 2;
 
+// A position past the array or before its start, in registers: no id
+// equals it and it belongs to no class.
+constexpr uint32_t NOSYM = 0x10000u;
+
 // Issue the loads of a thread's V = 16 symbols at g0 = tile * TILE + tid * 16
-// and, on the wave's edge lanes, of the neighbours the shuffles cannot
-// supply: h1 = sym[g0 - 1], h2 = sym[g0 - 2] on lane 0, hr = sym[g0 + 16] on
-// lane 63. Buffer loads through a resource covering the tile, the two
-// symbols before it and the one after it (within n): every lane issues the
-// same seven loads, a lane with nothing to load uses an offset past the
-// resource (the hardware returns 0 without a memory access), and a tile
-// past the end gets an empty resource. With no branch and a fixed count,
-// the compiler can wait for these loads alone, later. Values outside
-// [0, n) are undefined here; fix_tile replaces them by WS.
+// (two 16-byte loads) and, on the wave's edge lanes, of the neighbours the
+// shuffles cannot supply: hw = sym[g0 - 2] | sym[g0 - 1] << 16 on lane 0,
+// hr (low half: sym[g0 + 16]) on lane 63. Buffer loads through a resource
+// covering the tile, the two symbols before it and the one after it
+// (within n, in whole 4-byte words: the padded array holds the 16-bit word
+// past n): every lane issues the same four loads, a lane with nothing to
+// load uses an offset past the resource (the hardware returns 0 without a
+// memory access), and a tile past the end gets an empty resource. With no
+// branch and a fixed count, the compiler can wait for these loads alone,
+// later. The words stay packed until fix_tile, so that nothing reads them
+// in the round that issues them. Values outside [0, n) are undefined here;
+// fix_tile replaces them by NOSYM.
 template <int TILE>
-__device__ __forceinline__ void load_tile(const uint32_t* __restrict__ in, uint32_t n, uint32_t tile,
-                                          uint32_t ntiles, uint32_t tid, uint32_t lane, uint32_t (&x)[16],
-                                          uint32_t& h1, uint32_t& h2, uint32_t& hr) {
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ in, uint32_t n, uint32_t tile,
+                                          uint32_t ntiles, uint32_t tid, uint32_t lane, uint32_t (&xr)[8],
+                                          uint32_t& hw, uint32_t& hr) {
     tile = __builtin_amdgcn_readfirstlane(tile);  // uniform: the resource lives in SGPRs
-    const uint32_t ts = tile * TILE, hb = ts >= 2u ? ts - 2u : 0u;
+    const uint32_t ts = tile * TILE, hb = ts >= 2u ? ts - 2u : 0u;  // even: 4-byte aligned
     const uint32_t end = tile < ntiles ? min(n, ts + TILE + 1u) : hb;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(in) + hb, 0, (int)(4u * (end - hb)), BUF_RSRC_FLAGS);
-    const uint32_t g0 = ts + tid * 16u, o = 4u * (g0 - hb);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(in) + hb, 0, (int)((2u * (end - hb) + 2u) & ~3u), BUF_RSRC_FLAGS);
+    const uint32_t g0 = ts + tid * 16u, o = 2u * (g0 - hb);
     // the edge values first: the compiler can then wait for them without
     // waiting for the 16-byte loads (one in-order counter)
-    h1 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 1u) ? o - 4u : BUF_OOB, 0, 0);
-    h2 = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 8u : BUF_OOB, 0, 0);
-    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 64u : BUF_OOB, 0, 0);
+    hw = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 4u : BUF_OOB, 0, 0);
+    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 32u : BUF_OOB, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
-        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+        xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
     }
 }
 
-// After load_tile: WS in place of every value outside [0, n), then the
-// neighbours a1 = sym[g0 - 1], a2 = sym[g0 - 2], b1 = sym[g0 + 16].
-__device__ __forceinline__ void fix_tile(uint32_t (&x)[16], uint32_t h1, uint32_t h2, uint32_t hr, uint32_t g0,
-                                         uint32_t n, uint32_t lane, bool full, uint32_t& a1, uint32_t& a2,
-                                         uint32_t& b1) {
+// After load_tile: the 16 ids, NOSYM in place of every value outside
+// [0, n), then the neighbours a1 = sym[g0 - 1], a2 = sym[g0 - 2],
+// b1 = sym[g0 + 16] (NOSYM outside [0, n)).
+__device__ __forceinline__ void fix_tile(uint32_t (&x)[16], const uint32_t (&xr)[8], uint32_t hw, uint32_t hr,
+                                         uint32_t g0, uint32_t n, uint32_t lane, bool full, uint32_t& a1,
+                                         uint32_t& a2, uint32_t& b1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[2 * j] = xr[j] & 0xFFFFu;
+        x[2 * j + 1] = xr[j] >> 16;
+    }
     if (!full) {  // uniform: the last tile
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? x[j] : WS;
+        for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? x[j] : NOSYM;
     }
-    a1 = dpp<DPP_WAVE_SHR1>(WS, x[15]);  // from lane - 1
-    a2 = dpp<DPP_WAVE_SHR1>(WS, x[14]);
-    b1 = dpp<DPP_WAVE_SHL1>(WS, x[0]);  // from lane + 1
+    a1 = dpp<DPP_WAVE_SHR1>(NOSYM, x[15]);  // from lane - 1
+    a2 = dpp<DPP_WAVE_SHR1>(NOSYM, x[14]);
+    b1 = dpp<DPP_WAVE_SHL1>(NOSYM, x[0]);  // from lane + 1
     if (lane == 0) {
-        a1 = g0 >= 1u ? h1 : WS;
-        a2 = g0 >= 2u ? h2 : WS;
+        a1 = (g0 >= 1u && g0 - 1u < n) ? hw >> 16 : NOSYM;
+        a2 = (g0 >= 2u && g0 - 2u < n) ? hw & 0xFFFFu : NOSYM;
     }
-    if (lane == 63) b1 = (g0 + 16u < n) ? hr : WS;
+    if (lane == 63) b1 = (g0 + 16u < n) ? hr & 0xFFFFu : NOSYM;
 }
 
 // Occurrence bits of a thread (bit j: position g0 + j, bit V: position
@@ -368,73 +397,72 @@ __device__ __forceinline__ void occurrences(const uint32_t (&x)[V], uint32_t a1,
                                             uint32_t n, uint32_t L, uint32_t R, uint32_t& occ,
                                             uint32_t& valid) {
     // bitwise, not short-circuit: no branch per position. A position
-    // past n holds WS, and position 0 always carries WS, so the tag test
-    // also rules those out.
-    // Symbols hold bits 0-16 only (id and WS), so x == R tests the id and
-    // the absence of the tag at once.
+    // outside [0, n) holds NOSYM, which equals neither L nor R.
     occ = 0;
     uint32_t prev = a1;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const uint32_t o = (uint32_t)((prev & IDM) == L) & (uint32_t)(x[j] == R);
+        const uint32_t o = (uint32_t)(prev == L) & (uint32_t)(x[j] == R);
         occ |= o << j;
         prev = x[j];
     }
-    occ |= ((uint32_t)((x[V - 1] & IDM) == L) & (uint32_t)(b1 == R)) << V;
+    occ |= ((uint32_t)(x[V - 1] == L) & (uint32_t)(b1 == R)) << V;
     valid = (g0 >= n) ? 0u : (n - g0 >= (uint32_t)V ? (1u << V) - 1u : (1u << (n - g0)) - 1u);
 }
 
-// Write the kept symbols of a tile from LDS (st) to out[tile_off ..
-// tile_off + tile_kept): up to 3 single symbols to reach 16-byte alignment,
-// whole 16-byte groups, up to 3 single symbols at the end. Each thread
-// issues the same fixed sequence of buffer stores (one 4-byte, TILE/4/TPB
-// 16-byte, one 4-byte); a store with nothing to write gets an offset past
-// the buffer, which the hardware drops. With no branch and a fixed count,
-// the compiler can wait for loads issued before these stores without
-// waiting for the stores themselves.
+// Write the kept symbols of a tile from LDS (st, 32-bit slots) to
+// out[tile_off .. tile_off + tile_kept) as 16-bit ids: up to 7 single
+// symbols to reach 16-byte alignment, whole groups of 8 (one 16-byte store
+// each), up to 7 single symbols at the end. Each thread issues the same
+// fixed sequence of buffer stores (one 2-byte, TILE/8/TPB 16-byte, one
+// 2-byte); a store with nothing to write gets an offset past the buffer,
+// which the hardware drops. With no branch and a fixed count, the compiler
+// can wait for loads issued before these stores without waiting for the
+// stores themselves. out is 16-byte aligned.
 template <int TPB, int TILE>
-__device__ __forceinline__ void store_tile(uint32_t* __restrict__ out, const uint32_t* st, uint32_t tile_off,
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uint32_t* st, uint32_t tile_off,
                                            uint32_t tile_kept) {
     const uint32_t tid = threadIdx.x;
     tile_off = __builtin_amdgcn_readfirstlane(tile_off);  // uniform: the resource lives in SGPRs
     tile_kept = __builtin_amdgcn_readfirstlane(tile_kept);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(out + tile_off, 0, (int)(4u * tile_kept), BUF_RSRC_FLAGS);
-    const uint32_t head = min(tile_kept, (4u - (tile_off & 3u)) & 3u);
-    const uint32_t body = (tile_kept - head) >> 2;
-    const uint32_t rest = head + 4 * body;
+        __builtin_amdgcn_make_buffer_rsrc(out + tile_off, 0, (int)(2u * tile_kept), BUF_RSRC_FLAGS);
+    const uint32_t head = min(tile_kept, (8u - (tile_off & 7u)) & 7u);
+    const uint32_t body = (tile_kept - head) >> 3;
+    const uint32_t rest = head + 8 * body;
     {
         const bool on = tid < head;
         const uint32_t i = on ? tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b32(st[skew(i)], rs, on ? 4u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
-    // Group q of the thread holds symbols b + 4 * TPB * q .. + 3 with
-    // b = head + 4 * tid. A step of 4 * TPB symbols (a multiple of 32) moves
-    // every skewed index by the same amount, so the four LDS addresses are
-    // formed once and the groups add a constant. A group past the body
-    // still reads inside the (padded) staging buffer; its store is dropped.
-    constexpr uint32_t QSTEP = skew(4 * TPB);
-    static_assert((4 * TPB) % 32 == 0, "groups keep their offset within 32 symbols");
-    const uint32_t b = head + 4u * tid;
-    const uint32_t* p0 = st + skew(b);
-    const uint32_t* p1 = st + skew(b + 1u);
-    const uint32_t* p2 = st + skew(b + 2u);
-    const uint32_t* p3 = st + skew(b + 3u);
+    // Group q of the thread holds symbols b + 8 * TPB * q .. + 7 with
+    // b = head + 8 * tid. A step of 8 * TPB symbols (a multiple of 32) moves
+    // every skewed index by the same amount. A group past the body still
+    // reads inside the (padded) staging buffer; its store is dropped.
+    constexpr uint32_t QSTEP = skew(8 * TPB);
+    static_assert((8 * TPB) % 32 == 0, "groups keep their offset within 32 symbols");
+    const uint32_t b = head + 8u * tid;
+    uint32_t a[8];
 #pragma unroll
-    for (int q = 0; q < TILE / 4 / TPB; ++q) {
+    for (int k = 0; k < 8; ++k) a[k] = skew(b + (uint32_t)k);
+#pragma unroll
+    for (int q = 0; q < TILE / 8 / TPB; ++q) {
         const bool on = tid + q * TPB < body;
-        const v4u32 v = {p0[q * QSTEP], p1[q * QSTEP], p2[q * QSTEP], p3[q * QSTEP]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 4u * (b + 4u * TPB * q) : BUF_OOB, 0, BUF_NT);
+        uint32_t u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[k] = st[a[k] + q * QSTEP];
+        const v4u32 v = {u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16)};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 2u * (b + 8u * TPB * q) : BUF_OOB, 0, BUF_NT);
     }
     {
         const bool on = tid < tile_kept - rest;
         const uint32_t i = on ? rest + tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b32(st[skew(i)], rs, on ? 4u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
 }
 
 // Stage the kept symbols of a thread at tile-local offset o; a symbol whose
-// right neighbour merges into it becomes X (keeping its tag).
+// right neighbour merges into it becomes X.
 template <int V>
 __device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
                                       uint32_t sel, uint32_t X) {
@@ -452,7 +480,7 @@ __device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
-                st[skew(o)] = ((sel >> (j + 1)) & 1u) ? (X | (x[j] & WS)) : x[j];
+                st[skew(o)] = ((sel >> (j + 1)) & 1u) ? X : x[j];
                 ++o;
             }
         }
@@ -474,8 +502,8 @@ __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, ui
 // global_load_lds.
 constexpr int LB_PL = 4;
 constexpr int LB_WIN = 2 * 64 * LB_PL;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= 7, expcnt and lgkmcnt untouched
-constexpr int WAIT_VM7 = 0x0F77;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 4, expcnt and lgkmcnt untouched
+constexpr int WAIT_VM4 = 0x0F74;
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 
 // One persistent pass per iteration. Workgroups take tiles from a counter,
@@ -536,10 +564,9 @@ __device__ __forceinline__ void lds_copy16(const unsigned long long* src, const 
 // Values loaded by load_tile that a round does not consume: an empty use,
 // so that the compiler waits for their loads in that round and not when
 // the registers are next loaded.
-__device__ __forceinline__ void retire(const uint32_t (&x)[16], uint32_t h1, uint32_t h2, uint32_t hr) {
-    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
-                 "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]),
-                 "v"(h1), "v"(h2), "v"(hr));
+__device__ __forceinline__ void retire(const uint32_t (&xr)[8], uint32_t hw, uint32_t hr) {
+    asm volatile("" ::"v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]),
+                 "v"(xr[7]), "v"(hw), "v"(hr));
 }
 
 // ---------------------------------------------------------------- selection
@@ -771,23 +798,32 @@ __device__ __forceinline__ void finish_counts(LdsTable<LT>& tab, const GTable& g
     if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
 }
 
+// Dynamic LDS of the pass of iteration it: the class mask of ids up to
+// X = 256 + it.
+__host__ __device__ constexpr uint32_t cmask_lds_bytes(uint32_t it) { return 4u * (((BASE + it) >> 5) + 1u); }
+
 // One launch per iteration it (the host passes it; a launch after training
 // has stopped does nothing). The workgroup that draws ticket 0 selects the
 // merge and publishes it; the others read the publication while their
 // first tile's loads are in flight.
 template <int TPB, int LT>
 // two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
-__global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_t* __restrict__ buf0,
-                                               uint32_t* __restrict__ buf1, GTable gt,
+__global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
+                                               uint16_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
-                                               uint32_t* lengths, Sweep* sw, uint32_t* merges) {
-    constexpr int V = 16;  // symbols per thread: four 16-byte loads
+                                               uint32_t* lengths, Sweep* sw, uint32_t* merges,
+                                               uint8_t* __restrict__ cls, uint32_t* __restrict__ cmask) {
+    constexpr int V = 16;  // symbols per thread: two 16-byte loads
     constexpr int TILE = TPB * V;
     constexpr int NW = TPB / 64;
     constexpr uint32_t VM = (1u << V) - 1u;
     constexpr uint32_t SST = TILE + TILE / 32;  // one staging buffer (skewed)
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
-    __shared__ uint32_t s_stage[2 * SST + 4];  // + 4: reads of dropped store groups stay inside
+    __shared__ uint32_t s_stage[2 * SST + 8];  // + 8: reads of dropped store groups stay inside
+    // ids up to X in the merge's class: (X >> 5) + 1 words of dynamic LDS
+    // (cmask_lds_bytes), so that early passes of small corpora keep two
+    // workgroups per CU
+    extern __shared__ uint32_t s_cmask[];
     __shared__ uint32_t s_wagg[NW];
     __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now, s_u32;
     __shared__ unsigned long long s_best[NW];
@@ -797,8 +833,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
     if (ctl->done) return;  // training has stopped
     const uint32_t p = it & 1u;  // parity of the per-iteration counters
     const uint32_t n = ctl->n[it & 1u];
-    const uint32_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
-    uint32_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
+    const uint16_t* __restrict__ in = (it & 1u) ? buf1 : buf0;
+    uint16_t* __restrict__ out = (it & 1u) ? buf0 : buf1;
     const uint32_t ntiles = (n + TILE - 1) / TILE;
     const uint32_t epoch = it + 1;
     const uint32_t X = BASE + it;
@@ -834,9 +870,9 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
         lds_barrier();
     }
     uint32_t t = s_tile[0] - tile_base;
-    uint32_t x[V], h1, h2, hr;
+    uint32_t x[V], xr[V / 2], hw, hr;
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
-    load_tile<TILE>(in, n, t, ntiles, tid, lane, x, h1, h2, hr);
+    load_tile<TILE>(in, n, t, ntiles, tid, lane, xr, hw, hr);
     unsigned long long best = read_publication(sw, ctl, p, it, s_best);
     if (best == SEL_SWEEP) best = sweep_select<TPB>(gt, sw, ctl, p, it, s_best, &s_u32, lane, w, theta);  // uniform
     if (best == 0ull) {  // uniform: no countable pair is left
@@ -845,15 +881,31 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
     }
     // uniform: keep the merge in scalar registers
     const uint32_t key = __builtin_amdgcn_readfirstlane(~(uint32_t)best);
-    const uint32_t L = key >> 16, R = key & IDM;
+    const uint32_t L = key >> 16;
+    // the class of the merge (L < X: set by the start or an earlier pass);
+    // a replayed pair of two classes never occurs: its R matches no symbol
+    const uint32_t c = __builtin_amdgcn_readfirstlane((uint32_t)cls[L]);
+    if (c >= N_CLASSES) {  // uniform over the grid: the same L everywhere
+        if (blockIdx.x == 0 && tid == 0) {
+            atomicOr(&ctl->err, ERR_CLASS);
+            st_agent(&ctl->done, 1u);
+        }
+        return;
+    }
+    const uint32_t R = (uint32_t)cls[key & IDM] == c ? key & IDM : NOSYM + 1u;
     if (blockIdx.x == 0 && tid == 0) {
         merges[3 * it + 0] = L;
-        merges[3 * it + 1] = R;
+        merges[3 * it + 1] = key & IDM;
         merges[3 * it + 2] = __builtin_amdgcn_readfirstlane((uint32_t)(best >> 32));
         ctl->L = L;
-        ctl->R = R;
+        ctl->R = key & IDM;
         ctl->X = X;
+        // X has L's class; passes of this launch read only bits below X
+        cls[X] = (uint8_t)c;
+        atomicOr(&cmask[c * CLASS_WORDS + (X >> 5)], 1u << (X & 31u));
     }
+    // the mask of the merge's class, for the ids up to X
+    for (uint32_t i = tid; i <= (X >> 5) && i < CLASS_WORDS; i += TPB) s_cmask[i] = cmask[c * CLASS_WORDS + i];
 
     if (L != R) {
         // tp: the tile staged in the previous round, waiting for its offset
@@ -885,11 +937,11 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
                 uint32_t a1, a2, b1;
-                fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
+                fix_tile(x, xr, hw, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
                 uint32_t occ, valid;
                 occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
                 // sel = occ; the position before g0 is merged iff it is an occurrence
-                const uint32_t sel_in = (g0 >= 1 && !(a1 & WS) && (a2 & IDM) == L && (a1 & IDM) == R) ? 1u : 0u;
+                const uint32_t sel_in = (a2 == L && a1 == R) ? 1u : 0u;  // NOSYM before the start
 
                 // ---- kept counts: wave scan, then across the waves
                 const uint32_t kept = __popc(valid & ~occ & VM);
@@ -908,26 +960,26 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
                 uint32_t* st = s_stage + cur * SST;
                 stage<V>(st, my_local, x, valid, occ, X);
                 if (do_count && (occ | sel_in)) {
-                    const Changes<V> ch(x, occ, sel_in);
+                    const Changes<V> ch(occ, sel_in, valid);
                     cc = CountArgs{ch.gone, ch.born, occ, sel_in, a1, st, my_local, valid & ~occ};
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(x, h1, h2, hr);
+                retire(xr, hw, hr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, xr, hw, hr);
             if (cc.gone | cc.born)
                 count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
-                                  L, R, X);
+                                  L, R, X, s_cmask);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
                 if (tp != 0) {
-                    // the window's copies are older than the seven loads of
-                    // load_tile above: all but the last seven accesses done
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM7);
+                    // the window's copies are older than the four loads of
+                    // load_tile above: all but the last four accesses done
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll
@@ -996,7 +1048,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;
                 uint32_t a1, a2, b1;
-                fix_tile(x, h1, h2, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
+                fix_tile(x, xr, hw, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
                 uint32_t occ, valid;
                 occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
 
@@ -1019,7 +1071,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
                 if (lane == 63) s_wagg[w] = incl;
                 if (tid == 0) {
                     s_tile[round & 1u] = grab - tile_base;
-                    s_dep = (occ & 1u) | (uint32_t)((a2 & IDM) == L && (a1 & (WS | IDM)) == L);
+                    s_dep = (occ & 1u) | (uint32_t)(a2 == L && a1 == L);
                 }
                 lds_barrier();
                 uint32_t wave_excl;
@@ -1067,24 +1119,24 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint32_
                 uint32_t* st = s_stage + cur * SST;
                 stage<V>(st, my_local, x, valid, selbits, X);
                 if (do_count && (occ | sel_in)) {
-                    const Changes<V> ch(x, selbits, sel_in);
+                    const Changes<V> ch(selbits, sel_in, valid);
                     cc = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, my_local, valid & ~selbits};
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(x, h1, h2, hr);
+                retire(xr, hw, hr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, x, h1, h2, hr);
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, xr, hw, hr);
             if (cc.gone | cc.born)
                 count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
-                                  L, R, X);
+                                  L, R, X, s_cmask);
             // ---- the previous tile: its offset (unless its look-back is done)
             if (tp < ntiles && w == 0) {
                 uint32_t off = off_p, sel = 0;
                 if (!done_p) {  // tp != 0
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM7);
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll

@@ -31,8 +31,12 @@
  * adds the new pairs that touch the new symbol. Every other adjacency is
  * the same before and after the merge, so the table stays exact.
  *
- * Symbols are uint32: bits 0-15 hold the id, bit 16 the word-start tag,
- * bits 17-31 are zero. Ids fit in 16 bits, hence BPE_MAX_MERGES.
+ * Tokens are uint32: bits 0-15 hold the id, bit 16 the word-start tag,
+ * bits 17-31 are zero. Ids fit in 16 bits, hence BPE_MAX_MERGES. Between
+ * iterations the device holds 16-bit ids alone: a word is a maximal run of
+ * one byte class and every token lies inside one word, so a token's tag is
+ * a change of class from the token before it (or position 0), which the
+ * library derives from a per-id class table when tokens are read out.
  *
  * Pointers: arguments named "bytes", "merges", "tokens" and "lengths" may be
  * host or device pointers (device memory of the state's GPU); the library

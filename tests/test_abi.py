@@ -51,9 +51,10 @@ def test_strerror(bpe):
 def test_workspace_bytes(bpe):
     n = 1 << 28
     ws = bpe.workspace_bytes(n, 22)
-    # two uint32 symbol buffers + the global pair table of 2^22 8-byte
-    # slots, plus small parts (control block, look-back status, merges)
-    assert 2 * 4 * n + 8 * (1 << 22) <= ws <= 2 * 4 * n + 8 * (1 << 22) + (8 << 20)
+    # two buffers of 16-bit symbols + the global pair table of 2^22 8-byte
+    # slots, plus small parts (control block, look-back status, merges,
+    # the class of every id)
+    assert 2 * 2 * n + 8 * (1 << 22) <= ws <= 2 * 2 * n + 8 * (1 << 22) + (8 << 20)
     assert bpe.workspace_bytes(n, 24) - ws == 8 * ((1 << 24) - (1 << 22))
     assert bpe.workspace_bytes(10, 0) > 0
     assert bpe.workspace_bytes(1 << 31, 22) == 0       # above the size limit
