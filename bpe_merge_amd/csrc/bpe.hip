@@ -42,8 +42,8 @@ namespace {
 constexpr int MERGE_TPB_BIG = 1024;
 constexpr int MERGE_TPB_SMALL = 512;
 constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
-constexpr int TILE = MERGE_TPB_BIG * 16;   // the larger tile: symbol buffers are padded to it
-constexpr int TILE_SMALL = MERGE_TPB_SMALL * 16;
+constexpr int TILE = MERGE_TPB_BIG * bpek::MERGE_SYMS_PER_THREAD;  // the larger tile: symbol buffers are padded to it
+constexpr int TILE_SMALL = MERGE_TPB_SMALL * bpek::MERGE_SYMS_PER_THREAD;
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 
@@ -412,7 +412,7 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>,
                                                          MERGE_TPB_SMALL, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    const size_t merge_tile = size_t(s->merge_tpb) * 16;
+    const size_t merge_tile = size_t(s->merge_tpb) * bpek::MERGE_SYMS_PER_THREAD;
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, tag_grid_bound(n)));
     s->fill_grid = cus * 4;

@@ -242,8 +242,10 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
     }
 }
 
-// LDS index skew for staged output (thread-contiguous runs spread over banks)
-__host__ __device__ constexpr uint32_t skew(uint32_t i) { return i + (i >> 5); }
+// LDS index skew for staged output in 16-bit slots: one bank (two slots)
+// further every 128 symbols, so that the runs of consecutive threads, and
+// the store groups, start on different banks
+__host__ __device__ constexpr uint32_t skew(uint32_t i) { return i + 2u * (i >> 7); }
 
 
 
@@ -272,7 +274,7 @@ struct Changes {
 // the next tile's loads are issued (gone = born = 0: nothing to count).
 struct CountArgs {
     uint32_t gone, born, sel, sel_in, left;
-    const uint32_t* st;
+    const uint16_t* st;
     uint32_t o, kept;
 };
 
@@ -288,12 +290,12 @@ struct CountArgs {
 template <int LT>
 __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& gt, Ctl* ctl, Sweep* sw,
                                               uint32_t theta, uint32_t gone, uint32_t born, uint32_t sel,
-                                              uint32_t sel_in, uint32_t left, const uint32_t* st, uint32_t o,
+                                              uint32_t sel_in, uint32_t left, const uint16_t* st, uint32_t o,
                                               uint32_t kept, uint32_t L, uint32_t R, uint32_t X, const uint32_t* cm) {
     auto old_id = [&](uint32_t j) -> uint32_t {
         if ((sel >> j) & 1u) return R;
         if ((sel >> (j + 1)) & 1u) return L;
-        return st[skew(o + __popc(kept & ((1u << j) - 1u)))];
+        return (uint32_t)st[skew(o + __popc(kept & ((1u << j) - 1u)))];
     };
     auto in_class = [&](uint32_t v) -> bool { return v == X || (v < X && ((cm[v >> 5] >> (v & 31u)) & 1u)); };
     const uint32_t sm1 = (sel << 1) | sel_in;  // bit j: sel of position j - 1
@@ -315,8 +317,14 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
         }
         // one id of the pair is L, R or X: the pair lies in one word iff
         // the other id has the merge's class too
-        if (in_class(a) && in_class(b) && !tab.insert(pair_key(a, b), delta))
+        if (in_class(a) && in_class(b) && !tab.insert(pair_key(a, b), delta)) {
             gt_add_sel(gt, pair_key(a, b), delta, ctl, sw, theta);  // the LDS table is full
+            // (rare) drain this path's memory operations here: otherwise
+            // the compiler assumes they may still be pending where the
+            // paths join, and waits for every access, the next tile's
+            // loads included, before the look-back
+            __builtin_amdgcn_s_waitcnt(0);
+        }
     }
 }
 
@@ -331,63 +339,81 @@ constexpr int BUF_NT = 2;
 // equals it and it belongs to no class.
 constexpr uint32_t NOSYM = 0x10000u;
 
-// Issue the loads of a thread's V = 16 symbols at g0 = tile * TILE + tid * 16
-// (two 16-byte loads) and, on the wave's edge lanes, of the neighbours the
-// shuffles cannot supply: hw = sym[g0 - 2] | sym[g0 - 1] << 16 on lane 0,
-// hr (low half: sym[g0 + 16]) on lane 63. Buffer loads through a resource
-// covering the tile, the two symbols before it and the one after it
-// (within n, in whole 4-byte words: the padded array holds the 16-bit word
-// past n): every lane issues the same four loads, a lane with nothing to
-// load uses an offset past the resource (the hardware returns 0 without a
-// memory access), and a tile past the end gets an empty resource. With no
-// branch and a fixed count, the compiler can wait for these loads alone,
-// later. The words stay packed until fix_tile, so that nothing reads them
-// in the round that issues them. Values outside [0, n) are undefined here;
-// fix_tile replaces them by NOSYM.
+// A tile is two halves of TPB * 16 symbols; a thread holds 16 consecutive
+// symbols of each, at g0 = tile * TILE + tid * 16 and g0 + TILE / 2. Issue
+// the loads of both (two 16-byte loads each) and, on the wave's edge lanes,
+// of the neighbours the shuffles cannot supply: hw = sym[g0 - 2] |
+// sym[g0 - 1] << 16 on lane 0, hr (low half: sym[g0 + 16]) on lane 63.
+// Buffer loads through a resource covering the tile, the two symbols before
+// it and the one after it (within n, in whole 4-byte words: the padded
+// array holds the 16-bit word past n): every lane issues the same eight
+// loads, a lane with nothing to load uses an offset past the resource (the
+// hardware returns 0 without a memory access), and a tile past the end gets
+// an empty resource. With no branch and a fixed count, the compiler can
+// wait for these loads alone, later. The words stay packed until fix_tile,
+// so that nothing reads them in the round that issues them. Values outside
+// [0, n) are undefined here; fix_tile replaces them by NOSYM.
+struct TileRegs {
+    uint32_t xr[2][8];  // per half: 16 ids, two per word
+    uint32_t hw[2], hr[2];
+};
 template <int TILE>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ in, uint32_t n, uint32_t tile,
-                                          uint32_t ntiles, uint32_t tid, uint32_t lane, uint32_t (&xr)[8],
-                                          uint32_t& hw, uint32_t& hr) {
+                                          uint32_t ntiles, uint32_t tid, uint32_t lane, TileRegs& r) {
     tile = __builtin_amdgcn_readfirstlane(tile);  // uniform: the resource lives in SGPRs
     const uint32_t ts = tile * TILE, hb = ts >= 2u ? ts - 2u : 0u;  // even: 4-byte aligned
     const uint32_t end = tile < ntiles ? min(n, ts + TILE + 1u) : hb;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(in) + hb, 0, (int)((2u * (end - hb) + 2u) & ~3u), BUF_RSRC_FLAGS);
-    const uint32_t g0 = ts + tid * 16u, o = 2u * (g0 - hb);
     // the edge values first: the compiler can then wait for them without
     // waiting for the 16-byte loads (one in-order counter)
-    hw = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 4u : BUF_OOB, 0, 0);
-    hr = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 32u : BUF_OOB, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
-        xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t g0 = ts + (uint32_t)h * (TILE / 2) + tid * 16u, o = 2u * (g0 - hb);
+        r.hw[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 4u : BUF_OOB, 0, 0);
+        r.hr[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 32u : BUF_OOB, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t o = 2u * (ts + (uint32_t)h * (TILE / 2) + tid * 16u - hb);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
+            r.xr[h][4 * q] = v.x; r.xr[h][4 * q + 1] = v.y; r.xr[h][4 * q + 2] = v.z; r.xr[h][4 * q + 3] = v.w;
+        }
     }
 }
 
-// After load_tile: the 16 ids, NOSYM in place of every value outside
-// [0, n), then the neighbours a1 = sym[g0 - 1], a2 = sym[g0 - 2],
-// b1 = sym[g0 + 16] (NOSYM outside [0, n)).
-__device__ __forceinline__ void fix_tile(uint32_t (&x)[16], const uint32_t (&xr)[8], uint32_t hw, uint32_t hr,
-                                         uint32_t g0, uint32_t n, uint32_t lane, bool full, uint32_t& a1,
-                                         uint32_t& a2, uint32_t& b1) {
+// The 16 ids of one half, unpacked.
+__device__ __forceinline__ void unpack(uint32_t (&x)[16], const uint32_t (&xr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         x[2 * j] = xr[j] & 0xFFFFu;
         x[2 * j + 1] = xr[j] >> 16;
     }
+}
+
+// After load_tile, for one half: its 16 ids, NOSYM in place of every
+// value outside [0, n), then the neighbours a1 = sym[g0 - 1],
+// a2 = sym[g0 - 2], b1 = sym[g0 + 16] (NOSYM outside [0, n)).
+__device__ __forceinline__ void fix_tile(uint32_t (&x)[16], const uint32_t (&xr)[8], uint32_t hw, uint32_t hr,
+                                         uint32_t g0, uint32_t n, uint32_t lane, bool full, uint32_t& a1,
+                                         uint32_t& a2, uint32_t& b1) {
+    unpack(x, xr);
     if (!full) {  // uniform: the last tile
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? x[j] : NOSYM;
     }
-    a1 = dpp<DPP_WAVE_SHR1>(NOSYM, x[15]);  // from lane - 1
-    a2 = dpp<DPP_WAVE_SHR1>(NOSYM, x[14]);
-    b1 = dpp<DPP_WAVE_SHL1>(NOSYM, x[0]);  // from lane + 1
-    if (lane == 0) {
-        a1 = (g0 >= 1u && g0 - 1u < n) ? hw >> 16 : NOSYM;
-        a2 = (g0 >= 2u && g0 - 2u < n) ? hw & 0xFFFFu : NOSYM;
-    }
-    if (lane == 63) b1 = (g0 + 16u < n) ? hr & 0xFFFFu : NOSYM;
+    // selects, not conditional stores: the outputs stay in registers
+    const uint32_t d1 = dpp<DPP_WAVE_SHR1>(NOSYM, x[15]);  // from lane - 1
+    const uint32_t d2 = dpp<DPP_WAVE_SHR1>(NOSYM, x[14]);
+    const uint32_t d3 = dpp<DPP_WAVE_SHL1>(NOSYM, x[0]);  // from lane + 1
+    const uint32_t e1 = (g0 >= 1u && g0 - 1u < n) ? hw >> 16 : NOSYM;
+    const uint32_t e2 = (g0 >= 2u && g0 - 2u < n) ? hw & 0xFFFFu : NOSYM;
+    const uint32_t e3 = (g0 + 16u < n) ? hr & 0xFFFFu : NOSYM;
+    a1 = lane == 0 ? e1 : d1;
+    a2 = lane == 0 ? e2 : d2;
+    b1 = lane == 63 ? e3 : d3;
 }
 
 // Occurrence bits of a thread (bit j: position g0 + j, bit V: position
@@ -410,7 +436,7 @@ __device__ __forceinline__ void occurrences(const uint32_t (&x)[V], uint32_t a1,
     valid = (g0 >= n) ? 0u : (n - g0 >= (uint32_t)V ? (1u << V) - 1u : (1u << (n - g0)) - 1u);
 }
 
-// Write the kept symbols of a tile from LDS (st, 32-bit slots) to
+// Write the kept symbols of a tile from LDS (st, 16-bit slots) to
 // out[tile_off .. tile_off + tile_kept) as 16-bit ids: up to 7 single
 // symbols to reach 16-byte alignment, whole groups of 8 (one 16-byte store
 // each), up to 7 single symbols at the end. Each thread issues the same
@@ -420,7 +446,7 @@ __device__ __forceinline__ void occurrences(const uint32_t (&x)[V], uint32_t a1,
 // can wait for loads issued before these stores without waiting for the
 // stores themselves. out is 16-byte aligned.
 template <int TPB, int TILE>
-__device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uint32_t* st, uint32_t tile_off,
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uint16_t* st, uint32_t tile_off,
                                            uint32_t tile_kept) {
     const uint32_t tid = threadIdx.x;
     tile_off = __builtin_amdgcn_readfirstlane(tile_off);  // uniform: the resource lives in SGPRs
@@ -433,14 +459,14 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uin
     {
         const bool on = tid < head;
         const uint32_t i = on ? tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
     // Group q of the thread holds symbols b + 8 * TPB * q .. + 7 with
-    // b = head + 8 * tid. A step of 8 * TPB symbols (a multiple of 32) moves
-    // every skewed index by the same amount. A group past the body still
-    // reads inside the (padded) staging buffer; its store is dropped.
+    // b = head + 8 * tid. A step of 8 * TPB symbols (a multiple of 128)
+    // moves every skewed index by the same amount. A group past the body
+    // still reads inside the (padded) staging buffer; its store is dropped.
     constexpr uint32_t QSTEP = skew(8 * TPB);
-    static_assert((8 * TPB) % 32 == 0, "groups keep their offset within 32 symbols");
+    static_assert((8 * TPB) % 128 == 0, "groups keep their offset within 128 symbols");
     const uint32_t b = head + 8u * tid;
     uint32_t a[8];
 #pragma unroll
@@ -450,37 +476,37 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uin
         const bool on = tid + q * TPB < body;
         uint32_t u[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) u[k] = st[a[k] + q * QSTEP];
+        for (int k = 0; k < 8; ++k) u[k] = (uint32_t)st[a[k] + q * QSTEP];
         const v4u32 v = {u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16)};
         __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 2u * (b + 8u * TPB * q) : BUF_OOB, 0, BUF_NT);
     }
     {
         const bool on = tid < tile_kept - rest;
         const uint32_t i = on ? rest + tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
 }
 
 // Stage the kept symbols of a thread at tile-local offset o; a symbol whose
 // right neighbour merges into it becomes X.
 template <int V>
-__device__ __forceinline__ void stage(uint32_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
+__device__ __forceinline__ void stage(uint16_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
                                       uint32_t sel, uint32_t X) {
     constexpr uint32_t VM = (1u << V) - 1u;
     if (valid == VM && (sel & ((VM << 1) | 1u)) == 0u) {
         // nothing dropped or replaced (most threads): symbol j goes to
-        // skew(o + j) = o + (o >> 5) + j, one further once o + j reaches
-        // the next multiple of 32 (at most once in V < 32 symbols)
-        uint32_t* p0 = st + skew(o);
-        uint32_t* p1 = p0 + 1;
-        const uint32_t r = o & 31u;
+        // skew(o + j) = skew(o) + j, two further once o + j reaches the
+        // next multiple of 128 (at most once in V < 128 symbols)
+        uint16_t* p0 = st + skew(o);
+        uint16_t* p2 = p0 + 2;
+        const uint32_t r = o & 127u;
 #pragma unroll
-        for (int j = 0; j < V; ++j) (r + j >= 32u ? p1 : p0)[j] = x[j];
+        for (int j = 0; j < V; ++j) (r + j >= 128u ? p2 : p0)[j] = (uint16_t)x[j];
     } else {
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
-                st[skew(o)] = ((sel >> (j + 1)) & 1u) ? X : x[j];
+                st[skew(o)] = (uint16_t)(((sel >> (j + 1)) & 1u) ? X : x[j]);
                 ++o;
             }
         }
@@ -502,8 +528,8 @@ __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, ui
 // global_load_lds.
 constexpr int LB_PL = 4;
 constexpr int LB_WIN = 2 * 64 * LB_PL;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= 4, expcnt and lgkmcnt untouched
-constexpr int WAIT_VM4 = 0x0F74;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 8, expcnt and lgkmcnt untouched
+constexpr int WAIT_VM8 = 0x0F78;
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 
 // One persistent pass per iteration. Workgroups take tiles from a counter,
@@ -564,9 +590,11 @@ __device__ __forceinline__ void lds_copy16(const unsigned long long* src, const 
 // Values loaded by load_tile that a round does not consume: an empty use,
 // so that the compiler waits for their loads in that round and not when
 // the registers are next loaded.
-__device__ __forceinline__ void retire(const uint32_t (&xr)[8], uint32_t hw, uint32_t hr) {
-    asm volatile("" ::"v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]),
-                 "v"(xr[7]), "v"(hw), "v"(hr));
+__device__ __forceinline__ void retire(const TileRegs& r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        asm volatile("" ::"v"(r.xr[h][0]), "v"(r.xr[h][1]), "v"(r.xr[h][2]), "v"(r.xr[h][3]), "v"(r.xr[h][4]),
+                     "v"(r.xr[h][5]), "v"(r.xr[h][6]), "v"(r.xr[h][7]), "v"(r.hw[h]), "v"(r.hr[h]));
 }
 
 // ---------------------------------------------------------------- selection
@@ -798,6 +826,9 @@ __device__ __forceinline__ void finish_counts(LdsTable<LT>& tab, const GTable& g
     if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
 }
 
+// Symbols per thread of a merge pass's tile (two halves of 16).
+constexpr int MERGE_SYMS_PER_THREAD = 32;
+
 // Dynamic LDS of the pass of iteration it: the class mask of ids up to
 // X = 256 + it.
 __host__ __device__ constexpr uint32_t cmask_lds_bytes(uint32_t it) { return 4u * (((BASE + it) >> 5) + 1u); }
@@ -813,18 +844,20 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                                                unsigned long long* status,
                                                uint32_t* lengths, Sweep* sw, uint32_t* merges,
                                                uint8_t* __restrict__ cls, uint32_t* __restrict__ cmask) {
-    constexpr int V = 16;  // symbols per thread: two 16-byte loads
-    constexpr int TILE = TPB * V;
+    constexpr int V = 16;  // symbols per thread and half: two 16-byte loads
+    constexpr int HALF = TPB * V;
+    constexpr int TILE = 2 * HALF;
+    static_assert(TILE == TPB * MERGE_SYMS_PER_THREAD, "the host sizes grids by this tile");
     constexpr int NW = TPB / 64;
     constexpr uint32_t VM = (1u << V) - 1u;
-    constexpr uint32_t SST = TILE + TILE / 32;  // one staging buffer (skewed)
+    constexpr uint32_t SST = TILE + TILE / 64;  // one staging buffer (skewed)
     __shared__ LdsTable<LT> tab;  // count changes of this workgroup
-    __shared__ uint32_t s_stage[2 * SST + 8];  // + 8: reads of dropped store groups stay inside
+    __shared__ uint16_t s_stage[2 * SST + 8];  // + 8: reads of dropped store groups stay inside
     // ids up to X in the merge's class: (X >> 5) + 1 words of dynamic LDS
     // (cmask_lds_bytes), so that early passes of small corpora keep two
     // workgroups per CU
     extern __shared__ uint32_t s_cmask[];
-    __shared__ uint32_t s_wagg[NW];
+    __shared__ uint32_t s_wagg[NW], s_waggb[NW];
     __shared__ uint32_t s_tile[2], s_off[2], s_sel, s_dep, s_off_now, s_u32;
     __shared__ unsigned long long s_best[NW];
     __shared__ __align__(16) unsigned long long s_win[LB_WIN];
@@ -870,9 +903,9 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
         lds_barrier();
     }
     uint32_t t = s_tile[0] - tile_base;
-    uint32_t x[V], xr[V / 2], hw, hr;
-    static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread");
-    load_tile<TILE>(in, n, t, ntiles, tid, lane, xr, hw, hr);
+    TileRegs tr;
+    static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread and half");
+    load_tile<TILE>(in, n, t, ntiles, tid, lane, tr);
     unsigned long long best = read_publication(sw, ctl, p, it, s_best);
     if (best == SEL_SWEEP) best = sweep_select<TPB>(gt, sw, ctl, p, it, s_best, &s_u32, lane, w, theta);  // uniform
     if (best == 0ull) {  // uniform: no countable pair is left
@@ -922,7 +955,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0;
-            CountArgs cc{};
+            CountArgs cca{}, ccb{};
             // the previous tile's first look-back window (the 512 status
             // words below it), copied straight into LDS before anything else
             // of the round, so that it has arrived by the time wave 0
@@ -935,51 +968,67 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     lds_copy16(status + lb_base + 2 * (lane + 64 * q), s_win + 128 * q);
             }
             if (t < ntiles) {  // uniform
-                const uint32_t g0 = t * TILE + tid * V;
-                uint32_t a1, a2, b1;
-                fix_tile(x, xr, hw, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
-                uint32_t occ, valid;
-                occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
+                const uint32_t g0 = t * TILE + tid * V;  // half A; half B at g0 + HALF
+                const bool full = t * TILE + TILE <= n;
+                uint32_t x[V], a1, a2, b1, occa, valida, occb, validb;
+                fix_tile(x, tr.xr[0], tr.hw[0], tr.hr[0], g0, n, lane, full, a1, a2, b1);
+                occurrences<V>(x, a1, b1, g0, n, L, R, occa, valida);
                 // sel = occ; the position before g0 is merged iff it is an occurrence
-                const uint32_t sel_in = (a2 == L && a1 == R) ? 1u : 0u;  // NOSYM before the start
+                const uint32_t sel_ina = (a2 == L && a1 == R) ? 1u : 0u;  // NOSYM before the start
+                const uint32_t lefta = a1;
+                fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
+                occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
+                const uint32_t sel_inb = (a2 == L && a1 == R) ? 1u : 0u;
 
-                // ---- kept counts: wave scan, then across the waves
-                const uint32_t kept = __popc(valid & ~occ & VM);
+                // ---- kept counts of both halves in one word (at most HALF
+                // each): wave scan, then across the waves
+                const uint32_t kept = __popc(valida & ~occa & VM) | (__popc(validb & ~occb & VM) << 16);
                 const uint32_t incl = wave_scan(kept, 0u, [](uint32_t a, uint32_t b) { return a + b; });
                 if (lane == 63) s_wagg[w] = incl;
                 if (tid == 0) s_tile[round & 1u] = grab - tile_base;
                 lds_barrier();
-                uint32_t before;
-                waves_prefix<NW>(s_wagg, w, lane, 0u, [](uint32_t a, uint32_t b) { return a + b; }, before,
-                                 tile_kept);
-                const uint32_t my_local = incl - kept + before;
+                uint32_t before, all;
+                waves_prefix<NW>(s_wagg, w, lane, 0u, [](uint32_t a, uint32_t b) { return a + b; }, before, all);
+                const uint32_t kept_a = all & 0xFFFFu;
+                tile_kept = kept_a + (all >> 16);
+                const uint32_t ex = incl - kept + before;
                 // the tile's aggregate goes out before anything else is done
                 if (tid == 0 && t != 0)
                     st_store(status + t, st_pack(ST_AGG, epoch, tup_make(tile_kept, 0u, 0u, 0u)));
 
-                uint32_t* st = s_stage + cur * SST;
-                stage<V>(st, my_local, x, valid, occ, X);
-                if (do_count && (occ | sel_in)) {
-                    const Changes<V> ch(occ, sel_in, valid);
-                    cc = CountArgs{ch.gone, ch.born, occ, sel_in, a1, st, my_local, valid & ~occ};
+                uint16_t* st = s_stage + cur * SST;
+                // half B first (its ids are unpacked), then half A again from its words
+                stage<V>(st, kept_a + (ex >> 16), x, validb, occb, X);
+                if (do_count && (occb | sel_inb)) {
+                    const Changes<V> ch(occb, sel_inb, validb);
+                    ccb = CountArgs{ch.gone, ch.born, occb, sel_inb, a1, st, kept_a + (ex >> 16), validb & ~occb};
+                }
+                unpack(x, tr.xr[0]);
+                stage<V>(st, ex & 0xFFFFu, x, valida, occa, X);
+                if (do_count && (occa | sel_ina)) {
+                    const Changes<V> ch(occa, sel_ina, valida);
+                    cca = CountArgs{ch.gone, ch.born, occa, sel_ina, lefta, st, ex & 0xFFFFu, valida & ~occa};
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(xr, hw, hr);
+                retire(tr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, xr, hw, hr);
-            if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
-                                  L, R, X, s_cmask);
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, tr);
+            if (cca.gone | cca.born)
+                count_changes<LT>(tab, gt, ctl, sw, theta, cca.gone, cca.born, cca.sel, cca.sel_in, cca.left, cca.st,
+                                  cca.o, cca.kept, L, R, X, s_cmask);
+            if (ccb.gone | ccb.born)
+                count_changes<LT>(tab, gt, ctl, sw, theta, ccb.gone, ccb.born, ccb.sel, ccb.sel_in, ccb.left, ccb.st,
+                                  ccb.o, ccb.kept, L, R, X, s_cmask);
             // ---- the previous tile: its predecessors have had a round to publish
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
                 if (tp != 0) {
-                    // the window's copies are older than the four loads of
-                    // load_tile above: all but the last four accesses done
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
+                    // the window's copies are older than the eight loads of
+                    // load_tile above: all but the last eight accesses done
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll
@@ -1035,7 +1084,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
         store_tile<TPB, TILE>(out, s_stage, 0u, 0u);
         for (uint32_t round = 1; t < ntiles || tp < ntiles; ++round) {
             uint32_t tn = ntiles, tile_kept = 0, tile_agg = TUP_ID, off_t = 0;
-            CountArgs cc{};
+            CountArgs cca{}, ccb{};
             bool dep = false;
             const int lb_top = (int)tp - 1;
             const int lb_base = lb_top >= LB_WIN - 1 ? lb_top - (LB_WIN - 1) : 0;
@@ -1046,15 +1095,19 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     lds_copy16(status + lb_base + 2 * (lane + 64 * q), s_win + 128 * q);
             }
             if (t < ntiles) {  // uniform
-                const uint32_t g0 = t * TILE + tid * V;
-                uint32_t a1, a2, b1;
-                fix_tile(x, xr, hw, hr, g0, n, lane, t * TILE + TILE <= n, a1, a2, b1);
-                uint32_t occ, valid;
-                occurrences<V>(x, a1, b1, g0, n, L, R, occ, valid);
+                const uint32_t g0 = t * TILE + tid * V;  // half A; half B at g0 + HALF
+                const bool full = t * TILE + TILE <= n;
+                uint32_t x[V], a1, a2, b1, occa, valida, occb, validb;
+                fix_tile(x, tr.xr[0], tr.hw[0], tr.hr[0], g0, n, lane, full, a1, a2, b1);
+                occurrences<V>(x, a1, b1, g0, n, L, R, occa, valida);
+                const uint32_t lefta = a1;
+                const uint32_t dep0 = (occa & 1u) | (uint32_t)(a2 == L && a1 == L);  // used by thread 0
+                fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
+                occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
 
-                // ---- this thread's tuple, then inclusive scans over the wave and the waves
-                uint32_t tup;
-                {
+                // ---- each half's tuple per thread, then inclusive scans over
+                // the wave and the waves, half by half
+                auto thread_tuple = [](uint32_t occ, uint32_t valid) -> uint32_t {
                     uint32_t s0 = 0, s1 = 1, c0 = 0, c1 = 0;
 #pragma unroll
                     for (int j = 0; j < V; ++j) {
@@ -1064,19 +1117,26 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                         c0 += v & ~s0 & 1u;
                         c1 += v & ~s1 & 1u;
                     }
-                    tup = tup_make(c0, c1 - c0, s0, s1);
+                    return tup_make(c0, c1 - c0, s0, s1);
+                };
+                auto then = [](uint32_t a, uint32_t b) { return tup_then(a, b); };
+                const uint32_t incla = wave_scan(thread_tuple(occa, valida), TUP_ID, then);
+                const uint32_t inclb = wave_scan(thread_tuple(occb, validb), TUP_ID, then);
+                const uint32_t lane_excla = dpp<DPP_WAVE_SHR1>(TUP_ID, incla);
+                const uint32_t lane_exclb = dpp<DPP_WAVE_SHR1>(TUP_ID, inclb);
+                if (lane == 63) {
+                    s_wagg[w] = incla;
+                    s_waggb[w] = inclb;
                 }
-                const uint32_t incl = wave_scan(tup, TUP_ID, [](uint32_t a, uint32_t b) { return tup_then(a, b); });
-                const uint32_t lane_excl = dpp<DPP_WAVE_SHR1>(TUP_ID, incl);
-                if (lane == 63) s_wagg[w] = incl;
                 if (tid == 0) {
                     s_tile[round & 1u] = grab - tile_base;
-                    s_dep = (occ & 1u) | (uint32_t)(a2 == L && a1 == L);
+                    s_dep = dep0;
                 }
                 lds_barrier();
-                uint32_t wave_excl;
-                waves_prefix<NW>(s_wagg, w, lane, TUP_ID, [](uint32_t a, uint32_t b) { return tup_then(a, b); },
-                                 wave_excl, tile_agg);
+                uint32_t wave_excla, agg_a, wave_exclb, agg_b;
+                waves_prefix<NW>(s_wagg, w, lane, TUP_ID, then, wave_excla, agg_a);
+                waves_prefix<NW>(s_waggb, w, lane, TUP_ID, then, wave_exclb, agg_b);
+                tile_agg = tup_then(agg_a, agg_b);
                 dep = s_dep != 0u;  // uniform
                 // the tile's aggregate (tile 0: prefix) goes out before anything else is done
                 if (tid == 0)
@@ -1101,42 +1161,63 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     tile_sel = s_sel;
                     off_t = s_off_now;
                 }
-                const uint32_t texcl = tup_then(wave_excl, lane_excl);
-                const uint32_t my_local = tup_c0(texcl) + (tile_sel ? tup_d(texcl) : 0u);
-                const uint32_t sel_in = tup_o(texcl, tile_sel);
+                const uint32_t texcla = tup_then(wave_excla, lane_excla);
+                const uint32_t texclb = tup_then(agg_a, tup_then(wave_exclb, lane_exclb));
                 tile_kept = tup_c0(tile_agg) + (tile_sel ? tup_d(tile_agg) : 0u);
 
-                // ---- resolve sel, stage, count changes
-                uint32_t selbits = 0;
-                {
-                    uint32_t sv = sel_in;
+                // ---- resolve sel, stage, count changes (each half's ids
+                // unpacked again from its words: fewer registers held over
+                // the scans and the look-back)
+                auto resolve = [](uint32_t occ, uint32_t sel_in) -> uint32_t {
+                    uint32_t selbits = 0, sv = sel_in;
 #pragma unroll
                     for (int j = 0; j <= V; ++j) {
                         sv = (occ >> j) & ~sv & 1u;
                         selbits |= sv << j;
                     }
+                    return selbits;
+                };
+                uint16_t* st = s_stage + cur * SST;
+                unpack(x, tr.xr[1]);
+                {
+                    const uint32_t loc = tup_c0(texclb) + (tile_sel ? tup_d(texclb) : 0u);
+                    const uint32_t sel_in = tup_o(texclb, tile_sel);
+                    const uint32_t selbits = resolve(occb, sel_in);
+                    stage<V>(st, loc, x, validb, selbits, X);
+                    if (do_count && (occb | sel_in)) {
+                        const Changes<V> ch(selbits, sel_in, validb);
+                        ccb = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, loc, validb & ~selbits};
+                    }
                 }
-                uint32_t* st = s_stage + cur * SST;
-                stage<V>(st, my_local, x, valid, selbits, X);
-                if (do_count && (occ | sel_in)) {
-                    const Changes<V> ch(selbits, sel_in, valid);
-                    cc = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, my_local, valid & ~selbits};
+                unpack(x, tr.xr[0]);
+                {
+                    const uint32_t loc = tup_c0(texcla) + (tile_sel ? tup_d(texcla) : 0u);
+                    const uint32_t sel_in = tup_o(texcla, tile_sel);
+                    const uint32_t selbits = resolve(occa, sel_in);
+                    stage<V>(st, loc, x, valida, selbits, X);
+                    if (do_count && (occa | sel_in)) {
+                        const Changes<V> ch(selbits, sel_in, valida);
+                        cca = CountArgs{ch.gone, ch.born, selbits, sel_in, lefta, st, loc, valida & ~selbits};
+                    }
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(xr, hw, hr);
+                retire(tr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, xr, hw, hr);
-            if (cc.gone | cc.born)
-                count_changes<LT>(tab, gt, ctl, sw, theta, cc.gone, cc.born, cc.sel, cc.sel_in, cc.left, cc.st, cc.o, cc.kept,
-                                  L, R, X, s_cmask);
+            load_tile<TILE>(in, n, tn, ntiles, tid, lane, tr);
+            if (cca.gone | cca.born)
+                count_changes<LT>(tab, gt, ctl, sw, theta, cca.gone, cca.born, cca.sel, cca.sel_in, cca.left, cca.st,
+                                  cca.o, cca.kept, L, R, X, s_cmask);
+            if (ccb.gone | ccb.born)
+                count_changes<LT>(tab, gt, ctl, sw, theta, ccb.gone, ccb.born, ccb.sel, ccb.sel_in, ccb.left, ccb.st,
+                                  ccb.o, ccb.kept, L, R, X, s_cmask);
             // ---- the previous tile: its offset (unless its look-back is done)
             if (tp < ntiles && w == 0) {
                 uint32_t off = off_p, sel = 0;
                 if (!done_p) {  // tp != 0
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM4);
+                    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll
