@@ -246,6 +246,11 @@ __device__ __forceinline__ void lookback(const unsigned long long* status, uint3
 // further every 128 symbols, so that the runs of consecutive threads, and
 // the store groups, start on different banks
 __host__ __device__ constexpr uint32_t skew(uint32_t i) { return i + 2u * (i >> 7); }
+// The staging buffer is written and read both in 16-bit slots and in 4-byte
+// words (pairs of slots from an even index: the skew keeps them whole);
+// these types tell the compiler that the two views alias.
+typedef uint16_t __attribute__((may_alias)) lds16_t;
+typedef uint32_t __attribute__((may_alias)) lds32_t;
 
 
 
@@ -295,7 +300,7 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
     auto old_id = [&](uint32_t j) -> uint32_t {
         if ((sel >> j) & 1u) return R;
         if ((sel >> (j + 1)) & 1u) return L;
-        return (uint32_t)st[skew(o + __popc(kept & ((1u << j) - 1u)))];
+        return (uint32_t)reinterpret_cast<const lds16_t*>(st)[skew(o + __popc(kept & ((1u << j) - 1u)))];
     };
     auto in_class = [&](uint32_t v) -> bool { return v == X || (v < X && ((cm[v >> 5] >> (v & 31u)) & 1u)); };
     const uint32_t sm1 = (sel << 1) | sel_in;  // bit j: sel of position j - 1
@@ -456,57 +461,79 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const uin
     const uint32_t head = min(tile_kept, (8u - (tile_off & 7u)) & 7u);
     const uint32_t body = (tile_kept - head) >> 3;
     const uint32_t rest = head + 8 * body;
+    const lds16_t* s16 = reinterpret_cast<const lds16_t*>(st);
+    const lds32_t* s32 = reinterpret_cast<const lds32_t*>(st);
     {
         const bool on = tid < head;
         const uint32_t i = on ? tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16(st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(s16[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
     // Group q of the thread holds symbols b + 8 * TPB * q .. + 7 with
-    // b = head + 8 * tid. A step of 8 * TPB symbols (a multiple of 128)
-    // moves every skewed index by the same amount. A group past the body
-    // still reads inside the (padded) staging buffer; its store is dropped.
-    constexpr uint32_t QSTEP = skew(8 * TPB);
+    // b = head + 8 * tid, read as the five 4-byte words of slots b0 .. b0 + 9
+    // (b0 = b rounded down to even; the skew moves by whole words); when b
+    // is odd (head odd: uniform) the pairs are shifted by one slot with a
+    // funnel shift. A step of 8 * TPB symbols (a multiple of 128) moves
+    // every skewed index by the same amount. A group past the body still
+    // reads inside the (padded) staging buffer; its store is dropped.
+    constexpr uint32_t QSTEP = skew(8 * TPB) / 2;  // in words
     static_assert((8 * TPB) % 128 == 0, "groups keep their offset within 128 symbols");
     const uint32_t b = head + 8u * tid;
-    uint32_t a[8];
+    const uint32_t b0 = b & ~1u;
+    const bool odd = (head & 1u) != 0u;
+    uint32_t a[5];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = skew(b + (uint32_t)k);
+    for (int k = 0; k < 5; ++k) a[k] = skew(b0 + 2u * (uint32_t)k) >> 1;
 #pragma unroll
     for (int q = 0; q < TILE / 8 / TPB; ++q) {
         const bool on = tid + q * TPB < body;
-        uint32_t u[8];
+        uint32_t u[5];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) u[k] = (uint32_t)st[a[k] + q * QSTEP];
-        const v4u32 v = {u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16)};
+        for (int k = 0; k < 5; ++k) u[k] = s32[a[k] + q * QSTEP];
+        v4u32 v;
+        if (odd) {
+            v = v4u32{__builtin_amdgcn_alignbit(u[1], u[0], 16), __builtin_amdgcn_alignbit(u[2], u[1], 16),
+                      __builtin_amdgcn_alignbit(u[3], u[2], 16), __builtin_amdgcn_alignbit(u[4], u[3], 16)};
+        } else {
+            v = v4u32{u[0], u[1], u[2], u[3]};
+        }
         __builtin_amdgcn_raw_buffer_store_b128(v, rs, on ? 2u * (b + 8u * TPB * q) : BUF_OOB, 0, BUF_NT);
     }
     {
         const bool on = tid < tile_kept - rest;
         const uint32_t i = on ? rest + tid : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16(st[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(s16[skew(i)], rs, on ? 2u * i : BUF_OOB, 0, 0);
     }
 }
 
 // Stage the kept symbols of a thread at tile-local offset o; a symbol whose
 // right neighbour merges into it becomes X.
+// xr: the thread's 16 symbols as loaded (two per word); x: the same
+// unpacked (read only when something changes).
 template <int V>
-__device__ __forceinline__ void stage(uint16_t* st, uint32_t o, const uint32_t (&x)[V], uint32_t valid,
-                                      uint32_t sel, uint32_t X) {
+__device__ __forceinline__ void stage(uint16_t* st, uint32_t o, const uint32_t (&xr)[V / 2], const uint32_t (&x)[V],
+                                      uint32_t valid, uint32_t sel, uint32_t X) {
     constexpr uint32_t VM = (1u << V) - 1u;
+    lds16_t* s16 = reinterpret_cast<lds16_t*>(st);
     if (valid == VM && (sel & ((VM << 1) | 1u)) == 0u) {
-        // nothing dropped or replaced (most threads): symbol j goes to
-        // skew(o + j) = skew(o) + j, two further once o + j reaches the
-        // next multiple of 128 (at most once in V < 128 symbols)
-        uint16_t* p0 = st + skew(o);
-        uint16_t* p2 = p0 + 2;
-        const uint32_t r = o & 127u;
+        // nothing dropped or replaced (most threads): the loaded words go
+        // to LDS as they are, from the first even slot at or after o
+        // (o + 1 when o is odd: then the pairs are shifted by one symbol);
+        // the first symbol and the last two go alone, so that the same ten
+        // stores serve both cases
+        lds32_t* s32 = reinterpret_cast<lds32_t*>(st);
+        const bool odd = (o & 1u) != 0u;
+        const uint32_t e = o + (odd ? 1u : 0u);
+        s16[skew(o)] = (uint16_t)(xr[0] & 0xFFFFu);
 #pragma unroll
-        for (int j = 0; j < V; ++j) (r + j >= 128u ? p2 : p0)[j] = (uint16_t)x[j];
+        for (int k = 0; k < V / 2 - 1; ++k)
+            s32[skew(e + 2u * (uint32_t)k) >> 1] = odd ? __builtin_amdgcn_alignbit(xr[k + 1], xr[k], 16) : xr[k];
+        s16[skew(o + V - 2)] = (uint16_t)(xr[V / 2 - 1] & 0xFFFFu);
+        s16[skew(o + V - 1)] = (uint16_t)(xr[V / 2 - 1] >> 16);
     } else {
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             if (((valid >> j) & 1u) && !((sel >> j) & 1u)) {
-                st[skew(o)] = (uint16_t)(((sel >> (j + 1)) & 1u) ? X : x[j]);
+                s16[skew(o)] = (uint16_t)(((sel >> (j + 1)) & 1u) ? X : x[j]);
                 ++o;
             }
         }
@@ -998,13 +1025,13 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
 
                 uint16_t* st = s_stage + cur * SST;
                 // half B first (its ids are unpacked), then half A again from its words
-                stage<V>(st, kept_a + (ex >> 16), x, validb, occb, X);
+                stage<V>(st, kept_a + (ex >> 16), tr.xr[1], x, validb, occb, X);
                 if (do_count && (occb | sel_inb)) {
                     const Changes<V> ch(occb, sel_inb, validb);
                     ccb = CountArgs{ch.gone, ch.born, occb, sel_inb, a1, st, kept_a + (ex >> 16), validb & ~occb};
                 }
                 unpack(x, tr.xr[0]);
-                stage<V>(st, ex & 0xFFFFu, x, valida, occa, X);
+                stage<V>(st, ex & 0xFFFFu, tr.xr[0], x, valida, occa, X);
                 if (do_count && (occa | sel_ina)) {
                     const Changes<V> ch(occa, sel_ina, valida);
                     cca = CountArgs{ch.gone, ch.born, occa, sel_ina, lefta, st, ex & 0xFFFFu, valida & ~occa};
@@ -1183,7 +1210,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     const uint32_t loc = tup_c0(texclb) + (tile_sel ? tup_d(texclb) : 0u);
                     const uint32_t sel_in = tup_o(texclb, tile_sel);
                     const uint32_t selbits = resolve(occb, sel_in);
-                    stage<V>(st, loc, x, validb, selbits, X);
+                    stage<V>(st, loc, tr.xr[1], x, validb, selbits, X);
                     if (do_count && (occb | sel_in)) {
                         const Changes<V> ch(selbits, sel_in, validb);
                         ccb = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, loc, validb & ~selbits};
@@ -1194,7 +1221,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     const uint32_t loc = tup_c0(texcla) + (tile_sel ? tup_d(texcla) : 0u);
                     const uint32_t sel_in = tup_o(texcla, tile_sel);
                     const uint32_t selbits = resolve(occa, sel_in);
-                    stage<V>(st, loc, x, valida, selbits, X);
+                    stage<V>(st, loc, tr.xr[0], x, valida, selbits, X);
                     if (do_count && (occa | sel_in)) {
                         const Changes<V> ch(selbits, sel_in, valida);
                         cca = CountArgs{ch.gone, ch.born, selbits, sel_in, lefta, st, loc, valida & ~selbits};
