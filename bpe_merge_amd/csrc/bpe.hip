@@ -35,15 +35,19 @@ using bpek::Ctl;
 namespace {
 
 // launch shapes
-// The merge pass runs 1024-thread workgroups on 16384-symbol tiles (one per
-// CU, half the look-backs and tile-counter atomics per symbol), or, when a
-// corpus has fewer than two such tiles per CU, 512-thread workgroups on
-// 8192-symbol tiles (two per CU) so that more of the chip takes part.
+// The merge pass runs 1024-thread workgroups on 32768-symbol tiles (one per
+// CU; 32 symbols per thread: fewer look-backs, status words and
+// tile-counter atomics per symbol), or, when a corpus has fewer than two
+// such tiles per CU, 512-thread workgroups on 16384-symbol tiles (two per
+// CU), or, below one of those per CU, 256-thread workgroups on 8192-symbol
+// tiles, so that more of the chip takes part.
 constexpr int MERGE_TPB_BIG = 1024;
 constexpr int MERGE_TPB_SMALL = 512;
+constexpr int MERGE_TPB_TINY = 256;
 constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
 constexpr int TILE = MERGE_TPB_BIG * bpek::MERGE_SYMS_PER_THREAD;  // the larger tile: symbol buffers are padded to it
 constexpr int TILE_SMALL = MERGE_TPB_SMALL * bpek::MERGE_SYMS_PER_THREAD;
+constexpr int TILE_TINY = MERGE_TPB_TINY * bpek::MERGE_SYMS_PER_THREAD;  // the smallest tile
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 
@@ -116,7 +120,7 @@ Layout layout_for(size_t n, uint32_t tlog2) {
     L.table = a;
     a = align_up(a + 8 * (size_t(1) << tlog2), 256);
     // at least 512 words: the look-back copies a 512-word window from index 0
-    L.max_tiles = std::max<uint32_t>(uint32_t((n + TILE_SMALL - 1) / TILE_SMALL) + 1, 512);
+    L.max_tiles = std::max<uint32_t>(uint32_t((n + TILE_TINY - 1) / TILE_TINY) + 1, 512);
     L.status = a;
     a = align_up(a + 8 * size_t(L.max_tiles), 256);
     L.merges = a;
@@ -199,15 +203,20 @@ namespace {
 // training has stopped does nothing). Plain launches: no workgroup of the
 // pass waits for one that has not started, so the grid need not be
 // resident all at once.
+template <int TPB>
+void launch_merge_tpb(bpe_state* s, uint32_t it) {
+    hipLaunchKernelGGL((bpek::k_merge<TPB, MERGE_LT>), dim3(s->merge_grid), dim3(TPB), bpek::cmask_lds_bytes(it),
+                       s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
+                       s->merges, s->cls, s->cmask);
+}
+
 void launch_merge(bpe_state* s, uint32_t it) {
     if (s->merge_tpb == MERGE_TPB_BIG)
-        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_BIG),
-                           bpek::cmask_lds_bytes(it), s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           s->merges, s->cls, s->cmask);
+        launch_merge_tpb<MERGE_TPB_BIG>(s, it);
+    else if (s->merge_tpb == MERGE_TPB_SMALL)
+        launch_merge_tpb<MERGE_TPB_SMALL>(s, it);
     else
-        hipLaunchKernelGGL((bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>), dim3(s->merge_grid), dim3(MERGE_TPB_SMALL),
-                           bpek::cmask_lds_bytes(it), s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                           s->merges, s->cls, s->cmask);
+        launch_merge_tpb<MERGE_TPB_TINY>(s, it);
 }
 
 void launch_force(bpe_state* s) {
@@ -404,13 +413,20 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
         return fail(BPE_EHIP);
     }
     int per_cu = 0;
-    s->merge_tpb = (n + TILE - 1) / TILE >= 2 * size_t(cus) ? MERGE_TPB_BIG : MERGE_TPB_SMALL;
+    // the largest tile that still gives every CU work
+    const size_t tiles_small = (n + TILE_SMALL - 1) / TILE_SMALL;
+    s->merge_tpb = (n + TILE - 1) / TILE >= 2 * size_t(cus) ? MERGE_TPB_BIG
+                   : tiles_small >= size_t(cus)             ? MERGE_TPB_SMALL
+                                                            : MERGE_TPB_TINY;
     if (s->merge_tpb == MERGE_TPB_BIG)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>,
                                                          MERGE_TPB_BIG, 0);
-    else
+    else if (s->merge_tpb == MERGE_TPB_SMALL)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>,
                                                          MERGE_TPB_SMALL, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_TINY, MERGE_LT>,
+                                                         MERGE_TPB_TINY, 0);
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     const size_t merge_tile = size_t(s->merge_tpb) * bpek::MERGE_SYMS_PER_THREAD;
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));

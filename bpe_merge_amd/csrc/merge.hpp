@@ -865,8 +865,8 @@ __host__ __device__ constexpr uint32_t cmask_lds_bytes(uint32_t it) { return 4u 
 // merge and publishes it; the others read the publication while their
 // first tile's loads are in flight.
 template <int TPB, int LT>
-// two workgroups per CU = 4 waves per SIMD: at most 128 VGPRs
-__global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
+// 1024- and 512-thread workgroups: 4 waves per SIMD (at most 128 VGPRs); 256-thread ones (the smallest corpora): 2
+__global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
                                                uint16_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
                                                uint32_t* lengths, Sweep* sw, uint32_t* merges,

@@ -18,7 +18,7 @@ import oracle
 from oracle import reference as ref
 
 from checks import (BASE, CLASS, ID, WS, byte_class, check_invariants, rank_encode,
-                    selected_occurrences)
+                    selected_occurrences, vocab_bytes)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
@@ -184,6 +184,27 @@ def test_rank_encoding_identity_and_invariants():
         m, t, lengths = oracle.train_chunks(d, 200)
         check_invariants(d, m, t, lengths)
         assert np.array_equal(rank_encode(d, m), t)
+
+
+def test_word_start_is_a_class_change_between_tokens():
+    """After any number of merges, a token carries the word-start bit
+    exactly when its class (that of its first byte) differs from the class
+    of the token before it, or it is the first: a word is a maximal run of
+    one class ("Ne Yapar? 1") and no merge crosses a word start, so
+    neighbouring words differ in class and every token lies in one word.
+    The merge pass stores 16-bit ids and derives the bit this way."""
+    cases = list(_small_corpora(30, 8192, seed0=700))
+    cases.append(corpus.generate(corpus.CONFIGS[5].scaled(200_000, seed=701)))
+    cases.append(np.frombuffer(b"aa  bb\n\n11,,aa", dtype=np.uint8))
+    for d in cases:
+        for k in (0, 1, 50, 400):
+            m, t, _ = oracle.train_chunks(d, k)
+            v = vocab_bytes(m)
+            cls_of = np.array([CLASS[v[i][0]] for i in range(len(v))], dtype=np.int8)
+            c = cls_of[t & ID]
+            ws = np.ones(t.size, dtype=bool)
+            ws[1:] = c[1:] != c[:-1]
+            assert np.array_equal((t & WS) != 0, ws)
 
 
 def test_invariant_checker_catches_planted_mistakes():
