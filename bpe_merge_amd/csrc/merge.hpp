@@ -810,12 +810,12 @@ __device__ __forceinline__ void select_and_publish(const GTable& gt, Sweep* sw, 
             st_agent(&sw->shift, shift);  // read by the sweep, after the publication
         }
     }
-    static_assert(PUB_COPIES <= TPB, "one copy per thread");
+    static_assert(PUB_COPIES % TPB == 0 || TPB % PUB_COPIES == 0, "whole rounds of copies");
     __syncthreads();  // the shift above is complete before any copy is published
-    if (threadIdx.x < PUB_COPIES) {
-        st_agent(&sw->pub[p][threadIdx.x], sel);
+    for (uint32_t c = threadIdx.x; c < PUB_COPIES; c += TPB) {
+        st_agent(&sw->pub[p][c], sel);
         __builtin_amdgcn_s_waitcnt(0);  // the value is visible before its epoch
-        st_agent(&sw->pub_epoch[p][threadIdx.x], it + 1u);
+        st_agent(&sw->pub_epoch[p][c], it + 1u);
     }
 }
 
