@@ -36,18 +36,18 @@ namespace {
 
 // launch shapes
 // The merge pass runs 1024-thread workgroups on 32768-symbol tiles (one per
-// CU; 32 symbols per thread: fewer look-backs, status words and
-// tile-counter atomics per symbol), or, when a corpus has fewer than two
+// CU; two halves of 16 symbols per thread: fewer look-backs, status words
+// and tile-counter atomics per symbol), or, when a corpus has fewer than two
 // such tiles per CU, 512-thread workgroups on 16384-symbol tiles (two per
-// CU), or, below one of those per CU, 256-thread workgroups on 8192-symbol
-// tiles, so that more of the chip takes part.
+// CU), or, below one of those per CU, 512-thread workgroups on 8192-symbol
+// tiles (one half), so that more of the chip takes part.
+enum MergeKind { MERGE_BIG, MERGE_SMALL, MERGE_TINY };
 constexpr int MERGE_TPB_BIG = 1024;
 constexpr int MERGE_TPB_SMALL = 512;
-constexpr int MERGE_TPB_TINY = 256;
 constexpr int MERGE_LT = 1024;             // LDS slots for count changes, per workgroup
-constexpr int TILE = MERGE_TPB_BIG * bpek::MERGE_SYMS_PER_THREAD;  // the larger tile: symbol buffers are padded to it
-constexpr int TILE_SMALL = MERGE_TPB_SMALL * bpek::MERGE_SYMS_PER_THREAD;
-constexpr int TILE_TINY = MERGE_TPB_TINY * bpek::MERGE_SYMS_PER_THREAD;  // the smallest tile
+constexpr int TILE = bpek::merge_tile(MERGE_TPB_BIG, 2);  // the larger tile: symbol buffers are padded to it
+constexpr int TILE_SMALL = bpek::merge_tile(MERGE_TPB_SMALL, 2);
+constexpr int TILE_TINY = bpek::merge_tile(MERGE_TPB_SMALL, 1);  // the smallest tile
 constexpr int TAG_TPB = 256;
 constexpr int TAG_LT = 4096;
 
@@ -190,7 +190,7 @@ struct bpe_state {
     uint32_t* fpairs = nullptr;
     uint32_t requested = 0;  // iterations enqueued so far
     int merge_grid = 0, tag_grid = 0, fill_grid = 0;
-    int merge_tpb = MERGE_TPB_BIG;
+    int merge_kind = MERGE_BIG;
     bool poisoned = false;   // a device error was seen
 
     uint32_t slots() const { return 1u << tlog2; }
@@ -203,20 +203,20 @@ namespace {
 // training has stopped does nothing). Plain launches: no workgroup of the
 // pass waits for one that has not started, so the grid need not be
 // resident all at once.
-template <int TPB>
-void launch_merge_tpb(bpe_state* s, uint32_t it) {
-    hipLaunchKernelGGL((bpek::k_merge<TPB, MERGE_LT>), dim3(s->merge_grid), dim3(TPB), bpek::cmask_lds_bytes(it),
-                       s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status, s->lengths, s->sweep,
-                       s->merges, s->cls, s->cmask);
+template <int TPB, int HALVES>
+void launch_merge_kind(bpe_state* s, uint32_t it) {
+    hipLaunchKernelGGL((bpek::k_merge<TPB, MERGE_LT, HALVES>), dim3(s->merge_grid), dim3(TPB),
+                       bpek::cmask_lds_bytes(it), s->stream, it, s->ctl, s->sym0, s->sym1, s->gtable(), s->status,
+                       s->lengths, s->sweep, s->merges, s->cls, s->cmask);
 }
 
 void launch_merge(bpe_state* s, uint32_t it) {
-    if (s->merge_tpb == MERGE_TPB_BIG)
-        launch_merge_tpb<MERGE_TPB_BIG>(s, it);
-    else if (s->merge_tpb == MERGE_TPB_SMALL)
-        launch_merge_tpb<MERGE_TPB_SMALL>(s, it);
+    if (s->merge_kind == MERGE_BIG)
+        launch_merge_kind<MERGE_TPB_BIG, 2>(s, it);
+    else if (s->merge_kind == MERGE_SMALL)
+        launch_merge_kind<MERGE_TPB_SMALL, 2>(s, it);
     else
-        launch_merge_tpb<MERGE_TPB_TINY>(s, it);
+        launch_merge_kind<MERGE_TPB_SMALL, 1>(s, it);
 }
 
 void launch_force(bpe_state* s) {
@@ -415,20 +415,23 @@ bpe_status state_setup(bpe_state* s, const uint8_t* bytes, size_t n, const bpe_c
     int per_cu = 0;
     // the largest tile that still gives every CU work
     const size_t tiles_small = (n + TILE_SMALL - 1) / TILE_SMALL;
-    s->merge_tpb = (n + TILE - 1) / TILE >= 2 * size_t(cus) ? MERGE_TPB_BIG
-                   : tiles_small >= size_t(cus)             ? MERGE_TPB_SMALL
-                                                            : MERGE_TPB_TINY;
-    if (s->merge_tpb == MERGE_TPB_BIG)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_BIG, MERGE_LT>,
+    s->merge_kind = (n + TILE - 1) / TILE >= 2 * size_t(cus) ? MERGE_BIG
+                    : tiles_small >= size_t(cus)             ? MERGE_SMALL
+                                                             : MERGE_TINY;
+    size_t merge_tile = TILE;
+    if (s->merge_kind == MERGE_BIG) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_BIG, MERGE_LT, 2>,
                                                          MERGE_TPB_BIG, 0);
-    else if (s->merge_tpb == MERGE_TPB_SMALL)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT>,
+    } else if (s->merge_kind == MERGE_SMALL) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT, 2>,
                                                          MERGE_TPB_SMALL, 0);
-    else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_TINY, MERGE_LT>,
-                                                         MERGE_TPB_TINY, 0);
+        merge_tile = TILE_SMALL;
+    } else {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bpek::k_merge<MERGE_TPB_SMALL, MERGE_LT, 1>,
+                                                         MERGE_TPB_SMALL, 0);
+        merge_tile = TILE_TINY;
+    }
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    const size_t merge_tile = size_t(s->merge_tpb) * bpek::MERGE_SYMS_PER_THREAD;
     s->merge_grid = int(std::min<size_t>(size_t(cus) * per_cu, (n + merge_tile - 1) / merge_tile + 1));
     s->tag_grid = int(std::min<size_t>(size_t(cus) * 2, tag_grid_bound(n)));
     s->fill_grid = cus * 4;

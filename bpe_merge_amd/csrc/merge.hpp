@@ -344,15 +344,16 @@ constexpr int BUF_NT = 2;
 // equals it and it belongs to no class.
 constexpr uint32_t NOSYM = 0x10000u;
 
-// A tile is two halves of TPB * 16 symbols; a thread holds 16 consecutive
-// symbols of each, at g0 = tile * TILE + tid * 16 and g0 + TILE / 2. Issue
-// the loads of both (two 16-byte loads each) and, on the wave's edge lanes,
+// A tile is HALVES (two, or one for the smallest corpora) halves of
+// TPB * 16 symbols; a thread holds 16 consecutive symbols of each, at
+// g0 = tile * TILE + tid * 16 and g0 + TILE / 2. Issue the loads of each
+// (two 16-byte loads) and, on the wave's edge lanes,
 // of the neighbours the shuffles cannot supply: hw = sym[g0 - 2] |
 // sym[g0 - 1] << 16 on lane 0, hr (low half: sym[g0 + 16]) on lane 63.
 // Buffer loads through a resource covering the tile, the two symbols before
 // it and the one after it (within n, in whole 4-byte words: the padded
-// array holds the 16-bit word past n): every lane issues the same eight
-// loads, a lane with nothing to load uses an offset past the resource (the
+// array holds the 16-bit word past n): every lane issues the same four
+// loads per half, a lane with nothing to load uses an offset past the resource (the
 // hardware returns 0 without a memory access), and a tile past the end gets
 // an empty resource. With no branch and a fixed count, the compiler can
 // wait for these loads alone, later. The words stay packed until fix_tile,
@@ -362,7 +363,7 @@ struct TileRegs {
     uint32_t xr[2][8];  // per half: 16 ids, two per word
     uint32_t hw[2], hr[2];
 };
-template <int TILE>
+template <int TILE, int HALVES>
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ in, uint32_t n, uint32_t tile,
                                           uint32_t ntiles, uint32_t tid, uint32_t lane, TileRegs& r) {
     tile = __builtin_amdgcn_readfirstlane(tile);  // uniform: the resource lives in SGPRs
@@ -373,14 +374,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ in, uint3
     // the edge values first: the compiler can then wait for them without
     // waiting for the 16-byte loads (one in-order counter)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t g0 = ts + (uint32_t)h * (TILE / 2) + tid * 16u, o = 2u * (g0 - hb);
+    for (int h = 0; h < HALVES; ++h) {
+        const uint32_t g0 = ts + (uint32_t)h * (TILE / HALVES) + tid * 16u, o = 2u * (g0 - hb);
         r.hw[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane == 0 && g0 >= 2u) ? o - 4u : BUF_OOB, 0, 0);
         r.hr[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane == 63 ? o + 32u : BUF_OOB, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t o = 2u * (ts + (uint32_t)h * (TILE / 2) + tid * 16u - hb);
+    for (int h = 0; h < HALVES; ++h) {
+        const uint32_t o = 2u * (ts + (uint32_t)h * (TILE / HALVES) + tid * 16u - hb);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16u * q, 0, 0);
@@ -555,8 +556,9 @@ __device__ __forceinline__ void finish_iteration(Ctl* ctl, uint32_t* lengths, ui
 // global_load_lds.
 constexpr int LB_PL = 4;
 constexpr int LB_WIN = 2 * 64 * LB_PL;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= 8, expcnt and lgkmcnt untouched
-constexpr int WAIT_VM8 = 0x0F78;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= n (n < 16), expcnt and
+// lgkmcnt untouched
+constexpr int wait_vm(int n) { return 0x0F70 | n; }
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 
 // One persistent pass per iteration. Workgroups take tiles from a counter,
@@ -617,9 +619,10 @@ __device__ __forceinline__ void lds_copy16(const unsigned long long* src, const 
 // Values loaded by load_tile that a round does not consume: an empty use,
 // so that the compiler waits for their loads in that round and not when
 // the registers are next loaded.
+template <int HALVES>
 __device__ __forceinline__ void retire(const TileRegs& r) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < HALVES; ++h)
         asm volatile("" ::"v"(r.xr[h][0]), "v"(r.xr[h][1]), "v"(r.xr[h][2]), "v"(r.xr[h][3]), "v"(r.xr[h][4]),
                      "v"(r.xr[h][5]), "v"(r.xr[h][6]), "v"(r.xr[h][7]), "v"(r.hw[h]), "v"(r.hr[h]));
 }
@@ -853,8 +856,8 @@ __device__ __forceinline__ void finish_counts(LdsTable<LT>& tab, const GTable& g
     if (tab.used) flush_table_sel(tab, TPB, gt, ctl, sw, theta);  // uniform: read after the barrier
 }
 
-// Symbols per thread of a merge pass's tile (two halves of 16).
-constexpr int MERGE_SYMS_PER_THREAD = 32;
+// Symbols of a merge pass's tile: HALVES halves of 16 symbols per thread.
+__host__ __device__ constexpr int merge_tile(int tpb, int halves) { return tpb * 16 * halves; }
 
 // Dynamic LDS of the pass of iteration it: the class mask of ids up to
 // X = 256 + it.
@@ -864,17 +867,19 @@ __host__ __device__ constexpr uint32_t cmask_lds_bytes(uint32_t it) { return 4u 
 // has stopped does nothing). The workgroup that draws ticket 0 selects the
 // merge and publishes it; the others read the publication while their
 // first tile's loads are in flight.
-template <int TPB, int LT>
-// 1024- and 512-thread workgroups: 4 waves per SIMD (at most 128 VGPRs); 256-thread ones (the smallest corpora): 2
-__global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
+template <int TPB, int LT, int HALVES>
+// 4 waves per SIMD: at most 128 VGPRs
+__global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
                                                uint16_t* __restrict__ buf1, GTable gt,
                                                unsigned long long* status,
                                                uint32_t* lengths, Sweep* sw, uint32_t* merges,
                                                uint8_t* __restrict__ cls, uint32_t* __restrict__ cmask) {
     constexpr int V = 16;  // symbols per thread and half: two 16-byte loads
     constexpr int HALF = TPB * V;
-    constexpr int TILE = 2 * HALF;
-    static_assert(TILE == TPB * MERGE_SYMS_PER_THREAD, "the host sizes grids by this tile");
+    constexpr int TILE = HALVES * HALF;
+    constexpr bool TWO = HALVES == 2;
+    static_assert(HALVES == 1 || HALVES == 2, "one or two halves");
+    static_assert(TILE == merge_tile(TPB, HALVES), "the host sizes grids by this tile");
     constexpr int NW = TPB / 64;
     constexpr uint32_t VM = (1u << V) - 1u;
     constexpr uint32_t SST = TILE + TILE / 64;  // one staging buffer (skewed)
@@ -932,7 +937,7 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
     uint32_t t = s_tile[0] - tile_base;
     TileRegs tr;
     static_assert(V == 16, "load_tile and fix_tile take 16 symbols per thread and half");
-    load_tile<TILE>(in, n, t, ntiles, tid, lane, tr);
+    load_tile<TILE, HALVES>(in, n, t, ntiles, tid, lane, tr);
     unsigned long long best = read_publication(sw, ctl, p, it, s_best);
     if (best == SEL_SWEEP) best = sweep_select<TPB>(gt, sw, ctl, p, it, s_best, &s_u32, lane, w, theta);  // uniform
     if (best == 0ull) {  // uniform: no countable pair is left
@@ -997,15 +1002,18 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;  // half A; half B at g0 + HALF
                 const bool full = t * TILE + TILE <= n;
-                uint32_t x[V], a1, a2, b1, occa, valida, occb, validb;
+                uint32_t x[V], a1, a2, b1, occa, valida, occb = 0, validb = 0, sel_inb = 0, leftb = NOSYM;
                 fix_tile(x, tr.xr[0], tr.hw[0], tr.hr[0], g0, n, lane, full, a1, a2, b1);
                 occurrences<V>(x, a1, b1, g0, n, L, R, occa, valida);
                 // sel = occ; the position before g0 is merged iff it is an occurrence
                 const uint32_t sel_ina = (a2 == L && a1 == R) ? 1u : 0u;  // NOSYM before the start
                 const uint32_t lefta = a1;
-                fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
-                occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
-                const uint32_t sel_inb = (a2 == L && a1 == R) ? 1u : 0u;
+                if constexpr (TWO) {
+                    fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
+                    occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
+                    sel_inb = (a2 == L && a1 == R) ? 1u : 0u;
+                    leftb = a1;
+                }
 
                 // ---- kept counts of both halves in one word (at most HALF
                 // each): wave scan, then across the waves
@@ -1025,12 +1033,14 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
 
                 uint16_t* st = s_stage + cur * SST;
                 // half B first (its ids are unpacked), then half A again from its words
-                stage<V>(st, kept_a + (ex >> 16), tr.xr[1], x, validb, occb, X);
-                if (do_count && (occb | sel_inb)) {
-                    const Changes<V> ch(occb, sel_inb, validb);
-                    ccb = CountArgs{ch.gone, ch.born, occb, sel_inb, a1, st, kept_a + (ex >> 16), validb & ~occb};
+                if constexpr (TWO) {
+                    stage<V>(st, kept_a + (ex >> 16), tr.xr[1], x, validb, occb, X);
+                    if (do_count && (occb | sel_inb)) {
+                        const Changes<V> ch(occb, sel_inb, validb);
+                        ccb = CountArgs{ch.gone, ch.born, occb, sel_inb, leftb, st, kept_a + (ex >> 16), validb & ~occb};
+                    }
+                    unpack(x, tr.xr[0]);
                 }
-                unpack(x, tr.xr[0]);
                 stage<V>(st, ex & 0xFFFFu, tr.xr[0], x, valida, occa, X);
                 if (do_count && (occa | sel_ina)) {
                     const Changes<V> ch(occa, sel_ina, valida);
@@ -1038,11 +1048,11 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(tr);
+                retire<HALVES>(tr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, tr);
+            load_tile<TILE, HALVES>(in, n, tn, ntiles, tid, lane, tr);
             if (cca.gone | cca.born)
                 count_changes<LT>(tab, gt, ctl, sw, theta, cca.gone, cca.born, cca.sel, cca.sel_in, cca.left, cca.st,
                                   cca.o, cca.kept, L, R, X, s_cmask);
@@ -1053,9 +1063,9 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
             if (tp < ntiles && w == 0) {
                 uint32_t off = 0, sel = 0;
                 if (tp != 0) {
-                    // the window's copies are older than the eight loads of
-                    // load_tile above: all but the last eight accesses done
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+                    // the window's copies are older than the four loads per
+                    // half of load_tile above: all but that many accesses done
+                    __builtin_amdgcn_s_waitcnt(wait_vm(4 * HALVES));
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll
@@ -1124,13 +1134,16 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
             if (t < ntiles) {  // uniform
                 const uint32_t g0 = t * TILE + tid * V;  // half A; half B at g0 + HALF
                 const bool full = t * TILE + TILE <= n;
-                uint32_t x[V], a1, a2, b1, occa, valida, occb, validb;
+                uint32_t x[V], a1, a2, b1, occa, valida, occb = 0, validb = 0, leftb = NOSYM;
                 fix_tile(x, tr.xr[0], tr.hw[0], tr.hr[0], g0, n, lane, full, a1, a2, b1);
                 occurrences<V>(x, a1, b1, g0, n, L, R, occa, valida);
                 const uint32_t lefta = a1;
                 const uint32_t dep0 = (occa & 1u) | (uint32_t)(a2 == L && a1 == L);  // used by thread 0
-                fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
-                occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
+                if constexpr (TWO) {
+                    fix_tile(x, tr.xr[1], tr.hw[1], tr.hr[1], g0 + HALF, n, lane, full, a1, a2, b1);
+                    occurrences<V>(x, a1, b1, g0 + HALF, n, L, R, occb, validb);
+                    leftb = a1;
+                }
 
                 // ---- each half's tuple per thread, then inclusive scans over
                 // the wave and the waves, half by half
@@ -1148,21 +1161,21 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
                 };
                 auto then = [](uint32_t a, uint32_t b) { return tup_then(a, b); };
                 const uint32_t incla = wave_scan(thread_tuple(occa, valida), TUP_ID, then);
-                const uint32_t inclb = wave_scan(thread_tuple(occb, validb), TUP_ID, then);
+                const uint32_t inclb = TWO ? wave_scan(thread_tuple(occb, validb), TUP_ID, then) : TUP_ID;
                 const uint32_t lane_excla = dpp<DPP_WAVE_SHR1>(TUP_ID, incla);
                 const uint32_t lane_exclb = dpp<DPP_WAVE_SHR1>(TUP_ID, inclb);
                 if (lane == 63) {
                     s_wagg[w] = incla;
-                    s_waggb[w] = inclb;
+                    if constexpr (TWO) s_waggb[w] = inclb;
                 }
                 if (tid == 0) {
                     s_tile[round & 1u] = grab - tile_base;
                     s_dep = dep0;
                 }
                 lds_barrier();
-                uint32_t wave_excla, agg_a, wave_exclb, agg_b;
+                uint32_t wave_excla, agg_a, wave_exclb = TUP_ID, agg_b = TUP_ID;
                 waves_prefix<NW>(s_wagg, w, lane, TUP_ID, then, wave_excla, agg_a);
-                waves_prefix<NW>(s_waggb, w, lane, TUP_ID, then, wave_exclb, agg_b);
+                if constexpr (TWO) waves_prefix<NW>(s_waggb, w, lane, TUP_ID, then, wave_exclb, agg_b);
                 tile_agg = tup_then(agg_a, agg_b);
                 dep = s_dep != 0u;  // uniform
                 // the tile's aggregate (tile 0: prefix) goes out before anything else is done
@@ -1205,15 +1218,15 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
                     return selbits;
                 };
                 uint16_t* st = s_stage + cur * SST;
-                unpack(x, tr.xr[1]);
-                {
+                if constexpr (TWO) {
+                    unpack(x, tr.xr[1]);
                     const uint32_t loc = tup_c0(texclb) + (tile_sel ? tup_d(texclb) : 0u);
                     const uint32_t sel_in = tup_o(texclb, tile_sel);
                     const uint32_t selbits = resolve(occb, sel_in);
                     stage<V>(st, loc, tr.xr[1], x, validb, selbits, X);
                     if (do_count && (occb | sel_in)) {
                         const Changes<V> ch(selbits, sel_in, validb);
-                        ccb = CountArgs{ch.gone, ch.born, selbits, sel_in, a1, st, loc, validb & ~selbits};
+                        ccb = CountArgs{ch.gone, ch.born, selbits, sel_in, leftb, st, loc, validb & ~selbits};
                     }
                 }
                 unpack(x, tr.xr[0]);
@@ -1229,11 +1242,11 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
                 }
                 tn = s_tile[round & 1u];
             } else {
-                retire(tr);
+                retire<HALVES>(tr);
             }
             // ---- the next tile's loads (an empty resource when there is none), then this
             // tile's count changes (they need the old symbols only as masks and staged values)
-            load_tile<TILE>(in, n, tn, ntiles, tid, lane, tr);
+            load_tile<TILE, HALVES>(in, n, tn, ntiles, tid, lane, tr);
             if (cca.gone | cca.born)
                 count_changes<LT>(tab, gt, ctl, sw, theta, cca.gone, cca.born, cca.sel, cca.sel_in, cca.left, cca.st,
                                   cca.o, cca.kept, L, R, X, s_cmask);
@@ -1244,7 +1257,7 @@ __global__ __launch_bounds__(TPB, TPB >= 512 ? 4 : 2) void k_merge(uint32_t it, 
             if (tp < ntiles && w == 0) {
                 uint32_t off = off_p, sel = 0;
                 if (!done_p) {  // tp != 0
-                    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+                    __builtin_amdgcn_s_waitcnt(wait_vm(4 * HALVES));
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     unsigned long long lbw[LB_PL];
 #pragma unroll
