@@ -8,7 +8,9 @@
 // + prefix-scan compaction of the symbol array ("Ne Yapar? 3").
 //
 // How the work is laid out here (not the page's WGSL dispatch plan):
-//   k_tag_count  bytes -> tagged uint32 symbols, and the pair counts of
+//   k_tag_count  bytes -> 16-bit symbols (the word starts decide which
+//                pairs count; they are not stored: a word start is a change
+//                of class between neighbours), and the pair counts of
 //                iteration 0 in the global table (LDS aggregation first).
 //   k_merge      (merge.hpp) one persistent pass per iteration that selects
 //                the merge (from a candidate list, or by a sweep of the

@@ -14,8 +14,9 @@
 //      sums these changes in an LDS table and adds the sums to the global
 //      table at the end.
 // The page runs these as separate dispatches with a three-pass scan; here
-// the scan is a single-pass decoupled look-back over tiles of 16384 symbols
-// (1024-thread workgroups) or 8192 (512-thread workgroups, on small
+// the scan is a single-pass decoupled look-back over tiles of 32768 symbols
+// (1024-thread workgroups, two halves of 16 symbols per thread), 16384
+// (512 threads, two halves) or 8192 (512 threads, one half: the smallest
 // corpora), so the symbols are read once and written once per iteration.
 //
 // The symbol array holds 16-bit ids and no word-start bit. The page tags

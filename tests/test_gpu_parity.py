@@ -161,6 +161,26 @@ def test_host_pointer_input(bpe):
     assert np.array_equal(toks[: n_tok.value], ot)
 
 
+def test_tokens_read_into_host_memory_between_merges(bpe):
+    # bpe_tokens into host memory passes through the symbol buffer the next
+    # merge pass writes (in two halves); training goes on unchanged after it
+    import ctypes
+    for n in (1, 2, 3, 4097, 100_001):
+        d = corpus.generate(corpus.CONFIGS[3].scaled(n, seed=70 + n % 7))
+        _say("host tokens n=%d" % n)
+        with bpe.State(_dev(d), table_log2=16) as st:
+            for k in (0, 5, 40):
+                while len(st.merges()) < k and st.step() is not None:
+                    pass
+                done = len(st.merges())
+                toks = np.zeros(max(d.size, 1), dtype=np.uint32)
+                n_tok = ctypes.c_size_t(0)
+                assert bpe._lib.bpe_tokens(st._h, toks.ctypes.data, toks.size, ctypes.byref(n_tok)) == bpe.OK
+                _, ot, _ = oracle.train_chunks(d, done)
+                assert np.array_equal(toks[: n_tok.value], ot), (n, k)
+                assert np.array_equal(st.tokens().cpu().numpy().astype(np.uint32), ot), (n, k)
+
+
 def test_determinism_and_table_size_independence(bpe):
     d = corpus.generate(corpus.CONFIGS[5].scaled(400_000, seed=11))
     ref = gpu_train(bpe, d, 120, table_log2=17)
