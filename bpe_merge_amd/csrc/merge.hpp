@@ -264,17 +264,38 @@ typedef uint32_t __attribute__((may_alias)) lds32_t;
 // left neighbour is X when i - 1 was dropped (sel_{i-1}), otherwise the
 // unchanged old symbol i - 1; the value is X when sel_{i+1}. Both masks
 // hold candidates: a pair counts only if its ids share a class (no word
-// start between them), which count_changes tests.
+// start between them), which count_changes tests. For L != R the pair
+// (i - 1, i) of a dropped position i is (L, R) itself, and no other
+// changed position holds it: its count after the pass is 0, set once for
+// the whole pass (zero_count) instead of one decrement per site, so those
+// positions are left out (merged_pair_set).
 template <int V>
 struct Changes {
     uint32_t gone, born;  // position masks
-    __device__ __forceinline__ Changes(uint32_t sel, uint32_t sel_in, uint32_t valid) {
+    __device__ __forceinline__ Changes(uint32_t sel, uint32_t sel_in, uint32_t valid, bool merged_pair_set) {
         constexpr uint32_t VM = (1u << V) - 1u;
         const uint32_t sm1 = ((sel << 1) | sel_in) & VM, s0 = sel & VM, sp1 = (sel >> 1) & VM;
-        gone = (sm1 | s0 | sp1) & valid;
+        gone = (sm1 | (merged_pair_set ? 0u : s0) | sp1) & valid;
         born = ~s0 & (sm1 | sp1) & valid & VM;
     }
 };
+
+// The count of key in the global table set to 0 (no-op when the key has
+// no slot). Used for the merged pair (L, R) with L != R, which occurs
+// nowhere after its pass; no other change of the pass touches its slot.
+__device__ __forceinline__ void zero_count(const GTable& gt, uint32_t key) {
+    uint32_t h = mix32(key) & gt.mask;
+    for (uint32_t p = 0; p < GT_PROBES; ++p) {
+        const unsigned long long v = __hip_atomic_load(gt.slot + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t cur = (uint32_t)v;
+        if (cur == key) {
+            __hip_atomic_store(gt.slot + h, (unsigned long long)key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (cur == EMPTY) return;
+        h = (h + 1) & gt.mask;
+    }
+}
 
 // The arguments of count_changes, held from a tile's staging until after
 // the next tile's loads are issued (gone = born = 0: nothing to count).
@@ -303,33 +324,34 @@ __device__ __forceinline__ void count_changes(LdsTable<LT>& tab, const GTable& g
         if ((sel >> (j + 1)) & 1u) return L;
         return (uint32_t)reinterpret_cast<const lds16_t*>(st)[skew(o + __popc(kept & ((1u << j) - 1u)))];
     };
-    auto in_class = [&](uint32_t v) -> bool { return v == X || (v < X && ((cm[v >> 5] >> (v & 31u)) & 1u)); };
+    auto in_class = [&](uint32_t v) -> bool {
+        return v == X || v == L || v == R || (v < X && ((cm[v >> 5] >> (v & 31u)) & 1u));
+    };
     const uint32_t sm1 = (sel << 1) | sel_in;  // bit j: sel of position j - 1
-    while (gone | born) {
-        const bool is_gone = gone != 0u;
-        const uint32_t j = __ffs(is_gone ? gone : born) - 1;
-        const uint32_t xl = j ? old_id(j - 1) : left;
-        uint32_t a, b, delta;
-        if (is_gone) {
-            a = xl;
-            b = old_id(j);
-            delta = 0xFFFFFFFFu;
-            gone &= gone - 1u;
-        } else {
-            a = ((sm1 >> j) & 1u) ? X : xl;
-            b = ((sel >> (j + 1)) & 1u) ? X : old_id(j);
-            delta = 1u;
-            born &= born - 1u;
-        }
-        // one id of the pair is L, R or X: the pair lies in one word iff
+    // one position per loop turn: its old pair (gone) and its new pair
+    // (born) share the two old ids and their class tests
+    for (uint32_t both = gone | born; both; both &= both - 1u) {
+        const uint32_t j = __ffs(both) - 1;
+        const uint32_t xl = j ? old_id(j - 1) : left, xj = old_id(j);
+        // one id of each pair is L, R or X: the pair lies in one word iff
         // the other id has the merge's class too
-        if (in_class(a) && in_class(b) && !tab.insert(pair_key(a, b), delta)) {
-            gt_add_sel(gt, pair_key(a, b), delta, ctl, sw, theta);  // the LDS table is full
-            // (rare) drain this path's memory operations here: otherwise
-            // the compiler assumes they may still be pending where the
-            // paths join, and waits for every access, the next tile's
-            // loads included, before the look-back
-            __builtin_amdgcn_s_waitcnt(0);
+        const bool cl = in_class(xl), cj = in_class(xj);
+        const bool l_is_x = (sm1 >> j) & 1u, j_is_x = (sel >> (j + 1)) & 1u;
+        const bool g = ((gone >> j) & 1u) && cl && cj;
+        const bool b = ((born >> j) & 1u) && (l_is_x || cl) && (j_is_x || cj);
+        const uint32_t kg = pair_key(xl, xj), kb = pair_key(l_is_x ? X : xl, j_is_x ? X : xj);
+#pragma unroll 1
+        for (uint32_t e = 0; e < 2u; ++e) {
+            if (!(e ? b : g)) continue;
+            const uint32_t key = e ? kb : kg, delta = e ? 1u : 0xFFFFFFFFu;
+            if (!tab.insert(key, delta)) {
+                gt_add_sel(gt, key, delta, ctl, sw, theta);  // the LDS table is full
+                // (rare) drain this path's memory operations here: otherwise
+                // the compiler assumes they may still be pending where the
+                // paths join, and waits for every access, the next tile's
+                // loads included, before the look-back
+                __builtin_amdgcn_s_waitcnt(0);
+            }
         }
     }
 }
@@ -969,6 +991,8 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
         // X has L's class; passes of this launch read only bits below X
         cls[X] = (uint8_t)c;
         atomicOr(&cmask[c * CLASS_WORDS + (X >> 5)], 1u << (X & 31u));
+        // every (L, R) with L != R is merged: its count becomes 0 (Changes)
+        if (do_count && L != R && R == (key & IDM)) zero_count(gt, key);
     }
     // the mask of the merge's class, for the ids up to X
     for (uint32_t i = tid; i <= (X >> 5) && i < CLASS_WORDS; i += TPB) s_cmask[i] = cmask[c * CLASS_WORDS + i];
@@ -1037,14 +1061,14 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                 if constexpr (TWO) {
                     stage<V>(st, kept_a + (ex >> 16), tr.xr[1], x, validb, occb, X);
                     if (do_count && (occb | sel_inb)) {
-                        const Changes<V> ch(occb, sel_inb, validb);
+                        const Changes<V> ch(occb, sel_inb, validb, true);
                         ccb = CountArgs{ch.gone, ch.born, occb, sel_inb, leftb, st, kept_a + (ex >> 16), validb & ~occb};
                     }
                     unpack(x, tr.xr[0]);
                 }
                 stage<V>(st, ex & 0xFFFFu, tr.xr[0], x, valida, occa, X);
                 if (do_count && (occa | sel_ina)) {
-                    const Changes<V> ch(occa, sel_ina, valida);
+                    const Changes<V> ch(occa, sel_ina, valida, true);
                     cca = CountArgs{ch.gone, ch.born, occa, sel_ina, lefta, st, ex & 0xFFFFu, valida & ~occa};
                 }
                 tn = s_tile[round & 1u];
@@ -1226,7 +1250,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     const uint32_t selbits = resolve(occb, sel_in);
                     stage<V>(st, loc, tr.xr[1], x, validb, selbits, X);
                     if (do_count && (occb | sel_in)) {
-                        const Changes<V> ch(selbits, sel_in, validb);
+                        const Changes<V> ch(selbits, sel_in, validb, false);
                         ccb = CountArgs{ch.gone, ch.born, selbits, sel_in, leftb, st, loc, validb & ~selbits};
                     }
                 }
@@ -1237,7 +1261,7 @@ __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_
                     const uint32_t selbits = resolve(occa, sel_in);
                     stage<V>(st, loc, tr.xr[0], x, valida, selbits, X);
                     if (do_count && (occa | sel_in)) {
-                        const Changes<V> ch(selbits, sel_in, valida);
+                        const Changes<V> ch(selbits, sel_in, valida, false);
                         cca = CountArgs{ch.gone, ch.born, selbits, sel_in, lefta, st, loc, valida & ~selbits};
                     }
                 }
