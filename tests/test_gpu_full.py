@@ -97,7 +97,8 @@ def test_full_size_workload_matches_oracle(bpe, cfg):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,n_bytes", [(2, 8 << 20), (5, 4 << 20)])
+# 8 MiB and 4 MiB: 16384-symbol tiles; 3 MiB: 8192-symbol tiles (one half)
+@pytest.mark.parametrize("cfg,n_bytes", [(2, 8 << 20), (5, 4 << 20), (5, 3 << 20)])
 def test_training_to_the_last_id(bpe, cfg, n_bytes):
     # 65,280 merges: ids 256 .. 65,535; the last merge creates id 0xFFFF,
     # after which no pair is counted and no further merge is allowed
