@@ -584,22 +584,6 @@ constexpr int LB_WIN = 2 * 64 * LB_PL;
 constexpr int wait_vm(int n) { return 0x0F70 | n; }
 static_assert(LB_WIN % 128 == 0, "whole 16-byte copies per lane");
 
-// One persistent pass per iteration. Workgroups take tiles from a counter,
-// in order, so every tile a look-back waits for is held by a
-// running workgroup that has already published or is about to publish its
-// aggregate.
-//
-// L != R (nearly every merge): occurrences cannot overlap, so every
-// occurrence is merged and sel_i = occ_i. A tile's kept symbols, its staged
-// output and its count changes are then known from the tile and two
-// symbols before it; the look-back only supplies the tile's output offset.
-// The workgroup publishes the tile's aggregate, stages and counts, takes
-// the next tile and issues its loads, and only then waits for the look-back
-// and writes: the next tile's loads are in flight while it waits.
-//
-// L == R: the selection carries along runs (sel_i = occ_i and not
-// sel_{i-1}) and a tile's selection can depend on every tile before it, so
-// staging waits for the look-back's sel as well.
 // Prefixes over the workgroup's NW <= 16 wave totals tot[] in LDS, for the
 // calling wave w (uniform): the combination of the totals of waves 0 .. w-1
 // (ident for wave 0) and of all NW. Lane i of each 16-lane row takes total
@@ -889,7 +873,23 @@ __host__ __device__ constexpr uint32_t cmask_lds_bytes(uint32_t it) { return 4u 
 // One launch per iteration it (the host passes it; a launch after training
 // has stopped does nothing). The workgroup that draws ticket 0 selects the
 // merge and publishes it; the others read the publication while their
-// first tile's loads are in flight.
+// first tile's loads are in flight. Then a persistent pass: workgroups take
+// tiles from a counter, in order, so every tile a look-back waits for is
+// held by a running workgroup that has already published or is about to
+// publish its aggregate.
+//
+// L != R (nearly every merge): occurrences cannot overlap, so every
+// occurrence is merged and sel_i = occ_i. A tile's kept symbols, its staged
+// output and its count changes are then known from the tile and the two
+// symbols before each half; the look-back only supplies the tile's output
+// offset. The workgroup publishes the tile's aggregate, stages it, takes
+// the next tile and issues its loads, applies the count changes, and only
+// then waits for the look-back and writes: the next tile's loads are in
+// flight while it waits.
+//
+// L == R: the selection carries along runs (sel_i = occ_i and not
+// sel_{i-1}) and a tile's selection can depend on every tile before it, so
+// staging waits for the look-back's sel as well.
 template <int TPB, int LT, int HALVES>
 // 4 waves per SIMD: at most 128 VGPRs
 __global__ __launch_bounds__(TPB, 4) void k_merge(uint32_t it, Ctl* ctl, uint16_t* __restrict__ buf0,
