@@ -172,7 +172,7 @@ def train_chunked(data, n_merges: int, table_log2: int | None = None, tokens: bo
                   always_chunks: bool = False):
     """bpe_train_chunked on a uint8 CUDA tensor: training over the corpus's
     distinct words, each weighted by its frequency (or over the full symbol
-    array where their records would take more than 16 bytes per input
+    array where their records would take more than 8 bytes per input
     byte, unless always_chunks). Returns (merges, tokens) as train() does (tokens is
     None when tokens=False)."""
     torch = _torch()

@@ -180,8 +180,9 @@ bpe_status bpe_train_static(const uint8_t *bytes, size_t n, uint32_t n_merges, u
  * longer word, the pair table with 24 more bytes per slot for the pairs'
  * chunk lists, and up to 256 bytes per distinct word for the lists
  * themselves) and frees it before returning. Where the distinct words'
- * records would take more than 16 bytes per input byte (bytes with almost
- * no repeated word), it runs bpe_train instead.
+ * records would take more than 8 bytes per input byte (text with few
+ * repeated words, where the full array is faster), it runs bpe_train
+ * instead.
  * Blocks until done. Errors as bpe_train, and as bpe_encoder_encode for the
  * tokens.
  */

@@ -135,7 +135,7 @@ def test_host_buffers_through_the_c_abi(bpe):
 
 
 def test_default_path_choice_gives_the_same_results(bpe):
-    # as called (the full array only past a memory bound that these stay under)
+    # as called: over the chunks or, past the records' bound, over the full array
     for cfg, n in ((3, 1_000_003), (5, 1_000_003), (2, 300_001)):
         spec = corpus.CONFIGS[cfg].scaled(n, seed=540 + cfg)
         _check(bpe, corpus.generate(spec), 1200, "default path, %s" % spec.kind, always=False)
