@@ -1879,9 +1879,7 @@ bpe_status train_chunked(const uint8_t* bytes, size_t n, uint32_t n_merges, cons
         // memory against the corpus (an iteration reads 8 bytes of filter
         // per record and the records that hold the merged pair, the full
         // array's pass 4 bytes per symbol: the chunks win where the records
-        // are fewer than about one per 8 bytes; byte runs with mostly
-        // distinct random words, 128 MiB: 5.7k merges/s over the chunks,
-        // 7.0k over the full array)
+        // are fewer than about one per 8 bytes)
         const size_t n_rec = size_t(h[0]) + (h[2] - h[3]);
         if (!always && 64 * n_rec + 2 * size_t(h[4]) > 8 * n) {
             *full = true;
